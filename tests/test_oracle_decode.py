@@ -1,0 +1,185 @@
+"""Pins for the oracle's decode attention over a paged KVarN cache.
+
+The decode oracle is the plain definition (softmax attention over the
+read-back cache, double precision).  It is pinned against torch's
+scaled_dot_product_attention (a library routine) where the cache is all
+fp16, against the special cases the definition implies, and against the
+scale-folding identity that the fused path relies on (evermx.com KVarN
+review, method paragraph: scales folded back in at read time; the rotation
+is orthonormal, so scores are preserved).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth.cases import WORKLOADS, make_case
+
+
+def small(**over):
+    w = dict(WORKLOADS["tiny_d128_k4v2"])
+    w.update(over)
+    return w
+
+
+def np_case(c):
+    g = lambda t: None if t is None else t.cpu().numpy()
+    k16 = g(c["k16"]).view(np.uint16)
+    v16 = None if c["v16"] is None else g(c["v16"]).view(np.uint16)
+    q = c["q"]
+    qn = q.view(torch.int16).numpy().view(np.uint16) if q.dtype == torch.bfloat16 else g(q)
+    return k16, v16, g(c["block_table"]), g(c["seq_lens"]), qn
+
+
+def quantized_pools(c):
+    lay = c["layout"]
+    k16, v16, bt, sl, q = np_case(c)
+    H, T, D = lay["H"], lay["T"], lay["D"]
+    kb = oracle.record_bytes(T, D, lay["k_bits"])
+    vb = oracle.record_bytes(T, D, lay["v_bits"])
+    nq = max(c["n_qpages"], 1)
+    krec = np.zeros((nq, H, kb), np.uint8)
+    vrec = np.zeros((nq, H, vb), np.uint8)
+    oracle.quantize_pages(lay, k16, v16, c["src"].numpy(), c["dst"].numpy(), krec, vrec)
+    return krec, vrec
+
+
+def sdpa_reference(Kf, Vf, q, sm):
+    """torch SDPA in float64 for one query over fp16 keys/values [L, D]."""
+    qt = torch.tensor(q, dtype=torch.float64).view(1, 1, 1, -1)
+    kt = torch.tensor(Kf, dtype=torch.float64).view(1, 1, *Kf.shape)
+    vt = torch.tensor(Vf, dtype=torch.float64).view(1, 1, *Vf.shape)
+    return torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, scale=sm).view(-1).numpy()
+
+
+def test_fp16_only_cache_matches_sdpa():
+    # L <= sink + tail: nothing is quantized, so decode is textbook attention.
+    w = small(sink=128, tail=1024, permute=True)
+    c = make_case(w, seq_lens=[700, 1, 129], batch=3)
+    assert c["n_qpages"] == 0
+    k16, v16, bt, sl, q = np_case(c)
+    out = oracle.decode(c["layout"], np.zeros(1, np.uint8), np.zeros(1, np.uint8), k16, v16,
+                        bt, sl, q, c["Hq"], c["sm_scale"])
+    T, D, G = 128, 128, 4
+    for b in range(3):
+        L = int(sl[b])
+        for h in (0, 5, 31):
+            g = h // G
+            ks = np.concatenate([k16[bt[b, p], g] for p in range(math.ceil(L / T))])[:L]
+            vs = np.concatenate([v16[bt[b, p], g] for p in range(math.ceil(L / T))])[:L]
+            ref = sdpa_reference(ks.view(np.float16).astype(np.float64),
+                                 vs.view(np.float16).astype(np.float64), q[b, h], c["sm_scale"])
+            assert np.allclose(out[b, h], ref, rtol=1e-12, atol=1e-12)
+
+
+def _readback(c, krec, vrec, b, g):
+    """Per-token read-back of sequence b, KV head g, via the record fields
+    (not via the oracle's decode)."""
+    lay = c["layout"]
+    T, D = lay["T"], lay["D"]
+    k16, v16, bt, sl, _ = np_case(c)
+    L = int(sl[b])
+    nq = max(0, (L - lay["sink"] - lay["tail"]) // T)
+    sp = lay["sink"] // T
+    K, V = [], []
+    for p in range(math.ceil(L / T)):
+        if sp <= p < sp + nq:
+            K.append(oracle.dequantize_record(krec[bt[b, p], g], T, D, lay["k_bits"]))
+            V.append(oracle.dequantize_record(vrec[bt[b, p], g], T, D, lay["v_bits"], True))
+        else:
+            K.append(k16[bt[b, p], g].view(np.float16).astype(np.float64))
+            V.append(v16[bt[b, p], g].view(np.float16).astype(np.float64))
+    return np.concatenate(K)[:L], np.concatenate(V)[:L]
+
+
+def test_quantized_cache_matches_sdpa_on_readback():
+    w = small(sink=128, tail=256, permute=True)
+    c = make_case(w, seq_lens=[1024, 777], batch=2)
+    krec, vrec = quantized_pools(c)
+    k16, v16, bt, sl, q = np_case(c)
+    out = oracle.decode(c["layout"], krec, vrec, k16, v16, bt, sl, q, c["Hq"], c["sm_scale"])
+    for b in range(2):
+        for h in (0, 7, 30):
+            K, V = _readback(c, krec, vrec, b, h // 4)
+            ref = sdpa_reference(K, V, q[b, h], c["sm_scale"])
+            assert np.allclose(out[b, h], ref, rtol=1e-11, atol=1e-12)
+
+
+def test_scale_folding_identity():
+    # <q, k_t> = S_t <qt, code_t> + Zp_t sum(qt), qt = (H q) * C
+    rng = np.random.default_rng(4)
+    T, D, b = 128, 128, 4
+    x = (rng.standard_normal((T, D)) * np.where(rng.random(D) < 0.03, 20, 1)).astype(np.float16)
+    rec, _, _, _ = oracle.quantize_record(x.view(np.uint16), b, 6)
+    codes, S, Z, C = oracle.split_record(rec, T, D, b)
+    q = rng.standard_normal(D)
+    K = oracle.dequantize_record(rec, T, D, b)
+    qt = (oracle.hadamard(D) @ q) * C
+    folded = S * (codes.astype(np.float64) @ qt) + Z * qt.sum()
+    assert np.allclose(K @ q, folded, rtol=1e-10, atol=1e-10)
+
+
+def test_special_cases():
+    w = small(sink=0, tail=0, permute=False)
+    c = make_case(w, seq_lens=[1024], batch=1)
+    krec, vrec = quantized_pools(c)
+    k16, v16, bt, sl, q = np_case(c)
+    K, V = _readback(c, krec, vrec, 0, 0)
+    lay = c["layout"]
+    # q = 0: uniform weights, the mean of the read-back values
+    out = oracle.decode(lay, krec, vrec, k16, v16, bt, sl, np.zeros_like(q), c["Hq"], 0.125)
+    assert np.allclose(out[0, 0], V.mean(axis=0), rtol=1e-11, atol=1e-12)
+    # L = 1: the first token's value; a one-token sequence has no whole
+    # record, so the token is read from its fp16 page
+    out = oracle.decode(lay, krec, vrec, k16, v16, bt, np.array([1], np.int32), q, c["Hq"], 0.125)
+    v0 = v16[bt[0, 0], 0, 0].view(np.float16).astype(np.float64)
+    assert np.array_equal(out[0, 0], v0)
+    # one dominating score: the output is that token's value.  The key of
+    # largest norm has the largest inner product with itself; scale q so the
+    # gap to every other score is 80 (weights of the rest below e^-80).
+    t = int(np.argmax((K * K).sum(1)))
+    dots = K @ K[t]
+    gap = dots[t] - np.max(np.delete(dots, t))
+    assert gap > 0
+    qq = q.copy()
+    qq[0, 0] = K[t] * (80.0 / gap)
+    out = oracle.decode(lay, krec, vrec, k16, v16, bt, sl, qq, c["Hq"], 1.0)
+    assert np.allclose(out[0, 0], V[t], rtol=1e-9, atol=1e-9)
+
+
+def test_page_placement_invariance_and_pairs():
+    base = small(sink=128, tail=128)
+    outs = []
+    for perm in (False, True):
+        c = make_case(dict(base, permute=perm), seq_lens=[900, 1024], batch=2)
+        krec, vrec = quantized_pools(c)
+        k16, v16, bt, sl, q = np_case(c)
+        outs.append(oracle.decode(c["layout"], krec, vrec, k16, v16, bt, sl, q, c["Hq"],
+                                  c["sm_scale"]))
+    assert np.array_equal(outs[0], outs[1])
+    pairs = np.array([[1, 3], [0, 31]], np.int32)
+    sub = oracle.decode(c["layout"], krec, vrec, k16, v16, bt, sl, q, c["Hq"], c["sm_scale"],
+                        pairs=pairs)
+    assert np.array_equal(sub[0], outs[1][1, 3]) and np.array_equal(sub[1], outs[1][0, 31])
+
+
+def test_mla_latent_serves_as_key_and_value():
+    w = dict(WORKLOADS["mla_d512_b32_32k_int4"])
+    w.update(L=384, sink=128, tail=0, Hq=4)
+    c = make_case(w, batch=1)
+    lay = c["layout"]
+    k16, _, bt, sl, q = np_case(c)
+    kb = oracle.record_bytes(128, 512, 4)
+    krec = np.zeros((c["n_qpages"], 1, kb), np.uint8)
+    oracle.quantize_pages(lay, k16, None, c["src"].numpy(), c["dst"].numpy(), krec, None)
+    out = oracle.decode(lay, krec, None, k16, None, bt, sl, q, 4, 1 / math.sqrt(512))
+    K = [k16[bt[0, 0], 0].view(np.float16).astype(np.float64)]
+    for p in (1, 2):
+        K.append(oracle.dequantize_record(krec[bt[0, p], 0], 128, 512, 4))
+    K = np.concatenate(K)
+    qd = torch.tensor(q.view(np.uint16).astype(np.int32) << 16).view(torch.float32).double()
+    for h in range(4):
+        ref = sdpa_reference(K, K, qd[0, h].numpy(), 1 / math.sqrt(512))
+        assert np.allclose(out[0, h], ref, rtol=1e-11, atol=1e-12)
