@@ -1,0 +1,180 @@
+/*
+ * kvarn.h -- C ABI of the KVarN (variance-normalized KV-cache quantization)
+ * hot path on AMD Instinct MI355X (gfx950).
+ *
+ * Two operations:
+ *   kvarn_quantize     turns full fp16 KV pages into KVarN records;
+ *   kvarn_decode_attn  one decode step of paged GQA or MLA attention that
+ *                      reads the records (and the fp16 sink and tail) directly.
+ *
+ * Method, as the pages describe it:
+ *   - evermx.com review "KVarN vLLM KV-cache quantization", method paragraph:
+ *     per fixed-size KV tile -- raw fp16 tile, orthonormal Hadamard rotation
+ *     across channels, iterative Sinkhorn-like column/row standard-deviation
+ *     normalization in log space, asymmetric round-to-nearest, scales folded
+ *     back in at read time; preset kvarn_k4v2_g128 (4-bit K, 2-bit V,
+ *     128-token tiles) and a 64-token-tile variant; MLA latent quantized to
+ *     int4 (paragraph on MLA and hybrid models).
+ *   - gmlx documentation "KV cache quantization", "The two schemes": each head
+ *     Hadamard-rotated; records of 128 tokens; the first 128 tokens and the
+ *     newest tail tokens (default 1024) stay fp16; widths 2..8.  "Which layers
+ *     quantize": only head dimensions 128, 256 and 512; a model that cannot
+ *     use the scheme is refused with a reason, never silently given another.
+ *
+ * Conventions of every entry point:
+ *   - Pointers marked "device" are HIP device memory; "host" are host memory.
+ *   - The library allocates and frees nothing, keeps no device state, and
+ *     never synchronizes: work is enqueued on `stream` (a hipStream_t; NULL is
+ *     the default stream) and runs asynchronously.  The caller owns every
+ *     buffer and keeps it alive until the stream has run the work.
+ *   - Arguments are validated on the host before anything is enqueued.  A
+ *     non-zero status means nothing was enqueued; kvarn_last_error() returns
+ *     a message (per calling thread) saying why.  Unsupported shapes return
+ *     KVARN_EUNSUPPORTED; there is no fallback path.
+ *   - Device-side page ids are range-checked by the kernels: an id outside
+ *     its pool makes the kernel skip that page (no out-of-bounds access); the
+ *     affected outputs are then unspecified.
+ *
+ * Record format (one quantized page x one KV head x K or V; the latent for
+ * MLA), all little-endian, record bytes = T*D*b/8 + 4*T + 2*D (a multiple of
+ * 16 for every supported shape):
+ *   [0, T*D*b/8)         codes, element e in bits [e*b, e*b+b), LSB first;
+ *                        K and the MLA latent token-major (e = t*D + j),
+ *                        V channel-major (e = j*T + t)
+ *   next 4*T bytes       per token t: fp16 scale S_t, then fp16 zero-point Zp_t
+ *   next 2*D bytes       per channel j: fp16 column scale C_j
+ * A stored value reads back, in the rotated basis, as
+ *   y_tj = C_j * (S_t * code_tj + Zp_t),  and in the original basis x_t = H y_t,
+ * with H the natural-order Sylvester Hadamard matrix scaled by 1/sqrt(D).
+ *
+ * Pools:
+ *   record pools  [n_qpages][H][record bytes]   (K and V separately)
+ *   fp16 pools    [n_fpages][H][T][D] fp16       (K and V separately)
+ *
+ * Regions of a sequence of L tokens (page p covers tokens [p*T, p*T+T)):
+ *   nq(L) = max(0, floor((L - sink - tail) / T)) quantized pages;
+ *   pages p < sink/T                   fp16 sink        (fp16 pool)
+ *   sink/T <= p < sink/T + nq(L)       quantized        (record pool)
+ *   later pages                        fp16 tail, which keeps between `tail`
+ *                                      and tail+T-1 tokens (fp16 pool)
+ */
+#ifndef KVARN_H
+#define KVARN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t kvarn_status;
+#define KVARN_OK 0
+#define KVARN_EINVAL 1          /* bad argument (null pointer, negative size, ...) */
+#define KVARN_EUNSUPPORTED 2    /* shape or width this library does not implement */
+#define KVARN_EWORKSPACE 3      /* workspace missing or smaller than required */
+#define KVARN_EHIP 4            /* the HIP runtime reported an error at launch */
+
+#define KVARN_F32 0             /* query dtypes */
+#define KVARN_F16 1
+#define KVARN_BF16 2
+
+/* Shape and policy of one layer's cache.  Value type, caller-owned. */
+typedef struct kvarn_layout {
+    int32_t head_dim;      /* D: 128, 256 or 512 (MLA latent: 512) ("Which layers quantize") */
+    int32_t tile_tokens;   /* T = page size: 128 (g128) or 64 (g64) */
+    int32_t k_bits;        /* key code width: 2, 4 or 6 (MLA latent: 4) */
+    int32_t v_bits;        /* value code width: 2, 4 or 6; ignored when mla = 1 */
+    int32_t n_iters;       /* normalization iterations (column step + row step), 1..32 */
+    int32_t sink_tokens;   /* first tokens kept fp16; a multiple of T (default 128) */
+    int32_t tail_tokens;   /* newest tokens kept fp16, >= 0 (default 1024) */
+    int32_t num_kv_heads;  /* H >= 1; 1 when mla = 1 */
+    int32_t mla;           /* 1: one latent record per token serves as key and value */
+} kvarn_layout;
+
+/* Device pools of one layer.  Caller-owned; all pointers 16-byte aligned. */
+typedef struct kvarn_cache {
+    void *k_records;       /* device, [n_qpages][H][kvarn_record_bytes(L, 0)] */
+    void *v_records;       /* device, [n_qpages][H][kvarn_record_bytes(L, 1)]; NULL if mla */
+    void *k_fp16;          /* device, fp16 [n_fpages][H][T][D] */
+    void *v_fp16;          /* device, fp16 [n_fpages][H][T][D]; NULL if mla */
+    int64_t n_qpages;      /* pages in each record pool */
+    int64_t n_fpages;      /* pages in each fp16 pool */
+} kvarn_cache;
+
+/* Page table of a decode batch.  Caller-owned device arrays. */
+typedef struct kvarn_page_table {
+    const int32_t *block_table;  /* device, [batch][max_pages]: logical page -> id in the
+                                    pool of that page's region (see "Regions" above) */
+    const int32_t *seq_lens;     /* device, [batch]: tokens per sequence, 0..max_pages*T */
+    int32_t batch;
+    int32_t max_pages;
+} kvarn_page_table;
+
+/* Fill *out from a preset name "kvarn_k<kb>v<vb>_g<T>" (e.g. "kvarn_k4v2_g128",
+ * "kvarn_k4v2_g64", "kvarn_k6v6_g128"), the flag names of the evermx.com
+ * review ("--kv-cache-dtype kvarn_k4v2_g128"), with n_iters = 6,
+ * sink_tokens = 128, tail_tokens = 1024 (gmlx "The two schemes"), mla = 0,
+ * and head_dim = num_kv_heads = 0 for the caller to set.  Host-only. */
+kvarn_status kvarn_parse_preset(const char *name, kvarn_layout *out);
+
+/* Check a layout; KVARN_OK or the status and message the operations would
+ * return for it.  Host-only. */
+kvarn_status kvarn_layout_check(const kvarn_layout *layout);
+
+/* Bytes of one record: which = 0 keys (or the MLA latent), 1 values.
+ * 0 for an invalid layout.  Host-only. */
+size_t kvarn_record_bytes(const kvarn_layout *layout, int32_t which);
+
+/* nq(L): quantized pages of a sequence of seq_len tokens (see "Regions").
+ * -1 for an invalid layout.  Host-only. */
+int32_t kvarn_quantized_pages(const kvarn_layout *layout, int32_t seq_len);
+
+/* Quantize n full pages: for i < n, the fp16 page src_fpages[i] (all H heads,
+ * keys and values -- or the latent) becomes record page dst_qpages[i] of the
+ * record pools.  Per tile of T tokens x D channels and head: rotation
+ * Y = X H, n_iters column/row normalization steps on Y (root-mean-square
+ * statistics), per-token round-to-nearest with scale = range/(2^b - 1) and
+ * zero-point = minimum, codes packed as in the record format.
+ * src_fpages, dst_qpages: device int32 [n].  The caller guarantees that the
+ * source pages are full and committed (the review: a block commits only once
+ * all its tokens are accepted) and that dst ids are distinct.  n = 0 is a
+ * no-op.  Reads cache->k_fp16/v_fp16, writes cache->k_records/v_records. */
+kvarn_status kvarn_quantize(const kvarn_layout *layout, const kvarn_cache *cache,
+                            const int32_t *src_fpages, const int32_t *dst_qpages,
+                            int32_t n, void *stream);
+
+/* Workspace bytes kvarn_decode_attn needs for this batch shape (split-K
+ * partial results).  0 for invalid arguments.  Host-only. */
+size_t kvarn_decode_workspace_bytes(const kvarn_layout *layout, int32_t batch,
+                                    int32_t num_q_heads, int32_t max_pages);
+
+/* One decode step: for every sequence b and query head h (KV head
+ * h / (num_q_heads / H); MLA: the one latent),
+ *   out[b][h] = sum_t softmax_t(sm_scale * <q[b][h], k_t>) v_t
+ * over the L = seq_lens[b] tokens, with k_t, v_t read back from the records
+ * (quantized region) or the fp16 pages (sink, tail).  The rotation is
+ * applied once to q and once (inverse) to the output, and the scales are
+ * folded into the score and value sums: no dequantized cache is written.
+ * q: device [batch][num_q_heads][D] of q_dtype (KVARN_F32 or KVARN_BF16).
+ * out: device fp32 [batch][num_q_heads][D], original basis; a sequence with
+ * L = 0 gives zeros.  workspace: device, at least
+ * kvarn_decode_workspace_bytes(...) bytes, 256-byte aligned; its contents
+ * need no initialisation and are clobbered.  num_q_heads must be a multiple
+ * of H (GQA group 4 here; MLA: 16..128 in multiples of 16). */
+kvarn_status kvarn_decode_attn(const kvarn_layout *layout, const kvarn_cache *cache,
+                               const kvarn_page_table *pages, const void *q, int32_t q_dtype,
+                               int32_t num_q_heads, float sm_scale, float *out,
+                               void *workspace, size_t workspace_bytes, void *stream);
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char *kvarn_last_error(void);
+
+/* Library version string. */
+const char *kvarn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVARN_H */

@@ -1,0 +1,236 @@
+// C ABI of the KVarN hot path: host-side validation and dispatch.
+// Nothing is enqueued unless every argument checks out; a failure returns a
+// status and leaves a message for kvarn_last_error() (gmlx "KV cache
+// quantization": a cache that cannot use the scheme is refused with a
+// reason, never given a different one).
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "kvarn.h"
+#include "kvarn_internal.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+kvarn_status fail(kvarn_status st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+kvarn_status ok() {
+    g_err[0] = 0;
+    return KVARN_OK;
+}
+
+bool width_ok(int b) { return b == 2 || b == 4 || b == 6; }
+
+kvarn_status check_layout(const kvarn_layout* L) {
+    if (!L) return fail(KVARN_EINVAL, "layout is NULL");
+    if (L->head_dim != 128 && L->head_dim != 256 && L->head_dim != 512)
+        return fail(KVARN_EUNSUPPORTED, "head_dim %d: the scheme accepts head dimensions 128, 256 and 512 only",
+                    L->head_dim);
+    if (L->tile_tokens != 128 && L->tile_tokens != 64)
+        return fail(KVARN_EUNSUPPORTED, "tile_tokens %d: supported tiles are 128 (g128) and 64 (g64)",
+                    L->tile_tokens);
+    if (L->mla != 0 && L->mla != 1) return fail(KVARN_EINVAL, "mla must be 0 or 1");
+    if (!width_ok(L->k_bits)) return fail(KVARN_EUNSUPPORTED, "k_bits %d: widths 2, 4 and 6 are implemented", L->k_bits);
+    if (L->mla) {
+        if (L->head_dim != 512) return fail(KVARN_EUNSUPPORTED, "mla: the latent width must be 512");
+        if (L->k_bits != 4) return fail(KVARN_EUNSUPPORTED, "mla: the latent is quantized to int4 (k_bits 4)");
+        if (L->num_kv_heads != 1) return fail(KVARN_EINVAL, "mla: num_kv_heads must be 1");
+    } else {
+        if (!width_ok(L->v_bits))
+            return fail(KVARN_EUNSUPPORTED, "v_bits %d: widths 2, 4 and 6 are implemented", L->v_bits);
+        if (L->num_kv_heads < 1) return fail(KVARN_EINVAL, "num_kv_heads %d must be >= 1", L->num_kv_heads);
+    }
+    if (L->n_iters < 1 || L->n_iters > 32) return fail(KVARN_EINVAL, "n_iters %d outside 1..32", L->n_iters);
+    if (L->sink_tokens < 0 || L->sink_tokens % L->tile_tokens != 0)
+        return fail(KVARN_EUNSUPPORTED, "sink_tokens %d must be a non-negative multiple of tile_tokens %d",
+                    L->sink_tokens, L->tile_tokens);
+    if (L->tail_tokens < 0) return fail(KVARN_EINVAL, "tail_tokens %d must be >= 0", L->tail_tokens);
+    return KVARN_OK;
+}
+
+size_t rec_bytes(const kvarn_layout* L, int bits) {
+    return (size_t)L->tile_tokens * L->head_dim * bits / 8 + 4 * (size_t)L->tile_tokens + 2 * (size_t)L->head_dim;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+kvarn_status kvarn_parse_preset(const char* name, kvarn_layout* out) {
+    if (!name || !out) return fail(KVARN_EINVAL, "NULL argument");
+    int kb = 0, vb = 0, t = 0;
+    char tail = 0;
+    if (sscanf(name, "kvarn_k%dv%d_g%d%c", &kb, &vb, &t, &tail) != 3)
+        return fail(KVARN_EINVAL, "preset '%s' is not of the form kvarn_k<bits>v<bits>_g<tokens>", name);
+    if (!width_ok(kb) || !width_ok(vb))
+        return fail(KVARN_EUNSUPPORTED, "preset '%s': widths 2, 4 and 6 are implemented", name);
+    if (t != 128 && t != 64) return fail(KVARN_EUNSUPPORTED, "preset '%s': tiles of 128 or 64 tokens", name);
+    memset(out, 0, sizeof(*out));
+    out->tile_tokens = t;
+    out->k_bits = kb;
+    out->v_bits = vb;
+    out->n_iters = 6;
+    out->sink_tokens = 128;
+    out->tail_tokens = 1024;
+    return ok();
+}
+
+kvarn_status kvarn_layout_check(const kvarn_layout* layout) {
+    kvarn_status st = check_layout(layout);
+    return st == KVARN_OK ? ok() : st;
+}
+
+size_t kvarn_record_bytes(const kvarn_layout* layout, int32_t which) {
+    if (check_layout(layout) != KVARN_OK) return 0;
+    if (which != 0 && which != 1) {
+        fail(KVARN_EINVAL, "which must be 0 (keys) or 1 (values)");
+        return 0;
+    }
+    if (which == 1 && layout->mla) {
+        fail(KVARN_EINVAL, "mla layouts have no value records");
+        return 0;
+    }
+    return rec_bytes(layout, which == 0 ? layout->k_bits : layout->v_bits);
+}
+
+int32_t kvarn_quantized_pages(const kvarn_layout* layout, int32_t seq_len) {
+    if (check_layout(layout) != KVARN_OK) return -1;
+    if (seq_len < 0) {
+        fail(KVARN_EINVAL, "seq_len %d < 0", seq_len);
+        return -1;
+    }
+    const int64_t r = (int64_t)seq_len - layout->sink_tokens - layout->tail_tokens;
+    return r >= layout->tile_tokens ? (int32_t)(r / layout->tile_tokens) : 0;
+}
+
+kvarn_status kvarn_quantize(const kvarn_layout* layout, const kvarn_cache* cache, const int32_t* src_fpages,
+                            const int32_t* dst_qpages, int32_t n, void* stream) {
+    kvarn_status st = check_layout(layout);
+    if (st != KVARN_OK) return st;
+    if (!cache) return fail(KVARN_EINVAL, "cache is NULL");
+    if (n < 0) return fail(KVARN_EINVAL, "n %d < 0", n);
+    if (n == 0) return ok();
+    if (!src_fpages || !dst_qpages) return fail(KVARN_EINVAL, "page lists are NULL");
+    if (!cache->k_fp16 || !cache->k_records) return fail(KVARN_EINVAL, "key pools are NULL");
+    if (!layout->mla && (!cache->v_fp16 || !cache->v_records)) return fail(KVARN_EINVAL, "value pools are NULL");
+    if (!aligned16(cache->k_fp16) || !aligned16(cache->k_records) ||
+        (!layout->mla && (!aligned16(cache->v_fp16) || !aligned16(cache->v_records))))
+        return fail(KVARN_EINVAL, "pools must be 16-byte aligned");
+    if (cache->n_fpages < 1 || cache->n_qpages < 1) return fail(KVARN_EINVAL, "empty pools");
+    if ((int64_t)n * layout->num_kv_heads > 0x7fffffffLL) return fail(KVARN_EINVAL, "too many pages in one call");
+    kvarn::QuantizeArgs a{};
+    a.D = layout->head_dim;
+    a.T = layout->tile_tokens;
+    a.k_bits = layout->k_bits;
+    a.v_bits = layout->v_bits;
+    a.n_iters = layout->n_iters;
+    a.H = layout->num_kv_heads;
+    a.mla = layout->mla;
+    a.k_fp16 = cache->k_fp16;
+    a.v_fp16 = cache->v_fp16;
+    a.k_records = cache->k_records;
+    a.v_records = cache->v_records;
+    a.src = src_fpages;
+    a.dst = dst_qpages;
+    a.n = n;
+    a.n_fpages = cache->n_fpages;
+    a.n_qpages = cache->n_qpages;
+    hipError_t e = kvarn::launch_quantize(a, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(KVARN_EHIP, "quantize launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+size_t kvarn_decode_workspace_bytes(const kvarn_layout* layout, int32_t batch, int32_t num_q_heads,
+                                    int32_t max_pages) {
+    if (check_layout(layout) != KVARN_OK) return 0;
+    if (batch < 1 || num_q_heads < 1 || max_pages < 1) {
+        fail(KVARN_EINVAL, "batch, num_q_heads and max_pages must be >= 1");
+        return 0;
+    }
+    int ns = 1, pps = 1;
+    const int H = layout->num_kv_heads;
+    kvarn::decode_plan(layout->head_dim, H, num_q_heads / (H > 0 ? H : 1), layout->mla, batch, max_pages,
+                       layout->tile_tokens, &ns, &pps);
+    return kvarn::decode_workspace_floats(layout->head_dim, num_q_heads, batch, ns) * sizeof(float);
+}
+
+kvarn_status kvarn_decode_attn(const kvarn_layout* layout, const kvarn_cache* cache, const kvarn_page_table* pages,
+                               const void* q, int32_t q_dtype, int32_t num_q_heads, float sm_scale, float* out,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+    kvarn_status st = check_layout(layout);
+    if (st != KVARN_OK) return st;
+    if (!cache || !pages || !q || !out) return fail(KVARN_EINVAL, "NULL argument");
+    if (q_dtype != KVARN_F32 && q_dtype != KVARN_BF16)
+        return fail(KVARN_EUNSUPPORTED, "q_dtype %d: float32 and bfloat16 queries are implemented", q_dtype);
+    if (pages->batch < 1 || pages->max_pages < 1 || !pages->block_table || !pages->seq_lens)
+        return fail(KVARN_EINVAL, "page table: batch and max_pages must be >= 1, arrays non-NULL");
+    const int H = layout->num_kv_heads;
+    if (num_q_heads < 1 || num_q_heads % H != 0)
+        return fail(KVARN_EINVAL, "num_q_heads %d is not a multiple of num_kv_heads %d", num_q_heads, H);
+    const int G = num_q_heads / H;
+    if (layout->mla) {
+        return fail(KVARN_EUNSUPPORTED, "mla decode is not built yet");
+    } else if (G != 4) {
+        return fail(KVARN_EUNSUPPORTED, "GQA group %d: this build implements groups of 4 query heads", G);
+    }
+    if (!cache->k_fp16 || (!layout->mla && !cache->v_fp16)) return fail(KVARN_EINVAL, "fp16 pools are NULL");
+    if (cache->n_qpages > 0 && (!cache->k_records || (!layout->mla && !cache->v_records)))
+        return fail(KVARN_EINVAL, "record pools are NULL");
+    if (!(sm_scale > 0.f) || sm_scale > 1e30f) return fail(KVARN_EINVAL, "sm_scale must be positive and finite");
+    int ns = 1, pps = 1;
+    kvarn::decode_plan(layout->head_dim, H, G, layout->mla, pages->batch, pages->max_pages, layout->tile_tokens,
+                       &ns, &pps);
+    const size_t need = kvarn::decode_workspace_floats(layout->head_dim, num_q_heads, pages->batch, ns) * sizeof(float);
+    if (!workspace || workspace_bytes < need)
+        return fail(KVARN_EWORKSPACE, "workspace of %zu bytes is smaller than the %zu bytes required",
+                    workspace ? workspace_bytes : (size_t)0, need);
+    if (((uintptr_t)workspace & 255u) != 0) return fail(KVARN_EINVAL, "workspace must be 256-byte aligned");
+    kvarn::DecodeArgs a{};
+    a.D = layout->head_dim;
+    a.T = layout->tile_tokens;
+    a.k_bits = layout->k_bits;
+    a.v_bits = layout->v_bits;
+    a.sink = layout->sink_tokens;
+    a.tail = layout->tail_tokens;
+    a.H = H;
+    a.mla = layout->mla;
+    a.G = G;
+    a.B = pages->batch;
+    a.Hq = num_q_heads;
+    a.max_pages = pages->max_pages;
+    a.nsplit = ns;
+    a.pps = pps;
+    a.k_records = cache->k_records;
+    a.v_records = cache->v_records;
+    a.k_fp16 = cache->k_fp16;
+    a.v_fp16 = cache->v_fp16;
+    a.n_qpages = cache->n_qpages;
+    a.n_fpages = cache->n_fpages;
+    a.block_table = pages->block_table;
+    a.seq_lens = pages->seq_lens;
+    a.q = q;
+    a.q_bf16 = q_dtype == KVARN_BF16;
+    a.sm_scale = sm_scale;
+    a.out = out;
+    a.ws = static_cast<float*>(workspace);
+    hipError_t e = kvarn::launch_decode(a, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(KVARN_EHIP, "decode launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+const char* kvarn_last_error(void) { return g_err; }
+
+const char* kvarn_version(void) { return "kvarn-mi355x 0.1"; }
+
+}  // extern "C"

@@ -1,0 +1,64 @@
+"""Comparison of HIP results with the oracle, under the path's parity bar:
+
+  codes      identical except for at most 1e-4 of the elements, each of which
+             may differ by +-1 only where the oracle's pre-round value lies
+             within 1e-3 of a rounding boundary (|frac(u) - 0.5| < 1e-3);
+  scales     C and S within 1e-3 relative; Zp within 1e-3 * max(|Zp|, S);
+  decode     per (sequence, query head): max_j |o - o_ref| <= 2e-3 * max_j |o_ref|,
+             with the oracle run on the HIP path's own records.
+"""
+import numpy as np
+
+import oracle
+
+CODE_FRAC = 1e-4
+BAND = 1e-3
+SCALE_RTOL = 1e-3
+DECODE_RTOL = 2e-3
+
+
+class CodeStats:
+    def __init__(self):
+        self.n = 0
+        self.diff = 0
+        self.bad = []
+
+    def frac(self):
+        return self.diff / max(self.n, 1)
+
+
+def compare_record(gpu_rec, x16, T, D, bits, n_iters, channel_major, stats, where=""):
+    """Quantize the fp16 tile x16 with the oracle and compare with gpu_rec."""
+    ref, u, _, _ = oracle.quantize_record(x16, bits, n_iters, channel_major=channel_major)
+    gc, gS, gZ, gC = oracle.split_record(gpu_rec, T, D, bits, channel_major)
+    rc, rS, rZ, rC = oracle.split_record(ref, T, D, bits, channel_major)
+    assert np.all(np.abs(gC - rC) <= SCALE_RTOL * np.abs(rC)), f"{where}: column scales"
+    assert np.all(np.abs(gS - rS) <= SCALE_RTOL * np.abs(rS)), f"{where}: token scales"
+    assert np.all(np.abs(gZ - rZ) <= SCALE_RTOL * np.maximum(np.abs(rZ), rS)), f"{where}: zero-points"
+    d = gc.astype(np.int32) - rc.astype(np.int32)
+    nz = d != 0
+    stats.n += d.size
+    stats.diff += int(nz.sum())
+    if nz.any():
+        near = np.abs(np.abs(u - np.floor(u)) - 0.5) < BAND
+        ok = (np.abs(d) <= 1) & near
+        if not np.all(ok[nz]):
+            idx = np.argwhere(nz & ~ok)[:5]
+            stats.bad.append((where, idx.tolist(), [float(u[tuple(i)]) for i in idx],
+                              [int(gc[tuple(i)]) for i in idx], [int(rc[tuple(i)]) for i in idx]))
+    return ref
+
+
+def assert_code_stats(stats):
+    assert not stats.bad, f"codes differ away from a rounding boundary: {stats.bad[:3]}"
+    assert stats.frac() <= CODE_FRAC, f"{stats.diff} of {stats.n} codes differ ({stats.frac():.2e})"
+
+
+def decode_rel_err(out, ref):
+    """max over rows of max|out - ref| / max|ref| (rows = (b, h))."""
+    out = np.asarray(out, np.float64).reshape(-1, out.shape[-1])
+    ref = np.asarray(ref, np.float64).reshape(-1, ref.shape[-1])
+    den = np.abs(ref).max(axis=1)
+    num = np.abs(out - ref).max(axis=1)
+    rel = np.where(den > 0, num / np.where(den > 0, den, 1), num)
+    return float(rel.max()), int(rel.argmax())

@@ -1,0 +1,131 @@
+"""GPU parity of kvarn_quantize (HIP, through the C ABI) against the oracle.
+
+Full comparison on the one-layer case and on small cases of every shape;
+sampled records at the full sizes of the benchmark workloads, quantized in
+the same launch configuration the benchmark times.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import device, gpu_case, host_u16, run_quantize, say, workload
+from parity_util import CodeStats, assert_code_stats, compare_record
+
+pytestmark = pytest.mark.gpu
+
+
+def check_records(case, krec, vrec, idx, heads=None):
+    lay = case["layout"]
+    T, D, H = lay["T"], lay["D"], lay["H"]
+    src = case["src"].cpu().numpy()
+    dst = case["dst"].cpu().numpy()
+    k16 = case["k16"]
+    v16 = case["v16"]
+    stats = CodeStats()
+    kr = krec.cpu().numpy()
+    vr = None if vrec is None else vrec.cpu().numpy()
+    for i in idx:
+        sp, dp = int(src[i]), int(dst[i])
+        hs = range(H) if heads is None else heads
+        kt = host_u16(k16[sp])
+        vt = None if v16 is None else host_u16(v16[sp])
+        for h in hs:
+            compare_record(kr[dp, h], kt[h], T, D, lay["k_bits"], lay["n_iters"], False, stats,
+                           f"K page {i} head {h}")
+            if vr is not None:
+                compare_record(vr[dp, h], vt[h], T, D, lay["v_bits"], lay["n_iters"], True, stats,
+                               f"V page {i} head {h}")
+    assert_code_stats(stats)
+    return stats
+
+
+def test_quantize_one_layer_all_records():
+    case = gpu_case(workload("tiny_d128_k4v2"))
+    say("quantize tiny_d128_k4v2", case["n_qpages"], "pages")
+    L, krec, vrec = run_quantize(case)
+    st = check_records(case, krec, vrec, range(case["n_qpages"]))
+    say("codes differing:", st.diff, "of", st.n)
+
+
+SHAPES = [
+    # D, T, k_bits, v_bits, mla, dist
+    (128, 128, 4, 2, 0, "normal"),
+    (128, 64, 4, 2, 0, "normal"),
+    (128, 128, 6, 6, 0, "t3"),
+    (128, 128, 2, 4, 0, "t3"),
+    (256, 128, 6, 6, 0, "t3"),
+    (256, 64, 4, 6, 0, "normal"),
+    (512, 128, 6, 6, 0, "t3"),
+    (512, 64, 2, 2, 0, "normal"),
+    (512, 128, 4, 4, 1, "normal"),
+]
+
+
+@pytest.mark.parametrize("D,T,kb,vb,mla,dist", SHAPES)
+def test_quantize_shapes(D, T, kb, vb, mla, dist):
+    w = workload("tiny_d128_k4v2", D=D, T=T, k_bits=kb, v_bits=vb, mla=mla, H=1 if mla else 2,
+                 Hq=16 if mla else 8, L=3 * T, dist=dist, outliers=None if mla else ("per_head", 4),
+                 permute=True, seed=0x2000 + D + T + kb)
+    case = gpu_case(w, batch=2)
+    say("quantize shape", D, T, kb, vb, mla, dist)
+    L, krec, vrec = run_quantize(case)
+    check_records(case, krec, vrec, range(case["n_qpages"]))
+
+
+FULL = ["dense8b_b16_32k_k4v2_g128", "dense8b_b64_16k_k4v2_g64", "wide_d256_b8_64k_k6v6",
+        "wide_d512_b8_64k_k6v6", "mla_d512_b32_32k_int4"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_quantize_full_size_sampled(name):
+    case = gpu_case(workload(name))
+    say("quantize full", name, case["n_qpages"], "pages")
+    L, krec, vrec = run_quantize(case)
+    rng = np.random.default_rng(7)
+    idx = rng.choice(case["n_qpages"], 6, replace=False)
+    H = case["layout"]["H"]
+    heads = sorted(set(rng.integers(0, H, 2).tolist()))
+    check_records(case, krec, vrec, idx, heads)
+    # last page too (end of the pool)
+    check_records(case, krec, vrec, [case["n_qpages"] - 1], [H - 1])
+
+
+def test_quantize_deterministic_and_scale_equivariant():
+    w = workload("tiny_d128_k4v2", L=512)
+    case = gpu_case(w)
+    L, k1, v1 = run_quantize(case)
+    L, k2, v2 = run_quantize(case)
+    assert torch.equal(k1, k2) and torch.equal(v1, v2)
+    # x -> 2x: codes, S and Zp unchanged, C doubled (bit-exact)
+    case2 = dict(case)
+    case2["k16"] = case["k16"] * 2
+    case2["v16"] = case["v16"] * 2
+    L, k3, v3 = run_quantize(case2)
+    T, D = 128, 128
+    for a, b, bits in ((k1, k3, 4), (v1, v3, 2)):
+        cb = T * D * bits // 8
+        assert torch.equal(a[..., :cb + 4 * T], b[..., :cb + 4 * T])
+        ca = a[..., cb + 4 * T:].contiguous().view(torch.float16).float()
+        cc = b[..., cb + 4 * T:].contiguous().view(torch.float16).float()
+        assert torch.equal(ca * 2, cc)
+
+
+def test_quantize_zero_tile_and_invalid_ids():
+    w = workload("tiny_d128_k4v2", L=256, H=1, Hq=4)
+    case = gpu_case(w)
+    case["k16"].zero_()
+    L, krec, vrec = run_quantize(case)
+    T, D = 128, 128
+    cb = T * D * 4 // 8
+    rec = krec[0, 0]
+    assert int(rec[:cb + 4 * T].abs().sum()) == 0
+    C = rec[cb + 4 * T:].contiguous().view(torch.float16).float()
+    assert torch.all(C == 1.0)
+    # out-of-range page ids are skipped by the kernel: the records stay as they were
+    import kv_cache_quantization_kvarn_amd as kv
+    before = krec.clone()
+    bad_src = torch.tensor([10 ** 6, 0], dtype=torch.int32, device=device())
+    bad_dst = torch.tensor([0, -1], dtype=torch.int32, device=device())
+    kv.quantize(L, case["k16"], case["v16"], krec, vrec, bad_src, bad_dst)
+    torch.cuda.synchronize()
+    assert torch.equal(before, krec)
