@@ -7,8 +7,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkvarn.so")
-SOURCES = ["api.cpp", "quantize.hip", "decode_gqa.hip"]
-HEADERS = ["kvarn_device.hpp", "kvarn_internal.hpp"]
+SOURCES = ["api.cpp", "quantize.hip", "quantize_d128.hip", "quantize_d256.hip", "quantize_d512.hip",
+           "decode_gqa.hip"]
+HEADERS = ["kvarn_device.hpp", "kvarn_internal.hpp", "quantize_impl.hpp"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
@@ -22,7 +23,7 @@ def sources():
     return [os.path.join(CSRC, s) for s in SOURCES]
 
 
-def build(jobs: int = 4) -> str:
+def build() -> str:
     """Compile every source to an object in parallel, then link."""
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     objdir = os.path.join(ROOT, "_build")

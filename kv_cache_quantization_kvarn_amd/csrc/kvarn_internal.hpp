@@ -21,6 +21,11 @@ struct QuantizeArgs {
 
 hipError_t launch_quantize(const QuantizeArgs& a, hipStream_t st);
 
+// One kernel launch for keys and values (HASV) or the MLA latent alone;
+// explicitly instantiated per head_dim in quantize_d<D>.hip.
+template <int D, int T, int KB, int VB, bool HASV>
+hipError_t launch_quantize_shape(const QuantizeArgs& a, hipStream_t st);
+
 struct DecodeArgs {
     int D, T, k_bits, v_bits, sink, tail, H, mla;
     int G;            // query heads per KV head (MLA: all query heads)
