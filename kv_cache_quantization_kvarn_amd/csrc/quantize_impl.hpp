@@ -33,50 +33,112 @@ namespace {
 
 constexpr int QC = 16;  // channels per lane
 constexpr int QR = 4;   // rows per lane
+// x + kMagic (1.5 * 2^23) rounds x half-to-even to an integer kept in the low
+// mantissa bits, for -0.5 <= x < 2^22; bits 22 and up hold the constant.
+constexpr float kMagic = 12582912.0f;
 
 // lane bit carrying channel-group bit k
 __device__ __forceinline__ constexpr int cg_lane_bit(int k) {
     return k == 0 ? 0 : k == 1 ? 1 : k == 2 ? 3 : k == 3 ? 2 : 4;
 }
 
+// v + v[lane ^ (1 << BIT)]: one fused v_add_f32_dpp for bits 0, 1, 3.
 template <int BIT>
-__device__ __forceinline__ float butterfly(float v, int lane) {
-    // lower lane (bit clear): v + partner; upper lane: partner - v
-    const float p = xor_lane<BIT>(v);
-    return ((lane >> BIT) & 1) ? (p - v) : (v + p);
+__device__ __forceinline__ float xsum(float v) {
+    if constexpr (BIT == 0) return v + i2f(__builtin_amdgcn_update_dpp(0, f2i(v), 0xB1, 0xF, 0xF, true));
+    else if constexpr (BIT == 1) return v + i2f(__builtin_amdgcn_update_dpp(0, f2i(v), 0x4E, 0xF, 0xF, true));
+    else if constexpr (BIT == 3) return v + i2f(__builtin_amdgcn_update_dpp(0, f2i(v), 0x128, 0xF, 0xF, true));
+    else return v + xor_lane<BIT>(v);
 }
 
 template <int CGB>
 __device__ __forceinline__ float row_sum(float v) {
-    v += xor_lane<0>(v);
-    v += xor_lane<1>(v);
-    v += xor_lane<3>(v);
-    if constexpr (CGB >= 4) v += xor_lane<2>(v);
-    if constexpr (CGB >= 5) v += xor_lane<4>(v);
+    v = xsum<0>(v);
+    v = xsum<1>(v);
+    v = xsum<3>(v);
+    if constexpr (CGB >= 4) v = xsum<2>(v);
+    if constexpr (CGB >= 5) v = xsum<4>(v);
     return v;
 }
 
 template <int CGB>
-__device__ __forceinline__ float row_min(float v) {
-    v = fminf(v, xor_lane<0>(v));
-    v = fminf(v, xor_lane<1>(v));
-    v = fminf(v, xor_lane<3>(v));
-    if constexpr (CGB >= 4) v = fminf(v, xor_lane<2>(v));
-    if constexpr (CGB >= 5) v = fminf(v, xor_lane<4>(v));
-    return v;
+__device__ __forceinline__ void row_minmax(float& mn, float& mx) {
+    mn = fminf(mn, xor_lane<0>(mn)); mx = fmaxf(mx, xor_lane<0>(mx));
+    mn = fminf(mn, xor_lane<1>(mn)); mx = fmaxf(mx, xor_lane<1>(mx));
+    mn = fminf(mn, xor_lane<3>(mn)); mx = fmaxf(mx, xor_lane<3>(mx));
+    if constexpr (CGB >= 4) { mn = fminf(mn, xor_lane<2>(mn)); mx = fmaxf(mx, xor_lane<2>(mx)); }
+    if constexpr (CGB >= 5) { mn = fminf(mn, xor_lane<4>(mn)); mx = fmaxf(mx, xor_lane<4>(mx)); }
 }
 
-template <int CGB>
-__device__ __forceinline__ float row_max(float v) {
-    v = fmaxf(v, xor_lane<0>(v));
-    v = fmaxf(v, xor_lane<1>(v));
-    v = fmaxf(v, xor_lane<3>(v));
-    if constexpr (CGB >= 4) v = fmaxf(v, xor_lane<2>(v));
-    if constexpr (CGB >= 5) v = fmaxf(v, xor_lane<4>(v));
-    return v;
+// Cross-lane butterfly on lane bit BIT for 16 values: v <- v + s * partner,
+// s = +1 where the bit is clear and -1 where it is set, i.e. (l, u) ->
+// (l + u, u - l).  The upper output is the negated butterfly difference;
+// the negations commute with the other stages and leave every channel
+// multiplied by (-1)^(number of its cross-lane bits), undone at the end.
+// Bits 0, 1, 3: one v_fmac_f32_dpp each.
+#define KVARN_FMAC_DPP8(CTRL)                                                                   \
+    asm volatile("s_nop 1\n\t"                                                                   \
+                 "v_fmac_f32_dpp %0, %0, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"             \
+                 "v_fmac_f32_dpp %1, %1, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"             \
+                 "v_fmac_f32_dpp %2, %2, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"             \
+                 "v_fmac_f32_dpp %3, %3, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"             \
+                 "v_fmac_f32_dpp %4, %4, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"             \
+                 "v_fmac_f32_dpp %5, %5, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"             \
+                 "v_fmac_f32_dpp %6, %6, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"             \
+                 "v_fmac_f32_dpp %7, %7, %8 " CTRL " row_mask:0xf bank_mask:0xf"                 \
+                 : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]),       \
+                   "+v"(v[6]), "+v"(v[7])                                                         \
+                 : "v"(s))
+
+template <int BIT>
+__device__ __forceinline__ void xbutterfly8(float* v, float s) {
+    if constexpr (BIT == 0) {
+        KVARN_FMAC_DPP8("quad_perm:[1,0,3,2]");
+    } else if constexpr (BIT == 1) {
+        KVARN_FMAC_DPP8("quad_perm:[2,3,0,1]");
+    } else if constexpr (BIT == 3) {
+        KVARN_FMAC_DPP8("row_ror:8");
+    } else {
+#pragma unroll
+        for (int k = 0; k < 8; k++) v[k] = fmaf(xor_lane<BIT>(v[k]), s, v[k]);
+    }
+}
+
+template <int BIT>
+__device__ __forceinline__ void xbutterfly(float (&y)[QR][QC], int lane) {
+    const float s = ((lane >> BIT) & 1) ? -1.f : 1.f;
+#pragma unroll
+    for (int r = 0; r < QR; r++) {
+        xbutterfly8<BIT>(&y[r][0], s);
+        xbutterfly8<BIT>(&y[r][8], s);
+    }
 }
 
 __device__ __forceinline__ bool usable(float s) { return s > 0.f && s <= 3.0e38f; }
+
+__device__ __forceinline__ uint32_t fbits(float x) { return __builtin_bit_cast(uint32_t, x); }
+
+// Codes sit in the low bits of magic-rounded floats (junk from bit 22 up).
+// Pack n consecutive codes of width B into the low n*B bits; n*B <= 16 keeps
+// the junk of every addend above the result.
+template <int B>
+__device__ __forceinline__ uint32_t pack2(uint32_t f0, uint32_t f1) {  // low 2B bits clean
+    return (f1 << B) + f0;
+}
+
+__device__ __forceinline__ uint32_t bytes4(uint32_t b0, uint32_t b1, uint32_t b2, uint32_t b3) {
+    // byte 0 of each argument -> one dword
+    const uint32_t lo = __builtin_amdgcn_perm(b1, b0, 0x0c0c0400u);
+    const uint32_t hi = __builtin_amdgcn_perm(b3, b2, 0x0c0c0400u);
+    return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+}
+
+// 4 codes of 6 bits -> low 24 bits (clean above).
+__device__ __forceinline__ uint32_t pack6x4(uint32_t f0, uint32_t f1, uint32_t f2, uint32_t f3) {
+    const uint32_t x01 = ((f1 << 6) + f0) & 0xfffu;
+    const uint32_t x23 = (f3 << 6) + f2;   // bits 12..27 zero, junk from 28
+    return (x23 << 12) | x01;              // junk shifted out
+}
 
 template <int D, int T>
 struct TileShape {
@@ -87,15 +149,15 @@ struct TileShape {
     static constexpr int NW = T / RPW;                        // waves per workgroup
     static constexpr int NT = NW * 64;
     static constexpr int NSUB = (RGB == 3) ? 2 : 1;           // lane bit 2 left after the swaps
-    static constexpr int SMEM_CODES = T * D;
+    static constexpr int SMEM_CODES = T * D;                  // one byte per code at most
     static constexpr int SMEM_PART = NW * NSUB * D * 4;
     static constexpr int SMEM = SMEM_CODES > SMEM_PART ? SMEM_CODES : SMEM_PART;
 };
 
-// One tile -> one record.  smem: TileShape::SMEM bytes; bvec: D floats.
+// One tile -> one record.  smem: TileShape::SMEM bytes; vec: 3*D floats.
 template <int D, int T, int BITS, bool CHMAJOR>
 __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ tile, uint8_t* __restrict__ rec,
-                                              uint8_t* smem, float* bvec, int32_t n_iters) {
+                                              uint8_t* smem, float* vec, int32_t n_iters) {
     using S = TileShape<D, T>;
     constexpr int CGB = S::CGB, RGB = S::RGB, RPW = S::RPW, NW = S::NW, NT = S::NT, NSUB = S::NSUB;
     constexpr int QMAX = (1 << BITS) - 1;
@@ -107,6 +169,9 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ tile,
     static_assert(REC % 16 == 0, "records stay 16-byte aligned");
 
     float* colpart = reinterpret_cast<float*>(smem);
+    float* bvec = vec;           // b_j = exp(-2 lc_j), unnormalized basis
+    float* icvec = vec + D;      // (+-1 per channel) * sqrt(b_j): multiplies y into W
+    uint16_t* cvec = reinterpret_cast<uint16_t*>(vec + 2 * D);  // fp16 column scales
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -150,17 +215,12 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ tile,
                 }
             }
         }
-#pragma unroll
-        for (int c = 0; c < QC; c++) {
-            float v = y[r][c];
-            v = butterfly<0>(v, lane);
-            v = butterfly<1>(v, lane);
-            v = butterfly<3>(v, lane);
-            if constexpr (CGB >= 4) v = butterfly<2>(v, lane);
-            if constexpr (CGB >= 5) v = butterfly<4>(v, lane);
-            y[r][c] = v;
-        }
     }
+    xbutterfly<0>(y, lane);
+    xbutterfly<1>(y, lane);
+    xbutterfly<3>(y, lane);
+    if constexpr (CGB >= 4) xbutterfly<2>(y, lane);
+    if constexpr (CGB >= 5) xbutterfly<4>(y, lane);
 
     // ---- stage 3: normalization iterations on A = y^2 ----------------------
     float A[QR][QC];
@@ -176,6 +236,7 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ tile,
     float aw[QR] = {1.f, 1.f, 1.f, 1.f};
     float bw[QC];
     for (int it = 0; it < n_iters; it++) {
+        const bool last = it == n_iters - 1;
         // column step: partial sums over this lane's rows
         float p[QC];
 #pragma unroll
@@ -214,9 +275,18 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ tile,
             float s = 0.f;
 #pragma unroll
             for (int w = 0; w < NW * NSUB; w++) s += colpart[w * D + tid];
-            if (usable(s)) bvec[tid] = (float)T / s;
+            float b = bvec[tid];
+            if (usable(s)) b = (float)T * __builtin_amdgcn_rcpf(s);
+            bvec[tid] = b;
+            if (last) {
+                // channel sign left by the sign-tracked butterflies: (-1)^popcount(j >> 4)
+                const float sg = (__builtin_popcount((unsigned)tid >> 4) & 1) ? -1.f : 1.f;
+                icvec[tid] = sg * sqrtf(b);
+                cvec[tid] = (uint16_t)float_to_half_bits(__builtin_amdgcn_rsqf((float)D * b));
+            }
         }
         __syncthreads();
+        if (last) break;
 #pragma unroll
         for (int c4 = 0; c4 < QC / 4; c4++) {
             float4 v = *reinterpret_cast<const float4*>(bvec + ch0 + 4 * c4);
@@ -225,7 +295,6 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ tile,
             bw[4 * c4 + 2] = v.z;
             bw[4 * c4 + 3] = v.w;
         }
-        if (it == n_iters - 1) break;
         // row step
 #pragma unroll
         for (int r = 0; r < QR; r++) {
@@ -233,17 +302,23 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ tile,
 #pragma unroll
             for (int c = 1; c < QC; c++) s = fmaf(A[r][c], bw[c], s);
             s = row_sum<CGB>(s);
-            if (usable(s)) aw[r] = (float)D / s;
+            if (usable(s)) aw[r] = (float)D * __builtin_amdgcn_rcpf(s);
         }
     }
 
-    // ---- stage 4: per-token asymmetric round-to-nearest --------------------
+    // ---- stage 4: per-token asymmetric round-to-nearest, packed in LDS ------
     float ic[QC];
 #pragma unroll
-    for (int c = 0; c < QC; c++) ic[c] = sqrtf(bw[c]);  // 1 / c_j (unnormalized basis)
+    for (int c4 = 0; c4 < QC / 4; c4++) {
+        float4 v = *reinterpret_cast<const float4*>(icvec + ch0 + 4 * c4);
+        ic[4 * c4 + 0] = v.x;
+        ic[4 * c4 + 1] = v.y;
+        ic[4 * c4 + 2] = v.z;
+        ic[4 * c4 + 3] = v.w;
+    }
+    uint8_t* img = smem;  // image of the record's code block
     uint32_t sz[QR];
-    uint8_t* codes = smem;  // [record element order], one byte per code
-    uint32_t cw[QR][QC / 4];
+    uint32_t fq[QR][QC];  // magic-rounded codes
 #pragma unroll
     for (int r = 0; r < QR; r++) {
         float W[QC];
@@ -264,85 +339,85 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ tile,
             mn = fminf(mn, W[c]);
             mx = fmaxf(mx, W[c]);
         }
-        mn = row_min<CGB>(mn);
-        mx = row_max<CGB>(mx);
+        row_minmax<CGB>(mn, mx);
+        mn += 0.0f;  // a zero row stores +0, not the -0 of a sign-flipped channel
         const float range = mx - mn;
-        const float s = range / (float)QMAX;
-        const float inv = range > 0.f ? (float)QMAX / range : 0.f;
+        const float s = range * (1.0f / (float)QMAX);
+        const float inv = range > 0.f ? (float)QMAX * __builtin_amdgcn_rcpf(range) : 0.f;
+        const float nb = -mn * inv;
         sz[r] = float_to_half_bits(s) | (float_to_half_bits(mn) << 16);
 #pragma unroll
-        for (int c4 = 0; c4 < QC / 4; c4++) {
-            uint32_t word = 0;
-#pragma unroll
-            for (int k = 0; k < 4; k++) {
-                float u = (W[4 * c4 + k] - mn) * inv;
-                float qf = fminf(fmaxf(rintf(u), 0.f), (float)QMAX);
-                word |= (uint32_t)qf << (8 * k);
-            }
-            cw[r][c4] = word;
-        }
+        for (int c = 0; c < QC; c++) fq[r][c] = fbits(fmaf(W[c], inv, nb) + kMagic);
     }
-    // all statistics reads of the shared buffer are behind the last barrier;
-    // the code bytes reuse it
+    // the statistics are done with the shared buffer (last barrier above);
+    // the record's code image reuses it
     if constexpr (!CHMAJOR) {
+        // token-major: this lane's 16 codes of a row are contiguous
 #pragma unroll
         for (int r = 0; r < QR; r++) {
-            uint4 v = make_uint4(cw[r][0], cw[r][1], cw[r][2], cw[r][3]);
-            *reinterpret_cast<uint4*>(codes + (row0 + r) * D + ch0) = v;
+            const uint32_t* f = fq[r];
+            uint8_t* dstp = img + ((row0 + r) * D + ch0) * BITS / 8;
+            if constexpr (BITS == 4) {
+                uint32_t pr[8];
+#pragma unroll
+                for (int k = 0; k < 8; k++) pr[k] = pack2<4>(f[2 * k], f[2 * k + 1]);
+                uint2 v = make_uint2(bytes4(pr[0], pr[1], pr[2], pr[3]), bytes4(pr[4], pr[5], pr[6], pr[7]));
+                *reinterpret_cast<uint2*>(dstp) = v;
+            } else if constexpr (BITS == 2) {
+                uint32_t qd[4];
+#pragma unroll
+                for (int k = 0; k < 4; k++)
+                    qd[k] = (pack2<2>(f[4 * k + 2], f[4 * k + 3]) << 4) + pack2<2>(f[4 * k], f[4 * k + 1]);
+                *reinterpret_cast<uint32_t*>(dstp) = bytes4(qd[0], qd[1], qd[2], qd[3]);
+            } else {
+                uint32_t g[4];
+#pragma unroll
+                for (int k = 0; k < 4; k++) g[k] = pack6x4(f[4 * k], f[4 * k + 1], f[4 * k + 2], f[4 * k + 3]);
+                uint32_t* d32 = reinterpret_cast<uint32_t*>(dstp);
+                d32[0] = g[0] | (g[1] << 24);
+                d32[1] = (g[1] >> 8) | (g[2] << 16);
+                d32[2] = (g[2] >> 16) | (g[3] << 8);
+            }
         }
     } else {
+        // channel-major: this lane's 4 tokens of a channel are contiguous
 #pragma unroll
         for (int c = 0; c < QC; c++) {
-            uint32_t v = 0;
-#pragma unroll
-            for (int r = 0; r < QR; r++) v |= ((cw[r][c >> 2] >> (8 * (c & 3))) & 0xffu) << (8 * r);
-            *reinterpret_cast<uint32_t*>(codes + (ch0 + c) * T + row0) = v;
+            const int e0 = (ch0 + c) * T + row0;  // element index of the first of 4 codes
+            if constexpr (BITS == 2) {
+                const uint32_t v = (pack2<2>(fq[2][c], fq[3][c]) << 4) + pack2<2>(fq[0][c], fq[1][c]);
+                img[e0 / 4] = (uint8_t)v;
+            } else if constexpr (BITS == 4) {
+                const uint32_t v = __builtin_amdgcn_perm(pack2<4>(fq[2][c], fq[3][c]),
+                                                         pack2<4>(fq[0][c], fq[1][c]), 0x0c0c0400u);
+                *reinterpret_cast<uint16_t*>(img + e0 / 2) = (uint16_t)v;
+            } else {
+                const uint32_t v = pack6x4(fq[0][c], fq[1][c], fq[2][c], fq[3][c]);
+                uint8_t* d8 = img + e0 * 6 / 8;
+                d8[0] = (uint8_t)v;
+                d8[1] = (uint8_t)(v >> 8);
+                d8[2] = (uint8_t)(v >> 16);
+            }
         }
     }
     // per-token scale and zero-point: 4 consecutive tokens = 16 bytes
     if (cg == 0) {
         *reinterpret_cast<uint4*>(rec + CODE_BYTES + 4 * row0) = make_uint4(sz[0], sz[1], sz[2], sz[3]);
     }
-    // column scales, normalized basis: C_j = 1 / sqrt(D * b_j)
+    // column scales, normalized basis
     if (tid < D / 8) {
-        uint32_t w[4];
-#pragma unroll
-        for (int k = 0; k < 4; k++) {
-            float c0 = 1.0f / sqrtf((float)D * bvec[8 * tid + 2 * k]);
-            float c1 = 1.0f / sqrtf((float)D * bvec[8 * tid + 2 * k + 1]);
-            w[k] = float_to_half_bits(c0) | (float_to_half_bits(c1) << 16);
-        }
-        *reinterpret_cast<uint4*>(rec + CODE_BYTES + 4 * T + 16 * tid) = make_uint4(w[0], w[1], w[2], w[3]);
+        *reinterpret_cast<uint4*>(rec + CODE_BYTES + 4 * T + 16 * tid) =
+            *reinterpret_cast<const uint4*>(cvec + 8 * tid);
     }
     __syncthreads();
 
-    // ---- stage 5: pack 64 codes per thread, LSB first -----------------------
+    // ---- stage 5: the code image leaves in 16-byte stores -------------------
     {
-        const uint4* cp = reinterpret_cast<const uint4*>(codes + 64 * tid);
-        uint32_t in[16];
+        constexpr int PER = CODE_BYTES / NT;   // 8 * BITS bytes per thread
+        const uint4* src4 = reinterpret_cast<const uint4*>(img + tid * PER);
+        uint4* dst4 = reinterpret_cast<uint4*>(rec + (int64_t)tid * PER);
 #pragma unroll
-        for (int k = 0; k < 4; k++) {
-            uint4 v = cp[k];
-            in[4 * k] = v.x;
-            in[4 * k + 1] = v.y;
-            in[4 * k + 2] = v.z;
-            in[4 * k + 3] = v.w;
-        }
-        constexpr int NOUT = 2 * BITS;  // dwords for 64 codes
-        uint32_t out[NOUT];
-#pragma unroll
-        for (int k = 0; k < NOUT; k++) out[k] = 0;
-#pragma unroll
-        for (int k = 0; k < 64; k++) {
-            const uint32_t code = (in[k >> 2] >> (8 * (k & 3))) & 0xffu;
-            const int bit = k * BITS;
-            const int wd = bit >> 5, off = bit & 31;
-            out[wd] |= code << off;
-            if (off + BITS > 32) out[wd + 1] |= code >> (32 - off);
-        }
-        uint4* op = reinterpret_cast<uint4*>(rec + (int64_t)tid * NOUT * 4);
-#pragma unroll
-        for (int k = 0; k < NOUT / 4; k++) op[k] = make_uint4(out[4 * k], out[4 * k + 1], out[4 * k + 2], out[4 * k + 3]);
+        for (int k = 0; k < PER / 16; k++) dst4[k] = src4[k];
     }
 }
 
@@ -356,7 +431,7 @@ quantize_kernel(const uint16_t* __restrict__ kpool, const uint16_t* __restrict__
                 const int32_t* __restrict__ dst, int32_t H, int64_t n_fpages, int64_t n_qpages, int32_t n_iters) {
     using S = TileShape<D, T>;
     __shared__ __attribute__((aligned(16))) uint8_t smem[S::SMEM];
-    __shared__ __attribute__((aligned(16))) float bvec[D];
+    __shared__ __attribute__((aligned(16))) float vec[3 * D];
     const int kind = HASV ? (int)(blockIdx.x & 1u) : 0;
     const int r = HASV ? (int)(blockIdx.x >> 1) : (int)blockIdx.x;
     const int i = r / H;
@@ -367,10 +442,10 @@ quantize_kernel(const uint16_t* __restrict__ kpool, const uint16_t* __restrict__
     const int64_t tile_off = ((int64_t)sp * H + h) * (int64_t)(T * D);
     if (kind == 0) {
         constexpr int REC = T * D * KB / 8 + 4 * T + 2 * D;
-        quantize_tile<D, T, KB, false>(kpool + tile_off, krec + ((int64_t)dp * H + h) * REC, smem, bvec, n_iters);
+        quantize_tile<D, T, KB, false>(kpool + tile_off, krec + ((int64_t)dp * H + h) * REC, smem, vec, n_iters);
     } else if constexpr (HASV) {
         constexpr int REC = T * D * VB / 8 + 4 * T + 2 * D;
-        quantize_tile<D, T, VB, true>(vpool + tile_off, vrec + ((int64_t)dp * H + h) * REC, smem, bvec, n_iters);
+        quantize_tile<D, T, VB, true>(vpool + tile_off, vrec + ((int64_t)dp * H + h) * REC, smem, vec, n_iters);
     }
 }
 
