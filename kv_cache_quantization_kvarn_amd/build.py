@@ -8,7 +8,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkvarn.so")
 SOURCES = ["api.cpp", "quantize.hip", "quantize_d128.hip", "quantize_d256.hip", "quantize_d512.hip",
-           "decode_gqa.hip"]
+           "decode_gqa.hip", "decode_mla.hip"]
 HEADERS = ["kvarn_device.hpp", "kvarn_internal.hpp", "quantize_impl.hpp"]
 
 FLAGS = [
@@ -23,7 +23,8 @@ FLAGS = [
 # finite fp16 values
 EXTRA = {"quantize_d128.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"],
          "quantize_d256.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"],
-         "quantize_d512.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"]}
+         "quantize_d512.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"],
+         "decode_mla.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"]}
 
 
 def sources():

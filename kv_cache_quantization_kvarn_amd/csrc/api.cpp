@@ -162,6 +162,7 @@ size_t kvarn_decode_workspace_bytes(const kvarn_layout* layout, int32_t batch, i
     const int H = layout->num_kv_heads;
     kvarn::decode_plan(layout->head_dim, H, num_q_heads / (H > 0 ? H : 1), layout->mla, batch, max_pages,
                        layout->tile_tokens, &ns, &pps);
+    if (layout->mla) return kvarn::mla_workspace_floats(num_q_heads, batch, ns) * sizeof(float);
     return kvarn::decode_workspace_floats(layout->head_dim, num_q_heads, batch, ns) * sizeof(float);
 }
 
@@ -180,7 +181,8 @@ kvarn_status kvarn_decode_attn(const kvarn_layout* layout, const kvarn_cache* ca
         return fail(KVARN_EINVAL, "num_q_heads %d is not a multiple of num_kv_heads %d", num_q_heads, H);
     const int G = num_q_heads / H;
     if (layout->mla) {
-        return fail(KVARN_EUNSUPPORTED, "mla decode is not built yet");
+        if (num_q_heads != 16 && num_q_heads != 32 && num_q_heads != 64 && num_q_heads != 128)
+            return fail(KVARN_EUNSUPPORTED, "mla: %d query heads; 16, 32, 64 or 128 are implemented", num_q_heads);
     } else if (G != 4) {
         return fail(KVARN_EUNSUPPORTED, "GQA group %d: this build implements groups of 4 query heads", G);
     }
@@ -191,7 +193,9 @@ kvarn_status kvarn_decode_attn(const kvarn_layout* layout, const kvarn_cache* ca
     int ns = 1, pps = 1;
     kvarn::decode_plan(layout->head_dim, H, G, layout->mla, pages->batch, pages->max_pages, layout->tile_tokens,
                        &ns, &pps);
-    const size_t need = kvarn::decode_workspace_floats(layout->head_dim, num_q_heads, pages->batch, ns) * sizeof(float);
+    const size_t need = (layout->mla ? kvarn::mla_workspace_floats(num_q_heads, pages->batch, ns)
+                                     : kvarn::decode_workspace_floats(layout->head_dim, num_q_heads, pages->batch, ns)) *
+                        sizeof(float);
     if (!workspace || workspace_bytes < need)
         return fail(KVARN_EWORKSPACE, "workspace of %zu bytes is smaller than the %zu bytes required",
                     workspace ? workspace_bytes : (size_t)0, need);

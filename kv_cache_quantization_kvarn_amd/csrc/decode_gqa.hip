@@ -420,8 +420,11 @@ hipError_t gqa_bits(const DecodeArgs& a, hipStream_t st) {
 
 void decode_plan(int D, int H, int G, int mla, int B, int max_pages, int T, int* nsplit, int* pps) {
     (void)D; (void)G; (void)T;
-    const int units = mla ? B : B * H;
-    const int target = 1024;
+    // GQA: about four 4-wave workgroups per CU.  MLA: one 4-wave workgroup per
+    // CU holds 64 heads (its accumulators fill the register file), so up to 128
+    // heads take two workgroups per split.
+    const int units = mla ? B * ((G + 63) / 64) : B * H;
+    const int target = mla ? 256 : 1024;
     int ns = (target + units - 1) / units;
     if (ns < 1) ns = 1;
     if (ns > max_pages) ns = max_pages;
@@ -438,7 +441,7 @@ size_t decode_workspace_floats(int D, int Hq, int B, int nsplit) {
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
-    if (a.mla) return hipErrorNotSupported;
+    if (a.mla) return launch_mla(a, st);
     if (a.D == 128 && a.T == 128) return gqa_bits<128, 128>(a, st);
     if (a.D == 128 && a.T == 64) return gqa_bits<128, 64>(a, st);
     if (a.D == 256 && a.T == 128) return gqa_bits<256, 128>(a, st);

@@ -1,0 +1,454 @@
+// KVarN MLA decode for gfx950: one 512-wide int4 latent record per token
+// serves as key and value for all query heads (evermx.com KVarN review,
+// paragraph on MLA models: the compressed KV latent is quantized to int4).
+//
+// The heads share every latent element, so the path is a pair of GEMMs per
+// 32-token chunk on the 16x16x32 fp16 MFMA:
+//   S[h][t] = q'_h . y_t        O[h][j] += sum_t P[h][t] y_tj
+// with q' = H q (rotated once, per sequence and head, by qrot_kernel) and
+// y_t the record read back in the rotated basis, y_tj = C_j (S_t c_tj + Zp_t).
+// Each chunk is read back once into LDS (fp16) and used by all heads; it never
+// goes to HBM.  fp16 sink and tail chunks are rotated into the same basis on
+// the fly (an MFMA product with H_512, whose +-1 operand blocks are a fixed
+// per-lane pattern up to a sign), so a split keeps one accumulator.  The
+// softmax rescales O lazily: only when a head's running maximum grows by more
+// than 2^8, which keeps every weight below 256.  The combine applies H once.
+//
+// Workgroup: 4 waves per (head group of up to 64 heads, split, sequence).
+// QK: wave w owns head block w (16 heads).  PV: wave w owns 128 of the 512
+// channels for all the group's heads.  PV operands come from LDS through ds_read_b64_tr_b16 (4 rows
+// x 16 columns of halves transposed per 16 lanes).
+#include <math.h>
+
+#include "kvarn_device.hpp"
+#include "kvarn_internal.hpp"
+
+namespace kvarn {
+namespace {
+
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef short s4 __attribute__((ext_vector_type(4)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int MD = 512;        // latent width
+constexpr int CH = 32;         // tokens per chunk
+constexpr float kLazy = 8.0f;  // rescale when the maximum grows by more than this (log2 units)
+
+#define LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
+
+__device__ __forceinline__ h4 tr16(const void* p) {
+    s4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS(s4, p));
+    return __builtin_bit_cast(h4, v);
+}
+
+__device__ __forceinline__ h8 cat(h4 a, h4 b) {
+    return h8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+__device__ __forceinline__ float rmax16(float v) {  // max over the 16 lanes of a row
+    v = fmaxf(v, i2f(__builtin_amdgcn_mov_dpp(f2i(v), 0x128, 0xF, 0xF, false)));  // row_ror 8
+    v = fmaxf(v, i2f(__builtin_amdgcn_mov_dpp(f2i(v), 0x124, 0xF, 0xF, false)));  // row_ror 4
+    v = fmaxf(v, i2f(__builtin_amdgcn_mov_dpp(f2i(v), 0x122, 0xF, 0xF, false)));  // row_ror 2
+    v = fmaxf(v, i2f(__builtin_amdgcn_mov_dpp(f2i(v), 0x121, 0xF, 0xF, false)));  // row_ror 1
+    return v;
+}
+
+__device__ __forceinline__ float rsum16(float v) {
+    v += i2f(__builtin_amdgcn_update_dpp(0, f2i(v), 0x128, 0xF, 0xF, true));
+    v += i2f(__builtin_amdgcn_update_dpp(0, f2i(v), 0x124, 0xF, 0xF, true));
+    v += i2f(__builtin_amdgcn_update_dpp(0, f2i(v), 0x122, 0xF, 0xF, true));
+    v += i2f(__builtin_amdgcn_update_dpp(0, f2i(v), 0x121, 0xF, 0xF, true));
+    return v;
+}
+
+// q' = H q / sqrt(D) as fp16, one workgroup per (sequence, head).
+__global__ void __launch_bounds__(256) qrot_kernel(const void* __restrict__ q, int q_bf16, _Float16* __restrict__ qr) {
+    __shared__ float x[MD];
+    const int bh = blockIdx.x;
+    for (int j = threadIdx.x; j < MD; j += 256) {
+        const int64_t idx = (int64_t)bh * MD + j;
+        x[j] = q_bf16 ? __builtin_bit_cast(float, ((uint32_t) static_cast<const uint16_t*>(q)[idx]) << 16)
+                      : static_cast<const float*>(q)[idx];
+    }
+    __syncthreads();
+    for (int hs = 1; hs < MD; hs <<= 1) {
+        const int k = threadIdx.x;  // 256 butterflies per stage
+        const int i0 = (k / hs) * 2 * hs + (k % hs), i1 = i0 + hs;
+        const float a = x[i0], b = x[i1];
+        __syncthreads();
+        x[i0] = a + b;
+        x[i1] = a - b;
+        __syncthreads();
+    }
+    const float rs = 1.0f / sqrtf((float)MD);
+    for (int j = threadIdx.x; j < MD; j += 256) qr[(int64_t)bh * MD + j] = (_Float16)(x[j] * rs);
+}
+
+// H_512[m][k] for m = 16*mb + l16, k = 32*ks + 8*g4 + i factors as
+//   sign(mb, ks) * P(l16, g4, i) * (-1)^(mb_0 * g4_1),
+// with sign(mb, ks) = (-1)^popcount((mb >> 1) & ks) and
+// P = (-1)^(popcount(l16 & i & 7) + l16_3 * g4_0): two per-lane operand
+// patterns (and their negations) serve every block.
+
+// Workgroup of 4 waves.  QK: wave w owns head block w (16 heads).  PV: wave w
+// owns channels CPW*w .. CPW*w + CPW - 1.
+template <int HB>
+struct MlaShape {
+    static_assert(HB >= 1 && HB <= 4, "a workgroup holds at most 64 heads");
+    static constexpr int NWV = 4;
+    static constexpr int NT = NWV * 64;
+    static constexpr int CPW = MD / NWV;   // PV channels per wave
+    static constexpr int CBW = CPW / 16;   // PV channel blocks per wave
+    static constexpr int HQ = HB * 16;
+};
+
+template <int T, int HB>
+__global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs a) {
+    using SH = MlaShape<HB>;
+    constexpr int NWV = SH::NWV, NT = SH::NT, CPW = SH::CPW, CBW = SH::CBW, HQ = SH::HQ;
+    constexpr int KCB = T * MD / 2;                // int4 code bytes of a record
+    constexpr int KREC = KCB + 4 * T + 2 * MD;
+    constexpr int WS = MD + 4;                     // partial: m, l, pad, pad, O[512]
+    constexpr int TPT = NT / CH;                   // threads per token in the read-back
+    constexpr int CPT = MD / TPT;                  // channels per thread in the read-back
+    __shared__ __attribute__((aligned(16))) _Float16 ybuf[CH * MD];   // chunk, rotated basis
+    __shared__ __attribute__((aligned(16))) _Float16 pbuf[CH * HQ];   // weights [token][head]
+    __shared__ __attribute__((aligned(16))) h8 hpat[2][2][64];
+    __shared__ float alpha[HQ];
+    __shared__ int rescale_flag;
+
+    // Workgroup id -> (head group hg, split, sequence b).  Workgroups are dealt
+    // to the 8 XCDs round-robin; the head groups of one (split, sequence) get
+    // ids 8 apart, so they run on the same XCD at about the same time and read
+    // each latent chunk through that XCD's L2.
+    const int nhg = a.Hq / HQ;
+    const int units = a.B * a.nsplit;
+    const int id = blockIdx.x;
+    const int hg = (id % (8 * nhg)) / 8;
+    const int u = (id / (8 * nhg)) * 8 + (id % 8);
+    if (u >= units) return;
+    const int b = u / a.nsplit, split = u - b * a.nsplit;
+    const int h0 = hg * HQ;  // first query head of this workgroup
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, g4 = lane >> 4;
+    const float sm2 = a.sm_scale * kLog2e;
+    const bool qk_wave = wave < HB;
+
+    // rotated queries of this wave's head block, as QK A operands
+    const _Float16* qr = reinterpret_cast<const _Float16*>(a.ws);  // q' at the start of the workspace
+    h8 qa[16];
+#pragma unroll
+    for (int ks = 0; ks < 16; ks++) {
+        if (qk_wave) {
+            const _Float16* p = qr + ((int64_t)b * a.Hq + h0 + wave * 16 + l16) * MD + 32 * ks + 8 * g4;
+            qa[ks] = *reinterpret_cast<const h8*>(p);
+        } else {
+            qa[ks] = h8{0, 0, 0, 0, 0, 0, 0, 0};
+        }
+    }
+    // H_512 operand patterns for the fp16-chunk rotation, per lane: hpat[odd mb][negated][lane]
+    // (kept in LDS: only fp16 chunks use them)
+    if (wave == 0) {
+#pragma unroll
+        for (int od = 0; od < 2; od++) {
+            h8 v;
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                const int par = (__builtin_popcount((unsigned)(l16 & i & 7)) + ((l16 >> 3) & g4 & 1) + (od & (g4 >> 1))) & 1;
+                v[i] = par ? (_Float16)-1.0f : (_Float16)1.0f;
+            }
+            hpat[od][0][lane] = v;
+            hpat[od][1][lane] = -v;
+        }
+    }
+    __syncthreads();
+
+    f4 O[HB][CBW];
+#pragma unroll
+    for (int hb = 0; hb < HB; hb++)
+#pragma unroll
+        for (int c = 0; c < CBW; c++) O[hb][c] = f4{0.f, 0.f, 0.f, 0.f};
+    float mu[4], lp[4];  // running max (log2 units) and per-lane partial sums, heads 16*wave + 4*g4 + i
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        mu[i] = -INFINITY;
+        lp[i] = 0.f;
+    }
+
+    const int L = min(a.seq_lens[b], a.max_pages * T);
+    const int npages = L > 0 ? (L + T - 1) / T : 0;
+    const int nq = (L - a.sink - a.tail >= T) ? (L - a.sink - a.tail) / T : 0;
+    const int sp = a.sink / T;
+    const int pbeg = split * a.pps;
+    const int pend = min(pbeg + a.pps, npages);
+
+    for (int page = pbeg; page < pend; page++) {
+        const bool quant = page >= sp && page < sp + nq;
+        const int id = a.block_table[(int64_t)b * a.max_pages + page];
+        if (id < 0 || (quant ? (int64_t)id >= a.n_qpages : (int64_t)id >= a.n_fpages)) continue;
+        for (int c0 = 0; c0 < T; c0 += CH) {
+            if (page * T + c0 >= L) break;
+            // ---- 1. chunk -> ybuf (rotated basis, fp16) ----
+            if (quant) {
+                const uint8_t* rk = static_cast<const uint8_t*>(a.k_records) + (int64_t)id * KREC;
+                const int tt = tid / TPT, part = tid % TPT;  // token, CPT-channel part
+                const uint4* cp = reinterpret_cast<const uint4*>(rk + (int64_t)(c0 + tt) * (MD / 2) + (CPT / 2) * part);
+                uint32_t cw[CPT / 8];
+#pragma unroll
+                for (int k = 0; k < CPT / 32; k++) {
+                    const uint4 w = cp[k];
+                    cw[4 * k] = w.x; cw[4 * k + 1] = w.y; cw[4 * k + 2] = w.z; cw[4 * k + 3] = w.w;
+                }
+                const uint32_t sz = reinterpret_cast<const uint32_t*>(rk + KCB)[c0 + tt];
+                const float S = half_bits_to_float(sz & 0xffffu), Z = half_bits_to_float(sz >> 16);
+                const uint4* cc = reinterpret_cast<const uint4*>(rk + KCB + 4 * T + 2 * CPT * part);
+                uint32_t out[CPT / 2];
+#pragma unroll
+                for (int q8 = 0; q8 < CPT / 8; q8++) {
+                    if ((q8 & 1) == 0) __builtin_amdgcn_sched_barrier(0);
+                    const uint4 cv = cc[q8];  // column scales of channels CPT*part + 8*q8 .. +8
+                    const uint32_t cs[4] = {cv.x, cv.y, cv.z, cv.w};
+                    const uint32_t w = cw[q8];
+#pragma unroll
+                    for (int k = 0; k < 4; k++) {
+                        const float y0 = half_bits_to_float(cs[k] & 0xffffu) * fmaf(S, (float)((w >> (8 * k)) & 15u), Z);
+                        const float y1 = half_bits_to_float(cs[k] >> 16) * fmaf(S, (float)((w >> (8 * k + 4)) & 15u), Z);
+                        out[4 * q8 + k] = float_to_half_bits(y0) | (float_to_half_bits(y1) << 16);
+                    }
+                }
+                uint4* dst = reinterpret_cast<uint4*>(ybuf + tt * MD + CPT * part);
+#pragma unroll
+                for (int k = 0; k < CPT / 8; k++) dst[k] = make_uint4(out[4 * k], out[4 * k + 1], out[4 * k + 2], out[4 * k + 3]);
+                __syncthreads();
+            } else {
+                // y_t = H x_t / sqrt(512): Y^T = H X^T on the MFMA, the B operand read
+                // straight from the fp16 page (8 channels of one token per lane).
+                // Wave w writes channel blocks MBW*w .. of both 16-token halves.
+                constexpr int MBW = 32 / NWV;
+                const uint16_t* fp = static_cast<const uint16_t*>(a.k_fp16) + ((int64_t)id * T + c0) * MD;
+                const float rs = 1.0f / sqrtf((float)MD);
+#pragma unroll
+                for (int th = 0; th < 2; th++) {
+                    f4 z[MBW];
+#pragma unroll
+                    for (int m = 0; m < MBW; m++) z[m] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ks = 0; ks < 16; ks++) {
+                        if ((ks & 1) == 0) __builtin_amdgcn_sched_barrier(0);
+                        h8 bx = *reinterpret_cast<const h8*>(fp + (16 * th + l16) * MD + 32 * ks + 8 * g4);
+                        // sign(mb, ks) = (-1)^popcount(((MBW/2)*wave) & ks) * (-1)^popcount((m >> 1) & ks):
+                        // the wave part negates the B operand, the m part picks the pattern
+                        if (__builtin_popcount((unsigned)((MBW / 2) * wave) & (unsigned)ks) & 1) bx = -bx;
+#pragma unroll
+                        for (int m = 0; m < MBW; m++) {
+                            const h8 av = hpat[m & 1][__builtin_popcount((unsigned)((m >> 1) & ks)) & 1][lane];
+                            z[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bx, z[m], 0, 0, 0);
+                        }
+                    }
+                    // lane: channels 16*mb + 4*g4 .. +3 of token 16*th + l16; tokens past the
+                    // sequence end are zeroed (their weight is 0 and must not meet NaN)
+                    const bool tv = page * T + c0 + 16 * th + l16 < L;
+#pragma unroll
+                    for (int m = 0; m < MBW; m++) {
+                        const f4 v = z[m];
+                        uint2 pk = make_uint2(float_to_half_bits(v[0] * rs) | (float_to_half_bits(v[1] * rs) << 16),
+                                              float_to_half_bits(v[2] * rs) | (float_to_half_bits(v[3] * rs) << 16));
+                        if (!tv) pk = make_uint2(0u, 0u);
+                        *reinterpret_cast<uint2*>(ybuf + (16 * th + l16) * MD + 16 * (MBW * wave + m) + 4 * g4) = pk;
+                    }
+                }
+                __syncthreads();
+            }
+
+            // ---- 2. scores and weights for this wave's 16 heads ----
+            if (tid == 0) rescale_flag = 0;
+            bool need = false;
+            float s[2][4], cmax[4];
+            if (qk_wave) {
+                f4 sacc[2] = {f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+                for (int th = 0; th < 2; th++)
+#pragma unroll
+                    for (int ks = 0; ks < 16; ks++) {
+                        const h8 by = *reinterpret_cast<const h8*>(ybuf + (16 * th + l16) * MD + 32 * ks + 8 * g4);
+                        sacc[th] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[ks], by, sacc[th], 0, 0, 0);
+                        if ((ks & 3) == 3) __builtin_amdgcn_sched_barrier(0);  // bound operand prefetch
+                    }
+                // lane: heads 16*wave + 4*g4 + i, tokens c0 + 16*th + l16
+#pragma unroll
+                for (int th = 0; th < 2; th++) {
+                    const bool valid = page * T + c0 + 16 * th + l16 < L;
+#pragma unroll
+                    for (int i = 0; i < 4; i++) s[th][i] = valid ? sacc[th][i] * sm2 : -INFINITY;
+                }
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    cmax[i] = rmax16(fmaxf(s[0][i], s[1][i]));
+                    need |= cmax[i] > mu[i] + kLazy;
+                }
+            }
+            __syncthreads();
+            if (qk_wave) {
+                const bool any = __builtin_amdgcn_ballot_w64(need) != 0;
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    float al = 1.f;
+                    if (any) {
+                        const float mn = fmaxf(mu[i], cmax[i]);
+                        al = (mu[i] == -INFINITY) ? 0.f : exp2f(mu[i] - mn);
+                        lp[i] *= al;
+                        mu[i] = mn;
+                    }
+                    if (l16 == 0) alpha[16 * wave + 4 * g4 + i] = al;
+                }
+                if (any && lane == 0) atomicOr(&rescale_flag, 1);
+#pragma unroll
+                for (int th = 0; th < 2; th++) {
+                    float p[4];
+#pragma unroll
+                    for (int i = 0; i < 4; i++) {
+                        p[i] = (mu[i] == -INFINITY) ? 0.f : exp2f(s[th][i] - mu[i]);
+                        lp[i] += p[i];
+                    }
+                    const uint2 pk = make_uint2(float_to_half_bits(p[0]) | (float_to_half_bits(p[1]) << 16),
+                                                float_to_half_bits(p[2]) | (float_to_half_bits(p[3]) << 16));
+                    *reinterpret_cast<uint2*>(pbuf + (16 * th + l16) * HQ + 16 * wave + 4 * g4) = pk;
+                }
+            }
+            __syncthreads();
+
+            // ---- 3. O += P Y for this wave's channels ----
+            if (rescale_flag) {
+#pragma unroll
+                for (int hb = 0; hb < HB; hb++)
+#pragma unroll
+                    for (int i = 0; i < 4; i++) {
+                        const float al = alpha[16 * hb + 4 * g4 + i];
+#pragma unroll
+                        for (int c = 0; c < CBW; c++) O[hb][c][i] *= al;
+                    }
+            }
+            {
+                // tr16: lane 4k + q of a 16-lane group reads row k, columns 4q .. 4q+3;
+                // lane j receives column j of the 4 rows.  Rows are tokens.
+                const int row = 8 * g4 + (l16 >> 2), colq = 4 * (l16 & 3);
+                h8 bv[CBW];  // Y[32 tokens][16 channels]: lane channel l16, tokens 8*g4 .. +7
+#pragma unroll
+                for (int c = 0; c < CBW; c++) {
+                    const int ch = CPW * wave + 16 * c;
+                    bv[c] = cat(tr16(ybuf + row * MD + ch + colq), tr16(ybuf + (row + 4) * MD + ch + colq));
+                }
+#pragma unroll
+                for (int hb = 0; hb < HB; hb++) {
+                    // P[16 heads][32 tokens]: lane head l16, tokens 8*g4 .. +7
+                    const h8 pa = cat(tr16(pbuf + row * HQ + 16 * hb + colq), tr16(pbuf + (row + 4) * HQ + 16 * hb + colq));
+#pragma unroll
+                    for (int c = 0; c < CBW; c++) O[hb][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, bv[c], O[hb][c], 0, 0, 0);
+                }
+            }
+            __syncthreads();
+        }
+    }
+
+    // ---- partial results: m, l per head; O rows for this wave's channels ----
+    float* wsp = a.ws + (int64_t)a.B * a.Hq * MD / 2;  // partials follow the fp16 queries
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const float lt = rsum16(lp[i]);
+        if (qk_wave && l16 == 0) {
+            float* o = wsp + (((int64_t)b * a.Hq + h0 + 16 * wave + 4 * g4 + i) * a.nsplit + split) * WS;
+            o[0] = mu[i];
+            o[1] = lt;
+        }
+    }
+#pragma unroll
+    for (int hb = 0; hb < HB; hb++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            float* o = wsp + (((int64_t)b * a.Hq + h0 + 16 * hb + 4 * g4 + i) * a.nsplit + split) * WS + 4;
+#pragma unroll
+            for (int c = 0; c < CBW; c++) o[CPW * wave + 16 * c + l16] = O[hb][c][i];
+        }
+}
+
+// merge the splits of one (sequence, head), rotate back once, normalize
+__global__ void __launch_bounds__(256) mla_combine_kernel(const float* __restrict__ wsp, float* __restrict__ out, int nsplit) {
+    constexpr int WS = MD + 4;
+    __shared__ float x[MD];
+    const int bh = blockIdx.x;
+    const float* base = wsp + (int64_t)bh * nsplit * WS;
+    float M = -INFINITY;
+    for (int s = 0; s < nsplit; s++) M = fmaxf(M, base[s * WS]);
+    float Ls = 0.f, r0 = 0.f, r1 = 0.f;
+    const int j0 = threadIdx.x, j1 = threadIdx.x + 256;
+    if (M != -INFINITY) {
+        for (int s = 0; s < nsplit; s++) {
+            const float ms = base[s * WS];
+            if (ms == -INFINITY) continue;
+            const float e = exp2f(ms - M);
+            Ls = fmaf(base[s * WS + 1], e, Ls);
+            r0 = fmaf(base[s * WS + 4 + j0], e, r0);
+            r1 = fmaf(base[s * WS + 4 + j1], e, r1);
+        }
+    }
+    x[j0] = r0;
+    x[j1] = r1;
+    __syncthreads();
+    for (int hs = 1; hs < MD; hs <<= 1) {
+        const int k = threadIdx.x;
+        const int i0 = (k / hs) * 2 * hs + (k % hs), i1 = i0 + hs;
+        const float u = x[i0], v = x[i1];
+        __syncthreads();
+        x[i0] = u + v;
+        x[i1] = u - v;
+        __syncthreads();
+    }
+    const float sc = Ls > 0.f ? 1.0f / (Ls * sqrtf((float)MD)) : 0.f;
+    out[(int64_t)bh * MD + j0] = x[j0] * sc;
+    out[(int64_t)bh * MD + j1] = x[j1] * sc;
+}
+
+template <int T, int HB>
+hipError_t launch_mla_t(const DecodeArgs& a, hipStream_t st) {
+    hipLaunchKernelGGL(qrot_kernel, dim3(a.B * a.Hq), dim3(256), 0, st, a.q, a.q_bf16,
+                       reinterpret_cast<_Float16*>(a.ws));
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int nhg = a.Hq / (16 * HB);
+    const int units = a.B * a.nsplit;
+    const int blocks = ((units + 7) / 8) * 8 * nhg;
+    hipLaunchKernelGGL((mla_split_kernel<T, HB>), dim3(blocks), dim3(MlaShape<HB>::NT), 0, st, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const float* wsp = a.ws + (int64_t)a.B * a.Hq * MD / 2;
+    hipLaunchKernelGGL(mla_combine_kernel, dim3(a.B * a.Hq), dim3(256), 0, st, wsp, a.out, a.nsplit);
+    return hipGetLastError();
+}
+
+template <int T>
+hipError_t launch_mla_hb(const DecodeArgs& a, hipStream_t st) {
+    switch (a.Hq) {
+        case 16: return launch_mla_t<T, 1>(a, st);
+        case 32: return launch_mla_t<T, 2>(a, st);
+        case 64: return launch_mla_t<T, 4>(a, st);
+        case 128: return launch_mla_t<T, 4>(a, st);  // two 64-head workgroups
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+size_t mla_workspace_floats(int Hq, int B, int nsplit) {
+    return (size_t)B * Hq * MD / 2 + (size_t)B * Hq * nsplit * (MD + 4);
+}
+
+hipError_t launch_mla(const DecodeArgs& a, hipStream_t st) {
+    if (a.D != MD || a.k_bits != 4) return hipErrorInvalidValue;
+    if (a.T == 128) return launch_mla_hb<128>(a, st);
+    if (a.T == 64) return launch_mla_hb<64>(a, st);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace kvarn

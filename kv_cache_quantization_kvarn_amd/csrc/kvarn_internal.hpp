@@ -51,4 +51,8 @@ void decode_plan(int D, int H, int G, int mla, int B, int max_pages, int T, int*
 size_t decode_workspace_floats(int D, int Hq, int B, int nsplit);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
 
+// MLA: fp16 rotated queries [B][Hq][512] then split partials [B][Hq][nsplit][516] fp32.
+size_t mla_workspace_floats(int Hq, int B, int nsplit);
+hipError_t launch_mla(const DecodeArgs& a, hipStream_t st);
+
 }  // namespace kvarn

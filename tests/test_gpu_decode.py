@@ -93,3 +93,40 @@ def test_decode_full_size_sampled(name):
     pairs = np.array([(int(rng.integers(B)), int(rng.integers(Hq))) for _ in range(3)] + [(B - 1, Hq - 1)],
                      np.int32)
     check(case, out, krec, vrec, pairs)
+
+
+MLA_SHAPES = [
+    # Hq, T, lens, sink, tail
+    (16, 128, [700, 1, 300], 128, 128),
+    (32, 64, [900, 129, 64], 64, 100),
+    (64, 128, [1500, 640], 128, 256),
+    (128, 128, [1400, 0, 777], 128, 256),
+    (128, 64, [1000, 500], 0, 64),
+]
+
+
+@pytest.mark.parametrize("Hq,T,lens,sink,tail", MLA_SHAPES)
+def test_decode_mla_shapes(Hq, T, lens, sink, tail):
+    w = workload("mla_d512_b32_32k_int4", Hq=Hq, T=T, sink=sink, tail=tail, seed=0x5000 + Hq + T)
+    case = gpu_case(w, seq_lens=lens, batch=len(lens))
+    say("mla shape", Hq, T, lens)
+    L, krec, vrec = run_quantize(case)
+    out = run_decode(case, L, krec, vrec)
+    o = out.cpu().numpy()
+    for b, n in enumerate(lens):
+        if n == 0:
+            assert np.all(o[b] == 0)
+    pairs = np.array([(b, h) for b in range(len(lens)) if lens[b] > 0 for h in sorted({0, Hq // 2 + 1, Hq - 1})],
+                     np.int32)
+    check(case, out, krec, None, pairs)
+
+
+def test_decode_mla_full_size_sampled():
+    case = gpu_case(workload("mla_d512_b32_32k_int4"))
+    say("decode full mla")
+    L, krec, vrec = run_quantize(case)
+    out = run_decode(case, L, krec, vrec)
+    o = out.cpu().numpy()
+    assert np.all(np.isfinite(o))
+    pairs = np.array([(3, 5), (17, 100), (31, 127)], np.int32)
+    check(case, out, krec, None, pairs)
