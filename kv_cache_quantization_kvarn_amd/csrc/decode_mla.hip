@@ -116,6 +116,7 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
     __shared__ __attribute__((aligned(16))) _Float16 ybuf[CH * MD];   // chunk, rotated basis
     __shared__ __attribute__((aligned(16))) _Float16 pbuf[CH * HQ];   // weights [token][head]
     __shared__ __attribute__((aligned(16))) h8 hpat[2][2][64];
+    __shared__ __attribute__((aligned(16))) _Float16 cbuf[2][MD];     // column scales, by page parity
     __shared__ float alpha[HQ];
     __shared__ int rescale_flag;
 
@@ -184,172 +185,215 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
     const int pbeg = split * a.pps;
     const int pend = min(pbeg + a.pps, npages);
 
-    for (int page = pbeg; page < pend; page++) {
-        const bool quant = page >= sp && page < sp + nq;
-        const int id = a.block_table[(int64_t)b * a.max_pages + page];
-        if (id < 0 || (quant ? (int64_t)id >= a.n_qpages : (int64_t)id >= a.n_fpages)) continue;
-        for (int c0 = 0; c0 < T; c0 += CH) {
-            if (page * T + c0 >= L) break;
-            // ---- 1. chunk -> ybuf (rotated basis, fp16) ----
-            if (quant) {
-                const uint8_t* rk = static_cast<const uint8_t*>(a.k_records) + (int64_t)id * KREC;
-                const int tt = tid / TPT, part = tid % TPT;  // token, CPT-channel part
-                const uint4* cp = reinterpret_cast<const uint4*>(rk + (int64_t)(c0 + tt) * (MD / 2) + (CPT / 2) * part);
-                uint32_t cw[CPT / 8];
+    // Chunks of this split, in order: chunk ci is page pbeg + ci / CPP, tokens
+    // (ci % CPP) * CH .. +CH of it.  The codes and token scales of chunk ci + 1
+    // are loaded into registers while chunk ci runs its MFMAs; column scales are
+    // staged per page in LDS (cbuf, two slots by page parity).
+    constexpr int CPP = T / CH;
+    const int nch = pend > pbeg ? (min(pend * T, L) - pbeg * T + CH - 1) / CH : 0;
+    const int tt = tid / TPT, part = tid % TPT;  // read-back: token, CPT-channel part
+    uint4 pf_code[CPT / 32];
+    uint32_t pf_sz = 0;
+    uint4 pf_c = make_uint4(0u, 0u, 0u, 0u);
+    int pf_id = -1;
+    bool pf_quant = false;
+    auto chunk_info = [&](int ci, int& page, int& c0, bool& quant, int& id) {
+        page = pbeg + ci / CPP;
+        c0 = (ci % CPP) * CH;
+        quant = page >= sp && page < sp + nq;
+        id = a.block_table[(int64_t)b * a.max_pages + page];
+        if (id < 0 || (quant ? (int64_t)id >= a.n_qpages : (int64_t)id >= a.n_fpages)) id = -1;
+    };
+    auto prefetch = [&](int ci) {
+        int page, c0, id;
+        bool quant;
+        chunk_info(ci, page, c0, quant, id);
+        pf_id = id;
+        pf_quant = quant;
+        if (id >= 0 && quant) {
+            const uint8_t* rk = static_cast<const uint8_t*>(a.k_records) + (int64_t)id * KREC;
+            const uint4* cp = reinterpret_cast<const uint4*>(rk + (int64_t)(c0 + tt) * (MD / 2) + (CPT / 2) * part);
 #pragma unroll
-                for (int k = 0; k < CPT / 32; k++) {
-                    const uint4 w = cp[k];
-                    cw[4 * k] = w.x; cw[4 * k + 1] = w.y; cw[4 * k + 2] = w.z; cw[4 * k + 3] = w.w;
-                }
-                const uint32_t sz = reinterpret_cast<const uint32_t*>(rk + KCB)[c0 + tt];
-                const float S = half_bits_to_float(sz & 0xffffu), Z = half_bits_to_float(sz >> 16);
-                const uint4* cc = reinterpret_cast<const uint4*>(rk + KCB + 4 * T + 2 * CPT * part);
-                uint32_t out[CPT / 2];
-#pragma unroll
-                for (int q8 = 0; q8 < CPT / 8; q8++) {
-                    if ((q8 & 1) == 0) __builtin_amdgcn_sched_barrier(0);
-                    const uint4 cv = cc[q8];  // column scales of channels CPT*part + 8*q8 .. +8
-                    const uint32_t cs[4] = {cv.x, cv.y, cv.z, cv.w};
-                    const uint32_t w = cw[q8];
-#pragma unroll
-                    for (int k = 0; k < 4; k++) {
-                        const float y0 = half_bits_to_float(cs[k] & 0xffffu) * fmaf(S, (float)((w >> (8 * k)) & 15u), Z);
-                        const float y1 = half_bits_to_float(cs[k] >> 16) * fmaf(S, (float)((w >> (8 * k + 4)) & 15u), Z);
-                        out[4 * q8 + k] = float_to_half_bits(y0) | (float_to_half_bits(y1) << 16);
-                    }
-                }
-                uint4* dst = reinterpret_cast<uint4*>(ybuf + tt * MD + CPT * part);
-#pragma unroll
-                for (int k = 0; k < CPT / 8; k++) dst[k] = make_uint4(out[4 * k], out[4 * k + 1], out[4 * k + 2], out[4 * k + 3]);
+            for (int k = 0; k < CPT / 32; k++) pf_code[k] = cp[k];
+            pf_sz = reinterpret_cast<const uint32_t*>(rk + KCB)[c0 + tt];
+            if (c0 == 0 && tid < MD / 8) pf_c = reinterpret_cast<const uint4*>(rk + KCB + 4 * T)[tid];
+        }
+    };
+    if (nch > 0) prefetch(0);
+
+    for (int ci = 0; ci < nch; ci++) {
+        int page, c0, id;
+        bool quant;
+        chunk_info(ci, page, c0, quant, id);
+        if (id < 0) {  // uniform: skip a page whose id is outside its pool
+            if (ci + 1 < nch) prefetch(ci + 1);
+            continue;
+        }
+        // ---- 1. chunk -> ybuf (rotated basis, fp16) ----
+        if (quant) {
+            _Float16* cb = cbuf[page & 1];
+            if (c0 == 0) {
+                if (tid < MD / 8) reinterpret_cast<uint4*>(cb)[tid] = pf_c;
                 __syncthreads();
-            } else {
+            }
+            uint32_t cw[CPT / 8];
+#pragma unroll
+            for (int k = 0; k < CPT / 32; k++) {
+                cw[4 * k] = pf_code[k].x; cw[4 * k + 1] = pf_code[k].y;
+                cw[4 * k + 2] = pf_code[k].z; cw[4 * k + 3] = pf_code[k].w;
+            }
+            const float S = half_bits_to_float(pf_sz & 0xffffu), Z = half_bits_to_float(pf_sz >> 16);
+            const uint4* cc = reinterpret_cast<const uint4*>(cb + CPT * part);
+            uint32_t out[CPT / 2];
+#pragma unroll
+            for (int q8 = 0; q8 < CPT / 8; q8++) {
+                const uint4 cv = cc[q8];  // column scales of channels CPT*part + 8*q8 .. +8
+                const uint32_t cs[4] = {cv.x, cv.y, cv.z, cv.w};
+                const uint32_t w = cw[q8];
+#pragma unroll
+                for (int k = 0; k < 4; k++) {
+                    const float y0 = half_bits_to_float(cs[k] & 0xffffu) * fmaf(S, (float)((w >> (8 * k)) & 15u), Z);
+                    const float y1 = half_bits_to_float(cs[k] >> 16) * fmaf(S, (float)((w >> (8 * k + 4)) & 15u), Z);
+                    out[4 * q8 + k] = float_to_half_bits(y0) | (float_to_half_bits(y1) << 16);
+                }
+            }
+            uint4* dst = reinterpret_cast<uint4*>(ybuf + tt * MD + CPT * part);
+#pragma unroll
+            for (int k = 0; k < CPT / 8; k++) dst[k] = make_uint4(out[4 * k], out[4 * k + 1], out[4 * k + 2], out[4 * k + 3]);
+        } else {
                 // y_t = H x_t / sqrt(512): Y^T = H X^T on the MFMA, the B operand read
-                // straight from the fp16 page (8 channels of one token per lane).
-                // Wave w writes channel blocks MBW*w .. of both 16-token halves.
-                constexpr int MBW = 32 / NWV;
-                const uint16_t* fp = static_cast<const uint16_t*>(a.k_fp16) + ((int64_t)id * T + c0) * MD;
-                const float rs = 1.0f / sqrtf((float)MD);
+            // straight from the fp16 page (8 channels of one token per lane).
+            // Wave w writes channel blocks MBW*w .. of both 16-token halves.
+            constexpr int MBW = 32 / NWV;
+            const uint16_t* fp = static_cast<const uint16_t*>(a.k_fp16) + ((int64_t)id * T + c0) * MD;
+            const float rs = 1.0f / sqrtf((float)MD);
 #pragma unroll
-                for (int th = 0; th < 2; th++) {
-                    f4 z[MBW];
+            for (int th = 0; th < 2; th++) {
+                f4 z[MBW];
 #pragma unroll
-                    for (int m = 0; m < MBW; m++) z[m] = f4{0.f, 0.f, 0.f, 0.f};
+                for (int m = 0; m < MBW; m++) z[m] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int ks = 0; ks < 16; ks++) {
-                        if ((ks & 1) == 0) __builtin_amdgcn_sched_barrier(0);
-                        h8 bx = *reinterpret_cast<const h8*>(fp + (16 * th + l16) * MD + 32 * ks + 8 * g4);
-                        // sign(mb, ks) = (-1)^popcount(((MBW/2)*wave) & ks) * (-1)^popcount((m >> 1) & ks):
-                        // the wave part negates the B operand, the m part picks the pattern
-                        if (__builtin_popcount((unsigned)((MBW / 2) * wave) & (unsigned)ks) & 1) bx = -bx;
-#pragma unroll
-                        for (int m = 0; m < MBW; m++) {
-                            const h8 av = hpat[m & 1][__builtin_popcount((unsigned)((m >> 1) & ks)) & 1][lane];
-                            z[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bx, z[m], 0, 0, 0);
-                        }
-                    }
-                    // lane: channels 16*mb + 4*g4 .. +3 of token 16*th + l16; tokens past the
-                    // sequence end are zeroed (their weight is 0 and must not meet NaN)
-                    const bool tv = page * T + c0 + 16 * th + l16 < L;
+                for (int ks = 0; ks < 16; ks++) {
+                    if ((ks & 1) == 0) __builtin_amdgcn_sched_barrier(0);
+                    h8 bx = *reinterpret_cast<const h8*>(fp + (16 * th + l16) * MD + 32 * ks + 8 * g4);
+                    // sign(mb, ks) = (-1)^popcount(((MBW/2)*wave) & ks) * (-1)^popcount((m >> 1) & ks):
+                    // the wave part negates the B operand, the m part picks the pattern
+                    if (__builtin_popcount((unsigned)((MBW / 2) * wave) & (unsigned)ks) & 1) bx = -bx;
 #pragma unroll
                     for (int m = 0; m < MBW; m++) {
-                        const f4 v = z[m];
-                        uint2 pk = make_uint2(float_to_half_bits(v[0] * rs) | (float_to_half_bits(v[1] * rs) << 16),
-                                              float_to_half_bits(v[2] * rs) | (float_to_half_bits(v[3] * rs) << 16));
-                        if (!tv) pk = make_uint2(0u, 0u);
-                        *reinterpret_cast<uint2*>(ybuf + (16 * th + l16) * MD + 16 * (MBW * wave + m) + 4 * g4) = pk;
+                        const h8 av = hpat[m & 1][__builtin_popcount((unsigned)((m >> 1) & ks)) & 1][lane];
+                        z[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bx, z[m], 0, 0, 0);
                     }
                 }
-                __syncthreads();
-            }
-
-            // ---- 2. scores and weights for this wave's 16 heads ----
-            if (tid == 0) rescale_flag = 0;
-            bool need = false;
-            float s[2][4], cmax[4];
-            if (qk_wave) {
-                f4 sacc[2] = {f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f}};
+                // lane: channels 16*mb + 4*g4 .. +3 of token 16*th + l16; tokens past the
+                // sequence end are zeroed (their weight is 0 and must not meet NaN)
+                const bool tv = page * T + c0 + 16 * th + l16 < L;
 #pragma unroll
-                for (int th = 0; th < 2; th++)
-#pragma unroll
-                    for (int ks = 0; ks < 16; ks++) {
-                        const h8 by = *reinterpret_cast<const h8*>(ybuf + (16 * th + l16) * MD + 32 * ks + 8 * g4);
-                        sacc[th] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[ks], by, sacc[th], 0, 0, 0);
-                        if ((ks & 3) == 3) __builtin_amdgcn_sched_barrier(0);  // bound operand prefetch
-                    }
-                // lane: heads 16*wave + 4*g4 + i, tokens c0 + 16*th + l16
-#pragma unroll
-                for (int th = 0; th < 2; th++) {
-                    const bool valid = page * T + c0 + 16 * th + l16 < L;
-#pragma unroll
-                    for (int i = 0; i < 4; i++) s[th][i] = valid ? sacc[th][i] * sm2 : -INFINITY;
-                }
-#pragma unroll
-                for (int i = 0; i < 4; i++) {
-                    cmax[i] = rmax16(fmaxf(s[0][i], s[1][i]));
-                    need |= cmax[i] > mu[i] + kLazy;
+                for (int m = 0; m < MBW; m++) {
+                    const f4 v = z[m];
+                    uint2 pk = make_uint2(float_to_half_bits(v[0] * rs) | (float_to_half_bits(v[1] * rs) << 16),
+                                          float_to_half_bits(v[2] * rs) | (float_to_half_bits(v[3] * rs) << 16));
+                    if (!tv) pk = make_uint2(0u, 0u);
+                    *reinterpret_cast<uint2*>(ybuf + (16 * th + l16) * MD + 16 * (MBW * wave + m) + 4 * g4) = pk;
                 }
             }
-            __syncthreads();
-            if (qk_wave) {
-                const bool any = __builtin_amdgcn_ballot_w64(need) != 0;
-#pragma unroll
-                for (int i = 0; i < 4; i++) {
-                    float al = 1.f;
-                    if (any) {
-                        const float mn = fmaxf(mu[i], cmax[i]);
-                        al = (mu[i] == -INFINITY) ? 0.f : exp2f(mu[i] - mn);
-                        lp[i] *= al;
-                        mu[i] = mn;
-                    }
-                    if (l16 == 0) alpha[16 * wave + 4 * g4 + i] = al;
-                }
-                if (any && lane == 0) atomicOr(&rescale_flag, 1);
-#pragma unroll
-                for (int th = 0; th < 2; th++) {
-                    float p[4];
-#pragma unroll
-                    for (int i = 0; i < 4; i++) {
-                        p[i] = (mu[i] == -INFINITY) ? 0.f : exp2f(s[th][i] - mu[i]);
-                        lp[i] += p[i];
-                    }
-                    const uint2 pk = make_uint2(float_to_half_bits(p[0]) | (float_to_half_bits(p[1]) << 16),
-                                                float_to_half_bits(p[2]) | (float_to_half_bits(p[3]) << 16));
-                    *reinterpret_cast<uint2*>(pbuf + (16 * th + l16) * HQ + 16 * wave + 4 * g4) = pk;
-                }
-            }
-            __syncthreads();
-
-            // ---- 3. O += P Y for this wave's channels ----
-            if (rescale_flag) {
-#pragma unroll
-                for (int hb = 0; hb < HB; hb++)
-#pragma unroll
-                    for (int i = 0; i < 4; i++) {
-                        const float al = alpha[16 * hb + 4 * g4 + i];
-#pragma unroll
-                        for (int c = 0; c < CBW; c++) O[hb][c][i] *= al;
-                    }
-            }
-            {
-                // tr16: lane 4k + q of a 16-lane group reads row k, columns 4q .. 4q+3;
-                // lane j receives column j of the 4 rows.  Rows are tokens.
-                const int row = 8 * g4 + (l16 >> 2), colq = 4 * (l16 & 3);
-                h8 bv[CBW];  // Y[32 tokens][16 channels]: lane channel l16, tokens 8*g4 .. +7
-#pragma unroll
-                for (int c = 0; c < CBW; c++) {
-                    const int ch = CPW * wave + 16 * c;
-                    bv[c] = cat(tr16(ybuf + row * MD + ch + colq), tr16(ybuf + (row + 4) * MD + ch + colq));
-                }
-#pragma unroll
-                for (int hb = 0; hb < HB; hb++) {
-                    // P[16 heads][32 tokens]: lane head l16, tokens 8*g4 .. +7
-                    const h8 pa = cat(tr16(pbuf + row * HQ + 16 * hb + colq), tr16(pbuf + (row + 4) * HQ + 16 * hb + colq));
-#pragma unroll
-                    for (int c = 0; c < CBW; c++) O[hb][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, bv[c], O[hb][c], 0, 0, 0);
-                }
-            }
-            __syncthreads();
         }
+        __syncthreads();
+        if (ci + 1 < nch) prefetch(ci + 1);
+
+        // ---- 2. scores and weights for this wave's 16 heads ----
+        if (tid == 0) rescale_flag = 0;
+        bool need = false;
+        float s[2][4], cmax[4];
+        if (qk_wave) {
+            // four independent accumulation chains per token half keep the MFMA
+            // pipeline busy for a lone wave; summed afterwards
+            f4 sacc[2];
+#pragma unroll
+            for (int th = 0; th < 2; th++) {
+                f4 part4[4] = {f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f},
+                               f4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+                for (int ks = 0; ks < 16; ks++) {
+                    const h8 by = *reinterpret_cast<const h8*>(ybuf + (16 * th + l16) * MD + 32 * ks + 8 * g4);
+                    part4[ks & 3] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[ks], by, part4[ks & 3], 0, 0, 0);
+                    if ((ks & 3) == 3) __builtin_amdgcn_sched_barrier(0);  // bound operand prefetch
+                }
+                sacc[th] = (part4[0] + part4[1]) + (part4[2] + part4[3]);
+            }
+            // lane: heads 16*wave + 4*g4 + i, tokens c0 + 16*th + l16
+#pragma unroll
+            for (int th = 0; th < 2; th++) {
+                const bool valid = page * T + c0 + 16 * th + l16 < L;
+#pragma unroll
+                for (int i = 0; i < 4; i++) s[th][i] = valid ? sacc[th][i] * sm2 : -INFINITY;
+            }
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                cmax[i] = rmax16(fmaxf(s[0][i], s[1][i]));
+                need |= cmax[i] > mu[i] + kLazy;
+            }
+        }
+        __syncthreads();
+        if (qk_wave) {
+            const bool any = __builtin_amdgcn_ballot_w64(need) != 0;
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                float al = 1.f;
+                if (any) {
+                    const float mn = fmaxf(mu[i], cmax[i]);
+                    al = (mu[i] == -INFINITY) ? 0.f : exp2f(mu[i] - mn);
+                    lp[i] *= al;
+                    mu[i] = mn;
+                }
+                if (l16 == 0) alpha[16 * wave + 4 * g4 + i] = al;
+            }
+            if (any && lane == 0) atomicOr(&rescale_flag, 1);
+#pragma unroll
+            for (int th = 0; th < 2; th++) {
+                float p[4];
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    p[i] = (mu[i] == -INFINITY) ? 0.f : exp2f(s[th][i] - mu[i]);
+                    lp[i] += p[i];
+                }
+                const uint2 pk = make_uint2(float_to_half_bits(p[0]) | (float_to_half_bits(p[1]) << 16),
+                                            float_to_half_bits(p[2]) | (float_to_half_bits(p[3]) << 16));
+                *reinterpret_cast<uint2*>(pbuf + (16 * th + l16) * HQ + 16 * wave + 4 * g4) = pk;
+            }
+        }
+        __syncthreads();
+
+        // ---- 3. O += P Y for this wave's channels ----
+        if (rescale_flag) {
+#pragma unroll
+            for (int hb = 0; hb < HB; hb++)
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    const float al = alpha[16 * hb + 4 * g4 + i];
+#pragma unroll
+                    for (int c = 0; c < CBW; c++) O[hb][c][i] *= al;
+                }
+        }
+        {
+            // tr16: lane 4k + q of a 16-lane group reads row k, columns 4q .. 4q+3;
+            // lane j receives column j of the 4 rows.  Rows are tokens.
+            const int row = 8 * g4 + (l16 >> 2), colq = 4 * (l16 & 3);
+            h8 bv[CBW];  // Y[32 tokens][16 channels]: lane channel l16, tokens 8*g4 .. +7
+#pragma unroll
+            for (int c = 0; c < CBW; c++) {
+                const int ch = CPW * wave + 16 * c;
+                bv[c] = cat(tr16(ybuf + row * MD + ch + colq), tr16(ybuf + (row + 4) * MD + ch + colq));
+            }
+#pragma unroll
+            for (int hb = 0; hb < HB; hb++) {
+                // P[16 heads][32 tokens]: lane head l16, tokens 8*g4 .. +7
+                const h8 pa = cat(tr16(pbuf + row * HQ + 16 * hb + colq), tr16(pbuf + (row + 4) * HQ + 16 * hb + colq));
+#pragma unroll
+                for (int c = 0; c < CBW; c++) O[hb][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, bv[c], O[hb][c], 0, 0, 0);
+            }
+        }
+        __syncthreads();
     }
 
     // ---- partial results: m, l per head; O rows for this wave's channels ----
