@@ -24,7 +24,10 @@ FLAGS = [
 EXTRA = {"quantize_d128.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"],
          "quantize_d256.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"],
          "quantize_d512.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"],
-         "decode_mla.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"]}
+         "decode_mla.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee",
+                            # keep MFMA accumulators in ordinary VGPRs: the loop-carried
+                            # output tile is otherwise copied to and from AGPRs every chunk
+                            "-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def sources():

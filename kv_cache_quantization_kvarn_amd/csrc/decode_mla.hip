@@ -28,6 +28,7 @@ namespace {
 
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef short s4 __attribute__((ext_vector_type(4)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 
@@ -42,6 +43,24 @@ __device__ __forceinline__ h4 tr16(const void* p) {
     s4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS(s4, p));
     return __builtin_bit_cast(h4, v);
 }
+
+// LDS layout of a read-back chunk: token rows of YROW bytes (512 halves + 32
+// bytes of pad); the 16-byte unit u of token t sits at unit
+// u ^ ((u >> 3) & 7) ^ tswz(t) of its row.  With that, the score operand
+// reads (16 tokens, one unit), the transposed value reads (4 tokens, two
+// units, per 16 lanes), and the read-back stores (8 units of one token per 8
+// lanes, tokens t and t + 8 per 16 lanes) each touch every LDS bank once.
+constexpr int YROW = 2 * 512 + 32;
+__device__ __forceinline__ int uswz(int u) { return u ^ ((u >> 3) & 7); }
+__device__ __forceinline__ int tswz(int t) { return ((t >> 2) & 1) | (((t >> 3) & 1) << 3); }
+__device__ __forceinline__ int yoff(int t, int u) { return t * YROW + ((uswz(u) ^ tswz(t)) << 4); }
+// Within a 16-byte unit the eight channels are held in the order
+// 0,4,1,5,2,6,3,7 (the order in which packed nibbles unpack to fp16 pairs);
+// position p holds channel upos(p).
+__device__ __forceinline__ int upos(int p) { return (p >> 1) + 4 * (p & 1); }
+// weights: token rows of 160 bytes, with 128 more bytes after every 8 rows
+__device__ __forceinline__ int poff(int t) { return t * 160 + (t >> 3) * 128; }
+constexpr int PBYTES = 31 * 160 + 3 * 128 + 128;
 
 __device__ __forceinline__ h8 cat(h4 a, h4 b) {
     return h8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
@@ -113,10 +132,11 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
     constexpr int WS = MD + 4;                     // partial: m, l, pad, pad, O[512]
     constexpr int TPT = NT / CH;                   // threads per token in the read-back
     constexpr int CPT = MD / TPT;                  // channels per thread in the read-back
-    __shared__ __attribute__((aligned(16))) _Float16 ybuf[CH * MD];   // chunk, rotated basis
-    __shared__ __attribute__((aligned(16))) _Float16 pbuf[CH * HQ];   // weights [token][head]
+    static_assert(HQ * 2 <= 160, "weight rows hold at most 64 heads");
+    __shared__ __attribute__((aligned(16))) uint8_t ybuf[CH * YROW];   // chunk, rotated basis (fp16)
+    __shared__ __attribute__((aligned(16))) uint8_t pbuf[PBYTES];      // weights [token][head] (fp16)
     __shared__ __attribute__((aligned(16))) h8 hpat[2][2][64];
-    __shared__ __attribute__((aligned(16))) _Float16 cbuf[2][MD];     // column scales, by page parity
+    __shared__ __attribute__((aligned(16))) uint4 cbuf[2][MD / 8];    // column scales (units uswz), by page parity
     __shared__ float alpha[HQ];
     __shared__ int rescale_flag;
 
@@ -144,7 +164,8 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
     for (int ks = 0; ks < 16; ks++) {
         if (qk_wave) {
             const _Float16* p = qr + ((int64_t)b * a.Hq + h0 + wave * 16 + l16) * MD + 32 * ks + 8 * g4;
-            qa[ks] = *reinterpret_cast<const h8*>(p);
+            const h8 v = *reinterpret_cast<const h8*>(p);
+            qa[ks] = h8{v[0], v[4], v[1], v[5], v[2], v[6], v[3], v[7]};  // unit order
         } else {
             qa[ks] = h8{0, 0, 0, 0, 0, 0, 0, 0};
         }
@@ -191,7 +212,10 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
     // staged per page in LDS (cbuf, two slots by page parity).
     constexpr int CPP = T / CH;
     const int nch = pend > pbeg ? (min(pend * T, L) - pbeg * T + CH - 1) / CH : 0;
-    const int tt = tid / TPT, part = tid % TPT;  // read-back: token, CPT-channel part
+    // read-back: token tt, channels CPT*part .. +CPT; lanes 8..15 of each 16 take token tt + 8
+    static_assert(TPT == 8 && CPT == 64, "read-back mapping assumes 8 threads per token");
+    const int tt = ((tid >> 3) & 1) * 8 + ((tid >> 4) & 3) + 4 * (wave & 1) + 16 * (wave >> 1);
+    const int part = tid & 7;
     uint4 pf_code[CPT / 32];
     uint32_t pf_sz = 0;
     uint4 pf_c = make_uint4(0u, 0u, 0u, 0u);
@@ -231,9 +255,13 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
         }
         // ---- 1. chunk -> ybuf (rotated basis, fp16) ----
         if (quant) {
-            _Float16* cb = cbuf[page & 1];
+            uint4* cb = cbuf[page & 1];
             if (c0 == 0) {
-                if (tid < MD / 8) reinterpret_cast<uint4*>(cb)[tid] = pf_c;
+                if (tid < MD / 8)  // channels 8*tid .. +7 as pairs (0,4) (1,5) (2,6) (3,7)
+                    cb[uswz(tid)] = make_uint4(__builtin_amdgcn_perm(pf_c.z, pf_c.x, 0x05040100u),
+                                               __builtin_amdgcn_perm(pf_c.z, pf_c.x, 0x07060302u),
+                                               __builtin_amdgcn_perm(pf_c.w, pf_c.y, 0x05040100u),
+                                               __builtin_amdgcn_perm(pf_c.w, pf_c.y, 0x07060302u));
                 __syncthreads();
             }
             uint32_t cw[CPT / 8];
@@ -242,24 +270,25 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
                 cw[4 * k] = pf_code[k].x; cw[4 * k + 1] = pf_code[k].y;
                 cw[4 * k + 2] = pf_code[k].z; cw[4 * k + 3] = pf_code[k].w;
             }
-            const float S = half_bits_to_float(pf_sz & 0xffffu), Z = half_bits_to_float(pf_sz >> 16);
-            const uint4* cc = reinterpret_cast<const uint4*>(cb + CPT * part);
-            uint32_t out[CPT / 2];
+            // y = C (S c + Zp) in packed fp16: nibbles k and k + 4 of a code word
+            // become the pair (1024 + c, 1024 + c') by or-ing in the exponent of 1024
+            const h2 S2 = __builtin_bit_cast(h2, (pf_sz & 0xffffu) * 0x10001u);
+            const h2 Z2 = __builtin_bit_cast(h2, (pf_sz >> 16) * 0x10001u);
+            const h2 k1024 = h2{(_Float16)1024.0f, (_Float16)1024.0f};
 #pragma unroll
             for (int q8 = 0; q8 < CPT / 8; q8++) {
-                const uint4 cv = cc[q8];  // column scales of channels CPT*part + 8*q8 .. +8
+                const uint4 cv = cb[uswz(8 * part + q8)];  // column scales of unit 8*part + q8, pair order
                 const uint32_t cs[4] = {cv.x, cv.y, cv.z, cv.w};
                 const uint32_t w = cw[q8];
+                uint32_t o[4];
 #pragma unroll
                 for (int k = 0; k < 4; k++) {
-                    const float y0 = half_bits_to_float(cs[k] & 0xffffu) * fmaf(S, (float)((w >> (8 * k)) & 15u), Z);
-                    const float y1 = half_bits_to_float(cs[k] >> 16) * fmaf(S, (float)((w >> (8 * k + 4)) & 15u), Z);
-                    out[4 * q8 + k] = float_to_half_bits(y0) | (float_to_half_bits(y1) << 16);
+                    const h2 c = __builtin_bit_cast(h2, ((w >> (4 * k)) & 0x000F000Fu) | 0x64006400u) - k1024;
+                    const h2 y = __builtin_elementwise_fma(c, S2, Z2) * __builtin_bit_cast(h2, cs[k]);
+                    o[k] = __builtin_bit_cast(uint32_t, y);
                 }
+                *reinterpret_cast<uint4*>(ybuf + yoff(tt, 8 * part + q8)) = make_uint4(o[0], o[1], o[2], o[3]);
             }
-            uint4* dst = reinterpret_cast<uint4*>(ybuf + tt * MD + CPT * part);
-#pragma unroll
-            for (int k = 0; k < CPT / 8; k++) dst[k] = make_uint4(out[4 * k], out[4 * k + 1], out[4 * k + 2], out[4 * k + 3]);
         } else {
                 // y_t = H x_t / sqrt(512): Y^T = H X^T on the MFMA, the B operand read
             // straight from the fp16 page (8 channels of one token per lane).
@@ -290,11 +319,11 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
                 const bool tv = page * T + c0 + 16 * th + l16 < L;
 #pragma unroll
                 for (int m = 0; m < MBW; m++) {
-                    const f4 v = z[m];
-                    uint2 pk = make_uint2(float_to_half_bits(v[0] * rs) | (float_to_half_bits(v[1] * rs) << 16),
-                                          float_to_half_bits(v[2] * rs) | (float_to_half_bits(v[3] * rs) << 16));
-                    if (!tv) pk = make_uint2(0u, 0u);
-                    *reinterpret_cast<uint2*>(ybuf + (16 * th + l16) * MD + 16 * (MBW * wave + m) + 4 * g4) = pk;
+                    // channel 4*(g4&1) + i of unit 2*mb + (g4>>1) sits at position 2*i + (g4&1)
+                    uint8_t* dst = ybuf + yoff(16 * th + l16, 2 * (MBW * wave + m) + (g4 >> 1)) + 2 * (g4 & 1);
+#pragma unroll
+                    for (int i = 0; i < 4; i++)
+                        *reinterpret_cast<uint16_t*>(dst + 4 * i) = tv ? (uint16_t)float_to_half_bits(z[m][i] * rs) : (uint16_t)0;
                 }
             }
         }
@@ -315,7 +344,7 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
                                f4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
                 for (int ks = 0; ks < 16; ks++) {
-                    const h8 by = *reinterpret_cast<const h8*>(ybuf + (16 * th + l16) * MD + 32 * ks + 8 * g4);
+                    const h8 by = *reinterpret_cast<const h8*>(ybuf + yoff(16 * th + l16, 4 * ks + g4));
                     part4[ks & 3] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[ks], by, part4[ks & 3], 0, 0, 0);
                     if ((ks & 3) == 3) __builtin_amdgcn_sched_barrier(0);  // bound operand prefetch
                 }
@@ -359,7 +388,7 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
                 }
                 const uint2 pk = make_uint2(float_to_half_bits(p[0]) | (float_to_half_bits(p[1]) << 16),
                                             float_to_half_bits(p[2]) | (float_to_half_bits(p[3]) << 16));
-                *reinterpret_cast<uint2*>(pbuf + (16 * th + l16) * HQ + 16 * wave + 4 * g4) = pk;
+                *reinterpret_cast<uint2*>(pbuf + poff(16 * th + l16) + 32 * wave + 8 * g4) = pk;
             }
         }
         __syncthreads();
@@ -378,17 +407,17 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
         {
             // tr16: lane 4k + q of a 16-lane group reads row k, columns 4q .. 4q+3;
             // lane j receives column j of the 4 rows.  Rows are tokens.
-            const int row = 8 * g4 + (l16 >> 2), colq = 4 * (l16 & 3);
+            const int row = 8 * g4 + (l16 >> 2), q4 = l16 & 3;
             h8 bv[CBW];  // Y[32 tokens][16 channels]: lane channel l16, tokens 8*g4 .. +7
 #pragma unroll
             for (int c = 0; c < CBW; c++) {
-                const int ch = CPW * wave + 16 * c;
-                bv[c] = cat(tr16(ybuf + row * MD + ch + colq), tr16(ybuf + (row + 4) * MD + ch + colq));
+                const int u = (CPW * wave + 16 * c) / 8 + (q4 >> 1), hb8 = 8 * (q4 & 1);
+                bv[c] = cat(tr16(ybuf + yoff(row, u) + hb8), tr16(ybuf + yoff(row + 4, u) + hb8));
             }
 #pragma unroll
             for (int hb = 0; hb < HB; hb++) {
                 // P[16 heads][32 tokens]: lane head l16, tokens 8*g4 .. +7
-                const h8 pa = cat(tr16(pbuf + row * HQ + 16 * hb + colq), tr16(pbuf + (row + 4) * HQ + 16 * hb + colq));
+                const h8 pa = cat(tr16(pbuf + poff(row) + 32 * hb + 8 * q4), tr16(pbuf + poff(row + 4) + 32 * hb + 8 * q4));
 #pragma unroll
                 for (int c = 0; c < CBW; c++) O[hb][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, bv[c], O[hb][c], 0, 0, 0);
             }
@@ -413,7 +442,7 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
         for (int i = 0; i < 4; i++) {
             float* o = wsp + (((int64_t)b * a.Hq + h0 + 16 * hb + 4 * g4 + i) * a.nsplit + split) * WS + 4;
 #pragma unroll
-            for (int c = 0; c < CBW; c++) o[CPW * wave + 16 * c + l16] = O[hb][c][i];
+            for (int c = 0; c < CBW; c++) o[CPW * wave + 16 * c + 8 * (l16 >> 3) + upos(l16 & 7)] = O[hb][c][i];
         }
 }
 
