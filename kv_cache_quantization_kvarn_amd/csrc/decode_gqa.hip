@@ -2,20 +2,31 @@
 //
 // The records are never dequantized to memory (evermx.com KVarN review,
 // method paragraph: scales folded back in at read time).  With the rotated
-// query q' = H q and, per record, the column scales C, per-token scale S_t
-// and zero-point Zp_t:
+// query q' = H q / sqrt(D) and, per record, the column scales C, per-token
+// scale S_t and zero-point Zp_t:
 //   score_t  = <q, k_t> = S_t <q' * C, code_t> + Zp_t * sum(q' * C)
-//   sum_t p_t v_t = H ( C_V * ( sum_t (p_t S_t) code_t + sum_t p_t Zp_t ) )
+//   sum_t p_t v_t = H ( C_V * ( sum_t (p_t S_t) code_t + sum_t p_t Zp_t ) ) / sqrt(D)
 // so each split accumulates the value sum in the rotated basis and the
 // combine applies H once.  fp16 sink and tail pages (gmlx "KV cache
 // quantization", "The two schemes") are accumulated in the original basis
 // into a second sum that the combine adds after the rotation.
 //
-// Split kernel: one workgroup of four waves per (split, KV head, sequence);
-// each wave walks 64-token groups of the split's pages with its own online
-// softmax, and the waves are merged through LDS at the end.  Scores use
-// lane = token; value sums use lane = channel (channels CPL*lane .. +CPL-1).
+// Both contractions of a quantized page run on the 4x4x4 fp16 MFMA with 16
+// blocks: the four query heads of a KV head are its 4 rows, and one operand
+// is broadcast from one block to all 16 (CBSZ = 4, ABID = the block), so a
+// wave covers 64 tokens (scores, lane = token) or 64 channels (values,
+// lane = channel) per instruction.  A B-bit code c enters the MFMA as the
+// fp16 number 1 + c / 2^B, made by or-ing the code into the mantissa of 1.0;
+// the constant part is taken back out with sum(q' * C) and sum(p (Zp - 2^B S)).
+// The other operand (a query, the query times C, or the weights times S) is
+// split into fp16 high and low parts, two MFMAs on the same codes, so the
+// products keep fp32 accuracy.
+//
+// One wave per workgroup per (split, KV head, sequence); split s visits pages
+// s, s + nsplit, ..., so the fp16 pages at both ends spread over the splits.
 #include <math.h>
+
+#include <utility>
 
 #include "kvarn_device.hpp"
 #include "kvarn_internal.hpp"
@@ -23,7 +34,26 @@
 namespace kvarn {
 namespace {
 
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+
 constexpr float kLog2e = 1.4426950408889634f;
+
+// 4x4x4 fp16 MFMA with 16 blocks, operand A broadcast from block ABID
+template <int ABID>
+__device__ __forceinline__ f4 mfma_bcast(h4 a, h4 b, f4 c) {
+    return __builtin_amdgcn_mfma_f32_4x4x4f16(a, b, c, 4, ABID, 0);
+}
+
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+// f(integral_constant<int, i>) for i = 0 .. N-1, unrolled at compile time
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 __device__ __forceinline__ void wave_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -31,231 +61,349 @@ __device__ __forceinline__ void wave_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// code k of a little-endian LSB-first stream held in 32-bit words w[]
+// ---- packed codes as MFMA operands ----------------------------------------
+// The 4 k-slots of operand i hold codes code_of<B>(i, k) of an LSB-first
+// stream.  For B = 2 and 4 a 32-bit word holds codes s and s + 16/B in its
+// two 16-bit halves, so a pair is one shift and one and-or; the k order
+// follows the pairs.  6-bit codes are taken in stream order.
 template <int B>
-__device__ __forceinline__ uint32_t code_at(const uint32_t* w, int k) {
-    const int bit = k * B;
-    const int wd = bit >> 5, off = bit & 31;
-    uint32_t v = w[wd] >> off;
-    if (off + B > 32) v |= w[wd + 1] << (32 - off);
-    return v & ((1u << B) - 1u);
+__host__ __device__ constexpr int code_of(int i, int k) {
+    if constexpr (B == 4) return 8 * (i >> 1) + 2 * (i & 1) + (k >> 1) + 4 * (k & 1);
+    else if constexpr (B == 2) return 16 * (i >> 2) + 2 * (i & 3) + (k >> 1) + 8 * (k & 1);
+    else return 4 * i + k;
+}
+
+// position 4 i + k of stream code n (inverse of code_of)
+template <int B>
+__device__ __forceinline__ int pos_of(int n) {
+    if constexpr (B == 4) {
+        const int u = n & 7;
+        return 4 * (2 * (n >> 3) + ((u & 3) >> 1)) + (((u & 1) << 1) | (u >> 2));
+    } else if constexpr (B == 2) {
+        const int u = n & 15;
+        return 4 * (4 * (n >> 4) + ((u & 7) >> 1)) + (((u & 1) << 1) | (u >> 3));
+    } else {
+        return n;
+    }
+}
+
+// fp16 pair (1 + c_s / 2^B, 1 + c_{s + 16/B} / 2^B) from word w, B = 2 or 4
+template <int B>
+__device__ __forceinline__ uint32_t code_pair(uint32_t w, int s) {
+    constexpr uint32_t mask = B == 4 ? 0x03C003C0u : 0x03000300u;
+    const int sh = (10 - B) - B * s;  // code s to mantissa bits 10-B .. 9
+    const uint32_t v = sh >= 0 ? (w << sh) : (w >> -sh);
+    return (v & mask) | 0x3C003C00u;
+}
+
+// operand i (4 codes, as 1 + c / 2^B) from the words w[] of a stream segment
+template <int B>
+__device__ __forceinline__ h4 code_operand(const uint32_t* w, int i) {
+    uint32_t lo, hi;
+    if constexpr (B == 4) {
+        const uint32_t x = w[i >> 1];
+        lo = code_pair<4>(x, 2 * (i & 1));
+        hi = code_pair<4>(x, 2 * (i & 1) + 1);
+    } else if constexpr (B == 2) {
+        const uint32_t x = w[i >> 2];
+        lo = code_pair<2>(x, 2 * (i & 3));
+        hi = code_pair<2>(x, 2 * (i & 3) + 1);
+    } else {
+        // 16 codes in 3 words; operand i takes bits 24 (i & 3) .. +23 of group i >> 2
+        const int g = 3 * (i >> 2), e = i & 3;
+        const int bit = 24 * e;
+        const uint32_t f = (bit & 31) + 24 <= 32 ? (w[g + (bit >> 5)] >> (bit & 31))
+                                                : __builtin_amdgcn_alignbit(w[g + (bit >> 5) + 1], w[g + (bit >> 5)], bit & 31);
+        lo = ((f << 4) & 0x3F0u) | ((f << 14) & 0x03F00000u) | 0x3C003C00u;
+        hi = ((f >> 8) & 0x3F0u) | ((f << 2) & 0x03F00000u) | 0x3C003C00u;
+    }
+    return __builtin_bit_cast(h4, make_uint2(lo, hi));
+}
+
+__device__ __forceinline__ void load_words(uint32_t* w, const uint8_t* p, int nbytes16) {
+#pragma unroll
+    for (int k = 0; k < nbytes16; k++) {
+        const uint4 v = reinterpret_cast<const uint4*>(p)[k];
+        w[4 * k] = v.x; w[4 * k + 1] = v.y; w[4 * k + 2] = v.z; w[4 * k + 3] = v.w;
+    }
+}
+
+// sum over the 16 lanes of one residue class mod 4 within each 32-lane half
+__device__ __forceinline__ float sum_blocks_half(float v) {
+    v += i2f(__builtin_amdgcn_update_dpp(0, f2i(v), 0x124, 0xF, 0xF, true));  // row_ror 4
+    v += i2f(__builtin_amdgcn_update_dpp(0, f2i(v), 0x128, 0xF, 0xF, true));  // row_ror 8
+    v += xor_lane<4>(v);
+    return v;
 }
 
 template <int D, int T, int KB, int VB>
-__global__ void __launch_bounds__(256) decode_split_kernel(DecodeArgs a) {
+__global__ void __launch_bounds__(64) decode_split_kernel(DecodeArgs a) {
     constexpr int G = 4;
-    constexpr int NWV = 4;
-    constexpr int CPL = D / 64;   // channels per lane in the value sums
-    constexpr int GPP = T / 64;   // 64-token groups per page
+    constexpr int NS = D / 64;            // operand slots per lane; value channel sets
+    constexpr int NC = D / 128;           // 128-channel chunks of a key row
+    constexpr int TS = T / 64;            // 64-token sub-blocks of a page
     constexpr int KCB = T * D * KB / 8;
     constexpr int VCB = T * D * VB / 8;
     constexpr int KREC = KCB + 4 * T + 2 * D;
     constexpr int VREC = VCB + 4 * T + 2 * D;
-    constexpr int KROW = D * KB / 8;            // code bytes of one token (token-major K)
-    constexpr int SCB = (KB == 6) ? 48 : 16;    // bytes per inner chunk
-    constexpr int SCC = SCB * 8 / KB;           // codes per inner chunk
-    constexpr int VCH = 64 * VB / 8;            // code bytes of one channel over 64 tokens
+    constexpr int KROW = D * KB / 8;      // code bytes of one token
+    constexpr int KCH = 128 * KB / 8;     // code bytes of a 128-channel chunk
+    constexpr int VROW = T * VB / 8;      // code bytes of one channel
+    constexpr int CPL = D / 64;           // fp16 values: channels per lane
     constexpr int WS = 2 * D + 4;
+    constexpr float FK = (float)(1 << KB), FV = (float)(1 << VB);
+    static_assert(KCH % 16 == 0 && VROW % 16 == 0, "16-byte code segments");
 
-    __shared__ float4 qrot[D];        // rotated query (4 heads per channel)
-    __shared__ float4 qpl[D];         // plain query
-    __shared__ float4 qt[NWV][D];     // per wave: rotated query times column scales
-    __shared__ float4 pp[NWV][64];    // per wave: softmax weights (times S for records)
-    __shared__ float mlbuf[NWV][2 * G];
-    __shared__ float abuf[2][G][2 * D];
+    __shared__ __attribute__((aligned(16))) _Float16 pt[2][G][64];  // p * S_V of a sub-block (high, low), by operand position
+    __shared__ float4 pf[64];                                    // weights of an fp16 sub-block
 
     const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lane = threadIdx.x;
+    const int blk = lane >> 2, m = lane & 3;  // MFMA block; row (query head) of the broadcast operand
     const int Hq = a.Hq;
-    const float sm2 = a.sm_scale * kLog2e;   // scores in log2 units
+    const float sm2 = a.sm_scale * kLog2e;
 
-    // ---- query: load 4 heads, rotate (unnormalized butterflies in LDS) ----
-    float* qr = reinterpret_cast<float*>(qrot);
-    float* qp = reinterpret_cast<float*>(qpl);
-    for (int e = tid; e < G * D; e += 256) {
-        const int g = e / D, j = e - g * D;
-        const int64_t idx = ((int64_t)b * Hq + h * G + g) * D + j;
-        float v;
-        if (a.q_bf16) v = __builtin_bit_cast(float, ((uint32_t)static_cast<const uint16_t*>(a.q)[idx]) << 16);
-        else v = static_cast<const float*>(a.q)[idx];
-        qp[j * G + g] = v;
-        qr[j * G + g] = v;
-    }
-    __syncthreads();
-    for (int hs = 1; hs < D; hs <<= 1) {
-        for (int e = tid; e < G * D / 2; e += 256) {
-            const int g = e / (D / 2), k = e - g * (D / 2);
-            const int i0 = (k / hs) * 2 * hs + (k % hs), i1 = i0 + hs;
-            const float x = qr[i0 * G + g], y = qr[i1 * G + g];
-            qr[i0 * G + g] = x + y;
-            qr[i1 * G + g] = x - y;
+    // rotated query (fp32) at the channels of this lane's operand slots, and
+    // the plain query (fp16) for fp16 pages.  Slot r serves operand
+    // 32 (r >> 1) + blk + 16 (r & 1) of the scores.
+    const float* qr = a.ws + ((int64_t)b * Hq + h * G + m) * D;
+    float qv[NS][4];
+    h4 qp[NS], qpl[NS];
+#pragma unroll
+    for (int r = 0; r < NS; r++) {
+        const int i = 32 * (r >> 1) + blk + 16 * (r & 1);
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+            qv[r][k] = qr[code_of<KB>(i, k)];
+            const int64_t idx = ((int64_t)b * Hq + h * G + m) * D + 4 * i + k;
+            const float x = a.q_bf16 ? __builtin_bit_cast(float, ((uint32_t) static_cast<const uint16_t*>(a.q)[idx]) << 16)
+                                     : static_cast<const float*>(a.q)[idx];
+            qp[r][k] = (_Float16)x;
+            qpl[r][k] = (_Float16)(x - (float)qp[r][k]);
         }
-        __syncthreads();
     }
-    const float rs = 1.0f / sqrtf((float)D);
-    for (int e = tid; e < G * D; e += 256) qr[e] *= rs;
-    __syncthreads();
 
-    // ---- walk the split's 64-token groups ----------------------------------
-    // a length beyond the page table is clamped to it (never read past a row)
     const int L = min(a.seq_lens[b], a.max_pages * T);
     const int npages = L > 0 ? (L + T - 1) / T : 0;
     const int nq = (L - a.sink - a.tail >= T) ? (L - a.sink - a.tail) / T : 0;
     const int sp = a.sink / T;
-    const int pbeg = split * a.pps;
-    const int pend = min(pbeg + a.pps, npages);
-    const int ngroups = pend > pbeg ? (pend - pbeg) * GPP : 0;
 
-    float m[G], l[G], accr[G][CPL], accp[G][CPL];
+    float mrun[G], lp[G], accr[NS][G], accp[CPL][G];
 #pragma unroll
     for (int g = 0; g < G; g++) {
-        m[g] = -INFINITY;
-        l[g] = 0.f;
+        mrun[g] = -INFINITY;
+        lp[g] = 0.f;
 #pragma unroll
-        for (int c = 0; c < CPL; c++) accr[g][c] = accp[g][c] = 0.f;
+        for (int s = 0; s < NS; s++) accr[s][g] = 0.f;
+#pragma unroll
+        for (int c = 0; c < CPL; c++) accp[c][g] = 0.f;
     }
 
-    for (int gi = wave; gi < ngroups; gi += NWV) {
-        const int page = pbeg + gi / GPP;
-        const int half = gi % GPP;
-        const int tip = half * 64 + lane;          // token within the page
-        const bool valid = page * T + tip < L;
+    // Steps: (page, 64-token sub-block) of this split's pages, in order.  The
+    // key words, token scale words and column scales of the next quantized
+    // step are loaded while the current step runs; a step's value words are
+    // loaded before its scores, so they arrive during the score MFMAs.
+    constexpr int KW = KCH / 4;        // words of one 128-channel key chunk
+    constexpr int VW = 64 * VB / 32;   // value code words of one channel over 64 tokens
+    const int nst = npages > split ? ((npages - split + a.nsplit - 1) / a.nsplit) * TS : 0;
+    const uint8_t* const krec = static_cast<const uint8_t*>(a.k_records);
+    const uint8_t* const vrec = static_cast<const uint8_t*>(a.v_records);
+
+    uint32_t nkw[KW];
+    uint32_t nksz = 0, nvsz = 0;
+    uint16_t nck[NS][4], ncv[NS];
+#pragma unroll
+    for (int k = 0; k < KW; k++) nkw[k] = 0;
+#pragma unroll
+    for (int r = 0; r < NS; r++) {
+        ncv[r] = 0;
+#pragma unroll
+        for (int k = 0; k < 4; k++) nck[r][k] = 0;
+    }
+    auto prefetch = [&](int st) {
+        const int page = split + (st / TS) * a.nsplit, sb = st % TS;
+        if (!(page >= sp && page < sp + nq)) return;
+        const int id = a.block_table[(int64_t)b * a.max_pages + page];
+        if (id < 0 || (int64_t)id >= a.n_qpages) return;
+        const uint8_t* rk = krec + ((int64_t)id * a.H + h) * KREC;
+        const uint8_t* rv = vrec + ((int64_t)id * a.H + h) * VREC;
+        const int tok = 64 * sb + lane;
+        load_words(nkw, rk + (int64_t)tok * KROW, KW / 4);
+        nksz = reinterpret_cast<const uint32_t*>(rk + KCB)[tok];
+        nvsz = reinterpret_cast<const uint32_t*>(rv + VCB)[tok];
+        if (sb == 0) {
+            const uint16_t* ck = reinterpret_cast<const uint16_t*>(rk + KCB + 4 * T);
+            const uint16_t* cvp = reinterpret_cast<const uint16_t*>(rv + VCB + 4 * T);
+#pragma unroll
+            for (int r = 0; r < NS; r++) {
+                const int i = 32 * (r >> 1) + blk + 16 * (r & 1);
+#pragma unroll
+                for (int k = 0; k < 4; k++) nck[r][k] = ck[code_of<KB>(i, k)];
+                ncv[r] = cvp[64 * r + lane];
+            }
+        }
+    };
+    if (nst > 0) prefetch(0);
+
+    h4 qa[NS], qal[NS];  // score operands q' * C_K of the current page, high and low parts
+    float sq[G];         // their sums per head
+    float cvv[NS];       // value column scales of this lane's channels
+#pragma unroll
+    for (int g = 0; g < G; g++) sq[g] = 0.f;
+#pragma unroll
+    for (int r = 0; r < NS; r++) {
+        qa[r] = qal[r] = h4{0, 0, 0, 0};
+        cvv[r] = 0.f;
+    }
+
+    for (int st = 0; st < nst; st++) {
+        const int page = split + (st / TS) * a.nsplit, sb = st % TS;
         const bool quant = page >= sp && page < sp + nq;
         const int id = a.block_table[(int64_t)b * a.max_pages + page];
+        uint32_t kw[KW];
+#pragma unroll
+        for (int k = 0; k < KW; k++) kw[k] = nkw[k];
+        const uint32_t ksz = nksz, vsz = nvsz;
+        if (quant && sb == 0) {
+            // score operands of the new page and their per-head sums
+            float part = 0.f;
+#pragma unroll
+            for (int r = 0; r < NS; r++) {
+#pragma unroll
+                for (int k = 0; k < 4; k++) {
+                    const float x = qv[r][k] * half_bits_to_float(nck[r][k]);
+                    const _Float16 hi = (_Float16)x;
+                    const _Float16 lo = (_Float16)(x - (float)hi);
+                    qa[r][k] = hi;
+                    qal[r][k] = lo;
+                    part += (float)hi + (float)lo;
+                }
+                cvv[r] = half_bits_to_float(ncv[r]);
+            }
+            part = sum_blocks_half(part);  // lanes g and 32 + g hold the halves' sums for head g
+#pragma unroll
+            for (int g = 0; g < G; g++)
+                sq[g] = i2f(__builtin_amdgcn_readlane(f2i(part), g)) + i2f(__builtin_amdgcn_readlane(f2i(part), 32 + g));
+        }
+        if (st + 1 < nst) prefetch(st + 1);
         if (id < 0 || (quant ? (int64_t)id >= a.n_qpages : (int64_t)id >= a.n_fpages)) continue;
+        if (page * T + 64 * sb >= L) continue;  // no token of this sub-block is in the sequence
+        const int tok = 64 * sb + lane;
 
         float s[G];
-        const uint8_t* rv = nullptr;
+        const uint8_t* rk = krec + ((int64_t)id * a.H + h) * KREC;
+        const uint8_t* rv = vrec + ((int64_t)id * a.H + h) * VREC;
+        uint32_t vw[NS][VW];
         if (quant) {
-            const uint8_t* rk = static_cast<const uint8_t*>(a.k_records) + ((int64_t)id * a.H + h) * KREC;
-            rv = static_cast<const uint8_t*>(a.v_records) + ((int64_t)id * a.H + h) * VREC;
-            // fold the key column scales into the rotated query
-            const uint16_t* ck = reinterpret_cast<const uint16_t*>(rk + KCB + 4 * T);
-            float sq[G] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int c = 0; c < CPL; c++) {
-                const int j = CPL * lane + c;
-                const float cj = half_bits_to_float(ck[j]);
-                const float4 qv = qrot[j];
-                const float4 t4 = make_float4(qv.x * cj, qv.y * cj, qv.z * cj, qv.w * cj);
-                qt[wave][j] = t4;
-                sq[0] += t4.x; sq[1] += t4.y; sq[2] += t4.z; sq[3] += t4.w;
-            }
+            for (int sv = 0; sv < NS; sv++)
+                load_words(vw[sv], rv + (int64_t)(64 * sv + lane) * VROW + sb * (64 * VB / 8), VW / 4);
+            f4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int g = 0; g < G; g++) sq[g] = wave_sum_all(sq[g]);
-            wave_sync();
-            float raw[G] = {0.f, 0.f, 0.f, 0.f};
-            const uint8_t* kc = rk + (int64_t)tip * KROW;
-#pragma unroll 1
-            for (int ch = 0; ch < D / SCC; ch++) {
-                uint32_t w[SCB / 4 + 1];
+            for (int c = 0; c < NC; c++) {
+                uint32_t w[KW];
+                if (c == 0) {
 #pragma unroll
-                for (int k = 0; k < SCB / 16; k++) {
-                    const uint4 v = reinterpret_cast<const uint4*>(kc + ch * SCB)[k];
-                    w[4 * k] = v.x; w[4 * k + 1] = v.y; w[4 * k + 2] = v.z; w[4 * k + 3] = v.w;
+                    for (int k = 0; k < KW; k++) w[k] = kw[k];
+                } else {
+                    load_words(w, rk + (int64_t)tok * KROW + c * KCH, KW / 4);
                 }
-                w[SCB / 4] = 0;
-#pragma unroll
-                for (int k = 0; k < SCC; k++) {
-                    const float cv = (float)code_at<KB>(w, k);
-                    const float4 qv = qt[wave][ch * SCC + k];
-                    raw[0] = fmaf(qv.x, cv, raw[0]);
-                    raw[1] = fmaf(qv.y, cv, raw[1]);
-                    raw[2] = fmaf(qv.z, cv, raw[2]);
-                    raw[3] = fmaf(qv.w, cv, raw[3]);
-                }
+                static_for<32>([&](auto ic) {
+                    constexpr int il = decltype(ic)::value;
+                    const h4 bop = code_operand<KB>(w, il);
+                    acc0 = mfma_bcast<il & 15>(qa[2 * c + (il >> 4)], bop, acc0);
+                    acc1 = mfma_bcast<il & 15>(qal[2 * c + (il >> 4)], bop, acc1);
+                });
             }
-            const uint32_t sz = reinterpret_cast<const uint32_t*>(rk + KCB)[tip];
-            const float S = half_bits_to_float(sz & 0xffffu), Z = half_bits_to_float(sz >> 16);
+            const f4 R = acc0 + acc1;
+            const float S = half_bits_to_float(ksz & 0xffffu), Z = half_bits_to_float(ksz >> 16);
+            const float fs = FK * S, zc = Z - fs;
 #pragma unroll
-            for (int g = 0; g < G; g++) s[g] = valid ? sm2 * fmaf(S, raw[g], Z * sq[g]) : -INFINITY;
+            for (int g = 0; g < G; g++) s[g] = sm2 * fmaf(fs, R[g], sq[g] * zc);
         } else {
-            const uint16_t* kp = static_cast<const uint16_t*>(a.k_fp16) +
-                                 (((int64_t)id * a.H + h) * T + tip) * D;
-            float raw[G] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
-            for (int ch = 0; ch < D / 8; ch++) {
-                const uint4 v = reinterpret_cast<const uint4*>(kp)[ch];
-                const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+            const bool valid = page * T + tok < L;
+            const uint16_t* kr = static_cast<const uint16_t*>(a.k_fp16) + (((int64_t)id * a.H + h) * T + tok) * D;
+            f4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int k = 0; k < 8; k++) {
-                    const float kv = half_bits_to_float((w[k >> 1] >> (16 * (k & 1))) & 0xffffu);
-                    const float4 qv = qpl[ch * 8 + k];
-                    raw[0] = fmaf(qv.x, kv, raw[0]);
-                    raw[1] = fmaf(qv.y, kv, raw[1]);
-                    raw[2] = fmaf(qv.z, kv, raw[2]);
-                    raw[3] = fmaf(qv.w, kv, raw[3]);
-                }
+            for (int c = 0; c < NC; c++) {
+                static_for<16>([&](auto ic) {
+                    constexpr int il = 2 * decltype(ic)::value;
+                    const uint4 v = *reinterpret_cast<const uint4*>(kr + 128 * c + 4 * il);
+                    const h4 b0 = __builtin_bit_cast(h4, make_uint2(v.x, v.y));
+                    const h4 b1 = __builtin_bit_cast(h4, make_uint2(v.z, v.w));
+                    acc0 = mfma_bcast<il & 15>(qp[2 * c + (il >> 4)], b0, acc0);
+                    acc1 = mfma_bcast<il & 15>(qpl[2 * c + (il >> 4)], b0, acc1);
+                    acc0 = mfma_bcast<(il + 1) & 15>(qp[2 * c + ((il + 1) >> 4)], b1, acc0);
+                    acc1 = mfma_bcast<(il + 1) & 15>(qpl[2 * c + ((il + 1) >> 4)], b1, acc1);
+                });
             }
+            const f4 R = acc0 + acc1;
 #pragma unroll
-            for (int g = 0; g < G; g++) s[g] = valid ? sm2 * raw[g] : -INFINITY;
+            for (int g = 0; g < G; g++) s[g] = valid ? sm2 * R[g] : -INFINITY;
         }
 
-        // ---- online softmax (log2 domain) ----
+        // ---- online softmax over this sub-block (log2 domain) ----
         float p[G];
 #pragma unroll
         for (int g = 0; g < G; g++) {
             const float mx = wave_max_all(s[g]);
-            const float mnew = fmaxf(m[g], mx);
-            float alpha;
-            if (mnew == -INFINITY) {
-                alpha = 1.f;
-                p[g] = 0.f;
-            } else {
-                alpha = exp2f(m[g] - mnew);
-                p[g] = valid ? exp2f(s[g] - mnew) : 0.f;
-            }
-            l[g] = fmaf(l[g], alpha, wave_sum_all(p[g]));
-            m[g] = mnew;
+            const float mnew = fmaxf(mrun[g], mx);  // finite: the sub-block holds a valid token
+            const float alpha = mrun[g] == -INFINITY ? 0.f : exp2f(mrun[g] - mnew);
+            mrun[g] = mnew;
+            lp[g] *= alpha;
 #pragma unroll
-            for (int c = 0; c < CPL; c++) {
-                accr[g][c] *= alpha;
-                accp[g][c] *= alpha;
-            }
+            for (int sv = 0; sv < NS; sv++) accr[sv][g] *= alpha;
+#pragma unroll
+            for (int c = 0; c < CPL; c++) accp[c][g] *= alpha;
+            p[g] = exp2f(s[g] - mnew);
+            lp[g] += p[g];
         }
 
         if (quant) {
-            const uint32_t szv = reinterpret_cast<const uint32_t*>(rv + VCB)[tip];
-            const float Sv = half_bits_to_float(szv & 0xffffu), Zv = half_bits_to_float(szv >> 16);
-            float z[G];
+            // weights times S_V (fp16 high and low parts) into LDS by operand
+            // position; the constant 1 of the code operands returns through
+            // sum (p Zp - 2^B p S)
+            const float S = half_bits_to_float(vsz & 0xffffu), Z = half_bits_to_float(vsz >> 16);
+            const int pos = pos_of<VB>(lane);
+            float e[G];
 #pragma unroll
-            for (int g = 0; g < G; g++) z[g] = wave_sum_all(p[g] * Zv);
-            pp[wave][lane] = make_float4(p[0] * Sv, p[1] * Sv, p[2] * Sv, p[3] * Sv);
-            wave_sync();
-            const uint16_t* cvp = reinterpret_cast<const uint16_t*>(rv + VCB + 4 * T);
-#pragma unroll
-            for (int c = 0; c < CPL; c++) {
-                const int j = CPL * lane + c;
-                const uint8_t* vc = rv + ((int64_t)j * T + half * 64) * VB / 8;
-                uint32_t w[VCH / 4 + 1];
-#pragma unroll
-                for (int k = 0; k < VCH / 16; k++) {
-                    const uint4 v = reinterpret_cast<const uint4*>(vc)[k];
-                    w[4 * k] = v.x; w[4 * k + 1] = v.y; w[4 * k + 2] = v.z; w[4 * k + 3] = v.w;
-                }
-                w[VCH / 4] = 0;
-                float ag[G] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int t = 0; t < 64; t++) {
-                    const float cv = (float)code_at<VB>(w, t);
-                    const float4 pv = pp[wave][t];
-                    ag[0] = fmaf(pv.x, cv, ag[0]);
-                    ag[1] = fmaf(pv.y, cv, ag[1]);
-                    ag[2] = fmaf(pv.z, cv, ag[2]);
-                    ag[3] = fmaf(pv.w, cv, ag[3]);
-                }
-                const float cj = half_bits_to_float(cvp[j]);
-#pragma unroll
-                for (int g = 0; g < G; g++) accr[g][c] = fmaf(cj, ag[g] + z[g], accr[g][c]);
+            for (int g = 0; g < G; g++) {
+                const float x = p[g] * S;
+                const _Float16 hi = (_Float16)x;
+                const _Float16 lo = (_Float16)(x - (float)hi);
+                pt[0][g][pos] = hi;
+                pt[1][g][pos] = lo;
+                e[g] = fmaf(p[g], Z, -FV * ((float)hi + (float)lo));
             }
-        } else {
-            pp[wave][lane] = make_float4(p[0], p[1], p[2], p[3]);
+            float E[G];
+#pragma unroll
+            for (int g = 0; g < G; g++) E[g] = wave_sum_all(e[g]);
             wave_sync();
+            const h4 pa = *reinterpret_cast<const h4*>(&pt[0][m][4 * blk]);
+            const h4 pal = *reinterpret_cast<const h4*>(&pt[1][m][4 * blk]);
+#pragma unroll
+            for (int sv = 0; sv < NS; sv++) {
+                f4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+                static_for<16>([&](auto ic) {
+                    constexpr int i = decltype(ic)::value;
+                    const h4 bop = code_operand<VB>(vw[sv], i);
+                    acc0 = mfma_bcast<i>(pa, bop, acc0);
+                    acc1 = mfma_bcast<i>(pal, bop, acc1);
+                });
+                const f4 R = acc0 + acc1;
+#pragma unroll
+                for (int g = 0; g < G; g++) accr[sv][g] = fmaf(cvv[sv], fmaf(FV, R[g], E[g]), accr[sv][g]);
+            }
+            wave_sync();  // pt is rewritten by the next step
+        } else {
+            pf[lane] = make_float4(p[0], p[1], p[2], p[3]);
+            wave_sync();
+            const int nvalid = min(64, L - page * T - 64 * sb);  // tokens past the end may hold anything
             const uint16_t* vp = static_cast<const uint16_t*>(a.v_fp16) +
-                                 (((int64_t)id * a.H + h) * T + half * 64) * D + CPL * lane;
+                                 (((int64_t)id * a.H + h) * T + 64 * sb) * D + CPL * lane;
 #pragma unroll 4
-            for (int t = 0; t < 64; t++) {
-                const float4 pv = pp[wave][t];
+            for (int t = 0; t < nvalid; t++) {
+                const float4 pv = pf[t];
                 float vv[CPL];
                 if constexpr (CPL == 2) {
                     const uint32_t w = *reinterpret_cast<const uint32_t*>(vp + (int64_t)t * D);
@@ -273,86 +421,54 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeArgs a) {
                 }
 #pragma unroll
                 for (int c = 0; c < CPL; c++) {
-                    accp[0][c] = fmaf(pv.x, vv[c], accp[0][c]);
-                    accp[1][c] = fmaf(pv.y, vv[c], accp[1][c]);
-                    accp[2][c] = fmaf(pv.z, vv[c], accp[2][c]);
-                    accp[3][c] = fmaf(pv.w, vv[c], accp[3][c]);
+                    accp[c][0] = fmaf(pv.x, vv[c], accp[c][0]);
+                    accp[c][1] = fmaf(pv.y, vv[c], accp[c][1]);
+                    accp[c][2] = fmaf(pv.z, vv[c], accp[c][2]);
+                    accp[c][3] = fmaf(pv.w, vv[c], accp[c][3]);
                 }
             }
+            wave_sync();
         }
-        wave_sync();
     }
 
-    // ---- merge the four waves ----------------------------------------------
-    if (lane == 0) {
-#pragma unroll
-        for (int g = 0; g < G; g++) {
-            mlbuf[wave][g] = m[g];
-            mlbuf[wave][G + g] = l[g];
-        }
-    }
-    __syncthreads();
-    float M[G], Ls[G];
+    // ---- partial of this split: m, l, rotated-basis and fp16 value sums ----
+    float* wsp = a.ws + (int64_t)a.B * Hq * D;
 #pragma unroll
     for (int g = 0; g < G; g++) {
-        float mm = -INFINITY;
-#pragma unroll
-        for (int w = 0; w < NWV; w++) mm = fmaxf(mm, mlbuf[w][g]);
-        float ll = 0.f;
-        if (mm != -INFINITY) {
-#pragma unroll
-            for (int w = 0; w < NWV; w++) ll += mlbuf[w][G + g] * exp2f(mlbuf[w][g] - mm);
+        const float lt = wave_sum_all(lp[g]);
+        float* o = wsp + (((int64_t)b * Hq + h * G + g) * a.nsplit + split) * WS;
+        if (lane == 0) {
+            o[0] = mrun[g];
+            o[1] = lt;
         }
-        M[g] = mm;
-        Ls[g] = ll;
-        const float sc = (m[g] == -INFINITY) ? 0.f : exp2f(m[g] - mm);
 #pragma unroll
-        for (int c = 0; c < CPL; c++) {
-            accr[g][c] *= sc;
-            accp[g][c] *= sc;
-        }
+        for (int sv = 0; sv < NS; sv++) o[4 + 64 * sv + lane] = accr[sv][g];
+#pragma unroll
+        for (int c = 0; c < CPL; c++) o[4 + D + CPL * lane + c] = accp[c][g];
     }
-    // tree: waves 2,3 -> 0,1; then 1 -> 0
-#pragma unroll
-    for (int round = 0; round < 2; round++) {
-        const int lo = round == 0 ? 2 : 1;
-        const int hi = round == 0 ? 4 : 2;
-        if (wave >= lo && wave < hi) {
-#pragma unroll
-            for (int g = 0; g < G; g++)
-#pragma unroll
-                for (int c = 0; c < CPL; c++) {
-                    abuf[wave - lo][g][CPL * lane + c] = accr[g][c];
-                    abuf[wave - lo][g][D + CPL * lane + c] = accp[g][c];
-                }
-        }
+}
+
+// q' = H q / sqrt(D) in fp32, one workgroup of D/2 threads per (sequence, query head)
+template <int D>
+__global__ void __launch_bounds__(D / 2) qrot_kernel(const void* __restrict__ q, int q_bf16, float* __restrict__ qr) {
+    __shared__ float x[D];
+    const int bh = blockIdx.x, k = threadIdx.x;
+    for (int j = k; j < D; j += D / 2) {
+        const int64_t idx = (int64_t)bh * D + j;
+        x[j] = q_bf16 ? __builtin_bit_cast(float, ((uint32_t) static_cast<const uint16_t*>(q)[idx]) << 16)
+                      : static_cast<const float*>(q)[idx];
+    }
+    __syncthreads();
+    for (int hs = 1; hs < D; hs <<= 1) {
+        const int i0 = (k / hs) * 2 * hs + (k % hs), i1 = i0 + hs;
+        const float u = x[i0], v = x[i1];
         __syncthreads();
-        if (wave < lo) {
-#pragma unroll
-            for (int g = 0; g < G; g++)
-#pragma unroll
-                for (int c = 0; c < CPL; c++) {
-                    accr[g][c] += abuf[wave][g][CPL * lane + c];
-                    accp[g][c] += abuf[wave][g][D + CPL * lane + c];
-                }
-        }
+        x[i0] = u + v;
+        x[i1] = u - v;
         __syncthreads();
     }
-    if (wave == 0) {
-#pragma unroll
-        for (int g = 0; g < G; g++) {
-            float* o = a.ws + (((int64_t)b * Hq + h * G + g) * a.nsplit + split) * WS;
-            if (lane == 0) {
-                o[0] = M[g];
-                o[1] = Ls[g];
-            }
-#pragma unroll
-            for (int c = 0; c < CPL; c++) {
-                o[4 + CPL * lane + c] = accr[g][c];
-                o[4 + D + CPL * lane + c] = accp[g][c];
-            }
-        }
-    }
+    const float rs = 1.0f / sqrtf((float)D);
+    for (int j = k; j < D; j += D / 2) qr[(int64_t)bh * D + j] = x[j] * rs;
 }
 
 // One workgroup per (sequence, query head): merge the splits, rotate the
@@ -393,11 +509,15 @@ __global__ void __launch_bounds__(D) decode_combine_kernel(const float* __restri
 
 template <int D, int T, int KB, int VB>
 hipError_t launch_gqa(const DecodeArgs& a, hipStream_t st) {
-    dim3 grid(a.nsplit, a.H, a.B);
-    hipLaunchKernelGGL((decode_split_kernel<D, T, KB, VB>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((qrot_kernel<D>), dim3(a.B * a.Hq), dim3(D / 2), 0, st, a.q, a.q_bf16, a.ws);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(a.B * a.Hq), dim3(D), 0, st, a.ws, a.out, a.nsplit);
+    dim3 grid(a.nsplit, a.H, a.B);
+    hipLaunchKernelGGL((decode_split_kernel<D, T, KB, VB>), grid, dim3(64), 0, st, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(a.B * a.Hq), dim3(D), 0, st,
+                       a.ws + (int64_t)a.B * a.Hq * D, a.out, a.nsplit);
     return hipGetLastError();
 }
 
@@ -420,11 +540,11 @@ hipError_t gqa_bits(const DecodeArgs& a, hipStream_t st) {
 
 void decode_plan(int D, int H, int G, int mla, int B, int max_pages, int T, int* nsplit, int* pps) {
     (void)D; (void)G; (void)T;
-    // GQA: about four 4-wave workgroups per CU.  MLA: one 4-wave workgroup per
-    // CU holds 64 heads (its accumulators fill the register file), so up to 128
-    // heads take two workgroups per split.
+    // GQA: one-wave workgroups, about 12 per CU.  MLA: one 4-wave workgroup
+    // per CU holds 64 heads (its accumulators fill the register file), so up
+    // to 128 heads take two workgroups per split.
     const int units = mla ? B * ((G + 63) / 64) : B * H;
-    const int target = mla ? 256 : 1024;
+    const int target = mla ? 256 : 3072;
     int ns = (target + units - 1) / units;
     if (ns < 1) ns = 1;
     if (ns > max_pages) ns = max_pages;
@@ -436,12 +556,14 @@ void decode_plan(int D, int H, int G, int mla, int B, int max_pages, int T, int*
     if (*nsplit < 1) *nsplit = 1;
 }
 
+// fp32 rotated queries [B][Hq][D], then split partials [B][Hq][nsplit][2D + 4]
 size_t decode_workspace_floats(int D, int Hq, int B, int nsplit) {
-    return (size_t)B * Hq * nsplit * (2 * D + 4);
+    return (size_t)B * Hq * D + (size_t)B * Hq * nsplit * (2 * D + 4);
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
     if (a.mla) return launch_mla(a, st);
+    if (a.G != 4) return hipErrorInvalidValue;
     if (a.D == 128 && a.T == 128) return gqa_bits<128, 128>(a, st);
     if (a.D == 128 && a.T == 64) return gqa_bits<128, 64>(a, st);
     if (a.D == 256 && a.T == 128) return gqa_bits<256, 128>(a, st);
