@@ -21,7 +21,9 @@ FLAGS = [
 
 # min/max reductions in the quantizer need no NaN canonicalization: inputs are
 # finite fp16 values
-EXTRA = {"quantize_d128.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"],
+EXTRA = {"quantize_d128.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee",
+                              # the rotation's MFMA accumulators stay in ordinary VGPRs
+                              "-mllvm", "-amdgpu-mfma-vgpr-form=1"],
          "quantize_d256.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"],
          "quantize_d512.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"],
          "decode_mla.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee",

@@ -140,6 +140,22 @@ __device__ __forceinline__ uint32_t pack6x4(uint32_t f0, uint32_t f1, uint32_t f
     return (x23 << 12) | x01;              // junk shifted out
 }
 
+// D = 128: the rotation runs on the 16x16x32 fp16 MFMA (y = X H with the
+// fp16 tile as the A operand and +-1 blocks of H as the B operand), each wave
+// on its own 32 rows, and reaches the register layout through LDS.
+template <int D>
+struct MfmaRotation {
+    static constexpr bool on = D == 128;
+};
+
+// LDS unit (4 floats) of rotated column j (0..63 of the half being moved),
+// rows 4 ru .. 4 ru + 3 of a wave's 32 rows: column-major with the row unit
+// xor-ed with column bits, so that the MFMA-layout stores and the
+// register-layout loads each touch every bank once.
+__device__ __forceinline__ int rot_unit(int j, int ru) {
+    return 8 * j + (ru ^ ((j ^ (j >> 3)) & 7));
+}
+
 template <int D, int T>
 struct TileShape {
     static constexpr int LPR = D / QC;                        // lanes per token row
@@ -151,7 +167,12 @@ struct TileShape {
     static constexpr int NSUB = (RGB == 3) ? 2 : 1;           // lane bit 2 left after the swaps
     static constexpr int SMEM_CODES = T * D;                  // one byte per code at most
     static constexpr int SMEM_PART = NW * NSUB * D * 4;
-    static constexpr int SMEM = SMEM_CODES > SMEM_PART ? SMEM_CODES : SMEM_PART;
+    static constexpr int SMEM_ROT = MfmaRotation<D>::on ? T * D * 2 : 0;  // half the rotated tile, fp32
+    static constexpr int SMEM_A = SMEM_CODES > SMEM_PART ? SMEM_CODES : SMEM_PART;
+    // with the MFMA rotation the column partials get their own region after
+    // the tile image, so the statistics need not wait for the image to die
+    static constexpr int PART_OFF = MfmaRotation<D>::on ? (SMEM_ROT > SMEM_CODES ? SMEM_ROT : SMEM_CODES) : 0;
+    static constexpr int SMEM = MfmaRotation<D>::on ? PART_OFF + SMEM_PART : (SMEM_A > SMEM_ROT ? SMEM_A : SMEM_ROT);
 };
 
 // One tile -> one record.  smem: TileShape::SMEM bytes; vec: 3*D floats.
@@ -168,7 +189,7 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ tile,
     static_assert(T * D / 64 == NT, "one lane per 64 values");
     static_assert(REC % 16 == 0, "records stay 16-byte aligned");
 
-    float* colpart = reinterpret_cast<float*>(smem);
+    float* colpart = reinterpret_cast<float*>(smem + S::PART_OFF);
     float* bvec = vec;           // b_j = exp(-2 lc_j), unnormalized basis
     float* icvec = vec + D;      // (+-1 per channel) * sqrt(b_j): multiplies y into W
     uint16_t* cvec = reinterpret_cast<uint16_t*>(vec + 2 * D);  // fp16 column scales
@@ -186,41 +207,122 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ tile,
     const int row0 = wave * RPW + rg * QR;
     const int ch0 = cg * QC;
 
-    // ---- stage 1: load the fp16 tile ---------------------------------------
     float y[QR][QC];
+    if constexpr (MfmaRotation<D>::on) {
+        // ---- stages 1-2: y = X H on the MFMA, then into the register layout ----
+        // H_128 = H_4 (x) H_32 over channel j = 32 v + u: the MFMA takes each
+        // 32-channel group v through H_32 (k = u = 8 g4 + i, n = u' = 16 nb + l16,
+        // H_32[u][u'] = (-1)^popcount(i & l16 & 7) (-1)^(g4_0 l16_3) (-1)^(g4_1 nb):
+        // one per-lane pattern per nb), and the 4 groups meet in an in-lane
+        // 4-point butterfly.
+        typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+        typedef float f4 __attribute__((ext_vector_type(4)));
+        static_assert(RGB == 3 && CGB == 3 && RPW == 32, "rotation layout assumes 32 rows x 128 channels per wave");
+        const int l16 = lane & 15, g4 = lane >> 4;
+        // bit i of wm is parity(i & l16 & 7) (a row of the 8x8 Hadamard matrix)
+        const uint32_t m7 = (uint32_t)(l16 & 7);
+        const uint32_t wm = ((m7 & 1u) ? 0xAAu : 0u) ^ ((m7 & 2u) ? 0xCCu : 0u) ^ ((m7 & 4u) ? 0xF0u : 0u);
+        h8 hp[2];
 #pragma unroll
-    for (int r = 0; r < QR; r++) {
-        const uint4* p = reinterpret_cast<const uint4*>(tile + (int64_t)(row0 + r) * D + ch0);
-        uint4 u0 = p[0], u1 = p[1];
-        uint32_t w[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+        for (int nb = 0; nb < 2; nb++) {
+            const uint32_t flip = ((g4 & 1) & (l16 >> 3)) ^ ((g4 >> 1) & nb);
+            const uint32_t sw = wm ^ (flip ? 0xFFu : 0u);
+            uint32_t d[4];
 #pragma unroll
-        for (int k = 0; k < 8; k++) {
-            y[r][2 * k] = half_bits_to_float(w[k] & 0xffffu);
-            y[r][2 * k + 1] = half_bits_to_float(w[k] >> 16);
+            for (int k = 0; k < 4; k++) d[k] = 0x3C003C00u | (((sw >> (2 * k)) & 1u) << 15) | (((sw >> (2 * k + 1)) & 1u) << 31);
+            hp[nb] = __builtin_bit_cast(h8, make_uint4(d[0], d[1], d[2], d[3]));
         }
-    }
-    if (tid < D) bvec[tid] = 1.0f / (float)D;  // c_j = 1 in the normalized basis
+        // the wave's 32 x 128 block moves in two halves of 64 columns; lanes
+        // whose 16 channels lie in the half read it
+        // the wave's 32 x 128 block moves in two halves of 64 columns; lanes
+        // whose 16 channels lie in the half read it
+        float* yt = reinterpret_cast<float*>(smem) + wave * (RPW * D / 2);
+        f4 z[2][4][2];  // [token block][channel group v][nb]
+#pragma unroll
+        for (int tb = 0; tb < 2; tb++) {
+            const uint16_t* xr = tile + (int64_t)(wave * RPW + 16 * tb + l16) * D + 8 * g4;
+#pragma unroll
+            for (int v = 0; v < 4; v++) {
+                const h8 xa = *reinterpret_cast<const h8*>(xr + 32 * v);
+#pragma unroll
+                for (int nb = 0; nb < 2; nb++)
+                    z[tb][v][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa, hp[nb], f4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+            }
+        }
+        // H_4 across the groups: z[.][v'][.] becomes output group v'
+#pragma unroll
+        for (int tb = 0; tb < 2; tb++)
+#pragma unroll
+            for (int nb = 0; nb < 2; nb++) {
+                const f4 a0 = z[tb][0][nb] + z[tb][1][nb], a1 = z[tb][0][nb] - z[tb][1][nb];
+                const f4 a2 = z[tb][2][nb] + z[tb][3][nb], a3 = z[tb][2][nb] - z[tb][3][nb];
+                z[tb][0][nb] = a0 + a2;
+                z[tb][1][nb] = a1 + a3;
+                z[tb][2][nb] = a0 - a2;
+                z[tb][3][nb] = a1 - a3;
+            }
+#pragma unroll
+        for (int half = 0; half < 2; half++) {
+            // output columns 32 v + 16 nb + l16 with v = 2 half + (0, 1)
+#pragma unroll
+            for (int tb = 0; tb < 2; tb++)
+#pragma unroll
+                for (int vq = 0; vq < 2; vq++)
+#pragma unroll
+                    for (int nb = 0; nb < 2; nb++)
+                        *reinterpret_cast<f4*>(yt + 4 * rot_unit(32 * vq + 16 * nb + l16, 4 * tb + g4)) = z[tb][2 * half + vq][nb];
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            if ((cg >> 2) == half) {
+#pragma unroll
+                for (int c = 0; c < QC; c++) {
+                    const f4 v = *reinterpret_cast<const f4*>(yt + 4 * rot_unit((ch0 & 63) + c, rg));
+#pragma unroll
+                    for (int r = 0; r < QR; r++) y[r][c] = v[r];
+                }
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        }
+        if (tid < D) bvec[tid] = 1.0f / (float)D;  // c_j = 1 in the normalized basis
+    } else {
+        // ---- stage 1: load the fp16 tile ---------------------------------------
+#pragma unroll
+        for (int r = 0; r < QR; r++) {
+            const uint4* p = reinterpret_cast<const uint4*>(tile + (int64_t)(row0 + r) * D + ch0);
+            uint4 u0 = p[0], u1 = p[1];
+            uint32_t w[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+#pragma unroll
+            for (int k = 0; k < 8; k++) {
+                y[r][2 * k] = half_bits_to_float(w[k] & 0xffffu);
+                y[r][2 * k + 1] = half_bits_to_float(w[k] >> 16);
+            }
+        }
+        if (tid < D) bvec[tid] = 1.0f / (float)D;  // c_j = 1 in the normalized basis
 
-    // ---- stage 2: Hadamard rotation (unnormalized butterflies) -------------
+        // ---- stage 2: Hadamard rotation (unnormalized butterflies) -------------
 #pragma unroll
-    for (int r = 0; r < QR; r++) {
+        for (int r = 0; r < QR; r++) {
 #pragma unroll
-        for (int hs = 1; hs < QC; hs <<= 1) {
+            for (int hs = 1; hs < QC; hs <<= 1) {
 #pragma unroll
-            for (int c = 0; c < QC; c++) {
-                if ((c & hs) == 0) {
-                    float a = y[r][c], b = y[r][c + hs];
-                    y[r][c] = a + b;
-                    y[r][c + hs] = a - b;
+                for (int c = 0; c < QC; c++) {
+                    if ((c & hs) == 0) {
+                        float a = y[r][c], b = y[r][c + hs];
+                        y[r][c] = a + b;
+                        y[r][c + hs] = a - b;
+                    }
                 }
             }
         }
+        xbutterfly<0>(y, lane);
+        xbutterfly<1>(y, lane);
+        xbutterfly<3>(y, lane);
+        if constexpr (CGB >= 4) xbutterfly<2>(y, lane);
+        if constexpr (CGB >= 5) xbutterfly<4>(y, lane);
     }
-    xbutterfly<0>(y, lane);
-    xbutterfly<1>(y, lane);
-    xbutterfly<3>(y, lane);
-    if constexpr (CGB >= 4) xbutterfly<2>(y, lane);
-    if constexpr (CGB >= 5) xbutterfly<4>(y, lane);
 
     // ---- stage 3: normalization iterations on A = y^2 ----------------------
     float A[QR][QC];
@@ -280,7 +382,7 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ tile,
             bvec[tid] = b;
             if (last) {
                 // channel sign left by the sign-tracked butterflies: (-1)^popcount(j >> 4)
-                const float sg = (__builtin_popcount((unsigned)tid >> 4) & 1) ? -1.f : 1.f;
+                const float sg = (!MfmaRotation<D>::on && (__builtin_popcount((unsigned)tid >> 4) & 1)) ? -1.f : 1.f;
                 icvec[tid] = sg * sqrtf(b);
                 cvec[tid] = (uint16_t)float_to_half_bits(__builtin_amdgcn_rsqf((float)D * b));
             }
