@@ -17,7 +17,10 @@ Reported (one JSON line):
             1 GiB fill) before each call, outside the event pairs.
   roofline  the quantize kernel (the step's dominant kernel): algorithmic
             bytes per launch (fp16 read + records written) / launch time,
-            against 8 TB/s HBM.
+            against 8 TB/s HBM.  traffic: HBM bytes per launch from the
+            FETCH_SIZE / WRITE_SIZE counter passes recorded under profiles/
+            for this workload, scaled by a 1 GiB copy's readings; null when
+            the quantize sources differ from the ones profiled.
   components quantize and decode separately, each as GB/s and % of peak.
   cpu_baseline the oracle (plain C, fp64, OpenMP) on a bounded sample of the
             same workload, same byte formulas.
@@ -33,6 +36,41 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+# sources whose compiled code the recorded counter passes measured
+QUANTIZE_SOURCES = ["kv_cache_quantization_kvarn_amd/build.py"] + [
+    "kv_cache_quantization_kvarn_amd/csrc/" + f for f in
+    ("kvarn_device.hpp", "kvarn_internal.hpp", "quantize_impl.hpp", "quantize.hip", "quantize_d128.hip",
+     "quantize_d256.hip", "quantize_d512.hip")]
+
+
+def quantize_source_hash():
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in QUANTIZE_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(workload):
+    """HBM bytes per quantize launch recorded for this workload, if the
+    quantize sources are the ones that were profiled."""
+    path = os.path.join(ROOT, "profiles", f"quantize_kernel_{workload}_hbm.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    if fields.get("source_sha256") != quantize_source_hash():
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 METRIC = "quantize fp16 GB/s + decode-attn effective HBM GB/s, % of MI355X peak"
 
 
@@ -65,15 +103,19 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="dense8b_b16_32k_k4v2_g128")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-records", type=int, default=16384, help="records in the oracle's quantize sample")
-    ap.add_argument("--cpu-rows", type=int, default=16, help="(sequence, head) rows in the oracle's decode sample")
+    ap.add_argument("--cpu-records", type=int, default=0,
+                    help="records in the oracle's quantize sample (0: every record of the workload)")
+    ap.add_argument("--cpu-rows", type=int, default=64, help="(sequence, head) rows in the oracle's decode sample")
+    ap.add_argument("--print-source-hash", action="store_true", help="print the quantize source hash and exit")
     ap.add_argument("--copy-probe", action="store_true",
                     help="time a plain 1 GiB device-to-device copy instead (calibrates the HBM byte counters)")
     args = ap.parse_args()
+    if args.print_source_hash:
+        print(quantize_source_hash())
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (see the sharding notes in the "
-              "design document); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU: the path has no multi-GPU mode; run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -159,7 +201,8 @@ def main():
                    "sink": lay["sink"], "tail": lay["tail"], "mla": bool(lay["mla"])},
         "roofline": {"bound": "hbm", "kernel": "quantize_kernel", "achieved": round(q_gbs_ii, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(q_gbs_ii / HBM_PEAK_GBS, 4),
-                     "bytes_per_launch": q_fp16 + q_out, "launch_us": round(tq_m * 1e6, 2), "traffic": None},
+                     "bytes_per_launch": q_fp16 + q_out, "launch_us": round(tq_m * 1e6, 2),
+                     "traffic": recorded_traffic(args.workload)},
         "components": {
             "quantize": {"us": round(tq_m * 1e6, 2), "fp16_GBs": round(q_gbs_i, 1),
                          "fp16_frac": round(q_gbs_i / HBM_PEAK_GBS, 4), "traffic_GBs": round(q_gbs_ii, 1),
@@ -208,6 +251,8 @@ def cpu_baseline(case, krec, vrec, n_records, n_rows):
     threads = min(threads, int(os.environ.get("OMP_NUM_THREADS", threads)))
     kinds = 1 if mla else 2
     # quantize: n_records records (pages x heads x K/V) of the workload
+    if n_records <= 0:
+        n_records = case["n_qpages"] * H * kinds
     n_pages = max(1, min(case["n_qpages"], math.ceil(n_records / (H * kinds))))
     src = case["src"][:n_pages].cpu().numpy()
     pages = np.unique(src)
