@@ -163,7 +163,8 @@ size_t kvarn_decode_workspace_bytes(const kvarn_layout* layout, int32_t batch, i
     kvarn::decode_plan(layout->head_dim, H, num_q_heads / (H > 0 ? H : 1), layout->mla, batch, max_pages,
                        layout->tile_tokens, &ns, &pps);
     if (layout->mla) return kvarn::mla_workspace_floats(num_q_heads, batch, ns) * sizeof(float);
-    return kvarn::decode_workspace_floats(layout->head_dim, num_q_heads, batch, ns) * sizeof(float);
+    const int nf = kvarn::decode_fp16_pages(layout->tile_tokens, layout->sink_tokens, layout->tail_tokens, max_pages);
+    return kvarn::decode_workspace_floats(layout->head_dim, num_q_heads, batch, ns, nf) * sizeof(float);
 }
 
 kvarn_status kvarn_decode_attn(const kvarn_layout* layout, const kvarn_cache* cache, const kvarn_page_table* pages,
@@ -193,8 +194,11 @@ kvarn_status kvarn_decode_attn(const kvarn_layout* layout, const kvarn_cache* ca
     int ns = 1, pps = 1;
     kvarn::decode_plan(layout->head_dim, H, G, layout->mla, pages->batch, pages->max_pages, layout->tile_tokens,
                        &ns, &pps);
+    const int nf = kvarn::decode_fp16_pages(layout->tile_tokens, layout->sink_tokens, layout->tail_tokens,
+                                            pages->max_pages);
     const size_t need = (layout->mla ? kvarn::mla_workspace_floats(num_q_heads, pages->batch, ns)
-                                     : kvarn::decode_workspace_floats(layout->head_dim, num_q_heads, pages->batch, ns)) *
+                                     : kvarn::decode_workspace_floats(layout->head_dim, num_q_heads, pages->batch, ns,
+                                                                      nf)) *
                         sizeof(float);
     if (!workspace || workspace_bytes < need)
         return fail(KVARN_EWORKSPACE, "workspace of %zu bytes is smaller than the %zu bytes required",
@@ -214,6 +218,7 @@ kvarn_status kvarn_decode_attn(const kvarn_layout* layout, const kvarn_cache* ca
     a.Hq = num_q_heads;
     a.max_pages = pages->max_pages;
     a.nsplit = ns;
+    a.nfsplit = nf;
     a.pps = pps;
     a.k_records = cache->k_records;
     a.v_records = cache->v_records;

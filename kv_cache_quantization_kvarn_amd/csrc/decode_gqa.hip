@@ -23,7 +23,9 @@
 // products keep fp32 accuracy.
 //
 // One wave per workgroup per (split, KV head, sequence); split s visits pages
-// s, s + nsplit, ..., so the fp16 pages at both ends spread over the splits.
+// s, s + nsplit, ..., so the fp16 pages at both ends spread over the splits,
+// 64 tokens per step; the next step's codes and scales load during the
+// current one.
 #include <math.h>
 
 #include <utility>
@@ -154,8 +156,7 @@ __global__ void __launch_bounds__(64) decode_split_kernel(DecodeArgs a) {
     constexpr float FK = (float)(1 << KB), FV = (float)(1 << VB);
     static_assert(KCH % 16 == 0 && VROW % 16 == 0, "16-byte code segments");
 
-    __shared__ __attribute__((aligned(16))) _Float16 pt[2][G][64];  // p * S_V of a sub-block (high, low), by operand position
-    __shared__ float4 pf[64];                                    // weights of an fp16 sub-block
+    __shared__ __attribute__((aligned(16))) _Float16 pt[2][G][64];  // p * S_V of a step (high, low), by operand position
 
     const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int lane = threadIdx.x;
@@ -163,87 +164,100 @@ __global__ void __launch_bounds__(64) decode_split_kernel(DecodeArgs a) {
     const int Hq = a.Hq;
     const float sm2 = a.sm_scale * kLog2e;
 
-    // rotated query (fp32) at the channels of this lane's operand slots, and
-    // the plain query (fp16) for fp16 pages.  Slot r serves operand
-    // 32 (r >> 1) + blk + 16 (r & 1) of the scores.
+    // rotated query (fp32) at the channels of this lane's operand slots.
+    // Slot r serves operand 32 (r >> 1) + blk + 16 (r & 1) of the scores.
     const float* qr = a.ws + ((int64_t)b * Hq + h * G + m) * D;
     float qv[NS][4];
-    h4 qp[NS], qpl[NS];
 #pragma unroll
     for (int r = 0; r < NS; r++) {
         const int i = 32 * (r >> 1) + blk + 16 * (r & 1);
 #pragma unroll
-        for (int k = 0; k < 4; k++) {
-            qv[r][k] = qr[code_of<KB>(i, k)];
-            const int64_t idx = ((int64_t)b * Hq + h * G + m) * D + 4 * i + k;
-            const float x = a.q_bf16 ? __builtin_bit_cast(float, ((uint32_t) static_cast<const uint16_t*>(a.q)[idx]) << 16)
-                                     : static_cast<const float*>(a.q)[idx];
-            qp[r][k] = (_Float16)x;
-            qpl[r][k] = (_Float16)(x - (float)qp[r][k]);
-        }
+        for (int k = 0; k < 4; k++) qv[r][k] = qr[code_of<KB>(i, k)];
     }
 
     const int L = min(a.seq_lens[b], a.max_pages * T);
-    const int npages = L > 0 ? (L + T - 1) / T : 0;
     const int nq = (L - a.sink - a.tail >= T) ? (L - a.sink - a.tail) / T : 0;
     const int sp = a.sink / T;
 
-    float mrun[G], lp[G], accr[NS][G], accp[CPL][G];
+    float mrun[G], lp[G], accr[NS][G];
 #pragma unroll
     for (int g = 0; g < G; g++) {
         mrun[g] = -INFINITY;
         lp[g] = 0.f;
 #pragma unroll
         for (int s = 0; s < NS; s++) accr[s][g] = 0.f;
-#pragma unroll
-        for (int c = 0; c < CPL; c++) accp[c][g] = 0.f;
     }
 
-    // Steps: (page, 64-token sub-block) of this split's pages, in order.  The
-    // key words, token scale words and column scales of the next quantized
-    // step are loaded while the current step runs; a step's value words are
-    // loaded before its scores, so they arrive during the score MFMAs.
-    constexpr int KW = KCH / 4;        // words of one 128-channel key chunk
-    constexpr int VW = 64 * VB / 32;   // value code words of one channel over 64 tokens
-    const int nst = npages > split ? ((npages - split + a.nsplit - 1) / a.nsplit) * TS : 0;
+    // Steps: the 64-token halves h of this split's pages (pages split,
+    // split + nsplit, ...), in order.  A quantized step's key words (chunk 0),
+    // scale words and, on a page's first half, column scales are loaded during
+    // the previous step: the key part once that step's scores have consumed
+    // theirs, the value part once its value sums have.
+    constexpr int KW = KCH / 4;           // words of one 128-channel key chunk
+    constexpr int VRW = VROW / 4;         // value code words of one channel (whole page)
+    constexpr int VHW = 64 * VB / 32;     // value code words of one channel over 64 tokens
+    constexpr bool PREK = KW <= 32;
+    constexpr bool PREV = NS * VHW <= 32;
+    static_assert(VRW == TS * VHW, "a channel row is TS halves");
+    const int npg = nq > split ? (nq - split + a.nsplit - 1) / a.nsplit : 0;  // quantized pages of this split
+    const int nst = npg * TS;
     const uint8_t* const krec = static_cast<const uint8_t*>(a.k_records);
     const uint8_t* const vrec = static_cast<const uint8_t*>(a.v_records);
 
-    uint32_t nkw[KW];
-    uint32_t nksz = 0, nvsz = 0;
-    uint16_t nck[NS][4], ncv[NS];
+    struct StepRef {
+        int id, h;
+        bool ok;
+    };
+    auto step_ref = [&](int k) {
+        StepRef r;
+        r.h = k % TS;
+        r.id = k < nst ? a.block_table[(int64_t)b * a.max_pages + sp + split + (k / TS) * a.nsplit] : -1;
+        r.ok = k < nst && r.id >= 0 && (int64_t)r.id < a.n_qpages;
+        return r;
+    };
+
+    uint32_t kw[PREK ? KW : 1];
+    uint32_t vw[NS][PREV ? VHW : 1];
+    uint32_t ksz = 0, vsz = 0;
+    uint32_t ckr[NS][2], cvr[(NS + 1) / 2];  // fp16 column scales, two per word
 #pragma unroll
-    for (int k = 0; k < KW; k++) nkw[k] = 0;
+    for (int k = 0; k < (PREK ? KW : 1); k++) kw[k] = 0;
 #pragma unroll
     for (int r = 0; r < NS; r++) {
-        ncv[r] = 0;
+        cvr[r >> 1] = 0;
+        ckr[r][0] = ckr[r][1] = 0;
 #pragma unroll
-        for (int k = 0; k < 4; k++) nck[r][k] = 0;
+        for (int k = 0; k < (PREV ? VHW : 1); k++) vw[r][k] = 0;
     }
-    auto prefetch = [&](int st) {
-        const int page = split + (st / TS) * a.nsplit, sb = st % TS;
-        if (!(page >= sp && page < sp + nq)) return;
-        const int id = a.block_table[(int64_t)b * a.max_pages + page];
-        if (id < 0 || (int64_t)id >= a.n_qpages) return;
-        const uint8_t* rk = krec + ((int64_t)id * a.H + h) * KREC;
-        const uint8_t* rv = vrec + ((int64_t)id * a.H + h) * VREC;
-        const int tok = 64 * sb + lane;
-        load_words(nkw, rk + (int64_t)tok * KROW, KW / 4);
-        nksz = reinterpret_cast<const uint32_t*>(rk + KCB)[tok];
-        nvsz = reinterpret_cast<const uint32_t*>(rv + VCB)[tok];
-        if (sb == 0) {
+    auto issue_k = [&](const StepRef& r) {
+        if (!r.ok) return;
+        const uint8_t* rk = krec + ((int64_t)r.id * a.H + h) * KREC;
+        const int tok = 64 * r.h + lane;
+        if constexpr (PREK) load_words(kw, rk + (int64_t)tok * KROW, KW / 4);
+        ksz = reinterpret_cast<const uint32_t*>(rk + KCB)[tok];
+        if (r.h == 0) {
             const uint16_t* ck = reinterpret_cast<const uint16_t*>(rk + KCB + 4 * T);
-            const uint16_t* cvp = reinterpret_cast<const uint16_t*>(rv + VCB + 4 * T);
 #pragma unroll
-            for (int r = 0; r < NS; r++) {
-                const int i = 32 * (r >> 1) + blk + 16 * (r & 1);
-#pragma unroll
-                for (int k = 0; k < 4; k++) nck[r][k] = ck[code_of<KB>(i, k)];
-                ncv[r] = cvp[64 * r + lane];
+            for (int r2 = 0; r2 < NS; r2++) {
+                const int i = 32 * (r2 >> 1) + blk + 16 * (r2 & 1);
+                ckr[r2][0] = (uint32_t)ck[code_of<KB>(i, 0)] | ((uint32_t)ck[code_of<KB>(i, 1)] << 16);
+                ckr[r2][1] = (uint32_t)ck[code_of<KB>(i, 2)] | ((uint32_t)ck[code_of<KB>(i, 3)] << 16);
             }
         }
     };
-    if (nst > 0) prefetch(0);
+    auto issue_v = [&](const StepRef& r) {
+        if (!r.ok) return;
+        const uint8_t* rv = vrec + ((int64_t)r.id * a.H + h) * VREC;
+#pragma unroll
+        for (int sv = 0; sv < NS; sv++) {
+            if constexpr (PREV) load_words(vw[sv], rv + (int64_t)(64 * sv + lane) * VROW + r.h * (4 * VHW), VHW / 4);
+            if (r.h == 0) {
+                const uint32_t c16 = reinterpret_cast<const uint16_t*>(rv + VCB + 4 * T)[64 * sv + lane];
+                cvr[sv >> 1] = (sv & 1) ? (cvr[sv >> 1] | (c16 << 16)) : c16;
+            }
+        }
+        vsz = reinterpret_cast<const uint32_t*>(rv + VCB)[64 * r.h + lane];
+    };
 
     h4 qa[NS], qal[NS];  // score operands q' * C_K of the current page, high and low parts
     float sq[G];         // their sums per head
@@ -256,55 +270,54 @@ __global__ void __launch_bounds__(64) decode_split_kernel(DecodeArgs a) {
         cvv[r] = 0.f;
     }
 
-    for (int st = 0; st < nst; st++) {
-        const int page = split + (st / TS) * a.nsplit, sb = st % TS;
-        const bool quant = page >= sp && page < sp + nq;
-        const int id = a.block_table[(int64_t)b * a.max_pages + page];
-        uint32_t kw[KW];
-#pragma unroll
-        for (int k = 0; k < KW; k++) kw[k] = nkw[k];
-        const uint32_t ksz = nksz, vsz = nvsz;
-        if (quant && sb == 0) {
-            // score operands of the new page and their per-head sums
-            float part = 0.f;
-#pragma unroll
-            for (int r = 0; r < NS; r++) {
-#pragma unroll
-                for (int k = 0; k < 4; k++) {
-                    const float x = qv[r][k] * half_bits_to_float(nck[r][k]);
-                    const _Float16 hi = (_Float16)x;
-                    const _Float16 lo = (_Float16)(x - (float)hi);
-                    qa[r][k] = hi;
-                    qal[r][k] = lo;
-                    part += (float)hi + (float)lo;
-                }
-                cvv[r] = half_bits_to_float(ncv[r]);
-            }
-            part = sum_blocks_half(part);  // lanes g and 32 + g hold the halves' sums for head g
-#pragma unroll
-            for (int g = 0; g < G; g++)
-                sq[g] = i2f(__builtin_amdgcn_readlane(f2i(part), g)) + i2f(__builtin_amdgcn_readlane(f2i(part), 32 + g));
-        }
-        if (st + 1 < nst) prefetch(st + 1);
-        if (id < 0 || (quant ? (int64_t)id >= a.n_qpages : (int64_t)id >= a.n_fpages)) continue;
-        if (page * T + 64 * sb >= L) continue;  // no token of this sub-block is in the sequence
-        const int tok = 64 * sb + lane;
+    StepRef cur = step_ref(0);
+    issue_k(cur);
+    issue_v(cur);
 
-        float s[G];
+    for (int k = 0; k < nst; k++) {
+        const StepRef nxt = step_ref(k + 1);
+        if (!cur.ok) {  // uniform: a page whose id is outside the record pool is skipped
+            issue_k(nxt);
+            issue_v(nxt);
+            cur = nxt;
+            continue;
+        }
+        const int id = cur.id;
+        const int tok = 64 * cur.h + lane;
         const uint8_t* rk = krec + ((int64_t)id * a.H + h) * KREC;
         const uint8_t* rv = vrec + ((int64_t)id * a.H + h) * VREC;
-        uint32_t vw[NS][VW];
-        if (quant) {
+
+        // ---- scores, lane = token ----
+        float s[G];
+        {
+            if (cur.h == 0) {
+                // score operands of the new page (fp16 high and low parts) and their per-head sums
+                float part = 0.f;
 #pragma unroll
-            for (int sv = 0; sv < NS; sv++)
-                load_words(vw[sv], rv + (int64_t)(64 * sv + lane) * VROW + sb * (64 * VB / 8), VW / 4);
+                for (int r = 0; r < NS; r++) {
+#pragma unroll
+                    for (int kk = 0; kk < 4; kk++) {
+                        const float x = qv[r][kk] * half_bits_to_float((ckr[r][kk >> 1] >> (16 * (kk & 1))) & 0xffffu);
+                        const _Float16 hi = (_Float16)x;
+                        const _Float16 lo = (_Float16)(x - (float)hi);
+                        qa[r][kk] = hi;
+                        qal[r][kk] = lo;
+                        part += (float)hi + (float)lo;
+                    }
+                    cvv[r] = half_bits_to_float((cvr[r >> 1] >> (16 * (r & 1))) & 0xffffu);
+                }
+                part = sum_blocks_half(part);  // lanes g and 32 + g hold the halves' sums for head g
+#pragma unroll
+                for (int g = 0; g < G; g++)
+                    sq[g] = i2f(__builtin_amdgcn_readlane(f2i(part), g)) + i2f(__builtin_amdgcn_readlane(f2i(part), 32 + g));
+            }
             f4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int c = 0; c < NC; c++) {
                 uint32_t w[KW];
-                if (c == 0) {
+                if (PREK && c == 0) {
 #pragma unroll
-                    for (int k = 0; k < KW; k++) w[k] = kw[k];
+                    for (int kk = 0; kk < KW; kk++) w[kk] = kw[PREK ? kk : 0];
                 } else {
                     load_words(w, rk + (int64_t)tok * KROW + c * KCH, KW / 4);
                 }
@@ -320,46 +333,25 @@ __global__ void __launch_bounds__(64) decode_split_kernel(DecodeArgs a) {
             const float fs = FK * S, zc = Z - fs;
 #pragma unroll
             for (int g = 0; g < G; g++) s[g] = sm2 * fmaf(fs, R[g], sq[g] * zc);
-        } else {
-            const bool valid = page * T + tok < L;
-            const uint16_t* kr = static_cast<const uint16_t*>(a.k_fp16) + (((int64_t)id * a.H + h) * T + tok) * D;
-            f4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int c = 0; c < NC; c++) {
-                static_for<16>([&](auto ic) {
-                    constexpr int il = 2 * decltype(ic)::value;
-                    const uint4 v = *reinterpret_cast<const uint4*>(kr + 128 * c + 4 * il);
-                    const h4 b0 = __builtin_bit_cast(h4, make_uint2(v.x, v.y));
-                    const h4 b1 = __builtin_bit_cast(h4, make_uint2(v.z, v.w));
-                    acc0 = mfma_bcast<il & 15>(qp[2 * c + (il >> 4)], b0, acc0);
-                    acc1 = mfma_bcast<il & 15>(qpl[2 * c + (il >> 4)], b0, acc1);
-                    acc0 = mfma_bcast<(il + 1) & 15>(qp[2 * c + ((il + 1) >> 4)], b1, acc0);
-                    acc1 = mfma_bcast<(il + 1) & 15>(qpl[2 * c + ((il + 1) >> 4)], b1, acc1);
-                });
-            }
-            const f4 R = acc0 + acc1;
-#pragma unroll
-            for (int g = 0; g < G; g++) s[g] = valid ? sm2 * R[g] : -INFINITY;
         }
+        issue_k(nxt);  // the key registers are free
 
-        // ---- online softmax over this sub-block (log2 domain) ----
+        // ---- online softmax over the step (log2 domain) ----
         float p[G];
 #pragma unroll
         for (int g = 0; g < G; g++) {
             const float mx = wave_max_all(s[g]);
-            const float mnew = fmaxf(mrun[g], mx);  // finite: the sub-block holds a valid token
+            const float mnew = fmaxf(mrun[g], mx);  // finite: the step holds a valid token
             const float alpha = mrun[g] == -INFINITY ? 0.f : exp2f(mrun[g] - mnew);
             mrun[g] = mnew;
             lp[g] *= alpha;
 #pragma unroll
             for (int sv = 0; sv < NS; sv++) accr[sv][g] *= alpha;
-#pragma unroll
-            for (int c = 0; c < CPL; c++) accp[c][g] *= alpha;
             p[g] = exp2f(s[g] - mnew);
             lp[g] += p[g];
         }
 
-        if (quant) {
+        {
             // weights times S_V (fp16 high and low parts) into LDS by operand
             // position; the constant 1 of the code operands returns through
             // sum (p Zp - 2^B p S)
@@ -383,10 +375,17 @@ __global__ void __launch_bounds__(64) decode_split_kernel(DecodeArgs a) {
             const h4 pal = *reinterpret_cast<const h4*>(&pt[1][m][4 * blk]);
 #pragma unroll
             for (int sv = 0; sv < NS; sv++) {
+                uint32_t w[VHW];
+                if constexpr (PREV) {
+#pragma unroll
+                    for (int kk = 0; kk < VHW; kk++) w[kk] = vw[sv][PREV ? kk : 0];
+                } else {
+                    load_words(w, rv + (int64_t)(64 * sv + lane) * VROW + cur.h * (4 * VHW), VHW / 4);
+                }
                 f4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
                 static_for<16>([&](auto ic) {
                     constexpr int i = decltype(ic)::value;
-                    const h4 bop = code_operand<VB>(vw[sv], i);
+                    const h4 bop = code_operand<VB>(w, i);
                     acc0 = mfma_bcast<i>(pa, bop, acc0);
                     acc1 = mfma_bcast<i>(pal, bop, acc1);
                 });
@@ -395,40 +394,9 @@ __global__ void __launch_bounds__(64) decode_split_kernel(DecodeArgs a) {
                 for (int g = 0; g < G; g++) accr[sv][g] = fmaf(cvv[sv], fmaf(FV, R[g], E[g]), accr[sv][g]);
             }
             wave_sync();  // pt is rewritten by the next step
-        } else {
-            pf[lane] = make_float4(p[0], p[1], p[2], p[3]);
-            wave_sync();
-            const int nvalid = min(64, L - page * T - 64 * sb);  // tokens past the end may hold anything
-            const uint16_t* vp = static_cast<const uint16_t*>(a.v_fp16) +
-                                 (((int64_t)id * a.H + h) * T + 64 * sb) * D + CPL * lane;
-#pragma unroll 4
-            for (int t = 0; t < nvalid; t++) {
-                const float4 pv = pf[t];
-                float vv[CPL];
-                if constexpr (CPL == 2) {
-                    const uint32_t w = *reinterpret_cast<const uint32_t*>(vp + (int64_t)t * D);
-                    vv[0] = half_bits_to_float(w & 0xffffu);
-                    vv[1] = half_bits_to_float(w >> 16);
-                } else if constexpr (CPL == 4) {
-                    const uint2 w = *reinterpret_cast<const uint2*>(vp + (int64_t)t * D);
-                    vv[0] = half_bits_to_float(w.x & 0xffffu); vv[1] = half_bits_to_float(w.x >> 16);
-                    vv[2] = half_bits_to_float(w.y & 0xffffu); vv[3] = half_bits_to_float(w.y >> 16);
-                } else {
-                    const uint4 w = *reinterpret_cast<const uint4*>(vp + (int64_t)t * D);
-                    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-                    for (int k = 0; k < 8; k++) vv[k] = half_bits_to_float((ww[k >> 1] >> (16 * (k & 1))) & 0xffffu);
-                }
-#pragma unroll
-                for (int c = 0; c < CPL; c++) {
-                    accp[c][0] = fmaf(pv.x, vv[c], accp[c][0]);
-                    accp[c][1] = fmaf(pv.y, vv[c], accp[c][1]);
-                    accp[c][2] = fmaf(pv.z, vv[c], accp[c][2]);
-                    accp[c][3] = fmaf(pv.w, vv[c], accp[c][3]);
-                }
-            }
-            wave_sync();
         }
+        issue_v(nxt);  // the value registers are free
+        cur = nxt;
     }
 
     // ---- partial of this split: m, l, rotated-basis and fp16 value sums ----
@@ -436,7 +404,7 @@ __global__ void __launch_bounds__(64) decode_split_kernel(DecodeArgs a) {
 #pragma unroll
     for (int g = 0; g < G; g++) {
         const float lt = wave_sum_all(lp[g]);
-        float* o = wsp + (((int64_t)b * Hq + h * G + g) * a.nsplit + split) * WS;
+        float* o = wsp + (((int64_t)b * Hq + h * G + g) * (a.nsplit + a.nfsplit) + split) * WS;
         if (lane == 0) {
             o[0] = mrun[g];
             o[1] = lt;
@@ -444,7 +412,171 @@ __global__ void __launch_bounds__(64) decode_split_kernel(DecodeArgs a) {
 #pragma unroll
         for (int sv = 0; sv < NS; sv++) o[4 + 64 * sv + lane] = accr[sv][g];
 #pragma unroll
-        for (int c = 0; c < CPL; c++) o[4 + D + CPL * lane + c] = accp[c][g];
+        for (int c = 0; c < CPL; c++) o[4 + D + CPL * lane + c] = 0.f;  // fp16 pages: their own kernel
+    }
+}
+
+// fp16 sink and tail pages (gmlx "KV cache quantization", "The two
+// schemes"): one wave per (fp16-page slot f, KV head, sequence).  Slot f is
+// the f-th fp16 page of the sequence (sink pages, then tail pages); its
+// partial goes to split nsplit + f with a zero rotated-basis sum.  Scores on
+// the MFMA with the plain query (fp16 high and low parts), lane = token;
+// value sums on the VALU, D/8 lanes per token row.
+template <int D, int T>
+__global__ void __launch_bounds__(64) decode_fp16_kernel(DecodeArgs a) {
+    constexpr int G = 4;
+    constexpr int NS = D / 64;
+    constexpr int NC = D / 128;
+    constexpr int TS = T / 64;
+    constexpr int WS = 2 * D + 4;
+    __shared__ float4 pf[T];  // weights of the page
+
+    const int f = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int lane = threadIdx.x;
+    const int blk = lane >> 2, m = lane & 3;
+    const int Hq = a.Hq;
+    const float sm2 = a.sm_scale * kLog2e;
+    const int L = min(a.seq_lens[b], a.max_pages * T);
+    const int npages = L > 0 ? (L + T - 1) / T : 0;
+    const int nq = (L - a.sink - a.tail >= T) ? (L - a.sink - a.tail) / T : 0;
+    const int sp = a.sink / T;
+    const int page = f < sp ? f : sp + nq + (f - sp);
+    int id = -1;
+    if (page < npages) {
+        id = a.block_table[(int64_t)b * a.max_pages + page];
+        if (id < 0 || (int64_t)id >= a.n_fpages) id = -1;
+    }
+
+    constexpr int LPT = D / 8;     // lanes per token row in the value sums
+    constexpr int TG = 64 / LPT;   // tokens per load instruction
+    float mx[G], lsum[G], accp[8][G];
+#pragma unroll
+    for (int g = 0; g < G; g++) {
+        mx[g] = -INFINITY;
+        lsum[g] = 0.f;
+#pragma unroll
+        for (int c = 0; c < 8; c++) accp[c][g] = 0.f;
+    }
+    if (id >= 0) {  // uniform
+        // the plain query (fp16 high and low parts) at this lane's operand
+        // slots: 4 consecutive channels 4 i .. 4 i + 3 per slot
+        float qx[NS][4];
+        const int64_t qrow = ((int64_t)b * Hq + h * G + m) * D;
+        if (a.q_bf16) {  // uniform
+#pragma unroll
+            for (int r = 0; r < NS; r++) {
+                const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.q) + qrow +
+                                                                 4 * (32 * (r >> 1) + blk + 16 * (r & 1)));
+                qx[r][0] = __builtin_bit_cast(float, u.x << 16);
+                qx[r][1] = __builtin_bit_cast(float, u.x & 0xffff0000u);
+                qx[r][2] = __builtin_bit_cast(float, u.y << 16);
+                qx[r][3] = __builtin_bit_cast(float, u.y & 0xffff0000u);
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < NS; r++) {
+                const float4 v = *reinterpret_cast<const float4*>(static_cast<const float*>(a.q) + qrow +
+                                                                  4 * (32 * (r >> 1) + blk + 16 * (r & 1)));
+                qx[r][0] = v.x; qx[r][1] = v.y; qx[r][2] = v.z; qx[r][3] = v.w;
+            }
+        }
+        h4 qp[NS], qpl[NS];
+#pragma unroll
+        for (int r = 0; r < NS; r++)
+#pragma unroll
+            for (int kk = 0; kk < 4; kk++) {
+                qp[r][kk] = (_Float16)qx[r][kk];
+                qpl[r][kk] = (_Float16)(qx[r][kk] - (float)qp[r][kk]);
+            }
+        float s[TS][G];
+#pragma unroll
+        for (int sb = 0; sb < TS; sb++) {
+            const int tok = 64 * sb + lane;
+            const bool valid = page * T + tok < L;
+            const uint16_t* kr = static_cast<const uint16_t*>(a.k_fp16) + (((int64_t)id * a.H + h) * T + tok) * D;
+            f4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int c = 0; c < NC; c++) {
+                static_for<16>([&](auto ic) {
+                    constexpr int il = 2 * decltype(ic)::value;
+                    const uint4 v = *reinterpret_cast<const uint4*>(kr + 128 * c + 4 * il);
+                    const h4 b0 = __builtin_bit_cast(h4, make_uint2(v.x, v.y));
+                    const h4 b1 = __builtin_bit_cast(h4, make_uint2(v.z, v.w));
+                    acc0 = mfma_bcast<il & 15>(qp[2 * c + (il >> 4)], b0, acc0);
+                    acc1 = mfma_bcast<il & 15>(qpl[2 * c + (il >> 4)], b0, acc1);
+                    acc0 = mfma_bcast<(il + 1) & 15>(qp[2 * c + ((il + 1) >> 4)], b1, acc0);
+                    acc1 = mfma_bcast<(il + 1) & 15>(qpl[2 * c + ((il + 1) >> 4)], b1, acc1);
+                });
+            }
+            const f4 R = acc0 + acc1;
+#pragma unroll
+            for (int g = 0; g < G; g++) s[sb][g] = valid ? sm2 * R[g] : -INFINITY;
+        }
+        // softmax over the page: the first token of a visited page is valid
+        float p[TS][G];
+#pragma unroll
+        for (int g = 0; g < G; g++) {
+            float v = s[0][g];
+#pragma unroll
+            for (int sb = 1; sb < TS; sb++) v = fmaxf(v, s[sb][g]);
+            mx[g] = wave_max_all(v);
+#pragma unroll
+            for (int sb = 0; sb < TS; sb++) {
+                p[sb][g] = exp2f(s[sb][g] - mx[g]);
+                lsum[g] += p[sb][g];
+            }
+        }
+#pragma unroll
+        for (int sb = 0; sb < TS; sb++) pf[64 * sb + lane] = make_float4(p[sb][0], p[sb][1], p[sb][2], p[sb][3]);
+        wave_sync();
+        // value sums: D/8 lanes per token row (16-byte loads of 8 channels), TG
+        // tokens per load instruction, the token groups summed at the end
+        const int nvalid = min(T, L - page * T);  // tokens past the end may hold anything
+        const uint16_t* vp = static_cast<const uint16_t*>(a.v_fp16) + ((int64_t)id * a.H + h) * T * D;
+        const int tg = lane / LPT, cc = lane % LPT;
+        // branch-free: a token past the end has weight 0 (its score is
+        // -inf) and reads the last valid token's values instead of its own
+#pragma unroll 8
+        for (int t0 = 0; t0 < T; t0 += TG) {
+            const int t = t0 + tg;
+            const uint4 w = *reinterpret_cast<const uint4*>(vp + (int64_t)min(t, nvalid - 1) * D + 8 * cc);
+            const float4 pv = pf[t];
+            const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int kk = 0; kk < 8; kk++) {
+                const float v = half_bits_to_float((ww[kk >> 1] >> (16 * (kk & 1))) & 0xffffu);
+                accp[kk][0] = fmaf(pv.x, v, accp[kk][0]);
+                accp[kk][1] = fmaf(pv.y, v, accp[kk][1]);
+                accp[kk][2] = fmaf(pv.z, v, accp[kk][2]);
+                accp[kk][3] = fmaf(pv.w, v, accp[kk][3]);
+            }
+        }
+    }
+    // sum the token groups (lane bits above log2(LPT))
+#pragma unroll
+    for (int kk = 0; kk < 8; kk++)
+#pragma unroll
+        for (int g = 0; g < G; g++) {
+            float v = accp[kk][g];
+            if constexpr (TG >= 4) v += xor_lane<4>(v);
+            if constexpr (TG >= 2) v += lane_bcast32(v);
+            accp[kk][g] = v;
+        }
+    float* wsp = a.ws + (int64_t)a.B * Hq * D;
+#pragma unroll
+    for (int g = 0; g < G; g++) {
+        const float lt = wave_sum_all(lsum[g]);
+        float* o = wsp + (((int64_t)b * Hq + h * G + g) * (a.nsplit + a.nfsplit) + a.nsplit + f) * WS;
+        if (lane == 0) {
+            o[0] = mx[g];
+            o[1] = lt;
+        }
+#pragma unroll
+        for (int sv = 0; sv < NS; sv++) o[4 + 64 * sv + lane] = 0.f;
+        if (lane < LPT) {
+#pragma unroll
+            for (int c = 0; c < 8; c++) o[4 + D + 8 * lane + c] = accp[c][g];
+        }
     }
 }
 
@@ -482,13 +614,14 @@ __global__ void __launch_bounds__(D) decode_combine_kernel(const float* __restri
     const int j = threadIdx.x;
     const float* base = ws + (int64_t)bh * nsplit * WS;
     float M = -INFINITY;
+#pragma unroll 8
     for (int s = 0; s < nsplit; s++) M = fmaxf(M, base[s * WS]);
     float Ls = 0.f, r = 0.f, pl = 0.f;
     if (M != -INFINITY) {
+#pragma unroll 8
         for (int s = 0; s < nsplit; s++) {
             const float ms = base[s * WS];
-            if (ms == -INFINITY) continue;
-            const float e = exp2f(ms - M);
+            const float e = ms == -INFINITY ? 0.f : exp2f(ms - M);  // empty splits hold zeros
             Ls = fmaf(base[s * WS + 1], e, Ls);
             r = fmaf(base[s * WS + 4 + j], e, r);
             pl = fmaf(base[s * WS + 4 + D + j], e, pl);
@@ -512,12 +645,16 @@ hipError_t launch_gqa(const DecodeArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((qrot_kernel<D>), dim3(a.B * a.Hq), dim3(D / 2), 0, st, a.q, a.q_bf16, a.ws);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    dim3 grid(a.nsplit, a.H, a.B);
-    hipLaunchKernelGGL((decode_split_kernel<D, T, KB, VB>), grid, dim3(64), 0, st, a);
+    hipLaunchKernelGGL((decode_split_kernel<D, T, KB, VB>), dim3(a.nsplit, a.H, a.B), dim3(64), 0, st, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (a.nfsplit > 0) {
+        hipLaunchKernelGGL((decode_fp16_kernel<D, T>), dim3(a.nfsplit, a.H, a.B), dim3(64), 0, st, a);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(a.B * a.Hq), dim3(D), 0, st,
-                       a.ws + (int64_t)a.B * a.Hq * D, a.out, a.nsplit);
+                       a.ws + (int64_t)a.B * a.Hq * D, a.out, a.nsplit + a.nfsplit);
     return hipGetLastError();
 }
 
@@ -556,9 +693,17 @@ void decode_plan(int D, int H, int G, int mla, int B, int max_pages, int T, int*
     if (*nsplit < 1) *nsplit = 1;
 }
 
-// fp32 rotated queries [B][Hq][D], then split partials [B][Hq][nsplit][2D + 4]
-size_t decode_workspace_floats(int D, int Hq, int B, int nsplit) {
-    return (size_t)B * Hq * D + (size_t)B * Hq * nsplit * (2 * D + 4);
+int decode_fp16_pages(int T, int sink, int tail, int max_pages) {
+    // fp16 tokens of a sequence: fewer than sink + tail + T (with quantized
+    // pages: sink + tail + T - 1 at most), the sink a whole number of pages
+    const int n = sink / T + (tail + 2 * T - 2) / T;
+    return n < max_pages ? n : max_pages;
+}
+
+// fp32 rotated queries [B][Hq][D], then split partials
+// [B][Hq][nsplit + nfsplit][2D + 4] (quantized-page splits, then fp16-page slots)
+size_t decode_workspace_floats(int D, int Hq, int B, int nsplit, int nfsplit) {
+    return (size_t)B * Hq * D + (size_t)B * Hq * (nsplit + nfsplit) * (2 * D + 4);
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {

@@ -30,7 +30,8 @@ struct DecodeArgs {
     int D, T, k_bits, v_bits, sink, tail, H, mla;
     int G;            // query heads per KV head (MLA: all query heads)
     int B, Hq, max_pages;
-    int nsplit;       // splits of each sequence
+    int nsplit;       // splits of each sequence (GQA: over its quantized pages)
+    int nfsplit;      // GQA: fp16-page slots of each sequence (one workgroup each)
     int pps;          // pages per split
     const void* k_records;
     const void* v_records;
@@ -48,7 +49,9 @@ struct DecodeArgs {
 
 // Split plan shared by the workspace query and the launch.
 void decode_plan(int D, int H, int G, int mla, int B, int max_pages, int T, int* nsplit, int* pps);
-size_t decode_workspace_floats(int D, int Hq, int B, int nsplit);
+// GQA: the most fp16 (sink and tail) pages a sequence can have.
+int decode_fp16_pages(int T, int sink, int tail, int max_pages);
+size_t decode_workspace_floats(int D, int Hq, int B, int nsplit, int nfsplit);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
 
 // MLA: fp16 rotated queries [B][Hq][512] then split partials [B][Hq][nsplit][516] fp32.

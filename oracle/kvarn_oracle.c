@@ -144,11 +144,13 @@ void orc_rotate(int T, int D, const double *X, double *Y)
 {
     double *H = (double *)malloc(sizeof(double) * (size_t)D * D);
     orc_hadamard_matrix(D, H);
+    /* H is symmetric (H[k][j] = H[j][k]); reading row j keeps the same
+     * operands in the same summation order with unit-stride access. */
     for (int t = 0; t < T; t++) {
         for (int j = 0; j < D; j++) {
             double acc = 0.0;
             for (int k = 0; k < D; k++)
-                acc += X[(int64_t)t * D + k] * H[(int64_t)k * D + j];
+                acc += X[(int64_t)t * D + k] * H[(int64_t)j * D + k];
             Y[(int64_t)t * D + j] = acc;
         }
     }
