@@ -33,24 +33,31 @@ __device__ __forceinline__ float lane_bcast32(float v) {
     return i2f(__builtin_amdgcn_ds_bpermute(((int)(threadIdx.x & 63) ^ 32) << 2, f2i(v)));
 }
 
+// Reductions over the 64 lanes, every lane ending with the result, entirely
+// on the VALU: DPP inside each 16-lane row (xor 1, xor 2, then rotations by 4
+// and 8), then v_permlane16_swap and v_permlane32_swap, each of which, given
+// the same value twice, returns the halves whose combination is v op v[l ^ 16]
+// (resp. v[l ^ 32]).
 __device__ __forceinline__ float wave_max_all(float v) {
-    v = fmaxf(v, xor_lane<0>(v));
-    v = fmaxf(v, xor_lane<1>(v));
-    v = fmaxf(v, xor_lane<2>(v));
-    v = fmaxf(v, xor_lane<3>(v));
-    v = fmaxf(v, xor_lane<4>(v));
-    v = fmaxf(v, lane_bcast32(v));
-    return v;
+    v = fmaxf(v, i2f(__builtin_amdgcn_mov_dpp(f2i(v), 0xB1, 0xF, 0xF, false)));   // quad_perm xor 1
+    v = fmaxf(v, i2f(__builtin_amdgcn_mov_dpp(f2i(v), 0x4E, 0xF, 0xF, false)));   // quad_perm xor 2
+    v = fmaxf(v, i2f(__builtin_amdgcn_mov_dpp(f2i(v), 0x124, 0xF, 0xF, false)));  // row_ror 4
+    v = fmaxf(v, i2f(__builtin_amdgcn_mov_dpp(f2i(v), 0x128, 0xF, 0xF, false)));  // row_ror 8
+    const auto a16 = __builtin_amdgcn_permlane16_swap((unsigned)f2i(v), (unsigned)f2i(v), false, false);
+    v = fmaxf(i2f((int)a16[0]), i2f((int)a16[1]));
+    const auto a32 = __builtin_amdgcn_permlane32_swap((unsigned)f2i(v), (unsigned)f2i(v), false, false);
+    return fmaxf(i2f((int)a32[0]), i2f((int)a32[1]));
 }
 
 __device__ __forceinline__ float wave_sum_all(float v) {
-    v += xor_lane<0>(v);
-    v += xor_lane<1>(v);
-    v += xor_lane<2>(v);
-    v += xor_lane<3>(v);
-    v += xor_lane<4>(v);
-    v += lane_bcast32(v);
-    return v;
+    v += i2f(__builtin_amdgcn_update_dpp(0, f2i(v), 0xB1, 0xF, 0xF, true));
+    v += i2f(__builtin_amdgcn_update_dpp(0, f2i(v), 0x4E, 0xF, 0xF, true));
+    v += i2f(__builtin_amdgcn_update_dpp(0, f2i(v), 0x124, 0xF, 0xF, true));
+    v += i2f(__builtin_amdgcn_update_dpp(0, f2i(v), 0x128, 0xF, 0xF, true));
+    const auto a16 = __builtin_amdgcn_permlane16_swap((unsigned)f2i(v), (unsigned)f2i(v), false, false);
+    v = i2f((int)a16[0]) + i2f((int)a16[1]);
+    const auto a32 = __builtin_amdgcn_permlane32_swap((unsigned)f2i(v), (unsigned)f2i(v), false, false);
+    return i2f((int)a32[0]) + i2f((int)a32[1]);
 }
 
 __device__ __forceinline__ float half_bits_to_float(uint32_t h) {
