@@ -61,13 +61,33 @@ __device__ __forceinline__ float row_sum(float v) {
     return v;
 }
 
+// min and max of each of the lane's 4 rows over the D/16 lanes of a token
+// row.  Lane bits 0, 1 and 3 take one fused v_min/v_max_f32_dpp each (the
+// register is its own DPP source; s_nop 1 covers the VALU-write-then-DPP-read
+// wait states); bits 2 and 4 go through ds_swizzle.
+#define KVARN_MINMAX_DPP8(CTRL)                                                                 \
+    asm volatile("s_nop 1\n\t"                                                                   \
+                 "v_min_f32_dpp %0, %0, %0 " CTRL " row_mask:0xf bank_mask:0xf\n\t"             \
+                 "v_max_f32_dpp %4, %4, %4 " CTRL " row_mask:0xf bank_mask:0xf\n\t"             \
+                 "v_min_f32_dpp %1, %1, %1 " CTRL " row_mask:0xf bank_mask:0xf\n\t"             \
+                 "v_max_f32_dpp %5, %5, %5 " CTRL " row_mask:0xf bank_mask:0xf\n\t"             \
+                 "v_min_f32_dpp %2, %2, %2 " CTRL " row_mask:0xf bank_mask:0xf\n\t"             \
+                 "v_max_f32_dpp %6, %6, %6 " CTRL " row_mask:0xf bank_mask:0xf\n\t"             \
+                 "v_min_f32_dpp %3, %3, %3 " CTRL " row_mask:0xf bank_mask:0xf\n\t"             \
+                 "v_max_f32_dpp %7, %7, %7 " CTRL " row_mask:0xf bank_mask:0xf"                 \
+                 : "+v"(mn[0]), "+v"(mn[1]), "+v"(mn[2]), "+v"(mn[3]), "+v"(mx[0]), "+v"(mx[1]),   \
+                   "+v"(mx[2]), "+v"(mx[3]))
+
 template <int CGB>
-__device__ __forceinline__ void row_minmax(float& mn, float& mx) {
-    mn = fminf(mn, xor_lane<0>(mn)); mx = fmaxf(mx, xor_lane<0>(mx));
-    mn = fminf(mn, xor_lane<1>(mn)); mx = fmaxf(mx, xor_lane<1>(mx));
-    mn = fminf(mn, xor_lane<3>(mn)); mx = fmaxf(mx, xor_lane<3>(mx));
-    if constexpr (CGB >= 4) { mn = fminf(mn, xor_lane<2>(mn)); mx = fmaxf(mx, xor_lane<2>(mx)); }
-    if constexpr (CGB >= 5) { mn = fminf(mn, xor_lane<4>(mn)); mx = fmaxf(mx, xor_lane<4>(mx)); }
+__device__ __forceinline__ void row_minmax4(float (&mn)[4], float (&mx)[4]) {
+    KVARN_MINMAX_DPP8("quad_perm:[1,0,3,2]");
+    KVARN_MINMAX_DPP8("quad_perm:[2,3,0,1]");
+    KVARN_MINMAX_DPP8("row_ror:8");
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+        if constexpr (CGB >= 4) { mn[r] = fminf(mn[r], xor_lane<2>(mn[r])); mx[r] = fmaxf(mx[r], xor_lane<2>(mx[r])); }
+        if constexpr (CGB >= 5) { mn[r] = fminf(mn[r], xor_lane<4>(mn[r])); mx[r] = fmaxf(mx[r], xor_lane<4>(mx[r])); }
+    }
 }
 
 // Cross-lane butterfly on lane bit BIT for 16 values: v <- v + s * partner,
@@ -111,28 +131,18 @@ __device__ __forceinline__ void xbutterfly(float (&y)[QR][QC], int lane) {
     for (int r = 0; r < QR; r++) {
         xbutterfly8<BIT>(&y[r][0], s);
         xbutterfly8<BIT>(&y[r][8], s);
+        // ds_swizzle stages: keep at most one row's 16 exchanges in flight
+        // (hoisting all 64 would need 64 more registers)
+        if constexpr (BIT == 2 || BIT == 4) __builtin_amdgcn_sched_barrier(0);
     }
 }
 
-__device__ __forceinline__ bool usable(float s) { return s > 0.f && s <= 3.0e38f; }
+// finite and > 0: positive denormal or normal (one v_cmp_class)
+__device__ __forceinline__ bool usable(float s) { return __builtin_amdgcn_classf(s, 0x180); }
 
 __device__ __forceinline__ uint32_t fbits(float x) { return __builtin_bit_cast(uint32_t, x); }
 
-// Codes sit in the low bits of magic-rounded floats (junk from bit 22 up).
-// Pack n consecutive codes of width B into the low n*B bits; n*B <= 16 keeps
-// the junk of every addend above the result.
-template <int B>
-__device__ __forceinline__ uint32_t pack2(uint32_t f0, uint32_t f1) {  // low 2B bits clean
-    return (f1 << B) + f0;
-}
-
-__device__ __forceinline__ uint32_t bytes4(uint32_t b0, uint32_t b1, uint32_t b2, uint32_t b3) {
-    // byte 0 of each argument -> one dword
-    const uint32_t lo = __builtin_amdgcn_perm(b1, b0, 0x0c0c0400u);
-    const uint32_t hi = __builtin_amdgcn_perm(b3, b2, 0x0c0c0400u);
-    return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
-}
-
+// 6-bit codes sit in the low bits of magic-rounded floats (junk from bit 22 up).
 // 4 codes of 6 bits -> low 24 bits (clean above).
 __device__ __forceinline__ uint32_t pack6x4(uint32_t f0, uint32_t f1, uint32_t f2, uint32_t f3) {
     const uint32_t x01 = ((f1 << 6) + f0) & 0xfffu;
@@ -148,13 +158,36 @@ struct MfmaRotation {
     static constexpr bool on = D == 128;
 };
 
-// LDS unit (4 floats) of rotated column j (0..63 of the half being moved),
-// rows 4 ru .. 4 ru + 3 of a wave's 32 rows: column-major with the row unit
-// xor-ed with column bits, so that the MFMA-layout stores and the
-// register-layout loads each touch every bank once.
-__device__ __forceinline__ int rot_unit(int j, int ru) {
-    return 8 * j + (ru ^ ((j ^ (j >> 3)) & 7));
+// B operands of the rotation.  H_128 = H_4 (x) H_32 over channel j = 32 v + u
+// (popcount of (32 v + u) & (32 v' + u') splits over the two factors).  Lane
+// l of a 16x16x32 B operand holds rows k = 8 (l >> 4) + i, i = 0..7, of
+// column n = l & 15; with k = u and n = u' - 16 nb that is
+// H_32[u][u'] = (-1)^(popcount(i & n & 7) + ((l >> 4) & 1) (n >> 3) + (l >> 5) nb).
+// Entry [nb + 2 s][l] is lane l's operand for column block nb times (-1)^s,
+// the H_4 sign of an input group / output group pair; 8 fp16 +-1 per lane.
+struct RotOperands {
+    uint32_t w[4][64][4];
+};
+constexpr RotOperands make_rot_operands() {
+    RotOperands t{};
+    for (int sn = 0; sn < 4; sn++) {
+        const int nb = sn & 1, neg = sn >> 1;
+        for (int l = 0; l < 64; l++) {
+            const int n = l & 15, g4 = l >> 4;
+            for (int k = 0; k < 4; k++) {
+                uint32_t d = 0x3C003C00u;
+                for (int half = 0; half < 2; half++) {
+                    const int i = 2 * k + half;
+                    const int par = __builtin_popcount((unsigned)(i & n & 7)) + ((g4 & 1) & (n >> 3)) + ((g4 >> 1) & nb) + neg;
+                    if (par & 1) d |= 0x8000u << (16 * half);
+                }
+                t.w[sn][l][k] = d;
+            }
+        }
+    }
+    return t;
 }
+__device__ const RotOperands kRotOperands = make_rot_operands();
 
 template <int D, int T>
 struct TileShape {
@@ -175,7 +208,103 @@ struct TileShape {
     static constexpr int SMEM = MfmaRotation<D>::on ? PART_OFF + SMEM_PART : (SMEM_A > SMEM_ROT ? SMEM_A : SMEM_ROT);
 };
 
-// One tile -> one record.  smem: TileShape::SMEM bytes; vec: 3*D floats.
+// LDS position of channel ch in a slot of column partials: 4-float chunks xor-permuted inside each 8-chunk (32-float) window
+// with tau = bit 5 of ch | (bit 7 of ch ^ slot) << 1.  The lanes of any
+// 8-lane group (which differ in channel-group bits 0, 1 and 3, or 0 and 1
+// and the partial slot for D = 128) then touch 8 different 4-bank groups.
+__device__ __forceinline__ int chan_pos(int ch, int slot) {
+    const int tau = ((ch >> 5) & 1) | ((((ch >> 7) ^ slot) & 1) << 1);
+    return (((ch >> 2) ^ tau) << 2) | (ch & 3);
+}
+
+// D = 128: y = X H for this lane's 4 rows x 16 channels (MFMA, then LDS;
+// the wave's own 8 KB of smem).
+template <int D, int T>
+__device__ __forceinline__ void mfma_rotate(const uint16_t* __restrict__ tile, uint8_t* smem, int lane, int wave,
+                                            int cg, int rg, float (&y)[QR][QC]) {
+    using S = TileShape<D, T>;
+    constexpr int RGB = S::RGB, CGB = S::CGB, RPW = S::RPW;
+    // ---- stages 1-2: y = X H on the MFMA, then into the register layout ----
+    // Output group v' (channels 32 v' .. 32 v' + 31) of a 16-row block is
+    // sum_v X_v H_32 (-1)^popcount(v & v'): four chained MFMAs, the H_4
+    // sign carried by the B operand.
+    typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+    typedef float f4 __attribute__((ext_vector_type(4)));
+    static_assert(RGB == 3 && CGB == 3 && RPW == 32, "rotation layout assumes 32 rows x 128 channels per wave");
+    const int l16 = lane & 15, g4 = lane >> 4;
+    h8 hb[4];
+#pragma unroll
+    for (int sn = 0; sn < 4; sn++)
+        hb[sn] = __builtin_bit_cast(h8, *reinterpret_cast<const uint4*>(kRotOperands.w[sn][lane]));
+    f4 z[2][4][2];  // [token block][output group v'][nb]
+#pragma unroll
+    for (int tb = 0; tb < 2; tb++) {
+        const uint16_t* xr = tile + (int64_t)(wave * RPW + 16 * tb + l16) * D + 8 * g4;
+        h8 xa[4];
+#pragma unroll
+        for (int v = 0; v < 4; v++) xa[v] = *reinterpret_cast<const h8*>(xr + 32 * v);
+#pragma unroll
+        for (int v = 0; v < 4; v++)
+#pragma unroll
+            for (int vo = 0; vo < 4; vo++)
+#pragma unroll
+                for (int nb = 0; nb < 2; nb++) {
+                    const int sn = nb + 2 * (__builtin_popcount((unsigned)(v & vo)) & 1);
+                    z[tb][vo][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                        xa[v], hb[sn], v == 0 ? f4{0.f, 0.f, 0.f, 0.f} : z[tb][vo][nb], 0, 0, 0);
+                }
+    }
+    // Through LDS, 64 columns at a time.  Column j (of the half), rows
+    // 4 ru .. 4 ru + 3 of the wave's 32 rows sit in the 16-byte unit
+    // 8 j + (ru ^ ((j ^ (j >> 3)) & 7)): the MFMA-layout stores and the
+    // register-layout loads each touch every bank once.  For the stores
+    // (j = 32 vq + 16 nb + l16, ru = 4 tb + g4) and the loads
+    // (j = 16 (cg & 3) + c, ru = rg) the unit splits into a per-lane part
+    // and a compile-time xor and offset.
+    const uint32_t wbase = (uint32_t)wave * (uint32_t)(RPW * D / 2 * 4);
+    const uint32_t wa = wbase + 128u * (uint32_t)l16 + 16u * (uint32_t)(g4 ^ (l16 & 7) ^ (l16 >> 3));
+    const uint32_t cq = (uint32_t)(lane & 3);  // cg & 3
+    const uint32_t ra = wbase + 2048u * cq + 16u * ((uint32_t)rg ^ (2u * cq));
+#pragma unroll
+    for (int half = 0; half < 2; half++) {
+        // output columns 32 v + 16 nb + l16 with v = 2 half + vq
+#pragma unroll
+        for (int tb = 0; tb < 2; tb++)
+#pragma unroll
+            for (int vq = 0; vq < 2; vq++)
+#pragma unroll
+                for (int nb = 0; nb < 2; nb++)
+                    *reinterpret_cast<f4*>(smem + ((wa ^ (uint32_t)(64 * (tb ^ vq) + 32 * nb)) + 4096u * vq + 2048u * nb)) =
+                        z[tb][2 * half + vq][nb];
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        if ((cg >> 2) == half) {
+#pragma unroll
+            for (int c = 0; c < QC; c++) {
+                const f4 v = *reinterpret_cast<const f4*>(smem + ((ra ^ (uint32_t)(16 * ((c & 7) ^ (c >> 3)))) + 128u * c));
+#pragma unroll
+                for (int r = 0; r < QR; r++) y[r][c] = v[r];
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+}
+
+// Position of channel ch in the b and sqrt(b) vectors: 4 pad floats after
+// every 32 channels, so that the 16-byte broadcast reads of channel groups
+// 16 cg .. 16 cg + 15 (cg = 0..3 within an 8-lane group) start in different
+// bank quads.
+__device__ __forceinline__ constexpr int vec_pos(int ch) { return ch + 4 * (ch >> 5); }
+template <int D>
+struct VecShape {
+    static constexpr int PADDED = D + D / 8;       // floats per padded vector
+    static constexpr int FLOATS = 2 * PADDED + D / 2;  // b, sqrt b, fp16 column scales
+};
+
+// One tile -> one record.  smem: TileShape::SMEM bytes; vec: VecShape::FLOATS floats.
 template <int D, int T, int BITS, bool CHMAJOR>
 __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ tile, uint8_t* __restrict__ rec,
                                               uint8_t* smem, float* vec, int32_t n_iters) {
@@ -191,8 +320,8 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ tile,
 
     float* colpart = reinterpret_cast<float*>(smem + S::PART_OFF);
     float* bvec = vec;           // b_j = exp(-2 lc_j), unnormalized basis
-    float* icvec = vec + D;      // (+-1 per channel) * sqrt(b_j): multiplies y into W
-    uint16_t* cvec = reinterpret_cast<uint16_t*>(vec + 2 * D);  // fp16 column scales
+    float* icvec = vec + VecShape<D>::PADDED;  // (+-1 per channel) * sqrt(b_j): multiplies y into W
+    uint16_t* cvec = reinterpret_cast<uint16_t*>(vec + 2 * VecShape<D>::PADDED);  // fp16 column scales
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -209,84 +338,8 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ tile,
 
     float y[QR][QC];
     if constexpr (MfmaRotation<D>::on) {
-        // ---- stages 1-2: y = X H on the MFMA, then into the register layout ----
-        // H_128 = H_4 (x) H_32 over channel j = 32 v + u: the MFMA takes each
-        // 32-channel group v through H_32 (k = u = 8 g4 + i, n = u' = 16 nb + l16,
-        // H_32[u][u'] = (-1)^popcount(i & l16 & 7) (-1)^(g4_0 l16_3) (-1)^(g4_1 nb):
-        // one per-lane pattern per nb), and the 4 groups meet in an in-lane
-        // 4-point butterfly.
-        typedef _Float16 h8 __attribute__((ext_vector_type(8)));
-        typedef float f4 __attribute__((ext_vector_type(4)));
-        static_assert(RGB == 3 && CGB == 3 && RPW == 32, "rotation layout assumes 32 rows x 128 channels per wave");
-        const int l16 = lane & 15, g4 = lane >> 4;
-        // bit i of wm is parity(i & l16 & 7) (a row of the 8x8 Hadamard matrix)
-        const uint32_t m7 = (uint32_t)(l16 & 7);
-        const uint32_t wm = ((m7 & 1u) ? 0xAAu : 0u) ^ ((m7 & 2u) ? 0xCCu : 0u) ^ ((m7 & 4u) ? 0xF0u : 0u);
-        h8 hp[2];
-#pragma unroll
-        for (int nb = 0; nb < 2; nb++) {
-            const uint32_t flip = ((g4 & 1) & (l16 >> 3)) ^ ((g4 >> 1) & nb);
-            const uint32_t sw = wm ^ (flip ? 0xFFu : 0u);
-            uint32_t d[4];
-#pragma unroll
-            for (int k = 0; k < 4; k++) d[k] = 0x3C003C00u | (((sw >> (2 * k)) & 1u) << 15) | (((sw >> (2 * k + 1)) & 1u) << 31);
-            hp[nb] = __builtin_bit_cast(h8, make_uint4(d[0], d[1], d[2], d[3]));
-        }
-        // the wave's 32 x 128 block moves in two halves of 64 columns; lanes
-        // whose 16 channels lie in the half read it
-        // the wave's 32 x 128 block moves in two halves of 64 columns; lanes
-        // whose 16 channels lie in the half read it
-        float* yt = reinterpret_cast<float*>(smem) + wave * (RPW * D / 2);
-        f4 z[2][4][2];  // [token block][channel group v][nb]
-#pragma unroll
-        for (int tb = 0; tb < 2; tb++) {
-            const uint16_t* xr = tile + (int64_t)(wave * RPW + 16 * tb + l16) * D + 8 * g4;
-#pragma unroll
-            for (int v = 0; v < 4; v++) {
-                const h8 xa = *reinterpret_cast<const h8*>(xr + 32 * v);
-#pragma unroll
-                for (int nb = 0; nb < 2; nb++)
-                    z[tb][v][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa, hp[nb], f4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-            }
-        }
-        // H_4 across the groups: z[.][v'][.] becomes output group v'
-#pragma unroll
-        for (int tb = 0; tb < 2; tb++)
-#pragma unroll
-            for (int nb = 0; nb < 2; nb++) {
-                const f4 a0 = z[tb][0][nb] + z[tb][1][nb], a1 = z[tb][0][nb] - z[tb][1][nb];
-                const f4 a2 = z[tb][2][nb] + z[tb][3][nb], a3 = z[tb][2][nb] - z[tb][3][nb];
-                z[tb][0][nb] = a0 + a2;
-                z[tb][1][nb] = a1 + a3;
-                z[tb][2][nb] = a0 - a2;
-                z[tb][3][nb] = a1 - a3;
-            }
-#pragma unroll
-        for (int half = 0; half < 2; half++) {
-            // output columns 32 v + 16 nb + l16 with v = 2 half + (0, 1)
-#pragma unroll
-            for (int tb = 0; tb < 2; tb++)
-#pragma unroll
-                for (int vq = 0; vq < 2; vq++)
-#pragma unroll
-                    for (int nb = 0; nb < 2; nb++)
-                        *reinterpret_cast<f4*>(yt + 4 * rot_unit(32 * vq + 16 * nb + l16, 4 * tb + g4)) = z[tb][2 * half + vq][nb];
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            if ((cg >> 2) == half) {
-#pragma unroll
-                for (int c = 0; c < QC; c++) {
-                    const f4 v = *reinterpret_cast<const f4*>(yt + 4 * rot_unit((ch0 & 63) + c, rg));
-#pragma unroll
-                    for (int r = 0; r < QR; r++) y[r][c] = v[r];
-                }
-            }
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        }
-        if (tid < D) bvec[tid] = 1.0f / (float)D;  // c_j = 1 in the normalized basis
+        mfma_rotate<D, T>(tile, smem, lane, wave, cg, rg, y);
+        if (tid < D) bvec[vec_pos(tid)] = 1.0f / (float)D;  // c_j = 1 in the normalized basis
     } else {
         // ---- stage 1: load the fp16 tile ---------------------------------------
 #pragma unroll
@@ -300,7 +353,7 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ tile,
                 y[r][2 * k + 1] = half_bits_to_float(w[k] >> 16);
             }
         }
-        if (tid < D) bvec[tid] = 1.0f / (float)D;  // c_j = 1 in the normalized basis
+        if (tid < D) bvec[vec_pos(tid)] = 1.0f / (float)D;  // c_j = 1 in the normalized basis
 
         // ---- stage 2: Hadamard rotation (unnormalized butterflies) -------------
 #pragma unroll
@@ -335,7 +388,10 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ tile,
             if constexpr (!KEEP_Y) negbits[r] |= (y[r][c] < 0.f ? 1u : 0u) << c;
         }
 
-    float aw[QR] = {1.f, 1.f, 1.f, 1.f};
+    // Row weights are kept as a / D (exact: D is a power of two), so the row
+    // step is a bare reciprocal; the column step's T / D restores b.
+    constexpr float kInvD = 1.0f / (float)D;
+    float aw[QR] = {kInvD, kInvD, kInvD, kInvD};
     float bw[QC];
     for (int it = 0; it < n_iters; it++) {
         const bool last = it == n_iters - 1;
@@ -348,42 +404,49 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ tile,
             for (int r = 1; r < QR; r++) s = fmaf(A[r][c], aw[r], s);
             p[c] = s;
         }
-        // reduce over lane bit 5 (and 4) with permlane swaps: each lane keeps
-        // half (a quarter) of the columns, summed over the swapped lanes
+        // reduce over lane bit 5 (and 4) with permlane swaps: the lower half
+        // keeps the first argument's column, the upper half the second's, so
+        // a lane ends with channels ch0 + 8 b5 (+ 4 b4) + 0..NPART-1, stored
+        // as 4-float chunks
         float q[8];
 #pragma unroll
         for (int k = 0; k < 8; k++) {
-            auto s2 = __builtin_amdgcn_permlane32_swap((unsigned)f2i(p[2 * k]),
-                                                       (unsigned)f2i(p[2 * k + 1]), false, false);
+            auto s2 = __builtin_amdgcn_permlane32_swap((unsigned)f2i(p[k]), (unsigned)f2i(p[k + 8]), false, false);
             q[k] = i2f((int)s2[0]) + i2f((int)s2[1]);
         }
         const int b5 = (lane >> 5) & 1;
         const int b4 = (lane >> 4) & 1;
         const int sub = (NSUB == 2) ? ((lane >> 2) & 1) : 0;
-        float* part = colpart + (wave * NSUB + sub) * D + ch0;
+        const int slot = wave * NSUB + sub;
+        float* part = colpart + slot * D;
         if constexpr (NPART == 4) {
+            float4 v;
+            float* vv = reinterpret_cast<float*>(&v);
 #pragma unroll
             for (int k = 0; k < 4; k++) {
-                auto s2 = __builtin_amdgcn_permlane16_swap((unsigned)f2i(q[2 * k]),
-                                                           (unsigned)f2i(q[2 * k + 1]), false, false);
-                part[4 * k + 2 * b4 + b5] = i2f((int)s2[0]) + i2f((int)s2[1]);
+                auto s2 = __builtin_amdgcn_permlane16_swap((unsigned)f2i(q[k]), (unsigned)f2i(q[k + 4]), false, false);
+                vv[k] = i2f((int)s2[0]) + i2f((int)s2[1]);
             }
+            *reinterpret_cast<float4*>(part + chan_pos(ch0 + 8 * b5 + 4 * b4, slot)) = v;
         } else {
 #pragma unroll
-            for (int k = 0; k < 8; k++) part[2 * k + b5] = q[k];
+            for (int h = 0; h < 2; h++)
+                *reinterpret_cast<float4*>(part + chan_pos(ch0 + 8 * b5 + 4 * h, slot)) =
+                    make_float4(q[4 * h], q[4 * h + 1], q[4 * h + 2], q[4 * h + 3]);
         }
         __syncthreads();
         if (tid < D) {
             float s = 0.f;
 #pragma unroll
-            for (int w = 0; w < NW * NSUB; w++) s += colpart[w * D + tid];
-            float b = bvec[tid];
-            if (usable(s)) b = (float)T * __builtin_amdgcn_rcpf(s);
-            bvec[tid] = b;
+            for (int w = 0; w < NW * NSUB; w++) s += colpart[w * D + chan_pos(tid, w)];
+            const int pt = vec_pos(tid);
+            float b = bvec[pt];
+            if (usable(s)) b = ((float)T / (float)D) * __builtin_amdgcn_rcpf(s);
+            bvec[pt] = b;
             if (last) {
                 // channel sign left by the sign-tracked butterflies: (-1)^popcount(j >> 4)
                 const float sg = (!MfmaRotation<D>::on && (__builtin_popcount((unsigned)tid >> 4) & 1)) ? -1.f : 1.f;
-                icvec[tid] = sg * sqrtf(b);
+                icvec[pt] = sg * sqrtf(b);
                 cvec[tid] = (uint16_t)float_to_half_bits(__builtin_amdgcn_rsqf((float)D * b));
             }
         }
@@ -391,7 +454,7 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ tile,
         if (last) break;
 #pragma unroll
         for (int c4 = 0; c4 < QC / 4; c4++) {
-            float4 v = *reinterpret_cast<const float4*>(bvec + ch0 + 4 * c4);
+            float4 v = *reinterpret_cast<const float4*>(bvec + vec_pos(ch0) + 4 * c4);
             bw[4 * c4 + 0] = v.x;
             bw[4 * c4 + 1] = v.y;
             bw[4 * c4 + 2] = v.z;
@@ -404,7 +467,8 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ tile,
 #pragma unroll
             for (int c = 1; c < QC; c++) s = fmaf(A[r][c], bw[c], s);
             s = row_sum<CGB>(s);
-            if (usable(s)) aw[r] = (float)D * __builtin_amdgcn_rcpf(s);
+            const float rc = __builtin_amdgcn_rcpf(s);
+            aw[r] = usable(s) ? rc : aw[r];
         }
     }
 
@@ -412,69 +476,99 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ tile,
     float ic[QC];
 #pragma unroll
     for (int c4 = 0; c4 < QC / 4; c4++) {
-        float4 v = *reinterpret_cast<const float4*>(icvec + ch0 + 4 * c4);
+        float4 v = *reinterpret_cast<const float4*>(icvec + vec_pos(ch0) + 4 * c4);
         ic[4 * c4 + 0] = v.x;
         ic[4 * c4 + 1] = v.y;
         ic[4 * c4 + 2] = v.z;
         ic[4 * c4 + 3] = v.w;
     }
     uint8_t* img = smem;  // image of the record's code block
+    // 2- and 4-bit codes: v_cvt_pk_u8_f32 rounds half to even, clamps to
+    // [0, 255] and drops the byte into place; 6-bit codes: magic-number
+    // rounding (x + 1.5 * 2^23 keeps rint(x) in the low mantissa bits).
+    constexpr bool PKU8 = BITS != 6;
     uint32_t sz[QR];
-    uint32_t fq[QR][QC];  // magic-rounded codes
+    // W = y / c, then u = (W - mn) / s, then (6-bit) the magic-rounded code
+    // bits, all in place in the array that held y (or y^2 for D = 512)
+    float (&u)[QR][QC] = *[&]() -> float(*)[QR][QC] {
+        if constexpr (KEEP_Y) return &y; else return &A;
+    }();
+    {
+        float mn[QR], mx[QR];
 #pragma unroll
-    for (int r = 0; r < QR; r++) {
-        float W[QC];
+        for (int r = 0; r < QR; r++) {
 #pragma unroll
-        for (int c = 0; c < QC; c++) {
-            float yv;
-            if constexpr (KEEP_Y) {
-                yv = y[r][c];
-            } else {
-                yv = sqrtf(A[r][c]);
-                if ((negbits[r] >> c) & 1u) yv = -yv;
+            for (int c = 0; c < QC; c++) {
+                float yv;
+                if constexpr (KEEP_Y) {
+                    yv = y[r][c];
+                } else {
+                    yv = sqrtf(A[r][c]);
+                    if ((negbits[r] >> c) & 1u) yv = -yv;
+                }
+                u[r][c] = yv * ic[c];
             }
-            W[c] = yv * ic[c];
-        }
-        float mn = W[0], mx = W[0];
+            mn[r] = u[r][0];
+            mx[r] = u[r][0];
 #pragma unroll
-        for (int c = 1; c < QC; c++) {
-            mn = fminf(mn, W[c]);
-            mx = fmaxf(mx, W[c]);
+            for (int c = 1; c < QC; c++) {
+                mn[r] = fminf(mn[r], u[r][c]);
+                mx[r] = fmaxf(mx[r], u[r][c]);
+            }
         }
-        row_minmax<CGB>(mn, mx);
-        mn += 0.0f;  // a zero row stores +0, not the -0 of a sign-flipped channel
-        const float range = mx - mn;
-        const float s = range * (1.0f / (float)QMAX);
-        const float inv = range > 0.f ? (float)QMAX * __builtin_amdgcn_rcpf(range) : 0.f;
-        const float nb = -mn * inv;
-        sz[r] = float_to_half_bits(s) | (float_to_half_bits(mn) << 16);
+        row_minmax4<CGB>(mn, mx);
 #pragma unroll
-        for (int c = 0; c < QC; c++) fq[r][c] = fbits(fmaf(W[c], inv, nb) + kMagic);
+        for (int r = 0; r < QR; r++) {
+            const float m0 = mn[r] + 0.0f;  // a zero row stores +0, not the -0 of a sign-flipped channel
+            const float range = mx[r] - m0;
+            const float sc = range * (1.0f / (float)QMAX);
+            const float inv = range > 0.f ? (float)QMAX * __builtin_amdgcn_rcpf(range) : 0.f;
+            const float nb = -m0 * inv;
+            sz[r] = float_to_half_bits(sc) | (float_to_half_bits(m0) << 16);
+#pragma unroll
+            for (int c = 0; c < QC; c++) {
+                u[r][c] = fmaf(u[r][c], inv, nb);
+                if constexpr (!PKU8) u[r][c] += kMagic;  // rint(u) in the low mantissa bits
+            }
+        }
     }
+    auto fq = [&](int r, int c) -> uint32_t { return fbits(u[r][c]); };  // 6-bit: magic-rounded code
+    // 4 codes -> bytes 0..3 of a dword
+    auto pk4 = [](float a0, float a1, float a2, float a3) -> uint32_t {
+        uint32_t v = __builtin_amdgcn_cvt_pk_u8_f32(a0, 0u, 0u);
+        v = __builtin_amdgcn_cvt_pk_u8_f32(a1, 1u, v);
+        v = __builtin_amdgcn_cvt_pk_u8_f32(a2, 2u, v);
+        return __builtin_amdgcn_cvt_pk_u8_f32(a3, 3u, v);
+    };
     // the statistics are done with the shared buffer (last barrier above);
     // the record's code image reuses it
     if constexpr (!CHMAJOR) {
         // token-major: this lane's 16 codes of a row are contiguous
 #pragma unroll
         for (int r = 0; r < QR; r++) {
-            const uint32_t* f = fq[r];
+            const float* x = u[r];
             uint8_t* dstp = img + ((row0 + r) * D + ch0) * BITS / 8;
+            if constexpr (BITS == 4 && D == 128) {
+                // unit (16 bytes) c of token row t sits at unit c ^ ((t >> 2) & 3)
+                // of the row: the rows of lanes that differ in row-group bit 0
+                // then use different bank quads
+                const int t = row0 + r;
+                dstp = img + t * 64 + ((((cg >> 1) ^ (t >> 2)) & 3) << 4) + 8 * (cg & 1);
+            }
             if constexpr (BITS == 4) {
-                uint32_t pr[8];
-#pragma unroll
-                for (int k = 0; k < 8; k++) pr[k] = pack2<4>(f[2 * k], f[2 * k + 1]);
-                uint2 v = make_uint2(bytes4(pr[0], pr[1], pr[2], pr[3]), bytes4(pr[4], pr[5], pr[6], pr[7]));
-                *reinterpret_cast<uint2*>(dstp) = v;
+                // byte k = c_2k | c_2k+1 << 4
+                const uint32_t e0 = pk4(x[0], x[2], x[4], x[6]), o0 = pk4(x[1], x[3], x[5], x[7]);
+                const uint32_t e1 = pk4(x[8], x[10], x[12], x[14]), o1 = pk4(x[9], x[11], x[13], x[15]);
+                *reinterpret_cast<uint2*>(dstp) = make_uint2(e0 | (o0 << 4), e1 | (o1 << 4));
             } else if constexpr (BITS == 2) {
-                uint32_t qd[4];
-#pragma unroll
-                for (int k = 0; k < 4; k++)
-                    qd[k] = (pack2<2>(f[4 * k + 2], f[4 * k + 3]) << 4) + pack2<2>(f[4 * k], f[4 * k + 1]);
-                *reinterpret_cast<uint32_t*>(dstp) = bytes4(qd[0], qd[1], qd[2], qd[3]);
+                // byte k = c_4k | c_4k+1 << 2 | c_4k+2 << 4 | c_4k+3 << 6
+                const uint32_t p0 = pk4(x[0], x[4], x[8], x[12]), p1 = pk4(x[1], x[5], x[9], x[13]);
+                const uint32_t p2 = pk4(x[2], x[6], x[10], x[14]), p3 = pk4(x[3], x[7], x[11], x[15]);
+                *reinterpret_cast<uint32_t*>(dstp) = p0 | (p1 << 2) | (p2 << 4) | (p3 << 6);
             } else {
                 uint32_t g[4];
 #pragma unroll
-                for (int k = 0; k < 4; k++) g[k] = pack6x4(f[4 * k], f[4 * k + 1], f[4 * k + 2], f[4 * k + 3]);
+                for (int k = 0; k < 4; k++) g[k] = pack6x4(fq(r, 4 * k), fq(r, 4 * k + 1), fq(r, 4 * k + 2), fq(r, 4 * k + 3));
                 uint32_t* d32 = reinterpret_cast<uint32_t*>(dstp);
                 d32[0] = g[0] | (g[1] << 24);
                 d32[1] = (g[1] >> 8) | (g[2] << 16);
@@ -483,18 +577,38 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ tile,
         }
     } else {
         // channel-major: this lane's 4 tokens of a channel are contiguous
+        if constexpr (BITS == 2) {
+            // byte of channel c = its 4 codes, token-ascending, 2 bits each
 #pragma unroll
-        for (int c = 0; c < QC; c++) {
-            const int e0 = (ch0 + c) * T + row0;  // element index of the first of 4 codes
-            if constexpr (BITS == 2) {
-                const uint32_t v = (pack2<2>(fq[2][c], fq[3][c]) << 4) + pack2<2>(fq[0][c], fq[1][c]);
-                img[e0 / 4] = (uint8_t)v;
-            } else if constexpr (BITS == 4) {
-                const uint32_t v = __builtin_amdgcn_perm(pack2<4>(fq[2][c], fq[3][c]),
-                                                         pack2<4>(fq[0][c], fq[1][c]), 0x0c0c0400u);
-                *reinterpret_cast<uint16_t*>(img + e0 / 2) = (uint16_t)v;
-            } else {
-                const uint32_t v = pack6x4(fq[0][c], fq[1][c], fq[2][c], fq[3][c]);
+            for (int c4 = 0; c4 < QC / 4; c4++) {
+                uint32_t p[QR];
+#pragma unroll
+                for (int r = 0; r < QR; r++) p[r] = pk4(u[r][4 * c4], u[r][4 * c4 + 1], u[r][4 * c4 + 2], u[r][4 * c4 + 3]);
+                const uint32_t v = p[0] | (p[1] << 2) | (p[2] << 4) | (p[3] << 6);  // byte k: channel 4 c4 + k
+#pragma unroll
+                for (int k = 0; k < 4; k++) img[((ch0 + 4 * c4 + k) * T + row0) / 4] = (uint8_t)(v >> (8 * k));
+            }
+        } else if constexpr (BITS == 4) {
+            // 16 bits of channel c: (c_t0 | c_t1 << 4) then (c_t2 | c_t3 << 4)
+#pragma unroll
+            for (int c4 = 0; c4 < QC / 4; c4++) {
+                uint32_t p[QR];
+#pragma unroll
+                for (int r = 0; r < QR; r++) p[r] = pk4(u[r][4 * c4], u[r][4 * c4 + 1], u[r][4 * c4 + 2], u[r][4 * c4 + 3]);
+                const uint32_t lo = p[0] | (p[1] << 4), hi = p[2] | (p[3] << 4);
+                const uint32_t w01 = __builtin_amdgcn_perm(hi, lo, 0x05010400u);  // channels 0, 1
+                const uint32_t w23 = __builtin_amdgcn_perm(hi, lo, 0x07030602u);  // channels 2, 3
+                const int e0 = (ch0 + 4 * c4) * T + row0;
+                *reinterpret_cast<uint16_t*>(img + e0 / 2) = (uint16_t)w01;
+                *reinterpret_cast<uint16_t*>(img + (e0 + T) / 2) = (uint16_t)(w01 >> 16);
+                *reinterpret_cast<uint16_t*>(img + (e0 + 2 * T) / 2) = (uint16_t)w23;
+                *reinterpret_cast<uint16_t*>(img + (e0 + 3 * T) / 2) = (uint16_t)(w23 >> 16);
+            }
+        } else {
+#pragma unroll
+            for (int c = 0; c < QC; c++) {
+                const int e0 = (ch0 + c) * T + row0;  // element index of the first of 4 codes
+                const uint32_t v = pack6x4(fq(0, c), fq(1, c), fq(2, c), fq(3, c));
                 uint8_t* d8 = img + e0 * 6 / 8;
                 d8[0] = (uint8_t)v;
                 d8[1] = (uint8_t)(v >> 8);
@@ -515,11 +629,17 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ tile,
 
     // ---- stage 5: the code image leaves in 16-byte stores -------------------
     {
-        constexpr int PER = CODE_BYTES / NT;   // 8 * BITS bytes per thread
-        const uint4* src4 = reinterpret_cast<const uint4*>(img + tid * PER);
-        uint4* dst4 = reinterpret_cast<uint4*>(rec + (int64_t)tid * PER);
+        // thread tid moves units tid, tid + NT, ...: consecutive lanes read
+        // consecutive LDS units and write consecutive 16-byte chunks
+        constexpr int UNITS = CODE_BYTES / 16 / NT;   // BITS / 2 units per thread
+        uint4* dst4 = reinterpret_cast<uint4*>(rec);
 #pragma unroll
-        for (int k = 0; k < PER / 16; k++) dst4[k] = src4[k];
+        for (int k = 0; k < UNITS; k++) {
+            const int u = tid + k * NT;
+            int pu = u;
+            if constexpr (!CHMAJOR && BITS == 4 && D == 128) pu = (u & ~3) | ((u ^ (u >> 4)) & 3);  // row t = u >> 2
+            dst4[u] = reinterpret_cast<const uint4*>(img)[pu];
+        }
     }
 }
 
@@ -527,13 +647,16 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ tile,
 // 2*(i*H + h) + kind takes page i, head h, kind 0 = keys (token-major codes),
 // kind 1 = values (channel-major codes).
 template <int D, int T, int KB, int VB, bool HASV>
-__global__ void __launch_bounds__(T * D / 64)
+// D = 128: three waves per SIMD (168 VGPRs; the rotation's MFMA accumulators
+// and the rows it fills peak there); a D = 512 workgroup is itself four
+// waves per SIMD
+__global__ void __launch_bounds__(T * D / 64, D == 128 ? 3 : D == 256 ? 2 : 4)
 quantize_kernel(const uint16_t* __restrict__ kpool, const uint16_t* __restrict__ vpool,
                 uint8_t* __restrict__ krec, uint8_t* __restrict__ vrec, const int32_t* __restrict__ src,
                 const int32_t* __restrict__ dst, int32_t H, int64_t n_fpages, int64_t n_qpages, int32_t n_iters) {
     using S = TileShape<D, T>;
     __shared__ __attribute__((aligned(16))) uint8_t smem[S::SMEM];
-    __shared__ __attribute__((aligned(16))) float vec[3 * D];
+    __shared__ __attribute__((aligned(16))) float vec[VecShape<D>::FLOATS];
     const int kind = HASV ? (int)(blockIdx.x & 1u) : 0;
     const int r = HASV ? (int)(blockIdx.x >> 1) : (int)blockIdx.x;
     const int i = r / H;
