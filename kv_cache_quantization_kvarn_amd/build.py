@@ -26,7 +26,7 @@ EXTRA = {"quantize_d128.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee",
                               "-mllvm", "-amdgpu-mfma-vgpr-form=1"],
          "quantize_d256.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"],
          "quantize_d512.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"],
-         "decode_gqa.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+         "decode_gqa.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee", "-mllvm", "-amdgpu-mfma-vgpr-form=1"],
          "decode_mla.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee",
                             # keep MFMA accumulators in ordinary VGPRs: the loop-carried
                             # output tile is otherwise copied to and from AGPRs every chunk

@@ -161,7 +161,7 @@ size_t kvarn_decode_workspace_bytes(const kvarn_layout* layout, int32_t batch, i
     int ns = 1, pps = 1;
     const int H = layout->num_kv_heads;
     kvarn::decode_plan(layout->head_dim, H, num_q_heads / (H > 0 ? H : 1), layout->mla, batch, max_pages,
-                       layout->tile_tokens, &ns, &pps);
+                       layout->tile_tokens, layout->k_bits, layout->v_bits, &ns, &pps);
     if (layout->mla) return kvarn::mla_workspace_floats(num_q_heads, batch, ns) * sizeof(float);
     const int nf = kvarn::decode_fp16_pages(layout->tile_tokens, layout->sink_tokens, layout->tail_tokens, max_pages);
     return kvarn::decode_workspace_floats(layout->head_dim, num_q_heads, batch, ns, nf) * sizeof(float);
@@ -193,7 +193,7 @@ kvarn_status kvarn_decode_attn(const kvarn_layout* layout, const kvarn_cache* ca
     if (!(sm_scale > 0.f) || sm_scale > 1e30f) return fail(KVARN_EINVAL, "sm_scale must be positive and finite");
     int ns = 1, pps = 1;
     kvarn::decode_plan(layout->head_dim, H, G, layout->mla, pages->batch, pages->max_pages, layout->tile_tokens,
-                       &ns, &pps);
+                       layout->k_bits, layout->v_bits, &ns, &pps);
     const int nf = kvarn::decode_fp16_pages(layout->tile_tokens, layout->sink_tokens, layout->tail_tokens,
                                             pages->max_pages);
     const size_t need = (layout->mla ? kvarn::mla_workspace_floats(num_q_heads, pages->batch, ns)

@@ -416,6 +416,462 @@ __global__ void __launch_bounds__(64) decode_split_kernel(DecodeArgs a) {
     }
 }
 
+// ---- int8 operands -------------------------------------------------------------
+typedef int i4v __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// 4 of 16 6-bit codes (bits 24 e .. 24 e + 23 of the 3 words w) as int8 bytes
+template <int B>
+__device__ __forceinline__ int code_bytes(const uint32_t* w, int e) {
+    static_assert(B == 6, "6-bit codes only");
+    // t: low half = bits 0..15 of the run, high half = bits 8..23
+    uint32_t t;
+    if (e == 0) t = __builtin_amdgcn_perm(w[0], w[0], 0x02010100u);
+    else if (e == 1) t = __builtin_amdgcn_perm(w[1], w[0], 0x05040403u);
+    else if (e == 2) t = __builtin_amdgcn_perm(w[2], w[1], 0x04030302u);
+    else t = __builtin_amdgcn_perm(w[2], w[2], 0x03020201u);
+    // low half: codes 0, 1 at bits 0-5, 6-11; high half >> 4: codes 2, 3 there
+    const u16x2 hh = __builtin_bit_cast(u16x2, t) >> (u16x2){0, 4};
+    const uint32_t uu = __builtin_bit_cast(uint32_t, hh);
+    const uint32_t vv = __builtin_bit_cast(uint32_t, hh << (u16x2){2, 2});  // codes 1, 3 to bits 8-13
+    return (int)((uu & 0x003F003Fu) | (vv & 0x3F003F00u));
+}
+
+// x (|x| < 2^21 after scaling) rounded to an integer X = d2 65536 + d1 256 + d0
+// with balanced digits d in [-128, 127]: bytes 0, 1, 2 of the result are d0,
+// d1, d2 as int8 (adding 0x808080 makes each digit byte d + 128; the xor
+// turns that back into d's two's-complement byte).
+__device__ __forceinline__ uint32_t digits3(float x) {
+    const int X = (int)__builtin_rintf(x);
+    return ((uint32_t)X + 0x808080u) ^ 0x808080u;
+}
+
+// z[L] = digit L of y0, y1, y2, y3 in bytes 0..3
+__device__ __forceinline__ void digit_levels(uint32_t y0, uint32_t y1, uint32_t y2, uint32_t y3, int (&z)[3]) {
+    const uint32_t a = __builtin_amdgcn_perm(y1, y0, 0x05010400u);  // y0.0 y1.0 y0.1 y1.1
+    const uint32_t b = __builtin_amdgcn_perm(y3, y2, 0x05010400u);  // y2.0 y3.0 y2.1 y3.1
+    z[0] = (int)__builtin_amdgcn_perm(b, a, 0x05040100u);
+    z[1] = (int)__builtin_amdgcn_perm(b, a, 0x07060302u);
+    z[2] = (int)(__builtin_amdgcn_perm(y1, y0, 0x0c0c0602u) | __builtin_amdgcn_perm(y3, y2, 0x06020c0cu));
+}
+
+// max and sum over the 16 lanes of one residue class mod 4
+__device__ __forceinline__ float max_class4(float v) {
+    v = fmaxf(v, i2f(__builtin_amdgcn_update_dpp(f2i(v), f2i(v), 0x124, 0xF, 0xF, false)));  // row_ror 4
+    v = fmaxf(v, i2f(__builtin_amdgcn_update_dpp(f2i(v), f2i(v), 0x128, 0xF, 0xF, false)));  // row_ror 8
+    const auto a16 = __builtin_amdgcn_permlane16_swap((unsigned)f2i(v), (unsigned)f2i(v), false, false);
+    v = fmaxf(i2f((int)a16[0]), i2f((int)a16[1]));
+    const auto a32 = __builtin_amdgcn_permlane32_swap((unsigned)f2i(v), (unsigned)f2i(v), false, false);
+    return fmaxf(i2f((int)a32[0]), i2f((int)a32[1]));
+}
+__device__ __forceinline__ float sum_class4(float v) {
+    v += i2f(__builtin_amdgcn_update_dpp(0, f2i(v), 0x124, 0xF, 0xF, true));  // row_ror 4
+    v += i2f(__builtin_amdgcn_update_dpp(0, f2i(v), 0x128, 0xF, 0xF, true));  // row_ror 8
+    const auto a16 = __builtin_amdgcn_permlane16_swap((unsigned)f2i(v), (unsigned)f2i(v), false, false);
+    v = i2f((int)a16[0]) + i2f((int)a16[1]);
+    const auto a32 = __builtin_amdgcn_permlane32_swap((unsigned)f2i(v), (unsigned)f2i(v), false, false);
+    return i2f((int)a32[0]) + i2f((int)a32[1]);
+}
+
+// exponent e of x = f 2^e with 0.5 <= |f| < 1 (0 for x = 0)
+__device__ __forceinline__ int frexp_exp(float x) { return __builtin_amdgcn_frexp_expf(x); }
+
+// Reductions of four values per lane (one per query head) over the 64 lanes,
+// returned wave-uniform.  Inside each 16-lane row: fused DPP (xor 1, xor 2,
+// rotate 4, rotate 8); across rows the heads are paired, so one
+// v_permlane16_swap serves heads 0/1 (and 2/3) and one v_permlane32_swap
+// serves all four: afterwards row r holds head r's result, read from lane 16 r.
+#define KVARN_DPP4(OP, CTRL)                                                                  \
+    asm volatile("s_nop 1\n\t"                                                                 \
+                 OP "_dpp %0, %0, %0 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                 \
+                 OP "_dpp %1, %1, %1 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                 \
+                 OP "_dpp %2, %2, %2 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                 \
+                 OP "_dpp %3, %3, %3 " CTRL " row_mask:0xf bank_mask:0xf"                     \
+                 : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]))
+
+template <bool MAX>
+__device__ __forceinline__ void wave_reduce4(float (&v)[4], float (&out)[4]) {
+    if constexpr (MAX) {
+        KVARN_DPP4("v_max_f32", "quad_perm:[1,0,3,2]");
+        KVARN_DPP4("v_max_f32", "quad_perm:[2,3,0,1]");
+        KVARN_DPP4("v_max_f32", "row_ror:4");
+        KVARN_DPP4("v_max_f32", "row_ror:8");
+    } else {
+        KVARN_DPP4("v_add_f32", "quad_perm:[1,0,3,2]");
+        KVARN_DPP4("v_add_f32", "quad_perm:[2,3,0,1]");
+        KVARN_DPP4("v_add_f32", "row_ror:4");
+        KVARN_DPP4("v_add_f32", "row_ror:8");
+    }
+    auto op = [](float x, float y) { return MAX ? fmaxf(x, y) : x + y; };
+    const auto p01 = __builtin_amdgcn_permlane16_swap((unsigned)f2i(v[0]), (unsigned)f2i(v[1]), false, false);
+    const auto p23 = __builtin_amdgcn_permlane16_swap((unsigned)f2i(v[2]), (unsigned)f2i(v[3]), false, false);
+    const float m01 = op(i2f((int)p01[0]), i2f((int)p01[1]));  // rows 0, 2: head 0; rows 1, 3: head 1
+    const float m23 = op(i2f((int)p23[0]), i2f((int)p23[1]));  // rows 0, 2: head 2; rows 1, 3: head 3
+    const auto q = __builtin_amdgcn_permlane32_swap((unsigned)f2i(m01), (unsigned)f2i(m23), false, false);
+    const float r = op(i2f((int)q[0]), i2f((int)q[1]));        // row g: head g
+#pragma unroll
+    for (int g = 0; g < 4; g++) out[g] = i2f(__builtin_amdgcn_readlane(f2i(r), 16 * g));
+}
+
+// max over the 64 lanes of one value (fused DPP inside rows), wave-uniform
+__device__ __forceinline__ float wave_max_uniform(float x) {
+    asm volatile("s_nop 1\n\t"
+                 "v_max_f32_dpp %0, %0, %0 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+                 "s_nop 1\n\t"
+                 "v_max_f32_dpp %0, %0, %0 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+                 "s_nop 1\n\t"
+                 "v_max_f32_dpp %0, %0, %0 row_ror:4 row_mask:0xf bank_mask:0xf\n\t"
+                 "s_nop 1\n\t"
+                 "v_max_f32_dpp %0, %0, %0 row_ror:8 row_mask:0xf bank_mask:0xf"
+                 : "+v"(x));
+    const float r0 = i2f(__builtin_amdgcn_readlane(f2i(x), 0)), r1 = i2f(__builtin_amdgcn_readlane(f2i(x), 16));
+    const float r2 = i2f(__builtin_amdgcn_readlane(f2i(x), 32)), r3 = i2f(__builtin_amdgcn_readlane(f2i(x), 48));
+    return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
+// ---- D = 128: scores and value sums on the 32x32x32 int8 MFMA --------------
+//
+// One wave per (split, KV head, sequence), 64 tokens per step, as above, but
+// each contraction is a handful of 32x32x32 int8 MFMAs (32 tokens or 32
+// channels per instruction).  The rows of the int8 operand are (digit level
+// L, query head g) = 4 L + g, 12 of 32 used: the query times C of a page (or
+// the softmax weights times S of a step) is scaled by a power of two below
+// 2^21, rounded to an integer and split into three balanced base-256 digits,
+// so the int32 results are exact and recombine in fp32.  The codes are the
+// other operand, one byte per code.
+//
+// Lane l of a 32x32 result holds rows {8 j + 4 (l >> 5) + i}, i.e. levels 0
+// and 2 in the lower half-wave and level 1 in the upper one, for column
+// l & 31.  Two results (token blocks 0/1, or channel blocks 2 s / 2 s + 1)
+// are paired with v_permlane32_swap so that every lane ends with all three
+// levels of its own column: lane l holds token l of the step (scores) or
+// channel 64 s + l (value sums).
+typedef int i16v __attribute__((ext_vector_type(16)));
+
+// 16 codes (B bits each, LSB-first words w[0 .. B/2-1]) as 16 int8 bytes;
+// byte j holds code perm16<B>(j)
+template <int B>
+__device__ __forceinline__ i4v codes16(const uint32_t* w) {
+    if constexpr (B == 4) {
+        return i4v{(int)(w[0] & 0x0F0F0F0Fu), (int)((w[0] >> 4) & 0x0F0F0F0Fu), (int)(w[1] & 0x0F0F0F0Fu),
+                   (int)((w[1] >> 4) & 0x0F0F0F0Fu)};
+    } else if constexpr (B == 2) {
+        return i4v{(int)(w[0] & 0x03030303u), (int)((w[0] >> 2) & 0x03030303u), (int)((w[0] >> 4) & 0x03030303u),
+                   (int)((w[0] >> 6) & 0x03030303u)};
+    } else {
+        return i4v{code_bytes<6>(w, 0), code_bytes<6>(w, 1), code_bytes<6>(w, 2), code_bytes<6>(w, 3)};
+    }
+}
+// element of the 16 held in byte j by codes16<B>, and its inverse
+template <int B>
+__host__ __device__ constexpr int perm16(int j) {
+    if constexpr (B == 4) return (j & 8) + 2 * (j & 3) + ((j >> 2) & 1);
+    else if constexpr (B == 2) return 4 * (j & 3) + (j >> 2);
+    else return j;
+}
+template <int B>
+__host__ __device__ constexpr int perm16_inv(int c) {
+    if constexpr (B == 4) return (c & 8) + 4 * (c & 1) + ((c >> 1) & 3);
+    else if constexpr (B == 2) return 4 * (c & 3) + (c >> 2);
+    else return c;
+}
+
+__device__ __forceinline__ i16v mfma32_i8(i4v a, i4v b, i16v c) {
+    return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
+}
+
+// x: lanes 0-31 hold column c0's (L0 at x[g], L2 at x[4 + g]) and lanes 32-63
+// column c0's L1 at x[g]; y likewise for column c1.  Returns, per lane, the
+// value 65536 L2 + 256 L1 + L0 of its own column (c0 in the lower half, c1 in
+// the upper half) for g = 0..3.
+__device__ __forceinline__ f4 pair_levels(const i16v& x, const i16v& y) {
+    f4 r;
+#pragma unroll
+    for (int g = 0; g < 4; g++) {
+        const auto s01 = __builtin_amdgcn_permlane32_swap((unsigned)x[g], (unsigned)y[g], false, false);
+        const auto s2 = __builtin_amdgcn_permlane32_swap((unsigned)x[4 + g], (unsigned)y[4 + g], false, false);
+        // s01[0]: L0 of the lane's column, s01[1]: L1; s2[0]: L2
+        r[g] = fmaf((float)(int)s2[0], 65536.0f, fmaf((float)(int)s01[1], 256.0f, (float)(int)s01[0]));
+    }
+    return r;
+}
+
+template <int T, int KB, int VB>
+__global__ void __launch_bounds__(64) decode_split128_kernel(DecodeArgs a) {
+    constexpr int D = 128, G = 4;
+    constexpr int TS = T / 64;            // 64-token steps of a page
+    constexpr int KCB = T * D * KB / 8;
+    constexpr int VCB = T * D * VB / 8;
+    constexpr int KREC = KCB + 4 * T + 2 * D;
+    constexpr int VREC = VCB + 4 * T + 2 * D;
+    constexpr int KROW = D * KB / 8;      // code bytes of a token
+    constexpr int KW = KROW / 8;          // words of half a token row (64 channels)
+    constexpr int VROW = T * VB / 8;      // code bytes of a channel (whole page)
+    constexpr int VW = VB;                // words of 32 tokens of a channel
+    constexpr int WS = 2 * D + 4;
+    constexpr int QROW = D, WROW = 64;    // bytes per row of the query / weight digit tables
+    static_assert(KW == KB * 2 && (KROW / 2) % 16 == 0, "half token rows in 16-byte loads");
+
+    // digit tables, rows 4 L + g; row 12 stays zero (the unused operand rows)
+    __shared__ __attribute__((aligned(16))) uint8_t qt[13 * QROW];
+    __shared__ __attribute__((aligned(16))) uint8_t wt[13 * WROW];
+
+    const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int lane = threadIdx.x;
+    const int half = lane >> 5, col = lane & 31;
+    const int orow = min(col, 12);        // operand row of this lane (12: zeros)
+    const int Hq = a.Hq;
+    const float sm2 = a.sm_scale * kLog2e;
+
+    if (lane < 32) reinterpret_cast<uint32_t*>(qt + 12 * QROW)[lane] = 0u;
+    if (lane < 16) reinterpret_cast<uint32_t*>(wt + 12 * WROW)[lane] = 0u;
+
+    // query digit builder: lane = (head g = lane & 3, q = lane >> 2) owns the
+    // table positions 16 (q >> 1) + 4 u + k, u = 2 (q & 1) + i (i = 0, 1),
+    // i.e. channels 16 (q >> 1) + perm16<KB>(4 u + k)
+    const int bg = lane & 3, bq = lane >> 2;
+    auto bchan = [&](int i, int k) { return 16 * (bq >> 1) + perm16<KB>(4 * (2 * (bq & 1) + i) + k); };
+    float qv[2][4];
+    {
+        const float* qr = a.ws + ((int64_t)b * Hq + h * G + bg) * D;
+#pragma unroll
+        for (int i = 0; i < 2; i++)
+#pragma unroll
+            for (int k = 0; k < 4; k++) qv[i][k] = qr[bchan(i, k)];
+    }
+
+    // sequence length and page ids are wave-uniform (SGPRs)
+    const int L = __builtin_amdgcn_readfirstlane(min(a.seq_lens[b], a.max_pages * T));
+    const int nq = (L - a.sink - a.tail >= T) ? (L - a.sink - a.tail) / T : 0;
+    const int sp = a.sink / T;
+
+    float mrun[G], lp[G], accr[2][G];
+#pragma unroll
+    for (int g = 0; g < G; g++) {
+        mrun[g] = -INFINITY;
+        lp[g] = 0.f;
+        accr[0][g] = accr[1][g] = 0.f;
+    }
+
+    const int npg = nq > split ? (nq - split + a.nsplit - 1) / a.nsplit : 0;  // quantized pages of this split
+    const int nst = npg * TS;
+    const uint8_t* const krec = static_cast<const uint8_t*>(a.k_records);
+    const uint8_t* const vrec = static_cast<const uint8_t*>(a.v_records);
+
+    struct StepRef {
+        int id, h;
+        bool ok;
+    };
+    auto step_ref = [&](int k) {
+        StepRef r;
+        r.h = k % TS;
+        r.id = k < nst ? __builtin_amdgcn_readfirstlane(a.block_table[(int64_t)b * a.max_pages + sp + split + (k / TS) * a.nsplit])
+                       : -1;
+        r.ok = k < nst && r.id >= 0 && (int64_t)r.id < a.n_qpages;
+        return r;
+    };
+
+    // One step's loads: the lane's half rows of tokens col and 32 + col, the
+    // 32-token share of channels 32 cb + col (cb = 0..3), the scale words of
+    // token `lane`, and on a page's first step the builder's 8 column scales
+    // of K and this lane's 2 of V.
+    struct Buf {
+        uint32_t kw[2][KW];
+        uint32_t vw[4][VW];
+        uint32_t ksz, vsz;
+        uint32_t ck[4];   // fp16 pairs: C_K at bchan(i, 2 j), bchan(i, 2 j + 1), word 2 i + j
+        uint32_t cv;      // fp16 pair: C_V of channels lane, 64 + lane
+    };
+    // the key part of a step's loads (issued once the scores have used the
+    // buffer's key words) and the value part (once the value sums are done)
+    auto issue_k = [&](const StepRef& r, Buf& f) {
+        if (!r.ok) return;
+        const uint8_t* rk = krec + ((int64_t)r.id * a.H + h) * KREC;
+#pragma unroll
+        for (int tb = 0; tb < 2; tb++) {
+            const uint8_t* p = rk + (int64_t)(64 * r.h + 32 * tb + col) * KROW + half * (KROW / 2);
+            load_words(f.kw[tb], p, KW / 4);
+        }
+        f.ksz = reinterpret_cast<const uint32_t*>(rk + KCB)[64 * r.h + lane];
+        if (r.h == 0) {
+            const uint16_t* ck = reinterpret_cast<const uint16_t*>(rk + KCB + 4 * T);
+#pragma unroll
+            for (int i = 0; i < 2; i++)
+#pragma unroll
+                for (int j = 0; j < 2; j++)
+                    f.ck[2 * i + j] = (uint32_t)ck[bchan(i, 2 * j)] | ((uint32_t)ck[bchan(i, 2 * j + 1)] << 16);
+        }
+    };
+    auto issue_v = [&](const StepRef& r, Buf& f) {
+        if (!r.ok) return;
+        const uint8_t* rv = vrec + ((int64_t)r.id * a.H + h) * VREC;
+#pragma unroll
+        for (int cb = 0; cb < 4; cb++) {
+            const uint8_t* p = rv + (int64_t)(32 * cb + col) * VROW + (64 * r.h + 32 * half) * VB / 8;
+#pragma unroll
+            for (int j = 0; j < VW / 2; j++) {  // 8-byte pieces (the 6-bit share sits on an 8-byte boundary)
+                const uint2 v = reinterpret_cast<const uint2*>(p)[j];
+                f.vw[cb][2 * j] = v.x; f.vw[cb][2 * j + 1] = v.y;
+            }
+        }
+        f.vsz = reinterpret_cast<const uint32_t*>(rv + VCB)[64 * r.h + lane];
+        if (r.h == 0) {
+            const uint16_t* cvp = reinterpret_cast<const uint16_t*>(rv + VCB + 4 * T);
+            f.cv = (uint32_t)cvp[lane] | ((uint32_t)cvp[64 + lane] << 16);
+        }
+    };
+
+    float qs[G], sqs[G];  // per head: sm2 * 2^(e - 21) and sm2 * sum(q' * C) of the current page
+    float cvv[2];         // value column scales of channels lane, 64 + lane
+#pragma unroll
+    for (int g = 0; g < G; g++) qs[g] = sqs[g] = 0.f;
+    cvv[0] = cvv[1] = 0.f;
+    const int wpos = 16 * (lane >> 4) + perm16_inv<VB>(lane & 15);  // weight-table position of token `lane`
+
+    auto step = [&](const StepRef& cur, const StepRef& nxt, Buf& u) {
+        if (!cur.ok) {  // uniform: a page whose id is outside the record pool is skipped
+            issue_k(nxt, u);
+            issue_v(nxt, u);
+            return;
+        }
+        if (cur.h == 0) {
+            // query digits of the new page into the table: q~ = q' * C_K, per
+            // head scaled so that max |q~| 2^(21 - e) < 2^21
+            float qt4[2][4];
+            float mx = 0.f, sum = 0.f;
+#pragma unroll
+            for (int i = 0; i < 2; i++)
+#pragma unroll
+                for (int k = 0; k < 4; k++) {
+                    const uint32_t w = u.ck[2 * i + (k >> 1)];
+                    qt4[i][k] = qv[i][k] * half_bits_to_float((w >> (16 * (k & 1))) & 0xffffu);
+                    mx = fmaxf(mx, fabsf(qt4[i][k]));
+                    sum += qt4[i][k];
+                }
+            mx = max_class4(mx);    // the 16 lanes of head bg
+            sum = sum_class4(sum);
+            const int e = frexp_exp(mx);
+#pragma unroll
+            for (int i = 0; i < 2; i++) {
+                uint32_t y[4];
+#pragma unroll
+                for (int k = 0; k < 4; k++) y[k] = digits3(__builtin_amdgcn_ldexpf(qt4[i][k], 21 - e));
+                int z[3];
+                digit_levels(y[0], y[1], y[2], y[3], z);
+                const int pos = 16 * (bq >> 1) + 4 * (2 * (bq & 1) + i);
+#pragma unroll
+                for (int lv = 0; lv < 3; lv++) *reinterpret_cast<int*>(qt + (4 * lv + bg) * QROW + pos) = z[lv];
+            }
+            const float qsl = __builtin_amdgcn_ldexpf(sm2, e - 21);
+            const float sql = sm2 * sum;
+#pragma unroll
+            for (int g = 0; g < G; g++) {  // lanes 0..3 hold heads 0..3
+                qs[g] = i2f(__builtin_amdgcn_readlane(f2i(qsl), g));
+                sqs[g] = i2f(__builtin_amdgcn_readlane(f2i(sql), g));
+            }
+            cvv[0] = half_bits_to_float(u.cv & 0xffffu);
+            cvv[1] = half_bits_to_float(u.cv >> 16);
+            wave_sync();
+        }
+
+        // ---- scores: token blocks 0 and 1, k-step ks covers channels
+        // 64 half + 16 ks + perm16(j) in byte j of both operands ----
+        float s[G];
+        {
+            i16v d0 = {}, d1 = {};
+#pragma unroll
+            for (int ks = 0; ks < 4; ks++) {
+                const i4v aq = *reinterpret_cast<const i4v*>(qt + orow * QROW + 16 * (4 * half + ks));
+                d0 = mfma32_i8(aq, codes16<KB>(&u.kw[0][ks * KB / 2]), d0);
+                d1 = mfma32_i8(aq, codes16<KB>(&u.kw[1][ks * KB / 2]), d1);
+            }
+            const f4 R = pair_levels(d0, d1);  // token `lane`
+            const float S = half_bits_to_float(u.ksz & 0xffffu), Z = half_bits_to_float(u.ksz >> 16);
+#pragma unroll
+            for (int g = 0; g < G; g++) s[g] = fmaf(S * qs[g], R[g], Z * sqs[g]);
+        }
+        issue_k(nxt, u);  // the key words are used up
+
+        // ---- online softmax over the step (log2 domain) ----
+        float p[G];
+        {
+            float mx[G], t[G] = {s[0], s[1], s[2], s[3]};
+            wave_reduce4<true>(t, mx);
+#pragma unroll
+            for (int g = 0; g < G; g++) {
+                const float mnew = fmaxf(mrun[g], mx[g]);  // finite: the step holds a valid token
+                const float alpha = mrun[g] == -INFINITY ? 0.f : exp2f(mrun[g] - mnew);
+                mrun[g] = mnew;
+                lp[g] *= alpha;
+                accr[0][g] *= alpha;
+                accr[1][g] *= alpha;
+                p[g] = exp2f(s[g] - mnew);
+                lp[g] += p[g];
+            }
+        }
+
+        // ---- value sums: weights p S_V as digit levels through the table;
+        // k-step ks covers tokens 32 half + 16 ks + perm16(j) ----
+        {
+            const float S = half_bits_to_float(u.vsz & 0xffffu), Z = half_bits_to_float(u.vsz >> 16);
+            const int e = frexp_exp(wave_max_uniform(S));
+            float E[G], pz[G];
+#pragma unroll
+            for (int g = 0; g < G; g++) {
+                const uint32_t y = digits3(__builtin_amdgcn_ldexpf(p[g] * S, 21 - e));
+                wt[(0 + g) * WROW + wpos] = (uint8_t)y;
+                wt[(4 + g) * WROW + wpos] = (uint8_t)(y >> 8);
+                wt[(8 + g) * WROW + wpos] = (uint8_t)(y >> 16);
+                pz[g] = p[g] * Z;
+            }
+            wave_reduce4<false>(pz, E);
+            wave_sync();
+            const i4v aw0 = *reinterpret_cast<const i4v*>(wt + orow * WROW + 16 * (2 * half + 0));
+            const i4v aw1 = *reinterpret_cast<const i4v*>(wt + orow * WROW + 16 * (2 * half + 1));
+            const float wsc = __builtin_amdgcn_ldexpf(1.0f, e - 21);
+#pragma unroll
+            for (int sv = 0; sv < 2; sv++) {
+                i16v d0 = {}, d1 = {};
+                d0 = mfma32_i8(aw0, codes16<VB>(&u.vw[2 * sv][0]), d0);
+                d1 = mfma32_i8(aw0, codes16<VB>(&u.vw[2 * sv + 1][0]), d1);
+                d0 = mfma32_i8(aw1, codes16<VB>(&u.vw[2 * sv][VB / 2]), d0);
+                d1 = mfma32_i8(aw1, codes16<VB>(&u.vw[2 * sv + 1][VB / 2]), d1);
+                const f4 R = pair_levels(d0, d1);  // channel 64 sv + lane
+#pragma unroll
+                for (int g = 0; g < G; g++) accr[sv][g] = fmaf(cvv[sv], fmaf(wsc, R[g], E[g]), accr[sv][g]);
+            }
+            wave_sync();  // the tables are rewritten by later steps
+        }
+        issue_v(nxt, u);
+    };
+
+    Buf buf;
+    StepRef cur = step_ref(0);
+    issue_k(cur, buf);
+    issue_v(cur, buf);
+    for (int k = 0; k < nst; k++) {
+        const StepRef nx = step_ref(k + 1);
+        step(cur, nx, buf);
+        cur = nx;
+    }
+
+    // ---- partial of this split: m, l, rotated-basis and fp16 value sums ----
+    float* wsp = a.ws + (int64_t)a.B * Hq * D;
+#pragma unroll
+    for (int g = 0; g < G; g++) {
+        const float lt = wave_sum_all(lp[g]);
+        float* o = wsp + (((int64_t)b * Hq + h * G + g) * (a.nsplit + a.nfsplit) + split) * WS;
+        if (lane == 0) {
+            o[0] = mrun[g];
+            o[1] = lt;
+        }
+        o[4 + lane] = accr[0][g];
+        o[4 + 64 + lane] = accr[1][g];
+        o[4 + D + 2 * lane] = 0.f;  // fp16 pages: their own kernel
+        o[4 + D + 2 * lane + 1] = 0.f;
+    }
+}
+
 // fp16 sink and tail pages (gmlx "KV cache quantization", "The two
 // schemes"): one wave per (fp16-page slot f, KV head, sequence).  Slot f is
 // the f-th fp16 page of the sequence (sink pages, then tail pages); its
@@ -645,7 +1101,10 @@ hipError_t launch_gqa(const DecodeArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((qrot_kernel<D>), dim3(a.B * a.Hq), dim3(D / 2), 0, st, a.q, a.q_bf16, a.ws);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((decode_split_kernel<D, T, KB, VB>), dim3(a.nsplit, a.H, a.B), dim3(64), 0, st, a);
+    if constexpr (D == 128)
+        hipLaunchKernelGGL((decode_split128_kernel<T, KB, VB>), dim3(a.nsplit, a.H, a.B), dim3(64), 0, st, a);
+    else
+        hipLaunchKernelGGL((decode_split_kernel<D, T, KB, VB>), dim3(a.nsplit, a.H, a.B), dim3(64), 0, st, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.nfsplit > 0) {
@@ -675,8 +1134,9 @@ hipError_t gqa_bits(const DecodeArgs& a, hipStream_t st) {
 
 }  // namespace
 
-void decode_plan(int D, int H, int G, int mla, int B, int max_pages, int T, int* nsplit, int* pps) {
-    (void)D; (void)G; (void)T;
+void decode_plan(int D, int H, int G, int mla, int B, int max_pages, int T, int kb, int vb, int* nsplit,
+                 int* pps) {
+    (void)D; (void)G; (void)T; (void)kb; (void)vb;
     // GQA: one-wave workgroups, about 12 per CU.  MLA: one 4-wave workgroup
     // per CU holds 64 heads (its accumulators fill the register file), so up
     // to 128 heads take two workgroups per split.

@@ -48,7 +48,8 @@ struct DecodeArgs {
 };
 
 // Split plan shared by the workspace query and the launch.
-void decode_plan(int D, int H, int G, int mla, int B, int max_pages, int T, int* nsplit, int* pps);
+void decode_plan(int D, int H, int G, int mla, int B, int max_pages, int T, int kb, int vb, int* nsplit,
+                 int* pps);
 // GQA: the most fp16 (sink and tail) pages a sequence can have.
 int decode_fp16_pages(int T, int sink, int tail, int max_pages);
 size_t decode_workspace_floats(int D, int Hq, int B, int nsplit, int nfsplit);
