@@ -138,6 +138,170 @@ __device__ __forceinline__ float sum_blocks_half(float v) {
     return v;
 }
 
+// fp16 sink and tail pages (gmlx "KV cache quantization", "The two
+// schemes"): workgroups of the split kernels' grid past the splits, one wave
+// per (fp16-page slot f, KV head, sequence).  Slot f is
+// the f-th fp16 page of the sequence (sink pages, then tail pages); its
+// partial goes to split nsplit + f with a zero rotated-basis sum.  Scores on
+// the MFMA with the plain query (fp16 high and low parts), lane = token;
+// value sums on the VALU, D/8 lanes per token row.
+template <int D, int T>
+__device__ __forceinline__ void fp16_block(const DecodeArgs& a, const int f, const int h, const int b) {
+    constexpr int G = 4;
+    constexpr int NS = D / 64;
+    constexpr int NC = D / 128;
+    constexpr int TS = T / 64;
+    constexpr int WS = 2 * D + 4;
+    __shared__ float4 pf[T];  // weights of the page
+
+    const int lane = threadIdx.x;
+    const int blk = lane >> 2, m = lane & 3;
+    const int Hq = a.Hq;
+    const float sm2 = a.sm_scale * kLog2e;
+    const int L = min(a.seq_lens[b], a.max_pages * T);
+    const int npages = L > 0 ? (L + T - 1) / T : 0;
+    const int nq = (L - a.sink - a.tail >= T) ? (L - a.sink - a.tail) / T : 0;
+    const int sp = a.sink / T;
+    const int page = f < sp ? f : sp + nq + (f - sp);
+    int id = -1;
+    if (page < npages) {
+        id = a.block_table[(int64_t)b * a.max_pages + page];
+        if (id < 0 || (int64_t)id >= a.n_fpages) id = -1;
+    }
+
+    constexpr int LPT = D / 8;     // lanes per token row in the value sums
+    constexpr int TG = 64 / LPT;   // tokens per load instruction
+    float mx[G], lsum[G], accp[8][G];
+#pragma unroll
+    for (int g = 0; g < G; g++) {
+        mx[g] = -INFINITY;
+        lsum[g] = 0.f;
+#pragma unroll
+        for (int c = 0; c < 8; c++) accp[c][g] = 0.f;
+    }
+    if (id >= 0) {  // uniform
+        // the plain query (fp16 high and low parts) at this lane's operand
+        // slots: 4 consecutive channels 4 i .. 4 i + 3 per slot
+        float qx[NS][4];
+        const int64_t qrow = ((int64_t)b * Hq + h * G + m) * D;
+        if (a.q_bf16) {  // uniform
+#pragma unroll
+            for (int r = 0; r < NS; r++) {
+                const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.q) + qrow +
+                                                                 4 * (32 * (r >> 1) + blk + 16 * (r & 1)));
+                qx[r][0] = __builtin_bit_cast(float, u.x << 16);
+                qx[r][1] = __builtin_bit_cast(float, u.x & 0xffff0000u);
+                qx[r][2] = __builtin_bit_cast(float, u.y << 16);
+                qx[r][3] = __builtin_bit_cast(float, u.y & 0xffff0000u);
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < NS; r++) {
+                const float4 v = *reinterpret_cast<const float4*>(static_cast<const float*>(a.q) + qrow +
+                                                                  4 * (32 * (r >> 1) + blk + 16 * (r & 1)));
+                qx[r][0] = v.x; qx[r][1] = v.y; qx[r][2] = v.z; qx[r][3] = v.w;
+            }
+        }
+        h4 qp[NS], qpl[NS];
+#pragma unroll
+        for (int r = 0; r < NS; r++)
+#pragma unroll
+            for (int kk = 0; kk < 4; kk++) {
+                qp[r][kk] = (_Float16)qx[r][kk];
+                qpl[r][kk] = (_Float16)(qx[r][kk] - (float)qp[r][kk]);
+            }
+        float s[TS][G];
+#pragma unroll
+        for (int sb = 0; sb < TS; sb++) {
+            const int tok = 64 * sb + lane;
+            const bool valid = page * T + tok < L;
+            const uint16_t* kr = static_cast<const uint16_t*>(a.k_fp16) + (((int64_t)id * a.H + h) * T + tok) * D;
+            f4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int c = 0; c < NC; c++) {
+                static_for<16>([&](auto ic) {
+                    constexpr int il = 2 * decltype(ic)::value;
+                    const uint4 v = *reinterpret_cast<const uint4*>(kr + 128 * c + 4 * il);
+                    const h4 b0 = __builtin_bit_cast(h4, make_uint2(v.x, v.y));
+                    const h4 b1 = __builtin_bit_cast(h4, make_uint2(v.z, v.w));
+                    acc0 = mfma_bcast<il & 15>(qp[2 * c + (il >> 4)], b0, acc0);
+                    acc1 = mfma_bcast<il & 15>(qpl[2 * c + (il >> 4)], b0, acc1);
+                    acc0 = mfma_bcast<(il + 1) & 15>(qp[2 * c + ((il + 1) >> 4)], b1, acc0);
+                    acc1 = mfma_bcast<(il + 1) & 15>(qpl[2 * c + ((il + 1) >> 4)], b1, acc1);
+                });
+            }
+            const f4 R = acc0 + acc1;
+#pragma unroll
+            for (int g = 0; g < G; g++) s[sb][g] = valid ? sm2 * R[g] : -INFINITY;
+        }
+        // softmax over the page: the first token of a visited page is valid
+        float p[TS][G];
+#pragma unroll
+        for (int g = 0; g < G; g++) {
+            float v = s[0][g];
+#pragma unroll
+            for (int sb = 1; sb < TS; sb++) v = fmaxf(v, s[sb][g]);
+            mx[g] = wave_max_all(v);
+#pragma unroll
+            for (int sb = 0; sb < TS; sb++) {
+                p[sb][g] = exp2f(s[sb][g] - mx[g]);
+                lsum[g] += p[sb][g];
+            }
+        }
+#pragma unroll
+        for (int sb = 0; sb < TS; sb++) pf[64 * sb + lane] = make_float4(p[sb][0], p[sb][1], p[sb][2], p[sb][3]);
+        wave_sync();
+        // value sums: D/8 lanes per token row (16-byte loads of 8 channels), TG
+        // tokens per load instruction, the token groups summed at the end
+        const int nvalid = min(T, L - page * T);  // tokens past the end may hold anything
+        const uint16_t* vp = static_cast<const uint16_t*>(a.v_fp16) + ((int64_t)id * a.H + h) * T * D;
+        const int tg = lane / LPT, cc = lane % LPT;
+        // branch-free: a token past the end has weight 0 (its score is
+        // -inf) and reads the last valid token's values instead of its own
+#pragma unroll 8
+        for (int t0 = 0; t0 < T; t0 += TG) {
+            const int t = t0 + tg;
+            const uint4 w = *reinterpret_cast<const uint4*>(vp + (int64_t)min(t, nvalid - 1) * D + 8 * cc);
+            const float4 pv = pf[t];
+            const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int kk = 0; kk < 8; kk++) {
+                const float v = half_bits_to_float((ww[kk >> 1] >> (16 * (kk & 1))) & 0xffffu);
+                accp[kk][0] = fmaf(pv.x, v, accp[kk][0]);
+                accp[kk][1] = fmaf(pv.y, v, accp[kk][1]);
+                accp[kk][2] = fmaf(pv.z, v, accp[kk][2]);
+                accp[kk][3] = fmaf(pv.w, v, accp[kk][3]);
+            }
+        }
+    }
+    // sum the token groups (lane bits above log2(LPT))
+#pragma unroll
+    for (int kk = 0; kk < 8; kk++)
+#pragma unroll
+        for (int g = 0; g < G; g++) {
+            float v = accp[kk][g];
+            if constexpr (TG >= 4) v += xor_lane<4>(v);
+            if constexpr (TG >= 2) v += lane_bcast32(v);
+            accp[kk][g] = v;
+        }
+    float* wsp = a.ws + (int64_t)a.B * Hq * D;
+#pragma unroll
+    for (int g = 0; g < G; g++) {
+        const float lt = wave_sum_all(lsum[g]);
+        float* o = wsp + (((int64_t)b * Hq + h * G + g) * (a.nsplit + a.nfsplit) + a.nsplit + f) * WS;
+        if (lane == 0) {
+            o[0] = mx[g];
+            o[1] = lt;
+        }
+#pragma unroll
+        for (int sv = 0; sv < NS; sv++) o[4 + 64 * sv + lane] = 0.f;
+        if (lane < LPT) {
+#pragma unroll
+            for (int c = 0; c < 8; c++) o[4 + D + 8 * lane + c] = accp[c][g];
+        }
+    }
+}
+
 template <int D, int T, int KB, int VB>
 __global__ void __launch_bounds__(64) decode_split_kernel(DecodeArgs a) {
     constexpr int G = 4;
@@ -158,6 +322,13 @@ __global__ void __launch_bounds__(64) decode_split_kernel(DecodeArgs a) {
 
     __shared__ __attribute__((aligned(16))) _Float16 pt[2][G][64];  // p * S_V of a step (high, low), by operand position
 
+    // grid z < B: quantized-page splits; z >= B: fp16 page slots, dispatched
+    // after every split so that they fill the splits' tail
+    if ((int)blockIdx.z >= a.B) {
+        if ((int)blockIdx.x < a.nfsplit) fp16_block<D, T>(a, blockIdx.x, blockIdx.y, blockIdx.z - a.B);
+        return;
+    }
+    if ((int)blockIdx.x >= a.nsplit) return;
     const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int lane = threadIdx.x;
     const int blk = lane >> 2, m = lane & 3;  // MFMA block; row (query head) of the broadcast operand
@@ -616,6 +787,13 @@ __global__ void __launch_bounds__(64) decode_split128_kernel(DecodeArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t qt[13 * QROW];
     __shared__ __attribute__((aligned(16))) uint8_t wt[13 * WROW];
 
+    // grid z < B: quantized-page splits; z >= B: fp16 page slots, dispatched
+    // after every split so that they fill the splits' tail
+    if ((int)blockIdx.z >= a.B) {
+        if ((int)blockIdx.x < a.nfsplit) fp16_block<D, T>(a, blockIdx.x, blockIdx.y, blockIdx.z - a.B);
+        return;
+    }
+    if ((int)blockIdx.x >= a.nsplit) return;
     const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int lane = threadIdx.x;
     const int half = lane >> 5, col = lane & 31;
@@ -682,42 +860,51 @@ __global__ void __launch_bounds__(64) decode_split128_kernel(DecodeArgs a) {
         uint32_t ck[4];   // fp16 pairs: C_K at bchan(i, 2 j), bchan(i, 2 j + 1), word 2 i + j
         uint32_t cv;      // fp16 pair: C_V of channels lane, 64 + lane
     };
+    // Loads go through one buffer resource per pool (the pool sizes are below
+    // 4 GiB, checked on the host): the record offset is a scalar offset, the
+    // lane's part a 32-bit vector offset; reads past the pool return zeros.
+    const auto rsk = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(krec), (short)0,
+                                                       (int)(a.n_qpages * a.H * KREC), 0x00020000);
+    const auto rsv = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(vrec), (short)0,
+                                                       (int)(a.n_qpages * a.H * VREC), 0x00020000);
+    const uint32_t koff = (uint32_t)(col * KROW + half * (KROW / 2));
+    const uint32_t voff = (uint32_t)(col * VROW + 32 * half * VB / 8);
     // the key part of a step's loads (issued once the scores have used the
     // buffer's key words) and the value part (once the value sums are done)
     auto issue_k = [&](const StepRef& r, Buf& f) {
         if (!r.ok) return;
-        const uint8_t* rk = krec + ((int64_t)r.id * a.H + h) * KREC;
+        const int so = __builtin_amdgcn_readfirstlane((int)(((uint32_t)r.id * (uint32_t)a.H + (uint32_t)h) * (uint32_t)KREC));
 #pragma unroll
-        for (int tb = 0; tb < 2; tb++) {
-            const uint8_t* p = rk + (int64_t)(64 * r.h + 32 * tb + col) * KROW + half * (KROW / 2);
-            load_words(f.kw[tb], p, KW / 4);
-        }
-        f.ksz = reinterpret_cast<const uint32_t*>(rk + KCB)[64 * r.h + lane];
+        for (int tb = 0; tb < 2; tb++)
+#pragma unroll
+            for (int j = 0; j < KW / 4; j++) {
+                const auto v = __builtin_amdgcn_raw_buffer_load_b128(rsk, koff + (64 * r.h + 32 * tb) * KROW + 16 * j, so, 0);
+                f.kw[tb][4 * j] = v[0]; f.kw[tb][4 * j + 1] = v[1]; f.kw[tb][4 * j + 2] = v[2]; f.kw[tb][4 * j + 3] = v[3];
+            }
+        f.ksz = __builtin_amdgcn_raw_buffer_load_b32(rsk, 4 * lane + KCB + 256 * r.h, so, 0);
         if (r.h == 0) {
-            const uint16_t* ck = reinterpret_cast<const uint16_t*>(rk + KCB + 4 * T);
 #pragma unroll
             for (int i = 0; i < 2; i++)
 #pragma unroll
                 for (int j = 0; j < 2; j++)
-                    f.ck[2 * i + j] = (uint32_t)ck[bchan(i, 2 * j)] | ((uint32_t)ck[bchan(i, 2 * j + 1)] << 16);
+                    f.ck[2 * i + j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rsk, KCB + 4 * T + 2 * bchan(i, 2 * j), so, 0) |
+                                      ((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rsk, KCB + 4 * T + 2 * bchan(i, 2 * j + 1), so, 0) << 16);
         }
     };
     auto issue_v = [&](const StepRef& r, Buf& f) {
         if (!r.ok) return;
-        const uint8_t* rv = vrec + ((int64_t)r.id * a.H + h) * VREC;
+        const int so = __builtin_amdgcn_readfirstlane((int)(((uint32_t)r.id * (uint32_t)a.H + (uint32_t)h) * (uint32_t)VREC));
 #pragma unroll
-        for (int cb = 0; cb < 4; cb++) {
-            const uint8_t* p = rv + (int64_t)(32 * cb + col) * VROW + (64 * r.h + 32 * half) * VB / 8;
+        for (int cb = 0; cb < 4; cb++)
 #pragma unroll
             for (int j = 0; j < VW / 2; j++) {  // 8-byte pieces (the 6-bit share sits on an 8-byte boundary)
-                const uint2 v = reinterpret_cast<const uint2*>(p)[j];
-                f.vw[cb][2 * j] = v.x; f.vw[cb][2 * j + 1] = v.y;
+                const auto v = __builtin_amdgcn_raw_buffer_load_b64(rsv, voff + 32 * cb * VROW + 64 * r.h * VB / 8 + 8 * j, so, 0);
+                f.vw[cb][2 * j] = v[0]; f.vw[cb][2 * j + 1] = v[1];
             }
-        }
-        f.vsz = reinterpret_cast<const uint32_t*>(rv + VCB)[64 * r.h + lane];
+        f.vsz = __builtin_amdgcn_raw_buffer_load_b32(rsv, 4 * lane + VCB + 256 * r.h, so, 0);
         if (r.h == 0) {
-            const uint16_t* cvp = reinterpret_cast<const uint16_t*>(rv + VCB + 4 * T);
-            f.cv = (uint32_t)cvp[lane] | ((uint32_t)cvp[64 + lane] << 16);
+            f.cv = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rsv, VCB + 4 * T + 2 * lane, so, 0) |
+                   ((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rsv, VCB + 4 * T + 2 * (64 + lane), so, 0) << 16);
         }
     };
 
@@ -872,170 +1059,6 @@ __global__ void __launch_bounds__(64) decode_split128_kernel(DecodeArgs a) {
     }
 }
 
-// fp16 sink and tail pages (gmlx "KV cache quantization", "The two
-// schemes"): one wave per (fp16-page slot f, KV head, sequence).  Slot f is
-// the f-th fp16 page of the sequence (sink pages, then tail pages); its
-// partial goes to split nsplit + f with a zero rotated-basis sum.  Scores on
-// the MFMA with the plain query (fp16 high and low parts), lane = token;
-// value sums on the VALU, D/8 lanes per token row.
-template <int D, int T>
-__global__ void __launch_bounds__(64) decode_fp16_kernel(DecodeArgs a) {
-    constexpr int G = 4;
-    constexpr int NS = D / 64;
-    constexpr int NC = D / 128;
-    constexpr int TS = T / 64;
-    constexpr int WS = 2 * D + 4;
-    __shared__ float4 pf[T];  // weights of the page
-
-    const int f = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-    const int lane = threadIdx.x;
-    const int blk = lane >> 2, m = lane & 3;
-    const int Hq = a.Hq;
-    const float sm2 = a.sm_scale * kLog2e;
-    const int L = min(a.seq_lens[b], a.max_pages * T);
-    const int npages = L > 0 ? (L + T - 1) / T : 0;
-    const int nq = (L - a.sink - a.tail >= T) ? (L - a.sink - a.tail) / T : 0;
-    const int sp = a.sink / T;
-    const int page = f < sp ? f : sp + nq + (f - sp);
-    int id = -1;
-    if (page < npages) {
-        id = a.block_table[(int64_t)b * a.max_pages + page];
-        if (id < 0 || (int64_t)id >= a.n_fpages) id = -1;
-    }
-
-    constexpr int LPT = D / 8;     // lanes per token row in the value sums
-    constexpr int TG = 64 / LPT;   // tokens per load instruction
-    float mx[G], lsum[G], accp[8][G];
-#pragma unroll
-    for (int g = 0; g < G; g++) {
-        mx[g] = -INFINITY;
-        lsum[g] = 0.f;
-#pragma unroll
-        for (int c = 0; c < 8; c++) accp[c][g] = 0.f;
-    }
-    if (id >= 0) {  // uniform
-        // the plain query (fp16 high and low parts) at this lane's operand
-        // slots: 4 consecutive channels 4 i .. 4 i + 3 per slot
-        float qx[NS][4];
-        const int64_t qrow = ((int64_t)b * Hq + h * G + m) * D;
-        if (a.q_bf16) {  // uniform
-#pragma unroll
-            for (int r = 0; r < NS; r++) {
-                const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.q) + qrow +
-                                                                 4 * (32 * (r >> 1) + blk + 16 * (r & 1)));
-                qx[r][0] = __builtin_bit_cast(float, u.x << 16);
-                qx[r][1] = __builtin_bit_cast(float, u.x & 0xffff0000u);
-                qx[r][2] = __builtin_bit_cast(float, u.y << 16);
-                qx[r][3] = __builtin_bit_cast(float, u.y & 0xffff0000u);
-            }
-        } else {
-#pragma unroll
-            for (int r = 0; r < NS; r++) {
-                const float4 v = *reinterpret_cast<const float4*>(static_cast<const float*>(a.q) + qrow +
-                                                                  4 * (32 * (r >> 1) + blk + 16 * (r & 1)));
-                qx[r][0] = v.x; qx[r][1] = v.y; qx[r][2] = v.z; qx[r][3] = v.w;
-            }
-        }
-        h4 qp[NS], qpl[NS];
-#pragma unroll
-        for (int r = 0; r < NS; r++)
-#pragma unroll
-            for (int kk = 0; kk < 4; kk++) {
-                qp[r][kk] = (_Float16)qx[r][kk];
-                qpl[r][kk] = (_Float16)(qx[r][kk] - (float)qp[r][kk]);
-            }
-        float s[TS][G];
-#pragma unroll
-        for (int sb = 0; sb < TS; sb++) {
-            const int tok = 64 * sb + lane;
-            const bool valid = page * T + tok < L;
-            const uint16_t* kr = static_cast<const uint16_t*>(a.k_fp16) + (((int64_t)id * a.H + h) * T + tok) * D;
-            f4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int c = 0; c < NC; c++) {
-                static_for<16>([&](auto ic) {
-                    constexpr int il = 2 * decltype(ic)::value;
-                    const uint4 v = *reinterpret_cast<const uint4*>(kr + 128 * c + 4 * il);
-                    const h4 b0 = __builtin_bit_cast(h4, make_uint2(v.x, v.y));
-                    const h4 b1 = __builtin_bit_cast(h4, make_uint2(v.z, v.w));
-                    acc0 = mfma_bcast<il & 15>(qp[2 * c + (il >> 4)], b0, acc0);
-                    acc1 = mfma_bcast<il & 15>(qpl[2 * c + (il >> 4)], b0, acc1);
-                    acc0 = mfma_bcast<(il + 1) & 15>(qp[2 * c + ((il + 1) >> 4)], b1, acc0);
-                    acc1 = mfma_bcast<(il + 1) & 15>(qpl[2 * c + ((il + 1) >> 4)], b1, acc1);
-                });
-            }
-            const f4 R = acc0 + acc1;
-#pragma unroll
-            for (int g = 0; g < G; g++) s[sb][g] = valid ? sm2 * R[g] : -INFINITY;
-        }
-        // softmax over the page: the first token of a visited page is valid
-        float p[TS][G];
-#pragma unroll
-        for (int g = 0; g < G; g++) {
-            float v = s[0][g];
-#pragma unroll
-            for (int sb = 1; sb < TS; sb++) v = fmaxf(v, s[sb][g]);
-            mx[g] = wave_max_all(v);
-#pragma unroll
-            for (int sb = 0; sb < TS; sb++) {
-                p[sb][g] = exp2f(s[sb][g] - mx[g]);
-                lsum[g] += p[sb][g];
-            }
-        }
-#pragma unroll
-        for (int sb = 0; sb < TS; sb++) pf[64 * sb + lane] = make_float4(p[sb][0], p[sb][1], p[sb][2], p[sb][3]);
-        wave_sync();
-        // value sums: D/8 lanes per token row (16-byte loads of 8 channels), TG
-        // tokens per load instruction, the token groups summed at the end
-        const int nvalid = min(T, L - page * T);  // tokens past the end may hold anything
-        const uint16_t* vp = static_cast<const uint16_t*>(a.v_fp16) + ((int64_t)id * a.H + h) * T * D;
-        const int tg = lane / LPT, cc = lane % LPT;
-        // branch-free: a token past the end has weight 0 (its score is
-        // -inf) and reads the last valid token's values instead of its own
-#pragma unroll 8
-        for (int t0 = 0; t0 < T; t0 += TG) {
-            const int t = t0 + tg;
-            const uint4 w = *reinterpret_cast<const uint4*>(vp + (int64_t)min(t, nvalid - 1) * D + 8 * cc);
-            const float4 pv = pf[t];
-            const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-            for (int kk = 0; kk < 8; kk++) {
-                const float v = half_bits_to_float((ww[kk >> 1] >> (16 * (kk & 1))) & 0xffffu);
-                accp[kk][0] = fmaf(pv.x, v, accp[kk][0]);
-                accp[kk][1] = fmaf(pv.y, v, accp[kk][1]);
-                accp[kk][2] = fmaf(pv.z, v, accp[kk][2]);
-                accp[kk][3] = fmaf(pv.w, v, accp[kk][3]);
-            }
-        }
-    }
-    // sum the token groups (lane bits above log2(LPT))
-#pragma unroll
-    for (int kk = 0; kk < 8; kk++)
-#pragma unroll
-        for (int g = 0; g < G; g++) {
-            float v = accp[kk][g];
-            if constexpr (TG >= 4) v += xor_lane<4>(v);
-            if constexpr (TG >= 2) v += lane_bcast32(v);
-            accp[kk][g] = v;
-        }
-    float* wsp = a.ws + (int64_t)a.B * Hq * D;
-#pragma unroll
-    for (int g = 0; g < G; g++) {
-        const float lt = wave_sum_all(lsum[g]);
-        float* o = wsp + (((int64_t)b * Hq + h * G + g) * (a.nsplit + a.nfsplit) + a.nsplit + f) * WS;
-        if (lane == 0) {
-            o[0] = mx[g];
-            o[1] = lt;
-        }
-#pragma unroll
-        for (int sv = 0; sv < NS; sv++) o[4 + 64 * sv + lane] = 0.f;
-        if (lane < LPT) {
-#pragma unroll
-            for (int c = 0; c < 8; c++) o[4 + D + 8 * lane + c] = accp[c][g];
-        }
-    }
-}
-
 // q' = H q / sqrt(D) in fp32, one workgroup of D/2 threads per (sequence, query head)
 template <int D>
 __global__ void __launch_bounds__(D / 2) qrot_kernel(const void* __restrict__ q, int q_bf16, float* __restrict__ qr) {
@@ -1101,17 +1124,14 @@ hipError_t launch_gqa(const DecodeArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((qrot_kernel<D>), dim3(a.B * a.Hq), dim3(D / 2), 0, st, a.q, a.q_bf16, a.ws);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    // one launch: the quantized-page splits (z < B), then the fp16 page slots
+    const dim3 grid(a.nsplit > a.nfsplit ? a.nsplit : a.nfsplit, a.H, a.nfsplit > 0 ? 2 * a.B : a.B);
     if constexpr (D == 128)
-        hipLaunchKernelGGL((decode_split128_kernel<T, KB, VB>), dim3(a.nsplit, a.H, a.B), dim3(64), 0, st, a);
+        hipLaunchKernelGGL((decode_split128_kernel<T, KB, VB>), grid, dim3(64), 0, st, a);
     else
-        hipLaunchKernelGGL((decode_split_kernel<D, T, KB, VB>), dim3(a.nsplit, a.H, a.B), dim3(64), 0, st, a);
+        hipLaunchKernelGGL((decode_split_kernel<D, T, KB, VB>), grid, dim3(64), 0, st, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (a.nfsplit > 0) {
-        hipLaunchKernelGGL((decode_fp16_kernel<D, T>), dim3(a.nfsplit, a.H, a.B), dim3(64), 0, st, a);
-        e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
     hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(a.B * a.Hq), dim3(D), 0, st,
                        a.ws + (int64_t)a.B * a.Hq * D, a.out, a.nsplit + a.nfsplit);
     return hipGetLastError();
