@@ -13,8 +13,11 @@ Reported (one JSON line):
   value     (fp16 bytes consumed by quantize + decode effective bytes) /
             (quantize time + decode time), GB/s; times from HIP events around
             each call on the stream the kernels run on, averaged over the
-            timed steps.  L2 and the 256 MB last-level cache are flushed (a
-            1 GiB fill) before each call, outside the event pairs.
+            timed steps.  L2 and the 256 MB last-level cache are flushed
+            before each call, outside the event pairs, by reading a 1 GiB
+            buffer: the caches then hold clean lines of an unrelated buffer
+            (a fill would leave dirty lines whose write-back lands inside the
+            next timed call).
   roofline  the quantize kernel (the step's dominant kernel): algorithmic
             bytes per launch (fp16 read + records written) / launch time,
             against 8 TB/s HBM.  traffic: HBM bytes per launch from the
@@ -140,7 +143,12 @@ def main():
                                                device=dev)
     out = torch.empty((case["B"], case["Hq"], lay["D"]), dtype=torch.float32, device=dev)
     ws = kv.alloc_workspace(L, case["B"], case["Hq"], case["max_pages"], dev)
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    flush_buf = torch.ones(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
+    flush_sink = torch.zeros(1, dtype=torch.float32, device=dev)
+
+    def flush():
+        flush_sink.add_(flush_buf.sum())
+
     q_fp16, q_out, dec_bytes = byte_counts(case)
 
     def quantize():
@@ -153,11 +161,11 @@ def main():
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
 
     def step(timed):
-        flush.fill_(1)
+        flush()
         ev[0].record()
         quantize()
         ev[1].record()
-        flush.fill_(2)
+        flush()
         ev[2].record()
         decode()
         ev[3].record()

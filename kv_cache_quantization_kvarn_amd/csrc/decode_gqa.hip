@@ -146,13 +146,13 @@ __device__ __forceinline__ float sum_blocks_half(float v) {
 // the MFMA with the plain query (fp16 high and low parts), lane = token;
 // value sums on the VALU, D/8 lanes per token row.
 template <int D, int T>
-__device__ __forceinline__ void fp16_block(const DecodeArgs& a, const int f, const int h, const int b) {
+__device__ __forceinline__ void fp16_block(const DecodeArgs& a, const int f, const int h, const int b,
+                                           float4* pf /* LDS, T entries: weights of the page */) {
     constexpr int G = 4;
     constexpr int NS = D / 64;
     constexpr int NC = D / 128;
     constexpr int TS = T / 64;
     constexpr int WS = 2 * D + 4;
-    __shared__ float4 pf[T];  // weights of the page
 
     const int lane = threadIdx.x;
     const int blk = lane >> 2, m = lane & 3;
@@ -321,11 +321,12 @@ __global__ void __launch_bounds__(64) decode_split_kernel(DecodeArgs a) {
     static_assert(KCH % 16 == 0 && VROW % 16 == 0, "16-byte code segments");
 
     __shared__ __attribute__((aligned(16))) _Float16 pt[2][G][64];  // p * S_V of a step (high, low), by operand position
+    __shared__ float4 pf[T];
 
     // grid z < B: quantized-page splits; z >= B: fp16 page slots, dispatched
     // after every split so that they fill the splits' tail
     if ((int)blockIdx.z >= a.B) {
-        if ((int)blockIdx.x < a.nfsplit) fp16_block<D, T>(a, blockIdx.x, blockIdx.y, blockIdx.z - a.B);
+        if ((int)blockIdx.x < a.nfsplit) fp16_block<D, T>(a, blockIdx.x, blockIdx.y, blockIdx.z - a.B, pf);
         return;
     }
     if ((int)blockIdx.x >= a.nsplit) return;
@@ -767,6 +768,35 @@ __device__ __forceinline__ f4 pair_levels(const i16v& x, const i16v& y) {
     return r;
 }
 
+// LDS-DMA loads: each lane's 16 (or 4) bytes at buffer offset voff + soff
+// land at LDS address lds + 16 lane (4 lane).  Written as instructions so
+// that the compiler's wait-count tracking, which would hold every later LDS
+// read until all such loads have landed, stays out of the way: the caller
+// waits with s_waitcnt vmcnt before reading the bytes and keeps no other
+// vector-memory load in flight across them.  M0 carries the LDS address (the
+// compiler keeps nothing in M0 in these kernels).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_dma16(uint32_t lds, i4v rsrc, uint32_t voff, int soff) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 ::"s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
+}
+__device__ __forceinline__ void lds_dma4(uint32_t lds, i4v rsrc, uint32_t voff, int soff) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+                 ::"s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+// LDS byte address of a pointer into __shared__ memory
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+// raw buffer resource over [base, base + bytes): 32-bit offsets, no stride
+__device__ __forceinline__ i4v raw_buffer(const void* base, uint32_t bytes) {
+    const uint64_t p = (uint64_t)(uintptr_t)base;
+    return i4v{__builtin_amdgcn_readfirstlane((int)(uint32_t)p), __builtin_amdgcn_readfirstlane((int)(uint32_t)(p >> 32)),
+               __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000};
+}
+
 template <int T, int KB, int VB>
 __global__ void __launch_bounds__(64) decode_split128_kernel(DecodeArgs a) {
     constexpr int D = 128, G = 4;
@@ -783,6 +813,18 @@ __global__ void __launch_bounds__(64) decode_split128_kernel(DecodeArgs a) {
     constexpr int QROW = D, WROW = 64;    // bytes per row of the query / weight digit tables
     static_assert(KW == KB * 2 && (KROW / 2) % 16 == 0, "half token rows in 16-byte loads");
 
+    // The LDS stage of one step, filled by LDS-DMA loads issued one step
+    // ahead: key codes (the step's 64 token rows, 16-byte pieces swizzled for
+    // KB = 4), the token scale words of K and V, the column scales of K and V
+    // (a page's first step), value codes (channel-major, the 8 VB bytes of a
+    // channel's 64 tokens).  fp16 page slots use the same memory for their
+    // weights.
+    constexpr int KST = 64 * KROW;
+    constexpr int VST = 128 * 8 * VB;
+    constexpr int KSC = KST, VSC = KSC + 256, CKO = VSC + 256, CVO = CKO + 256, VSO = CVO + 256;
+    constexpr int STAGE = VSO + VST;
+    static_assert(STAGE >= 16 * T && KST % 1024 == 0 && VST % 1024 == 0, "stage sizes");
+    __shared__ __attribute__((aligned(16))) uint8_t stage[STAGE];
     // digit tables, rows 4 L + g; row 12 stays zero (the unused operand rows)
     __shared__ __attribute__((aligned(16))) uint8_t qt[13 * QROW];
     __shared__ __attribute__((aligned(16))) uint8_t wt[13 * WROW];
@@ -790,7 +832,8 @@ __global__ void __launch_bounds__(64) decode_split128_kernel(DecodeArgs a) {
     // grid z < B: quantized-page splits; z >= B: fp16 page slots, dispatched
     // after every split so that they fill the splits' tail
     if ((int)blockIdx.z >= a.B) {
-        if ((int)blockIdx.x < a.nfsplit) fp16_block<D, T>(a, blockIdx.x, blockIdx.y, blockIdx.z - a.B);
+        if ((int)blockIdx.x < a.nfsplit)
+            fp16_block<D, T>(a, blockIdx.x, blockIdx.y, blockIdx.z - a.B, reinterpret_cast<float4*>(stage));
         return;
     }
     if ((int)blockIdx.x >= a.nsplit) return;
@@ -815,7 +858,10 @@ __global__ void __launch_bounds__(64) decode_split128_kernel(DecodeArgs a) {
 #pragma unroll
         for (int i = 0; i < 2; i++)
 #pragma unroll
-            for (int k = 0; k < 4; k++) qv[i][k] = qr[bchan(i, k)];
+            for (int k = 0; k < 4; k++) {
+                qv[i][k] = qr[bchan(i, k)];
+                asm volatile("" ::"v"(qv[i][k]));  // loaded before any LDS-DMA load is in flight
+            }
     }
 
     // sequence length and page ids are wave-uniform (SGPRs)
@@ -831,11 +877,20 @@ __global__ void __launch_bounds__(64) decode_split128_kernel(DecodeArgs a) {
         accr[0][g] = accr[1][g] = 0.f;
     }
 
-    const int npg = nq > split ? (nq - split + a.nsplit - 1) / a.nsplit : 0;  // quantized pages of this split
+    const int npg = __builtin_amdgcn_readfirstlane(nq > split ? (nq - split + a.nsplit - 1) / a.nsplit : 0);  // quantized pages of this split
     const int nst = npg * TS;
     const uint8_t* const krec = static_cast<const uint8_t*>(a.k_records);
     const uint8_t* const vrec = static_cast<const uint8_t*>(a.v_records);
 
+    // the split's page ids, 64 at a time, page 64 c + l in lane l
+    const int* const btrow = a.block_table + (int64_t)b * a.max_pages + sp + split;
+    auto page_ids = [&](int c) {
+        const int i = 64 * c + lane;
+        const int id = i < npg ? btrow[(int64_t)i * a.nsplit] : -1;
+        asm volatile("" ::"v"(id));  // the load completes here, before any LDS-DMA load is in flight
+        return id;
+    };
+    int ids = page_ids(0);
     struct StepRef {
         int id, h;
         bool ok;
@@ -843,16 +898,15 @@ __global__ void __launch_bounds__(64) decode_split128_kernel(DecodeArgs a) {
     auto step_ref = [&](int k) {
         StepRef r;
         r.h = k % TS;
-        r.id = k < nst ? __builtin_amdgcn_readfirstlane(a.block_table[(int64_t)b * a.max_pages + sp + split + (k / TS) * a.nsplit])
-                       : -1;
+        r.id = k < nst ? __builtin_amdgcn_readlane(ids, (k / TS) & 63) : -1;
         r.ok = k < nst && r.id >= 0 && (int64_t)r.id < a.n_qpages;
         return r;
     };
 
-    // One step's loads: the lane's half rows of tokens col and 32 + col, the
-    // 32-token share of channels 32 cb + col (cb = 0..3), the scale words of
-    // token `lane`, and on a page's first step the builder's 8 column scales
-    // of K and this lane's 2 of V.
+    // A step's operands in registers: the lane's half rows of tokens col and
+    // 32 + col, the 32-token share of channels 32 cb + col (cb = 0..3), the
+    // scale words of token `lane`, and on a page's first step the builder's 8
+    // column scales of K and this lane's 2 of V.
     struct Buf {
         uint32_t kw[2][KW];
         uint32_t vw[4][VW];
@@ -862,49 +916,64 @@ __global__ void __launch_bounds__(64) decode_split128_kernel(DecodeArgs a) {
     };
     // Loads go through one buffer resource per pool (the pool sizes are below
     // 4 GiB, checked on the host): the record offset is a scalar offset, the
-    // lane's part a 32-bit vector offset; reads past the pool return zeros.
-    const auto rsk = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(krec), (short)0,
-                                                       (int)(a.n_qpages * a.H * KREC), 0x00020000);
-    const auto rsv = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(vrec), (short)0,
-                                                       (int)(a.n_qpages * a.H * VREC), 0x00020000);
-    const uint32_t koff = (uint32_t)(col * KROW + half * (KROW / 2));
-    const uint32_t voff = (uint32_t)(col * VROW + 32 * half * VB / 8);
-    // the key part of a step's loads (issued once the scores have used the
-    // buffer's key words) and the value part (once the value sums are done)
-    auto issue_k = [&](const StepRef& r, Buf& f) {
+    // lane's part a 32-bit vector offset.
+    const i4v rsk = raw_buffer(krec, (uint32_t)(a.n_qpages * a.H * KREC));
+    const i4v rsv = raw_buffer(vrec, (uint32_t)(a.n_qpages * a.H * VREC));
+    // key piece u (16 bytes; u = KB t + p for token t of the step) sits at
+    // stage piece kswz(u): for KB = 4 the 4 pieces of a row rotate with bits
+    // 1-2 of the token, so that 8 lanes reading one piece of 8 consecutive
+    // tokens hit 8 different bank groups (kswz is an involution)
+    auto kswz = [](int u) { return KB == 4 ? (u ^ ((u >> 3) & 3)) : u; };
+    const uint32_t sb = lds_address(stage);
+    // all of a step's loads into the stage
+    auto issue = [&](const StepRef& r) {
         if (!r.ok) return;
-        const int so = __builtin_amdgcn_readfirstlane((int)(((uint32_t)r.id * (uint32_t)a.H + (uint32_t)h) * (uint32_t)KREC));
+        const uint32_t rec = (uint32_t)r.id * (uint32_t)a.H + (uint32_t)h;
+        const int sk = __builtin_amdgcn_readfirstlane((int)(rec * (uint32_t)KREC));
+        const int sv = __builtin_amdgcn_readfirstlane((int)(rec * (uint32_t)VREC));
+#pragma unroll
+        for (int i = 0; i < KST / 1024; i++) lds_dma16(sb + 1024 * i, rsk, 16 * kswz(64 * i + lane), sk + KST * r.h);
+        lds_dma4(sb + KSC, rsk, 4 * lane, sk + KCB + 256 * r.h);
+        lds_dma4(sb + VSC, rsv, 4 * lane, sv + VCB + 256 * r.h);
+        if (r.h == 0) {
+            lds_dma4(sb + CKO, rsk, 4 * lane, sk + KCB + 4 * T);
+            lds_dma4(sb + CVO, rsv, 4 * lane, sv + VCB + 4 * T);
+        }
+#pragma unroll
+        for (int i = 0; i < VST / 1024; i++) {
+            const int u = 64 * i + lane;   // piece u: channel u / (VB / 2), part u % (VB / 2)
+            lds_dma16(sb + VSO + 1024 * i, rsv, (u / (VB / 2)) * VROW + 16 * (u % (VB / 2)), sv + 8 * VB * r.h);
+        }
+    };
+    // the lane's operands of a step out of the stage (after its loads have
+    // landed); once these reads are done the stage may be refilled
+    auto fetch = [&](const StepRef& r, Buf& f) {
 #pragma unroll
         for (int tb = 0; tb < 2; tb++)
 #pragma unroll
-            for (int j = 0; j < KW / 4; j++) {
-                const auto v = __builtin_amdgcn_raw_buffer_load_b128(rsk, koff + (64 * r.h + 32 * tb) * KROW + 16 * j, so, 0);
-                f.kw[tb][4 * j] = v[0]; f.kw[tb][4 * j + 1] = v[1]; f.kw[tb][4 * j + 2] = v[2]; f.kw[tb][4 * j + 3] = v[3];
+            for (int j = 0; j < KB / 2; j++) {
+                const int u = KB * (32 * tb + col) + (KB / 2) * half + j;
+                const uint4 v = *reinterpret_cast<const uint4*>(stage + 16 * kswz(u));
+                f.kw[tb][4 * j] = v.x; f.kw[tb][4 * j + 1] = v.y; f.kw[tb][4 * j + 2] = v.z; f.kw[tb][4 * j + 3] = v.w;
             }
-        f.ksz = __builtin_amdgcn_raw_buffer_load_b32(rsk, 4 * lane + KCB + 256 * r.h, so, 0);
+#pragma unroll
+        for (int cb = 0; cb < 4; cb++)
+#pragma unroll
+            for (int j = 0; j < VW / 2; j++) {
+                const uint2 v = *reinterpret_cast<const uint2*>(stage + VSO + (32 * cb + col) * 8 * VB + 4 * VB * half + 8 * j);
+                f.vw[cb][2 * j] = v.x; f.vw[cb][2 * j + 1] = v.y;
+            }
+        f.ksz = *reinterpret_cast<const uint32_t*>(stage + KSC + 4 * lane);
+        f.vsz = *reinterpret_cast<const uint32_t*>(stage + VSC + 4 * lane);
         if (r.h == 0) {
+            const uint16_t* ckc = reinterpret_cast<const uint16_t*>(stage + CKO);
+            const uint16_t* cvc = reinterpret_cast<const uint16_t*>(stage + CVO);
 #pragma unroll
             for (int i = 0; i < 2; i++)
 #pragma unroll
                 for (int j = 0; j < 2; j++)
-                    f.ck[2 * i + j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rsk, KCB + 4 * T + 2 * bchan(i, 2 * j), so, 0) |
-                                      ((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rsk, KCB + 4 * T + 2 * bchan(i, 2 * j + 1), so, 0) << 16);
-        }
-    };
-    auto issue_v = [&](const StepRef& r, Buf& f) {
-        if (!r.ok) return;
-        const int so = __builtin_amdgcn_readfirstlane((int)(((uint32_t)r.id * (uint32_t)a.H + (uint32_t)h) * (uint32_t)VREC));
-#pragma unroll
-        for (int cb = 0; cb < 4; cb++)
-#pragma unroll
-            for (int j = 0; j < VW / 2; j++) {  // 8-byte pieces (the 6-bit share sits on an 8-byte boundary)
-                const auto v = __builtin_amdgcn_raw_buffer_load_b64(rsv, voff + 32 * cb * VROW + 64 * r.h * VB / 8 + 8 * j, so, 0);
-                f.vw[cb][2 * j] = v[0]; f.vw[cb][2 * j + 1] = v[1];
-            }
-        f.vsz = __builtin_amdgcn_raw_buffer_load_b32(rsv, 4 * lane + VCB + 256 * r.h, so, 0);
-        if (r.h == 0) {
-            f.cv = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rsv, VCB + 4 * T + 2 * lane, so, 0) |
-                   ((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rsv, VCB + 4 * T + 2 * (64 + lane), so, 0) << 16);
+                    f.ck[2 * i + j] = (uint32_t)ckc[bchan(i, 2 * j)] | ((uint32_t)ckc[bchan(i, 2 * j + 1)] << 16);
+            f.cv = (uint32_t)cvc[lane] | ((uint32_t)cvc[64 + lane] << 16);
         }
     };
 
@@ -917,10 +986,13 @@ __global__ void __launch_bounds__(64) decode_split128_kernel(DecodeArgs a) {
 
     auto step = [&](const StepRef& cur, const StepRef& nxt, Buf& u) {
         if (!cur.ok) {  // uniform: a page whose id is outside the record pool is skipped
-            issue_k(nxt, u);
-            issue_v(nxt, u);
+            issue(nxt);
             return;
         }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");    // this step's stage has landed
+        fetch(cur, u);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // ... and has been read
+        issue(nxt);
         if (cur.h == 0) {
             // query digits of the new page into the table: q~ = q' * C_K, per
             // head scaled so that max |q~| 2^(21 - e) < 2^21
@@ -977,7 +1049,6 @@ __global__ void __launch_bounds__(64) decode_split128_kernel(DecodeArgs a) {
 #pragma unroll
             for (int g = 0; g < G; g++) s[g] = fmaf(S * qs[g], R[g], Z * sqs[g]);
         }
-        issue_k(nxt, u);  // the key words are used up
 
         // ---- online softmax over the step (log2 domain) ----
         float p[G];
@@ -1029,14 +1100,16 @@ __global__ void __launch_bounds__(64) decode_split128_kernel(DecodeArgs a) {
             }
             wave_sync();  // the tables are rewritten by later steps
         }
-        issue_v(nxt, u);
     };
 
     Buf buf;
     StepRef cur = step_ref(0);
-    issue_k(cur, buf);
-    issue_v(cur, buf);
+    issue(cur);
     for (int k = 0; k < nst; k++) {
+        if ((k + 1) % (64 * TS) == 0 && k + 1 < nst) {  // the next 64 pages' ids (the stage's loads wait)
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            ids = page_ids((k + 1) / (64 * TS));
+        }
         const StepRef nx = step_ref(k + 1);
         step(cur, nx, buf);
         cur = nx;
