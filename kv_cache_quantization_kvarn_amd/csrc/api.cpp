@@ -163,7 +163,7 @@ size_t kvarn_decode_workspace_bytes(const kvarn_layout* layout, int32_t batch, i
     kvarn::decode_plan(layout->head_dim, H, num_q_heads / (H > 0 ? H : 1), layout->mla, batch, max_pages,
                        layout->tile_tokens, layout->k_bits, layout->v_bits, &ns, &pps);
     if (layout->mla) return kvarn::mla_workspace_floats(num_q_heads, batch, ns) * sizeof(float);
-    const int nf = kvarn::decode_fp16_pages(layout->tile_tokens, layout->sink_tokens, layout->tail_tokens, max_pages);
+    const int nf = kvarn::decode_fp16_slots(layout->tile_tokens, layout->sink_tokens, layout->tail_tokens, max_pages);
     return kvarn::decode_workspace_floats(layout->head_dim, num_q_heads, batch, ns, nf) * sizeof(float);
 }
 
@@ -202,7 +202,7 @@ kvarn_status kvarn_decode_attn(const kvarn_layout* layout, const kvarn_cache* ca
     int ns = 1, pps = 1;
     kvarn::decode_plan(layout->head_dim, H, G, layout->mla, pages->batch, pages->max_pages, layout->tile_tokens,
                        layout->k_bits, layout->v_bits, &ns, &pps);
-    const int nf = kvarn::decode_fp16_pages(layout->tile_tokens, layout->sink_tokens, layout->tail_tokens,
+    const int nf = kvarn::decode_fp16_slots(layout->tile_tokens, layout->sink_tokens, layout->tail_tokens,
                                             pages->max_pages);
     const size_t need = (layout->mla ? kvarn::mla_workspace_floats(num_q_heads, pages->batch, ns)
                                      : kvarn::decode_workspace_floats(layout->head_dim, num_q_heads, pages->batch, ns,

@@ -140,14 +140,14 @@ __device__ __forceinline__ float sum_blocks_half(float v) {
 
 // fp16 sink and tail pages (gmlx "KV cache quantization", "The two
 // schemes"): workgroups of the split kernels' grid past the splits, one wave
-// per (fp16-page slot f, KV head, sequence).  Slot f is
-// the f-th fp16 page of the sequence (sink pages, then tail pages); its
-// partial goes to split nsplit + f with a zero rotated-basis sum.  Scores on
-// the MFMA with the plain query (fp16 high and low parts), lane = token;
-// value sums on the VALU, D/8 lanes per token row.
+// per (fp16 slot f, KV head, sequence).  Slot f is the 64-token part f % (T /
+// 64) of the (f / (T / 64))-th fp16 page of the sequence (sink pages, then
+// tail pages); its partial goes to split nsplit + f with a zero rotated-basis
+// sum.  Scores on the MFMA with the plain query (fp16 high and low parts),
+// lane = token; value sums on the VALU, D/8 lanes per token row.
 template <int D, int T>
 __device__ __forceinline__ void fp16_block(const DecodeArgs& a, const int f, const int h, const int b,
-                                           float4* pf /* LDS, T entries: weights of the page */) {
+                                           float4* pf /* LDS, 64 entries: weights of the part */) {
     constexpr int G = 4;
     constexpr int NS = D / 64;
     constexpr int NC = D / 128;
@@ -162,11 +162,14 @@ __device__ __forceinline__ void fp16_block(const DecodeArgs& a, const int f, con
     const int npages = L > 0 ? (L + T - 1) / T : 0;
     const int nq = (L - a.sink - a.tail >= T) ? (L - a.sink - a.tail) / T : 0;
     const int sp = a.sink / T;
-    const int page = f < sp ? f : sp + nq + (f - sp);
+    const int fpg = f / TS, sb = f % TS;
+    const int page = fpg < sp ? fpg : sp + nq + (fpg - sp);
     int id = -1;
+    int nvalid = 0;  // valid tokens of the part
     if (page < npages) {
+        nvalid = min(64, min(T, L - page * T) - 64 * sb);
         id = a.block_table[(int64_t)b * a.max_pages + page];
-        if (id < 0 || (int64_t)id >= a.n_fpages) id = -1;
+        if (id < 0 || (int64_t)id >= a.n_fpages || nvalid <= 0) id = -1;
     }
 
     constexpr int LPT = D / 8;     // lanes per token row in the value sums
@@ -210,12 +213,9 @@ __device__ __forceinline__ void fp16_block(const DecodeArgs& a, const int f, con
                 qp[r][kk] = (_Float16)qx[r][kk];
                 qpl[r][kk] = (_Float16)(qx[r][kk] - (float)qp[r][kk]);
             }
-        float s[TS][G];
-#pragma unroll
-        for (int sb = 0; sb < TS; sb++) {
-            const int tok = 64 * sb + lane;
-            const bool valid = page * T + tok < L;
-            const uint16_t* kr = static_cast<const uint16_t*>(a.k_fp16) + (((int64_t)id * a.H + h) * T + tok) * D;
+        float s[G];
+        {
+            const uint16_t* kr = static_cast<const uint16_t*>(a.k_fp16) + (((int64_t)id * a.H + h) * T + 64 * sb + lane) * D;
             f4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int c = 0; c < NC; c++) {
@@ -231,36 +231,29 @@ __device__ __forceinline__ void fp16_block(const DecodeArgs& a, const int f, con
                 });
             }
             const f4 R = acc0 + acc1;
+            const bool valid = lane < nvalid;
 #pragma unroll
-            for (int g = 0; g < G; g++) s[sb][g] = valid ? sm2 * R[g] : -INFINITY;
+            for (int g = 0; g < G; g++) s[g] = valid ? sm2 * R[g] : -INFINITY;
         }
-        // softmax over the page: the first token of a visited page is valid
-        float p[TS][G];
+        // softmax over the part: its first token is valid
+        float p[G];
 #pragma unroll
         for (int g = 0; g < G; g++) {
-            float v = s[0][g];
-#pragma unroll
-            for (int sb = 1; sb < TS; sb++) v = fmaxf(v, s[sb][g]);
-            mx[g] = wave_max_all(v);
-#pragma unroll
-            for (int sb = 0; sb < TS; sb++) {
-                p[sb][g] = exp2f(s[sb][g] - mx[g]);
-                lsum[g] += p[sb][g];
-            }
+            mx[g] = wave_max_all(s[g]);
+            p[g] = exp2f(s[g] - mx[g]);
+            lsum[g] += p[g];
         }
-#pragma unroll
-        for (int sb = 0; sb < TS; sb++) pf[64 * sb + lane] = make_float4(p[sb][0], p[sb][1], p[sb][2], p[sb][3]);
+        pf[lane] = make_float4(p[0], p[1], p[2], p[3]);
         wave_sync();
         // value sums: D/8 lanes per token row (16-byte loads of 8 channels), TG
         // tokens per load instruction, the token groups summed at the end
-        const int nvalid = min(T, L - page * T);  // tokens past the end may hold anything
-        const uint16_t* vp = static_cast<const uint16_t*>(a.v_fp16) + ((int64_t)id * a.H + h) * T * D;
+        const uint16_t* vp = static_cast<const uint16_t*>(a.v_fp16) + (((int64_t)id * a.H + h) * T + 64 * sb) * D;
         const int tg = lane / LPT, cc = lane % LPT;
         // branch-free: a token past the end has weight 0 (its score is
         // -inf) and reads the last valid token's values instead of its own
 #pragma unroll 8
-        for (int t0 = 0; t0 < T; t0 += TG) {
-            const int t = t0 + tg;
+        for (int tt = 0; tt < 64; tt += TG) {
+            const int t = tt + tg;
             const uint4 w = *reinterpret_cast<const uint4*>(vp + (int64_t)min(t, nvalid - 1) * D + 8 * cc);
             const float4 pv = pf[t];
             const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
@@ -321,7 +314,7 @@ __global__ void __launch_bounds__(64) decode_split_kernel(DecodeArgs a) {
     static_assert(KCH % 16 == 0 && VROW % 16 == 0, "16-byte code segments");
 
     __shared__ __attribute__((aligned(16))) _Float16 pt[2][G][64];  // p * S_V of a step (high, low), by operand position
-    __shared__ float4 pf[T];
+    __shared__ float4 pf[64];
 
     // grid z < B: quantized-page splits; z >= B: fp16 page slots, dispatched
     // after every split so that they fill the splits' tail
@@ -752,10 +745,11 @@ __device__ __forceinline__ i16v mfma32_i8(i4v a, i4v b, i16v c) {
     return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
 }
 
-// x: lanes 0-31 hold column c0's (L0 at x[g], L2 at x[4 + g]) and lanes 32-63
-// column c0's L1 at x[g]; y likewise for column c1.  Returns, per lane, the
-// value 65536 L2 + 256 L1 + L0 of its own column (c0 in the lower half, c1 in
-// the upper half) for g = 0..3.
+// x: lanes 0-31 hold column c0's L0 at x[g] and L2 at x[4 + g], lanes 32-63
+// its L1 at x[g]; y likewise for column c1.  Returns, per lane, 65536 L2 +
+// 256 L1 + L0 of its own column (c0 in the lower half, c1 in the upper half)
+// for g = 0..3; L0 + 256 L1 is summed in int32 (each level is a sum of at
+// most 128 digit-code products, below 2^21 in magnitude).
 __device__ __forceinline__ f4 pair_levels(const i16v& x, const i16v& y) {
     f4 r;
 #pragma unroll
@@ -763,13 +757,13 @@ __device__ __forceinline__ f4 pair_levels(const i16v& x, const i16v& y) {
         const auto s01 = __builtin_amdgcn_permlane32_swap((unsigned)x[g], (unsigned)y[g], false, false);
         const auto s2 = __builtin_amdgcn_permlane32_swap((unsigned)x[4 + g], (unsigned)y[4 + g], false, false);
         // s01[0]: L0 of the lane's column, s01[1]: L1; s2[0]: L2
-        r[g] = fmaf((float)(int)s2[0], 65536.0f, fmaf((float)(int)s01[1], 256.0f, (float)(int)s01[0]));
+        r[g] = fmaf((float)(int)s2[0], 65536.0f, (float)((int)s01[0] + (int)(s01[1] << 8)));
     }
     return r;
 }
 
-// LDS-DMA loads: each lane's 16 (or 4) bytes at buffer offset voff + soff
-// land at LDS address lds + 16 lane (4 lane).  Written as instructions so
+// LDS-DMA loads: each active lane's 16 bytes at buffer offset voff + soff
+// land at LDS address lds + 16 lane.  Written as instructions so
 // that the compiler's wait-count tracking, which would hold every later LDS
 // read until all such loads have landed, stays out of the way: the caller
 // waits with s_waitcnt vmcnt before reading the bytes and keeps no other
@@ -779,10 +773,6 @@ __device__ __forceinline__ f4 pair_levels(const i16v& x, const i16v& y) {
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void lds_dma16(uint32_t lds, i4v rsrc, uint32_t voff, int soff) {
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-                 ::"s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
-}
-__device__ __forceinline__ void lds_dma4(uint32_t lds, i4v rsrc, uint32_t voff, int soff) {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
                  ::"s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
 }
 #pragma clang diagnostic pop
@@ -815,15 +805,17 @@ __global__ void __launch_bounds__(64) decode_split128_kernel(DecodeArgs a) {
 
     // The LDS stage of one step, filled by LDS-DMA loads issued one step
     // ahead: key codes (the step's 64 token rows, 16-byte pieces swizzled for
-    // KB = 4), the token scale words of K and V, the column scales of K and V
-    // (a page's first step), value codes (channel-major, the 8 VB bytes of a
-    // channel's 64 tokens).  fp16 page slots use the same memory for their
-    // weights.
+    // KB = 4), the scale blocks of the page's K and V records (token scales
+    // and column scales, loaded with the page's first step), value codes
+    // (channel-major, the 8 VB bytes of a channel's 64 tokens).  fp16 slots
+    // use the same memory for their weights.
     constexpr int KST = 64 * KROW;
     constexpr int VST = 128 * 8 * VB;
-    constexpr int KSC = KST, VSC = KSC + 256, CKO = VSC + 256, CVO = CKO + 256, VSO = CVO + 256;
+    constexpr int SB = 4 * T + 2 * D;     // scale block of a record
+    constexpr int KSC = KST, VSC = KSC + SB, VSO = VSC + SB;
     constexpr int STAGE = VSO + VST;
-    static_assert(STAGE >= 16 * T && KST % 1024 == 0 && VST % 1024 == 0, "stage sizes");
+    static_assert(SB % 16 == 0 && SB / 16 <= 64, "scale block in one 16-byte load");
+    static_assert(STAGE >= 16 * 64 && KST % 1024 == 0 && VST % 1024 == 0, "stage sizes");
     __shared__ __attribute__((aligned(16))) uint8_t stage[STAGE];
     // digit tables, rows 4 L + g; row 12 stays zero (the unused operand rows)
     __shared__ __attribute__((aligned(16))) uint8_t qt[13 * QROW];
@@ -933,11 +925,9 @@ __global__ void __launch_bounds__(64) decode_split128_kernel(DecodeArgs a) {
         const int sv = __builtin_amdgcn_readfirstlane((int)(rec * (uint32_t)VREC));
 #pragma unroll
         for (int i = 0; i < KST / 1024; i++) lds_dma16(sb + 1024 * i, rsk, 16 * kswz(64 * i + lane), sk + KST * r.h);
-        lds_dma4(sb + KSC, rsk, 4 * lane, sk + KCB + 256 * r.h);
-        lds_dma4(sb + VSC, rsv, 4 * lane, sv + VCB + 256 * r.h);
-        if (r.h == 0) {
-            lds_dma4(sb + CKO, rsk, 4 * lane, sk + KCB + 4 * T);
-            lds_dma4(sb + CVO, rsv, 4 * lane, sv + VCB + 4 * T);
+        if (r.h == 0 && lane < SB / 16) {  // the page's scale blocks
+            lds_dma16(sb + KSC, rsk, 16 * lane, sk + KCB);
+            lds_dma16(sb + VSC, rsv, 16 * lane, sv + VCB);
         }
 #pragma unroll
         for (int i = 0; i < VST / 1024; i++) {
@@ -963,11 +953,11 @@ __global__ void __launch_bounds__(64) decode_split128_kernel(DecodeArgs a) {
                 const uint2 v = *reinterpret_cast<const uint2*>(stage + VSO + (32 * cb + col) * 8 * VB + 4 * VB * half + 8 * j);
                 f.vw[cb][2 * j] = v.x; f.vw[cb][2 * j + 1] = v.y;
             }
-        f.ksz = *reinterpret_cast<const uint32_t*>(stage + KSC + 4 * lane);
-        f.vsz = *reinterpret_cast<const uint32_t*>(stage + VSC + 4 * lane);
+        f.ksz = *reinterpret_cast<const uint32_t*>(stage + KSC + 4 * (64 * r.h + lane));
+        f.vsz = *reinterpret_cast<const uint32_t*>(stage + VSC + 4 * (64 * r.h + lane));
         if (r.h == 0) {
-            const uint16_t* ckc = reinterpret_cast<const uint16_t*>(stage + CKO);
-            const uint16_t* cvc = reinterpret_cast<const uint16_t*>(stage + CVO);
+            const uint16_t* ckc = reinterpret_cast<const uint16_t*>(stage + KSC + 4 * T);
+            const uint16_t* cvc = reinterpret_cast<const uint16_t*>(stage + VSC + 4 * T);
 #pragma unroll
             for (int i = 0; i < 2; i++)
 #pragma unroll
@@ -1246,15 +1236,16 @@ void decode_plan(int D, int H, int G, int mla, int B, int max_pages, int T, int 
     if (*nsplit < 1) *nsplit = 1;
 }
 
-int decode_fp16_pages(int T, int sink, int tail, int max_pages) {
+int decode_fp16_slots(int T, int sink, int tail, int max_pages) {
     // fp16 tokens of a sequence: fewer than sink + tail + T (with quantized
-    // pages: sink + tail + T - 1 at most), the sink a whole number of pages
+    // pages: sink + tail + T - 1 at most), the sink a whole number of pages;
+    // one slot per 64-token part of such a page
     const int n = sink / T + (tail + 2 * T - 2) / T;
-    return n < max_pages ? n : max_pages;
+    return (n < max_pages ? n : max_pages) * (T / 64);
 }
 
 // fp32 rotated queries [B][Hq][D], then split partials
-// [B][Hq][nsplit + nfsplit][2D + 4] (quantized-page splits, then fp16-page slots)
+// [B][Hq][nsplit + nfsplit][2D + 4] (quantized-page splits, then fp16 slots)
 size_t decode_workspace_floats(int D, int Hq, int B, int nsplit, int nfsplit) {
     return (size_t)B * Hq * D + (size_t)B * Hq * (nsplit + nfsplit) * (2 * D + 4);
 }

@@ -31,7 +31,7 @@ struct DecodeArgs {
     int G;            // query heads per KV head (MLA: all query heads)
     int B, Hq, max_pages;
     int nsplit;       // splits of each sequence (GQA: over its quantized pages)
-    int nfsplit;      // GQA: fp16-page slots of each sequence (one workgroup each)
+    int nfsplit;      // GQA: fp16 slots (64-token parts of fp16 pages) of each sequence, one workgroup each
     int pps;          // pages per split
     const void* k_records;
     const void* v_records;
@@ -51,7 +51,7 @@ struct DecodeArgs {
 void decode_plan(int D, int H, int G, int mla, int B, int max_pages, int T, int kb, int vb, int* nsplit,
                  int* pps);
 // GQA: the most fp16 (sink and tail) pages a sequence can have.
-int decode_fp16_pages(int T, int sink, int tail, int max_pages);
+int decode_fp16_slots(int T, int sink, int tail, int max_pages);
 size_t decode_workspace_floats(int D, int Hq, int B, int nsplit, int nfsplit);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
 
