@@ -191,13 +191,13 @@ kvarn_status kvarn_decode_attn(const kvarn_layout* layout, const kvarn_cache* ca
     if (cache->n_qpages > 0 && (!cache->k_records || (!layout->mla && !cache->v_records)))
         return fail(KVARN_EINVAL, "record pools are NULL");
     if (!(sm_scale > 0.f) || sm_scale > 1e30f) return fail(KVARN_EINVAL, "sm_scale must be positive and finite");
-    if (!layout->mla && layout->head_dim == 128) {
-        // the head_dim 128 kernel addresses each record pool with 32-bit byte offsets
+    if (layout->mla || layout->head_dim == 128) {
+        // the MLA and head_dim 128 kernels address each record pool with 32-bit byte offsets
         const uint64_t kb = (uint64_t)cache->n_qpages * (uint64_t)H * kvarn_record_bytes(layout, 0);
-        const uint64_t vb = (uint64_t)cache->n_qpages * (uint64_t)H * kvarn_record_bytes(layout, 1);
+        const uint64_t vb = layout->mla ? 0 : (uint64_t)cache->n_qpages * (uint64_t)H * kvarn_record_bytes(layout, 1);
         if (kb >= (1ull << 32) || vb >= (1ull << 32))
-            return fail(KVARN_EUNSUPPORTED, "head_dim 128: record pools of %llu / %llu bytes; below 4 GiB each is "
-                        "implemented", (unsigned long long)kb, (unsigned long long)vb);
+            return fail(KVARN_EUNSUPPORTED, "%s: record pools of %llu / %llu bytes; below 4 GiB each is implemented",
+                        layout->mla ? "mla" : "head_dim 128", (unsigned long long)kb, (unsigned long long)vb);
     }
     int ns = 1, pps = 1;
     kvarn::decode_plan(layout->head_dim, H, G, layout->mla, pages->batch, pages->max_pages, layout->tile_tokens,

@@ -762,31 +762,6 @@ __device__ __forceinline__ f4 pair_levels(const i16v& x, const i16v& y) {
     return r;
 }
 
-// LDS-DMA loads: each active lane's 16 bytes at buffer offset voff + soff
-// land at LDS address lds + 16 lane.  Written as instructions so
-// that the compiler's wait-count tracking, which would hold every later LDS
-// read until all such loads have landed, stays out of the way: the caller
-// waits with s_waitcnt vmcnt before reading the bytes and keeps no other
-// vector-memory load in flight across them.  M0 carries the LDS address (the
-// compiler keeps nothing in M0 in these kernels).
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void lds_dma16(uint32_t lds, i4v rsrc, uint32_t voff, int soff) {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-                 ::"s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
-}
-#pragma clang diagnostic pop
-// LDS byte address of a pointer into __shared__ memory
-__device__ __forceinline__ uint32_t lds_address(const void* p) {
-    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-// raw buffer resource over [base, base + bytes): 32-bit offsets, no stride
-__device__ __forceinline__ i4v raw_buffer(const void* base, uint32_t bytes) {
-    const uint64_t p = (uint64_t)(uintptr_t)base;
-    return i4v{__builtin_amdgcn_readfirstlane((int)(uint32_t)p), __builtin_amdgcn_readfirstlane((int)(uint32_t)(p >> 32)),
-               __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000};
-}
-
 template <int T, int KB, int VB>
 __global__ void __launch_bounds__(64) decode_split128_kernel(DecodeArgs a) {
     constexpr int D = 128, G = 4;
@@ -1227,6 +1202,8 @@ void decode_plan(int D, int H, int G, int mla, int B, int max_pages, int T, int 
     const int target = mla ? 256 : 3072;
     int ns = (target + units - 1) / units;
     if (ns < 1) ns = 1;
+    // MLA: a split holds its page ids in one register, 64 at most
+    if (mla && ns < (max_pages + 63) / 64) ns = (max_pages + 63) / 64;
     if (ns > max_pages) ns = max_pages;
     if (ns < 1) ns = 1;
     int p = (max_pages + ns - 1) / ns;

@@ -139,6 +139,11 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
     __shared__ __attribute__((aligned(16))) uint4 cbuf[2][MD / 8];    // column scales (units uswz), by page parity
     __shared__ float alpha[HQ];
     __shared__ int rescale_flag;
+    // ring of chunk slots: codes, token scales (SSC), column scales (SCC)
+    constexpr int NR = 8;
+    constexpr int SSC = CH * MD / 2, SCC = SSC + 4 * CH, SLOT = SCC + 2 * MD;
+    __shared__ __attribute__((aligned(16))) uint8_t ring[NR * SLOT];
+    __shared__ __attribute__((aligned(16))) uint8_t scratch[16 * NWV];  // targets of the stand-in loads
 
     // Workgroup id -> (head group hg, split, sequence b).  Workgroups are dealt
     // to the 8 XCDs round-robin; the head groups of one (split, sequence) get
@@ -152,7 +157,7 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
     if (u >= units) return;
     const int b = u / a.nsplit, split = u - b * a.nsplit;
     const int h0 = hg * HQ;  // first query head of this workgroup
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, g4 = lane >> 4;
     const float sm2 = a.sm_scale * kLog2e;
     const bool qk_wave = wave < HB;
@@ -207,73 +212,88 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
     const int pend = min(pbeg + a.pps, npages);
 
     // Chunks of this split, in order: chunk ci is page pbeg + ci / CPP, tokens
-    // (ci % CPP) * CH .. +CH of it.  The codes and token scales of chunk ci + 1
-    // are loaded into registers while chunk ci runs its MFMAs; column scales are
-    // staged per page in LDS (cbuf, two slots by page parity).
+    // (ci % CPP) * CH .. +CH of it.  A ring of NR chunk slots in LDS is filled
+    // by LDS-DMA loads NR - 1 chunks ahead: the codes (8 KB, a quarter per
+    // wave), the token scales and, on a page's first chunk, the column scales
+    // (staged per page in cbuf, two slots by page parity, when the chunk is
+    // read back).  Every wave issues exactly three such loads per chunk (a
+    // one-lane load into a scratch line stands in for a load it has no use
+    // for), so a fixed s_waitcnt vmcnt count marks the oldest chunk as landed.
     constexpr int CPP = T / CH;
     const int nch = pend > pbeg ? (min(pend * T, L) - pbeg * T + CH - 1) / CH : 0;
     // read-back: token tt, channels CPT*part .. +CPT; lanes 8..15 of each 16 take token tt + 8
     static_assert(TPT == 8 && CPT == 64, "read-back mapping assumes 8 threads per token");
     const int tt = ((tid >> 3) & 1) * 8 + ((tid >> 4) & 3) + 4 * (wave & 1) + 16 * (wave >> 1);
     const int part = tid & 7;
-    uint4 pf_code[CPT / 32];
-    uint32_t pf_sz = 0;
-    uint4 pf_c = make_uint4(0u, 0u, 0u, 0u);
-    int pf_id = -1;
-    bool pf_quant = false;
+    // the split's page ids (at most 64 pages per split), page pbeg + l in lane l
+    const int pid = lane < pend - pbeg ? a.block_table[(int64_t)b * a.max_pages + pbeg + lane] : -1;
+    asm volatile("" ::"v"(pid));  // loaded before any LDS-DMA load is in flight
+#pragma unroll
+    for (int ks = 0; ks < 16; ks++) asm volatile("" ::"v"(qa[ks]));
     auto chunk_info = [&](int ci, int& page, int& c0, bool& quant, int& id) {
         page = pbeg + ci / CPP;
         c0 = (ci % CPP) * CH;
         quant = page >= sp && page < sp + nq;
-        id = a.block_table[(int64_t)b * a.max_pages + page];
+        id = __builtin_amdgcn_readlane(pid, (page - pbeg) & 63);
         if (id < 0 || (quant ? (int64_t)id >= a.n_qpages : (int64_t)id >= a.n_fpages)) id = -1;
     };
-    auto prefetch = [&](int ci) {
-        int page, c0, id;
-        bool quant;
-        chunk_info(ci, page, c0, quant, id);
-        pf_id = id;
-        pf_quant = quant;
-        if (id >= 0 && quant) {
-            const uint8_t* rk = static_cast<const uint8_t*>(a.k_records) + (int64_t)id * KREC;
-            const uint4* cp = reinterpret_cast<const uint4*>(rk + (int64_t)(c0 + tt) * (MD / 2) + (CPT / 2) * part);
+    const i32x4 rs = raw_buffer(a.k_records, (uint32_t)(a.n_qpages * KREC));
+    const uint32_t ring_lds = lds_address(ring), dummy_lds = lds_address(scratch) + 16 * wave;
+    auto issue_chunk = [&](int cj) {
+        int page = 0, c0 = 0, id = -1;
+        bool quant = false;
+        if (cj < nch) chunk_info(cj, page, c0, quant, id);
+        const bool q = id >= 0 && quant;
+        const uint32_t sl = ring_lds + (uint32_t)((cj % NR) * SLOT);
+        const int rec = __builtin_amdgcn_readfirstlane(q ? id * KREC : 0);
 #pragma unroll
-            for (int k = 0; k < CPT / 32; k++) pf_code[k] = cp[k];
-            pf_sz = reinterpret_cast<const uint32_t*>(rk + KCB)[c0 + tt];
-            if (c0 == 0 && tid < MD / 8) pf_c = reinterpret_cast<const uint4*>(rk + KCB + 4 * T)[tid];
+        for (int k = 0; k < 2; k++) {
+            if (q) lds_dma16(sl + 1024 * (2 * wave + k), rs, 16 * lane + 1024 * (2 * wave + k), rec + c0 * (MD / 2));
+            else if (lane == 0) lds_dma16(dummy_lds, rs, 0, 0);
+        }
+        if (q && wave == 0) {
+            if (lane < CH / 4) lds_dma16(sl + SSC, rs, 16 * lane, rec + KCB + 4 * c0);
+        } else if (q && wave == 1 && c0 == 0) {
+            lds_dma16(sl + SCC, rs, 16 * lane, rec + KCB + 4 * T);
+        } else if (lane == 0) {
+            lds_dma16(dummy_lds, rs, 0, 0);
         }
     };
-    if (nch > 0) prefetch(0);
+#pragma unroll
+    for (int cj = 0; cj < NR - 1; cj++) issue_chunk(cj);
 
     for (int ci = 0; ci < nch; ci++) {
+        issue_chunk(ci + NR - 1);
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * (NR - 1)) : "memory");  // chunk ci has landed
+        __syncthreads();
         int page, c0, id;
         bool quant;
         chunk_info(ci, page, c0, quant, id);
-        if (id < 0) {  // uniform: skip a page whose id is outside its pool
-            if (ci + 1 < nch) prefetch(ci + 1);
-            continue;
-        }
+        if (id < 0) continue;  // uniform: skip a page whose id is outside its pool
+        const uint8_t* slot = ring + (ci % NR) * SLOT;
         // ---- 1. chunk -> ybuf (rotated basis, fp16) ----
         if (quant) {
             uint4* cb = cbuf[page & 1];
             if (c0 == 0) {
+                const uint4 cpg = tid < MD / 8 ? reinterpret_cast<const uint4*>(slot + SCC)[tid] : make_uint4(0u, 0u, 0u, 0u);
                 if (tid < MD / 8)  // channels 8*tid .. +7 as pairs (0,4) (1,5) (2,6) (3,7)
-                    cb[uswz(tid)] = make_uint4(__builtin_amdgcn_perm(pf_c.z, pf_c.x, 0x05040100u),
-                                               __builtin_amdgcn_perm(pf_c.z, pf_c.x, 0x07060302u),
-                                               __builtin_amdgcn_perm(pf_c.w, pf_c.y, 0x05040100u),
-                                               __builtin_amdgcn_perm(pf_c.w, pf_c.y, 0x07060302u));
+                    cb[uswz(tid)] = make_uint4(__builtin_amdgcn_perm(cpg.z, cpg.x, 0x05040100u),
+                                               __builtin_amdgcn_perm(cpg.z, cpg.x, 0x07060302u),
+                                               __builtin_amdgcn_perm(cpg.w, cpg.y, 0x05040100u),
+                                               __builtin_amdgcn_perm(cpg.w, cpg.y, 0x07060302u));
                 __syncthreads();
             }
             uint32_t cw[CPT / 8];
 #pragma unroll
             for (int k = 0; k < CPT / 32; k++) {
-                cw[4 * k] = pf_code[k].x; cw[4 * k + 1] = pf_code[k].y;
-                cw[4 * k + 2] = pf_code[k].z; cw[4 * k + 3] = pf_code[k].w;
+                const uint4 v = *reinterpret_cast<const uint4*>(slot + tt * (MD / 2) + (CPT / 2) * part + 16 * k);
+                cw[4 * k] = v.x; cw[4 * k + 1] = v.y; cw[4 * k + 2] = v.z; cw[4 * k + 3] = v.w;
             }
+            const uint32_t szw = reinterpret_cast<const uint32_t*>(slot + SSC)[tt];
             // y = C (S c + Zp) in packed fp16: nibbles k and k + 4 of a code word
             // become the pair (1024 + c, 1024 + c') by or-ing in the exponent of 1024
-            const h2 S2 = __builtin_bit_cast(h2, (pf_sz & 0xffffu) * 0x10001u);
-            const h2 Z2 = __builtin_bit_cast(h2, (pf_sz >> 16) * 0x10001u);
+            const h2 S2 = __builtin_bit_cast(h2, (szw & 0xffffu) * 0x10001u);
+            const h2 Z2 = __builtin_bit_cast(h2, (szw >> 16) * 0x10001u);
             const h2 k1024 = h2{(_Float16)1024.0f, (_Float16)1024.0f};
 #pragma unroll
             for (int q8 = 0; q8 < CPT / 8; q8++) {
@@ -301,10 +321,13 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
                 f4 z[MBW];
 #pragma unroll
                 for (int m = 0; m < MBW; m++) z[m] = f4{0.f, 0.f, 0.f, 0.f};
+                // the half's 16 operand loads are all issued before the first MFMA
+                h8 bxs[16];
+#pragma unroll
+                for (int ks = 0; ks < 16; ks++) bxs[ks] = *reinterpret_cast<const h8*>(fp + (16 * th + l16) * MD + 32 * ks + 8 * g4);
 #pragma unroll
                 for (int ks = 0; ks < 16; ks++) {
-                    if ((ks & 1) == 0) __builtin_amdgcn_sched_barrier(0);
-                    h8 bx = *reinterpret_cast<const h8*>(fp + (16 * th + l16) * MD + 32 * ks + 8 * g4);
+                    h8 bx = bxs[ks];
                     // sign(mb, ks) = (-1)^popcount(((MBW/2)*wave) & ks) * (-1)^popcount((m >> 1) & ks):
                     // the wave part negates the B operand, the m part picks the pattern
                     if (__builtin_popcount((unsigned)((MBW / 2) * wave) & (unsigned)ks) & 1) bx = -bx;
@@ -328,7 +351,6 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
             }
         }
         __syncthreads();
-        if (ci + 1 < nch) prefetch(ci + 1);
 
         // ---- 2. scores and weights for this wave's 16 heads ----
         if (tid == 0) rescale_flag = 0;
@@ -424,6 +446,8 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
         }
         __syncthreads();
     }
+
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no load may land in LDS after the workgroup ends
 
     // ---- partial results: m, l per head; O rows for this wave's channels ----
     float* wsp = a.ws + (int64_t)a.B * a.Hq * MD / 2;  // partials follow the fp16 queries

@@ -68,4 +68,35 @@ __device__ __forceinline__ uint32_t float_to_half_bits(float f) {
     return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
 }
 
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// LDS-DMA loads: each active lane's 16 bytes at buffer offset voff + soff
+// land at LDS address lds + 16 lane.  Written as instructions so
+// that the compiler's wait-count tracking, which would hold every later LDS
+// read until all such loads have landed, stays out of the way: the caller
+// waits with s_waitcnt vmcnt before reading the bytes and keeps no other
+// vector-memory load in flight across them.  M0 carries the LDS address (the
+// compiler keeps nothing in M0 in these kernels).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// lds and soff must be wave-uniform.
+__device__ __forceinline__ void lds_dma16(uint32_t lds, i32x4 rsrc, uint32_t voff, int soff) {
+    lds = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds);
+    soff = __builtin_amdgcn_readfirstlane(soff);
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 ::"s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+// LDS byte address of a pointer into __shared__ memory
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+// raw buffer resource over [base, base + bytes): 32-bit offsets, no stride
+__device__ __forceinline__ i32x4 raw_buffer(const void* base, uint32_t bytes) {
+    const uint64_t p = (uint64_t)(uintptr_t)base;
+    return i32x4{__builtin_amdgcn_readfirstlane((int)(uint32_t)p), __builtin_amdgcn_readfirstlane((int)(uint32_t)(p >> 32)),
+               __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000};
+}
+
 }  // namespace kvarn
