@@ -1202,8 +1202,10 @@ void decode_plan(int D, int H, int G, int mla, int B, int max_pages, int T, int 
     const int target = mla ? 256 : 3072;
     int ns = (target + units - 1) / units;
     if (ns < 1) ns = 1;
-    // MLA: a split holds its page ids in one register, 64 at most
-    if (mla && ns < (max_pages + 63) / 64) ns = (max_pages + 63) / 64;
+    // MLA: a split holds its page ids in two registers, 128 at most (with the
+    // quantized and fp16 pages dealt separately, ceil(max_pages / 126) splits
+    // keep every split within that)
+    if (mla && ns < (max_pages + 125) / 126) ns = (max_pages + 125) / 126;
     if (ns > max_pages) ns = max_pages;
     if (ns < 1) ns = 1;
     int p = (max_pages + ns - 1) / ns;

@@ -14,10 +14,11 @@
 // softmax rescales O lazily: only when a head's running maximum grows by more
 // than 2^8, which keeps every weight below 256.  The combine applies H once.
 //
-// Workgroup: 4 waves per (head group of up to 64 heads, split, sequence).
-// QK: wave w owns head block w (16 heads).  PV: wave w owns 128 of the 512
-// channels for all the group's heads.  PV operands come from LDS through ds_read_b64_tr_b16 (4 rows
-// x 16 columns of halves transposed per 16 lanes).
+// Workgroup: 8 waves (two per SIMD) per (head group of up to 64 heads,
+// split, sequence).  QK: each wave owns one head block (16 heads) and one
+// 16-token half of a chunk.  PV: each wave owns 64 of the 512 channels for
+// all the group's heads.  PV operands come from LDS through ds_read_b64_tr_b16
+// (4 rows x 16 columns of halves transposed per 16 lanes).
 #include <math.h>
 
 #include "kvarn_device.hpp"
@@ -111,37 +112,44 @@ __global__ void __launch_bounds__(256) qrot_kernel(const void* __restrict__ q, i
 // P = (-1)^(popcount(l16 & i & 7) + l16_3 * g4_0): two per-lane operand
 // patterns (and their negations) serve every block.
 
-// Workgroup of 4 waves.  QK: wave w owns head block w (16 heads).  PV: wave w
-// owns channels CPW*w .. CPW*w + CPW - 1.
+// Workgroup of 8 waves, two per SIMD.  QK: wave w owns head block w & 3 (16
+// heads) and token half w >> 2 of a chunk.  PV: wave w owns channels
+// CPW*w .. CPW*w + CPW - 1 for all the group's heads.
 template <int HB>
 struct MlaShape {
     static_assert(HB >= 1 && HB <= 4, "a workgroup holds at most 64 heads");
-    static constexpr int NWV = 4;
+    static constexpr int NWV = 8;
     static constexpr int NT = NWV * 64;
     static constexpr int CPW = MD / NWV;   // PV channels per wave
     static constexpr int CBW = CPW / 16;   // PV channel blocks per wave
     static constexpr int HQ = HB * 16;
 };
 
+// Work of a split: the quantized pages of the sequence are cut into nsplit
+// contiguous ranges, and the fp16 pages (sink, then tail) are dealt to the
+// splits round-robin, so every split gets the same share of both kinds.
+// A split runs its quantized chunks first (their loads stream through an LDS
+// ring), then its fp16 chunks.
 template <int T, int HB>
 __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs a) {
     using SH = MlaShape<HB>;
-    constexpr int NWV = SH::NWV, NT = SH::NT, CPW = SH::CPW, CBW = SH::CBW, HQ = SH::HQ;
+    constexpr int NWV = SH::NWV, CPW = SH::CPW, CBW = SH::CBW, HQ = SH::HQ;
     constexpr int KCB = T * MD / 2;                // int4 code bytes of a record
     constexpr int KREC = KCB + 4 * T + 2 * MD;
     constexpr int WS = MD + 4;                     // partial: m, l, pad, pad, O[512]
-    constexpr int TPT = NT / CH;                   // threads per token in the read-back
-    constexpr int CPT = MD / TPT;                  // channels per thread in the read-back
+    constexpr int CPP = T / CH;                    // chunks per page
     static_assert(HQ * 2 <= 160, "weight rows hold at most 64 heads");
     __shared__ __attribute__((aligned(16))) uint8_t ybuf[CH * YROW];   // chunk, rotated basis (fp16)
     __shared__ __attribute__((aligned(16))) uint8_t pbuf[PBYTES];      // weights [token][head] (fp16)
     __shared__ __attribute__((aligned(16))) h8 hpat[2][2][64];
     __shared__ __attribute__((aligned(16))) uint4 cbuf[2][MD / 8];    // column scales (units uswz), by page parity
     __shared__ float alpha[HQ];
+    __shared__ float cmx[2][HQ];                    // per token half: chunk maximum of each head
     __shared__ int rescale_flag;
     // ring of chunk slots: codes, token scales (SSC), column scales (SCC)
     constexpr int NR = 8;
     constexpr int SSC = CH * MD / 2, SCC = SSC + 4 * CH, SLOT = SCC + 2 * MD;
+    static_assert(SSC == NWV * 1024, "one 1 KB code load per wave and chunk");
     __shared__ __attribute__((aligned(16))) uint8_t ring[NR * SLOT];
     __shared__ __attribute__((aligned(16))) uint8_t scratch[16 * NWV];  // targets of the stand-in loads
 
@@ -151,16 +159,17 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
     // each latent chunk through that XCD's L2.
     const int nhg = a.Hq / HQ;
     const int units = a.B * a.nsplit;
-    const int id = blockIdx.x;
-    const int hg = (id % (8 * nhg)) / 8;
-    const int u = (id / (8 * nhg)) * 8 + (id % 8);
+    const int wid = blockIdx.x;
+    const int hg = (wid % (8 * nhg)) / 8;
+    const int u = (wid / (8 * nhg)) * 8 + (wid % 8);
     if (u >= units) return;
     const int b = u / a.nsplit, split = u - b * a.nsplit;
     const int h0 = hg * HQ;  // first query head of this workgroup
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, g4 = lane >> 4;
     const float sm2 = a.sm_scale * kLog2e;
-    const bool qk_wave = wave < HB;
+    const int hbq = wave & 3, thq = wave >> 2;   // QK: head block, token half
+    const bool qk_wave = hbq < HB;
 
     // rotated queries of this wave's head block, as QK A operands
     const _Float16* qr = reinterpret_cast<const _Float16*>(a.ws);  // q' at the start of the workspace
@@ -168,7 +177,7 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
 #pragma unroll
     for (int ks = 0; ks < 16; ks++) {
         if (qk_wave) {
-            const _Float16* p = qr + ((int64_t)b * a.Hq + h0 + wave * 16 + l16) * MD + 32 * ks + 8 * g4;
+            const _Float16* p = qr + ((int64_t)b * a.Hq + h0 + hbq * 16 + l16) * MD + 32 * ks + 8 * g4;
             const h8 v = *reinterpret_cast<const h8*>(p);
             qa[ks] = h8{v[0], v[4], v[1], v[5], v[2], v[6], v[3], v[7]};  // unit order
         } else {
@@ -176,7 +185,6 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
         }
     }
     // H_512 operand patterns for the fp16-chunk rotation, per lane: hpat[odd mb][negated][lane]
-    // (kept in LDS: only fp16 chunks use them)
     if (wave == 0) {
 #pragma unroll
         for (int od = 0; od < 2; od++) {
@@ -190,14 +198,15 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
             hpat[od][1][lane] = -v;
         }
     }
-    __syncthreads();
 
     f4 O[HB][CBW];
 #pragma unroll
     for (int hb = 0; hb < HB; hb++)
 #pragma unroll
         for (int c = 0; c < CBW; c++) O[hb][c] = f4{0.f, 0.f, 0.f, 0.f};
-    float mu[4], lp[4];  // running max (log2 units) and per-lane partial sums, heads 16*wave + 4*g4 + i
+    // running max (log2 units, the same in both token-half waves of a head
+    // block) and per-lane partial sums; heads 16*hbq + 4*g4 + i
+    float mu[4], lp[4];
 #pragma unroll
     for (int i = 0; i < 4; i++) {
         mu[i] = -INFINITY;
@@ -207,187 +216,69 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
     const int L = min(a.seq_lens[b], a.max_pages * T);
     const int npages = L > 0 ? (L + T - 1) / T : 0;
     const int nq = (L - a.sink - a.tail >= T) ? (L - a.sink - a.tail) / T : 0;
-    const int sp = a.sink / T;
-    const int pbeg = split * a.pps;
-    const int pend = min(pbeg + a.pps, npages);
-
-    // Chunks of this split, in order: chunk ci is page pbeg + ci / CPP, tokens
-    // (ci % CPP) * CH .. +CH of it.  A ring of NR chunk slots in LDS is filled
-    // by LDS-DMA loads NR - 1 chunks ahead: the codes (8 KB, a quarter per
-    // wave), the token scales and, on a page's first chunk, the column scales
-    // (staged per page in cbuf, two slots by page parity, when the chunk is
-    // read back).  Every wave issues exactly three such loads per chunk (a
-    // one-lane load into a scratch line stands in for a load it has no use
-    // for), so a fixed s_waitcnt vmcnt count marks the oldest chunk as landed.
-    constexpr int CPP = T / CH;
-    const int nch = pend > pbeg ? (min(pend * T, L) - pbeg * T + CH - 1) / CH : 0;
-    // read-back: token tt, channels CPT*part .. +CPT; lanes 8..15 of each 16 take token tt + 8
-    static_assert(TPT == 8 && CPT == 64, "read-back mapping assumes 8 threads per token");
-    const int tt = ((tid >> 3) & 1) * 8 + ((tid >> 4) & 3) + 4 * (wave & 1) + 16 * (wave >> 1);
-    const int part = tid & 7;
-    // the split's page ids (at most 64 pages per split), page pbeg + l in lane l
-    const int pid = lane < pend - pbeg ? a.block_table[(int64_t)b * a.max_pages + pbeg + lane] : -1;
-    asm volatile("" ::"v"(pid));  // loaded before any LDS-DMA load is in flight
+    const int sp = min(a.sink / T, npages);
+    const int nf = npages - nq;                           // fp16 pages: sink, then tail
+    const int qbeg = sp + (int)(((int64_t)nq * split) / a.nsplit);
+    const int nqp = sp + (int)(((int64_t)nq * (split + 1)) / a.nsplit) - qbeg;   // quantized pages of the split
+    const int nfp = nf > split ? (nf - split + a.nsplit - 1) / a.nsplit : 0;     // fp16 pages of the split
+    auto fpage = [&](int j) {  // page of the split's j-th fp16 page
+        const int f = split + j * a.nsplit;
+        return f < sp ? f : sp + nq + (f - sp);
+    };
+    // the split's page ids (128 at most), entry k in lane k & 63 of pid[k >> 6]:
+    // quantized pages first, then its fp16 pages
+    int pid[2];
+#pragma unroll
+    for (int r = 0; r < 2; r++) {
+        const int k = 64 * r + lane;
+        pid[r] = -1;
+        if (k < nqp) pid[r] = a.block_table[(int64_t)b * a.max_pages + qbeg + k];
+        else if (k < nqp + nfp) pid[r] = a.block_table[(int64_t)b * a.max_pages + fpage(k - nqp)];
+        asm volatile("" ::"v"(pid[r]));  // loaded before any LDS-DMA load is in flight
+    }
+    auto page_id = [&](int k) {  // k wave-uniform, < 128
+        const int x = __builtin_amdgcn_readlane(pid[0], k & 63), y = __builtin_amdgcn_readlane(pid[1], k & 63);
+        return k < 64 ? x : y;
+    };
 #pragma unroll
     for (int ks = 0; ks < 16; ks++) asm volatile("" ::"v"(qa[ks]));
-    auto chunk_info = [&](int ci, int& page, int& c0, bool& quant, int& id) {
-        page = pbeg + ci / CPP;
-        c0 = (ci % CPP) * CH;
-        quant = page >= sp && page < sp + nq;
-        id = __builtin_amdgcn_readlane(pid, (page - pbeg) & 63);
-        if (id < 0 || (quant ? (int64_t)id >= a.n_qpages : (int64_t)id >= a.n_fpages)) id = -1;
-    };
-    const i32x4 rs = raw_buffer(a.k_records, (uint32_t)(a.n_qpages * KREC));
-    const uint32_t ring_lds = lds_address(ring), dummy_lds = lds_address(scratch) + 16 * wave;
-    auto issue_chunk = [&](int cj) {
-        int page = 0, c0 = 0, id = -1;
-        bool quant = false;
-        if (cj < nch) chunk_info(cj, page, c0, quant, id);
-        const bool q = id >= 0 && quant;
-        const uint32_t sl = ring_lds + (uint32_t)((cj % NR) * SLOT);
-        const int rec = __builtin_amdgcn_readfirstlane(q ? id * KREC : 0);
-#pragma unroll
-        for (int k = 0; k < 2; k++) {
-            if (q) lds_dma16(sl + 1024 * (2 * wave + k), rs, 16 * lane + 1024 * (2 * wave + k), rec + c0 * (MD / 2));
-            else if (lane == 0) lds_dma16(dummy_lds, rs, 0, 0);
-        }
-        if (q && wave == 0) {
-            if (lane < CH / 4) lds_dma16(sl + SSC, rs, 16 * lane, rec + KCB + 4 * c0);
-        } else if (q && wave == 1 && c0 == 0) {
-            lds_dma16(sl + SCC, rs, 16 * lane, rec + KCB + 4 * T);
-        } else if (lane == 0) {
-            lds_dma16(dummy_lds, rs, 0, 0);
-        }
-    };
-#pragma unroll
-    for (int cj = 0; cj < NR - 1; cj++) issue_chunk(cj);
+    __syncthreads();
 
-    for (int ci = 0; ci < nch; ci++) {
-        issue_chunk(ci + NR - 1);
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * (NR - 1)) : "memory");  // chunk ci has landed
-        __syncthreads();
-        int page, c0, id;
-        bool quant;
-        chunk_info(ci, page, c0, quant, id);
-        if (id < 0) continue;  // uniform: skip a page whose id is outside its pool
-        const uint8_t* slot = ring + (ci % NR) * SLOT;
-        // ---- 1. chunk -> ybuf (rotated basis, fp16) ----
-        if (quant) {
-            uint4* cb = cbuf[page & 1];
-            if (c0 == 0) {
-                const uint4 cpg = tid < MD / 8 ? reinterpret_cast<const uint4*>(slot + SCC)[tid] : make_uint4(0u, 0u, 0u, 0u);
-                if (tid < MD / 8)  // channels 8*tid .. +7 as pairs (0,4) (1,5) (2,6) (3,7)
-                    cb[uswz(tid)] = make_uint4(__builtin_amdgcn_perm(cpg.z, cpg.x, 0x05040100u),
-                                               __builtin_amdgcn_perm(cpg.z, cpg.x, 0x07060302u),
-                                               __builtin_amdgcn_perm(cpg.w, cpg.y, 0x05040100u),
-                                               __builtin_amdgcn_perm(cpg.w, cpg.y, 0x07060302u));
-                __syncthreads();
-            }
-            uint32_t cw[CPT / 8];
-#pragma unroll
-            for (int k = 0; k < CPT / 32; k++) {
-                const uint4 v = *reinterpret_cast<const uint4*>(slot + tt * (MD / 2) + (CPT / 2) * part + 16 * k);
-                cw[4 * k] = v.x; cw[4 * k + 1] = v.y; cw[4 * k + 2] = v.z; cw[4 * k + 3] = v.w;
-            }
-            const uint32_t szw = reinterpret_cast<const uint32_t*>(slot + SSC)[tt];
-            // y = C (S c + Zp) in packed fp16: nibbles k and k + 4 of a code word
-            // become the pair (1024 + c, 1024 + c') by or-ing in the exponent of 1024
-            const h2 S2 = __builtin_bit_cast(h2, (szw & 0xffffu) * 0x10001u);
-            const h2 Z2 = __builtin_bit_cast(h2, (szw >> 16) * 0x10001u);
-            const h2 k1024 = h2{(_Float16)1024.0f, (_Float16)1024.0f};
-#pragma unroll
-            for (int q8 = 0; q8 < CPT / 8; q8++) {
-                const uint4 cv = cb[uswz(8 * part + q8)];  // column scales of unit 8*part + q8, pair order
-                const uint32_t cs[4] = {cv.x, cv.y, cv.z, cv.w};
-                const uint32_t w = cw[q8];
-                uint32_t o[4];
-#pragma unroll
-                for (int k = 0; k < 4; k++) {
-                    const h2 c = __builtin_bit_cast(h2, ((w >> (4 * k)) & 0x000F000Fu) | 0x64006400u) - k1024;
-                    const h2 y = __builtin_elementwise_fma(c, S2, Z2) * __builtin_bit_cast(h2, cs[k]);
-                    o[k] = __builtin_bit_cast(uint32_t, y);
-                }
-                *reinterpret_cast<uint4*>(ybuf + yoff(tt, 8 * part + q8)) = make_uint4(o[0], o[1], o[2], o[3]);
-            }
-        } else {
-                // y_t = H x_t / sqrt(512): Y^T = H X^T on the MFMA, the B operand read
-            // straight from the fp16 page (8 channels of one token per lane).
-            // Wave w writes channel blocks MBW*w .. of both 16-token halves.
-            constexpr int MBW = 32 / NWV;
-            const uint16_t* fp = static_cast<const uint16_t*>(a.k_fp16) + ((int64_t)id * T + c0) * MD;
-            const float rs = 1.0f / sqrtf((float)MD);
-#pragma unroll
-            for (int th = 0; th < 2; th++) {
-                f4 z[MBW];
-#pragma unroll
-                for (int m = 0; m < MBW; m++) z[m] = f4{0.f, 0.f, 0.f, 0.f};
-                // the half's 16 operand loads are all issued before the first MFMA
-                h8 bxs[16];
-#pragma unroll
-                for (int ks = 0; ks < 16; ks++) bxs[ks] = *reinterpret_cast<const h8*>(fp + (16 * th + l16) * MD + 32 * ks + 8 * g4);
-#pragma unroll
-                for (int ks = 0; ks < 16; ks++) {
-                    h8 bx = bxs[ks];
-                    // sign(mb, ks) = (-1)^popcount(((MBW/2)*wave) & ks) * (-1)^popcount((m >> 1) & ks):
-                    // the wave part negates the B operand, the m part picks the pattern
-                    if (__builtin_popcount((unsigned)((MBW / 2) * wave) & (unsigned)ks) & 1) bx = -bx;
-#pragma unroll
-                    for (int m = 0; m < MBW; m++) {
-                        const h8 av = hpat[m & 1][__builtin_popcount((unsigned)((m >> 1) & ks)) & 1][lane];
-                        z[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bx, z[m], 0, 0, 0);
-                    }
-                }
-                // lane: channels 16*mb + 4*g4 .. +3 of token 16*th + l16; tokens past the
-                // sequence end are zeroed (their weight is 0 and must not meet NaN)
-                const bool tv = page * T + c0 + 16 * th + l16 < L;
-#pragma unroll
-                for (int m = 0; m < MBW; m++) {
-                    // channel 4*(g4&1) + i of unit 2*mb + (g4>>1) sits at position 2*i + (g4&1)
-                    uint8_t* dst = ybuf + yoff(16 * th + l16, 2 * (MBW * wave + m) + (g4 >> 1)) + 2 * (g4 & 1);
-#pragma unroll
-                    for (int i = 0; i < 4; i++)
-                        *reinterpret_cast<uint16_t*>(dst + 4 * i) = tv ? (uint16_t)float_to_half_bits(z[m][i] * rs) : (uint16_t)0;
-                }
-            }
-        }
-        __syncthreads();
-
-        // ---- 2. scores and weights for this wave's 16 heads ----
+    // ---- scores, weights and value sums of the chunk in ybuf; tokens past
+    // the sequence end (tv = false for the token) get weight 0 ----
+    auto attend = [&](int tok0) {  // tok0: sequence position of the chunk's first token
         if (tid == 0) rescale_flag = 0;
-        bool need = false;
-        float s[2][4], cmax[4];
+        float s[4];
         if (qk_wave) {
-            // four independent accumulation chains per token half keep the MFMA
-            // pipeline busy for a lone wave; summed afterwards
-            f4 sacc[2];
+            // four independent accumulation chains keep the MFMA pipeline busy
+            f4 part4[4] = {f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f},
+                           f4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-            for (int th = 0; th < 2; th++) {
-                f4 part4[4] = {f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f},
-                               f4{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-                for (int ks = 0; ks < 16; ks++) {
-                    const h8 by = *reinterpret_cast<const h8*>(ybuf + yoff(16 * th + l16, 4 * ks + g4));
-                    part4[ks & 3] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[ks], by, part4[ks & 3], 0, 0, 0);
-                    if ((ks & 3) == 3) __builtin_amdgcn_sched_barrier(0);  // bound operand prefetch
-                }
-                sacc[th] = (part4[0] + part4[1]) + (part4[2] + part4[3]);
+            for (int ks = 0; ks < 16; ks++) {
+                const h8 by = *reinterpret_cast<const h8*>(ybuf + yoff(16 * thq + l16, 4 * ks + g4));
+                part4[ks & 3] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[ks], by, part4[ks & 3], 0, 0, 0);
+                if ((ks & 3) == 3) __builtin_amdgcn_sched_barrier(0);  // bound operand prefetch
             }
-            // lane: heads 16*wave + 4*g4 + i, tokens c0 + 16*th + l16
-#pragma unroll
-            for (int th = 0; th < 2; th++) {
-                const bool valid = page * T + c0 + 16 * th + l16 < L;
-#pragma unroll
-                for (int i = 0; i < 4; i++) s[th][i] = valid ? sacc[th][i] * sm2 : -INFINITY;
-            }
+            const f4 sacc = (part4[0] + part4[1]) + (part4[2] + part4[3]);
+            // lane: heads 16*hbq + 4*g4 + i, token 16*thq + l16 of the chunk
+            const bool valid = tok0 + 16 * thq + l16 < L;
 #pragma unroll
             for (int i = 0; i < 4; i++) {
-                cmax[i] = rmax16(fmaxf(s[0][i], s[1][i]));
-                need |= cmax[i] > mu[i] + kLazy;
+                s[i] = valid ? sacc[i] * sm2 : -INFINITY;
+                const float m = rmax16(s[i]);
+                if (l16 == 0) cmx[thq][16 * hbq + 4 * g4 + i] = m;
             }
         }
         __syncthreads();
         if (qk_wave) {
-            const bool any = __builtin_amdgcn_ballot_w64(need) != 0;
+            float cmax[4];
+            bool need = false;
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                cmax[i] = fmaxf(cmx[0][16 * hbq + 4 * g4 + i], cmx[1][16 * hbq + 4 * g4 + i]);
+                need |= cmax[i] > mu[i] + kLazy;
+            }
+            const bool any = __builtin_amdgcn_ballot_w64(need) != 0;  // the same in both token halves
 #pragma unroll
             for (int i = 0; i < 4; i++) {
                 float al = 1.f;
@@ -397,25 +288,21 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
                     lp[i] *= al;
                     mu[i] = mn;
                 }
-                if (l16 == 0) alpha[16 * wave + 4 * g4 + i] = al;
+                if (thq == 0 && l16 == 0) alpha[16 * hbq + 4 * g4 + i] = al;
             }
             if (any && lane == 0) atomicOr(&rescale_flag, 1);
+            float p[4];
 #pragma unroll
-            for (int th = 0; th < 2; th++) {
-                float p[4];
-#pragma unroll
-                for (int i = 0; i < 4; i++) {
-                    p[i] = (mu[i] == -INFINITY) ? 0.f : exp2f(s[th][i] - mu[i]);
-                    lp[i] += p[i];
-                }
-                const uint2 pk = make_uint2(float_to_half_bits(p[0]) | (float_to_half_bits(p[1]) << 16),
-                                            float_to_half_bits(p[2]) | (float_to_half_bits(p[3]) << 16));
-                *reinterpret_cast<uint2*>(pbuf + poff(16 * th + l16) + 32 * wave + 8 * g4) = pk;
+            for (int i = 0; i < 4; i++) {
+                p[i] = (mu[i] == -INFINITY) ? 0.f : exp2f(s[i] - mu[i]);
+                lp[i] += p[i];
             }
+            const uint2 pk = make_uint2(float_to_half_bits(p[0]) | (float_to_half_bits(p[1]) << 16),
+                                        float_to_half_bits(p[2]) | (float_to_half_bits(p[3]) << 16));
+            *reinterpret_cast<uint2*>(pbuf + poff(16 * thq + l16) + 32 * hbq + 8 * g4) = pk;
         }
         __syncthreads();
-
-        // ---- 3. O += P Y for this wave's channels ----
+        // O += P Y for this wave's channels
         if (rescale_flag) {
 #pragma unroll
             for (int hb = 0; hb < HB; hb++)
@@ -433,8 +320,8 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
             h8 bv[CBW];  // Y[32 tokens][16 channels]: lane channel l16, tokens 8*g4 .. +7
 #pragma unroll
             for (int c = 0; c < CBW; c++) {
-                const int u = (CPW * wave + 16 * c) / 8 + (q4 >> 1), hb8 = 8 * (q4 & 1);
-                bv[c] = cat(tr16(ybuf + yoff(row, u) + hb8), tr16(ybuf + yoff(row + 4, u) + hb8));
+                const int uu = (CPW * wave + 16 * c) / 8 + (q4 >> 1), hb8 = 8 * (q4 & 1);
+                bv[c] = cat(tr16(ybuf + yoff(row, uu) + hb8), tr16(ybuf + yoff(row + 4, uu) + hb8));
             }
 #pragma unroll
             for (int hb = 0; hb < HB; hb++) {
@@ -444,20 +331,165 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
                 for (int c = 0; c < CBW; c++) O[hb][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, bv[c], O[hb][c], 0, 0, 0);
             }
         }
-        __syncthreads();
-    }
+        __syncthreads();  // ybuf and pbuf are rewritten by the next chunk
+    };
 
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no load may land in LDS after the workgroup ends
+    // ---- quantized chunks: chunk ci is page qbeg + ci / CPP, tokens
+    // (ci % CPP) * CH .. +CH.  A ring of NR chunk slots in LDS is filled by
+    // LDS-DMA loads NR - 1 chunks ahead: the codes (1 KB per wave), the token
+    // scales and, on a page's first chunk, the column scales (staged per page
+    // in cbuf, by page parity, when the chunk is read back).  Every wave
+    // issues exactly two such loads per chunk (a one-lane load into a scratch
+    // line stands in for a load it has no use for), so a fixed s_waitcnt
+    // vmcnt count marks the oldest chunk as landed. ----
+    const int nqc = nqp * CPP;
+    // read-back: token tt, channels 32*part .. +32 (units 4*part .. +3)
+    const int tt = 4 * wave + (lane >> 4), part = lane & 15;
+    auto qchunk = [&](int ci, int& page, int& c0, int& id) {
+        page = qbeg + ci / CPP;
+        c0 = (ci % CPP) * CH;
+        id = page_id(ci / CPP);
+        if (id < 0 || (int64_t)id >= a.n_qpages) id = -1;
+    };
+    const i32x4 rs = raw_buffer(a.k_records, (uint32_t)(a.n_qpages * KREC));
+    const uint32_t ring_lds = lds_address(ring), dummy_lds = lds_address(scratch) + 16 * wave;
+    auto issue_chunk = [&](int cj) {
+        int page = 0, c0 = 0, id = -1;
+        if (cj < nqc) qchunk(cj, page, c0, id);
+        const bool q = id >= 0;
+        const uint32_t sl = ring_lds + (uint32_t)((cj % NR) * SLOT);
+        const int rec = q ? id * KREC : 0;
+        if (q) lds_dma16(sl + 1024 * wave, rs, 16 * lane + 1024 * wave, rec + c0 * (MD / 2));
+        else if (lane == 0) lds_dma16(dummy_lds, rs, 0, 0);
+        if (q && wave == 0) {
+            if (lane < CH / 4) lds_dma16(sl + SSC, rs, 16 * lane, rec + KCB + 4 * c0);
+        } else if (q && wave == 1 && c0 == 0) {
+            lds_dma16(sl + SCC, rs, 16 * lane, rec + KCB + 4 * T);
+        } else if (lane == 0) {
+            lds_dma16(dummy_lds, rs, 0, 0);
+        }
+    };
+#pragma unroll
+    for (int cj = 0; cj < NR - 1; cj++) issue_chunk(cj);
+
+    for (int ci = 0; ci < nqc; ci++) {
+        issue_chunk(ci + NR - 1);
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * (NR - 1)) : "memory");  // chunk ci has landed
+        __syncthreads();
+        int page, c0, id;
+        qchunk(ci, page, c0, id);
+        if (id < 0) continue;  // uniform: skip a page whose id is outside its pool
+        const uint8_t* slot = ring + (ci % NR) * SLOT;
+        // chunk -> ybuf (rotated basis, fp16)
+        uint4* cb = cbuf[page & 1];
+        if (c0 == 0) {
+            if (tid < MD / 8) {  // channels 8*tid .. +7 as pairs (0,4) (1,5) (2,6) (3,7)
+                const uint4 cpg = reinterpret_cast<const uint4*>(slot + SCC)[tid];
+                cb[uswz(tid)] = make_uint4(__builtin_amdgcn_perm(cpg.z, cpg.x, 0x05040100u),
+                                           __builtin_amdgcn_perm(cpg.z, cpg.x, 0x07060302u),
+                                           __builtin_amdgcn_perm(cpg.w, cpg.y, 0x05040100u),
+                                           __builtin_amdgcn_perm(cpg.w, cpg.y, 0x07060302u));
+            }
+            __syncthreads();
+        }
+        const uint4 cw4 = *reinterpret_cast<const uint4*>(slot + tt * (MD / 2) + 16 * part);
+        const uint32_t cw[4] = {cw4.x, cw4.y, cw4.z, cw4.w};
+        const uint32_t szw = reinterpret_cast<const uint32_t*>(slot + SSC)[tt];
+        // y = C (S c + Zp) in packed fp16: nibbles k and k + 4 of a code word
+        // become the pair (1024 + c, 1024 + c') by or-ing in the exponent of 1024
+        const h2 S2 = __builtin_bit_cast(h2, (szw & 0xffffu) * 0x10001u);
+        const h2 Z2 = __builtin_bit_cast(h2, (szw >> 16) * 0x10001u);
+        const h2 k1024 = h2{(_Float16)1024.0f, (_Float16)1024.0f};
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            const uint4 cv = cb[uswz(4 * part + q)];  // column scales of unit 4*part + q, pair order
+            const uint32_t cs[4] = {cv.x, cv.y, cv.z, cv.w};
+            const uint32_t w = cw[q];
+            uint32_t o[4];
+#pragma unroll
+            for (int k = 0; k < 4; k++) {
+                const h2 c = __builtin_bit_cast(h2, ((w >> (4 * k)) & 0x000F000Fu) | 0x64006400u) - k1024;
+                const h2 y = __builtin_elementwise_fma(c, S2, Z2) * __builtin_bit_cast(h2, cs[k]);
+                o[k] = __builtin_bit_cast(uint32_t, y);
+            }
+            *reinterpret_cast<uint4*>(ybuf + yoff(tt, 4 * part + q)) = make_uint4(o[0], o[1], o[2], o[3]);
+        }
+        __syncthreads();
+        attend(page * T + c0);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no load may land in LDS after this point
+
+    // ---- fp16 chunks: y_t = H x_t / sqrt(512), Y^T = H X^T on the MFMA, the B
+    // operand read straight from the fp16 page (8 channels of one token per
+    // lane).  Wave w writes channel blocks MBW*w .. of both 16-token halves. ----
+    for (int j = 0; j < nfp; j++) {
+        const int page = fpage(j);
+        int id = page_id(nqp + j);
+        if (id < 0 || (int64_t)id >= a.n_fpages) continue;  // uniform
+        const int nck = (min(L - page * T, T) + CH - 1) / CH;  // chunks holding tokens
+        for (int cc = 0; cc < nck; cc++) {
+            const int c0 = cc * CH;
+            constexpr int MBW = 32 / NWV;
+            const uint16_t* fp = static_cast<const uint16_t*>(a.k_fp16) + ((int64_t)id * T + c0) * MD;
+            const float rsq = 1.0f / sqrtf((float)MD);
+#pragma unroll
+            for (int th = 0; th < 2; th++) {
+                f4 z[MBW];
+#pragma unroll
+                for (int m = 0; m < MBW; m++) z[m] = f4{0.f, 0.f, 0.f, 0.f};
+                // the half's operand loads are issued four at a time before their MFMAs
+#pragma unroll
+                for (int k8 = 0; k8 < 4; k8++) {
+                    h8 bxs[4];
+#pragma unroll
+                    for (int kk = 0; kk < 4; kk++)
+                        bxs[kk] = *reinterpret_cast<const h8*>(fp + (16 * th + l16) * MD + 32 * (4 * k8 + kk) + 8 * g4);
+#pragma unroll
+                    for (int kk = 0; kk < 4; kk++) {
+                        const int ks = 4 * k8 + kk;
+                        h8 bx = bxs[kk];
+                        // sign(mb, ks) = (-1)^popcount(((MBW/2)*wave) & ks) * (-1)^popcount((m >> 1) & ks):
+                        // the wave part negates the B operand, the m part picks the pattern
+                        if (__builtin_popcount((unsigned)((MBW / 2) * wave) & (unsigned)ks) & 1) bx = -bx;
+#pragma unroll
+                        for (int m = 0; m < MBW; m++) {
+                            const h8 av = hpat[m & 1][__builtin_popcount((unsigned)((m >> 1) & ks)) & 1][lane];
+                            z[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bx, z[m], 0, 0, 0);
+                        }
+                    }
+                }
+                // lane: channels 16*mb + 4*g4 .. +3 of token 16*th + l16; tokens past the
+                // sequence end are zeroed (their weight is 0 and must not meet NaN)
+                const bool tv = page * T + c0 + 16 * th + l16 < L;
+#pragma unroll
+                for (int m = 0; m < MBW; m++) {
+                    // channel 4*(g4&1) + i of unit 2*mb + (g4>>1) sits at position 2*i + (g4&1)
+                    uint8_t* dst = ybuf + yoff(16 * th + l16, 2 * (MBW * wave + m) + (g4 >> 1)) + 2 * (g4 & 1);
+#pragma unroll
+                    for (int i = 0; i < 4; i++)
+                        *reinterpret_cast<uint16_t*>(dst + 4 * i) = tv ? (uint16_t)float_to_half_bits(z[m][i] * rsq) : (uint16_t)0;
+                }
+            }
+            __syncthreads();
+            attend(page * T + c0);
+        }
+    }
 
     // ---- partial results: m, l per head; O rows for this wave's channels ----
     float* wsp = a.ws + (int64_t)a.B * a.Hq * MD / 2;  // partials follow the fp16 queries
 #pragma unroll
     for (int i = 0; i < 4; i++) {
         const float lt = rsum16(lp[i]);
-        if (qk_wave && l16 == 0) {
-            float* o = wsp + (((int64_t)b * a.Hq + h0 + 16 * wave + 4 * g4 + i) * a.nsplit + split) * WS;
+        if (qk_wave && l16 == 0) cmx[thq][16 * hbq + 4 * g4 + i] = lt;
+    }
+    __syncthreads();
+    if (qk_wave && thq == 0 && l16 == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int hh = 16 * hbq + 4 * g4 + i;
+            float* o = wsp + (((int64_t)b * a.Hq + h0 + hh) * a.nsplit + split) * WS;
             o[0] = mu[i];
-            o[1] = lt;
+            o[1] = cmx[0][hh] + cmx[1][hh];
         }
     }
 #pragma unroll
