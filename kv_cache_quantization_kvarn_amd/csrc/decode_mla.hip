@@ -15,10 +15,11 @@
 // than 2^8, which keeps every weight below 256.  The combine applies H once.
 //
 // Workgroup: 8 waves (two per SIMD) per (head group of up to 64 heads,
-// split, sequence).  QK: each wave owns one head block (16 heads) and one
-// 16-token half of a chunk.  PV: each wave owns 64 of the 512 channels for
-// all the group's heads.  PV operands come from LDS through ds_read_b64_tr_b16
-// (4 rows x 16 columns of halves transposed per 16 lanes).
+// split, sequence).  Scores: waves 0..3 own one head block (16 heads) each
+// while waves 4..7 read the next chunk back.  Value sums: each wave owns 64
+// of the 512 channels for all the group's heads; their operands come from LDS
+// through ds_read_b64_tr_b16 (4 rows x 16 columns of halves transposed per 16
+// lanes).
 #include <math.h>
 
 #include "kvarn_device.hpp"
@@ -46,15 +47,15 @@ __device__ __forceinline__ h4 tr16(const void* p) {
 }
 
 // LDS layout of a read-back chunk: token rows of YROW bytes (512 halves + 32
-// bytes of pad); the 16-byte unit u of token t sits at unit
-// u ^ ((u >> 3) & 7) ^ tswz(t) of its row.  With that, the score operand
-// reads (16 tokens, one unit), the transposed value reads (4 tokens, two
-// units, per 16 lanes), and the read-back stores (8 units of one token per 8
-// lanes, tokens t and t + 8 per 16 lanes) each touch every LDS bank once.
+// bytes of pad), row t starting 16 bytes late when bit 2 of t is set; the
+// 16-byte unit u of token t sits at 16 u of its row.  Every access is a
+// per-lane base plus a constant, and in 128 bytes of banks the 16-byte units
+// of 8 consecutive tokens in one column fall on 8 different bank groups
+// (score operand reads, read-back stores) while 4 rows x 32 bytes of the
+// transposed value reads cover all 32 banks once.
 constexpr int YROW = 2 * 512 + 32;
-__device__ __forceinline__ int uswz(int u) { return u ^ ((u >> 3) & 7); }
-__device__ __forceinline__ int tswz(int t) { return ((t >> 2) & 1) | (((t >> 3) & 1) << 3); }
-__device__ __forceinline__ int yoff(int t, int u) { return t * YROW + ((uswz(u) ^ tswz(t)) << 4); }
+__device__ __forceinline__ int yoff(int t, int u) { return t * YROW + 16 * ((t >> 2) & 1) + 16 * u; }
+static_assert(31 * YROW + 16 + 16 * 64 <= 32 * YROW, "the last row fits");
 // Within a 16-byte unit the eight channels are held in the order
 // 0,4,1,5,2,6,3,7 (the order in which packed nibbles unpack to fp16 pairs);
 // position p holds channel upos(p).
@@ -112,9 +113,11 @@ __global__ void __launch_bounds__(256) qrot_kernel(const void* __restrict__ q, i
 // P = (-1)^(popcount(l16 & i & 7) + l16_3 * g4_0): two per-lane operand
 // patterns (and their negations) serve every block.
 
-// Workgroup of 8 waves, two per SIMD.  QK: wave w owns head block w & 3 (16
-// heads) and token half w >> 2 of a chunk.  PV: wave w owns channels
-// CPW*w .. CPW*w + CPW - 1 for all the group's heads.
+// Workgroup of 8 waves, two per SIMD.  Waves 0..3 ("score waves") own one
+// head block (16 heads) each: scores over a whole chunk, its softmax and its
+// weights.  Waves 4..7 read the next chunk back meanwhile.  All 8 waves then
+// form the value sums, wave w for channels CPW*w .. CPW*w + CPW - 1 of every
+// head.
 template <int HB>
 struct MlaShape {
     static_assert(HB >= 1 && HB <= 4, "a workgroup holds at most 64 heads");
@@ -128,8 +131,9 @@ struct MlaShape {
 // Work of a split: the quantized pages of the sequence are cut into nsplit
 // contiguous ranges, and the fp16 pages (sink, then tail) are dealt to the
 // splits round-robin, so every split gets the same share of both kinds.
-// A split runs its quantized chunks first (their loads stream through an LDS
-// ring), then its fp16 chunks.
+// A split runs its quantized chunks first, software-pipelined (their loads
+// stream through an LDS ring; chunk c + 1 is read back while chunk c is
+// scored), then its fp16 chunks.
 template <int T, int HB>
 __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs a) {
     using SH = MlaShape<HB>;
@@ -139,13 +143,12 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
     constexpr int WS = MD + 4;                     // partial: m, l, pad, pad, O[512]
     constexpr int CPP = T / CH;                    // chunks per page
     static_assert(HQ * 2 <= 160, "weight rows hold at most 64 heads");
-    __shared__ __attribute__((aligned(16))) uint8_t ybuf[CH * YROW];   // chunk, rotated basis (fp16)
-    __shared__ __attribute__((aligned(16))) uint8_t pbuf[PBYTES];      // weights [token][head] (fp16)
+    __shared__ __attribute__((aligned(16))) uint8_t ybuf[2][CH * YROW];  // chunks, rotated basis (fp16), by parity
+    __shared__ __attribute__((aligned(16))) uint8_t pbuf[PBYTES];         // weights [token][head] (fp16)
     __shared__ __attribute__((aligned(16))) h8 hpat[2][2][64];
-    __shared__ __attribute__((aligned(16))) uint4 cbuf[2][MD / 8];    // column scales (units uswz), by page parity
+    __shared__ __attribute__((aligned(16))) uint4 cbuf[2][MD / 8];       // column scales by unit, by page parity
     __shared__ float alpha[HQ];
-    __shared__ float cmx[2][HQ];                    // per token half: chunk maximum of each head
-    __shared__ int rescale_flag;
+    __shared__ int rescale_flag[2];                                        // by chunk parity
     // ring of chunk slots: codes, token scales (SSC), column scales (SCC)
     constexpr int NR = 8;
     constexpr int SSC = CH * MD / 2, SCC = SSC + 4 * CH, SLOT = SCC + 2 * MD;
@@ -168,8 +171,8 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, g4 = lane >> 4;
     const float sm2 = a.sm_scale * kLog2e;
-    const int hbq = wave & 3, thq = wave >> 2;   // QK: head block, token half
-    const bool qk_wave = hbq < HB;
+    const bool qk_wave = wave < HB;     // score wave with a head block
+    const bool rb_wave = wave >= 4;     // read-back wave
 
     // rotated queries of this wave's head block, as QK A operands
     const _Float16* qr = reinterpret_cast<const _Float16*>(a.ws);  // q' at the start of the workspace
@@ -177,7 +180,7 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
 #pragma unroll
     for (int ks = 0; ks < 16; ks++) {
         if (qk_wave) {
-            const _Float16* p = qr + ((int64_t)b * a.Hq + h0 + hbq * 16 + l16) * MD + 32 * ks + 8 * g4;
+            const _Float16* p = qr + ((int64_t)b * a.Hq + h0 + wave * 16 + l16) * MD + 32 * ks + 8 * g4;
             const h8 v = *reinterpret_cast<const h8*>(p);
             qa[ks] = h8{v[0], v[4], v[1], v[5], v[2], v[6], v[3], v[7]};  // unit order
         } else {
@@ -198,14 +201,14 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
             hpat[od][1][lane] = -v;
         }
     }
+    if (tid < 2) rescale_flag[tid] = 0;
 
     f4 O[HB][CBW];
 #pragma unroll
     for (int hb = 0; hb < HB; hb++)
 #pragma unroll
         for (int c = 0; c < CBW; c++) O[hb][c] = f4{0.f, 0.f, 0.f, 0.f};
-    // running max (log2 units, the same in both token-half waves of a head
-    // block) and per-lane partial sums; heads 16*hbq + 4*g4 + i
+    // score waves: running max (log2 units) and per-lane partial sums, heads 16*wave + 4*g4 + i
     float mu[4], lp[4];
 #pragma unroll
     for (int i = 0; i < 4; i++) {
@@ -244,66 +247,71 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
     for (int ks = 0; ks < 16; ks++) asm volatile("" ::"v"(qa[ks]));
     __syncthreads();
 
-    // ---- scores, weights and value sums of the chunk in ybuf; tokens past
-    // the sequence end (tv = false for the token) get weight 0 ----
-    auto attend = [&](int tok0) {  // tok0: sequence position of the chunk's first token
-        if (tid == 0) rescale_flag = 0;
-        float s[4];
-        if (qk_wave) {
-            // four independent accumulation chains keep the MFMA pipeline busy
-            f4 part4[4] = {f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f},
-                           f4{0.f, 0.f, 0.f, 0.f}};
+    // ---- score waves: scores, softmax and weights of the chunk in yb (32
+    // tokens from sequence position tok0; positions past the sequence end get
+    // weight 0).  Sets rescale_flag[par] when a running maximum moves. ----
+    auto score = [&](const uint8_t* yb, int tok0, int par) {
+        // 32 k-steps (token half th = k >> 4, channels 32 (k & 15) ..), the B
+        // operand loaded PF steps ahead; two accumulation chains per half
+        constexpr int PF = 8;
+        auto ld = [&](int k) {
+            return *reinterpret_cast<const h8*>(yb + yoff(16 * (k >> 4) + l16, 4 * (k & 15) + g4));
+        };
+        h8 by[PF];
 #pragma unroll
-            for (int ks = 0; ks < 16; ks++) {
-                const h8 by = *reinterpret_cast<const h8*>(ybuf + yoff(16 * thq + l16, 4 * ks + g4));
-                part4[ks & 3] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[ks], by, part4[ks & 3], 0, 0, 0);
-                if ((ks & 3) == 3) __builtin_amdgcn_sched_barrier(0);  // bound operand prefetch
-            }
-            const f4 sacc = (part4[0] + part4[1]) + (part4[2] + part4[3]);
-            // lane: heads 16*hbq + 4*g4 + i, token 16*thq + l16 of the chunk
-            const bool valid = tok0 + 16 * thq + l16 < L;
+        for (int k = 0; k < PF; k++) by[k] = ld(k);
+        f4 acc[2][2] = {{f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f}}, {f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f}}};
 #pragma unroll
-            for (int i = 0; i < 4; i++) {
-                s[i] = valid ? sacc[i] * sm2 : -INFINITY;
-                const float m = rmax16(s[i]);
-                if (l16 == 0) cmx[thq][16 * hbq + 4 * g4 + i] = m;
-            }
+        for (int k = 0; k < 32; k++) {
+            const h8 cur = by[k % PF];
+            if (k + PF < 32) by[k % PF] = ld(k + PF);
+            acc[k >> 4][k & 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[k & 15], cur, acc[k >> 4][k & 1], 0, 0, 0);
         }
-        __syncthreads();
-        if (qk_wave) {
-            float cmax[4];
-            bool need = false;
+        const f4 sacc[2] = {acc[0][0] + acc[0][1], acc[1][0] + acc[1][1]};
+        // lane: heads 16*wave + 4*g4 + i, tokens 16*th + l16 of the chunk
+        float s[2][4], cmax[4];
+        bool need = false;
 #pragma unroll
-            for (int i = 0; i < 4; i++) {
-                cmax[i] = fmaxf(cmx[0][16 * hbq + 4 * g4 + i], cmx[1][16 * hbq + 4 * g4 + i]);
-                need |= cmax[i] > mu[i] + kLazy;
-            }
-            const bool any = __builtin_amdgcn_ballot_w64(need) != 0;  // the same in both token halves
+        for (int th = 0; th < 2; th++) {
+            const bool valid = tok0 + 16 * th + l16 < L;
 #pragma unroll
-            for (int i = 0; i < 4; i++) {
-                float al = 1.f;
-                if (any) {
-                    const float mn = fmaxf(mu[i], cmax[i]);
-                    al = (mu[i] == -INFINITY) ? 0.f : exp2f(mu[i] - mn);
-                    lp[i] *= al;
-                    mu[i] = mn;
-                }
-                if (thq == 0 && l16 == 0) alpha[16 * hbq + 4 * g4 + i] = al;
+            for (int i = 0; i < 4; i++) s[th][i] = valid ? sacc[th][i] * sm2 : -INFINITY;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            cmax[i] = rmax16(fmaxf(s[0][i], s[1][i]));
+            need |= cmax[i] > mu[i] + kLazy;
+        }
+        const bool any = __builtin_amdgcn_ballot_w64(need) != 0;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            float al = 1.f;
+            if (any) {
+                const float mn = fmaxf(mu[i], cmax[i]);
+                al = (mu[i] == -INFINITY) ? 0.f : exp2f(mu[i] - mn);
+                lp[i] *= al;
+                mu[i] = mn;
             }
-            if (any && lane == 0) atomicOr(&rescale_flag, 1);
+            if (l16 == 0) alpha[16 * wave + 4 * g4 + i] = al;
+        }
+        if (any && lane == 0) atomicOr(&rescale_flag[par], 1);
+#pragma unroll
+        for (int th = 0; th < 2; th++) {
             float p[4];
 #pragma unroll
             for (int i = 0; i < 4; i++) {
-                p[i] = (mu[i] == -INFINITY) ? 0.f : exp2f(s[i] - mu[i]);
+                p[i] = (mu[i] == -INFINITY) ? 0.f : exp2f(s[th][i] - mu[i]);
                 lp[i] += p[i];
             }
             const uint2 pk = make_uint2(float_to_half_bits(p[0]) | (float_to_half_bits(p[1]) << 16),
                                         float_to_half_bits(p[2]) | (float_to_half_bits(p[3]) << 16));
-            *reinterpret_cast<uint2*>(pbuf + poff(16 * thq + l16) + 32 * hbq + 8 * g4) = pk;
+            *reinterpret_cast<uint2*>(pbuf + poff(16 * th + l16) + 32 * wave + 8 * g4) = pk;
         }
-        __syncthreads();
-        // O += P Y for this wave's channels
-        if (rescale_flag) {
+    };
+    // ---- all waves: O += P Y for this wave's channels (after the weights of
+    // the chunk in yb are in pbuf); clears the other parity's flag ----
+    auto accumulate = [&](const uint8_t* yb, int par) {
+        if (rescale_flag[par]) {
 #pragma unroll
             for (int hb = 0; hb < HB; hb++)
 #pragma unroll
@@ -313,38 +321,33 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
                     for (int c = 0; c < CBW; c++) O[hb][c][i] *= al;
                 }
         }
-        {
-            // tr16: lane 4k + q of a 16-lane group reads row k, columns 4q .. 4q+3;
-            // lane j receives column j of the 4 rows.  Rows are tokens.
-            const int row = 8 * g4 + (l16 >> 2), q4 = l16 & 3;
-            h8 bv[CBW];  // Y[32 tokens][16 channels]: lane channel l16, tokens 8*g4 .. +7
+        if (tid == 0) rescale_flag[par ^ 1] = 0;  // last read before the previous barrier
+        // tr16: lane 4k + q of a 16-lane group reads row k, columns 4q .. 4q+3;
+        // lane j receives column j of the 4 rows.  Rows are tokens.
+        const int row = 8 * g4 + (l16 >> 2), q4 = l16 & 3;
+        h8 bv[CBW];  // Y[32 tokens][16 channels]: lane channel l16, tokens 8*g4 .. +7
 #pragma unroll
-            for (int c = 0; c < CBW; c++) {
-                const int uu = (CPW * wave + 16 * c) / 8 + (q4 >> 1), hb8 = 8 * (q4 & 1);
-                bv[c] = cat(tr16(ybuf + yoff(row, uu) + hb8), tr16(ybuf + yoff(row + 4, uu) + hb8));
-            }
-#pragma unroll
-            for (int hb = 0; hb < HB; hb++) {
-                // P[16 heads][32 tokens]: lane head l16, tokens 8*g4 .. +7
-                const h8 pa = cat(tr16(pbuf + poff(row) + 32 * hb + 8 * q4), tr16(pbuf + poff(row + 4) + 32 * hb + 8 * q4));
-#pragma unroll
-                for (int c = 0; c < CBW; c++) O[hb][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, bv[c], O[hb][c], 0, 0, 0);
-            }
+        for (int c = 0; c < CBW; c++) {
+            const int uu = (CPW * wave + 16 * c) / 8 + (q4 >> 1), hb8 = 8 * (q4 & 1);
+            bv[c] = cat(tr16(yb + yoff(row, uu) + hb8), tr16(yb + yoff(row + 4, uu) + hb8));
         }
-        __syncthreads();  // ybuf and pbuf are rewritten by the next chunk
+#pragma unroll
+        for (int hb = 0; hb < HB; hb++) {
+            // P[16 heads][32 tokens]: lane head l16, tokens 8*g4 .. +7
+            const h8 pa = cat(tr16(pbuf + poff(row) + 32 * hb + 8 * q4), tr16(pbuf + poff(row + 4) + 32 * hb + 8 * q4));
+#pragma unroll
+            for (int c = 0; c < CBW; c++) O[hb][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, bv[c], O[hb][c], 0, 0, 0);
+        }
     };
 
     // ---- quantized chunks: chunk ci is page qbeg + ci / CPP, tokens
     // (ci % CPP) * CH .. +CH.  A ring of NR chunk slots in LDS is filled by
-    // LDS-DMA loads NR - 1 chunks ahead: the codes (1 KB per wave), the token
-    // scales and, on a page's first chunk, the column scales (staged per page
-    // in cbuf, by page parity, when the chunk is read back).  Every wave
-    // issues exactly two such loads per chunk (a one-lane load into a scratch
-    // line stands in for a load it has no use for), so a fixed s_waitcnt
-    // vmcnt count marks the oldest chunk as landed. ----
+    // LDS-DMA loads: the codes (1 KB per wave), the token scales and, on a
+    // page's first chunk, the column scales.  Every wave issues exactly two
+    // such loads per chunk (a one-lane load into a scratch line stands in for
+    // a load it has no use for), so a fixed s_waitcnt vmcnt count marks a
+    // chunk as landed. ----
     const int nqc = nqp * CPP;
-    // read-back: token tt, channels 32*part .. +32 (units 4*part .. +3)
-    const int tt = 4 * wave + (lane >> 4), part = lane & 15;
     auto qchunk = [&](int ci, int& page, int& c0, int& id) {
         page = qbeg + ci / CPP;
         c0 = (ci % CPP) * CH;
@@ -359,7 +362,10 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
         const bool q = id >= 0;
         const uint32_t sl = ring_lds + (uint32_t)((cj % NR) * SLOT);
         const int rec = q ? id * KREC : 0;
-        if (q) lds_dma16(sl + 1024 * wave, rs, 16 * lane + 1024 * wave, rec + c0 * (MD / 2));
+        if (q) {  // slot piece 64 w + l holds piece k ^ (t & 7) of token t's row (t = piece >> 4, k = piece & 15)
+            const int pc = 64 * wave + lane, t = pc >> 4;
+            lds_dma16(sl + 1024 * wave, rs, t * (MD / 2) + 16 * ((pc & 15) ^ (t & 7)), rec + c0 * (MD / 2));
+        }
         else if (lane == 0) lds_dma16(dummy_lds, rs, 0, 0);
         if (q && wave == 0) {
             if (lane < CH / 4) lds_dma16(sl + SSC, rs, 16 * lane, rec + KCB + 4 * c0);
@@ -369,42 +375,36 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
             lds_dma16(dummy_lds, rs, 0, 0);
         }
     };
-#pragma unroll
-    for (int cj = 0; cj < NR - 1; cj++) issue_chunk(cj);
-
-    for (int ci = 0; ci < nqc; ci++) {
-        issue_chunk(ci + NR - 1);
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * (NR - 1)) : "memory");  // chunk ci has landed
-        __syncthreads();
+    // read-back waves: chunk ci (landed) -> ybuf[ci & 1], rotated basis, fp16.
+    // Lane l of read-back wave 4 + v takes token tt = 8 v + (l & 7), units
+    // 8 part .. +8 (channels 64 part ..) with part = l >> 3: the 8 lanes of an
+    // 8-lane group hold 8 tokens of one column.  The column scales of a page
+    // come from the slot of its first chunk, where they are also staged in
+    // cbuf[page & 1] for its later chunks.
+    const int tt = 8 * ((wave - 4) & 3) + (lane & 7), part = (lane >> 3) & 7;
+    auto read_back = [&](int ci) {
         int page, c0, id;
         qchunk(ci, page, c0, id);
-        if (id < 0) continue;  // uniform: skip a page whose id is outside its pool
+        if (id < 0) return;
         const uint8_t* slot = ring + (ci % NR) * SLOT;
-        // chunk -> ybuf (rotated basis, fp16)
+        uint8_t* yb = ybuf[ci & 1];
         uint4* cb = cbuf[page & 1];
-        if (c0 == 0) {
-            if (tid < MD / 8) {  // channels 8*tid .. +7 as pairs (0,4) (1,5) (2,6) (3,7)
-                const uint4 cpg = reinterpret_cast<const uint4*>(slot + SCC)[tid];
-                cb[uswz(tid)] = make_uint4(__builtin_amdgcn_perm(cpg.z, cpg.x, 0x05040100u),
-                                           __builtin_amdgcn_perm(cpg.z, cpg.x, 0x07060302u),
-                                           __builtin_amdgcn_perm(cpg.w, cpg.y, 0x05040100u),
-                                           __builtin_amdgcn_perm(cpg.w, cpg.y, 0x07060302u));
-            }
-            __syncthreads();
+        const uint4* cpg = reinterpret_cast<const uint4*>(slot + SCC);
+        uint32_t cw[8];
+#pragma unroll
+        for (int k = 0; k < 2; k++) {  // pieces 2 part + k of the token's row (see issue_chunk)
+            const uint4 v = *reinterpret_cast<const uint4*>(slot + tt * (MD / 2) + 16 * ((2 * part + k) ^ (tt & 7)));
+            cw[4 * k] = v.x; cw[4 * k + 1] = v.y; cw[4 * k + 2] = v.z; cw[4 * k + 3] = v.w;
         }
-        const uint4 cw4 = *reinterpret_cast<const uint4*>(slot + tt * (MD / 2) + 16 * part);
-        const uint32_t cw[4] = {cw4.x, cw4.y, cw4.z, cw4.w};
         const uint32_t szw = reinterpret_cast<const uint32_t*>(slot + SSC)[tt];
         // y = C (S c + Zp) in packed fp16: nibbles k and k + 4 of a code word
         // become the pair (1024 + c, 1024 + c') by or-ing in the exponent of 1024
         const h2 S2 = __builtin_bit_cast(h2, (szw & 0xffffu) * 0x10001u);
         const h2 Z2 = __builtin_bit_cast(h2, (szw >> 16) * 0x10001u);
         const h2 k1024 = h2{(_Float16)1024.0f, (_Float16)1024.0f};
-#pragma unroll
-        for (int q = 0; q < 4; q++) {
-            const uint4 cv = cb[uswz(4 * part + q)];  // column scales of unit 4*part + q, pair order
+        auto unit = [&](int q8, const uint4 cv) {  // cv: column scales of the unit, pair order
             const uint32_t cs[4] = {cv.x, cv.y, cv.z, cv.w};
-            const uint32_t w = cw[q];
+            const uint32_t w = cw[q8];
             uint32_t o[4];
 #pragma unroll
             for (int k = 0; k < 4; k++) {
@@ -412,16 +412,62 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
                 const h2 y = __builtin_elementwise_fma(c, S2, Z2) * __builtin_bit_cast(h2, cs[k]);
                 o[k] = __builtin_bit_cast(uint32_t, y);
             }
-            *reinterpret_cast<uint4*>(ybuf + yoff(tt, 4 * part + q)) = make_uint4(o[0], o[1], o[2], o[3]);
+            *reinterpret_cast<uint4*>(yb + yoff(tt, 8 * part + q8)) = make_uint4(o[0], o[1], o[2], o[3]);
+        };
+        if (c0 == 0) {  // uniform: the page's first chunk brings its column scales
+            uint4 keep = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+            for (int q8 = 0; q8 < 8; q8++) {
+                const uint4 c = cpg[8 * part + q8];  // pairs (0,4) (1,5) (2,6) (3,7) of unit 8 part + q8
+                const uint4 cv = make_uint4(__builtin_amdgcn_perm(c.z, c.x, 0x05040100u), __builtin_amdgcn_perm(c.z, c.x, 0x07060302u),
+                                            __builtin_amdgcn_perm(c.w, c.y, 0x05040100u), __builtin_amdgcn_perm(c.w, c.y, 0x07060302u));
+                if (q8 == (tt & 7)) keep = cv;
+                unit(q8, cv);
+            }
+            if (tt < 8) cb[8 * part + tt] = keep;  // staged once per unit for the page's later chunks
+        } else {
+#pragma unroll
+            for (int q8 = 0; q8 < 8; q8++) unit(q8, cb[8 * part + q8]);
+        }
+    };
+    auto chunk_ok = [&](int ci) {
+        int page, c0, id;
+        qchunk(ci, page, c0, id);
+        return id >= 0;
+    };
+
+#pragma unroll
+    for (int cj = 0; cj < NR - 1; cj++) issue_chunk(cj);
+    if (nqc > 0) {
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * (NR - 2)) : "memory");  // chunk 0 has landed
+        __syncthreads();
+        if (rb_wave) read_back(0);
+        __syncthreads();
+    }
+    // iteration ci: issue chunk ci + NR - 1 into the slot chunk ci - 1 used;
+    // score chunk ci while chunk ci + 1 is read back; then the value sums of ci
+    for (int ci = 0; ci < nqc; ci++) {
+        issue_chunk(ci + NR - 1);
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * (NR - 2)) : "memory");  // chunk ci + 1 has landed
+        __syncthreads();
+        const bool ok = chunk_ok(ci);
+        if (qk_wave && ok) {
+            int page, c0, id;
+            qchunk(ci, page, c0, id);
+            score(ybuf[ci & 1], page * T + c0, ci & 1);
+        } else if (rb_wave && ci + 1 < nqc) {
+            read_back(ci + 1);
         }
         __syncthreads();
-        attend(page * T + c0);
+        if (ok) accumulate(ybuf[ci & 1], ci & 1);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no load may land in LDS after this point
+    __syncthreads();
 
     // ---- fp16 chunks: y_t = H x_t / sqrt(512), Y^T = H X^T on the MFMA, the B
     // operand read straight from the fp16 page (8 channels of one token per
     // lane).  Wave w writes channel blocks MBW*w .. of both 16-token halves. ----
+    int fpar = nqc & 1;  // chunk parity continues from the quantized chunks
     for (int j = 0; j < nfp; j++) {
         const int page = fpage(j);
         int id = page_id(nqp + j);
@@ -430,6 +476,7 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
         for (int cc = 0; cc < nck; cc++) {
             const int c0 = cc * CH;
             constexpr int MBW = 32 / NWV;
+            uint8_t* yb = ybuf[fpar];
             const uint16_t* fp = static_cast<const uint16_t*>(a.k_fp16) + ((int64_t)id * T + c0) * MD;
             const float rsq = 1.0f / sqrtf((float)MD);
 #pragma unroll
@@ -464,14 +511,17 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
 #pragma unroll
                 for (int m = 0; m < MBW; m++) {
                     // channel 4*(g4&1) + i of unit 2*mb + (g4>>1) sits at position 2*i + (g4&1)
-                    uint8_t* dst = ybuf + yoff(16 * th + l16, 2 * (MBW * wave + m) + (g4 >> 1)) + 2 * (g4 & 1);
+                    uint8_t* dst = yb + yoff(16 * th + l16, 2 * (MBW * wave + m) + (g4 >> 1)) + 2 * (g4 & 1);
 #pragma unroll
                     for (int i = 0; i < 4; i++)
                         *reinterpret_cast<uint16_t*>(dst + 4 * i) = tv ? (uint16_t)float_to_half_bits(z[m][i] * rsq) : (uint16_t)0;
                 }
             }
             __syncthreads();
-            attend(page * T + c0);
+            if (qk_wave) score(yb, page * T + c0, fpar);
+            __syncthreads();
+            accumulate(yb, fpar);
+            fpar ^= 1;
         }
     }
 
@@ -480,16 +530,10 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
 #pragma unroll
     for (int i = 0; i < 4; i++) {
         const float lt = rsum16(lp[i]);
-        if (qk_wave && l16 == 0) cmx[thq][16 * hbq + 4 * g4 + i] = lt;
-    }
-    __syncthreads();
-    if (qk_wave && thq == 0 && l16 == 0) {
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const int hh = 16 * hbq + 4 * g4 + i;
-            float* o = wsp + (((int64_t)b * a.Hq + h0 + hh) * a.nsplit + split) * WS;
+        if (qk_wave && l16 == 0) {
+            float* o = wsp + (((int64_t)b * a.Hq + h0 + 16 * wave + 4 * g4 + i) * a.nsplit + split) * WS;
             o[0] = mu[i];
-            o[1] = cmx[0][hh] + cmx[1][hh];
+            o[1] = lt;
         }
     }
 #pragma unroll
