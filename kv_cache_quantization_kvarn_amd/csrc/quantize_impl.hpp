@@ -137,6 +137,20 @@ __device__ __forceinline__ void xbutterfly(float (&y)[QR][QC], int lane) {
     }
 }
 
+// |a| * b + c in one v_fma_f32 with the abs source modifier.  Written as an
+// instruction so that |a| is never materialized (the compiler would hoist
+// it out of the iteration loop and hold both a and |a| in registers).
+__device__ __forceinline__ float fma_abs(float a, float b, float c) {
+    float d;
+    asm("v_fma_f32 %0, |%1|, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
+    return d;
+}
+__device__ __forceinline__ float mul_abs(float a, float b) {
+    float d;
+    asm("v_mul_f32_e64 %0, |%1|, %2" : "=v"(d) : "v"(a), "v"(b));
+    return d;
+}
+
 // finite and > 0: positive denormal or normal (one v_cmp_class)
 __device__ __forceinline__ bool usable(float s) { return __builtin_amdgcn_classf(s, 0x180); }
 
@@ -314,7 +328,7 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ tile,
     constexpr int CODE_BYTES = T * D * BITS / 8;
     constexpr int REC = CODE_BYTES + 4 * T + 2 * D;
     constexpr int NPART = (RGB >= 2) ? 4 : 8;          // column partials per lane after swaps
-    constexpr bool KEEP_Y = D <= 256;                  // D = 512 rebuilds y from y^2 and signs
+    constexpr bool KEEP_Y = D <= 256;                  // D = 512 keeps y |y| and rebuilds y from it
     static_assert(T * D / 64 == NT, "one lane per 64 values");
     static_assert(REC % 16 == 0, "records stay 16-byte aligned");
 
@@ -378,15 +392,13 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ tile,
     }
 
     // ---- stage 3: normalization iterations on A = y^2 ----------------------
+    // A holds y^2 (D = 512: y |y|, the sign of y on y^2; the statistics read
+    // |A| through the free abs source modifier)
     float A[QR][QC];
-    uint32_t negbits[QR] = {0, 0, 0, 0};
 #pragma unroll
     for (int r = 0; r < QR; r++)
 #pragma unroll
-        for (int c = 0; c < QC; c++) {
-            A[r][c] = y[r][c] * y[r][c];
-            if constexpr (!KEEP_Y) negbits[r] |= (y[r][c] < 0.f ? 1u : 0u) << c;
-        }
+        for (int c = 0; c < QC; c++) A[r][c] = KEEP_Y ? y[r][c] * y[r][c] : y[r][c] * fabsf(y[r][c]);
 
     // Row weights are kept as a / D (exact: D is a power of two), so the row
     // step is a bare reciprocal; the column step's T / D restores b.
@@ -399,9 +411,16 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ tile,
         float p[QC];
 #pragma unroll
         for (int c = 0; c < QC; c++) {
-            float s = A[0][c] * aw[0];
+            float s;
+            if constexpr (KEEP_Y) {
+                s = A[0][c] * aw[0];
 #pragma unroll
-            for (int r = 1; r < QR; r++) s = fmaf(A[r][c], aw[r], s);
+                for (int r = 1; r < QR; r++) s = fmaf(A[r][c], aw[r], s);
+            } else {
+                s = mul_abs(A[0][c], aw[0]);
+#pragma unroll
+                for (int r = 1; r < QR; r++) s = fma_abs(A[r][c], aw[r], s);
+            }
             p[c] = s;
         }
         // reduce over lane bit 5 (and 4) with permlane swaps: the lower half
@@ -463,9 +482,16 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ tile,
         // row step
 #pragma unroll
         for (int r = 0; r < QR; r++) {
-            float s = A[r][0] * bw[0];
+            float s;
+            if constexpr (KEEP_Y) {
+                s = A[r][0] * bw[0];
 #pragma unroll
-            for (int c = 1; c < QC; c++) s = fmaf(A[r][c], bw[c], s);
+                for (int c = 1; c < QC; c++) s = fmaf(A[r][c], bw[c], s);
+            } else {
+                s = mul_abs(A[r][0], bw[0]);
+#pragma unroll
+                for (int c = 1; c < QC; c++) s = fma_abs(A[r][c], bw[c], s);
+            }
             s = row_sum<CGB>(s);
             const float rc = __builtin_amdgcn_rcpf(s);
             aw[r] = usable(s) ? rc : aw[r];
@@ -503,8 +529,10 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ tile,
                 if constexpr (KEEP_Y) {
                     yv = y[r][c];
                 } else {
-                    yv = sqrtf(A[r][c]);
-                    if ((negbits[r] >> c) & 1u) yv = -yv;
+                    // y = sign(A) sqrt(|A|): v_sqrt_f32 (within 1 ulp), sign bit
+                    // inserted with one v_bfi_b32
+                    yv = __builtin_bit_cast(float, (fbits(__builtin_amdgcn_sqrtf(fabsf(A[r][c]))) & 0x7fffffffu) |
+                                                       (fbits(A[r][c]) & 0x80000000u));
                 }
                 u[r][c] = yv * ic[c];
             }
