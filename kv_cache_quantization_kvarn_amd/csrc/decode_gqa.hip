@@ -152,7 +152,7 @@ __device__ __forceinline__ void fp16_block(const DecodeArgs& a, const int f, con
     constexpr int NS = D / 64;
     constexpr int NC = D / 128;
     constexpr int TS = T / 64;
-    constexpr int WS = 2 * D + 4;
+    constexpr int WS = D + 4;           // partial: m, l, pad, pad, value sums
 
     const int lane = threadIdx.x;
     const int blk = lane >> 2, m = lane & 3;
@@ -286,11 +286,9 @@ __device__ __forceinline__ void fp16_block(const DecodeArgs& a, const int f, con
             o[0] = mx[g];
             o[1] = lt;
         }
-#pragma unroll
-        for (int sv = 0; sv < NS; sv++) o[4 + 64 * sv + lane] = 0.f;
         if (lane < LPT) {
 #pragma unroll
-            for (int c = 0; c < 8; c++) o[4 + D + 8 * lane + c] = accp[c][g];
+            for (int c = 0; c < 8; c++) o[4 + 8 * lane + c] = accp[c][g];
         }
     }
 }
@@ -308,8 +306,7 @@ __global__ void __launch_bounds__(64) decode_split_kernel(DecodeArgs a) {
     constexpr int KROW = D * KB / 8;      // code bytes of one token
     constexpr int KCH = 128 * KB / 8;     // code bytes of a 128-channel chunk
     constexpr int VROW = T * VB / 8;      // code bytes of one channel
-    constexpr int CPL = D / 64;           // fp16 values: channels per lane
-    constexpr int WS = 2 * D + 4;
+    constexpr int WS = D + 4;           // partial: m, l, pad, pad, value sums
     constexpr float FK = (float)(1 << KB), FV = (float)(1 << VB);
     static_assert(KCH % 16 == 0 && VROW % 16 == 0, "16-byte code segments");
 
@@ -576,8 +573,6 @@ __global__ void __launch_bounds__(64) decode_split_kernel(DecodeArgs a) {
         }
 #pragma unroll
         for (int sv = 0; sv < NS; sv++) o[4 + 64 * sv + lane] = accr[sv][g];
-#pragma unroll
-        for (int c = 0; c < CPL; c++) o[4 + D + CPL * lane + c] = 0.f;  // fp16 pages: their own kernel
     }
 }
 
@@ -774,7 +769,7 @@ __global__ void __launch_bounds__(64) decode_split128_kernel(DecodeArgs a) {
     constexpr int KW = KROW / 8;          // words of half a token row (64 channels)
     constexpr int VROW = T * VB / 8;      // code bytes of a channel (whole page)
     constexpr int VW = VB;                // words of 32 tokens of a channel
-    constexpr int WS = 2 * D + 4;
+    constexpr int WS = D + 4;           // partial: m, l, pad, pad, value sums
     constexpr int QROW = D, WROW = 64;    // bytes per row of the query / weight digit tables
     static_assert(KW == KB * 2 && (KROW / 2) % 16 == 0, "half token rows in 16-byte loads");
 
@@ -819,16 +814,59 @@ __global__ void __launch_bounds__(64) decode_split128_kernel(DecodeArgs a) {
     // i.e. channels 16 (q >> 1) + perm16<KB>(4 u + k)
     const int bg = lane & 3, bq = lane >> 2;
     auto bchan = [&](int i, int k) { return 16 * (bq >> 1) + perm16<KB>(4 * (2 * (bq & 1) + i) + k); };
+    // q' = H q / sqrt(D) of the wave's 4 heads, rotated here: lane (g = lane
+    // >> 4, m = lane & 15) holds channels 8 m .. 8 m + 7 of head h G + g;
+    // channel bits 0-2 are butterflies in registers, bits 3-6 (lane bits 0-3)
+    // across lanes; the result goes through the (still idle) LDS stage to the
+    // builder lanes.
     float qv[2][4];
     {
-        const float* qr = a.ws + ((int64_t)b * Hq + h * G + bg) * D;
+        const int g = lane >> 4, m = lane & 15;
+        const int64_t qrow = ((int64_t)b * Hq + h * G + g) * D + 8 * m;
+        float x[8];
+        if (a.q_bf16) {  // uniform
+            const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) + qrow);
+            const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+            for (int k = 0; k < 4; k++) {
+                x[2 * k] = __builtin_bit_cast(float, w[k] << 16);
+                x[2 * k + 1] = __builtin_bit_cast(float, w[k] & 0xffff0000u);
+            }
+        } else {
+            const float4 u0 = *reinterpret_cast<const float4*>(static_cast<const float*>(a.q) + qrow);
+            const float4 u1 = *reinterpret_cast<const float4*>(static_cast<const float*>(a.q) + qrow + 4);
+            x[0] = u0.x; x[1] = u0.y; x[2] = u0.z; x[3] = u0.w; x[4] = u1.x; x[5] = u1.y; x[6] = u1.z; x[7] = u1.w;
+        }
+#pragma unroll
+        for (int hs = 1; hs < 8; hs <<= 1)
+#pragma unroll
+            for (int e = 0; e < 8; e++)
+                if ((e & hs) == 0) {
+                    const float u = x[e], v = x[e + hs];
+                    x[e] = u + v;
+                    x[e + hs] = u - v;
+                }
+        // lane bit k: the lane with the bit set keeps partner - self, the other self + partner
+        auto xstage = [&](auto bitc) {
+            constexpr int BIT = decltype(bitc)::value;
+            const float sg = ((lane >> BIT) & 1) ? -1.f : 1.f;
+#pragma unroll
+            for (int e = 0; e < 8; e++) x[e] = fmaf(sg, x[e], xor_lane<BIT>(x[e]));
+        };
+        xstage(std::integral_constant<int, 0>{});
+        xstage(std::integral_constant<int, 1>{});
+        xstage(std::integral_constant<int, 2>{});
+        xstage(std::integral_constant<int, 3>{});
+        float* qs = reinterpret_cast<float*>(stage);  // [4 heads][D]
+        const float rs = 1.0f / sqrtf((float)D);
+        *reinterpret_cast<float4*>(qs + g * D + 8 * m) = make_float4(x[0] * rs, x[1] * rs, x[2] * rs, x[3] * rs);
+        *reinterpret_cast<float4*>(qs + g * D + 8 * m + 4) = make_float4(x[4] * rs, x[5] * rs, x[6] * rs, x[7] * rs);
+        wave_sync();
 #pragma unroll
         for (int i = 0; i < 2; i++)
 #pragma unroll
-            for (int k = 0; k < 4; k++) {
-                qv[i][k] = qr[bchan(i, k)];
-                asm volatile("" ::"v"(qv[i][k]));  // loaded before any LDS-DMA load is in flight
-            }
+            for (int k = 0; k < 4; k++) qv[i][k] = qs[bg * D + bchan(i, k)];
+        wave_sync();  // the stage is reused by the loads below
     }
 
     // sequence length and page ids are wave-uniform (SGPRs)
@@ -1092,8 +1130,6 @@ __global__ void __launch_bounds__(64) decode_split128_kernel(DecodeArgs a) {
         }
         o[4 + lane] = accr[0][g];
         o[4 + 64 + lane] = accr[1][g];
-        o[4 + D + 2 * lane] = 0.f;  // fp16 pages: their own kernel
-        o[4 + D + 2 * lane + 1] = 0.f;
     }
 }
 
@@ -1120,12 +1156,14 @@ __global__ void __launch_bounds__(D / 2) qrot_kernel(const void* __restrict__ q,
     for (int j = k; j < D; j += D / 2) qr[(int64_t)bh * D + j] = x[j] * rs;
 }
 
-// One workgroup per (sequence, query head): merge the splits, rotate the
-// record part back once, add the fp16 part, normalize.
+// One workgroup per (sequence, query head): merge the partials (the first
+// nq of them are quantized-page splits with rotated-basis value sums, the
+// rest fp16 slots with original-basis ones), rotate the record part back
+// once, add the fp16 part, normalize.
 template <int D>
 __global__ void __launch_bounds__(D) decode_combine_kernel(const float* __restrict__ ws, float* __restrict__ out,
-                                                            int nsplit) {
-    constexpr int WS = 2 * D + 4;
+                                                            int nq, int nsplit) {
+    constexpr int WS = D + 4;           // partial: m, l, pad, pad, value sums
     __shared__ float x[D];
     const int bh = blockIdx.x;
     const int j = threadIdx.x;
@@ -1136,12 +1174,18 @@ __global__ void __launch_bounds__(D) decode_combine_kernel(const float* __restri
     float Ls = 0.f, r = 0.f, pl = 0.f;
     if (M != -INFINITY) {
 #pragma unroll 8
-        for (int s = 0; s < nsplit; s++) {
+        for (int s = 0; s < nq; s++) {
             const float ms = base[s * WS];
             const float e = ms == -INFINITY ? 0.f : exp2f(ms - M);  // empty splits hold zeros
             Ls = fmaf(base[s * WS + 1], e, Ls);
             r = fmaf(base[s * WS + 4 + j], e, r);
-            pl = fmaf(base[s * WS + 4 + D + j], e, pl);
+        }
+#pragma unroll 8
+        for (int s = nq; s < nsplit; s++) {
+            const float ms = base[s * WS];
+            const float e = ms == -INFINITY ? 0.f : exp2f(ms - M);
+            Ls = fmaf(base[s * WS + 1], e, Ls);
+            pl = fmaf(base[s * WS + 4 + j], e, pl);
         }
     }
     x[j] = r;
@@ -1159,9 +1203,12 @@ __global__ void __launch_bounds__(D) decode_combine_kernel(const float* __restri
 
 template <int D, int T, int KB, int VB>
 hipError_t launch_gqa(const DecodeArgs& a, hipStream_t st) {
-    hipLaunchKernelGGL((qrot_kernel<D>), dim3(a.B * a.Hq), dim3(D / 2), 0, st, a.q, a.q_bf16, a.ws);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    hipError_t e;
+    if constexpr (D != 128) {  // the head_dim 128 split kernel rotates its queries itself
+        hipLaunchKernelGGL((qrot_kernel<D>), dim3(a.B * a.Hq), dim3(D / 2), 0, st, a.q, a.q_bf16, a.ws);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     // one launch: the quantized-page splits (z < B), then the fp16 page slots
     const dim3 grid(a.nsplit > a.nfsplit ? a.nsplit : a.nfsplit, a.H, a.nfsplit > 0 ? 2 * a.B : a.B);
     if constexpr (D == 128)
@@ -1171,7 +1218,7 @@ hipError_t launch_gqa(const DecodeArgs& a, hipStream_t st) {
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(a.B * a.Hq), dim3(D), 0, st,
-                       a.ws + (int64_t)a.B * a.Hq * D, a.out, a.nsplit + a.nfsplit);
+                       a.ws + (int64_t)a.B * a.Hq * D, a.out, a.nsplit, a.nsplit + a.nfsplit);
     return hipGetLastError();
 }
 
@@ -1224,9 +1271,10 @@ int decode_fp16_slots(int T, int sink, int tail, int max_pages) {
 }
 
 // fp32 rotated queries [B][Hq][D], then split partials
-// [B][Hq][nsplit + nfsplit][2D + 4] (quantized-page splits, then fp16 slots)
+// [B][Hq][nsplit + nfsplit][D + 4] (quantized-page splits with rotated-basis
+// value sums, then fp16 slots with original-basis ones)
 size_t decode_workspace_floats(int D, int Hq, int B, int nsplit, int nfsplit) {
-    return (size_t)B * Hq * D + (size_t)B * Hq * (nsplit + nfsplit) * (2 * D + 4);
+    return (size_t)B * Hq * D + (size_t)B * Hq * (nsplit + nfsplit) * (D + 4);
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
