@@ -328,7 +328,7 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ tile,
     constexpr int CODE_BYTES = T * D * BITS / 8;
     constexpr int REC = CODE_BYTES + 4 * T + 2 * D;
     constexpr int NPART = (RGB >= 2) ? 4 : 8;          // column partials per lane after swaps
-    constexpr bool KEEP_Y = D <= 256;                  // D = 512 keeps y |y| and rebuilds y from it
+    constexpr bool KEEP_Y = D <= 128;                  // D = 256, 512 keep y |y| and rebuild y from it
     static_assert(T * D / 64 == NT, "one lane per 64 values");
     static_assert(REC % 16 == 0, "records stay 16-byte aligned");
 
@@ -678,7 +678,7 @@ template <int D, int T, int KB, int VB, bool HASV>
 // D = 128: three waves per SIMD (168 VGPRs; the rotation's MFMA accumulators
 // and the rows it fills peak there); a D = 512 workgroup is itself four
 // waves per SIMD
-__global__ void __launch_bounds__(T * D / 64, D == 128 ? 3 : D == 256 ? 2 : 4)
+__global__ void __launch_bounds__(T * D / 64, D == 128 ? 3 : 4)
 quantize_kernel(const uint16_t* __restrict__ kpool, const uint16_t* __restrict__ vpool,
                 uint8_t* __restrict__ krec, uint8_t* __restrict__ vrec, const int32_t* __restrict__ src,
                 const int32_t* __restrict__ dst, int32_t H, int64_t n_fpages, int64_t n_qpages, int32_t n_iters) {
