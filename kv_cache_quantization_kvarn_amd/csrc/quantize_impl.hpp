@@ -331,6 +331,7 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ tile,
     constexpr bool KEEP_Y = D <= 128;                  // D = 256, 512 keep y |y| and rebuild y from it
     static_assert(T * D / 64 == NT, "one lane per 64 values");
     static_assert(REC % 16 == 0, "records stay 16-byte aligned");
+    static_assert(CODE_BYTES + 4 * (D / 16) <= S::SMEM_CODES, "the code image and its channel-row pad fit");
 
     float* colpart = reinterpret_cast<float*>(smem + S::PART_OFF);
     float* bvec = vec;           // b_j = exp(-2 lc_j), unnormalized basis
@@ -604,7 +605,11 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ tile,
             }
         }
     } else {
-        // channel-major: this lane's 4 tokens of a channel are contiguous
+        // channel-major: this lane's 4 tokens of a channel are contiguous.
+        // Channel c's row of the image starts at cm_off(c): 4 bytes of pad
+        // after every 16 channels put the rows of the D/16 lanes that store
+        // the same code position of their channels on different banks.
+        auto cm_off = [](int c) { return c * (T * BITS / 8) + 4 * (c >> 4); };
         if constexpr (BITS == 2) {
             // byte of channel c = its 4 codes, token-ascending, 2 bits each
 #pragma unroll
@@ -614,7 +619,7 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ tile,
                 for (int r = 0; r < QR; r++) p[r] = pk4(u[r][4 * c4], u[r][4 * c4 + 1], u[r][4 * c4 + 2], u[r][4 * c4 + 3]);
                 const uint32_t v = p[0] | (p[1] << 2) | (p[2] << 4) | (p[3] << 6);  // byte k: channel 4 c4 + k
 #pragma unroll
-                for (int k = 0; k < 4; k++) img[((ch0 + 4 * c4 + k) * T + row0) / 4] = (uint8_t)(v >> (8 * k));
+                for (int k = 0; k < 4; k++) img[cm_off(ch0 + 4 * c4 + k) + row0 / 4] = (uint8_t)(v >> (8 * k));
             }
         } else if constexpr (BITS == 4) {
             // 16 bits of channel c: (c_t0 | c_t1 << 4) then (c_t2 | c_t3 << 4)
@@ -626,18 +631,17 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ tile,
                 const uint32_t lo = p[0] | (p[1] << 4), hi = p[2] | (p[3] << 4);
                 const uint32_t w01 = __builtin_amdgcn_perm(hi, lo, 0x05010400u);  // channels 0, 1
                 const uint32_t w23 = __builtin_amdgcn_perm(hi, lo, 0x07030602u);  // channels 2, 3
-                const int e0 = (ch0 + 4 * c4) * T + row0;
-                *reinterpret_cast<uint16_t*>(img + e0 / 2) = (uint16_t)w01;
-                *reinterpret_cast<uint16_t*>(img + (e0 + T) / 2) = (uint16_t)(w01 >> 16);
-                *reinterpret_cast<uint16_t*>(img + (e0 + 2 * T) / 2) = (uint16_t)w23;
-                *reinterpret_cast<uint16_t*>(img + (e0 + 3 * T) / 2) = (uint16_t)(w23 >> 16);
+                const int c0 = ch0 + 4 * c4;
+                *reinterpret_cast<uint16_t*>(img + cm_off(c0) + row0 / 2) = (uint16_t)w01;
+                *reinterpret_cast<uint16_t*>(img + cm_off(c0 + 1) + row0 / 2) = (uint16_t)(w01 >> 16);
+                *reinterpret_cast<uint16_t*>(img + cm_off(c0 + 2) + row0 / 2) = (uint16_t)w23;
+                *reinterpret_cast<uint16_t*>(img + cm_off(c0 + 3) + row0 / 2) = (uint16_t)(w23 >> 16);
             }
         } else {
 #pragma unroll
             for (int c = 0; c < QC; c++) {
-                const int e0 = (ch0 + c) * T + row0;  // element index of the first of 4 codes
                 const uint32_t v = pack6x4(fq(0, c), fq(1, c), fq(2, c), fq(3, c));
-                uint8_t* d8 = img + e0 * 6 / 8;
+                uint8_t* d8 = img + cm_off(ch0 + c) + row0 * 6 / 8;
                 d8[0] = (uint8_t)v;
                 d8[1] = (uint8_t)(v >> 8);
                 d8[2] = (uint8_t)(v >> 16);
@@ -664,9 +668,17 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ tile,
 #pragma unroll
         for (int k = 0; k < UNITS; k++) {
             const int u = tid + k * NT;
-            int pu = u;
-            if constexpr (!CHMAJOR && BITS == 4 && D == 128) pu = (u & ~3) | ((u ^ (u >> 4)) & 3);  // row t = u >> 2
-            dst4[u] = reinterpret_cast<const uint4*>(img)[pu];
+            if constexpr (CHMAJOR) {
+                // unit u lies in channel row 16 u / (T BITS / 8) (rows are 16-byte
+                // multiples), shifted by that row's pad: 4-byte aligned
+                static_assert((T * BITS / 8) % 16 == 0, "channel rows of whole 16-byte units");
+                const uint32_t* p = reinterpret_cast<const uint32_t*>(img + 16 * u + 4 * ((16 * u / (T * BITS / 8)) >> 4));
+                dst4[u] = make_uint4(p[0], p[1], p[2], p[3]);
+            } else {
+                int pu = u;
+                if constexpr (BITS == 4 && D == 128) pu = (u & ~3) | ((u ^ (u >> 4)) & 3);  // row t = u >> 2
+                dst4[u] = reinterpret_cast<const uint4*>(img)[pu];
+            }
         }
     }
 }
