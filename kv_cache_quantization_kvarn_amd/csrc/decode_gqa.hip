@@ -294,7 +294,7 @@ __device__ __forceinline__ void fp16_block(const DecodeArgs& a, const int f, con
 }
 
 template <int D, int T, int KB, int VB>
-__global__ void __launch_bounds__(64) decode_split_kernel(DecodeArgs a) {
+__global__ void __launch_bounds__(64, 2) decode_split_kernel(DecodeArgs a) {
     constexpr int G = 4;
     constexpr int NS = D / 64;            // operand slots per lane; value channel sets
     constexpr int NC = D / 128;           // 128-channel chunks of a key row
@@ -1241,12 +1241,13 @@ hipError_t gqa_bits(const DecodeArgs& a, hipStream_t st) {
 
 void decode_plan(int D, int H, int G, int mla, int B, int max_pages, int T, int kb, int vb, int* nsplit,
                  int* pps) {
-    (void)D; (void)G; (void)T; (void)kb; (void)vb;
-    // GQA: one-wave workgroups, about 12 per CU.  MLA: one 4-wave workgroup
-    // per CU holds 64 heads (its accumulators fill the register file), so up
-    // to 128 heads take two workgroups per split.
+    (void)G; (void)T; (void)kb; (void)vb;
+    // GQA: one-wave workgroups, as many as fit at once: three per SIMD for
+    // head_dim 128 (128 VGPRs, but the fp16 slots take the fourth), two for
+    // 256/512 (256 VGPRs).  MLA: one 8-wave workgroup per CU holds 64 heads,
+    // so up to 128 heads take two workgroups per split.
     const int units = mla ? B * ((G + 63) / 64) : B * H;
-    const int target = mla ? 256 : 3072;
+    const int target = mla ? 256 : (D == 128 ? 3072 : 2048);
     int ns = (target + units - 1) / units;
     if (ns < 1) ns = 1;
     // MLA: a split holds its page ids in two registers, 128 at most (with the
