@@ -198,6 +198,12 @@ kvarn_status kvarn_decode_attn(const kvarn_layout* layout, const kvarn_cache* ca
         if (kb >= (1ull << 32) || vb >= (1ull << 32))
             return fail(KVARN_EUNSUPPORTED, "%s: record pools of %llu / %llu bytes; below 4 GiB each is implemented",
                         layout->mla ? "mla" : "head_dim 128", (unsigned long long)kb, (unsigned long long)vb);
+        // the MLA kernel also streams its fp16 pool through 32-bit offsets
+        const uint64_t fb = (uint64_t)cache->n_fpages * (uint64_t)H * (uint64_t)layout->tile_tokens *
+                            (uint64_t)layout->head_dim * 2u;
+        if (layout->mla && fb >= (1ull << 32))
+            return fail(KVARN_EUNSUPPORTED, "mla: an fp16 pool of %llu bytes; below 4 GiB is implemented",
+                        (unsigned long long)fb);
     }
     int ns = 1, pps = 1;
     kvarn::decode_plan(layout->head_dim, H, G, layout->mla, pages->batch, pages->max_pages, layout->tile_tokens,

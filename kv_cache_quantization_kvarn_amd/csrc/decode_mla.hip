@@ -464,54 +464,83 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no load may land in LDS after this point
     __syncthreads();
 
-    // ---- fp16 chunks: y_t = H x_t / sqrt(512), Y^T = H X^T on the MFMA, the B
-    // operand read straight from the fp16 page (8 channels of one token per
-    // lane).  Wave w writes channel blocks MBW*w .. of both 16-token halves. ----
-    int fpar = nqc & 1;  // chunk parity continues from the quantized chunks
-    for (int j = 0; j < nfp; j++) {
+    // ---- fp16 chunks: y_t = H x_t / sqrt(512), Y^T = H X^T on the MFMA.  The
+    // 32 KB of a chunk (token rows of 1 KB) come through two LDS buffers in
+    // the (now idle) ring by LDS-DMA loads one chunk ahead, 16-byte piece p of
+    // token t at piece p ^ (t & 7) of its row so that 8 lanes reading one
+    // piece of 8 tokens hit 8 bank groups; the B operand is 8 channels of one
+    // token per lane.  Wave w writes channel blocks MBW*w .. of both 16-token
+    // halves. ----
+    static_assert(2 * CH * MD * 2 <= NR * SLOT, "two fp16 chunks fit the ring");
+    const i32x4 rf = raw_buffer(a.k_fp16, (uint32_t)(a.n_fpages * T * MD * 2));
+    auto fchunks = [&](int j) {  // chunks holding tokens of the split's j-th fp16 page (0: none or a bad id)
         const int page = fpage(j);
-        int id = page_id(nqp + j);
-        if (id < 0 || (int64_t)id >= a.n_fpages) continue;  // uniform
-        const int nck = (min(L - page * T, T) + CH - 1) / CH;  // chunks holding tokens
-        for (int cc = 0; cc < nck; cc++) {
-            const int c0 = cc * CH;
+        const int id = page_id(nqp + j);
+        if (id < 0 || (int64_t)id >= a.n_fpages) return 0;
+        return (min(L - page * T, T) + CH - 1) / CH;
+    };
+    struct FChunk {
+        int j, cc;
+    };
+    auto fnext = [&](FChunk f) {  // the split's next fp16 chunk (j == nfp: none)
+        f.cc++;
+        while (f.j < nfp && f.cc >= fchunks(f.j)) {
+            f.j++;
+            f.cc = 0;
+        }
+        return f;
+    };
+    auto issue_f = [&](FChunk f, int buf) {
+        if (f.j >= nfp) return;
+        const int id = page_id(nqp + f.j);
+        const int base = (id * T + f.cc * CH) * (MD * 2);
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int t = 4 * wave + i;  // token of the chunk
+            lds_dma16(ring_lds + buf * (CH * MD * 2) + 1024 * t, rf, 1024 * t + 16 * (lane ^ (t & 7)), base);
+        }
+    };
+    int fpar = nqc & 1;  // chunk parity continues from the quantized chunks
+    FChunk fc = fnext(FChunk{0, -1});
+    int fb = 0;
+    issue_f(fc, 0);
+    while (fc.j < nfp) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this chunk has landed
+        __syncthreads();
+        const FChunk fn = fnext(fc);
+        issue_f(fn, fb ^ 1);  // the other buffer's last reader finished before the barrier above
+        const int page = fpage(fc.j);
+        const int c0 = fc.cc * CH;
+        {
             constexpr int MBW = 32 / NWV;
             uint8_t* yb = ybuf[fpar];
-            const uint16_t* fp = static_cast<const uint16_t*>(a.k_fp16) + ((int64_t)id * T + c0) * MD;
+            const uint8_t* xb = ring + fb * (CH * MD * 2);
             const float rsq = 1.0f / sqrtf((float)MD);
 #pragma unroll
             for (int th = 0; th < 2; th++) {
                 f4 z[MBW];
 #pragma unroll
                 for (int m = 0; m < MBW; m++) z[m] = f4{0.f, 0.f, 0.f, 0.f};
-                // the half's operand loads are issued four at a time before their MFMAs
+                const int t = 16 * th + l16;
 #pragma unroll
-                for (int k8 = 0; k8 < 4; k8++) {
-                    h8 bxs[4];
+                for (int ks = 0; ks < 16; ks++) {
+                    h8 bx = *reinterpret_cast<const h8*>(xb + 1024 * t + 16 * ((4 * ks + g4) ^ (t & 7)));
+                    // sign(mb, ks) = (-1)^popcount(((MBW/2)*wave) & ks) * (-1)^popcount((m >> 1) & ks):
+                    // the wave part negates the B operand, the m part picks the pattern
+                    if (__builtin_popcount((unsigned)((MBW / 2) * wave) & (unsigned)ks) & 1) bx = -bx;
 #pragma unroll
-                    for (int kk = 0; kk < 4; kk++)
-                        bxs[kk] = *reinterpret_cast<const h8*>(fp + (16 * th + l16) * MD + 32 * (4 * k8 + kk) + 8 * g4);
-#pragma unroll
-                    for (int kk = 0; kk < 4; kk++) {
-                        const int ks = 4 * k8 + kk;
-                        h8 bx = bxs[kk];
-                        // sign(mb, ks) = (-1)^popcount(((MBW/2)*wave) & ks) * (-1)^popcount((m >> 1) & ks):
-                        // the wave part negates the B operand, the m part picks the pattern
-                        if (__builtin_popcount((unsigned)((MBW / 2) * wave) & (unsigned)ks) & 1) bx = -bx;
-#pragma unroll
-                        for (int m = 0; m < MBW; m++) {
-                            const h8 av = hpat[m & 1][__builtin_popcount((unsigned)((m >> 1) & ks)) & 1][lane];
-                            z[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bx, z[m], 0, 0, 0);
-                        }
+                    for (int m = 0; m < MBW; m++) {
+                        const h8 av = hpat[m & 1][__builtin_popcount((unsigned)((m >> 1) & ks)) & 1][lane];
+                        z[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bx, z[m], 0, 0, 0);
                     }
                 }
                 // lane: channels 16*mb + 4*g4 .. +3 of token 16*th + l16; tokens past the
                 // sequence end are zeroed (their weight is 0 and must not meet NaN)
-                const bool tv = page * T + c0 + 16 * th + l16 < L;
+                const bool tv = page * T + c0 + t < L;
 #pragma unroll
                 for (int m = 0; m < MBW; m++) {
                     // channel 4*(g4&1) + i of unit 2*mb + (g4>>1) sits at position 2*i + (g4&1)
-                    uint8_t* dst = yb + yoff(16 * th + l16, 2 * (MBW * wave + m) + (g4 >> 1)) + 2 * (g4 & 1);
+                    uint8_t* dst = yb + yoff(t, 2 * (MBW * wave + m) + (g4 >> 1)) + 2 * (g4 & 1);
 #pragma unroll
                     for (int i = 0; i < 4; i++)
                         *reinterpret_cast<uint16_t*>(dst + 4 * i) = tv ? (uint16_t)float_to_half_bits(z[m][i] * rsq) : (uint16_t)0;
@@ -521,8 +550,10 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
             if (qk_wave) score(yb, page * T + c0, fpar);
             __syncthreads();
             accumulate(yb, fpar);
-            fpar ^= 1;
         }
+        fpar ^= 1;
+        fb ^= 1;
+        fc = fn;
     }
 
     // ---- partial results: m, l per head; O rows for this wave's channels ----
