@@ -24,7 +24,7 @@ FLAGS = [
 EXTRA = {"quantize_d128.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee",
                               # the rotation's MFMA accumulators stay in ordinary VGPRs
                               "-mllvm", "-amdgpu-mfma-vgpr-form=1"],
-         "quantize_d256.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"],
+         "quantize_d256.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee", "-mllvm", "-amdgpu-mfma-vgpr-form=1"],
          "quantize_d512.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"],
          "decode_gqa.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee", "-mllvm", "-amdgpu-mfma-vgpr-form=1"],
          "decode_mla.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee",

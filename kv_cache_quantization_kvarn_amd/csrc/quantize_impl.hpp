@@ -14,8 +14,9 @@
 // (DPP patterns: quad_perm and row_ror:8), then 2 and 4 (ds_swizzle).  The
 // remaining lane bits (of 2, 4, 5) and the wave index carry the row group.
 //
-// The rotation is the unnormalized +-1 butterfly (4 in-lane stages, then one
-// cross-lane stage per channel-group bit).  Statistics use the squared tile
+// The rotation is the unnormalized +-1 Hadamard product: on the fp16 MFMA
+// for D = 128 and 256; for D = 512 as butterflies (4 in-lane stages, then
+// one cross-lane stage per channel-group bit).  Statistics use the squared tile
 // A = y^2; with a_i = exp(-2 lr_i) and b_j = exp(-2 lc_j), the column step
 // is b_j = T / sum_i A_ij a_i and the row step a_i = D / sum_j A_ij b_j --
 // the log-space updates "lc_j += ln sigma_j", "lr_i += ln sigma_i" with the
@@ -164,12 +165,19 @@ __device__ __forceinline__ uint32_t pack6x4(uint32_t f0, uint32_t f1, uint32_t f
     return (x23 << 12) | x01;              // junk shifted out
 }
 
-// D = 128: the rotation runs on the 16x16x32 fp16 MFMA (y = X H with the
-// fp16 tile as the A operand and +-1 blocks of H as the B operand), each wave
-// on its own 32 rows, and reaches the register layout through LDS.
+// D = 128, 256: the rotation runs on the 16x16x32 fp16 MFMA (y = X H with
+// the fp16 tile as the A operand and +-1 blocks of H as the B operand) and
+// reaches the register layout through LDS; D = 128 with each wave on its own
+// 32 rows, D = 256 on its own 16 rows.  D = 512 (one 16-wave workgroup per
+// CU, 8 rows per wave) keeps the butterflies: the MFMA form needs two waves
+// per 16-row block and workgroup barriers, which measured slower there.  The
+// sign-tracked cross-lane butterflies leave channel j multiplied by
+// (-1)^popcount(j >> 4), undone with the column scales.
 template <int D>
 struct MfmaRotation {
-    static constexpr bool on = D == 128;
+    static constexpr bool narrow = D == 128;
+    static constexpr bool wide = D == 256;
+    static constexpr unsigned XMASK = (narrow || wide) ? 0u : (unsigned)(D / 16 - 1);  // bits of j >> 4
 };
 
 // B operands of the rotation.  H_128 = H_4 (x) H_32 over channel j = 32 v + u
@@ -203,6 +211,30 @@ constexpr RotOperands make_rot_operands() {
 }
 __device__ const RotOperands kRotOperands = make_rot_operands();
 
+// B operands of the wide rotation: column n of half nh is channel
+// 16 (n >> 3) + 8 nh + (n & 7) of the 32-channel group, so that an output
+// block holds channels 8 nh .. 8 nh + 7 of two 16-channel blocks.  Entry
+// [nh + 2 s][l] is lane l's operand times (-1)^s.
+constexpr RotOperands make_rot_operands_split() {
+    RotOperands t{};
+    for (int sn = 0; sn < 4; sn++) {
+        const int nh = sn & 1, neg = sn >> 1;
+        for (int l = 0; l < 64; l++) {
+            const int n = l & 15, col = 16 * (n >> 3) + 8 * nh + (n & 7);
+            for (int k = 0; k < 4; k++) {
+                uint32_t d = 0x3C003C00u;
+                for (int half = 0; half < 2; half++) {
+                    const int row = 8 * (l >> 4) + 2 * k + half;
+                    if ((__builtin_popcount((unsigned)(row & col)) + neg) & 1) d |= 0x8000u << (16 * half);
+                }
+                t.w[sn][l][k] = d;
+            }
+        }
+    }
+    return t;
+}
+__device__ const RotOperands kRotOperandsSplit = make_rot_operands_split();
+
 template <int D, int T>
 struct TileShape {
     static constexpr int LPR = D / QC;                        // lanes per token row
@@ -214,12 +246,15 @@ struct TileShape {
     static constexpr int NSUB = (RGB == 3) ? 2 : 1;           // lane bit 2 left after the swaps
     static constexpr int SMEM_CODES = T * D;                  // one byte per code at most
     static constexpr int SMEM_PART = NW * NSUB * D * 4;
-    static constexpr int SMEM_ROT = MfmaRotation<D>::on ? T * D * 2 : 0;  // half the rotated tile, fp32
+    // rotation image: D = 128 half the rotated tile (fp32); D = 256 half of
+    // each wave's 16 x 256 block (fp32), 8 KB per wave
+    static constexpr int SMEM_ROT = MfmaRotation<D>::narrow ? T * D * 2 : MfmaRotation<D>::wide ? NW * 8192 : 0;
     static constexpr int SMEM_A = SMEM_CODES > SMEM_PART ? SMEM_CODES : SMEM_PART;
-    // with the MFMA rotation the column partials get their own region after
-    // the tile image, so the statistics need not wait for the image to die
-    static constexpr int PART_OFF = MfmaRotation<D>::on ? (SMEM_ROT > SMEM_CODES ? SMEM_ROT : SMEM_CODES) : 0;
-    static constexpr int SMEM = MfmaRotation<D>::on ? PART_OFF + SMEM_PART : (SMEM_A > SMEM_ROT ? SMEM_A : SMEM_ROT);
+    // D = 128: the column partials get their own region after the rotation
+    // image, so the statistics need not wait for every wave's image to die;
+    // D = 256 ends the rotation with a workgroup barrier and reuses it
+    static constexpr int PART_OFF = MfmaRotation<D>::narrow ? (SMEM_ROT > SMEM_CODES ? SMEM_ROT : SMEM_CODES) : 0;
+    static constexpr int SMEM = MfmaRotation<D>::narrow ? PART_OFF + SMEM_PART : (SMEM_A > SMEM_ROT ? SMEM_A : SMEM_ROT);
 };
 
 // LDS position of channel ch in a slot of column partials: 4-float chunks xor-permuted inside each 8-chunk (32-float) window
@@ -307,6 +342,84 @@ __device__ __forceinline__ void mfma_rotate(const uint16_t* __restrict__ tile, u
     }
 }
 
+// D = 256: y = X H_256 for this lane's 4 rows x 16 channels (MFMA, then
+// LDS; the wave's own 8 KB of smem).  H_256 = H_8 (x) H_32: output group og
+// (32 channels) of the wave's 16 rows is sum_j X_j H_32 (-1)^popcount(j & og),
+// eight chained MFMAs per 16-column half.  Pass p moves channels 8 p ..
+// 8 p + 7 of every 16-channel block (the output blocks of B-operand half p)
+// through 16-byte units [row quad][16-channel block cb][c ^ ((cb >> 1) & 7)],
+// c = channel - 16 cb - 8 p: the MFMA-layout stores and the register-layout
+// loads of 16 lanes touch 16 different units modulo 16, and every lane loads
+// in both passes.
+template <int D, int T>
+__device__ __forceinline__ void mfma_rotate_wide(const uint16_t* __restrict__ tile, uint8_t* smem, int lane, int wave,
+                                                 int cg, int rg, float (&y)[QR][QC]) {
+    using S = TileShape<D, T>;
+    typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+    typedef float f4 __attribute__((ext_vector_type(4)));
+    static_assert(D == 256 && S::RPW == 16 && S::RGB == 2, "one wave per 16 rows x 256 channels");
+    constexpr int NCB = D / 16;           // 16-channel blocks
+    const int l16 = lane & 15, g4 = lane >> 4;
+    uint8_t* region = smem + wave * 8192;
+    h8 hb[4];
+#pragma unroll
+    for (int sn = 0; sn < 4; sn++)
+        hb[sn] = __builtin_bit_cast(h8, *reinterpret_cast<const uint4*>(kRotOperandsSplit.w[sn][lane]));
+    // A operands: row 16 wave + l16, input group j, channels 32 j + 8 g4 .. + 7
+    h8 xa[8];
+    {
+        const uint16_t* xr = tile + (int64_t)(16 * wave + l16) * D + 8 * g4;
+#pragma unroll
+        for (int j = 0; j < 8; j++) xa[j] = *reinterpret_cast<const h8*>(xr + 32 * j);
+    }
+    auto unit = [](int qq, int cb, int c) { return 16 * (qq * 8 * NCB + 8 * cb + (c ^ ((cb >> 1) & 7))); };
+    auto block = [&](int p, int og) -> f4 {
+        f4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            const int sn = p + 2 * (__builtin_popcount((unsigned)(j & og)) & 1);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[j], hb[sn], acc, 0, 0, 0);
+        }
+        return acc;
+    };
+    // output block (p, og): channel 32 og + 16 (l16 >> 3) + 8 p + (l16 & 7), rows 4 g4 .. 4 g4 + 3
+    auto store = [&](int og, f4 zv) {
+        *reinterpret_cast<f4*>(region + unit(g4, 2 * og + (l16 >> 3), l16 & 7)) = zv;
+    };
+    // this lane: rows 4 rg .. 4 rg + 3 (rg = g4), channels 16 cg + 8 p + c
+    auto load = [&](int p) {
+#pragma unroll
+        for (int c = 0; c < 8; c++) {
+            const f4 v = *reinterpret_cast<const f4*>(region + unit(rg, cg, c));
+#pragma unroll
+            for (int r = 0; r < QR; r++) y[r][8 * p + c] = v[r];
+        }
+    };
+    auto sync = []() {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
+    // pass 0's blocks go to LDS as they are formed, pass 1's wait in
+    // registers until pass 0 has been read back: y is born only after the
+    // MFMA operands have died
+#pragma unroll
+    for (int og = 0; og < 8; og++) store(og, block(0, og));
+    __builtin_amdgcn_sched_barrier(0);
+    f4 z1[8];
+#pragma unroll
+    for (int og = 0; og < 8; og++) z1[og] = block(1, og);
+    sync();
+    load(0);
+    sync();
+#pragma unroll
+    for (int og = 0; og < 8; og++) store(og, z1[og]);
+    sync();
+    load(1);
+    // the statistics reuse the shared buffer
+    __syncthreads();
+}
+
 // Position of channel ch in the b and sqrt(b) vectors: 4 pad floats after
 // every 32 channels, so that the 16-byte broadcast reads of channel groups
 // 16 cg .. 16 cg + 15 (cg = 0..3 within an 8-lane group) start in different
@@ -351,10 +464,12 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ tile,
     const int row0 = wave * RPW + rg * QR;
     const int ch0 = cg * QC;
 
+    if (tid < D) bvec[vec_pos(tid)] = 1.0f / (float)D;  // c_j = 1 in the normalized basis
     float y[QR][QC];
-    if constexpr (MfmaRotation<D>::on) {
+    if constexpr (MfmaRotation<D>::narrow) {
         mfma_rotate<D, T>(tile, smem, lane, wave, cg, rg, y);
-        if (tid < D) bvec[vec_pos(tid)] = 1.0f / (float)D;  // c_j = 1 in the normalized basis
+    } else if constexpr (MfmaRotation<D>::wide) {
+        mfma_rotate_wide<D, T>(tile, smem, lane, wave, cg, rg, y);
     } else {
         // ---- stage 1: load the fp16 tile ---------------------------------------
 #pragma unroll
@@ -368,7 +483,6 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ tile,
                 y[r][2 * k + 1] = half_bits_to_float(w[k] >> 16);
             }
         }
-        if (tid < D) bvec[vec_pos(tid)] = 1.0f / (float)D;  // c_j = 1 in the normalized basis
 
         // ---- stage 2: Hadamard rotation (unnormalized butterflies) -------------
 #pragma unroll
@@ -464,8 +578,9 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ tile,
             if (usable(s)) b = ((float)T / (float)D) * __builtin_amdgcn_rcpf(s);
             bvec[pt] = b;
             if (last) {
-                // channel sign left by the sign-tracked butterflies: (-1)^popcount(j >> 4)
-                const float sg = (!MfmaRotation<D>::on && (__builtin_popcount((unsigned)tid >> 4) & 1)) ? -1.f : 1.f;
+                // channel sign left by the sign-tracked cross-lane butterflies
+                const float sg = (__builtin_popcount(((unsigned)tid >> 4) & MfmaRotation<D>::XMASK) & 1)
+                                     ? -1.f : 1.f;
                 icvec[pt] = sg * sqrtf(b);
                 cvec[tid] = (uint16_t)float_to_half_bits(__builtin_amdgcn_rsqf((float)D * b));
             }
