@@ -16,10 +16,11 @@
 //
 // Workgroup: 8 waves (two per SIMD) per (head group of up to 64 heads,
 // split, sequence).  Scores: waves 0..3 own one head block (16 heads) each
-// while waves 4..7 read the next chunk back.  Value sums: each wave owns 64
-// of the 512 channels for all the group's heads; their operands come from LDS
-// through ds_read_b64_tr_b16 (4 rows x 16 columns of halves transposed per 16
-// lanes).
+// while waves 4..7 read the next chunk back; then every wave forms the value
+// sums of the previous chunk, so one barrier per chunk separates the stages.
+// Value sums: each wave owns 64 of the 512 channels for all the group's
+// heads; their operands come from LDS through ds_read_b64_tr_b16 (4 rows x 16
+// columns of halves transposed per 16 lanes).
 #include <math.h>
 
 #include "kvarn_device.hpp"
@@ -115,9 +116,9 @@ __global__ void __launch_bounds__(256) qrot_kernel(const void* __restrict__ q, i
 
 // Workgroup of 8 waves, two per SIMD.  Waves 0..3 ("score waves") own one
 // head block (16 heads) each: scores over a whole chunk, its softmax and its
-// weights.  Waves 4..7 read the next chunk back meanwhile.  All 8 waves then
-// form the value sums, wave w for channels CPW*w .. CPW*w + CPW - 1 of every
-// head.
+// weights.  Waves 4..7 read the next chunk back meanwhile.  All 8 waves form
+// the value sums of the chunk before, wave w for channels CPW*w .. CPW*w +
+// CPW - 1 of every head.
 template <int HB>
 struct MlaShape {
     static_assert(HB >= 1 && HB <= 4, "a workgroup holds at most 64 heads");
@@ -132,8 +133,10 @@ struct MlaShape {
 // contiguous ranges, and the fp16 pages (sink, then tail) are dealt to the
 // splits round-robin, so every split gets the same share of both kinds.
 // A split runs its quantized chunks first, software-pipelined (their loads
-// stream through an LDS ring; chunk c + 1 is read back while chunk c is
-// scored), then its fp16 chunks.
+// stream through an LDS ring; between two barriers chunk c + 1 is read back
+// and chunk c scored, and the value sums of chunk c - 1 are formed), then its
+// fp16 chunks.  Chunk s (the quantized ones, then the fp16 ones) uses read-back
+// buffer s mod 3 (quantized) or 0 (fp16), weight and rescale buffers s mod 2 and rescale flag s mod 3.
 template <int T, int HB>
 __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs a) {
     using SH = MlaShape<HB>;
@@ -143,14 +146,14 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
     constexpr int WS = MD + 4;                     // partial: m, l, pad, pad, O[512]
     constexpr int CPP = T / CH;                    // chunks per page
     static_assert(HQ * 2 <= 160, "weight rows hold at most 64 heads");
-    __shared__ __attribute__((aligned(16))) uint8_t ybuf[2][CH * YROW];  // chunks, rotated basis (fp16), by parity
-    __shared__ __attribute__((aligned(16))) uint8_t pbuf[PBYTES];         // weights [token][head] (fp16)
+    __shared__ __attribute__((aligned(16))) uint8_t ybuf[3][CH * YROW];  // chunks, rotated basis (fp16)
+    __shared__ __attribute__((aligned(16))) uint8_t pbuf[2][PBYTES];      // weights [token][head] (fp16)
     __shared__ __attribute__((aligned(16))) h8 hpat[2][2][64];
     __shared__ __attribute__((aligned(16))) uint4 cbuf[2][MD / 8];       // column scales by unit, by page parity
-    __shared__ float alpha[HQ];
-    __shared__ int rescale_flag[2];                                        // by chunk parity
+    __shared__ float alpha[2][HQ];
+    __shared__ int rescale_flag[3];
     // ring of chunk slots: codes, token scales (SSC), column scales (SCC)
-    constexpr int NR = 8;
+    constexpr int NR = 4;
     constexpr int SSC = CH * MD / 2, SCC = SSC + 4 * CH, SLOT = SCC + 2 * MD;
     static_assert(SSC == NWV * 1024, "one 1 KB code load per wave and chunk");
     __shared__ __attribute__((aligned(16))) uint8_t ring[NR * SLOT];
@@ -166,8 +169,10 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
     const int hg = (wid % (8 * nhg)) / 8;
     const int u = (wid / (8 * nhg)) * 8 + (wid % 8);
     if (u >= units) return;
-    const int b = u / a.nsplit, split = u - b * a.nsplit;
-    const int h0 = hg * HQ;  // first query head of this workgroup
+    // workgroup-uniform: held in scalar registers
+    const int b = __builtin_amdgcn_readfirstlane(u / a.nsplit);
+    const int split = __builtin_amdgcn_readfirstlane(u - b * a.nsplit);
+    const int h0 = __builtin_amdgcn_readfirstlane(hg * HQ);  // first query head of this workgroup
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, g4 = lane >> 4;
     const float sm2 = a.sm_scale * kLog2e;
@@ -201,7 +206,7 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
             hpat[od][1][lane] = -v;
         }
     }
-    if (tid < 2) rescale_flag[tid] = 0;
+    if (tid < 3) rescale_flag[tid] = 0;
 
     f4 O[HB][CBW];
 #pragma unroll
@@ -247,10 +252,11 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
     for (int ks = 0; ks < 16; ks++) asm volatile("" ::"v"(qa[ks]));
     __syncthreads();
 
-    // ---- score waves: scores, softmax and weights of the chunk in yb (32
-    // tokens from sequence position tok0; positions past the sequence end get
-    // weight 0).  Sets rescale_flag[par] when a running maximum moves. ----
-    auto score = [&](const uint8_t* yb, int tok0, int par) {
+    // ---- score waves: scores, softmax and weights of chunk seq, held in yb
+    // (32 tokens from sequence position tok0; positions past the sequence end
+    // get weight 0).  Sets rescale_flag[seq % 3] when a running maximum
+    // moves. ----
+    auto score = [&](const uint8_t* yb, int tok0, int seq) {
         // 32 k-steps (token half th = k >> 4, channels 32 (k & 15) ..), the B
         // operand loaded PF steps ahead; two accumulation chains per half
         constexpr int PF = 8;
@@ -292,9 +298,9 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
                 lp[i] *= al;
                 mu[i] = mn;
             }
-            if (l16 == 0) alpha[16 * wave + 4 * g4 + i] = al;
+            if (l16 == 0) alpha[seq & 1][16 * wave + 4 * g4 + i] = al;
         }
-        if (any && lane == 0) atomicOr(&rescale_flag[par], 1);
+        if (any && lane == 0) atomicOr(&rescale_flag[seq % 3], 1);
 #pragma unroll
         for (int th = 0; th < 2; th++) {
             float p[4];
@@ -305,23 +311,24 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
             }
             const uint2 pk = make_uint2(float_to_half_bits(p[0]) | (float_to_half_bits(p[1]) << 16),
                                         float_to_half_bits(p[2]) | (float_to_half_bits(p[3]) << 16));
-            *reinterpret_cast<uint2*>(pbuf + poff(16 * th + l16) + 32 * wave + 8 * g4) = pk;
+            *reinterpret_cast<uint2*>(pbuf[seq & 1] + poff(16 * th + l16) + 32 * wave + 8 * g4) = pk;
         }
     };
-    // ---- all waves: O += P Y for this wave's channels (after the weights of
-    // the chunk in yb are in pbuf); clears the other parity's flag ----
-    auto accumulate = [&](const uint8_t* yb, int par) {
-        if (rescale_flag[par]) {
+    // ---- all waves: O += P Y for this wave's channels, chunk seq held in yb
+    // (after its weights are in pbuf[seq & 1]); clears the flag of chunk
+    // seq + 2, which no wave reads or sets before the next barrier ----
+    auto accumulate = [&](const uint8_t* yb, int seq) {
+        if (rescale_flag[seq % 3]) {
 #pragma unroll
             for (int hb = 0; hb < HB; hb++)
 #pragma unroll
                 for (int i = 0; i < 4; i++) {
-                    const float al = alpha[16 * hb + 4 * g4 + i];
+                    const float al = alpha[seq & 1][16 * hb + 4 * g4 + i];
 #pragma unroll
                     for (int c = 0; c < CBW; c++) O[hb][c][i] *= al;
                 }
         }
-        if (tid == 0) rescale_flag[par ^ 1] = 0;  // last read before the previous barrier
+        if (tid == 0) rescale_flag[(seq + 2) % 3] = 0;
         // tr16: lane 4k + q of a 16-lane group reads row k, columns 4q .. 4q+3;
         // lane j receives column j of the 4 rows.  Rows are tokens.
         const int row = 8 * g4 + (l16 >> 2), q4 = l16 & 3;
@@ -334,7 +341,8 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
 #pragma unroll
         for (int hb = 0; hb < HB; hb++) {
             // P[16 heads][32 tokens]: lane head l16, tokens 8*g4 .. +7
-            const h8 pa = cat(tr16(pbuf + poff(row) + 32 * hb + 8 * q4), tr16(pbuf + poff(row + 4) + 32 * hb + 8 * q4));
+            const uint8_t* pb = pbuf[seq & 1];
+            const h8 pa = cat(tr16(pb + poff(row) + 32 * hb + 8 * q4), tr16(pb + poff(row + 4) + 32 * hb + 8 * q4));
 #pragma unroll
             for (int c = 0; c < CBW; c++) O[hb][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, bv[c], O[hb][c], 0, 0, 0);
         }
@@ -375,7 +383,7 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
             lds_dma16(dummy_lds, rs, 0, 0);
         }
     };
-    // read-back waves: chunk ci (landed) -> ybuf[ci & 1], rotated basis, fp16.
+    // read-back waves: chunk ci (landed) -> ybuf[ci % 3], rotated basis, fp16.
     // Lane l of read-back wave 4 + v takes token tt = 8 v + (l & 7), units
     // 8 part .. +8 (channels 64 part ..) with part = l >> 3: the 8 lanes of an
     // 8-lane group hold 8 tokens of one column.  The column scales of a page
@@ -387,7 +395,7 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
         qchunk(ci, page, c0, id);
         if (id < 0) return;
         const uint8_t* slot = ring + (ci % NR) * SLOT;
-        uint8_t* yb = ybuf[ci & 1];
+        uint8_t* yb = ybuf[ci % 3];
         uint4* cb = cbuf[page & 1];
         const uint4* cpg = reinterpret_cast<const uint4*>(slot + SCC);
         uint32_t cw[8];
@@ -445,33 +453,34 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
         __syncthreads();
     }
     // iteration ci: issue chunk ci + NR - 1 into the slot chunk ci - 1 used;
-    // score chunk ci while chunk ci + 1 is read back; then the value sums of ci
-    for (int ci = 0; ci < nqc; ci++) {
+    // score chunk ci while chunk ci + 1 is read back, then the value sums of
+    // chunk ci - 1 (iteration nqc only forms those of the last chunk)
+    for (int ci = 0; ci <= nqc; ci++) {
         issue_chunk(ci + NR - 1);
         asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * (NR - 2)) : "memory");  // chunk ci + 1 has landed
         __syncthreads();
-        const bool ok = chunk_ok(ci);
-        if (qk_wave && ok) {
-            int page, c0, id;
-            qchunk(ci, page, c0, id);
-            score(ybuf[ci & 1], page * T + c0, ci & 1);
-        } else if (rb_wave && ci + 1 < nqc) {
-            read_back(ci + 1);
+        if (ci < nqc) {
+            if (qk_wave) {
+                int page, c0, id;
+                qchunk(ci, page, c0, id);
+                if (id >= 0) score(ybuf[ci % 3], page * T + c0, ci);
+            } else if (rb_wave && ci + 1 < nqc) {
+                read_back(ci + 1);
+            }
         }
-        __syncthreads();
-        if (ok) accumulate(ybuf[ci & 1], ci & 1);
+        if (ci > 0 && chunk_ok(ci - 1)) accumulate(ybuf[(ci - 1) % 3], ci - 1);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no load may land in LDS after this point
     __syncthreads();
 
-    // ---- fp16 chunks: y_t = H x_t / sqrt(512), Y^T = H X^T on the MFMA.  The
-    // 32 KB of a chunk (token rows of 1 KB) come through two LDS buffers in
-    // the (now idle) ring by LDS-DMA loads one chunk ahead, 16-byte piece p of
+    // ---- fp16 chunks: y_t = H x_t / sqrt(512), Y^T = H X^T on the MFMA into
+    // ybuf[0].  The 32 KB of a chunk (token rows of 1 KB) come through ybuf[1]
+    // and ybuf[2] (idle now) by LDS-DMA loads one chunk ahead, 16-byte piece p of
     // token t at piece p ^ (t & 7) of its row so that 8 lanes reading one
     // piece of 8 tokens hit 8 bank groups; the B operand is 8 channels of one
     // token per lane.  Wave w writes channel blocks MBW*w .. of both 16-token
     // halves. ----
-    static_assert(2 * CH * MD * 2 <= NR * SLOT, "two fp16 chunks fit the ring");
+    static_assert(CH * MD * 2 <= CH * YROW, "an fp16 chunk fits a read-back buffer");
     const i32x4 rf = raw_buffer(a.k_fp16, (uint32_t)(a.n_fpages * T * MD * 2));
     auto fchunks = [&](int j) {  // chunks holding tokens of the split's j-th fp16 page (0: none or a bad id)
         const int page = fpage(j);
@@ -497,10 +506,10 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
 #pragma unroll
         for (int i = 0; i < 4; i++) {
             const int t = 4 * wave + i;  // token of the chunk
-            lds_dma16(ring_lds + buf * (CH * MD * 2) + 1024 * t, rf, 1024 * t + 16 * (lane ^ (t & 7)), base);
+            lds_dma16(lds_address(ybuf[1 + buf]) + 1024 * t, rf, 1024 * t + 16 * (lane ^ (t & 7)), base);
         }
     };
-    int fpar = nqc & 1;  // chunk parity continues from the quantized chunks
+    int fseq = nqc;  // chunk numbering continues from the quantized chunks
     FChunk fc = fnext(FChunk{0, -1});
     int fb = 0;
     issue_f(fc, 0);
@@ -513,8 +522,8 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
         const int c0 = fc.cc * CH;
         {
             constexpr int MBW = 32 / NWV;
-            uint8_t* yb = ybuf[fpar];
-            const uint8_t* xb = ring + fb * (CH * MD * 2);
+            uint8_t* yb = ybuf[0];
+            const uint8_t* xb = ybuf[1 + fb];
             const float rsq = 1.0f / sqrtf((float)MD);
 #pragma unroll
             for (int th = 0; th < 2; th++) {
@@ -547,22 +556,23 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
                 }
             }
             __syncthreads();
-            if (qk_wave) score(yb, page * T + c0, fpar);
+            if (qk_wave) score(yb, page * T + c0, fseq);
             __syncthreads();
-            accumulate(yb, fpar);
+            accumulate(yb, fseq);
         }
-        fpar ^= 1;
+        fseq++;
         fb ^= 1;
         fc = fn;
     }
 
     // ---- partial results: m, l per head; O rows for this wave's channels ----
     float* wsp = a.ws + (int64_t)a.B * a.Hq * MD / 2;  // partials follow the fp16 queries
+    const int64_t brow = (int64_t)b * a.Hq + h0;
 #pragma unroll
     for (int i = 0; i < 4; i++) {
         const float lt = rsum16(lp[i]);
         if (qk_wave && l16 == 0) {
-            float* o = wsp + (((int64_t)b * a.Hq + h0 + 16 * wave + 4 * g4 + i) * a.nsplit + split) * WS;
+            float* o = wsp + ((brow + 16 * wave + 4 * g4 + i) * a.nsplit + split) * WS;
             o[0] = mu[i];
             o[1] = lt;
         }
@@ -571,7 +581,7 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
     for (int hb = 0; hb < HB; hb++)
 #pragma unroll
         for (int i = 0; i < 4; i++) {
-            float* o = wsp + (((int64_t)b * a.Hq + h0 + 16 * hb + 4 * g4 + i) * a.nsplit + split) * WS + 4;
+            float* o = wsp + ((brow + 16 * hb + 4 * g4 + i) * a.nsplit + split) * WS + 4;
 #pragma unroll
             for (int c = 0; c < CBW; c++) o[CPW * wave + 16 * c + 8 * (l16 >> 3) + upos(l16 & 7)] = O[hb][c][i];
         }
