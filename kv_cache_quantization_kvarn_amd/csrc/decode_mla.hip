@@ -39,6 +39,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr int MD = 512;        // latent width
 constexpr int CH = 32;         // tokens per chunk
 constexpr float kLazy = 8.0f;  // rescale when the maximum grows by more than this (log2 units)
+constexpr float kFloor = -1.0e30f;  // finite stand-in for a running maximum of -inf
 
 #define LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
 
@@ -69,12 +70,19 @@ __device__ __forceinline__ h8 cat(h4 a, h4 b) {
     return h8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
-__device__ __forceinline__ float rmax16(float v) {  // max over the 16 lanes of a row
-    v = fmaxf(v, i2f(__builtin_amdgcn_mov_dpp(f2i(v), 0x128, 0xF, 0xF, false)));  // row_ror 8
-    v = fmaxf(v, i2f(__builtin_amdgcn_mov_dpp(f2i(v), 0x124, 0xF, 0xF, false)));  // row_ror 4
-    v = fmaxf(v, i2f(__builtin_amdgcn_mov_dpp(f2i(v), 0x122, 0xF, 0xF, false)));  // row_ror 2
-    v = fmaxf(v, i2f(__builtin_amdgcn_mov_dpp(f2i(v), 0x121, 0xF, 0xF, false)));  // row_ror 1
-    return v;
+// max over the 16 lanes of a row for 4 values: fused v_max_f32_dpp (each
+// value's next DPP read comes 4 instructions after its write; s_nop 1 covers
+// the write just before the block)
+__device__ __forceinline__ void rmax16x4(float (&v)[4]) {
+#define KVARN_RMAX4(CTRL)                                                                          \
+    "v_max_f32_dpp %0, %0, %0 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                          \
+    "v_max_f32_dpp %1, %1, %1 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                          \
+    "v_max_f32_dpp %2, %2, %2 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                          \
+    "v_max_f32_dpp %3, %3, %3 " CTRL " row_mask:0xf bank_mask:0xf\n\t"
+    asm volatile("s_nop 1\n\t" KVARN_RMAX4("row_ror:8") KVARN_RMAX4("row_ror:4") KVARN_RMAX4("row_ror:2")
+                     KVARN_RMAX4("row_ror:1")
+                 : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]));
+#undef KVARN_RMAX4
 }
 
 __device__ __forceinline__ float rsum16(float v) {
@@ -276,37 +284,50 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
         const f4 sacc[2] = {acc[0][0] + acc[0][1], acc[1][0] + acc[1][1]};
         // lane: heads 16*wave + 4*g4 + i, tokens 16*th + l16 of the chunk
         float s[2][4], cmax[4];
+        if (tok0 + CH <= L) {  // uniform: every token of the chunk is in the sequence
+#pragma unroll
+            for (int th = 0; th < 2; th++)
+#pragma unroll
+                for (int i = 0; i < 4; i++) s[th][i] = sacc[th][i] * sm2;
+        } else {
+#pragma unroll
+            for (int th = 0; th < 2; th++) {
+                const bool valid = tok0 + 16 * th + l16 < L;
+#pragma unroll
+                for (int i = 0; i < 4; i++) s[th][i] = valid ? sacc[th][i] * sm2 : -INFINITY;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; i++) cmax[i] = fmaxf(s[0][i], s[1][i]);
+        rmax16x4(cmax);
         bool need = false;
 #pragma unroll
-        for (int th = 0; th < 2; th++) {
-            const bool valid = tok0 + 16 * th + l16 < L;
+        for (int i = 0; i < 4; i++) need |= cmax[i] > mu[i] + kLazy;
+        // The heads of a block see the same tokens: either every cmax is
+        // finite (and a maximum of -inf, no token yet, moves) or none is.
+        // Below, max(mu, kFloor) stands in for mu: with mu = -inf the factors
+        // and the weights of the (then all -inf) scores come out as 0 from the
+        // bare v_exp_f32.
+        if (__builtin_amdgcn_ballot_w64(need) != 0) {
 #pragma unroll
-            for (int i = 0; i < 4; i++) s[th][i] = valid ? sacc[th][i] * sm2 : -INFINITY;
-        }
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            cmax[i] = rmax16(fmaxf(s[0][i], s[1][i]));
-            need |= cmax[i] > mu[i] + kLazy;
-        }
-        const bool any = __builtin_amdgcn_ballot_w64(need) != 0;
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            float al = 1.f;
-            if (any) {
+            for (int i = 0; i < 4; i++) {
                 const float mn = fmaxf(mu[i], cmax[i]);
-                al = (mu[i] == -INFINITY) ? 0.f : exp2f(mu[i] - mn);
+                const float al = __builtin_amdgcn_exp2f(fmaxf(mu[i], kFloor) - mn);
                 lp[i] *= al;
                 mu[i] = mn;
+                if (l16 == 0) alpha[seq & 1][16 * wave + 4 * g4 + i] = al;
             }
-            if (l16 == 0) alpha[seq & 1][16 * wave + 4 * g4 + i] = al;
+            if (lane == 0) atomicOr(&rescale_flag[seq % 3], 1);
         }
-        if (any && lane == 0) atomicOr(&rescale_flag[seq % 3], 1);
+        float mf[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) mf[i] = fmaxf(mu[i], kFloor);
 #pragma unroll
         for (int th = 0; th < 2; th++) {
             float p[4];
 #pragma unroll
             for (int i = 0; i < 4; i++) {
-                p[i] = (mu[i] == -INFINITY) ? 0.f : exp2f(s[th][i] - mu[i]);
+                p[i] = __builtin_amdgcn_exp2f(s[th][i] - mf[i]);  // s <= mu + kLazy: p <= 256
                 lp[i] += p[i];
             }
             const uint2 pk = make_uint2(float_to_half_bits(p[0]) | (float_to_half_bits(p[1]) << 16),
