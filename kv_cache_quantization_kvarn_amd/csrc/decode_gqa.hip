@@ -359,7 +359,12 @@ __global__ void __launch_bounds__(64, 2) decode_split_kernel(DecodeArgs a) {
     constexpr int VRW = VROW / 4;         // value code words of one channel (whole page)
     constexpr int VHW = 64 * VB / 32;     // value code words of one channel over 64 tokens
     constexpr bool PREK = KW <= 32;
-    constexpr bool PREV = NS * VHW <= 32;
+    // key chunks prefetched one step ahead: all of them at head_dim 256
+    // (the register budget of two waves per SIMD holds them), else chunk 0
+    constexpr int NKP = PREK ? (D == 256 ? NC : 1) : 1;
+    // value words of a step prefetched one step ahead when they fit the
+    // register budget (two waves per SIMD): 48 words at head_dim 256
+    constexpr bool PREV = NS * VHW <= (D == 256 ? 48 : 32);
     static_assert(VRW == TS * VHW, "a channel row is TS halves");
     const int npg = nq > split ? (nq - split + a.nsplit - 1) / a.nsplit : 0;  // quantized pages of this split
     const int nst = npg * TS;
@@ -378,12 +383,14 @@ __global__ void __launch_bounds__(64, 2) decode_split_kernel(DecodeArgs a) {
         return r;
     };
 
-    uint32_t kw[PREK ? KW : 1];
+    uint32_t kw[NKP][PREK ? KW : 1];
     uint32_t vw[NS][PREV ? VHW : 1];
     uint32_t ksz = 0, vsz = 0;
     uint32_t ckr[NS][2], cvr[(NS + 1) / 2];  // fp16 column scales, two per word
 #pragma unroll
-    for (int k = 0; k < (PREK ? KW : 1); k++) kw[k] = 0;
+    for (int c = 0; c < NKP; c++)
+#pragma unroll
+        for (int k = 0; k < (PREK ? KW : 1); k++) kw[c][k] = 0;
 #pragma unroll
     for (int r = 0; r < NS; r++) {
         cvr[r >> 1] = 0;
@@ -395,7 +402,10 @@ __global__ void __launch_bounds__(64, 2) decode_split_kernel(DecodeArgs a) {
         if (!r.ok) return;
         const uint8_t* rk = krec + ((int64_t)r.id * a.H + h) * KREC;
         const int tok = 64 * r.h + lane;
-        if constexpr (PREK) load_words(kw, rk + (int64_t)tok * KROW, KW / 4);
+        if constexpr (PREK) {
+#pragma unroll
+            for (int c = 0; c < NKP; c++) load_words(kw[c], rk + (int64_t)tok * KROW + c * KCH, KW / 4);
+        }
         ksz = reinterpret_cast<const uint32_t*>(rk + KCB)[tok];
         if (r.h == 0) {
             const uint16_t* ck = reinterpret_cast<const uint16_t*>(rk + KCB + 4 * T);
@@ -477,9 +487,9 @@ __global__ void __launch_bounds__(64, 2) decode_split_kernel(DecodeArgs a) {
 #pragma unroll
             for (int c = 0; c < NC; c++) {
                 uint32_t w[KW];
-                if (PREK && c == 0) {
+                if (PREK && c < NKP) {
 #pragma unroll
-                    for (int kk = 0; kk < KW; kk++) w[kk] = kw[PREK ? kk : 0];
+                    for (int kk = 0; kk < KW; kk++) w[kk] = kw[c < NKP ? c : 0][PREK ? kk : 0];
                 } else {
                     load_words(w, rk + (int64_t)tok * KROW + c * KCH, KW / 4);
                 }
