@@ -294,7 +294,7 @@ __device__ __forceinline__ void fp16_block(const DecodeArgs& a, const int f, con
 }
 
 template <int D, int T, int KB, int VB>
-__global__ void __launch_bounds__(64, 2) decode_split_kernel(DecodeArgs a) {
+__global__ void __launch_bounds__(64, D == 512 ? 1 : 2) decode_split_kernel(DecodeArgs a) {
     constexpr int G = 4;
     constexpr int NS = D / 64;            // operand slots per lane; value channel sets
     constexpr int NC = D / 128;           // 128-channel chunks of a key row
@@ -359,12 +359,13 @@ __global__ void __launch_bounds__(64, 2) decode_split_kernel(DecodeArgs a) {
     constexpr int VRW = VROW / 4;         // value code words of one channel (whole page)
     constexpr int VHW = 64 * VB / 32;     // value code words of one channel over 64 tokens
     constexpr bool PREK = KW <= 32;
-    // key chunks prefetched one step ahead: all of them at head_dim 256
-    // (the register budget of two waves per SIMD holds them), else chunk 0
-    constexpr int NKP = PREK ? (D == 256 ? NC : 1) : 1;
+    // key chunks prefetched one step ahead: all of them at head_dim 256 (the
+    // register budget of two waves per SIMD holds them) and 512 (one wave per
+    // SIMD, 512 registers), else chunk 0
+    constexpr int NKP = PREK ? (D >= 256 ? NC : 1) : 1;
     // value words of a step prefetched one step ahead when they fit the
-    // register budget (two waves per SIMD): 48 words at head_dim 256
-    constexpr bool PREV = NS * VHW <= (D == 256 ? 48 : 32);
+    // register budget: 48 words at head_dim 256, 96 at 512
+    constexpr bool PREV = NS * VHW <= (D == 256 ? 48 : D == 512 ? 96 : 32);
     static_assert(VRW == TS * VHW, "a channel row is TS halves");
     const int npg = nq > split ? (nq - split + a.nsplit - 1) / a.nsplit : 0;  // quantized pages of this split
     const int nst = npg * TS;
@@ -1273,10 +1274,11 @@ void decode_plan(int D, int H, int G, int mla, int B, int max_pages, int T, int 
     (void)G; (void)T; (void)kb; (void)vb;
     // GQA: one-wave workgroups, as many as fit at once: three per SIMD for
     // head_dim 128 (128 VGPRs, but the fp16 slots take the fourth), two for
-    // 256/512 (256 VGPRs).  MLA: one 8-wave workgroup per CU holds 64 heads,
+    // 256 (256 VGPRs), one for 512 (512 registers: a whole step's codes are
+    // prefetched).  MLA: one 8-wave workgroup per CU holds 64 heads,
     // so up to 128 heads take two workgroups per split.
     const int units = mla ? B * ((G + 63) / 64) : B * H;
-    const int target = mla ? 256 : (D == 128 ? 3072 : 2048);
+    const int target = mla ? 256 : (D == 128 ? 3072 : D == 256 ? 2048 : 1024);
     int ns = (target + units - 1) / units;
     if (ns < 1) ns = 1;
     // MLA: a split holds its page ids in two registers, 128 at most (with the
