@@ -154,7 +154,7 @@ __device__ __forceinline__ void fp16_block(const DecodeArgs& a, const int f, con
     constexpr int TS = T / 64;
     constexpr int WS = D + 4;           // partial: m, l, pad, pad, value sums
 
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x & 63;  // workgroups of head_dim 512 hold two waves
     const int blk = lane >> 2, m = lane & 3;
     const int Hq = a.Hq;
     const float sm2 = a.sm_scale * kLog2e;
@@ -293,11 +293,20 @@ __device__ __forceinline__ void fp16_block(const DecodeArgs& a, const int f, con
     }
 }
 
+// Waves per (split, KV head, sequence) of decode_split_kernel: head_dim 512
+// takes two, each with half of the channels (partial scores summed through
+// LDS once per step), so that a whole step's codes fit the registers of two
+// waves per SIMD.
+template <int D>
+constexpr int split_waves() { return D == 512 ? 2 : 1; }
+
 template <int D, int T, int KB, int VB>
-__global__ void __launch_bounds__(64, D == 512 ? 1 : 2) decode_split_kernel(DecodeArgs a) {
+__global__ void __launch_bounds__(64 * split_waves<D>(), 2) decode_split_kernel(DecodeArgs a) {
     constexpr int G = 4;
-    constexpr int NS = D / 64;            // operand slots per lane; value channel sets
-    constexpr int NC = D / 128;           // 128-channel chunks of a key row
+    constexpr int NWV = split_waves<D>();
+    constexpr int DH = D / NWV;           // channels of one wave
+    constexpr int NS = DH / 64;           // operand slots per lane; value channel sets
+    constexpr int NC = DH / 128;          // 128-channel chunks of a key row
     constexpr int TS = T / 64;            // 64-token sub-blocks of a page
     constexpr int KCB = T * D * KB / 8;
     constexpr int VCB = T * D * VB / 8;
@@ -310,29 +319,33 @@ __global__ void __launch_bounds__(64, D == 512 ? 1 : 2) decode_split_kernel(Deco
     constexpr float FK = (float)(1 << KB), FV = (float)(1 << VB);
     static_assert(KCH % 16 == 0 && VROW % 16 == 0, "16-byte code segments");
 
-    __shared__ __attribute__((aligned(16))) _Float16 pt[2][G][64];  // p * S_V of a step (high, low), by operand position
-    __shared__ float4 pf[64];
+    __shared__ __attribute__((aligned(16))) _Float16 pt[NWV][2][G][64];  // p * S_V of a step (high, low), by operand position
+    __shared__ float4 pf[NWV][64];
+    __shared__ float xs[NWV > 1 ? 2 : 1][NWV][G][64];  // partial scores by step parity
 
-    // grid z < B: quantized-page splits; z >= B: fp16 page slots, dispatched
-    // after every split so that they fill the splits' tail
+    const int wave = NWV > 1 ? __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) : 0;
+    const int lane = threadIdx.x & 63;
+    // grid z < B: quantized-page splits; z >= B: fp16 page slots (one per
+    // wave), dispatched after every split so that they fill the splits' tail
     if ((int)blockIdx.z >= a.B) {
-        if ((int)blockIdx.x < a.nfsplit) fp16_block<D, T>(a, blockIdx.x, blockIdx.y, blockIdx.z - a.B, pf);
+        const int slot = (int)blockIdx.x * NWV + wave;
+        if (slot < a.nfsplit) fp16_block<D, T>(a, slot, blockIdx.y, blockIdx.z - a.B, pf[wave]);
         return;
     }
     if ((int)blockIdx.x >= a.nsplit) return;
     const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-    const int lane = threadIdx.x;
     const int blk = lane >> 2, m = lane & 3;  // MFMA block; row (query head) of the broadcast operand
     const int Hq = a.Hq;
     const float sm2 = a.sm_scale * kLog2e;
 
     // rotated query (fp32) at the channels of this lane's operand slots.
-    // Slot r serves operand 32 (r >> 1) + blk + 16 (r & 1) of the scores.
+    // Slot r serves operand 32 (r >> 1) + blk + 16 (r & 1) of the wave's
+    // channels, operand DH / 4 * wave + ... of the row.
     const float* qr = a.ws + ((int64_t)b * Hq + h * G + m) * D;
     float qv[NS][4];
 #pragma unroll
     for (int r = 0; r < NS; r++) {
-        const int i = 32 * (r >> 1) + blk + 16 * (r & 1);
+        const int i = 32 * (r >> 1) + blk + 16 * (r & 1) + (DH / 4) * wave;
 #pragma unroll
         for (int k = 0; k < 4; k++) qv[r][k] = qr[code_of<KB>(i, k)];
     }
@@ -359,13 +372,13 @@ __global__ void __launch_bounds__(64, D == 512 ? 1 : 2) decode_split_kernel(Deco
     constexpr int VRW = VROW / 4;         // value code words of one channel (whole page)
     constexpr int VHW = 64 * VB / 32;     // value code words of one channel over 64 tokens
     constexpr bool PREK = KW <= 32;
-    // key chunks prefetched one step ahead: all of them at head_dim 256 (the
-    // register budget of two waves per SIMD holds them) and 512 (one wave per
-    // SIMD, 512 registers), else chunk 0
+    // key chunks prefetched one step ahead: all of the wave's at head_dim 256
+    // and 512 (the register budget of two waves per SIMD holds them), else
+    // chunk 0
     constexpr int NKP = PREK ? (D >= 256 ? NC : 1) : 1;
     // value words of a step prefetched one step ahead when they fit the
-    // register budget: 48 words at head_dim 256, 96 at 512
-    constexpr bool PREV = NS * VHW <= (D == 256 ? 48 : D == 512 ? 96 : 32);
+    // register budget: 48 words at head_dim 256 and 512 (per wave)
+    constexpr bool PREV = NS * VHW <= (D >= 256 ? 48 : 32);
     static_assert(VRW == TS * VHW, "a channel row is TS halves");
     const int npg = nq > split ? (nq - split + a.nsplit - 1) / a.nsplit : 0;  // quantized pages of this split
     const int nst = npg * TS;
@@ -405,14 +418,14 @@ __global__ void __launch_bounds__(64, D == 512 ? 1 : 2) decode_split_kernel(Deco
         const int tok = 64 * r.h + lane;
         if constexpr (PREK) {
 #pragma unroll
-            for (int c = 0; c < NKP; c++) load_words(kw[c], rk + (int64_t)tok * KROW + c * KCH, KW / 4);
+            for (int c = 0; c < NKP; c++) load_words(kw[c], rk + (int64_t)tok * KROW + (NC * wave + c) * KCH, KW / 4);
         }
         ksz = reinterpret_cast<const uint32_t*>(rk + KCB)[tok];
         if (r.h == 0) {
             const uint16_t* ck = reinterpret_cast<const uint16_t*>(rk + KCB + 4 * T);
 #pragma unroll
             for (int r2 = 0; r2 < NS; r2++) {
-                const int i = 32 * (r2 >> 1) + blk + 16 * (r2 & 1);
+                const int i = 32 * (r2 >> 1) + blk + 16 * (r2 & 1) + (DH / 4) * wave;
                 ckr[r2][0] = (uint32_t)ck[code_of<KB>(i, 0)] | ((uint32_t)ck[code_of<KB>(i, 1)] << 16);
                 ckr[r2][1] = (uint32_t)ck[code_of<KB>(i, 2)] | ((uint32_t)ck[code_of<KB>(i, 3)] << 16);
             }
@@ -423,9 +436,9 @@ __global__ void __launch_bounds__(64, D == 512 ? 1 : 2) decode_split_kernel(Deco
         const uint8_t* rv = vrec + ((int64_t)r.id * a.H + h) * VREC;
 #pragma unroll
         for (int sv = 0; sv < NS; sv++) {
-            if constexpr (PREV) load_words(vw[sv], rv + (int64_t)(64 * sv + lane) * VROW + r.h * (4 * VHW), VHW / 4);
+            if constexpr (PREV) load_words(vw[sv], rv + (int64_t)(64 * (NS * wave + sv) + lane) * VROW + r.h * (4 * VHW), VHW / 4);
             if (r.h == 0) {
-                const uint32_t c16 = reinterpret_cast<const uint16_t*>(rv + VCB + 4 * T)[64 * sv + lane];
+                const uint32_t c16 = reinterpret_cast<const uint16_t*>(rv + VCB + 4 * T)[64 * (NS * wave + sv) + lane];
                 cvr[sv >> 1] = (sv & 1) ? (cvr[sv >> 1] | (c16 << 16)) : c16;
             }
         }
@@ -492,7 +505,7 @@ __global__ void __launch_bounds__(64, D == 512 ? 1 : 2) decode_split_kernel(Deco
 #pragma unroll
                     for (int kk = 0; kk < KW; kk++) w[kk] = kw[c < NKP ? c : 0][PREK ? kk : 0];
                 } else {
-                    load_words(w, rk + (int64_t)tok * KROW + c * KCH, KW / 4);
+                    load_words(w, rk + (int64_t)tok * KROW + (NC * wave + c) * KCH, KW / 4);
                 }
                 static_for<32>([&](auto ic) {
                     constexpr int il = decltype(ic)::value;
@@ -506,6 +519,20 @@ __global__ void __launch_bounds__(64, D == 512 ? 1 : 2) decode_split_kernel(Deco
             const float fs = FK * S, zc = Z - fs;
 #pragma unroll
             for (int g = 0; g < G; g++) s[g] = sm2 * fmaf(fs, R[g], sq[g] * zc);
+            if constexpr (NWV > 1) {
+                // the score is linear in the channel halves: sum the waves'
+                // partials (same order in every wave, so all see equal scores)
+#pragma unroll
+                for (int g = 0; g < G; g++) xs[k & 1][wave][g][lane] = s[g];
+                __syncthreads();
+#pragma unroll
+                for (int g = 0; g < G; g++) {
+                    float t = xs[k & 1][0][g][lane];
+#pragma unroll
+                    for (int w2 = 1; w2 < NWV; w2++) t += xs[k & 1][w2][g][lane];
+                    s[g] = t;
+                }
+            }
         }
         issue_k(nxt);  // the key registers are free
 
@@ -536,16 +563,16 @@ __global__ void __launch_bounds__(64, D == 512 ? 1 : 2) decode_split_kernel(Deco
                 const float x = p[g] * S;
                 const _Float16 hi = (_Float16)x;
                 const _Float16 lo = (_Float16)(x - (float)hi);
-                pt[0][g][pos] = hi;
-                pt[1][g][pos] = lo;
+                pt[wave][0][g][pos] = hi;
+                pt[wave][1][g][pos] = lo;
                 e[g] = fmaf(p[g], Z, -FV * ((float)hi + (float)lo));
             }
             float E[G];
 #pragma unroll
             for (int g = 0; g < G; g++) E[g] = wave_sum_all(e[g]);
             wave_sync();
-            const h4 pa = *reinterpret_cast<const h4*>(&pt[0][m][4 * blk]);
-            const h4 pal = *reinterpret_cast<const h4*>(&pt[1][m][4 * blk]);
+            const h4 pa = *reinterpret_cast<const h4*>(&pt[wave][0][m][4 * blk]);
+            const h4 pal = *reinterpret_cast<const h4*>(&pt[wave][1][m][4 * blk]);
 #pragma unroll
             for (int sv = 0; sv < NS; sv++) {
                 uint32_t w[VHW];
@@ -553,7 +580,7 @@ __global__ void __launch_bounds__(64, D == 512 ? 1 : 2) decode_split_kernel(Deco
 #pragma unroll
                     for (int kk = 0; kk < VHW; kk++) w[kk] = vw[sv][PREV ? kk : 0];
                 } else {
-                    load_words(w, rv + (int64_t)(64 * sv + lane) * VROW + cur.h * (4 * VHW), VHW / 4);
+                    load_words(w, rv + (int64_t)(64 * (NS * wave + sv) + lane) * VROW + cur.h * (4 * VHW), VHW / 4);
                 }
                 f4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
                 static_for<16>([&](auto ic) {
@@ -578,12 +605,12 @@ __global__ void __launch_bounds__(64, D == 512 ? 1 : 2) decode_split_kernel(Deco
     for (int g = 0; g < G; g++) {
         const float lt = wave_sum_all(lp[g]);
         float* o = wsp + (((int64_t)b * Hq + h * G + g) * (a.nsplit + a.nfsplit) + split) * WS;
-        if (lane == 0) {
+        if (lane == 0 && wave == 0) {
             o[0] = mrun[g];
             o[1] = lt;
         }
 #pragma unroll
-        for (int sv = 0; sv < NS; sv++) o[4 + 64 * sv + lane] = accr[sv][g];
+        for (int sv = 0; sv < NS; sv++) o[4 + 64 * (NS * wave + sv) + lane] = accr[sv][g];
     }
 }
 
@@ -1240,11 +1267,13 @@ hipError_t launch_gqa(const DecodeArgs& a, hipStream_t st) {
         if (e != hipSuccess) return e;
     }
     // one launch: the quantized-page splits (z < B), then the fp16 page slots
-    const dim3 grid(a.nsplit > a.nfsplit ? a.nsplit : a.nfsplit, a.H, a.nfsplit > 0 ? 2 * a.B : a.B);
+    constexpr int NWV = D == 128 ? 1 : split_waves<D>();
+    const int nfx = (a.nfsplit + NWV - 1) / NWV;  // fp16 slots: one per wave
+    const dim3 grid(a.nsplit > nfx ? a.nsplit : nfx, a.H, a.nfsplit > 0 ? 2 * a.B : a.B);
     if constexpr (D == 128)
         hipLaunchKernelGGL((decode_split128_kernel<T, KB, VB>), grid, dim3(64), 0, st, a);
     else
-        hipLaunchKernelGGL((decode_split_kernel<D, T, KB, VB>), grid, dim3(64), 0, st, a);
+        hipLaunchKernelGGL((decode_split_kernel<D, T, KB, VB>), grid, dim3(64 * NWV), 0, st, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(a.B * a.Hq), dim3(combine_groups<D>() * D), 0, st,
@@ -1272,13 +1301,12 @@ hipError_t gqa_bits(const DecodeArgs& a, hipStream_t st) {
 void decode_plan(int D, int H, int G, int mla, int B, int max_pages, int T, int kb, int vb, int* nsplit,
                  int* pps) {
     (void)G; (void)T; (void)kb; (void)vb;
-    // GQA: one-wave workgroups, as many as fit at once: three per SIMD for
-    // head_dim 128 (128 VGPRs, but the fp16 slots take the fourth), two for
-    // 256 (256 VGPRs), one for 512 (512 registers: a whole step's codes are
-    // prefetched).  MLA: one 8-wave workgroup per CU holds 64 heads,
+    // GQA: as many waves as fit at once: three per SIMD for head_dim 128 (128
+    // VGPRs, but the fp16 slots take the fourth), two for 256 and 512 (256
+    // VGPRs; head_dim 512 splits are two-wave workgroups).  MLA: one 8-wave workgroup per CU holds 64 heads,
     // so up to 128 heads take two workgroups per split.
     const int units = mla ? B * ((G + 63) / 64) : B * H;
-    const int target = mla ? 256 : (D == 128 ? 3072 : D == 256 ? 2048 : 1024);
+    const int target = mla ? 256 : (D == 128 ? 3072 : D == 256 ? 2048 : 1024);  // workgroups
     int ns = (target + units - 1) / units;
     if (ns < 1) ns = 1;
     // MLA: a split holds its page ids in two registers, 128 at most (with the
