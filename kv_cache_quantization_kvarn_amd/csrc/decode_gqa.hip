@@ -293,15 +293,14 @@ __device__ __forceinline__ void fp16_block(const DecodeArgs& a, const int f, con
     }
 }
 
-// Waves per (split, KV head, sequence) of decode_split_kernel: head_dim 512
-// takes two, each with half of the channels (partial scores summed through
-// LDS once per step), so that a whole step's codes fit the registers of two
-// waves per SIMD.
+// Waves per (split, KV head, sequence) of decode_split_kernel: one per 128
+// channels, the partial scores summed through LDS once per step, so that a
+// whole step's codes are prefetched in the registers of three waves per SIMD.
 template <int D>
-constexpr int split_waves() { return D == 512 ? 2 : 1; }
+constexpr int split_waves() { return D / 128; }
 
 template <int D, int T, int KB, int VB>
-__global__ void __launch_bounds__(64 * split_waves<D>(), 2) decode_split_kernel(DecodeArgs a) {
+__global__ void __launch_bounds__(64 * split_waves<D>(), 3) decode_split_kernel(DecodeArgs a) {
     constexpr int G = 4;
     constexpr int NWV = split_waves<D>();
     constexpr int DH = D / NWV;           // channels of one wave
@@ -372,13 +371,10 @@ __global__ void __launch_bounds__(64 * split_waves<D>(), 2) decode_split_kernel(
     constexpr int VRW = VROW / 4;         // value code words of one channel (whole page)
     constexpr int VHW = 64 * VB / 32;     // value code words of one channel over 64 tokens
     constexpr bool PREK = KW <= 32;
-    // key chunks prefetched one step ahead: all of the wave's at head_dim 256
-    // and 512 (the register budget of two waves per SIMD holds them), else
-    // chunk 0
-    constexpr int NKP = PREK ? (D >= 256 ? NC : 1) : 1;
-    // value words of a step prefetched one step ahead when they fit the
-    // register budget: 48 words at head_dim 256 and 512 (per wave)
-    constexpr bool PREV = NS * VHW <= (D >= 256 ? 48 : 32);
+    // the wave's key chunk prefetched one step ahead
+    constexpr int NKP = 1;
+    // the wave's value words of a step prefetched one step ahead (24 words at most)
+    constexpr bool PREV = NS * VHW <= 32;
     static_assert(VRW == TS * VHW, "a channel row is TS halves");
     const int npg = nq > split ? (nq - split + a.nsplit - 1) / a.nsplit : 0;  // quantized pages of this split
     const int nst = npg * TS;
@@ -1301,12 +1297,12 @@ hipError_t gqa_bits(const DecodeArgs& a, hipStream_t st) {
 void decode_plan(int D, int H, int G, int mla, int B, int max_pages, int T, int kb, int vb, int* nsplit,
                  int* pps) {
     (void)G; (void)T; (void)kb; (void)vb;
-    // GQA: as many waves as fit at once: three per SIMD for head_dim 128 (128
-    // VGPRs, but the fp16 slots take the fourth), two for 256 and 512 (256
-    // VGPRs; head_dim 512 splits are two-wave workgroups).  MLA: one 8-wave workgroup per CU holds 64 heads,
+    // GQA: as many waves as fit at once: three per SIMD (head_dim 128: 128
+    // VGPRs, but the fp16 slots take the fourth; 256 and 512: up to 170 VGPRs,
+    // splits of two and four waves).  MLA: one 8-wave workgroup per CU holds 64 heads,
     // so up to 128 heads take two workgroups per split.
     const int units = mla ? B * ((G + 63) / 64) : B * H;
-    const int target = mla ? 256 : (D == 128 ? 3072 : D == 256 ? 2048 : 1024);  // workgroups
+    const int target = mla ? 256 : 3072 / (D == 128 ? 1 : D / 128);  // workgroups
     int ns = (target + units - 1) / units;
     if (ns < 1) ns = 1;
     // MLA: a split holds its page ids in two registers, 128 at most (with the
