@@ -8,11 +8,12 @@
 // with q' = H q (rotated once, per sequence and head, by qrot_kernel) and
 // y_t the record read back in the rotated basis, y_tj = C_j (S_t c_tj + Zp_t).
 // Each chunk is read back once into LDS (fp16) and used by all heads; it never
-// goes to HBM.  fp16 sink and tail chunks are rotated into the same basis on
-// the fly (an MFMA product with H_512, whose +-1 operand blocks are a fixed
-// per-lane pattern up to a sign), so a split keeps one accumulator.  The
-// softmax rescales O lazily: only when a head's running maximum grows by more
-// than 2^8, which keeps every weight below 256.  The combine applies H once.
+// goes to HBM.  fp16 sink and tail chunks stay in the original basis (q' . y
+// = q . x for the orthonormal H): the plain query meets the stored rows, and
+// their value sums form a second partial of the split.  The softmax rescales
+// O lazily: only when a head's running maximum grows by more than 2^8, which
+// keeps every weight below 256.  The combine applies H once, to the rotated
+// partials.
 //
 // Workgroup: 8 waves (two per SIMD) per (head group of up to 64 heads,
 // split, sequence).  Scores: waves 0..3 own one head block (16 heads) each
@@ -116,12 +117,6 @@ __global__ void __launch_bounds__(256) qrot_kernel(const void* __restrict__ q, i
     for (int j = threadIdx.x; j < MD; j += 256) qr[(int64_t)bh * MD + j] = (_Float16)(x[j] * rs);
 }
 
-// H_512[m][k] for m = 16*mb + l16, k = 32*ks + 8*g4 + i factors as
-//   sign(mb, ks) * P(l16, g4, i) * (-1)^(mb_0 * g4_1),
-// with sign(mb, ks) = (-1)^popcount((mb >> 1) & ks) and
-// P = (-1)^(popcount(l16 & i & 7) + l16_3 * g4_0): two per-lane operand
-// patterns (and their negations) serve every block.
-
 // Workgroup of 8 waves, two per SIMD.  Waves 0..3 ("score waves") own one
 // head block (16 heads) each: scores over a whole chunk, its softmax and its
 // weights.  Waves 4..7 read the next chunk back meanwhile.  All 8 waves form
@@ -156,7 +151,6 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
     static_assert(HQ * 2 <= 160, "weight rows hold at most 64 heads");
     __shared__ __attribute__((aligned(16))) uint8_t ybuf[3][CH * YROW];  // chunks, rotated basis (fp16)
     __shared__ __attribute__((aligned(16))) uint8_t pbuf[2][PBYTES];      // weights [token][head] (fp16)
-    __shared__ __attribute__((aligned(16))) h8 hpat[2][2][64];
     __shared__ __attribute__((aligned(16))) uint4 cbuf[2][MD / 8];       // column scales by unit, by page parity
     __shared__ float alpha[2][HQ];
     __shared__ int rescale_flag[3];
@@ -198,20 +192,6 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
             qa[ks] = h8{v[0], v[4], v[1], v[5], v[2], v[6], v[3], v[7]};  // unit order
         } else {
             qa[ks] = h8{0, 0, 0, 0, 0, 0, 0, 0};
-        }
-    }
-    // H_512 operand patterns for the fp16-chunk rotation, per lane: hpat[odd mb][negated][lane]
-    if (wave == 0) {
-#pragma unroll
-        for (int od = 0; od < 2; od++) {
-            h8 v;
-#pragma unroll
-            for (int i = 0; i < 8; i++) {
-                const int par = (__builtin_popcount((unsigned)(l16 & i & 7)) + ((l16 >> 3) & g4 & 1) + (od & (g4 >> 1))) & 1;
-                v[i] = par ? (_Float16)-1.0f : (_Float16)1.0f;
-            }
-            hpat[od][0][lane] = v;
-            hpat[od][1][lane] = -v;
         }
     }
     if (tid < 3) rescale_flag[tid] = 0;
@@ -494,13 +474,71 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no load may land in LDS after this point
     __syncthreads();
 
-    // ---- fp16 chunks: y_t = H x_t / sqrt(512), Y^T = H X^T on the MFMA into
-    // ybuf[0].  The 32 KB of a chunk (token rows of 1 KB) come through ybuf[1]
-    // and ybuf[2] (idle now) by LDS-DMA loads one chunk ahead, 16-byte piece p of
-    // token t at piece p ^ (t & 7) of its row so that 8 lanes reading one
-    // piece of 8 tokens hit 8 bank groups; the B operand is 8 channels of one
-    // token per lane.  Wave w writes channel blocks MBW*w .. of both 16-token
-    // halves. ----
+    // ---- partial results: m, l per head; O rows for this wave's channels.
+    // Split s writes partial s (quantized chunks, rotated basis, channels in
+    // unit order) and partial nsplit + s (fp16 chunks, original basis). ----
+    float* wsp = a.ws + (int64_t)a.B * a.Hq * MD / 2;  // partials follow the fp16 queries
+    const int64_t brow = (int64_t)b * a.Hq + h0;
+    const int np = 2 * a.nsplit;
+    auto write_partial = [&](int slot, bool plain) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const float lt = rsum16(lp[i]);
+            if (qk_wave && l16 == 0) {
+                float* o = wsp + ((brow + 16 * wave + 4 * g4 + i) * np + slot) * WS;
+                o[0] = mu[i];
+                o[1] = lt;
+            }
+        }
+#pragma unroll
+        for (int hb = 0; hb < HB; hb++)
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                float* o = wsp + ((brow + 16 * hb + 4 * g4 + i) * np + slot) * WS + 4;
+#pragma unroll
+                for (int c = 0; c < CBW; c++)
+                    o[CPW * wave + 16 * c + (plain ? l16 : 8 * (l16 >> 3) + upos(l16 & 7))] = O[hb][c][i];
+            }
+    };
+    write_partial(split, false);
+
+    // ---- fp16 chunks, in the original basis (q'.y = q.x): the plain query
+    // against the stored rows, value sums into a fresh accumulator.  The 32 KB
+    // of a chunk come by LDS-DMA loads one chunk ahead straight into the
+    // read-back row layout of ybuf[1] or ybuf[2] (idle now; one 1 KB token
+    // row per load, channels in natural order); rows past the sequence end
+    // are zeroed instead (their weight is 0 and must not meet NaN). ----
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        mu[i] = -INFINITY;
+        lp[i] = 0.f;
+    }
+#pragma unroll
+    for (int hb = 0; hb < HB; hb++)
+#pragma unroll
+        for (int c = 0; c < CBW; c++) O[hb][c] = f4{0.f, 0.f, 0.f, 0.f};
+    if (qk_wave && nfp > 0) {  // the plain query of this wave's head block, natural channel order
+        const int64_t qi = ((int64_t)b * a.Hq + h0 + wave * 16 + l16) * MD + 8 * g4;
+#pragma unroll
+        for (int ks = 0; ks < 16; ks++) {
+            h8 v;
+            if (a.q_bf16) {
+                const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) + qi + 32 * ks);
+                const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    v[2 * e] = (_Float16)__builtin_bit_cast(float, w[e] << 16);
+                    v[2 * e + 1] = (_Float16)__builtin_bit_cast(float, w[e] & 0xffff0000u);
+                }
+            } else {
+                const float4 x0 = *reinterpret_cast<const float4*>(static_cast<const float*>(a.q) + qi + 32 * ks);
+                const float4 x1 = *reinterpret_cast<const float4*>(static_cast<const float*>(a.q) + qi + 32 * ks + 4);
+                v = h8{(_Float16)x0.x, (_Float16)x0.y, (_Float16)x0.z, (_Float16)x0.w,
+                       (_Float16)x1.x, (_Float16)x1.y, (_Float16)x1.z, (_Float16)x1.w};
+            }
+            qa[ks] = v;
+        }
+    }
     static_assert(CH * MD * 2 <= CH * YROW, "an fp16 chunk fits a read-back buffer");
     const i32x4 rf = raw_buffer(a.k_fp16, (uint32_t)(a.n_fpages * T * MD * 2));
     auto fchunks = [&](int j) {  // chunks holding tokens of the split's j-th fp16 page (0: none or a bad id)
@@ -524,10 +562,13 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
         if (f.j >= nfp) return;
         const int id = page_id(nqp + f.j);
         const int base = (id * T + f.cc * CH) * (MD * 2);
+        const int nvalid = min(CH, L - (fpage(f.j) * T + f.cc * CH));  // >= 1
+        uint8_t* yb = ybuf[1 + buf];
 #pragma unroll
         for (int i = 0; i < 4; i++) {
             const int t = 4 * wave + i;  // token of the chunk
-            lds_dma16(lds_address(ybuf[1 + buf]) + 1024 * t, rf, 1024 * t + 16 * (lane ^ (t & 7)), base);
+            if (t < nvalid) lds_dma16(lds_address(yb) + (uint32_t)yoff(t, 0), rf, 16 * lane, base + 1024 * t);
+            else *reinterpret_cast<uint4*>(yb + yoff(t, lane)) = make_uint4(0u, 0u, 0u, 0u);
         }
     };
     int fseq = nqc;  // chunk numbering continues from the quantized chunks
@@ -539,73 +580,16 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
         __syncthreads();
         const FChunk fn = fnext(fc);
         issue_f(fn, fb ^ 1);  // the other buffer's last reader finished before the barrier above
-        const int page = fpage(fc.j);
-        const int c0 = fc.cc * CH;
-        {
-            constexpr int MBW = 32 / NWV;
-            uint8_t* yb = ybuf[0];
-            const uint8_t* xb = ybuf[1 + fb];
-            const float rsq = 1.0f / sqrtf((float)MD);
-#pragma unroll
-            for (int th = 0; th < 2; th++) {
-                f4 z[MBW];
-#pragma unroll
-                for (int m = 0; m < MBW; m++) z[m] = f4{0.f, 0.f, 0.f, 0.f};
-                const int t = 16 * th + l16;
-#pragma unroll
-                for (int ks = 0; ks < 16; ks++) {
-                    h8 bx = *reinterpret_cast<const h8*>(xb + 1024 * t + 16 * ((4 * ks + g4) ^ (t & 7)));
-                    // sign(mb, ks) = (-1)^popcount(((MBW/2)*wave) & ks) * (-1)^popcount((m >> 1) & ks):
-                    // the wave part negates the B operand, the m part picks the pattern
-                    if (__builtin_popcount((unsigned)((MBW / 2) * wave) & (unsigned)ks) & 1) bx = -bx;
-#pragma unroll
-                    for (int m = 0; m < MBW; m++) {
-                        const h8 av = hpat[m & 1][__builtin_popcount((unsigned)((m >> 1) & ks)) & 1][lane];
-                        z[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bx, z[m], 0, 0, 0);
-                    }
-                }
-                // lane: channels 16*mb + 4*g4 .. +3 of token 16*th + l16; tokens past the
-                // sequence end are zeroed (their weight is 0 and must not meet NaN)
-                const bool tv = page * T + c0 + t < L;
-#pragma unroll
-                for (int m = 0; m < MBW; m++) {
-                    // channel 4*(g4&1) + i of unit 2*mb + (g4>>1) sits at position 2*i + (g4&1)
-                    uint8_t* dst = yb + yoff(t, 2 * (MBW * wave + m) + (g4 >> 1)) + 2 * (g4 & 1);
-#pragma unroll
-                    for (int i = 0; i < 4; i++)
-                        *reinterpret_cast<uint16_t*>(dst + 4 * i) = tv ? (uint16_t)float_to_half_bits(z[m][i] * rsq) : (uint16_t)0;
-                }
-            }
-            __syncthreads();
-            if (qk_wave) score(yb, page * T + c0, fseq);
-            __syncthreads();
-            accumulate(yb, fseq);
-        }
+        const uint8_t* yb = ybuf[1 + fb];
+        if (qk_wave) score(yb, fpage(fc.j) * T + fc.cc * CH, fseq);
+        __syncthreads();
+        accumulate(yb, fseq);
         fseq++;
         fb ^= 1;
         fc = fn;
     }
-
-    // ---- partial results: m, l per head; O rows for this wave's channels ----
-    float* wsp = a.ws + (int64_t)a.B * a.Hq * MD / 2;  // partials follow the fp16 queries
-    const int64_t brow = (int64_t)b * a.Hq + h0;
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        const float lt = rsum16(lp[i]);
-        if (qk_wave && l16 == 0) {
-            float* o = wsp + ((brow + 16 * wave + 4 * g4 + i) * a.nsplit + split) * WS;
-            o[0] = mu[i];
-            o[1] = lt;
-        }
-    }
-#pragma unroll
-    for (int hb = 0; hb < HB; hb++)
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            float* o = wsp + ((brow + 16 * hb + 4 * g4 + i) * a.nsplit + split) * WS + 4;
-#pragma unroll
-            for (int c = 0; c < CBW; c++) o[CPW * wave + 16 * c + 8 * (l16 >> 3) + upos(l16 & 7)] = O[hb][c][i];
-        }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    write_partial(a.nsplit + split, true);
 }
 
 // merge the splits of one (sequence, head), rotate back once, normalize
@@ -613,19 +597,25 @@ __global__ void __launch_bounds__(256) mla_combine_kernel(const float* __restric
     constexpr int WS = MD + 4;
     __shared__ float x[MD];
     const int bh = blockIdx.x;
-    const float* base = wsp + (int64_t)bh * nsplit * WS;
+    const int np = 2 * nsplit;  // partials s < nsplit: rotated basis; s >= nsplit: original basis
+    const float* base = wsp + (int64_t)bh * np * WS;
     float M = -INFINITY;
-    for (int s = 0; s < nsplit; s++) M = fmaxf(M, base[s * WS]);
-    float Ls = 0.f, r0 = 0.f, r1 = 0.f;
+    for (int s = 0; s < np; s++) M = fmaxf(M, base[s * WS]);
+    float Ls = 0.f, r0 = 0.f, r1 = 0.f, p0 = 0.f, p1 = 0.f;
     const int j0 = threadIdx.x, j1 = threadIdx.x + 256;
     if (M != -INFINITY) {
-        for (int s = 0; s < nsplit; s++) {
+        for (int s = 0; s < np; s++) {
             const float ms = base[s * WS];
             if (ms == -INFINITY) continue;
             const float e = exp2f(ms - M);
             Ls = fmaf(base[s * WS + 1], e, Ls);
-            r0 = fmaf(base[s * WS + 4 + j0], e, r0);
-            r1 = fmaf(base[s * WS + 4 + j1], e, r1);
+            if (s < nsplit) {
+                r0 = fmaf(base[s * WS + 4 + j0], e, r0);
+                r1 = fmaf(base[s * WS + 4 + j1], e, r1);
+            } else {
+                p0 = fmaf(base[s * WS + 4 + j0], e, p0);
+                p1 = fmaf(base[s * WS + 4 + j1], e, p1);
+            }
         }
     }
     x[j0] = r0;
@@ -640,9 +630,10 @@ __global__ void __launch_bounds__(256) mla_combine_kernel(const float* __restric
         x[i1] = u - v;
         __syncthreads();
     }
-    const float sc = Ls > 0.f ? 1.0f / (Ls * sqrtf((float)MD)) : 0.f;
-    out[(int64_t)bh * MD + j0] = x[j0] * sc;
-    out[(int64_t)bh * MD + j1] = x[j1] * sc;
+    const float il = Ls > 0.f ? 1.0f / Ls : 0.f;
+    const float sc = il / sqrtf((float)MD);
+    out[(int64_t)bh * MD + j0] = fmaf(x[j0], sc, p0 * il);
+    out[(int64_t)bh * MD + j1] = fmaf(x[j1], sc, p1 * il);
 }
 
 template <int T, int HB>
@@ -676,7 +667,8 @@ hipError_t launch_mla_hb(const DecodeArgs& a, hipStream_t st) {
 }  // namespace
 
 size_t mla_workspace_floats(int Hq, int B, int nsplit) {
-    return (size_t)B * Hq * MD / 2 + (size_t)B * Hq * nsplit * (MD + 4);
+    // fp16 queries, then two partials per split (quantized and fp16 chunks)
+    return (size_t)B * Hq * MD / 2 + (size_t)B * Hq * 2 * nsplit * (MD + 4);
 }
 
 hipError_t launch_mla(const DecodeArgs& a, hipStream_t st) {
