@@ -1302,7 +1302,10 @@ void decode_plan(int D, int H, int G, int mla, int B, int max_pages, int T, int 
     // splits of two and four waves).  MLA: one 8-wave workgroup per CU holds 64 heads,
     // so up to 128 heads take two workgroups per split.
     const int units = mla ? B * ((G + 63) / 64) : B * H;
-    const int target = mla ? 256 : 3072 / (D == 128 ? 1 : D / 128);  // workgroups
+    // (head_dim 128: 3584 one-wave workgroups, a seventh more than the 3072
+    // resident at once, measured best: the splits' lengths vary with the
+    // sequence lengths and the fp16 slots fill in behind them)
+    const int target = mla ? 256 : (D == 128 ? 3584 : 3072 / (D / 128));  // workgroups
     int ns = (target + units - 1) / units;
     if (ns < 1) ns = 1;
     // MLA: a split holds its page ids in two registers, 128 at most (with the
