@@ -138,23 +138,25 @@ void orc_hadamard_matrix(int D, double *H)
             H[(int64_t)k * D + j] = (popcount_int((unsigned)(k & j)) & 1) ? -s : s;
 }
 
-/* Y = X . H applied to every token row of a T x D tile (plain matrix
- * product with the explicit matrix). */
+/* Y = X . H applied to every token row of a T x D tile: the +-1 signs of
+ * the Sylvester matrix are summed first and the sum is divided by sqrt(D)
+ * once.  For fp16 inputs every partial sum is exact in fp64 (an fp16 value
+ * is an integer multiple of 2^-24 below 2^16, and D <= 2^9 of them need at
+ * most 49 bits), so Y is the exact rotation rounded once; in particular a
+ * channel that the rotation cancels comes out exactly zero. */
 void orc_rotate(int T, int D, const double *X, double *Y)
 {
-    double *H = (double *)malloc(sizeof(double) * (size_t)D * D);
-    orc_hadamard_matrix(D, H);
-    /* H is symmetric (H[k][j] = H[j][k]); reading row j keeps the same
-     * operands in the same summation order with unit-stride access. */
+    const double rt = sqrt((double)D);
     for (int t = 0; t < T; t++) {
         for (int j = 0; j < D; j++) {
             double acc = 0.0;
-            for (int k = 0; k < D; k++)
-                acc += X[(int64_t)t * D + k] * H[(int64_t)j * D + k];
-            Y[(int64_t)t * D + j] = acc;
+            for (int k = 0; k < D; k++) {
+                double x = X[(int64_t)t * D + k];
+                acc += (popcount_int((unsigned)(k & j)) & 1) ? -x : x;
+            }
+            Y[(int64_t)t * D + j] = acc / rt;
         }
     }
-    free(H);
 }
 
 /* ------------------------------------------------------------------------ */

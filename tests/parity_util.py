@@ -62,3 +62,24 @@ def decode_rel_err(out, ref):
     num = np.abs(out - ref).max(axis=1)
     rel = np.where(den > 0, num / np.where(den > 0, den, 1), num)
     return float(rel.max()), int(rel.argmax())
+
+
+def degenerate_tile(T, D, seed, zero_rows=9):
+    """fp16 tile (uint16 bits, [T, D]) with exactly zero token rows and exactly
+    zero channels after the rotation: every row is an integer combination of
+    half of the +-1 sign patterns s_k(j) = (-1)^popcount(j & k) (the rows of
+    the unnormalized Sylvester matrix, mutually orthogonal), so the rotated
+    row is zero in every other channel; every zero_rows-th row is zero.  The
+    entries are integers of magnitude at most 2 D, exact in fp16.
+
+    Returns (bits, kept channels k)."""
+    rng = np.random.default_rng(seed)
+    keep = np.sort(rng.choice(D, D // 2, replace=False))
+    j = np.arange(D)
+    signs = np.array([1 - 2 * (np.unpackbits(np.array([k & jj for jj in j], np.uint16).view(np.uint8))
+                                .reshape(D, 16).sum(1) & 1) for k in keep], np.int64)  # [D/2, D]
+    coef = rng.integers(-4, 5, (T, D // 2))
+    x = coef @ signs
+    x[::zero_rows] = 0
+    assert np.abs(x).max() <= 2 * D
+    return x.astype(np.float16).view(np.uint16), keep

@@ -9,7 +9,7 @@ import pytest
 import torch
 
 from gpu_util import device, gpu_case, host_u16, run_quantize, say, workload
-from parity_util import CodeStats, assert_code_stats, compare_record
+from parity_util import CodeStats, assert_code_stats, compare_record, degenerate_tile
 
 pytestmark = pytest.mark.gpu
 
@@ -129,3 +129,31 @@ def test_quantize_zero_tile_and_invalid_ids():
     kv.quantize(L, case["k16"], case["v16"], krec, vrec, bad_src, bad_dst)
     torch.cuda.synchronize()
     assert torch.equal(before, krec)
+
+
+@pytest.mark.parametrize("D,kb,vb,mla", [(128, 4, 2, 0), (256, 6, 6, 0), (512, 2, 6, 0), (512, 4, 4, 1)])
+def test_quantize_zero_rows_and_channels(D, kb, vb, mla):
+    """Degenerate tiles: head 0 holds rows that are integer combinations of
+    half of the Sylvester sign patterns (every other rotated channel exactly
+    zero) with every 9th row zero; head 1 random values with every 9th row
+    zero.  A zero row or channel has no spread and keeps its scale."""
+    T = 128
+    w = workload("tiny_d128_k4v2", D=D, T=T, k_bits=kb, v_bits=vb, mla=mla, H=1 if mla else 2,
+                 Hq=16 if mla else 8, L=2 * T, seed=0x3000 + D + kb)
+    case = gpu_case(w)
+    say("quantize degenerate", D, kb, vb, mla)
+    H = case["layout"]["H"]
+    for name in ("k16", "v16"):
+        t = case[name]
+        if t is None:
+            continue
+        host = host_u16(t).copy()
+        for i, sp in enumerate(case["src"].cpu().tolist()):
+            x, _ = degenerate_tile(T, D, seed=1000 * i + D + (name == "v16"))
+            host[sp, 0] = x
+            if H > 1:
+                host[sp, 1, ::9] = 0
+        case[name] = torch.from_numpy(host.view(np.int16)).view(torch.float16).to(device())
+    L, krec, vrec = run_quantize(case)
+    st = check_records(case, krec, vrec, range(case["n_qpages"]))
+    say("codes differing:", st.diff, "of", st.n)

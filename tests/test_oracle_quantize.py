@@ -14,6 +14,7 @@ import pytest
 import scipy.linalg
 
 import oracle
+import parity_util
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -217,3 +218,33 @@ def test_rotation_and_normalization_beat_plain_rtn_on_outliers():
     codes, s, mn, _ = oracle.rtn(X, np.zeros(128), 4)
     e_plain = np.linalg.norm(mn[:, None] + s[:, None] * codes - X) / np.linalg.norm(X)
     assert e_kvarn < 0.5 * e_plain
+
+
+# ------------------------------------------------------- degenerate tiles --
+@pytest.mark.parametrize("D", [128, 512])
+def test_zero_rows_and_channels_keep_their_scales(D):
+    """A token row or a rotated channel that is exactly zero has no spread:
+    its log-scale stays at 0 (column scale 1), its codes are those of W = 0
+    (a zero row: all 0 with S = Zp = 0; a zero channel: the same code as
+    every other zero channel of its row), and every row has the full code
+    range."""
+    T, bits = 128, 4
+    x, keep = parity_util.degenerate_tile(T, D, seed=D)
+    Y = oracle.rotate(x.view(np.float16).astype(np.float64))
+    zc = np.setdiff1d(np.arange(D), keep)
+    assert np.all(Y[:, zc] == 0.0) and np.all(Y[::9] == 0.0)
+    rec, u, lc, lr = oracle.quantize_record(x, bits, 6)
+    codes, S, Z, C = oracle.split_record(rec, T, D, bits)
+    assert np.all(C[zc] == 1.0) and np.all(lc[zc] == 0.0)
+    assert np.all(C[keep] != 1.0)
+    zr = np.zeros(T, bool)
+    zr[::9] = True
+    assert np.all(lr[zr] == 0.0)
+    assert np.all(codes[zr] == 0) and np.all(S[zr] == 0) and np.all(Z[zr] == 0)
+    nz = ~zr
+    qmax = (1 << bits) - 1
+    assert np.all(codes[nz].min(1) == 0) and np.all(codes[nz].max(1) == qmax)
+    assert np.all(codes[nz][:, zc] == codes[nz][:, zc[:1]])
+    # the zero channels read back as 0 up to the row's rounding step
+    W0 = C[zc][None, :] * (S[nz][:, None] * codes[nz][:, zc] + Z[nz][:, None])
+    assert np.all(np.abs(W0) <= 0.5 * S[nz][:, None] * (1 + 1e-2))
