@@ -11,8 +11,8 @@
  *  [R] evermx.com review "KVarN vLLM KV-cache quantization", second paragraph:
  *      per fixed-size KV tile, four stages -- raw fp16 tile, Hadamard rotation
  *      across channels (orthonormal, scores preserved), iterative variance
- *      normalization (Sinkhorn-like alternation of column- and row-wise
- *      standard-deviation normalization in log space), then asymmetric
+ *      normalization (per-channel and per-token spreads equalized in turn,
+ *      Sinkhorn style, on log-scales), then asymmetric
  *      round-to-nearest with the scales folded back in at read time;
  *      preset kvarn_k4v2_g128 = 4-bit keys, 2-bit values, 128-token tiles;
  *      fourth paragraph: MLA latent quantized to int4.
@@ -147,22 +147,25 @@ void orc_hadamard_matrix(int D, double *H)
 void orc_rotate(int T, int D, const double *X, double *Y)
 {
     const double rt = sqrt((double)D);
+    double *S = (double *)malloc(sizeof(double) * (size_t)D * D);  /* +-1 signs, symmetric */
+    for (int k = 0; k < D; k++)
+        for (int j = 0; j < D; j++)
+            S[(int64_t)k * D + j] = (popcount_int((unsigned)(k & j)) & 1) ? -1.0 : 1.0;
     for (int t = 0; t < T; t++) {
         for (int j = 0; j < D; j++) {
             double acc = 0.0;
-            for (int k = 0; k < D; k++) {
-                double x = X[(int64_t)t * D + k];
-                acc += (popcount_int((unsigned)(k & j)) & 1) ? -x : x;
-            }
+            for (int k = 0; k < D; k++)
+                acc += X[(int64_t)t * D + k] * S[(int64_t)j * D + k];
             Y[(int64_t)t * D + j] = acc / rt;
         }
     }
+    free(S);
 }
 
 /* ------------------------------------------------------------------------ */
 /* Stage 3: iterative variance normalization [R ¶2; G "The two schemes"].   */
-/* "Sinkhorn-like alternation of column- and row-wise standard-deviation    */
-/* normalization in log space."  Readings:                                  */
+/* Channel spreads and token spreads are divided out in turn, the scales    */
+/* kept as logarithms, as in Sinkhorn's matrix balancing.  Readings:        */
 /*   - log-scales lr (per token row) and lc (per channel column) start at 0; */
 /*   - the normalized tile is Z_ij = Y_ij * exp(-lr_i - lc_j);              */
 /*   - one iteration = a column step (lc_j += ln sigma of column j of Z)    */
