@@ -451,7 +451,7 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ tile,
     float* icvec = vec + VecShape<D>::PADDED;  // (+-1 per channel) * sqrt(b_j): multiplies y into W
     uint16_t* cvec = reinterpret_cast<uint16_t*>(vec + 2 * VecShape<D>::PADDED);  // fp16 column scales
 
-    const int tid = threadIdx.x;
+    const int tid = tid_x();
     const int lane = tid & 63;
     const int wave = tid >> 6;
     int cg = 0;
@@ -812,8 +812,8 @@ quantize_kernel(const uint16_t* __restrict__ kpool, const uint16_t* __restrict__
     using S = TileShape<D, T>;
     __shared__ __attribute__((aligned(16))) uint8_t smem[S::SMEM];
     __shared__ __attribute__((aligned(16))) float vec[VecShape<D>::FLOATS];
-    const int kind = HASV ? (int)(blockIdx.x & 1u) : 0;
-    const int r = HASV ? (int)(blockIdx.x >> 1) : (int)blockIdx.x;
+    const int kind = HASV ? (int)(wg_x() & 1u) : 0;
+    const int r = HASV ? (int)(wg_x() >> 1) : (int)wg_x();
     const int i = r / H;
     const int h = r - i * H;
     const int sp = src[i];
