@@ -163,8 +163,9 @@ size_t kvarn_decode_workspace_bytes(const kvarn_layout *layout, int32_t batch,
  * need no initialisation and are clobbered.  num_q_heads must be a multiple
  * of H (GQA group 4 here; MLA: 16, 32, 64 or 128).  With head_dim 128
  * (GQA) and with MLA each record pool, n_qpages * H * record bytes, must be
- * below 4 GiB, and with MLA the fp16 pool too (KVARN_EUNSUPPORTED
- * otherwise). */
+ * below 4 GiB, and with MLA the fp16 pool too; GQA takes at most 32767
+ * sequences per call (KVARN_EUNSUPPORTED otherwise).  Negative pool sizes are
+ * KVARN_EINVAL. */
 kvarn_status kvarn_decode_attn(const kvarn_layout *layout, const kvarn_cache *cache,
                                const kvarn_page_table *pages, const void *q, int32_t q_dtype,
                                int32_t num_q_heads, float sm_scale, float *out,

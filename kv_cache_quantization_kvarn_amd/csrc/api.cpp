@@ -128,7 +128,8 @@ kvarn_status kvarn_quantize(const kvarn_layout* layout, const kvarn_cache* cache
         (!layout->mla && (!aligned16(cache->v_fp16) || !aligned16(cache->v_records))))
         return fail(KVARN_EINVAL, "pools must be 16-byte aligned");
     if (cache->n_fpages < 1 || cache->n_qpages < 1) return fail(KVARN_EINVAL, "empty pools");
-    if ((int64_t)n * layout->num_kv_heads > 0x7fffffffLL) return fail(KVARN_EINVAL, "too many pages in one call");
+    if ((int64_t)n * layout->num_kv_heads * (layout->mla ? 1 : 2) > 0x7fffffffLL)
+        return fail(KVARN_EINVAL, "too many pages in one call: pages x heads x (K, V) must fit one grid");
     kvarn::QuantizeArgs a{};
     a.D = layout->head_dim;
     a.T = layout->tile_tokens;
@@ -188,6 +189,11 @@ kvarn_status kvarn_decode_attn(const kvarn_layout* layout, const kvarn_cache* ca
         return fail(KVARN_EUNSUPPORTED, "GQA group %d: this build implements groups of 4 query heads", G);
     }
     if (!cache->k_fp16 || (!layout->mla && !cache->v_fp16)) return fail(KVARN_EINVAL, "fp16 pools are NULL");
+    if (cache->n_qpages < 0 || cache->n_fpages < 0) return fail(KVARN_EINVAL, "negative pool size");
+    // GQA grids carry the sequence (and the fp16 slots of each) in grid z, at most 65535
+    if (!layout->mla && pages->batch > 32767)
+        return fail(KVARN_EUNSUPPORTED, "batch %d: at most 32767 sequences per call", pages->batch);
+    if (H > 65535) return fail(KVARN_EUNSUPPORTED, "num_kv_heads %d: at most 65535", H);
     if (cache->n_qpages > 0 && (!cache->k_records || (!layout->mla && !cache->v_records)))
         return fail(KVARN_EINVAL, "record pools are NULL");
     if (!(sm_scale > 0.f) || sm_scale > 1e30f) return fail(KVARN_EINVAL, "sm_scale must be positive and finite");

@@ -109,3 +109,13 @@ def test_decode_rejects_before_any_device_work():
     assert lib.kvarn_decode_attn(*args(32, None, need)) == kv.KVARN_EWORKSPACE
     assert lib.kvarn_decode_attn(*args(32, ctypes.c_void_p(256), need, qd=7)) == kv.KVARN_EUNSUPPORTED
     assert lib.kvarn_decode_attn(*args(32, ctypes.c_void_p(260), need)) == kv.KVARN_EINVAL
+    # negative pool sizes and batches beyond the grid are refused on the host
+    bad = kv.Cache(ctypes.c_void_p(16), ctypes.c_void_p(16), ctypes.c_void_p(16), ctypes.c_void_p(16), -1, 1)
+    assert lib.kvarn_decode_attn(ctypes.byref(L), ctypes.byref(bad), ctypes.byref(pt), ctypes.c_void_p(16),
+                                 kv.KVARN_F32, 32, ctypes.c_float(0.1), ctypes.c_void_p(16), ctypes.c_void_p(256),
+                                 need, None) == kv.KVARN_EINVAL
+    big = kv.PageTable(ctypes.c_void_p(16), ctypes.c_void_p(16), 40000, 4)
+    assert lib.kvarn_decode_attn(ctypes.byref(L), ctypes.byref(cache), ctypes.byref(big), ctypes.c_void_p(16),
+                                 kv.KVARN_F32, 32, ctypes.c_float(0.1), ctypes.c_void_p(16), ctypes.c_void_p(256),
+                                 1 << 40, None) == kv.KVARN_EUNSUPPORTED
+    assert "32767" in lib.kvarn_last_error().decode()
