@@ -26,9 +26,16 @@ EXTRA = {"quantize_d128.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee",
                               "-mllvm", "-amdgpu-mfma-vgpr-form=1",
                               # loop heads on 64-byte instruction-cache lines (1-2 % on
                               # the D = 128 layers; neutral for D = 256 and 512)
-                              "-falign-loops=64"],
-         "quantize_d256.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee", "-mllvm", "-amdgpu-mfma-vgpr-form=1"],
-         "quantize_d512.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"],
+                              "-falign-loops=64",
+                              # see the note on the scheduler below
+                              "-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
+         # The quantizer is bound by VALU issue and by dependent chains between
+         # its barriers; the iterative ILP scheduler interleaves independent
+         # rows and channels further than the default occupancy-driven one,
+         # at the same occupancy (A/B in one process: 2-6 % on all five layers)
+         "quantize_d256.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee", "-mllvm", "-amdgpu-mfma-vgpr-form=1",
+                               "-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
+         "quantize_d512.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee", "-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
          "decode_gqa.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee", "-mllvm", "-amdgpu-mfma-vgpr-form=1"],
          "decode_mla.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee",
                             # keep MFMA accumulators in ordinary VGPRs: the loop-carried
