@@ -25,7 +25,8 @@ EXTRA = {"quantize_d128.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee",
                               # the rotation's MFMA accumulators stay in ordinary VGPRs
                               "-mllvm", "-amdgpu-mfma-vgpr-form=1",
                               # loop heads on 64-byte instruction-cache lines (1-2 % on
-                              # the D = 128 layers; neutral for D = 256 and 512)
+                              # the D = 128 layers under the default scheduler, neutral
+                              # under the one below and for D = 256 and 512)
                               "-falign-loops=64",
                               # see the note on the scheduler below
                               "-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
