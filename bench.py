@@ -4,29 +4,34 @@ One step = kvarn_quantize over every full page of the cache that leaves the
 fp16 sink and tail (keys and values), then one kvarn_decode_attn step over the
 whole batch reading those records plus the fp16 sink and tail.
 
-Default workload: a dense 8B-like layer -- 32 query / 8 KV heads, head_dim
-128, batch 16, 32768-token context, k4v2 with 128-token tiles, fp16 first 128
-and last 1024 tokens, page size 128, K/V ~ N(0,1) with 1% outlier channels
-x20 (synthetic, seeded).
+Headline workload (the largest single-GPU configuration): a dense 8B-like
+layer with 64-token tiles -- 32 query / 8 KV heads, head_dim 128, batch 64,
+16384-token context, k4v2 (4-bit keys, 2-bit values), 6 normalization
+iterations, fp16 first 128 and last 1024 tokens, page size 64, K/V ~ N(0,1)
+with 4 outlier channels per head x20 (synthetic, seeded).  Exactly --steps
+steps are timed after --warmup untimed ones.
 
 Reported (one JSON line):
-  value     (fp16 bytes consumed by quantize + decode effective bytes) /
-            (quantize time + decode time), GB/s; times from HIP events around
-            each call on the stream the kernels run on, averaged over the
-            timed steps.  L2 and the 256 MB last-level cache are flushed
-            before each call, outside the event pairs, by reading a 1 GiB
-            buffer: the caches then hold clean lines of an unrelated buffer
-            (a fill would leave dirty lines whose write-back lands inside the
-            next timed call).
-  roofline  the quantize kernel (the step's dominant kernel): algorithmic
-            bytes per launch (fp16 read + records written) / launch time,
-            against 8 TB/s HBM.  traffic: HBM bytes per launch from the
-            FETCH_SIZE / WRITE_SIZE counter passes recorded under profiles/
-            for this workload, scaled by a 1 GiB copy's readings; null when
-            the quantize sources differ from the ones profiled.
-  components quantize and decode separately, each as GB/s and % of peak.
+  value      (fp16 bytes consumed by quantize + decode effective bytes) /
+             (median quantize time + median decode time), GB/s; times from
+             HIP events around each call on the stream the kernels run on.
+             L2 and the 256 MB last-level cache are flushed before each call,
+             outside the event pairs, by reading a 1 GiB buffer (a fill would
+             leave dirty lines whose write-back lands inside the next call).
+  roofline   the quantize kernel (the step's dominant kernel): algorithmic
+             bytes per launch (fp16 read + records written) / mean launch
+             time, against 8 TB/s HBM.  traffic: HBM bytes per launch from
+             the FETCH_SIZE / WRITE_SIZE counter passes recorded under
+             profiles/ for this workload, scaled by a 1 GiB copy's readings;
+             null when the quantize sources differ from the ones profiled.
+  components every workload of the suite (the headline one included):
+             quantize under both byte readings (fp16 consumed; fp16 read +
+             records written) and decode, each as GB/s and fraction of HBM
+             peak, median with p10 / p90 of the per-call times; the MLA decode
+             also as a fraction of the fp16 MFMA peak (its roofline).
   cpu_baseline the oracle (plain C, fp64, OpenMP) on a bounded sample of the
-            same workload, same byte formulas.
+             headline workload, same byte formulas; per_core: the oracle on
+             one thread over the one-layer 1024-token case.
 """
 import argparse
 import json
@@ -39,11 +44,16 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0   # dense fp16 / bf16 matrix peak of the MI355X
+HEADLINE = "dense8b_b64_16k_k4v2_g64"
+SUITE = ["tiny_d128_k4v2", "dense8b_b16_32k_k4v2_g128", "dense8b_b64_16k_k4v2_g64", "wide_d256_b8_64k_k6v6",
+         "wide_d512_b8_64k_k6v6", "mla_d512_b32_32k_int4"]
 # sources whose compiled code the recorded counter passes measured
 QUANTIZE_SOURCES = ["kv_cache_quantization_kvarn_amd/build.py"] + [
     "kv_cache_quantization_kvarn_amd/csrc/" + f for f in
     ("kvarn_device.hpp", "kvarn_internal.hpp", "quantize_impl.hpp", "quantize.hip", "quantize_d128.hip",
      "quantize_d256.hip", "quantize_d512.hip")]
+METRIC = "quantize fp16 GB/s + decode-attn effective HBM GB/s, % of MI355X peak"
 
 
 def quantize_source_hash():
@@ -74,11 +84,13 @@ def recorded_traffic(workload):
         return int(fields["traffic_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
-METRIC = "quantize fp16 GB/s + decode-attn effective HBM GB/s, % of MI355X peak"
 
 
 def byte_counts(case):
-    """Algorithmic bytes of one step (the formulas of the design notes)."""
+    """Algorithmic bytes of one step: fp16 consumed by quantize, records
+    written by quantize, decode effective bytes (records + fp16 sink/tail +
+    q + out); and the decode's matrix flops (4 per query head, channel and
+    token: one multiply-add each for the score and the value sum)."""
     lay = case["layout"]
     T, D, H, kb, vb, mla = lay["T"], lay["D"], lay["H"], lay["k_bits"], lay["v_bits"], lay["mla"]
     rec = lambda b: T * D * b // 8 + 4 * T + 2 * D
@@ -86,25 +98,132 @@ def byte_counts(case):
     kinds = [kb] if mla else [kb, vb]
     q_fp16 = nq * H * T * D * 2 * len(kinds)
     q_out = nq * H * sum(rec(b) for b in kinds)
-    # decode: every record of every sequence + fp16 sink/tail tokens + q + out
     seq = case["seq_lens"].cpu().tolist()
     dec = 0
+    flops = 0
     for L in seq:
         nqs = max(0, (L - lay["sink"] - lay["tail"]) // T)
         nf_tok = L - nqs * T
         dec += nqs * H * sum(rec(b) for b in kinds)
         dec += nf_tok * H * D * 2 * len(kinds)
+        flops += 4 * case["Hq"] * D * L
     qbytes = case["q"].numel() * case["q"].element_size()
     dec += qbytes + case["B"] * case["Hq"] * D * 4
-    return q_fp16, q_out, dec
+    return q_fp16, q_out, dec, flops
+
+
+def stats(ts):
+    """median, p10, p90, mean of a list of seconds, in microseconds."""
+    import numpy as np
+
+    a = np.asarray(ts, np.float64) * 1e6
+    return {"median": float(np.median(a)), "p10": float(np.percentile(a, 10)), "p90": float(np.percentile(a, 90)),
+            "mean": float(a.mean())}
+
+
+class Runner:
+    """One workload on the device: pools, records, workspace, and the timed
+    quantize + decode calls."""
+
+    def __init__(self, name, dev):
+        import torch
+
+        import kv_cache_quantization_kvarn_amd as kv
+        from synth.cases import WORKLOADS, make_case
+
+        self.kv, self.torch = kv, torch
+        self.name = name
+        self.w = WORKLOADS[name]
+        self.case = case = make_case(self.w, device=dev)
+        lay = case["layout"]
+        self.L = kv.layout_from_dict(lay)
+        H = lay["H"]
+        nq = max(case["n_qpages"], 1)
+        self.krec = torch.empty((nq, H, kv.record_bytes(self.L, 0)), dtype=torch.uint8, device=dev)
+        self.vrec = None if lay["mla"] else torch.empty((nq, H, kv.record_bytes(self.L, 1)), dtype=torch.uint8,
+                                                        device=dev)
+        self.out = torch.empty((case["B"], case["Hq"], lay["D"]), dtype=torch.float32, device=dev)
+        self.ws = kv.alloc_workspace(self.L, case["B"], case["Hq"], case["max_pages"], dev)
+        self.bytes = byte_counts(case)
+
+    def quantize(self):
+        c = self.case
+        self.kv.quantize(self.L, c["k16"], c["v16"], self.krec, self.vrec, c["src"], c["dst"])
+
+    def decode(self):
+        c = self.case
+        self.kv.decode_attn(self.L, self.krec, self.vrec, c["k16"], c["v16"], c["block_table"], c["seq_lens"],
+                            c["q"], c["sm_scale"], out=self.out, workspace=self.ws)
+
+    def time_steps(self, steps, warmup, flush):
+        """HIP events (on the current stream, where the calls are enqueued)
+        around each call; returns per-step quantize and decode seconds."""
+        torch = self.torch
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+
+        def step():
+            flush()
+            ev[0].record()
+            self.quantize()
+            ev[1].record()
+            flush()
+            ev[2].record()
+            self.decode()
+            ev[3].record()
+
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        tq, td = [], []
+        for _ in range(steps):
+            step()
+            torch.cuda.synchronize()
+            tq.append(ev[0].elapsed_time(ev[1]) * 1e-3)
+            td.append(ev[2].elapsed_time(ev[3]) * 1e-3)
+        return tq, td
+
+    def component(self, tq, td):
+        q_fp16, q_out, dec, flops = self.bytes
+        sq, sd = stats(tq), stats(td)
+        lay = self.case["layout"]
+        r = lambda x, n=2: round(x, n)
+        comp = {
+            "quantize": {"us": r(sq["median"]), "us_p10": r(sq["p10"]), "us_p90": r(sq["p90"]),
+                         "us_mean": r(sq["mean"]),
+                         "fp16_GBs": r(q_fp16 / sq["median"] / 1e3, 1),
+                         "fp16_frac": r(q_fp16 / sq["median"] / 1e3 / HBM_PEAK_GBS, 4),
+                         "traffic_GBs": r((q_fp16 + q_out) / sq["median"] / 1e3, 1),
+                         "traffic_frac": r((q_fp16 + q_out) / sq["median"] / 1e3 / HBM_PEAK_GBS, 4),
+                         "fp16_bytes": q_fp16, "out_bytes": q_out},
+            "decode": {"us": r(sd["median"]), "us_p10": r(sd["p10"]), "us_p90": r(sd["p90"]), "us_mean": r(sd["mean"]),
+                       "GBs": r(dec / sd["median"] / 1e3, 1), "frac": r(dec / sd["median"] / 1e3 / HBM_PEAK_GBS, 4),
+                       "bytes": dec, "flops": flops},
+        }
+        if lay["mla"]:
+            tf = flops / sd["median"] / 1e6
+            comp["decode"]["bound"] = "mfma"
+            comp["decode"]["TFLOPs"] = r(tf, 1)
+            comp["decode"]["mfma_frac"] = r(tf / MFMA_F16_PEAK_TFLOPS, 4)
+        else:
+            comp["decode"]["bound"] = "hbm"
+        if self.name == "tiny_d128_k4v2":
+            comp["note"] = "cache-resident (fits L2 and the last-level cache): parity case, not a bandwidth figure"
+        return comp
+
+    def free(self):
+        del self.case, self.krec, self.vrec, self.out, self.ws
+        self.torch.cuda.empty_cache()
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="dense8b_b16_32k_k4v2_g128")
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--component-steps", type=int, default=20,
+                    help="timed calls per other workload of the suite (0: headline only)")
+    ap.add_argument("--component-warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-records", type=int, default=0,
                     help="records in the oracle's quantize sample (0: every record of the workload)")
@@ -118,77 +237,39 @@ def main():
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: the path has no multi-GPU mode; run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU: the path has no multi-GPU mode (each shard of a multi-GPU "
+              "deployment runs this same single-GPU kernel); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
-
-    import kv_cache_quantization_kvarn_amd as kv
-    from synth.cases import WORKLOADS, make_case
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if args.copy_probe:
         copy_probe(args.steps)
         return
-    w = WORKLOADS[args.workload]
-    print(f"[bench] building {args.workload} on {torch.cuda.get_device_name(dev)}", file=sys.stderr, flush=True)
-    case = make_case(w, device=dev)
-    lay = case["layout"]
-    L = kv.layout_from_dict(lay)
-    H = lay["H"]
-    krec = torch.empty((case["n_qpages"], H, kv.record_bytes(L, 0)), dtype=torch.uint8, device=dev)
-    vrec = None if lay["mla"] else torch.empty((case["n_qpages"], H, kv.record_bytes(L, 1)), dtype=torch.uint8,
-                                               device=dev)
-    out = torch.empty((case["B"], case["Hq"], lay["D"]), dtype=torch.float32, device=dev)
-    ws = kv.alloc_workspace(L, case["B"], case["Hq"], case["max_pages"], dev)
     flush_buf = torch.ones(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
     flush_sink = torch.zeros(1, dtype=torch.float32, device=dev)
 
     def flush():
         flush_sink.add_(flush_buf.sum())
 
-    q_fp16, q_out, dec_bytes = byte_counts(case)
-
-    def quantize():
-        kv.quantize(L, case["k16"], case["v16"], krec, vrec, case["src"], case["dst"])
-
-    def decode():
-        kv.decode_attn(L, krec, vrec, case["k16"], case["v16"], case["block_table"], case["seq_lens"], case["q"],
-                       case["sm_scale"], out=out, workspace=ws)
-
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-
-    def step(timed):
-        flush()
-        ev[0].record()
-        quantize()
-        ev[1].record()
-        flush()
-        ev[2].record()
-        decode()
-        ev[3].record()
-
-    for _ in range(args.warmup):
-        step(False)
+    print(f"[bench] building {args.workload} on {torch.cuda.get_device_name(dev)}", file=sys.stderr, flush=True)
+    run = Runner(args.workload, dev)
     torch.cuda.synchronize()
-    tq, td = [], []
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step(True)
-        torch.cuda.synchronize()
-        tq.append(ev[0].elapsed_time(ev[1]) * 1e-3)
-        td.append(ev[2].elapsed_time(ev[3]) * 1e-3)
+    tq, td = run.time_steps(args.steps, args.warmup, flush)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    print(f"[bench] timed {args.steps} steps", file=sys.stderr, flush=True)
+    print(f"[bench] timed {args.steps} steps of {args.workload}", file=sys.stderr, flush=True)
 
-    tq_m, td_m = float(np.mean(tq)), float(np.mean(td))
-    value = (q_fp16 + dec_bytes) / (tq_m + td_m) / 1e9
-    q_gbs_i = q_fp16 / tq_m / 1e9
-    q_gbs_ii = (q_fp16 + q_out) / tq_m / 1e9
-    d_gbs = dec_bytes / td_m / 1e9
+    q_fp16, q_out, dec_bytes, _ = run.bytes
+    head = run.component(tq, td)
+    sq, sd = stats(tq), stats(td)
+    tq_med, td_med = sq["median"] * 1e-6, sd["median"] * 1e-6
+    value = (q_fp16 + dec_bytes) / (tq_med + td_med) / 1e9
+    ach = (q_fp16 + q_out) / (sq["mean"] * 1e-6) / 1e9
+    case, lay, w = run.case, run.case["layout"], run.w
     res = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -196,32 +277,38 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(wall / args.steps * 1e3, 4),
-        "kernel_ms_per_step": round((tq_m + td_m) * 1e3, 4),
+        "ms_per_step": round(wall / max(args.steps, 1) * 1e3, 4),
+        "kernel_ms_per_step": round((tq_med + td_med) * 1e3, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f16" if lay["mla"] else "f32",
         "data": "synthetic",
         "config": {"workload": args.workload, "batch": case["B"], "context": int(w["L"]), "q_heads": case["Hq"],
-                   "kv_heads": H, "head_dim": lay["D"], "tile_tokens": lay["T"], "k_bits": lay["k_bits"],
+                   "kv_heads": lay["H"], "head_dim": lay["D"], "tile_tokens": lay["T"], "k_bits": lay["k_bits"],
                    "v_bits": None if lay["mla"] else lay["v_bits"], "iters": lay["n_iters"],
                    "sink": lay["sink"], "tail": lay["tail"], "mla": bool(lay["mla"])},
-        "roofline": {"bound": "hbm", "kernel": "quantize_kernel", "achieved": round(q_gbs_ii, 1),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(q_gbs_ii / HBM_PEAK_GBS, 4),
-                     "bytes_per_launch": q_fp16 + q_out, "launch_us": round(tq_m * 1e6, 2),
+        "roofline": {"bound": "hbm", "kernel": "quantize_kernel", "achieved": round(ach, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
+                     "bytes_per_launch": q_fp16 + q_out, "launch_us": round(sq["mean"], 2),
+                     "launch_us_median": round(sq["median"], 2),
                      "traffic": recorded_traffic(args.workload)},
-        "components": {
-            "quantize": {"us": round(tq_m * 1e6, 2), "fp16_GBs": round(q_gbs_i, 1),
-                         "fp16_frac": round(q_gbs_i / HBM_PEAK_GBS, 4), "traffic_GBs": round(q_gbs_ii, 1),
-                         "traffic_frac": round(q_gbs_ii / HBM_PEAK_GBS, 4), "fp16_bytes": q_fp16,
-                         "out_bytes": q_out},
-            "decode": {"us": round(td_m * 1e6, 2), "GBs": round(d_gbs, 1), "frac": round(d_gbs / HBM_PEAK_GBS, 4),
-                       "bytes": dec_bytes},
-        },
+        "components": {args.workload: head},
     }
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(case, krec, vrec, args.cpu_records, args.cpu_rows)
+        res["cpu_baseline"] = cpu_baseline(run.case, run.krec, run.vrec, args.cpu_records, args.cpu_rows)
+        print(f"[bench] oracle timed on the host", file=sys.stderr, flush=True)
+    run.free()
+    del run
+    if args.component_steps > 0:
+        for name in SUITE:
+            if name == args.workload:
+                continue
+            r = Runner(name, dev)
+            tq, td = r.time_steps(args.component_steps, args.component_warmup, flush)
+            res["components"][name] = r.component(tq, td)
+            r.free()
+            print(f"[bench] component {name} done", file=sys.stderr, flush=True)
     print(json.dumps(res), flush=True)
 
 
@@ -246,6 +333,41 @@ def copy_probe(steps):
                       "GBs": round(2 * n / t / 1e9, 1)}), flush=True)
 
 
+def _threads():
+    threads = len(os.sched_getaffinity(0))
+    return min(threads, int(os.environ.get("OMP_NUM_THREADS", threads)))
+
+
+def _oracle_quantize_sample(case, n_records, threads):
+    """The oracle's quantize on the first records of the workload; returns
+    (seconds, fp16 bytes consumed, records)."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    lay = case["layout"]
+    T, D, H, mla = lay["T"], lay["D"], lay["H"], lay["mla"]
+    kinds = 1 if mla else 2
+    if n_records <= 0:
+        n_records = case["n_qpages"] * H * kinds
+    n_pages = max(1, min(case["n_qpages"], math.ceil(n_records / (H * kinds))))
+    src = case["src"][:n_pages].cpu().numpy()
+    pages = np.unique(src)
+    remap = {int(p): i for i, p in enumerate(pages)}
+    idx = torch.as_tensor(pages, device=case["k16"].device).long()
+    k16 = case["k16"][idx].cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+    v16 = None if mla else case["v16"][idx].cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+    s_loc = np.array([remap[int(p)] for p in src], np.int32)
+    d_loc = np.arange(n_pages, dtype=np.int32)
+    rb = lambda b: T * D * b // 8 + 4 * T + 2 * D
+    kr = np.zeros((n_pages, H, rb(lay["k_bits"])), np.uint8)
+    vr = None if mla else np.zeros((n_pages, H, rb(lay["v_bits"])), np.uint8)
+    t0 = time.perf_counter()
+    oracle.quantize_pages(lay, k16, v16, s_loc, d_loc, kr, vr, n_threads=threads)
+    return time.perf_counter() - t0, n_pages * H * T * D * 2 * kinds, n_pages * H * kinds
+
+
 def cpu_baseline(case, krec, vrec, n_records, n_rows):
     """The oracle on a bounded sample of the same workload."""
     import numpy as np
@@ -255,31 +377,10 @@ def cpu_baseline(case, krec, vrec, n_records, n_rows):
 
     lay = case["layout"]
     T, D, H, mla = lay["T"], lay["D"], lay["H"], lay["mla"]
-    threads = len(os.sched_getaffinity(0))
-    threads = min(threads, int(os.environ.get("OMP_NUM_THREADS", threads)))
+    threads = _threads()
     kinds = 1 if mla else 2
-    # quantize: n_records records (pages x heads x K/V) of the workload
-    if n_records <= 0:
-        n_records = case["n_qpages"] * H * kinds
-    n_pages = max(1, min(case["n_qpages"], math.ceil(n_records / (H * kinds))))
-    src = case["src"][:n_pages].cpu().numpy()
-    pages = np.unique(src)
-    remap = {int(p): i for i, p in enumerate(pages)}
-    k16 = case["k16"][torch.as_tensor(pages, device=case["k16"].device).long()].cpu().contiguous()
-    k16 = k16.view(torch.int16).numpy().view(np.uint16)
-    v16 = None
-    if not mla:
-        v16 = case["v16"][torch.as_tensor(pages, device=case["v16"].device).long()].cpu().contiguous()
-        v16 = v16.view(torch.int16).numpy().view(np.uint16)
-    s_loc = np.array([remap[int(p)] for p in src], np.int32)
-    d_loc = np.arange(n_pages, dtype=np.int32)
     rb = lambda b: T * D * b // 8 + 4 * T + 2 * D
-    kr = np.zeros((n_pages, H, rb(lay["k_bits"])), np.uint8)
-    vr = None if mla else np.zeros((n_pages, H, rb(lay["v_bits"])), np.uint8)
-    t0 = time.perf_counter()
-    oracle.quantize_pages(lay, k16, v16, s_loc, d_loc, kr, vr, n_threads=threads)
-    tq = time.perf_counter() - t0
-    qbytes = n_pages * H * T * D * 2 * kinds
+    tq, qbytes, nrec = _oracle_quantize_sample(case, n_records, threads)
     # decode: n_rows (sequence, query head) rows, on the HIP path's records
     rng = np.random.default_rng(5)
     pairs = np.array([(int(rng.integers(case["B"])), int(rng.integers(case["Hq"]))) for _ in range(n_rows)],
@@ -306,11 +407,18 @@ def cpu_baseline(case, krec, vrec, n_records, n_rows):
         nqs = max(0, (Lb - lay["sink"] - lay["tail"]) // T)
         per_head = nqs * (rb(lay["k_bits"]) + (0 if mla else rb(lay["v_bits"]))) + (Lb - nqs * T) * D * 2 * kinds
         dbytes += per_head / G
+    # one core: the oracle's quantize of the one-layer 1024-token case
+    from synth.cases import WORKLOADS, make_case
+
+    tiny = make_case(WORKLOADS["tiny_d128_k4v2"], device="cpu")
+    t1, b1, n1 = _oracle_quantize_sample(tiny, 0, 1)
     return {"value": round((qbytes + dbytes) / (tq + td) / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
             "quantize_GBs": round(qbytes / tq / 1e9, 4), "decode_GBs": round(dbytes / td / 1e9, 4),
             "seconds": round(tq + td, 2),
-            "sample": f"quantize {n_pages * H * kinds} of {case['n_qpages'] * H * kinds} records; decode "
+            "per_core": {"quantize_GBs": round(b1 / t1 / 1e9, 5), "cores": 1,
+                         "sample": f"quantize all {n1} records of the one-layer 1024-token k4v2 case"},
+            "sample": f"quantize {nrec} of {case['n_qpages'] * H * kinds} records; decode "
                       f"{n_rows} of {case['B'] * case['Hq']} (sequence, query head) rows on the GPU's records"}
 
 

@@ -136,9 +136,9 @@ int32_t kvarn_quantized_pages(const kvarn_layout *layout, int32_t seq_len);
  * Y = X H, n_iters column/row normalization steps on Y (root-mean-square
  * statistics), per-token round-to-nearest with scale = range/(2^b - 1) and
  * zero-point = minimum, codes packed as in the record format.
- * src_fpages, dst_qpages: device int32 [n].  The caller guarantees that the
- * source pages are full and committed (the review: a block commits only once
- * all its tokens are accepted) and that dst ids are distinct.  n = 0 is a
+ * src_fpages, dst_qpages: device int32 [n].  The caller passes only pages
+ * that are full and whose every token has been accepted (the commit rule of
+ * the evermx.com review, MLA and hybrid paragraph) and distinct dst ids.  n = 0 is a
  * no-op.  Reads cache->k_fp16/v_fp16, writes cache->k_records/v_records. */
 kvarn_status kvarn_quantize(const kvarn_layout *layout, const kvarn_cache *cache,
                             const int32_t *src_fpages, const int32_t *dst_qpages,

@@ -6,7 +6,7 @@
 // normalization iterations, per-token asymmetric round-to-nearest, packed
 // codes (evermx.com KVarN review, method paragraph: the four stages; gmlx
 // "KV cache quantization", "The two schemes": per-head Hadamard rotation,
-// records scaled so that no token or channel dominates).
+// records whose token and channel spreads are evened out).
 //
 // Register layout: every lane holds R = 4 consecutive tokens x C = 16
 // consecutive channels (64 values).  D/16 lanes share a token row; their

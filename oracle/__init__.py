@@ -56,6 +56,7 @@ def _load():
     lib.orc_quantized_pages.restype = i32
     lib.orc_quantized_pages.argtypes = [P, i32]
     lib.orc_decode.argtypes = [P, P, P, P, P, P, P, i32, P, i32, i32, dbl, P, i32, P, i32]
+    lib.orc_decode_groups.argtypes = [P, P, P, P, P, P, P, i32, P, i32, i32, dbl, P, i32, P, i32]
     _lib = lib
     return lib
 
@@ -221,4 +222,29 @@ def decode(layout, krec, vrec, k16, v16, block_table, seq_lens, q, Hq, sm_scale,
     _load().orc_decode(_p(cfg), _p(krec), _p(vrec), _p(k16), _p(v16), _p(block_table),
                        _p(seq_lens), int(max_pages), _p(q), int(is_bf16), int(Hq),
                        float(sm_scale), _p(pairs), len(pairs), _p(out), int(n_threads))
+    return out.reshape(B, Hq, D) if full else out
+
+
+def decode_groups(layout, krec, vrec, k16, v16, block_table, seq_lens, q, Hq, sm_scale,
+                  groups=None, n_threads=0):
+    """The same definition as decode() for whole (sequence b, KV head g)
+    groups: each group's tokens are read back once and attended by its
+    G = Hq / H query heads.  Returns float64 [B, Hq, D] when groups is None,
+    else [n_groups, G, D]."""
+    cfg = _cfg(layout)
+    block_table = _c(block_table, np.int32)
+    seq_lens = _c(seq_lens, np.int32)
+    B, max_pages = block_table.shape
+    is_bf16 = q.dtype == np.uint16
+    q = np.ascontiguousarray(q)
+    D, H = int(layout["D"]), int(layout["H"])
+    G = Hq // H
+    full = groups is None
+    if full:
+        groups = np.array([(b, g) for b in range(B) for g in range(H)], np.int32)
+    groups = _c(groups, np.int32).reshape(-1, 2)
+    out = np.zeros((len(groups), G, D), np.float64)
+    _load().orc_decode_groups(_p(cfg), _p(krec), _p(vrec), _p(k16), _p(v16), _p(block_table),
+                              _p(seq_lens), int(max_pages), _p(q), int(is_bf16), int(Hq),
+                              float(sm_scale), _p(groups), len(groups), _p(out), int(n_threads))
     return out.reshape(B, Hq, D) if full else out

@@ -450,16 +450,90 @@ int orc_quantized_pages(const int32_t *cfg, int L)
 /* pairs: n_pairs (b, h) pairs; out: [n_pairs][D].                          */
 /* ------------------------------------------------------------------------ */
 
+/* Read back every token t < L of sequence b, KV head g: dequantized record
+ * values (rotated back to the original basis) for pages in the quantized
+ * region, the stored fp16 values for the sink and tail.  Kh, Vh: at least
+ * ceil(L / T) * T * D doubles each. */
+static void read_back(const int32_t *cfg, const uint8_t *krec, const uint8_t *vrec,
+                      const uint16_t *k16, const uint16_t *v16,
+                      const int32_t *block_table, int max_pages, int b, int g, int L,
+                      double *Kh, double *Vh)
+{
+    int T = cfg[C_T], D = cfg[C_D], H = cfg[C_H], mla = cfg[C_MLA];
+    int sink_pages = cfg[C_SINK] / T;
+    int64_t kb = orc_record_bytes(T, D, cfg[C_KB]);
+    int64_t vb = orc_record_bytes(T, D, cfg[C_VB]);
+    int nq = orc_quantized_pages(cfg, L);
+    int npages = (L + T - 1) / T;
+    for (int p = 0; p < npages; p++) {
+        int id = block_table[(int64_t)b * max_pages + p];
+        int quant = (p >= sink_pages) && (p < sink_pages + nq);
+        double *kd = Kh + (int64_t)p * T * D, *vd = Vh + (int64_t)p * T * D;
+        if (quant) {
+            orc_dequantize_record(krec + ((int64_t)id * H + g) * kb, T, D, cfg[C_KB], 0, kd);
+            if (mla)
+                memcpy(vd, kd, sizeof(double) * (size_t)T * D);
+            else
+                orc_dequantize_record(vrec + ((int64_t)id * H + g) * vb, T, D, cfg[C_VB], 1, vd);
+        } else {
+            const uint16_t *ks = k16 + ((int64_t)id * H + g) * T * D;
+            const uint16_t *vs = (mla ? k16 : v16) + ((int64_t)id * H + g) * T * D;
+            for (int64_t e = 0; e < (int64_t)T * D; e++) {
+                kd[e] = orc_half_to_double(ks[e]);
+                vd[e] = orc_half_to_double(vs[e]);
+            }
+        }
+    }
+}
+
+/* The query vector of (b, h), widened exactly to double. */
+static void load_query(const void *q, int q_is_bf16, int Hq, int D, int b, int h, double *qv)
+{
+    for (int j = 0; j < D; j++) {
+        int64_t idx = ((int64_t)b * Hq + h) * D + j;
+        if (q_is_bf16)
+            qv[j] = orc_bf16_to_double(((const uint16_t *)q)[idx]);
+        else
+            qv[j] = (double)((const float *)q)[idx];
+    }
+}
+
+/* out = sum_{t < L} softmax_t(sm_scale * <q, k_t>) v_t, max-subtracted
+ * softmax in double precision; zeros when L = 0. */
+static void attend(const double *qv, const double *Kh, const double *Vh, int L, int D,
+                   double sm_scale, double *out)
+{
+    double *sc = (double *)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
+    double m = -INFINITY;
+    for (int t = 0; t < L; t++) {
+        double acc = 0.0;
+        for (int j = 0; j < D; j++)
+            acc += qv[j] * Kh[(int64_t)t * D + j];
+        sc[t] = sm_scale * acc;
+        if (sc[t] > m)
+            m = sc[t];
+    }
+    double l = 0.0;
+    for (int t = 0; t < L; t++) {
+        sc[t] = exp(sc[t] - m);
+        l += sc[t];
+    }
+    for (int j = 0; j < D; j++) {
+        double acc = 0.0;
+        for (int t = 0; t < L; t++)
+            acc += sc[t] * Vh[(int64_t)t * D + j];
+        out[j] = L > 0 ? acc / l : 0.0;
+    }
+    free(sc);
+}
+
 int orc_decode(const int32_t *cfg, const uint8_t *krec, const uint8_t *vrec,
                const uint16_t *k16, const uint16_t *v16,
                const int32_t *block_table, const int32_t *seq_lens, int max_pages,
                const void *q, int q_is_bf16, int Hq, double sm_scale,
                const int32_t *pairs, int n_pairs, double *out, int n_threads)
 {
-    int T = cfg[C_T], D = cfg[C_D], H = cfg[C_H], mla = cfg[C_MLA];
-    int sink_pages = cfg[C_SINK] / T;
-    int64_t kb = orc_record_bytes(T, D, cfg[C_KB]);
-    int64_t vb = orc_record_bytes(T, D, cfg[C_VB]);
+    int T = cfg[C_T], D = cfg[C_D], H = cfg[C_H];
     int G = Hq / H;
 #ifdef _OPENMP
     if (n_threads > 0)
@@ -468,61 +542,49 @@ int orc_decode(const int32_t *cfg, const uint8_t *krec, const uint8_t *vrec,
 #endif
     for (int pi = 0; pi < n_pairs; pi++) {
         int b = pairs[2 * pi], h = pairs[2 * pi + 1];
-        int g = h / G;
         int L = seq_lens[b];
-        int nq = orc_quantized_pages(cfg, L);
         int npages = (L + T - 1) / T;
         double *qv = (double *)malloc(sizeof(double) * D);
-        for (int j = 0; j < D; j++) {
-            int64_t idx = ((int64_t)b * Hq + h) * D + j;
-            if (q_is_bf16)
-                qv[j] = orc_bf16_to_double(((const uint16_t *)q)[idx]);
-            else
-                qv[j] = (double)((const float *)q)[idx];
-        }
         double *Kh = (double *)malloc(sizeof(double) * (size_t)npages * T * D + 8);
         double *Vh = (double *)malloc(sizeof(double) * (size_t)npages * T * D + 8);
-        for (int p = 0; p < npages; p++) {
-            int id = block_table[(int64_t)b * max_pages + p];
-            int quant = (p >= sink_pages) && (p < sink_pages + nq);
-            double *kd = Kh + (int64_t)p * T * D, *vd = Vh + (int64_t)p * T * D;
-            if (quant) {
-                orc_dequantize_record(krec + ((int64_t)id * H + g) * kb, T, D, cfg[C_KB], 0, kd);
-                if (mla)
-                    memcpy(vd, kd, sizeof(double) * (size_t)T * D);
-                else
-                    orc_dequantize_record(vrec + ((int64_t)id * H + g) * vb, T, D, cfg[C_VB], 1, vd);
-            } else {
-                const uint16_t *ks = k16 + ((int64_t)id * H + g) * T * D;
-                const uint16_t *vs = (mla ? k16 : v16) + ((int64_t)id * H + g) * T * D;
-                for (int64_t e = 0; e < (int64_t)T * D; e++) {
-                    kd[e] = orc_half_to_double(ks[e]);
-                    vd[e] = orc_half_to_double(vs[e]);
-                }
-            }
+        load_query(q, q_is_bf16, Hq, D, b, h, qv);
+        read_back(cfg, krec, vrec, k16, v16, block_table, max_pages, b, h / G, L, Kh, Vh);
+        attend(qv, Kh, Vh, L, D, sm_scale, out + (int64_t)pi * D);
+        free(qv); free(Kh); free(Vh);
+    }
+    return 0;
+}
+
+/* The same definition for whole query-head groups: for each requested
+ * (b, g) the tokens of KV head g are read back once and attended by each of
+ * its G = Hq / H query heads h = g G .. g G + G - 1.
+ * groups: n_groups (b, g) pairs; out: [n_groups][G][D]. */
+int orc_decode_groups(const int32_t *cfg, const uint8_t *krec, const uint8_t *vrec,
+                      const uint16_t *k16, const uint16_t *v16,
+                      const int32_t *block_table, const int32_t *seq_lens, int max_pages,
+                      const void *q, int q_is_bf16, int Hq, double sm_scale,
+                      const int32_t *groups, int n_groups, double *out, int n_threads)
+{
+    int T = cfg[C_T], D = cfg[C_D], H = cfg[C_H];
+    int G = Hq / H;
+#ifdef _OPENMP
+    if (n_threads > 0)
+        omp_set_num_threads(n_threads);
+#pragma omp parallel for schedule(dynamic, 1)
+#endif
+    for (int gi = 0; gi < n_groups; gi++) {
+        int b = groups[2 * gi], g = groups[2 * gi + 1];
+        int L = seq_lens[b];
+        int npages = (L + T - 1) / T;
+        double *qv = (double *)malloc(sizeof(double) * D);
+        double *Kh = (double *)malloc(sizeof(double) * (size_t)npages * T * D + 8);
+        double *Vh = (double *)malloc(sizeof(double) * (size_t)npages * T * D + 8);
+        read_back(cfg, krec, vrec, k16, v16, block_table, max_pages, b, g, L, Kh, Vh);
+        for (int k = 0; k < G; k++) {
+            load_query(q, q_is_bf16, Hq, D, b, g * G + k, qv);
+            attend(qv, Kh, Vh, L, D, sm_scale, out + ((int64_t)gi * G + k) * D);
         }
-        double *sc = (double *)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
-        double m = -INFINITY;
-        for (int t = 0; t < L; t++) {
-            double acc = 0.0;
-            for (int j = 0; j < D; j++)
-                acc += qv[j] * Kh[(int64_t)t * D + j];
-            sc[t] = sm_scale * acc;
-            if (sc[t] > m)
-                m = sc[t];
-        }
-        double l = 0.0;
-        for (int t = 0; t < L; t++) {
-            sc[t] = exp(sc[t] - m);
-            l += sc[t];
-        }
-        for (int j = 0; j < D; j++) {
-            double acc = 0.0;
-            for (int t = 0; t < L; t++)
-                acc += sc[t] * Vh[(int64_t)t * D + j];
-            out[(int64_t)pi * D + j] = L > 0 ? acc / l : 0.0;
-        }
-        free(qv); free(Kh); free(Vh); free(sc);
+        free(qv); free(Kh); free(Vh);
     }
     return 0;
 }

@@ -83,3 +83,30 @@ def degenerate_tile(T, D, seed, zero_rows=9):
     x[::zero_rows] = 0
     assert np.abs(x).max() <= 2 * D
     return x.astype(np.float16).view(np.uint16), keep
+
+
+def cancelling_tile(T, D, seed, hi_exp, lo_exp):
+    """fp16 tile (uint16 bits, [T, D]) whose exact rotation has channel 0 equal
+    to zero in every row while the row's entries span exponents lo_exp ..
+    hi_exp: row t holds s*2^hi at channel a, s*k*2^lo at b, -s*(2^hi - m) at c,
+    -s*m at d and -s*k*2^lo at e (five distinct channels, random per row,
+    s = +-1, k in 1..3, m = 2^(hi - 10)), so its plain sum is exactly 0.  With
+    hi_exp - lo_exp below 24 every partial sum of a row is exact in float32;
+    above, a float32 rotation can round the small entries away in one partial
+    sum and not in another."""
+    rng = np.random.default_rng(seed)
+    x = np.zeros((T, D), np.float64)
+    m = 2.0 ** (hi_exp - 10)
+    for t in range(T):
+        a, b, c, d, e = rng.choice(D, 5, replace=False)
+        s = 1.0 if rng.integers(2) else -1.0
+        k = float(rng.integers(1, 4))
+        x[t, a] = s * 2.0 ** hi_exp
+        x[t, b] = s * k * 2.0 ** lo_exp
+        x[t, c] = -s * (2.0 ** hi_exp - m)
+        x[t, d] = -s * m
+        x[t, e] = -s * k * 2.0 ** lo_exp
+    h = x.astype(np.float16)
+    assert np.array_equal(h.astype(np.float64), x), "entries must be exact in fp16"
+    assert np.all(x.sum(axis=1) == 0.0)
+    return h.view(np.uint16)

@@ -76,23 +76,58 @@ def test_decode_zero_query_is_mean_of_values():
     check(case, out, krec, vrec)
 
 
-FULL = ["dense8b_b16_32k_k4v2_g128", "dense8b_b64_16k_k4v2_g64", "wide_d256_b8_64k_k6v6",
-        "wide_d512_b8_64k_k6v6"]
+FULL_ALL_ROWS = ["dense8b_b16_32k_k4v2_g128"]
+FULL_SAMPLED = ["dense8b_b64_16k_k4v2_g64", "wide_d256_b8_64k_k6v6", "wide_d512_b8_64k_k6v6"]
 
 
-@pytest.mark.parametrize("name", FULL)
-def test_decode_full_size_sampled(name):
+def check_groups(case, out, krec, vrec, groups, name):
+    """Every query head of each (sequence, KV head) group against the
+    oracle's plain attention over the HIP path's records."""
+    from gpu_util import host_q, host_u16
+    import oracle
+
+    H = case["layout"]["H"]
+    G = case["Hq"] // H
+    ref = oracle.decode_groups(case["layout"], krec.cpu().numpy(), None if vrec is None else vrec.cpu().numpy(),
+                               host_u16(case["k16"]), host_u16(case["v16"]), case["block_table"].cpu().numpy(),
+                               case["seq_lens"].cpu().numpy(), host_q(case["q"]), case["Hq"], case["sm_scale"],
+                               groups=groups)
+    o = out.cpu().numpy().astype(np.float64)
+    got = np.stack([o[b, g * G:(g + 1) * G] for b, g in groups])
+    err, where = decode_rel_err(got, ref)
+    say(f"[parity] {name}: decode worst rel err {err:.3e} over {got.shape[0] * got.shape[1]} rows "
+        f"(row {where}); bar {DECODE_RTOL}")
+    assert err <= DECODE_RTOL
+    return err
+
+
+@pytest.mark.parametrize("name", FULL_ALL_ROWS)
+def test_decode_full_size_every_row(name):
     case = gpu_case(workload(name))
-    say("decode full", name)
+    say("decode full, every row:", name)
+    L, krec, vrec = run_quantize(case)
+    out = run_decode(case, L, krec, vrec)
+    o = out.cpu().numpy()
+    assert np.all(np.isfinite(o))
+    H = case["layout"]["H"]
+    groups = np.array([(b, g) for b in range(case["B"]) for g in range(H)], np.int32)
+    check_groups(case, out, krec, vrec, groups, name)
+
+
+@pytest.mark.parametrize("name", FULL_SAMPLED)
+def test_decode_full_size_sampled(name):
+    """Every query head of four sequences (the last one included)."""
+    case = gpu_case(workload(name))
+    say("decode full, sampled sequences:", name)
     L, krec, vrec = run_quantize(case)
     out = run_decode(case, L, krec, vrec)
     o = out.cpu().numpy()
     assert np.all(np.isfinite(o))
     rng = np.random.default_rng(11)
-    B, Hq = case["B"], case["Hq"]
-    pairs = np.array([(int(rng.integers(B)), int(rng.integers(Hq))) for _ in range(3)] + [(B - 1, Hq - 1)],
-                     np.int32)
-    check(case, out, krec, vrec, pairs)
+    B, H = case["B"], case["layout"]["H"]
+    seqs = sorted(set(rng.choice(B - 1, 3, replace=False).tolist()) | {B - 1})
+    groups = np.array([(b, g) for b in seqs for g in range(H)], np.int32)
+    check_groups(case, out, krec, vrec, groups, name)
 
 
 MLA_SHAPES = [
@@ -121,12 +156,93 @@ def test_decode_mla_shapes(Hq, T, lens, sink, tail):
     check(case, out, krec, None, pairs)
 
 
-def test_decode_mla_full_size_sampled():
+def test_decode_mla_full_size_every_row():
     case = gpu_case(workload("mla_d512_b32_32k_int4"))
-    say("decode full mla")
+    say("decode full mla, every row")
     L, krec, vrec = run_quantize(case)
     out = run_decode(case, L, krec, vrec)
     o = out.cpu().numpy()
     assert np.all(np.isfinite(o))
-    pairs = np.array([(3, 5), (17, 100), (31, 127)], np.int32)
-    check(case, out, krec, None, pairs)
+    groups = np.array([(b, 0) for b in range(case["B"])], np.int32)
+    check_groups(case, out, krec, None, groups, "mla_d512_b32_32k_int4")
+
+
+# every pair of key and value widths at each head dim, on short sequences
+WIDTHS = (2, 4, 6)
+
+
+@pytest.mark.parametrize("D", [128, 256, 512])
+@pytest.mark.parametrize("kb", WIDTHS)
+@pytest.mark.parametrize("vb", WIDTHS)
+def test_decode_width_pairs(D, kb, vb):
+    T = 64 if (kb + vb) % 4 == 0 else 128
+    w = workload("wide_d256_b8_64k_k6v6", D=D, T=T, k_bits=kb, v_bits=vb, Hq=8, H=2, L=1100, sink=T, tail=100,
+                 dist="normal", outliers=("per_head", 4), seed=0x4100 + D + 10 * kb + vb)
+    case = gpu_case(w, seq_lens=[1100, 421], batch=2)
+    say("decode widths", D, T, kb, vb)
+    L, krec, vrec = run_quantize(case)
+    out = run_decode(case, L, krec, vrec)
+    check(case, out, krec, vrec)
+
+
+@pytest.mark.parametrize("D", [128, 256, 512])
+def test_decode_bf16_queries(D):
+    w = workload("wide_d256_b8_64k_k6v6", D=D, T=128, k_bits=4, v_bits=2, Hq=8, H=2, L=1500, sink=128, tail=256,
+                 dist="normal", outliers=("per_head", 4), q_dtype="bf16", seed=0x4200 + D)
+    case = gpu_case(w, seq_lens=[1500, 700, 1], batch=3)
+    assert case["q"].dtype == torch.bfloat16
+    say("decode bf16 queries", D)
+    L, krec, vrec = run_quantize(case)
+    out = run_decode(case, L, krec, vrec)
+    check(case, out, krec, vrec)
+
+
+def _read_back(case, rec, b, h, t, which):
+    """Read-back key (which = 0) or value (1) of token t for query head h of
+    sequence b: the dequantized record row rotated back to the original
+    basis in the quantized region, the stored fp16 value elsewhere."""
+    import oracle
+    from gpu_util import host_u16
+
+    lay = case["layout"]
+    T, D, H = lay["T"], lay["D"], lay["H"]
+    g = h // (case["Hq"] // H)
+    p = t // T
+    pid = int(case["block_table"][b, p])
+    nq = oracle.quantized_pages(lay, int(case["seq_lens"][b]))
+    if lay["sink"] // T <= p < lay["sink"] // T + nq:
+        bits = lay["k_bits"] if which == 0 or lay["mla"] else lay["v_bits"]
+        cm = which == 1 and not lay["mla"]
+        return oracle.dequantize_record(rec[pid, g].cpu().numpy(), T, D, bits, channel_major=cm)[t % T]
+    pool = case["k16"] if which == 0 or lay["mla"] else case["v16"]
+    return host_u16(pool[pid, g]).view(np.float16).astype(np.float64)[t % T]
+
+
+@pytest.mark.parametrize("mla", [0, 1])
+def test_decode_dominating_score(mla):
+    """One token's score exceeds every other by tens: the output is that
+    token's read-back value (a quantized token for one head, an fp16 tail
+    token for another, a sink-adjacent quantized token for a third)."""
+    name = "mla_d512_b32_32k_int4" if mla else "tiny_d128_k4v2"
+    # no outlier channels: keys then share no large common component, and
+    # every other token scores tens below the aimed one
+    w = workload(name, L=1500, sink=128, tail=256, outliers=None, seed=0x4300 + mla)
+    case = gpu_case(w, seq_lens=[1500, 900], batch=2)
+    say("decode dominating score, mla =", mla)
+    L, krec, vrec = run_quantize(case)
+    hq = case["Hq"]
+    aims = [(0, 5, 700), (0, 77 if mla else 9, 1300), (1, hq - 1, 140)]
+    q = case["q"].clone()
+    for b, h, t in aims:
+        k = _read_back(case, krec, b, h, t, 0)
+        # score on token t: 60 (sm_scale included)
+        q[b, h] = torch.tensor(60.0 / case["sm_scale"] * k / np.dot(k, k), dtype=q.dtype)
+    case["q"] = q
+    out = run_decode(case, L, krec, vrec)
+    check(case, out, krec, vrec)
+    for b, h, t in aims:
+        v = _read_back(case, krec if mla else vrec, b, h, t, 1)
+        got = out[b, h].cpu().numpy().astype(np.float64)
+        err = np.abs(got - v).max() / np.abs(v).max()
+        say("dominating token", b, h, t, f"rel err vs its read-back value {err:.2e}")
+        assert err <= DECODE_RTOL

@@ -9,7 +9,7 @@ import pytest
 import torch
 
 from gpu_util import device, gpu_case, host_u16, run_quantize, say, workload
-from parity_util import CodeStats, assert_code_stats, compare_record, degenerate_tile
+from parity_util import CodeStats, assert_code_stats, cancelling_tile, compare_record, degenerate_tile
 
 pytestmark = pytest.mark.gpu
 
@@ -78,16 +78,34 @@ FULL = ["dense8b_b16_32k_k4v2_g128", "dense8b_b64_16k_k4v2_g64", "wide_d256_b8_6
 
 @pytest.mark.parametrize("name", FULL)
 def test_quantize_full_size_sampled(name):
+    """Every head of 32 sampled pages (and the pool's last page) of the full
+    workload, quantized in the launch the benchmark times."""
     case = gpu_case(workload(name))
     say("quantize full", name, case["n_qpages"], "pages")
     L, krec, vrec = run_quantize(case)
     rng = np.random.default_rng(7)
-    idx = rng.choice(case["n_qpages"], 6, replace=False)
-    H = case["layout"]["H"]
-    heads = sorted(set(rng.integers(0, H, 2).tolist()))
-    check_records(case, krec, vrec, idx, heads)
-    # last page too (end of the pool)
-    check_records(case, krec, vrec, [case["n_qpages"] - 1], [H - 1])
+    idx = sorted(set(rng.choice(case["n_qpages"], 32, replace=False).tolist()) | {case["n_qpages"] - 1})
+    st = check_records(case, krec, vrec, idx)
+    say(f"[parity] {name}: {st.diff} of {st.n} codes differ by one at a rounding boundary "
+        f"({st.frac():.2e}; bar 1e-4)")
+
+
+WIDTHS = (2, 4, 6)
+
+
+@pytest.mark.parametrize("D", [128, 256, 512])
+@pytest.mark.parametrize("kb", WIDTHS)
+@pytest.mark.parametrize("vb", WIDTHS)
+def test_quantize_width_pairs(D, kb, vb):
+    """Every pair of key and value widths at each head dim (128- and 64-token
+    tiles alternate over the pairs)."""
+    T = 64 if (kb + vb) % 4 == 0 else 128
+    w = workload("tiny_d128_k4v2", D=D, T=T, k_bits=kb, v_bits=vb, H=2, Hq=8, L=2 * T, dist="t3",
+                 outliers=("per_head", 4), permute=True, seed=0x2100 + D + 10 * kb + vb)
+    case = gpu_case(w, batch=2)
+    say("quantize widths", D, T, kb, vb)
+    L, krec, vrec = run_quantize(case)
+    check_records(case, krec, vrec, range(case["n_qpages"]))
 
 
 def test_quantize_deterministic_and_scale_equivariant():
@@ -157,3 +175,38 @@ def test_quantize_zero_rows_and_channels(D, kb, vb, mla):
     L, krec, vrec = run_quantize(case)
     st = check_records(case, krec, vrec, range(case["n_qpages"]))
     say("codes differing:", st.diff, "of", st.n)
+
+
+@pytest.mark.parametrize("D,kb,vb,mla", [(128, 4, 2, 0), (256, 6, 6, 0), (512, 4, 2, 0), (512, 4, 4, 1)])
+def test_quantize_cancelling_channel_within_float32(D, kb, vb, mla):
+    """Tiles whose exact rotation is zero in channel 0 of every row, with
+    entries spanning 2^-4 .. 2^9: every partial sum of a row is exact in
+    float32, so the kernel's rotation cancels that channel exactly, the
+    zero column keeps its scale (C = 1) and its codes match the oracle's."""
+    T = 128
+    w = workload("tiny_d128_k4v2", D=D, T=T, k_bits=kb, v_bits=vb, mla=mla, H=1 if mla else 2,
+                 Hq=16 if mla else 8, L=2 * T, seed=0x3100 + D + kb)
+    case = gpu_case(w)
+    say("quantize cancelling channel", D, kb, vb, mla)
+    H = case["layout"]["H"]
+    for name in ("k16", "v16"):
+        t = case[name]
+        if t is None:
+            continue
+        host = host_u16(t).copy()
+        for i, sp in enumerate(case["src"].cpu().tolist()):
+            for h in range(H):
+                host[sp, h] = cancelling_tile(T, D, seed=100 * i + 10 * h + (name == "v16"), hi_exp=9, lo_exp=-4)
+        case[name] = torch.from_numpy(host.view(np.int16)).view(torch.float16).to(device())
+    L, krec, vrec = run_quantize(case)
+    st = check_records(case, krec, vrec, range(case["n_qpages"]))
+    say("codes differing:", st.diff, "of", st.n)
+    # channel 0's column scale stays exactly 1
+    import oracle
+    for rec, bits, cm in ((krec, kb, False), (vrec, vb, True)):
+        if rec is None:
+            continue
+        for dp in case["dst"].cpu().tolist():
+            for h in range(H):
+                _, _, _, C = oracle.split_record(rec[dp, h].cpu().numpy(), T, D, bits, cm)
+                assert C[0] == 1.0

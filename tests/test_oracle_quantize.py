@@ -66,6 +66,32 @@ def test_rotation_preserves_scores_and_is_self_inverse(D):
     assert np.allclose(oracle.rotate(e0), 1.0 / np.sqrt(D), rtol=0, atol=1e-15)
 
 
+@pytest.mark.parametrize("D", [128, 256, 512])
+def test_rotation_is_the_natural_order_matrix_product(D):
+    """Y = X . H_D with H_D the natural-order Sylvester matrix (scipy's
+    hadamard, scaled by 1/sqrt(D)); a sequency- or Walsh-ordered matrix would
+    preserve scores and be self-inverse too, but fails this."""
+    rng = np.random.default_rng(100 + D)
+    X = rng.standard_normal((7, D)).astype(np.float16).astype(np.float64)
+    ref = X @ (scipy.linalg.hadamard(D).astype(np.float64) / np.sqrt(D))
+    assert np.abs(oracle.rotate(X) - ref).max() < 1e-12
+    # each basis vector e_k maps to row k of the matrix
+    E = np.eye(D)[[0, 1, 5, D // 2 + 3, D - 1]]
+    assert np.abs(oracle.rotate(E) - scipy.linalg.hadamard(D)[[0, 1, 5, D // 2 + 3, D - 1]] / np.sqrt(D)).max() < 1e-15
+
+
+@pytest.mark.parametrize("L,T,nq", [(32768, 128, 247), (16384, 64, 238), (65536, 128, 503), (1279, 128, 0),
+                                    (1280, 128, 1), (1152, 128, 0), (0, 128, 0), (1407, 128, 1), (1408, 128, 2),
+                                    (1216, 64, 1), (1215, 64, 0)])
+def test_quantized_page_counts_of_the_workloads(L, T, nq):
+    """Region rule with the gmlx defaults (fp16 first 128 and newest 1024
+    tokens, "The two schemes"): whole pages after the sink, leaving at least
+    the tail.  The 16 x 32K, 64 x 16K (g64) and 64K-context layers quantize
+    247, 238 and 503 pages of each sequence."""
+    lay = dict(T=T, D=128, k_bits=4, v_bits=2, n_iters=6, sink=128, tail=1024, H=8, mla=0)
+    assert oracle.quantized_pages(lay, L) == nq
+
+
 # ------------------------------------------------------------ normalization --
 def _sinkhorn_knopp(A, n):
     """Textbook Sinkhorn-Knopp scaling, columns first, to unit means.
