@@ -242,8 +242,8 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
 
     // ---- score waves: scores, softmax and weights of chunk seq, held in yb
     // (32 tokens from sequence position tok0; positions past the sequence end
-    // get weight 0).  Sets rescale_flag[seq % 3] when a running maximum
-    // moves. ----
+    // get weight 0).  Sets bit `wave` of rescale_flag[seq % 3] when a
+    // running maximum of its head block moves. ----
     auto score = [&](const uint8_t* yb, int tok0, int seq) {
         // 32 k-steps (token half th = k >> 4, channels 32 (k & 15) ..), the B
         // operand loaded PF steps ahead; two accumulation chains per half
@@ -297,7 +297,9 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
                 mu[i] = mn;
                 if (l16 == 0) alpha[seq & 1][16 * wave + 4 * g4 + i] = al;
             }
-            if (lane == 0) atomicOr(&rescale_flag[seq % 3], 1);
+            // one bit per head block: only the blocks whose wave wrote new
+            // factors are rescaled (the others' factor slots are stale)
+            if (lane == 0) atomicOr(&rescale_flag[seq % 3], 1 << wave);
         }
         float mf[4];
 #pragma unroll
@@ -319,15 +321,18 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
     // (after its weights are in pbuf[seq & 1]); clears the flag of chunk
     // seq + 2, which no wave reads or sets before the next barrier ----
     auto accumulate = [&](const uint8_t* yb, int seq) {
-        if (rescale_flag[seq % 3]) {
+        const int flags = rescale_flag[seq % 3];
+        if (flags) {
 #pragma unroll
-            for (int hb = 0; hb < HB; hb++)
+            for (int hb = 0; hb < HB; hb++) {
+                if (!((flags >> hb) & 1)) continue;
 #pragma unroll
                 for (int i = 0; i < 4; i++) {
                     const float al = alpha[seq & 1][16 * hb + 4 * g4 + i];
 #pragma unroll
                     for (int c = 0; c < CBW; c++) O[hb][c][i] *= al;
                 }
+            }
         }
         if (tid == 0) rescale_flag[(seq + 2) % 3] = 0;
         // tr16: lane 4k + q of a 16-lane group reads row k, columns 4q .. 4q+3;
