@@ -171,6 +171,46 @@ kvarn_status kvarn_decode_attn(const kvarn_layout *layout, const kvarn_cache *ca
                                int32_t num_q_heads, float sm_scale, float *out,
                                void *workspace, size_t workspace_bytes, void *stream);
 
+/* Append n_new tokens to every sequence of the batch: the keys and values
+ * (MLA: latents) of new token i of sequence b go to position seq_lens[b] + i,
+ * i.e. slot (pos % T) of fp16 page block_table[b][pos / T] of the fp16
+ * pools -- always an fp16 page, since the region rule puts every position
+ * at or after seq_lens[b] in the fp16 tail (gmlx "KV cache quantization",
+ * "The two schemes": the newest tokens stay fp16).  seq_lens is read, not
+ * changed: appended tokens count only once kvarn_commit accepts them, and a
+ * later append overwrites tokens that were never accepted.
+ * k_new, v_new: device [batch][n_new][H][D] of dtype (KVARN_F32, KVARN_F16
+ * or KVARN_BF16; converted to fp16 by round to nearest even, values beyond
+ * the fp16 range become infinities), 16-byte aligned; v_new is NULL for MLA.
+ * The caller assigns the block-table entries of pages that receive tokens
+ * (ids of fp16 pages).  A position past max_pages * T or a page id outside
+ * the fp16 pool is skipped.  n_new = 0 is a no-op. */
+kvarn_status kvarn_append(const kvarn_layout *layout, const kvarn_cache *cache,
+                          const kvarn_page_table *pages, const void *k_new, const void *v_new,
+                          int32_t dtype, int32_t n_new, void *stream);
+
+/* Accept n_accept[b] of the appended tokens of every sequence b and keep the
+ * quantized region up to date, all on the device:
+ *   - seq_lens[b] += n_accept[b];
+ *   - when that moves a page out of the fp16 tail (the region rule above:
+ *     whole pages after the sink, leaving at least tail_tokens in fp16), the
+ *     page -- every token of which is now committed, the commit rule of the
+ *     evermx.com review, MLA and hybrid paragraph -- is quantized (as by
+ *     kvarn_quantize) from its fp16 page into record page new_qpages[b], and
+ *     block_table[b][page] is set to new_qpages[b].
+ * promoted_fpages[b] reports, per sequence: the fp16 page id that was
+ * quantized (>= 0; the caller may reuse that fp16 page), -1 nothing
+ * promoted, -2 n_accept[b] outside [0, T] or seq_lens[b] + n_accept[b] past
+ * max_pages * T, -3 the page's fp16 id or new_qpages[b] outside its pool;
+ * on -2 and -3 the sequence's length and block table are left unchanged.
+ * With n_accept[b] <= T at most one page per sequence is due.
+ * block_table [batch][max_pages], seq_lens, n_accept, new_qpages,
+ * promoted_fpages [batch]: device int32, caller-owned; new_qpages ids must
+ * be distinct and unused (an entry not needed this step stays free). */
+kvarn_status kvarn_commit(const kvarn_layout *layout, const kvarn_cache *cache, int32_t *block_table,
+                          int32_t *seq_lens, int32_t batch, int32_t max_pages, const int32_t *n_accept,
+                          const int32_t *new_qpages, int32_t *promoted_fpages, void *stream);
+
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char *kvarn_last_error(void);
 

@@ -18,7 +18,7 @@ KVARN_F32, KVARN_F16, KVARN_BF16 = 0, 1, 2
 
 EXPORTS = ("kvarn_parse_preset", "kvarn_layout_check", "kvarn_record_bytes", "kvarn_quantized_pages",
            "kvarn_quantize", "kvarn_decode_workspace_bytes", "kvarn_decode_attn", "kvarn_last_error",
-           "kvarn_version")
+           "kvarn_version", "kvarn_append", "kvarn_commit")
 
 
 class KvarnError(RuntimeError):
@@ -70,6 +70,10 @@ def lib():
     L.kvarn_decode_workspace_bytes.restype = sz
     L.kvarn_decode_attn.argtypes = [PL, PC, PT, P, i32, i32, ctypes.c_float, P, P, sz, P]
     L.kvarn_decode_attn.restype = i32
+    L.kvarn_append.argtypes = [PL, PC, PT, P, P, i32, i32, P]
+    L.kvarn_append.restype = i32
+    L.kvarn_commit.argtypes = [PL, PC, P, P, i32, i32, P, P, P, P]
+    L.kvarn_commit.restype = i32
     L.kvarn_last_error.argtypes = []
     L.kvarn_last_error.restype = ctypes.c_char_p
     L.kvarn_version.argtypes = []
@@ -162,3 +166,26 @@ def decode_attn(layout, k_records, v_records, k_fp16, v_fp16, block_table, seq_l
     _check(lib().kvarn_decode_attn(ctypes.byref(layout), ctypes.byref(cache), ctypes.byref(pt), _ptr(q), qd, Hq,
                                    float(sm_scale), _ptr(out), _ptr(workspace), workspace.numel(), _stream()))
     return out
+
+
+def append(layout, k_fp16, v_fp16, block_table, seq_lens, k_new, v_new):
+    """kvarn_append on the current stream: k_new / v_new [B, n_new, H, D]
+    (MLA: v_new None) written after each sequence's seq_lens[b] tokens."""
+    B, n_new = int(k_new.shape[0]), int(k_new.shape[1])
+    assert k_new.is_contiguous() and (v_new is None or v_new.is_contiguous())
+    dt = {torch.float32: KVARN_F32, torch.float16: KVARN_F16, torch.bfloat16: KVARN_BF16}[k_new.dtype]
+    cache = make_cache(None, None, k_fp16, v_fp16)
+    pt = PageTable(_ptr(block_table), _ptr(seq_lens), B, int(block_table.shape[1]))
+    _check(lib().kvarn_append(ctypes.byref(layout), ctypes.byref(cache), ctypes.byref(pt), _ptr(k_new), _ptr(v_new),
+                              dt, n_new, _stream()))
+
+
+def commit(layout, k_records, v_records, k_fp16, v_fp16, block_table, seq_lens, n_accept, new_qpages, promoted):
+    """kvarn_commit on the current stream; block_table and seq_lens are
+    updated in place, promoted [B] receives the per-sequence report."""
+    B, max_pages = int(block_table.shape[0]), int(block_table.shape[1])
+    for t in (block_table, seq_lens, n_accept, new_qpages, promoted):
+        assert t.dtype == torch.int32 and t.is_contiguous()
+    cache = make_cache(k_records, v_records, k_fp16, v_fp16)
+    _check(lib().kvarn_commit(ctypes.byref(layout), ctypes.byref(cache), _ptr(block_table), _ptr(seq_lens), B,
+                              max_pages, _ptr(n_accept), _ptr(new_qpages), _ptr(promoted), _stream()))

@@ -65,6 +65,16 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 }  // namespace
 
+namespace kvarn {
+kvarn_status set_error(kvarn_status st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return st;
+}
+}  // namespace kvarn
+
 extern "C" {
 
 kvarn_status kvarn_parse_preset(const char* name, kvarn_layout* out) {
@@ -255,6 +265,96 @@ kvarn_status kvarn_decode_attn(const kvarn_layout* layout, const kvarn_cache* ca
     a.ws = static_cast<float*>(workspace);
     hipError_t e = kvarn::launch_decode(a, (hipStream_t)stream);
     if (e != hipSuccess) return fail(KVARN_EHIP, "decode launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+kvarn_status kvarn_append(const kvarn_layout* layout, const kvarn_cache* cache, const kvarn_page_table* pages,
+                          const void* k_new, const void* v_new, int32_t dtype, int32_t n_new, void* stream) {
+    kvarn_status st = check_layout(layout);
+    if (st != KVARN_OK) return st;
+    if (!cache || !pages) return fail(KVARN_EINVAL, "NULL argument");
+    if (dtype != KVARN_F32 && dtype != KVARN_F16 && dtype != KVARN_BF16)
+        return fail(KVARN_EINVAL, "dtype %d: float32, float16 or bfloat16", dtype);
+    if (n_new < 0) return fail(KVARN_EINVAL, "n_new %d < 0", n_new);
+    if (pages->batch < 1 || pages->max_pages < 1 || !pages->block_table || !pages->seq_lens)
+        return fail(KVARN_EINVAL, "page table: batch and max_pages must be >= 1, arrays non-NULL");
+    if (n_new == 0) return ok();
+    if (!k_new || (!layout->mla && !v_new)) return fail(KVARN_EINVAL, "new key / value arrays are NULL");
+    if (!cache->k_fp16 || (!layout->mla && !cache->v_fp16)) return fail(KVARN_EINVAL, "fp16 pools are NULL");
+    if (!aligned16(k_new) || (!layout->mla && !aligned16(v_new)) || !aligned16(cache->k_fp16) ||
+        (!layout->mla && !aligned16(cache->v_fp16)))
+        return fail(KVARN_EINVAL, "new tokens and fp16 pools must be 16-byte aligned");
+    if (cache->n_fpages < 1) return fail(KVARN_EINVAL, "empty fp16 pool");
+    const int64_t threads = (int64_t)pages->batch * n_new * layout->num_kv_heads * (layout->head_dim / 8);
+    if (threads > ((int64_t)1 << 40)) return fail(KVARN_EINVAL, "too many new values in one call");
+    kvarn::AppendArgs a{};
+    a.D = layout->head_dim;
+    a.T = layout->tile_tokens;
+    a.H = layout->num_kv_heads;
+    a.B = pages->batch;
+    a.n_new = n_new;
+    a.max_pages = pages->max_pages;
+    a.dtype = dtype;
+    a.k_new = k_new;
+    a.v_new = layout->mla ? nullptr : v_new;
+    a.k_fp16 = cache->k_fp16;
+    a.v_fp16 = layout->mla ? nullptr : cache->v_fp16;
+    a.block_table = pages->block_table;
+    a.seq_lens = pages->seq_lens;
+    a.n_fpages = cache->n_fpages;
+    hipError_t e = kvarn::launch_append(a, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(KVARN_EHIP, "append launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+kvarn_status kvarn_commit(const kvarn_layout* layout, const kvarn_cache* cache, int32_t* block_table,
+                          int32_t* seq_lens, int32_t batch, int32_t max_pages, const int32_t* n_accept,
+                          const int32_t* new_qpages, int32_t* promoted_fpages, void* stream) {
+    kvarn_status st = check_layout(layout);
+    if (st != KVARN_OK) return st;
+    if (!cache || !block_table || !seq_lens || !n_accept || !new_qpages || !promoted_fpages)
+        return fail(KVARN_EINVAL, "NULL argument");
+    if (batch < 1 || max_pages < 1) return fail(KVARN_EINVAL, "batch and max_pages must be >= 1");
+    if (!cache->k_fp16 || !cache->k_records || (!layout->mla && (!cache->v_fp16 || !cache->v_records)))
+        return fail(KVARN_EINVAL, "pools are NULL");
+    if (!aligned16(cache->k_fp16) || !aligned16(cache->k_records) ||
+        (!layout->mla && (!aligned16(cache->v_fp16) || !aligned16(cache->v_records))))
+        return fail(KVARN_EINVAL, "pools must be 16-byte aligned");
+    if (cache->n_fpages < 1 || cache->n_qpages < 1) return fail(KVARN_EINVAL, "empty pools");
+    if ((int64_t)batch * layout->num_kv_heads * (layout->mla ? 1 : 2) > 0x7fffffffLL)
+        return fail(KVARN_EINVAL, "batch x heads x (K, V) must fit one grid");
+    kvarn::CommitArgs c{};
+    c.T = layout->tile_tokens;
+    c.sink = layout->sink_tokens;
+    c.tail = layout->tail_tokens;
+    c.B = batch;
+    c.max_pages = max_pages;
+    c.block_table = block_table;
+    c.seq_lens = seq_lens;
+    c.n_accept = n_accept;
+    c.new_qpages = new_qpages;
+    c.promoted = promoted_fpages;
+    c.n_fpages = cache->n_fpages;
+    c.n_qpages = cache->n_qpages;
+    kvarn::QuantizeArgs q{};
+    q.D = layout->head_dim;
+    q.T = layout->tile_tokens;
+    q.k_bits = layout->k_bits;
+    q.v_bits = layout->v_bits;
+    q.n_iters = layout->n_iters;
+    q.H = layout->num_kv_heads;
+    q.mla = layout->mla;
+    q.k_fp16 = cache->k_fp16;
+    q.v_fp16 = cache->v_fp16;
+    q.k_records = cache->k_records;
+    q.v_records = cache->v_records;
+    q.src = promoted_fpages;
+    q.dst = new_qpages;
+    q.n = batch;
+    q.n_fpages = cache->n_fpages;
+    q.n_qpages = cache->n_qpages;
+    hipError_t e = kvarn::launch_commit(c, q, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(KVARN_EHIP, "commit launch failed: %s", hipGetErrorString(e));
     return ok();
 }
 

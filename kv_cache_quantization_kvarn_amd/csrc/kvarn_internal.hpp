@@ -7,6 +7,9 @@
 
 namespace kvarn {
 
+// Record a message for kvarn_last_error() on this thread and return st.
+int32_t set_error(int32_t st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+
 struct QuantizeArgs {
     int D, T, k_bits, v_bits, n_iters, H, mla;
     const void* k_fp16;
@@ -54,6 +57,31 @@ void decode_plan(int D, int H, int G, int mla, int B, int max_pages, int T, int 
 int decode_fp16_slots(int T, int sink, int tail, int max_pages);
 size_t decode_workspace_floats(int D, int Hq, int B, int nsplit, int nfsplit);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
+
+struct AppendArgs {
+    int D, T, H, B, n_new, max_pages, dtype;  // dtype: 0 f32, 1 f16, 2 bf16
+    const void* k_new;
+    const void* v_new;  // NULL for MLA
+    void* k_fp16;
+    void* v_fp16;       // NULL for MLA
+    const int32_t* block_table;
+    const int32_t* seq_lens;
+    int64_t n_fpages;
+};
+hipError_t launch_append(const AppendArgs& a, hipStream_t st);
+
+struct CommitArgs {
+    int T, sink, tail, B, max_pages;
+    int32_t* block_table;
+    int32_t* seq_lens;
+    const int32_t* n_accept;
+    const int32_t* new_qpages;
+    int32_t* promoted;
+    int64_t n_fpages, n_qpages;
+};
+// plan kernel, quantize of the promoted pages (q.src = promoted,
+// q.dst = new_qpages, q.n = B), apply kernel
+hipError_t launch_commit(const CommitArgs& a, const QuantizeArgs& q, hipStream_t st);
 
 // MLA: fp16 rotated queries [B][Hq][512] then split partials [B][Hq][nsplit][516] fp32.
 size_t mla_workspace_floats(int Hq, int B, int nsplit);

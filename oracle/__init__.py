@@ -248,3 +248,40 @@ def decode_groups(layout, krec, vrec, k16, v16, block_table, seq_lens, q, Hq, sm
                               _p(seq_lens), int(max_pages), _p(q), int(is_bf16), int(Hq),
                               float(sm_scale), _p(groups), len(groups), _p(out), int(n_threads))
     return out.reshape(B, Hq, D) if full else out
+
+
+def commit_plan(layout, block_table, seq_lens, n_accept, new_qpages, n_fpages, n_qpages):
+    """What one commit step does to a paged cache, stated per sequence from
+    the region rule: seq_len L grows by the accepted count a (0 <= a <= T and
+    L + a within the page table, else the sequence is left as it was and
+    reported -2); if the rule now places one more page in the quantized
+    region (whole pages after the fp16 sink, leaving at least `tail` tokens
+    in fp16 -- gmlx "KV cache quantization", "The two schemes"), that page,
+    every token of which is committed (evermx.com KVarN review, MLA and
+    hybrid paragraph), is quantized from its fp16 page into record page
+    new_qpages[b], the block table entry is pointed at the record page and
+    the fp16 page id is reported (-3 and no change if either id lies outside
+    its pool); otherwise -1.
+
+    Returns (block_table', seq_lens', promoted) as new arrays."""
+    T, sink = int(layout["T"]), int(layout["sink"])
+    bt = np.array(block_table, np.int32, copy=True)
+    sl = np.array(seq_lens, np.int32, copy=True)
+    B, max_pages = bt.shape
+    promoted = np.full(B, -1, np.int32)
+    for b in range(B):
+        a, L = int(n_accept[b]), int(sl[b])
+        if a < 0 or a > T or L < 0 or L + a > max_pages * T:
+            promoted[b] = -2
+            continue
+        n0, n1 = quantized_pages(layout, L), quantized_pages(layout, L + a)
+        if n1 > n0:
+            p = sink // T + n1 - 1
+            src, dst = int(bt[b, p]), int(new_qpages[b])
+            if not (0 <= src < n_fpages and 0 <= dst < n_qpages):
+                promoted[b] = -3
+                continue
+            promoted[b] = src
+            bt[b, p] = dst
+        sl[b] = L + a
+    return bt, sl, promoted

@@ -183,3 +183,41 @@ def test_mla_latent_serves_as_key_and_value():
     for h in range(4):
         ref = sdpa_reference(K, K, qd[0, h].numpy(), 1 / math.sqrt(512))
         assert np.allclose(out[0, h], ref, rtol=1e-11, atol=1e-12)
+
+
+def _quantized_set(lay, L):
+    """Brute force: the pages whose every token lies after the sink and at
+    least `tail` tokens before the end, counted one page at a time."""
+    T, sink, tail = lay["T"], lay["sink"], lay["tail"]
+    out = set()
+    p = sink // T
+    while (p + 1) * T <= L - tail:
+        out.add(p)
+        p += 1
+    return out
+
+
+@pytest.mark.parametrize("T,sink,tail", [(64, 64, 96), (128, 128, 1024), (64, 0, 0), (128, 0, 5)])
+def test_commit_plan_promotes_exactly_the_pages_entering_the_quantized_region(T, sink, tail):
+    lay = dict(T=T, D=128, k_bits=4, v_bits=2, n_iters=6, sink=sink, tail=tail, H=1, mla=0)
+    rng = np.random.default_rng(T + sink + tail)
+    max_pages = 40
+    B = 64
+    lens = rng.integers(0, max_pages * T - T, B)
+    acc = rng.integers(0, T + 1, B)
+    bt = rng.permutation(B * max_pages).reshape(B, max_pages).astype(np.int32)
+    newq = np.arange(1000, 1000 + B, dtype=np.int32)
+    bt2, sl2, prom = oracle.commit_plan(lay, bt, lens, acc, newq, n_fpages=B * max_pages, n_qpages=2000)
+    for b in range(B):
+        before, after = _quantized_set(lay, lens[b]), _quantized_set(lay, lens[b] + acc[b])
+        new = sorted(after - before)
+        assert before <= after and len(new) <= 1
+        assert sl2[b] == lens[b] + acc[b]
+        if new:
+            assert prom[b] == bt[b, new[0]] and bt2[b, new[0]] == newq[b]
+            assert np.array_equal(np.delete(bt2[b], new[0]), np.delete(bt[b], new[0]))
+        else:
+            assert prom[b] == -1 and np.array_equal(bt2[b], bt[b])
+    # refusals leave the sequence unchanged
+    bad = oracle.commit_plan(lay, bt[:2], [10, 10], [T + 1, -1], newq[:2], B * max_pages, 2000)
+    assert list(bad[2]) == [-2, -2] and list(bad[1]) == [10, 10]
