@@ -23,10 +23,11 @@
  *
  * Conventions of every entry point:
  *   - Pointers marked "device" are HIP device memory; "host" are host memory.
- *   - The library allocates and frees nothing, keeps no device state, and
- *     never synchronizes: work is enqueued on `stream` (a hipStream_t; NULL is
- *     the default stream) and runs asynchronously.  The caller owns every
- *     buffer and keeps it alive until the stream has run the work.
+ *   - The library allocates and frees nothing and never synchronizes: work
+ *     is enqueued on `stream` (a hipStream_t; NULL is the default stream) and
+ *     runs asynchronously.  The caller owns every buffer and keeps it alive
+ *     until the stream has run the work.  The only device state of the
+ *     library is the fixed array of kvarn_decode_attn_noalloc.
  *   - Arguments are validated on the host before anything is enqueued.  A
  *     non-zero status means nothing was enqueued; kvarn_last_error() returns
  *     a message (per calling thread) saying why.  Unsupported shapes return
@@ -210,6 +211,28 @@ kvarn_status kvarn_append(const kvarn_layout *layout, const kvarn_cache *cache,
 kvarn_status kvarn_commit(const kvarn_layout *layout, const kvarn_cache *cache, int32_t *block_table,
                           int32_t *seq_lens, int32_t batch, int32_t max_pages, const int32_t *n_accept,
                           const int32_t *new_qpages, int32_t *promoted_fpages, void *stream);
+
+/* Size of the fixed device array kvarn_decode_attn_noalloc uses as its
+ * workspace: 96 MiB, held on every GPU the library runs on until the
+ * process ends. */
+#define KVARN_NOALLOC_SCRATCH_BYTES ((size_t)96 << 20)
+
+/* kvarn_decode_attn without a workspace argument and without allocating:
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc).  The
+ * split-K partials go to a fixed device array of KVARN_NOALLOC_SCRATCH_BYTES
+ * inside this library instead of a caller buffer; everything else --
+ * arguments, layout, outputs, validation and statuses -- is that of
+ * kvarn_decode_attn, on the current device (the stream must belong to it).
+ * A shape whose workspace (kvarn_decode_workspace_bytes) exceeds the array
+ * returns KVARN_EWORKSPACE and enqueues nothing.  The array's address on a
+ * device is looked up on the first call there (KVARN_EHIP if that fails).
+ * All calls on one GPU share the one array: calls that can overlap on a GPU
+ * (other streams, other threads) race on it and must be ordered by the
+ * caller.  Nothing in it needs clearing between calls. */
+kvarn_status kvarn_decode_attn_noalloc(const kvarn_layout *layout, const kvarn_cache *cache,
+                                       const kvarn_page_table *pages, const void *q, int32_t q_dtype,
+                                       int32_t num_q_heads, float sm_scale, float *out, void *stream);
 
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char *kvarn_last_error(void);

@@ -18,7 +18,7 @@ KVARN_F32, KVARN_F16, KVARN_BF16 = 0, 1, 2
 
 EXPORTS = ("kvarn_parse_preset", "kvarn_layout_check", "kvarn_record_bytes", "kvarn_quantized_pages",
            "kvarn_quantize", "kvarn_decode_workspace_bytes", "kvarn_decode_attn", "kvarn_last_error",
-           "kvarn_version", "kvarn_append", "kvarn_commit")
+           "kvarn_version", "kvarn_decode_attn_noalloc", "kvarn_append", "kvarn_commit")
 
 
 class KvarnError(RuntimeError):
@@ -70,6 +70,8 @@ def lib():
     L.kvarn_decode_workspace_bytes.restype = sz
     L.kvarn_decode_attn.argtypes = [PL, PC, PT, P, i32, i32, ctypes.c_float, P, P, sz, P]
     L.kvarn_decode_attn.restype = i32
+    L.kvarn_decode_attn_noalloc.argtypes = [PL, PC, PT, P, i32, i32, ctypes.c_float, P, P]
+    L.kvarn_decode_attn_noalloc.restype = i32
     L.kvarn_append.argtypes = [PL, PC, PT, P, P, i32, i32, P]
     L.kvarn_append.restype = i32
     L.kvarn_commit.argtypes = [PL, PC, P, P, i32, i32, P, P, P, P]
@@ -165,6 +167,23 @@ def decode_attn(layout, k_records, v_records, k_fp16, v_fp16, block_table, seq_l
     pt = PageTable(_ptr(block_table), _ptr(seq_lens), B, int(block_table.shape[1]))
     _check(lib().kvarn_decode_attn(ctypes.byref(layout), ctypes.byref(cache), ctypes.byref(pt), _ptr(q), qd, Hq,
                                    float(sm_scale), _ptr(out), _ptr(workspace), workspace.numel(), _stream()))
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 96 << 20
+
+
+def decode_attn_noalloc(layout, k_records, v_records, k_fp16, v_fp16, block_table, seq_lens, q, sm_scale, out):
+    """kvarn_decode_attn_noalloc on the current stream: the workspace is the
+    library's fixed device array; out [B, Hq, D] fp32 is caller-provided."""
+    B, Hq, D = q.shape
+    assert block_table.dtype == torch.int32 and seq_lens.dtype == torch.int32
+    assert q.is_contiguous() and block_table.is_contiguous() and out.is_contiguous()
+    qd = {torch.float32: KVARN_F32, torch.bfloat16: KVARN_BF16, torch.float16: KVARN_F16}[q.dtype]
+    cache = make_cache(k_records, v_records, k_fp16, v_fp16)
+    pt = PageTable(_ptr(block_table), _ptr(seq_lens), B, int(block_table.shape[1]))
+    _check(lib().kvarn_decode_attn_noalloc(ctypes.byref(layout), ctypes.byref(cache), ctypes.byref(pt), _ptr(q), qd,
+                                           Hq, float(sm_scale), _ptr(out), _stream()))
     return out
 
 

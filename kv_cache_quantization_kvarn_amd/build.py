@@ -8,7 +8,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkvarn.so")
 SOURCES = ["api.cpp", "quantize.hip", "quantize_d128.hip", "quantize_d256.hip", "quantize_d512.hip",
-           "decode_gqa.hip", "decode_mla.hip", "commit.hip"]
+           "decode_gqa.hip", "decode_mla.hip", "noalloc.hip",
+           "commit.hip"]
 HEADERS = ["kvarn_device.hpp", "kvarn_internal.hpp", "quantize_impl.hpp"]
 
 FLAGS = [
