@@ -84,8 +84,8 @@ typedef int32_t kvarn_status;
 typedef struct kvarn_layout {
     int32_t head_dim;      /* D: 128, 256 or 512 (MLA latent: 512) ("Which layers quantize") */
     int32_t tile_tokens;   /* T = page size: 128 (g128) or 64 (g64) */
-    int32_t k_bits;        /* key code width: 2, 4 or 6 (MLA latent: 4) */
-    int32_t v_bits;        /* value code width: 2, 4 or 6; ignored when mla = 1 */
+    int32_t k_bits;        /* key code width: 2, 3, 4, 5, 6 or 8 (gmlx "The two schemes"; MLA latent: 4) */
+    int32_t v_bits;        /* value code width: 2, 3, 4, 5, 6 or 8; ignored when mla = 1 */
     int32_t n_iters;       /* normalization iterations (column step + row step), 1..32 */
     int32_t sink_tokens;   /* first tokens kept fp16; a multiple of T (default 128) */
     int32_t tail_tokens;   /* newest tokens kept fp16, >= 0 (default 1024) */
@@ -113,7 +113,7 @@ typedef struct kvarn_page_table {
 } kvarn_page_table;
 
 /* Fill *out from a preset name "kvarn_k<kb>v<vb>_g<T>" (e.g. "kvarn_k4v2_g128",
- * "kvarn_k4v2_g64", "kvarn_k6v6_g128"), the flag names of the evermx.com
+ * "kvarn_k4v2_g64", "kvarn_k6v6_g128", "kvarn_k3v5_g64"), the flag names of the evermx.com
  * review ("--kv-cache-dtype kvarn_k4v2_g128"), with n_iters = 6,
  * sink_tokens = 128, tail_tokens = 1024 (gmlx "The two schemes"), mla = 0,
  * and head_dim = num_kv_heads = 0 for the caller to set.  Host-only. */

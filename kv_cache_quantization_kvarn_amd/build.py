@@ -8,9 +8,10 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkvarn.so")
 SOURCES = ["api.cpp", "quantize.hip", "quantize_d128.hip", "quantize_d256.hip", "quantize_d512.hip",
-           "decode_gqa.hip", "decode_mla.hip", "noalloc.hip",
-           "commit.hip"]
-HEADERS = ["kvarn_device.hpp", "kvarn_internal.hpp", "quantize_impl.hpp"]
+           "decode_gqa.hip", "decode_gqa_w128.hip", "decode_gqa_w256.hip", "decode_gqa_w512.hip", "decode_mla.hip",
+           "noalloc.hip", "commit.hip"]
+HEADERS = ["kvarn_device.hpp", "kvarn_internal.hpp", "quantize_impl.hpp", "decode_gqa_impl.hpp",
+           "decode_gqa_wide.hpp"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
@@ -39,6 +40,9 @@ EXTRA = {"quantize_d128.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee",
                                "-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
          "quantize_d512.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee", "-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
          "decode_gqa.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee", "-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+         "decode_gqa_w128.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee", "-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+         "decode_gqa_w256.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee", "-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+         "decode_gqa_w512.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee", "-mllvm", "-amdgpu-mfma-vgpr-form=1"],
          "decode_mla.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee",
                             # keep MFMA accumulators in ordinary VGPRs: the loop-carried
                             # output tile is otherwise copied to and from AGPRs every chunk

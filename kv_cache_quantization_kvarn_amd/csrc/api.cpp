@@ -28,7 +28,8 @@ kvarn_status ok() {
     return KVARN_OK;
 }
 
-bool width_ok(int b) { return b == 2 || b == 4 || b == 6; }
+// code widths of the gmlx documentation, "The two schemes": 2, 3, 4, 5, 6 and 8
+bool width_ok(int b) { return b == 2 || b == 3 || b == 4 || b == 5 || b == 6 || b == 8; }
 
 kvarn_status check_layout(const kvarn_layout* L) {
     if (!L) return fail(KVARN_EINVAL, "layout is NULL");
@@ -39,14 +40,14 @@ kvarn_status check_layout(const kvarn_layout* L) {
         return fail(KVARN_EUNSUPPORTED, "tile_tokens %d: supported tiles are 128 (g128) and 64 (g64)",
                     L->tile_tokens);
     if (L->mla != 0 && L->mla != 1) return fail(KVARN_EINVAL, "mla must be 0 or 1");
-    if (!width_ok(L->k_bits)) return fail(KVARN_EUNSUPPORTED, "k_bits %d: widths 2, 4 and 6 are implemented", L->k_bits);
+    if (!width_ok(L->k_bits)) return fail(KVARN_EUNSUPPORTED, "k_bits %d: widths 2, 3, 4, 5, 6 and 8 are implemented", L->k_bits);
     if (L->mla) {
         if (L->head_dim != 512) return fail(KVARN_EUNSUPPORTED, "mla: the latent width must be 512");
         if (L->k_bits != 4) return fail(KVARN_EUNSUPPORTED, "mla: the latent is quantized to int4 (k_bits 4)");
         if (L->num_kv_heads != 1) return fail(KVARN_EINVAL, "mla: num_kv_heads must be 1");
     } else {
         if (!width_ok(L->v_bits))
-            return fail(KVARN_EUNSUPPORTED, "v_bits %d: widths 2, 4 and 6 are implemented", L->v_bits);
+            return fail(KVARN_EUNSUPPORTED, "v_bits %d: widths 2, 3, 4, 5, 6 and 8 are implemented", L->v_bits);
         if (L->num_kv_heads < 1) return fail(KVARN_EINVAL, "num_kv_heads %d must be >= 1", L->num_kv_heads);
     }
     if (L->n_iters < 1 || L->n_iters > 32) return fail(KVARN_EINVAL, "n_iters %d outside 1..32", L->n_iters);
@@ -84,7 +85,7 @@ kvarn_status kvarn_parse_preset(const char* name, kvarn_layout* out) {
     if (sscanf(name, "kvarn_k%dv%d_g%d%c", &kb, &vb, &t, &tail) != 3)
         return fail(KVARN_EINVAL, "preset '%s' is not of the form kvarn_k<bits>v<bits>_g<tokens>", name);
     if (!width_ok(kb) || !width_ok(vb))
-        return fail(KVARN_EUNSUPPORTED, "preset '%s': widths 2, 4 and 6 are implemented", name);
+        return fail(KVARN_EUNSUPPORTED, "preset '%s': widths 2, 3, 4, 5, 6 and 8 are implemented", name);
     if (t != 128 && t != 64) return fail(KVARN_EUNSUPPORTED, "preset '%s': tiles of 128 or 64 tokens", name);
     memset(out, 0, sizeof(*out));
     out->tile_tokens = t;

@@ -28,6 +28,9 @@ hipError_t launch_quantize(const QuantizeArgs& a, hipStream_t st);
 // explicitly instantiated per head_dim in quantize_d<D>.hip.
 template <int D, int T, int KB, int VB, bool HASV>
 hipError_t launch_quantize_shape(const QuantizeArgs& a, hipStream_t st);
+// Keys (token-major) or values (channel-major) alone, any width 2..8.
+template <int D, int T, int BITS, bool CHMAJOR>
+hipError_t launch_quantize_one(const QuantizeArgs& a, hipStream_t st);
 
 struct DecodeArgs {
     int D, T, k_bits, v_bits, sink, tail, H, mla;
@@ -57,6 +60,10 @@ void decode_plan(int D, int H, int G, int mla, int B, int max_pages, int T, int 
 int decode_fp16_slots(int T, int sink, int tail, int max_pages);
 size_t decode_workspace_floats(int D, int Hq, int B, int nsplit, int nfsplit);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
+// GQA with a code width of 3, 5 or 8: the fp16-MFMA split kernel at any head
+// dim; instantiated per head dim in decode_gqa_w<D>.hip.
+template <int D, int T, int KB, int VB>
+hipError_t launch_gqa_wide(const DecodeArgs& a, hipStream_t st);
 
 struct AppendArgs {
     int D, T, H, B, n_new, max_pages, dtype;  // dtype: 0 f32, 1 f16, 2 bf16

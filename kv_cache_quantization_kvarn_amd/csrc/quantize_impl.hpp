@@ -444,7 +444,12 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ tile,
     constexpr bool KEEP_Y = D <= 128;                  // D = 256, 512 keep y |y| and rebuild y from it
     static_assert(T * D / 64 == NT, "one lane per 64 values");
     static_assert(REC % 16 == 0, "records stay 16-byte aligned");
-    static_assert(CODE_BYTES + 4 * (D / 16) <= S::SMEM_CODES, "the code image and its channel-row pad fit");
+    // widths 2, 4, 6 pack in registers; 3, 5 and 8 go through an image of one
+    // byte per code (record order), which for 8 bits is the record itself
+    constexpr bool BYTE_IMAGE = BITS == 3 || BITS == 5 || BITS == 8;
+    static_assert(BITS == 2 || BITS == 3 || BITS == 4 || BITS == 5 || BITS == 6 || BITS == 8, "code width");
+    static_assert(BYTE_IMAGE || CODE_BYTES + 4 * (D / 16) <= S::SMEM_CODES, "the code image and its channel-row pad fit");
+    static_assert(T * D <= S::SMEM_CODES, "one byte per code fits");
 
     float* colpart = reinterpret_cast<float*>(smem + S::PART_OFF);
     float* bvec = vec;           // b_j = exp(-2 lc_j), unnormalized basis
@@ -686,7 +691,23 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ tile,
     };
     // the statistics are done with the shared buffer (last barrier above);
     // the record's code image reuses it
-    if constexpr (!CHMAJOR) {
+    if constexpr (BYTE_IMAGE) {
+        if constexpr (!CHMAJOR) {
+            // token row t: codes of channels ch0 .. ch0 + 15 at bytes t D + ch0 ..
+#pragma unroll
+            for (int r = 0; r < QR; r++) {
+                const float* x = u[r];
+                *reinterpret_cast<uint4*>(img + (row0 + r) * D + ch0) =
+                    make_uint4(pk4(x[0], x[1], x[2], x[3]), pk4(x[4], x[5], x[6], x[7]), pk4(x[8], x[9], x[10], x[11]),
+                               pk4(x[12], x[13], x[14], x[15]));
+            }
+        } else {
+            // channel row c: codes of tokens row0 .. row0 + 3 at bytes c T + row0 ..
+#pragma unroll
+            for (int c = 0; c < QC; c++)
+                *reinterpret_cast<uint32_t*>(img + (ch0 + c) * T + row0) = pk4(u[0][c], u[1][c], u[2][c], u[3][c]);
+        }
+    } else if constexpr (!CHMAJOR) {
         // token-major: this lane's 16 codes of a row are contiguous
 #pragma unroll
         for (int r = 0; r < QR; r++) {
@@ -775,7 +796,51 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ tile,
     __syncthreads();
 
     // ---- stage 5: the code image leaves in 16-byte stores -------------------
-    {
+    if constexpr (BITS == 3 || BITS == 5) {
+        // every 32 consecutive codes of the byte image become BITS dwords of
+        // the LSB-first stream; all groups are read before any is written back
+        constexpr int NG = T * D / 32;
+        static_assert(NG % NT == 0, "whole groups per thread");
+        constexpr int GPT = NG / NT;
+        constexpr uint32_t M = (1u << BITS) - 1;
+        // 4 codes (bytes of d) -> 4 BITS bits
+        auto pack4 = [](uint32_t d) -> uint32_t {
+            return (d & M) | ((d >> (8 - BITS)) & (M << BITS)) | ((d >> (16 - 2 * BITS)) & (M << (2 * BITS))) |
+                   ((d >> (24 - 3 * BITS)) & (M << (3 * BITS)));
+        };
+        uint32_t words[GPT][BITS];
+#pragma unroll
+        for (int k = 0; k < GPT; k++) {
+            const int g = tid + k * NT;
+            const uint4 a = reinterpret_cast<const uint4*>(img)[2 * g];
+            const uint4 b = reinterpret_cast<const uint4*>(img)[2 * g + 1];
+            const uint32_t d[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+            uint64_t acc = 0;
+            int nb = 0, o = 0;
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                acc |= (uint64_t)pack4(d[i]) << nb;
+                nb += 4 * BITS;
+                if (nb >= 32) {
+                    words[k][o++] = (uint32_t)acc;
+                    acc >>= 32;
+                    nb -= 32;
+                }
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < GPT; k++) {
+            uint32_t* dst = reinterpret_cast<uint32_t*>(img) + BITS * (tid + k * NT);
+#pragma unroll
+            for (int o = 0; o < BITS; o++) dst[o] = words[k][o];
+        }
+        __syncthreads();
+    }
+    if constexpr (BYTE_IMAGE) {
+        uint4* dst4 = reinterpret_cast<uint4*>(rec);
+        for (int u = tid; u < CODE_BYTES / 16; u += NT) dst4[u] = reinterpret_cast<const uint4*>(img)[u];
+    } else {
         // thread tid moves units tid, tid + NT, ...: consecutive lanes read
         // consecutive LDS units and write consecutive 16-byte chunks
         constexpr int UNITS = CODE_BYTES / 16 / NT;   // BITS / 2 units per thread
@@ -829,7 +894,38 @@ quantize_kernel(const uint16_t* __restrict__ kpool, const uint16_t* __restrict__
     }
 }
 
+// Keys or values alone (code widths outside 2, 4, 6 pair through two of
+// these launches): workgroup i*H + h takes page i, head h.
+template <int D, int T, int BITS, bool CHMAJOR>
+__global__ void __launch_bounds__(T * D / 64, D == 128 ? 3 : 4)
+quantize_one_kernel(const uint16_t* __restrict__ pool, uint8_t* __restrict__ recs, const int32_t* __restrict__ src,
+                    const int32_t* __restrict__ dst, int32_t H, int64_t n_fpages, int64_t n_qpages, int32_t n_iters) {
+    using S = TileShape<D, T>;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[S::SMEM];
+    __shared__ __attribute__((aligned(16))) float vec[VecShape<D>::FLOATS];
+    const int r = (int)wg_x();
+    const int i = r / H;
+    const int h = r - i * H;
+    const int sp = src[i];
+    const int dp = dst[i];
+    if (sp < 0 || (int64_t)sp >= n_fpages || dp < 0 || (int64_t)dp >= n_qpages) return;
+    constexpr int REC = T * D * BITS / 8 + 4 * T + 2 * D;
+    quantize_tile<D, T, BITS, CHMAJOR>(pool + ((int64_t)sp * H + h) * (int64_t)(T * D),
+                                       recs + ((int64_t)dp * H + h) * REC, smem, vec, n_iters);
+}
+
 }  // namespace
+
+template <int D, int T, int BITS, bool CHMAJOR>
+hipError_t launch_quantize_one(const QuantizeArgs& a, hipStream_t st) {
+    const int64_t blocks = (int64_t)a.n * a.H;
+    if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((quantize_one_kernel<D, T, BITS, CHMAJOR>), dim3((unsigned)blocks), dim3(T * D / 64), 0, st,
+                       static_cast<const uint16_t*>(CHMAJOR ? a.v_fp16 : a.k_fp16),
+                       static_cast<uint8_t*>(CHMAJOR ? a.v_records : a.k_records), a.src, a.dst, a.H, a.n_fpages,
+                       a.n_qpages, a.n_iters);
+    return hipGetLastError();
+}
 
 template <int D, int T, int KB, int VB, bool HASV>
 hipError_t launch_quantize_shape(const QuantizeArgs& a, hipStream_t st) {
@@ -860,6 +956,14 @@ hipError_t launch_quantize_shape(const QuantizeArgs& a, hipStream_t st) {
     template hipError_t launch_quantize_shape<D, 64, 4, 6, true>(const QuantizeArgs&, hipStream_t);  \
     template hipError_t launch_quantize_shape<D, 64, 6, 2, true>(const QuantizeArgs&, hipStream_t);  \
     template hipError_t launch_quantize_shape<D, 64, 6, 4, true>(const QuantizeArgs&, hipStream_t);  \
-    template hipError_t launch_quantize_shape<D, 64, 6, 6, true>(const QuantizeArgs&, hipStream_t);
+    template hipError_t launch_quantize_shape<D, 64, 6, 6, true>(const QuantizeArgs&, hipStream_t);  \
+    KVARN_QUANTIZE_ONE_T(D, 128)                                                                 \
+    KVARN_QUANTIZE_ONE_T(D, 64)
+#define KVARN_QUANTIZE_ONE_T(D, T)                                                               \
+    KVARN_QUANTIZE_ONE_B(D, T, 2) KVARN_QUANTIZE_ONE_B(D, T, 3) KVARN_QUANTIZE_ONE_B(D, T, 4)    \
+    KVARN_QUANTIZE_ONE_B(D, T, 5) KVARN_QUANTIZE_ONE_B(D, T, 6) KVARN_QUANTIZE_ONE_B(D, T, 8)
+#define KVARN_QUANTIZE_ONE_B(D, T, B)                                                            \
+    template hipError_t launch_quantize_one<D, T, B, false>(const QuantizeArgs&, hipStream_t);    \
+    template hipError_t launch_quantize_one<D, T, B, true>(const QuantizeArgs&, hipStream_t);
 
 }  // namespace kvarn

@@ -39,7 +39,12 @@ def test_parse_presets():
     assert L.tile_tokens == 64
     L = kv.parse_preset("kvarn_k6v6_g128")
     assert (L.k_bits, L.v_bits) == (6, 6)
-    for bad, st in [("kvarn_k3v2_g128", kv.KVARN_EUNSUPPORTED), ("kvarn_k4v2_g32", kv.KVARN_EUNSUPPORTED),
+    L = kv.parse_preset("kvarn_k3v5_g64")
+    assert (L.k_bits, L.v_bits, L.tile_tokens) == (3, 5, 64)
+    L = kv.parse_preset("kvarn_k8v8_g128")
+    assert (L.k_bits, L.v_bits) == (8, 8)
+    for bad, st in [("kvarn_k7v2_g128", kv.KVARN_EUNSUPPORTED), ("kvarn_k4v1_g128", kv.KVARN_EUNSUPPORTED),
+                    ("kvarn_k4v2_g32", kv.KVARN_EUNSUPPORTED),
                     ("fp8", kv.KVARN_EINVAL), ("kvarn_k4v2_g128x", kv.KVARN_EINVAL)]:
         with pytest.raises(kv.KvarnError) as e:
             kv.parse_preset(bad)
@@ -56,8 +61,9 @@ def test_head_dim_gate():
 
 @pytest.mark.parametrize("kw,st", [
     (dict(sink_tokens=100), kv.KVARN_EUNSUPPORTED),
-    (dict(k_bits=3), kv.KVARN_EUNSUPPORTED),
-    (dict(v_bits=8), kv.KVARN_EUNSUPPORTED),
+    (dict(k_bits=7), kv.KVARN_EUNSUPPORTED),
+    (dict(v_bits=1), kv.KVARN_EUNSUPPORTED),
+    (dict(v_bits=16), kv.KVARN_EUNSUPPORTED),
     (dict(n_iters=0), kv.KVARN_EINVAL),
     (dict(tail_tokens=-1), kv.KVARN_EINVAL),
     (dict(num_kv_heads=0), kv.KVARN_EINVAL),
@@ -67,6 +73,18 @@ def test_layout_rejections(kw, st):
     base = dict(head_dim=128, tile_tokens=128, k_bits=4, v_bits=2, num_kv_heads=8)
     base.update(kw)
     assert kv.layout_check(kv.make_layout(**base)) == st
+
+
+@pytest.mark.parametrize("kb", [2, 3, 4, 5, 6, 8])
+def test_every_width_of_the_pages_is_accepted(kb):
+    # gmlx "The two schemes": widths 2, 3, 4, 5, 6 and 8, separately for keys and values
+    for vb in (2, 3, 4, 5, 6, 8):
+        for T in (64, 128):
+            for D in (128, 256, 512):
+                L = kv.make_layout(D, T, kb, vb, num_kv_heads=2)
+                assert kv.layout_check(L) == kv.KVARN_OK
+                assert kv.record_bytes(L, 0) == T * D * kb // 8 + 4 * T + 2 * D
+                assert kv.record_bytes(L, 0) % 16 == 0 and kv.record_bytes(L, 1) % 16 == 0
 
 
 def test_record_bytes_and_region_rule():

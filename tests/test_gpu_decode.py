@@ -168,7 +168,7 @@ def test_decode_mla_full_size_every_row():
 
 
 # every pair of key and value widths at each head dim, on short sequences
-WIDTHS = (2, 4, 6)
+WIDTHS = (2, 3, 4, 5, 6, 8)
 
 
 @pytest.mark.parametrize("D", [128, 256, 512])

@@ -90,7 +90,7 @@ def test_quantize_full_size_sampled(name):
         f"({st.frac():.2e}; bar 1e-4)")
 
 
-WIDTHS = (2, 4, 6)
+WIDTHS = (2, 3, 4, 5, 6, 8)
 
 
 @pytest.mark.parametrize("D", [128, 256, 512])
