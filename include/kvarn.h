@@ -157,7 +157,8 @@ size_t kvarn_decode_workspace_bytes(const kvarn_layout *layout, int32_t batch,
  * (quantized region) or the fp16 pages (sink, tail).  The rotation is
  * applied once to q and once (inverse) to the output, and the scales are
  * folded into the score and value sums: no dequantized cache is written.
- * q: device [batch][num_q_heads][D] of q_dtype (KVARN_F32 or KVARN_BF16).
+ * q: device [batch][num_q_heads][D] of q_dtype (KVARN_F32, KVARN_F16 or
+ * KVARN_BF16; any other value is KVARN_EINVAL), 16-byte aligned.
  * out: device fp32 [batch][num_q_heads][D], original basis; a sequence with
  * L = 0 gives zeros.  workspace: device, at least
  * kvarn_decode_workspace_bytes(...) bytes, 256-byte aligned; its contents

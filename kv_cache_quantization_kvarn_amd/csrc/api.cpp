@@ -185,8 +185,8 @@ kvarn_status kvarn_decode_attn(const kvarn_layout* layout, const kvarn_cache* ca
     kvarn_status st = check_layout(layout);
     if (st != KVARN_OK) return st;
     if (!cache || !pages || !q || !out) return fail(KVARN_EINVAL, "NULL argument");
-    if (q_dtype != KVARN_F32 && q_dtype != KVARN_BF16)
-        return fail(KVARN_EUNSUPPORTED, "q_dtype %d: float32 and bfloat16 queries are implemented", q_dtype);
+    if (q_dtype != KVARN_F32 && q_dtype != KVARN_F16 && q_dtype != KVARN_BF16)
+        return fail(KVARN_EINVAL, "q_dtype %d: KVARN_F32, KVARN_F16 or KVARN_BF16", q_dtype);
     if (pages->batch < 1 || pages->max_pages < 1 || !pages->block_table || !pages->seq_lens)
         return fail(KVARN_EINVAL, "page table: batch and max_pages must be >= 1, arrays non-NULL");
     const int H = layout->num_kv_heads;
@@ -260,7 +260,7 @@ kvarn_status kvarn_decode_attn(const kvarn_layout* layout, const kvarn_cache* ca
     a.block_table = pages->block_table;
     a.seq_lens = pages->seq_lens;
     a.q = q;
-    a.q_bf16 = q_dtype == KVARN_BF16;
+    a.q_dtype = q_dtype;
     a.sm_scale = sm_scale;
     a.out = out;
     a.ws = static_cast<float*>(workspace);

@@ -221,24 +221,8 @@ __device__ __forceinline__ void fp16_block(const DecodeArgs& a, const int f, con
         // slots: 4 consecutive channels 4 i .. 4 i + 3 per slot
         float qx[NS][4];
         const int64_t qrow = ((int64_t)b * Hq + h * G + m) * D;
-        if (a.q_bf16) {  // uniform
 #pragma unroll
-            for (int r = 0; r < NS; r++) {
-                const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.q) + qrow +
-                                                                 4 * (32 * (r >> 1) + blk + 16 * (r & 1)));
-                qx[r][0] = __builtin_bit_cast(float, u.x << 16);
-                qx[r][1] = __builtin_bit_cast(float, u.x & 0xffff0000u);
-                qx[r][2] = __builtin_bit_cast(float, u.y << 16);
-                qx[r][3] = __builtin_bit_cast(float, u.y & 0xffff0000u);
-            }
-        } else {
-#pragma unroll
-            for (int r = 0; r < NS; r++) {
-                const float4 v = *reinterpret_cast<const float4*>(static_cast<const float*>(a.q) + qrow +
-                                                                  4 * (32 * (r >> 1) + blk + 16 * (r & 1)));
-                qx[r][0] = v.x; qx[r][1] = v.y; qx[r][2] = v.z; qx[r][3] = v.w;
-            }
-        }
+        for (int r = 0; r < NS; r++) q_load<4>(a.q, a.q_dtype, qrow + 4 * (32 * (r >> 1) + blk + 16 * (r & 1)), qx[r]);
         h4 qp[NS], qpl[NS];
 #pragma unroll
         for (int r = 0; r < NS; r++)
@@ -894,19 +878,7 @@ __global__ void __launch_bounds__(64) decode_split128_kernel(DecodeArgs a) {
         const int g = lane >> 4, m = lane & 15;
         const int64_t qrow = ((int64_t)b * Hq + h * G + g) * D + 8 * m;
         float x[8];
-        if (a.q_bf16) {  // uniform
-            const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) + qrow);
-            const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-            for (int k = 0; k < 4; k++) {
-                x[2 * k] = __builtin_bit_cast(float, w[k] << 16);
-                x[2 * k + 1] = __builtin_bit_cast(float, w[k] & 0xffff0000u);
-            }
-        } else {
-            const float4 u0 = *reinterpret_cast<const float4*>(static_cast<const float*>(a.q) + qrow);
-            const float4 u1 = *reinterpret_cast<const float4*>(static_cast<const float*>(a.q) + qrow + 4);
-            x[0] = u0.x; x[1] = u0.y; x[2] = u0.z; x[3] = u0.w; x[4] = u1.x; x[5] = u1.y; x[6] = u1.z; x[7] = u1.w;
-        }
+        q_load<8>(a.q, a.q_dtype, qrow, x);
 #pragma unroll
         for (int hs = 1; hs < 8; hs <<= 1)
 #pragma unroll
@@ -1205,14 +1177,10 @@ __global__ void __launch_bounds__(64) decode_split128_kernel(DecodeArgs a) {
 
 // q' = H q / sqrt(D) in fp32, one workgroup of D/2 threads per (sequence, query head)
 template <int D>
-__global__ void __launch_bounds__(D / 2) qrot_kernel(const void* __restrict__ q, int q_bf16, float* __restrict__ qr) {
+__global__ void __launch_bounds__(D / 2) qrot_kernel(const void* __restrict__ q, int q_dtype, float* __restrict__ qr) {
     __shared__ float x[D];
     const int bh = blockIdx.x, k = threadIdx.x;
-    for (int j = k; j < D; j += D / 2) {
-        const int64_t idx = (int64_t)bh * D + j;
-        x[j] = q_bf16 ? __builtin_bit_cast(float, ((uint32_t) static_cast<const uint16_t*>(q)[idx]) << 16)
-                      : static_cast<const float*>(q)[idx];
-    }
+    for (int j = k; j < D; j += D / 2) x[j] = q_at(q, q_dtype, (int64_t)bh * D + j);
     __syncthreads();
     for (int hs = 1; hs < D; hs <<= 1) {
         const int i0 = (k / hs) * 2 * hs + (k % hs), i1 = i0 + hs;
@@ -1294,7 +1262,7 @@ template <int D, int T, int KB, int VB>
 hipError_t launch_gqa(const DecodeArgs& a, hipStream_t st) {
     hipError_t e;
     if constexpr (D != 128) {  // the head_dim 128 split kernel rotates its queries itself
-        hipLaunchKernelGGL((qrot_kernel<D>), dim3(a.B * a.Hq), dim3(D / 2), 0, st, a.q, a.q_bf16, a.ws);
+        hipLaunchKernelGGL((qrot_kernel<D>), dim3(a.B * a.Hq), dim3(D / 2), 0, st, a.q, a.q_dtype, a.ws);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

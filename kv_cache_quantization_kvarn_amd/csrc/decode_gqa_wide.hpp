@@ -11,7 +11,7 @@ namespace kvarn {
 // the combine.  Explicitly instantiated per head dim in decode_gqa_w<D>.hip.
 template <int D, int T, int KB, int VB>
 hipError_t launch_gqa_wide(const DecodeArgs& a, hipStream_t st) {
-    hipLaunchKernelGGL((qrot_kernel<D>), dim3(a.B * a.Hq), dim3(D / 2), 0, st, a.q, a.q_bf16, a.ws);
+    hipLaunchKernelGGL((qrot_kernel<D>), dim3(a.B * a.Hq), dim3(D / 2), 0, st, a.q, a.q_dtype, a.ws);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     constexpr int NWV = split_waves<D>();

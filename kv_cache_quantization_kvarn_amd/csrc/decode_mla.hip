@@ -95,14 +95,10 @@ __device__ __forceinline__ float rsum16(float v) {
 }
 
 // q' = H q / sqrt(D) as fp16, one workgroup per (sequence, head).
-__global__ void __launch_bounds__(256) qrot_kernel(const void* __restrict__ q, int q_bf16, _Float16* __restrict__ qr) {
+__global__ void __launch_bounds__(256) qrot_kernel(const void* __restrict__ q, int q_dtype, _Float16* __restrict__ qr) {
     __shared__ float x[MD];
     const int bh = blockIdx.x;
-    for (int j = threadIdx.x; j < MD; j += 256) {
-        const int64_t idx = (int64_t)bh * MD + j;
-        x[j] = q_bf16 ? __builtin_bit_cast(float, ((uint32_t) static_cast<const uint16_t*>(q)[idx]) << 16)
-                      : static_cast<const float*>(q)[idx];
-    }
+    for (int j = threadIdx.x; j < MD; j += 256) x[j] = q_at(q, q_dtype, (int64_t)bh * MD + j);
     __syncthreads();
     for (int hs = 1; hs < MD; hs <<= 1) {
         const int k = threadIdx.x;  // 256 butterflies per stage
@@ -526,22 +522,10 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
         const int64_t qi = ((int64_t)b * a.Hq + h0 + wave * 16 + l16) * MD + 8 * g4;
 #pragma unroll
         for (int ks = 0; ks < 16; ks++) {
-            h8 v;
-            if (a.q_bf16) {
-                const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) + qi + 32 * ks);
-                const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-                for (int e = 0; e < 4; e++) {
-                    v[2 * e] = (_Float16)__builtin_bit_cast(float, w[e] << 16);
-                    v[2 * e + 1] = (_Float16)__builtin_bit_cast(float, w[e] & 0xffff0000u);
-                }
-            } else {
-                const float4 x0 = *reinterpret_cast<const float4*>(static_cast<const float*>(a.q) + qi + 32 * ks);
-                const float4 x1 = *reinterpret_cast<const float4*>(static_cast<const float*>(a.q) + qi + 32 * ks + 4);
-                v = h8{(_Float16)x0.x, (_Float16)x0.y, (_Float16)x0.z, (_Float16)x0.w,
-                       (_Float16)x1.x, (_Float16)x1.y, (_Float16)x1.z, (_Float16)x1.w};
-            }
-            qa[ks] = v;
+            float x[8];
+            q_load<8>(a.q, a.q_dtype, qi + 32 * ks, x);
+            qa[ks] = h8{(_Float16)x[0], (_Float16)x[1], (_Float16)x[2], (_Float16)x[3],
+                        (_Float16)x[4], (_Float16)x[5], (_Float16)x[6], (_Float16)x[7]};
         }
     }
     static_assert(CH * MD * 2 <= CH * YROW, "an fp16 chunk fits a read-back buffer");
@@ -643,7 +627,7 @@ __global__ void __launch_bounds__(256) mla_combine_kernel(const float* __restric
 
 template <int T, int HB>
 hipError_t launch_mla_t(const DecodeArgs& a, hipStream_t st) {
-    hipLaunchKernelGGL(qrot_kernel, dim3(a.B * a.Hq), dim3(256), 0, st, a.q, a.q_bf16,
+    hipLaunchKernelGGL(qrot_kernel, dim3(a.B * a.Hq), dim3(256), 0, st, a.q, a.q_dtype,
                        reinterpret_cast<_Float16*>(a.ws));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

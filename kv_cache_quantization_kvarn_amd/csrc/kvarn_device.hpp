@@ -82,6 +82,47 @@ __device__ __forceinline__ uint32_t float_to_half_bits(float f) {
 }
 
 
+// Query elements of the three query dtypes of the C ABI (0 float32, 1
+// float16, 2 bfloat16), widened exactly to float.
+__device__ __forceinline__ float q_at(const void* q, int dt, int64_t idx) {
+    if (dt == 0) return static_cast<const float*>(q)[idx];
+    const uint32_t h = static_cast<const uint16_t*>(q)[idx];
+    return dt == 2 ? __builtin_bit_cast(float, h << 16) : half_bits_to_float(h);
+}
+// N = 4 or 8 consecutive elements from idx, a multiple of N (whole 8- or
+// 16-byte units for the 16-bit dtypes)
+template <int N>
+__device__ __forceinline__ void q_load(const void* q, int dt, int64_t idx, float (&x)[N]) {
+    static_assert(N == 4 || N == 8, "4 or 8 elements");
+    if (dt == 0) {
+        const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(q) + idx);
+#pragma unroll
+        for (int k = 0; k < N / 4; k++) {
+            const float4 v = p[k];
+            x[4 * k] = v.x; x[4 * k + 1] = v.y; x[4 * k + 2] = v.z; x[4 * k + 3] = v.w;
+        }
+        return;
+    }
+    uint32_t w[N / 2];
+    if constexpr (N == 8) {
+        const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(q) + idx);
+        w[0] = u.x; w[1] = u.y; w[2] = u.z; w[3] = u.w;
+    } else {
+        const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(q) + idx);
+        w[0] = u.x; w[1] = u.y;
+    }
+#pragma unroll
+    for (int k = 0; k < N / 2; k++) {
+        if (dt == 2) {
+            x[2 * k] = __builtin_bit_cast(float, w[k] << 16);
+            x[2 * k + 1] = __builtin_bit_cast(float, w[k] & 0xffff0000u);
+        } else {
+            x[2 * k] = half_bits_to_float(w[k] & 0xffffu);
+            x[2 * k + 1] = half_bits_to_float(w[k] >> 16);
+        }
+    }
+}
+
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 // LDS-DMA loads: each active lane's 16 bytes at buffer offset voff + soff

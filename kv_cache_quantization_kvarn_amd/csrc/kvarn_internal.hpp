@@ -47,7 +47,7 @@ struct DecodeArgs {
     const int32_t* block_table;
     const int32_t* seq_lens;
     const void* q;
-    int q_bf16;
+    int q_dtype;      // 0 float32, 1 float16, 2 bfloat16
     float sm_scale;
     float* out;
     float* ws;        // split partials

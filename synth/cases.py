@@ -145,7 +145,7 @@ def make_case(w, device="cpu", seq_lens=None, batch=None, with_v=True):
 
     nq_elems = B * Hq * D
     qv = normal(w["seed"], Q_STREAM, nq_elems, device=device).view(B, Hq, D)
-    q = qv.to(torch.bfloat16) if w["q_dtype"] == "bf16" else qv.to(torch.float32)
+    q = qv.to({"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[w["q_dtype"]])
 
     return dict(
         w=w, layout=layout_of(w), B=B, Hq=Hq, seq_lens=torch.tensor(seq_lens, dtype=torch.int32,

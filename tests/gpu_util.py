@@ -60,9 +60,11 @@ def host_u16(t):
 
 
 def host_q(q):
+    """Queries for the oracle: bfloat16 bits, or float32 (fp16 queries are
+    widened to float32, which holds every fp16 value exactly)."""
     if q.dtype == torch.bfloat16:
         return q.cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
-    return q.cpu().numpy()
+    return q.cpu().float().numpy()
 
 
 def oracle_decode(case, krec, vrec, pairs=None, k16=None, v16=None):

@@ -125,7 +125,7 @@ def test_decode_rejects_before_any_device_work():
     assert lib.kvarn_decode_attn(*args(64, ctypes.c_void_p(256), need)) == kv.KVARN_EUNSUPPORTED
     assert lib.kvarn_decode_attn(*args(32, ctypes.c_void_p(256), need - 1)) == kv.KVARN_EWORKSPACE
     assert lib.kvarn_decode_attn(*args(32, None, need)) == kv.KVARN_EWORKSPACE
-    assert lib.kvarn_decode_attn(*args(32, ctypes.c_void_p(256), need, qd=7)) == kv.KVARN_EUNSUPPORTED
+    assert lib.kvarn_decode_attn(*args(32, ctypes.c_void_p(256), need, qd=7)) == kv.KVARN_EINVAL
     assert lib.kvarn_decode_attn(*args(32, ctypes.c_void_p(260), need)) == kv.KVARN_EINVAL
     # negative pool sizes and batches beyond the grid are refused on the host
     bad = kv.Cache(ctypes.c_void_p(16), ctypes.c_void_p(16), ctypes.c_void_p(16), ctypes.c_void_p(16), -1, 1)

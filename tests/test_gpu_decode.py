@@ -185,13 +185,14 @@ def test_decode_width_pairs(D, kb, vb):
     check(case, out, krec, vrec)
 
 
-@pytest.mark.parametrize("D", [128, 256, 512])
-def test_decode_bf16_queries(D):
-    w = workload("wide_d256_b8_64k_k6v6", D=D, T=128, k_bits=4, v_bits=2, Hq=8, H=2, L=1500, sink=128, tail=256,
-                 dist="normal", outliers=("per_head", 4), q_dtype="bf16", seed=0x4200 + D)
+@pytest.mark.parametrize("qd", ["bf16", "f16"])
+@pytest.mark.parametrize("D,kb,vb", [(128, 4, 2), (256, 4, 2), (512, 4, 2), (128, 3, 5)])
+def test_decode_16bit_queries(D, kb, vb, qd):
+    w = workload("wide_d256_b8_64k_k6v6", D=D, T=128, k_bits=kb, v_bits=vb, Hq=8, H=2, L=1500, sink=128, tail=256,
+                 dist="normal", outliers=("per_head", 4), q_dtype=qd, seed=0x4200 + D)
     case = gpu_case(w, seq_lens=[1500, 700, 1], batch=3)
-    assert case["q"].dtype == torch.bfloat16
-    say("decode bf16 queries", D)
+    assert case["q"].dtype == {"bf16": torch.bfloat16, "f16": torch.float16}[qd]
+    say("decode 16-bit queries", D, kb, vb, qd)
     L, krec, vrec = run_quantize(case)
     out = run_decode(case, L, krec, vrec)
     check(case, out, krec, vrec)
@@ -246,3 +247,13 @@ def test_decode_dominating_score(mla):
         err = np.abs(got - v).max() / np.abs(v).max()
         say("dominating token", b, h, t, f"rel err vs its read-back value {err:.2e}")
         assert err <= DECODE_RTOL
+
+
+@pytest.mark.parametrize("qd", ["f16", "f32"])
+def test_decode_mla_other_query_dtypes(qd):
+    w = workload("mla_d512_b32_32k_int4", Hq=32, T=128, sink=128, tail=256, q_dtype=qd, seed=0x5300)
+    case = gpu_case(w, seq_lens=[1400, 333], batch=2)
+    say("mla queries", qd)
+    L, krec, vrec = run_quantize(case)
+    out = run_decode(case, L, krec, vrec)
+    check(case, out, krec, None)
