@@ -173,6 +173,32 @@ kvarn_status kvarn_decode_attn(const kvarn_layout *layout, const kvarn_cache *ca
                                int32_t num_q_heads, float sm_scale, float *out,
                                void *workspace, size_t workspace_bytes, void *stream);
 
+/* Workspace bytes kvarn_decode_attn_mq needs; 0 for invalid arguments
+ * (num_q_tokens outside 1..4 included).  Host-only. */
+size_t kvarn_decode_workspace_bytes_mq(const kvarn_layout *layout, int32_t batch, int32_t num_q_tokens,
+                                       int32_t num_q_heads, int32_t max_pages);
+
+/* Decode of num_q_tokens (1..4) query tokens per sequence, causal among
+ * themselves -- a speculative-decoding verify step, which checks at most
+ * four tokens a row (gmlx "KV cache quantization", "Speed and speculative
+ * decoding").  The query tokens are the newest tokens of each sequence,
+ * appended (kvarn_append) but not committed: token i of sequence b sits at
+ * position seq_lens[b] + i, and
+ *   out[b][i][h] = sum_{t <= seq_lens[b] + i} softmax_t(sm_scale <q[b][i][h], k_t>) v_t.
+ * The regions (see "Regions") follow seq_lens[b], the committed tokens, so
+ * the query tokens and every token the causal mask drops lie in fp16 pages
+ * (the commit rule keeps uncommitted tokens out of the records).  The
+ * records of a sequence are read once for all its query tokens: the
+ * workgroups of a sequence's tokens run on one XCD and share its L2.
+ * q: device [batch][num_q_tokens][num_q_heads][D] of q_dtype; out: device
+ * fp32 [batch][num_q_tokens][num_q_heads][D].  Workspace:
+ * kvarn_decode_workspace_bytes_mq(...) bytes.  Everything else as
+ * kvarn_decode_attn; batch * num_q_tokens is at most 32767 for GQA. */
+kvarn_status kvarn_decode_attn_mq(const kvarn_layout *layout, const kvarn_cache *cache,
+                                  const kvarn_page_table *pages, const void *q, int32_t q_dtype,
+                                  int32_t num_q_tokens, int32_t num_q_heads, float sm_scale, float *out,
+                                  void *workspace, size_t workspace_bytes, void *stream);
+
 /* Append n_new tokens to every sequence of the batch: the keys and values
  * (MLA: latents) of new token i of sequence b go to position seq_lens[b] + i,
  * i.e. slot (pos % T) of fp16 page block_table[b][pos / T] of the fp16

@@ -18,7 +18,8 @@ KVARN_F32, KVARN_F16, KVARN_BF16 = 0, 1, 2
 
 EXPORTS = ("kvarn_parse_preset", "kvarn_layout_check", "kvarn_record_bytes", "kvarn_quantized_pages",
            "kvarn_quantize", "kvarn_decode_workspace_bytes", "kvarn_decode_attn", "kvarn_last_error",
-           "kvarn_version", "kvarn_decode_attn_noalloc", "kvarn_append", "kvarn_commit")
+           "kvarn_version", "kvarn_decode_attn_noalloc", "kvarn_append", "kvarn_commit",
+           "kvarn_decode_attn_mq", "kvarn_decode_workspace_bytes_mq")
 
 
 class KvarnError(RuntimeError):
@@ -72,6 +73,10 @@ def lib():
     L.kvarn_decode_attn.restype = i32
     L.kvarn_decode_attn_noalloc.argtypes = [PL, PC, PT, P, i32, i32, ctypes.c_float, P, P]
     L.kvarn_decode_attn_noalloc.restype = i32
+    L.kvarn_decode_workspace_bytes_mq.argtypes = [PL, i32, i32, i32, i32]
+    L.kvarn_decode_workspace_bytes_mq.restype = sz
+    L.kvarn_decode_attn_mq.argtypes = [PL, PC, PT, P, i32, i32, i32, ctypes.c_float, P, P, sz, P]
+    L.kvarn_decode_attn_mq.restype = i32
     L.kvarn_append.argtypes = [PL, PC, PT, P, P, i32, i32, P]
     L.kvarn_append.restype = i32
     L.kvarn_commit.argtypes = [PL, PC, P, P, i32, i32, P, P, P, P]
@@ -208,3 +213,28 @@ def commit(layout, k_records, v_records, k_fp16, v_fp16, block_table, seq_lens, 
     cache = make_cache(k_records, v_records, k_fp16, v_fp16)
     _check(lib().kvarn_commit(ctypes.byref(layout), ctypes.byref(cache), _ptr(block_table), _ptr(seq_lens), B,
                               max_pages, _ptr(n_accept), _ptr(new_qpages), _ptr(promoted), _stream()))
+
+
+def decode_workspace_bytes_mq(layout, batch, num_q_tokens, num_q_heads, max_pages):
+    return int(lib().kvarn_decode_workspace_bytes_mq(ctypes.byref(layout), batch, num_q_tokens, num_q_heads,
+                                                      max_pages))
+
+
+def decode_attn_mq(layout, k_records, v_records, k_fp16, v_fp16, block_table, seq_lens, q, sm_scale, out=None,
+                   workspace=None):
+    """kvarn_decode_attn_mq on the current stream: q [B, M, Hq, D] (M <= 4
+    query tokens at positions seq_lens[b] + i); returns out [B, M, Hq, D] fp32."""
+    B, M, Hq, D = q.shape
+    assert block_table.dtype == torch.int32 and seq_lens.dtype == torch.int32
+    assert q.is_contiguous() and block_table.is_contiguous()
+    qd = {torch.float32: KVARN_F32, torch.bfloat16: KVARN_BF16, torch.float16: KVARN_F16}[q.dtype]
+    if out is None:
+        out = torch.empty((B, M, Hq, D), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        n = decode_workspace_bytes_mq(layout, B, M, Hq, int(block_table.shape[1]))
+        workspace = torch.empty(max(n, 256), dtype=torch.uint8, device=q.device)
+    cache = make_cache(k_records, v_records, k_fp16, v_fp16)
+    pt = PageTable(_ptr(block_table), _ptr(seq_lens), B, int(block_table.shape[1]))
+    _check(lib().kvarn_decode_attn_mq(ctypes.byref(layout), ctypes.byref(cache), ctypes.byref(pt), _ptr(q), qd, M, Hq,
+                                      float(sm_scale), _ptr(out), _ptr(workspace), workspace.numel(), _stream()))
+    return out

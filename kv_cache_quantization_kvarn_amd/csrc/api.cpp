@@ -64,6 +64,127 @@ size_t rec_bytes(const kvarn_layout* L, int bits) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+
+// Workspace of a decode call with M query tokens per sequence (rows =
+// batch x M; a causal call's fp16 tail may hold M more tokens).
+size_t decode_workspace(const kvarn_layout* layout, int32_t batch, int32_t M, int causal, int32_t num_q_heads,
+                        int32_t max_pages) {
+    if (check_layout(layout) != KVARN_OK) return 0;
+    if (batch < 1 || num_q_heads < 1 || max_pages < 1) {
+        fail(KVARN_EINVAL, "batch, num_q_heads and max_pages must be >= 1");
+        return 0;
+    }
+    const int64_t rows = (int64_t)batch * M;
+    if (rows > 0x7fffffff / 2) {
+        fail(KVARN_EINVAL, "batch x query tokens too large");
+        return 0;
+    }
+    int ns = 1, pps = 1;
+    const int H = layout->num_kv_heads;
+    kvarn::decode_plan(layout->head_dim, H, num_q_heads / (H > 0 ? H : 1), layout->mla, (int)rows, max_pages,
+                       layout->tile_tokens, layout->k_bits, layout->v_bits, &ns, &pps);
+    if (layout->mla) return kvarn::mla_workspace_floats(num_q_heads, (int)rows, ns) * sizeof(float);
+    const int nf = kvarn::decode_fp16_slots(layout->tile_tokens, layout->sink_tokens,
+                                            layout->tail_tokens + (causal ? M : 0), max_pages);
+    return kvarn::decode_workspace_floats(layout->head_dim, num_q_heads, (int)rows, ns, nf) * sizeof(float);
+}
+
+kvarn_status decode_common(const kvarn_layout* layout, const kvarn_cache* cache, const kvarn_page_table* pages,
+                           const void* q, int32_t q_dtype, int32_t M, int causal, int32_t num_q_heads,
+                           float sm_scale, float* out, void* workspace, size_t workspace_bytes, void* stream) {
+    kvarn_status st = check_layout(layout);
+    if (st != KVARN_OK) return st;
+    if (!cache || !pages || !q || !out) return fail(KVARN_EINVAL, "NULL argument");
+    if (q_dtype != KVARN_F32 && q_dtype != KVARN_F16 && q_dtype != KVARN_BF16)
+        return fail(KVARN_EINVAL, "q_dtype %d: KVARN_F32, KVARN_F16 or KVARN_BF16", q_dtype);
+    if (pages->batch < 1 || pages->max_pages < 1 || !pages->block_table || !pages->seq_lens)
+        return fail(KVARN_EINVAL, "page table: batch and max_pages must be >= 1, arrays non-NULL");
+    const int H = layout->num_kv_heads;
+    if (num_q_heads < 1 || num_q_heads % H != 0)
+        return fail(KVARN_EINVAL, "num_q_heads %d is not a multiple of num_kv_heads %d", num_q_heads, H);
+    const int G = num_q_heads / H;
+    if (layout->mla) {
+        if (num_q_heads != 16 && num_q_heads != 32 && num_q_heads != 64 && num_q_heads != 128)
+            return fail(KVARN_EUNSUPPORTED, "mla: %d query heads; 16, 32, 64 or 128 are implemented", num_q_heads);
+    } else if (G != 4) {
+        return fail(KVARN_EUNSUPPORTED, "GQA group %d: this build implements groups of 4 query heads", G);
+    }
+    if (!cache->k_fp16 || (!layout->mla && !cache->v_fp16)) return fail(KVARN_EINVAL, "fp16 pools are NULL");
+    if (cache->n_qpages < 0 || cache->n_fpages < 0) return fail(KVARN_EINVAL, "negative pool size");
+    const int64_t rows = (int64_t)pages->batch * M;
+    // GQA grids carry the query rows (and the fp16 slots of each) in grid z, at most 65535
+    if (!layout->mla && rows > 32767)
+        return fail(KVARN_EUNSUPPORTED, "batch %d x %d query tokens: at most 32767 query rows per call",
+                    pages->batch, M);
+    if (layout->mla && rows > (1 << 24))
+        return fail(KVARN_EUNSUPPORTED, "mla: at most 2^24 query rows per call");
+    if (H > 65535) return fail(KVARN_EUNSUPPORTED, "num_kv_heads %d: at most 65535", H);
+    if (cache->n_qpages > 0 && (!cache->k_records || (!layout->mla && !cache->v_records)))
+        return fail(KVARN_EINVAL, "record pools are NULL");
+    if (!(sm_scale > 0.f) || sm_scale > 1e30f) return fail(KVARN_EINVAL, "sm_scale must be positive and finite");
+    if (layout->mla || layout->head_dim == 128) {
+        // the MLA and head_dim 128 kernels address each record pool with 32-bit byte offsets
+        const uint64_t kb = (uint64_t)cache->n_qpages * (uint64_t)H * kvarn_record_bytes(layout, 0);
+        const uint64_t vb = layout->mla ? 0 : (uint64_t)cache->n_qpages * (uint64_t)H * kvarn_record_bytes(layout, 1);
+        if (kb >= (1ull << 32) || vb >= (1ull << 32))
+            return fail(KVARN_EUNSUPPORTED, "%s: record pools of %llu / %llu bytes; below 4 GiB each is implemented",
+                        layout->mla ? "mla" : "head_dim 128", (unsigned long long)kb, (unsigned long long)vb);
+        // the MLA kernel also streams its fp16 pool through 32-bit offsets
+        const uint64_t fb = (uint64_t)cache->n_fpages * (uint64_t)H * (uint64_t)layout->tile_tokens *
+                            (uint64_t)layout->head_dim * 2u;
+        if (layout->mla && fb >= (1ull << 32))
+            return fail(KVARN_EUNSUPPORTED, "mla: an fp16 pool of %llu bytes; below 4 GiB is implemented",
+                        (unsigned long long)fb);
+    }
+    int ns = 1, pps = 1;
+    kvarn::decode_plan(layout->head_dim, H, G, layout->mla, (int)rows, pages->max_pages, layout->tile_tokens,
+                       layout->k_bits, layout->v_bits, &ns, &pps);
+    const int nf = kvarn::decode_fp16_slots(layout->tile_tokens, layout->sink_tokens,
+                                            layout->tail_tokens + (causal ? M : 0), pages->max_pages);
+    const size_t need = (layout->mla ? kvarn::mla_workspace_floats(num_q_heads, (int)rows, ns)
+                                     : kvarn::decode_workspace_floats(layout->head_dim, num_q_heads, (int)rows, ns,
+                                                                      nf)) *
+                        sizeof(float);
+    if (!workspace || workspace_bytes < need)
+        return fail(KVARN_EWORKSPACE, "workspace of %zu bytes is smaller than the %zu bytes required",
+                    workspace ? workspace_bytes : (size_t)0, need);
+    if (((uintptr_t)workspace & 255u) != 0) return fail(KVARN_EINVAL, "workspace must be 256-byte aligned");
+    kvarn::DecodeArgs a{};
+    a.D = layout->head_dim;
+    a.T = layout->tile_tokens;
+    a.k_bits = layout->k_bits;
+    a.v_bits = layout->v_bits;
+    a.sink = layout->sink_tokens;
+    a.tail = layout->tail_tokens;
+    a.H = H;
+    a.mla = layout->mla;
+    a.G = G;
+    a.B = (int)rows;
+    a.M = M;
+    a.causal = causal;
+    a.Hq = num_q_heads;
+    a.max_pages = pages->max_pages;
+    a.nsplit = ns;
+    a.nfsplit = nf;
+    a.pps = pps;
+    a.k_records = cache->k_records;
+    a.v_records = cache->v_records;
+    a.k_fp16 = cache->k_fp16;
+    a.v_fp16 = cache->v_fp16;
+    a.n_qpages = cache->n_qpages;
+    a.n_fpages = cache->n_fpages;
+    a.block_table = pages->block_table;
+    a.seq_lens = pages->seq_lens;
+    a.q = q;
+    a.q_dtype = q_dtype;
+    a.sm_scale = sm_scale;
+    a.out = out;
+    a.ws = static_cast<float*>(workspace);
+    hipError_t e = kvarn::launch_decode(a, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(KVARN_EHIP, "decode launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
 }  // namespace
 
 namespace kvarn {
@@ -165,108 +286,34 @@ kvarn_status kvarn_quantize(const kvarn_layout* layout, const kvarn_cache* cache
 
 size_t kvarn_decode_workspace_bytes(const kvarn_layout* layout, int32_t batch, int32_t num_q_heads,
                                     int32_t max_pages) {
-    if (check_layout(layout) != KVARN_OK) return 0;
-    if (batch < 1 || num_q_heads < 1 || max_pages < 1) {
-        fail(KVARN_EINVAL, "batch, num_q_heads and max_pages must be >= 1");
+    return decode_workspace(layout, batch, 1, 0, num_q_heads, max_pages);
+}
+
+size_t kvarn_decode_workspace_bytes_mq(const kvarn_layout* layout, int32_t batch, int32_t num_q_tokens,
+                                       int32_t num_q_heads, int32_t max_pages) {
+    if (num_q_tokens < 1 || num_q_tokens > 4) {
+        fail(KVARN_EINVAL, "num_q_tokens %d outside 1..4", num_q_tokens);
         return 0;
     }
-    int ns = 1, pps = 1;
-    const int H = layout->num_kv_heads;
-    kvarn::decode_plan(layout->head_dim, H, num_q_heads / (H > 0 ? H : 1), layout->mla, batch, max_pages,
-                       layout->tile_tokens, layout->k_bits, layout->v_bits, &ns, &pps);
-    if (layout->mla) return kvarn::mla_workspace_floats(num_q_heads, batch, ns) * sizeof(float);
-    const int nf = kvarn::decode_fp16_slots(layout->tile_tokens, layout->sink_tokens, layout->tail_tokens, max_pages);
-    return kvarn::decode_workspace_floats(layout->head_dim, num_q_heads, batch, ns, nf) * sizeof(float);
+    return decode_workspace(layout, batch, num_q_tokens, 1, num_q_heads, max_pages);
 }
 
 kvarn_status kvarn_decode_attn(const kvarn_layout* layout, const kvarn_cache* cache, const kvarn_page_table* pages,
                                const void* q, int32_t q_dtype, int32_t num_q_heads, float sm_scale, float* out,
                                void* workspace, size_t workspace_bytes, void* stream) {
-    kvarn_status st = check_layout(layout);
-    if (st != KVARN_OK) return st;
-    if (!cache || !pages || !q || !out) return fail(KVARN_EINVAL, "NULL argument");
-    if (q_dtype != KVARN_F32 && q_dtype != KVARN_F16 && q_dtype != KVARN_BF16)
-        return fail(KVARN_EINVAL, "q_dtype %d: KVARN_F32, KVARN_F16 or KVARN_BF16", q_dtype);
-    if (pages->batch < 1 || pages->max_pages < 1 || !pages->block_table || !pages->seq_lens)
-        return fail(KVARN_EINVAL, "page table: batch and max_pages must be >= 1, arrays non-NULL");
-    const int H = layout->num_kv_heads;
-    if (num_q_heads < 1 || num_q_heads % H != 0)
-        return fail(KVARN_EINVAL, "num_q_heads %d is not a multiple of num_kv_heads %d", num_q_heads, H);
-    const int G = num_q_heads / H;
-    if (layout->mla) {
-        if (num_q_heads != 16 && num_q_heads != 32 && num_q_heads != 64 && num_q_heads != 128)
-            return fail(KVARN_EUNSUPPORTED, "mla: %d query heads; 16, 32, 64 or 128 are implemented", num_q_heads);
-    } else if (G != 4) {
-        return fail(KVARN_EUNSUPPORTED, "GQA group %d: this build implements groups of 4 query heads", G);
-    }
-    if (!cache->k_fp16 || (!layout->mla && !cache->v_fp16)) return fail(KVARN_EINVAL, "fp16 pools are NULL");
-    if (cache->n_qpages < 0 || cache->n_fpages < 0) return fail(KVARN_EINVAL, "negative pool size");
-    // GQA grids carry the sequence (and the fp16 slots of each) in grid z, at most 65535
-    if (!layout->mla && pages->batch > 32767)
-        return fail(KVARN_EUNSUPPORTED, "batch %d: at most 32767 sequences per call", pages->batch);
-    if (H > 65535) return fail(KVARN_EUNSUPPORTED, "num_kv_heads %d: at most 65535", H);
-    if (cache->n_qpages > 0 && (!cache->k_records || (!layout->mla && !cache->v_records)))
-        return fail(KVARN_EINVAL, "record pools are NULL");
-    if (!(sm_scale > 0.f) || sm_scale > 1e30f) return fail(KVARN_EINVAL, "sm_scale must be positive and finite");
-    if (layout->mla || layout->head_dim == 128) {
-        // the MLA and head_dim 128 kernels address each record pool with 32-bit byte offsets
-        const uint64_t kb = (uint64_t)cache->n_qpages * (uint64_t)H * kvarn_record_bytes(layout, 0);
-        const uint64_t vb = layout->mla ? 0 : (uint64_t)cache->n_qpages * (uint64_t)H * kvarn_record_bytes(layout, 1);
-        if (kb >= (1ull << 32) || vb >= (1ull << 32))
-            return fail(KVARN_EUNSUPPORTED, "%s: record pools of %llu / %llu bytes; below 4 GiB each is implemented",
-                        layout->mla ? "mla" : "head_dim 128", (unsigned long long)kb, (unsigned long long)vb);
-        // the MLA kernel also streams its fp16 pool through 32-bit offsets
-        const uint64_t fb = (uint64_t)cache->n_fpages * (uint64_t)H * (uint64_t)layout->tile_tokens *
-                            (uint64_t)layout->head_dim * 2u;
-        if (layout->mla && fb >= (1ull << 32))
-            return fail(KVARN_EUNSUPPORTED, "mla: an fp16 pool of %llu bytes; below 4 GiB is implemented",
-                        (unsigned long long)fb);
-    }
-    int ns = 1, pps = 1;
-    kvarn::decode_plan(layout->head_dim, H, G, layout->mla, pages->batch, pages->max_pages, layout->tile_tokens,
-                       layout->k_bits, layout->v_bits, &ns, &pps);
-    const int nf = kvarn::decode_fp16_slots(layout->tile_tokens, layout->sink_tokens, layout->tail_tokens,
-                                            pages->max_pages);
-    const size_t need = (layout->mla ? kvarn::mla_workspace_floats(num_q_heads, pages->batch, ns)
-                                     : kvarn::decode_workspace_floats(layout->head_dim, num_q_heads, pages->batch, ns,
-                                                                      nf)) *
-                        sizeof(float);
-    if (!workspace || workspace_bytes < need)
-        return fail(KVARN_EWORKSPACE, "workspace of %zu bytes is smaller than the %zu bytes required",
-                    workspace ? workspace_bytes : (size_t)0, need);
-    if (((uintptr_t)workspace & 255u) != 0) return fail(KVARN_EINVAL, "workspace must be 256-byte aligned");
-    kvarn::DecodeArgs a{};
-    a.D = layout->head_dim;
-    a.T = layout->tile_tokens;
-    a.k_bits = layout->k_bits;
-    a.v_bits = layout->v_bits;
-    a.sink = layout->sink_tokens;
-    a.tail = layout->tail_tokens;
-    a.H = H;
-    a.mla = layout->mla;
-    a.G = G;
-    a.B = pages->batch;
-    a.Hq = num_q_heads;
-    a.max_pages = pages->max_pages;
-    a.nsplit = ns;
-    a.nfsplit = nf;
-    a.pps = pps;
-    a.k_records = cache->k_records;
-    a.v_records = cache->v_records;
-    a.k_fp16 = cache->k_fp16;
-    a.v_fp16 = cache->v_fp16;
-    a.n_qpages = cache->n_qpages;
-    a.n_fpages = cache->n_fpages;
-    a.block_table = pages->block_table;
-    a.seq_lens = pages->seq_lens;
-    a.q = q;
-    a.q_dtype = q_dtype;
-    a.sm_scale = sm_scale;
-    a.out = out;
-    a.ws = static_cast<float*>(workspace);
-    hipError_t e = kvarn::launch_decode(a, (hipStream_t)stream);
-    if (e != hipSuccess) return fail(KVARN_EHIP, "decode launch failed: %s", hipGetErrorString(e));
-    return ok();
+    return decode_common(layout, cache, pages, q, q_dtype, 1, 0, num_q_heads, sm_scale, out, workspace,
+                         workspace_bytes, stream);
+}
+
+kvarn_status kvarn_decode_attn_mq(const kvarn_layout* layout, const kvarn_cache* cache,
+                                  const kvarn_page_table* pages, const void* q, int32_t q_dtype,
+                                  int32_t num_q_tokens, int32_t num_q_heads, float sm_scale, float* out,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+    if (num_q_tokens < 1 || num_q_tokens > 4)
+        return fail(KVARN_EINVAL, "num_q_tokens %d outside 1..4 (a verify step checks at most four tokens a row)",
+                    num_q_tokens);
+    return decode_common(layout, cache, pages, q, q_dtype, num_q_tokens, 1, num_q_heads, sm_scale, out, workspace,
+                         workspace_bytes, stream);
 }
 
 kvarn_status kvarn_append(const kvarn_layout* layout, const kvarn_cache* cache, const kvarn_page_table* pages,

@@ -192,8 +192,10 @@ __device__ __forceinline__ void fp16_block(const DecodeArgs& a, const int f, con
     const int blk = lane >> 2, m = lane & 3;
     const int Hq = a.Hq;
     const float sm2 = a.sm_scale * kLog2e;
-    const int L = min(a.seq_lens[b], a.max_pages * T);
-    const int npages = L > 0 ? (L + T - 1) / T : 0;
+    const int bs = b / a.M;  // sequence of query row b
+    const int L = min(a.seq_lens[bs], a.max_pages * T);
+    const int A = attend_len(a, b, L, a.max_pages * T);  // tokens this row attends
+    const int npages = A > 0 ? (A + T - 1) / T : 0;
     const int nq = (L - a.sink - a.tail >= T) ? (L - a.sink - a.tail) / T : 0;
     const int sp = a.sink / T;
     const int fpg = f / TS, sb = f % TS;
@@ -201,8 +203,8 @@ __device__ __forceinline__ void fp16_block(const DecodeArgs& a, const int f, con
     int id = -1;
     int nvalid = 0;  // valid tokens of the part
     if (page < npages) {
-        nvalid = min(64, min(T, L - page * T) - 64 * sb);
-        id = a.block_table[(int64_t)b * a.max_pages + page];
+        nvalid = min(64, min(T, A - page * T) - 64 * sb);
+        id = a.block_table[(int64_t)bs * a.max_pages + page];
         if (id < 0 || (int64_t)id >= a.n_fpages || nvalid <= 0) id = -1;
     }
 
@@ -367,7 +369,8 @@ __global__ void __launch_bounds__(64 * split_waves<D>(), 3) decode_split_kernel(
         for (int k = 0; k < 4; k++) qv[r][k] = qr[code_of<KB>(i, k)];
     }
 
-    const int L = min(a.seq_lens[b], a.max_pages * T);
+    const int bs = b / a.M;  // sequence of query row b (its quantized pages lie before every query token)
+    const int L = min(a.seq_lens[bs], a.max_pages * T);
     const int nq = (L - a.sink - a.tail >= T) ? (L - a.sink - a.tail) / T : 0;
     const int sp = a.sink / T;
 
@@ -408,7 +411,7 @@ __global__ void __launch_bounds__(64 * split_waves<D>(), 3) decode_split_kernel(
     auto step_ref = [&](int k) {
         StepRef r;
         r.h = k % TS;
-        r.id = k < nst ? a.block_table[(int64_t)b * a.max_pages + sp + split + (k / TS) * a.nsplit] : -1;
+        r.id = k < nst ? a.block_table[(int64_t)bs * a.max_pages + sp + split + (k / TS) * a.nsplit] : -1;
         r.ok = k < nst && r.id >= 0 && (int64_t)r.id < a.n_qpages;
         return r;
     };
@@ -727,22 +730,6 @@ __device__ __forceinline__ void wave_reduce4(float (&v)[4], float (&out)[4]) {
     for (int g = 0; g < 4; g++) out[g] = i2f(__builtin_amdgcn_readlane(f2i(r), 16 * g));
 }
 
-// max over the 64 lanes of one value (fused DPP inside rows), wave-uniform
-__device__ __forceinline__ float wave_max_uniform(float x) {
-    asm volatile("s_nop 1\n\t"
-                 "v_max_f32_dpp %0, %0, %0 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
-                 "s_nop 1\n\t"
-                 "v_max_f32_dpp %0, %0, %0 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
-                 "s_nop 1\n\t"
-                 "v_max_f32_dpp %0, %0, %0 row_ror:4 row_mask:0xf bank_mask:0xf\n\t"
-                 "s_nop 1\n\t"
-                 "v_max_f32_dpp %0, %0, %0 row_ror:8 row_mask:0xf bank_mask:0xf"
-                 : "+v"(x));
-    const float r0 = i2f(__builtin_amdgcn_readlane(f2i(x), 0)), r1 = i2f(__builtin_amdgcn_readlane(f2i(x), 16));
-    const float r2 = i2f(__builtin_amdgcn_readlane(f2i(x), 32)), r3 = i2f(__builtin_amdgcn_readlane(f2i(x), 48));
-    return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
-}
-
 // ---- D = 128: scores and value sums on the 32x32x32 int8 MFMA --------------
 //
 // One wave per (split, KV head, sequence), 64 tokens per step, as above, but
@@ -912,7 +899,8 @@ __global__ void __launch_bounds__(64) decode_split128_kernel(DecodeArgs a) {
     }
 
     // sequence length and page ids are wave-uniform (SGPRs)
-    const int L = __builtin_amdgcn_readfirstlane(min(a.seq_lens[b], a.max_pages * T));
+    const int bs = b / a.M;  // sequence of query row b (its quantized pages lie before every query token)
+    const int L = __builtin_amdgcn_readfirstlane(min(a.seq_lens[bs], a.max_pages * T));
     const int nq = (L - a.sink - a.tail >= T) ? (L - a.sink - a.tail) / T : 0;
     const int sp = a.sink / T;
 
@@ -930,7 +918,7 @@ __global__ void __launch_bounds__(64) decode_split128_kernel(DecodeArgs a) {
     const uint8_t* const vrec = static_cast<const uint8_t*>(a.v_records);
 
     // the split's page ids, 64 at a time, page 64 c + l in lane l
-    const int* const btrow = a.block_table + (int64_t)b * a.max_pages + sp + split;
+    const int* const btrow = a.block_table + (int64_t)bs * a.max_pages + sp + split;
     auto page_ids = [&](int c) {
         const int i = 64 * c + lane;
         const int id = i < npg ? btrow[(int64_t)i * a.nsplit] : -1;
@@ -1117,11 +1105,23 @@ __global__ void __launch_bounds__(64) decode_split128_kernel(DecodeArgs a) {
         // k-step ks covers tokens 32 half + 16 ks + perm16(j) ----
         {
             const float S = half_bits_to_float(u.vsz & 0xffffu), Z = half_bits_to_float(u.vsz >> 16);
-            const int e = frexp_exp(wave_max_uniform(S));
-            float E[G], pz[G];
+            // each head's weights p S_V scaled by 2^(21 - e), e the exponent of
+            // that head's largest weight of the step: every step keeps 21 bits
+            // relative to its own largest contribution (a step whose tokens all
+            // score far below the running maximum would otherwise keep only a
+            // few bits, and their rounding -- times non-negative codes -- would
+            // not cancel against the zero-point sum)
+            float ps[G], pmax[G], E[G], pz[G];
+#pragma unroll
+            for (int g = 0; g < G; g++) ps[g] = pmax[g] = p[g] * S;
+            float mxw[G];
+            wave_reduce4<true>(pmax, mxw);
+            float wsc[G];
 #pragma unroll
             for (int g = 0; g < G; g++) {
-                const uint32_t y = digits3(__builtin_amdgcn_ldexpf(p[g] * S, 21 - e));
+                const int e = frexp_exp(mxw[g]);
+                wsc[g] = __builtin_amdgcn_ldexpf(1.0f, e - 21);
+                const uint32_t y = digits3(__builtin_amdgcn_ldexpf(ps[g], 21 - e));
                 wt[(0 + g) * WROW + wpos] = (uint8_t)y;
                 wt[(4 + g) * WROW + wpos] = (uint8_t)(y >> 8);
                 wt[(8 + g) * WROW + wpos] = (uint8_t)(y >> 16);
@@ -1131,7 +1131,6 @@ __global__ void __launch_bounds__(64) decode_split128_kernel(DecodeArgs a) {
             wave_sync();
             const i4v aw0 = *reinterpret_cast<const i4v*>(wt + orow * WROW + 16 * (2 * half + 0));
             const i4v aw1 = *reinterpret_cast<const i4v*>(wt + orow * WROW + 16 * (2 * half + 1));
-            const float wsc = __builtin_amdgcn_ldexpf(1.0f, e - 21);
 #pragma unroll
             for (int sv = 0; sv < 2; sv++) {
                 i16v d0 = {}, d1 = {};
@@ -1141,7 +1140,7 @@ __global__ void __launch_bounds__(64) decode_split128_kernel(DecodeArgs a) {
                 d1 = mfma32_i8(aw1, codes16<VB>(&u.vw[2 * sv + 1][VB / 2]), d1);
                 const f4 R = pair_levels(d0, d1);  // channel 64 sv + lane
 #pragma unroll
-                for (int g = 0; g < G; g++) accr[sv][g] = fmaf(cvv[sv], fmaf(wsc, R[g], E[g]), accr[sv][g]);
+                for (int g = 0; g < G; g++) accr[sv][g] = fmaf(cvv[sv], fmaf(wsc[g], R[g], E[g]), accr[sv][g]);
             }
             wave_sync();  // the tables are rewritten by later steps
         }
@@ -1258,6 +1257,17 @@ __global__ void __launch_bounds__(D * combine_groups<D>()) decode_combine_kernel
     }
 }
 
+// Grid x of a split launch.  With several query rows per sequence (M > 1)
+// the rows of one sequence are adjacent in grid z; x is padded (the extra
+// workgroups return at once) so that x * y is a multiple of 8, which puts
+// the rows' workgroups -- dispatched to the 8 XCDs in turn by linear id -- on
+// one XCD, where they read the sequence's records through one L2.
+inline unsigned split_grid_x(unsigned gx, unsigned gy, int M) {
+    if (M > 1)
+        while ((gx * gy) % 8u) gx++;
+    return gx;
+}
+
 template <int D, int T, int KB, int VB>
 hipError_t launch_gqa(const DecodeArgs& a, hipStream_t st) {
     hipError_t e;
@@ -1269,7 +1279,7 @@ hipError_t launch_gqa(const DecodeArgs& a, hipStream_t st) {
     // one launch: the quantized-page splits (z < B), then the fp16 page slots
     constexpr int NWV = D == 128 ? 1 : split_waves<D>();
     const int nfx = (a.nfsplit + NWV - 1) / NWV;  // fp16 slots: one per wave
-    const dim3 grid(a.nsplit > nfx ? a.nsplit : nfx, a.H, a.nfsplit > 0 ? 2 * a.B : a.B);
+    const dim3 grid(split_grid_x(a.nsplit > nfx ? a.nsplit : nfx, a.H, a.M), a.H, a.nfsplit > 0 ? 2 * a.B : a.B);
     if constexpr (D == 128)
         hipLaunchKernelGGL((decode_split128_kernel<T, KB, VB>), grid, dim3(64), 0, st, a);
     else

@@ -157,19 +157,24 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
     __shared__ __attribute__((aligned(16))) uint8_t ring[NR * SLOT];
     __shared__ __attribute__((aligned(16))) uint8_t scratch[16 * NWV];  // targets of the stand-in loads
 
-    // Workgroup id -> (head group hg, split, sequence b).  Workgroups are dealt
-    // to the 8 XCDs round-robin; the head groups of one (split, sequence) get
-    // ids 8 apart, so they run on the same XCD at about the same time and read
-    // each latent chunk through that XCD's L2.
+    // Workgroup id -> (head group hg, query token m, split, sequence bs).
+    // Workgroups are dealt to the 8 XCDs round-robin; the head groups and the
+    // query tokens of one (split, sequence) get ids 8 apart, so they run on
+    // the same XCD at about the same time and read each latent chunk through
+    // that XCD's L2.  Unit v = bs * nsplit + split; ids come in runs of 8 * nhg
+    // per (v / 8, m).
     const int nhg = a.Hq / HQ;
-    const int units = a.B * a.nsplit;
+    const int units = (a.B / a.M) * a.nsplit;
     const int wid = blockIdx.x;
     const int hg = (wid % (8 * nhg)) / 8;
-    const int u = (wid / (8 * nhg)) * 8 + (wid % 8);
-    if (u >= units) return;
+    const int g8 = wid / (8 * nhg);
+    const int mtok = g8 % a.M;
+    const int v = (g8 / a.M) * 8 + (wid % 8);
+    if (v >= units) return;
     // workgroup-uniform: held in scalar registers
-    const int b = __builtin_amdgcn_readfirstlane(u / a.nsplit);
-    const int split = __builtin_amdgcn_readfirstlane(u - b * a.nsplit);
+    const int bs = __builtin_amdgcn_readfirstlane(v / a.nsplit);
+    const int split = __builtin_amdgcn_readfirstlane(v - bs * a.nsplit);
+    const int b = __builtin_amdgcn_readfirstlane(bs * a.M + mtok);  // query row
     const int h0 = __builtin_amdgcn_readfirstlane(hg * HQ);  // first query head of this workgroup
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, g4 = lane >> 4;
@@ -205,9 +210,11 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
         lp[i] = 0.f;
     }
 
-    const int L = min(a.seq_lens[b], a.max_pages * T);
+    // regions by the committed length; the row attends its first A tokens
+    const int Lc = min(a.seq_lens[bs], a.max_pages * T);
+    const int L = attend_len(a, b, Lc, a.max_pages * T);
     const int npages = L > 0 ? (L + T - 1) / T : 0;
-    const int nq = (L - a.sink - a.tail >= T) ? (L - a.sink - a.tail) / T : 0;
+    const int nq = (Lc - a.sink - a.tail >= T) ? (Lc - a.sink - a.tail) / T : 0;
     const int sp = min(a.sink / T, npages);
     const int nf = npages - nq;                           // fp16 pages: sink, then tail
     const int qbeg = sp + (int)(((int64_t)nq * split) / a.nsplit);
@@ -224,8 +231,8 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
     for (int r = 0; r < 2; r++) {
         const int k = 64 * r + lane;
         pid[r] = -1;
-        if (k < nqp) pid[r] = a.block_table[(int64_t)b * a.max_pages + qbeg + k];
-        else if (k < nqp + nfp) pid[r] = a.block_table[(int64_t)b * a.max_pages + fpage(k - nqp)];
+        if (k < nqp) pid[r] = a.block_table[(int64_t)bs * a.max_pages + qbeg + k];
+        else if (k < nqp + nfp) pid[r] = a.block_table[(int64_t)bs * a.max_pages + fpage(k - nqp)];
         asm volatile("" ::"v"(pid[r]));  // loaded before any LDS-DMA load is in flight
     }
     auto page_id = [&](int k) {  // k wave-uniform, < 128
@@ -632,8 +639,8 @@ hipError_t launch_mla_t(const DecodeArgs& a, hipStream_t st) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int nhg = a.Hq / (16 * HB);
-    const int units = a.B * a.nsplit;
-    const int blocks = ((units + 7) / 8) * 8 * nhg;
+    const int units = (a.B / a.M) * a.nsplit;
+    const int blocks = ((units + 7) / 8) * 8 * nhg * a.M;
     hipLaunchKernelGGL((mla_split_kernel<T, HB>), dim3(blocks), dim3(MlaShape<HB>::NT), 0, st, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;

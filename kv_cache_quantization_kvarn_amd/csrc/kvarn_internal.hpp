@@ -35,7 +35,10 @@ hipError_t launch_quantize_one(const QuantizeArgs& a, hipStream_t st);
 struct DecodeArgs {
     int D, T, k_bits, v_bits, sink, tail, H, mla;
     int G;            // query heads per KV head (MLA: all query heads)
-    int B, Hq, max_pages;
+    int B, Hq, max_pages;  // B: query rows = sequences x query tokens (row b = sequence b / M, token b % M)
+    int M;            // query tokens per sequence (1 for a plain decode step)
+    int causal;       // 0: every row attends the seq_lens tokens; 1: token i of a sequence sits at
+                      // position seq_lens + i and attends seq_lens + i + 1 tokens (its own included)
     int nsplit;       // splits of each sequence (GQA: over its quantized pages)
     int nfsplit;      // GQA: fp16 slots (64-token parts of fp16 pages) of each sequence, one workgroup each
     int pps;          // pages per split
@@ -52,6 +55,15 @@ struct DecodeArgs {
     float* out;
     float* ws;        // split partials
 };
+
+// Attend length of query row b: the region rule uses seq_lens of its sequence
+// (committed tokens); a causal row also sees the uncommitted query tokens up
+// to and including its own.
+__device__ __forceinline__ int attend_len(const DecodeArgs& a, int b, int L, int cap) {
+    if (!a.causal) return L;
+    const int A = L + (b % a.M) + 1;
+    return A < cap ? A : cap;
+}
 
 // Split plan shared by the workspace query and the launch.
 void decode_plan(int D, int H, int G, int mla, int B, int max_pages, int T, int kb, int vb, int* nsplit,

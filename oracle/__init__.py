@@ -57,6 +57,7 @@ def _load():
     lib.orc_quantized_pages.argtypes = [P, i32]
     lib.orc_decode.argtypes = [P, P, P, P, P, P, P, i32, P, i32, i32, dbl, P, i32, P, i32]
     lib.orc_decode_groups.argtypes = [P, P, P, P, P, P, P, i32, P, i32, i32, dbl, P, i32, P, i32]
+    lib.orc_decode_mq.argtypes = [P, P, P, P, P, P, P, i32, P, i32, i32, i32, dbl, P, i32, P, i32]
     _lib = lib
     return lib
 
@@ -285,3 +286,28 @@ def commit_plan(layout, block_table, seq_lens, n_accept, new_qpages, n_fpages, n
             bt[b, p] = dst
         sl[b] = L + a
     return bt, sl, promoted
+
+
+def decode_mq(layout, krec, vrec, k16, v16, block_table, seq_lens, q, Hq, sm_scale, rows=None, n_threads=0):
+    """Verify-step decode by its plain definition: q [B, M, Hq, D] (float32,
+    or uint16 bfloat16 bits), token i of sequence b at position
+    seq_lens[b] + i attending every token up to and including itself; the
+    quantized region is that of the seq_lens[b] committed tokens.
+    Returns float64 [B, M, Hq, D] (rows None) or [n_rows, D] for (b, i, h) rows."""
+    cfg = _cfg(layout)
+    block_table = _c(block_table, np.int32)
+    seq_lens = _c(seq_lens, np.int32)
+    B, max_pages = block_table.shape
+    is_bf16 = q.dtype == np.uint16
+    q = np.ascontiguousarray(q)
+    M = int(q.shape[1])
+    D = int(layout["D"])
+    full = rows is None
+    if full:
+        rows = np.array([(b, i, h) for b in range(B) for i in range(M) for h in range(Hq)], np.int32)
+    rows = _c(rows, np.int32).reshape(-1, 3)
+    out = np.zeros((len(rows), D), np.float64)
+    _load().orc_decode_mq(_p(cfg), _p(krec), _p(vrec), _p(k16), _p(v16), _p(block_table), _p(seq_lens),
+                          int(max_pages), _p(q), int(is_bf16), M, int(Hq), float(sm_scale), _p(rows), len(rows),
+                          _p(out), int(n_threads))
+    return out.reshape(B, M, Hq, D) if full else out

@@ -450,21 +450,22 @@ int orc_quantized_pages(const int32_t *cfg, int L)
 /* pairs: n_pairs (b, h) pairs; out: [n_pairs][D].                          */
 /* ------------------------------------------------------------------------ */
 
-/* Read back every token t < L of sequence b, KV head g: dequantized record
+/* Read back every token t < La of sequence b, KV head g: dequantized record
  * values (rotated back to the original basis) for pages in the quantized
- * region, the stored fp16 values for the sink and tail.  Kh, Vh: at least
- * ceil(L / T) * T * D doubles each. */
+ * region of a sequence of Lr tokens, the stored fp16 values elsewhere (sink,
+ * tail, and tokens past Lr).  Kh, Vh: at least ceil(La / T) * T * D doubles
+ * each. */
 static void read_back(const int32_t *cfg, const uint8_t *krec, const uint8_t *vrec,
                       const uint16_t *k16, const uint16_t *v16,
-                      const int32_t *block_table, int max_pages, int b, int g, int L,
+                      const int32_t *block_table, int max_pages, int b, int g, int Lr, int La,
                       double *Kh, double *Vh)
 {
     int T = cfg[C_T], D = cfg[C_D], H = cfg[C_H], mla = cfg[C_MLA];
     int sink_pages = cfg[C_SINK] / T;
     int64_t kb = orc_record_bytes(T, D, cfg[C_KB]);
     int64_t vb = orc_record_bytes(T, D, cfg[C_VB]);
-    int nq = orc_quantized_pages(cfg, L);
-    int npages = (L + T - 1) / T;
+    int nq = orc_quantized_pages(cfg, Lr);
+    int npages = (La + T - 1) / T;
     for (int p = 0; p < npages; p++) {
         int id = block_table[(int64_t)b * max_pages + p];
         int quant = (p >= sink_pages) && (p < sink_pages + nq);
@@ -548,7 +549,7 @@ int orc_decode(const int32_t *cfg, const uint8_t *krec, const uint8_t *vrec,
         double *Kh = (double *)malloc(sizeof(double) * (size_t)npages * T * D + 8);
         double *Vh = (double *)malloc(sizeof(double) * (size_t)npages * T * D + 8);
         load_query(q, q_is_bf16, Hq, D, b, h, qv);
-        read_back(cfg, krec, vrec, k16, v16, block_table, max_pages, b, h / G, L, Kh, Vh);
+        read_back(cfg, krec, vrec, k16, v16, block_table, max_pages, b, h / G, L, L, Kh, Vh);
         attend(qv, Kh, Vh, L, D, sm_scale, out + (int64_t)pi * D);
         free(qv); free(Kh); free(Vh);
     }
@@ -579,11 +580,50 @@ int orc_decode_groups(const int32_t *cfg, const uint8_t *krec, const uint8_t *vr
         double *qv = (double *)malloc(sizeof(double) * D);
         double *Kh = (double *)malloc(sizeof(double) * (size_t)npages * T * D + 8);
         double *Vh = (double *)malloc(sizeof(double) * (size_t)npages * T * D + 8);
-        read_back(cfg, krec, vrec, k16, v16, block_table, max_pages, b, g, L, Kh, Vh);
+        read_back(cfg, krec, vrec, k16, v16, block_table, max_pages, b, g, L, L, Kh, Vh);
         for (int k = 0; k < G; k++) {
             load_query(q, q_is_bf16, Hq, D, b, g * G + k, qv);
             attend(qv, Kh, Vh, L, D, sm_scale, out + ((int64_t)gi * G + k) * D);
         }
+        free(qv); free(Kh); free(Vh);
+    }
+    return 0;
+}
+
+/* Verify-step decode, by its plain definition: M query tokens per sequence,
+ * token i of sequence b at position L_b + i (L_b = seq_lens[b], the
+ * committed tokens; the M tokens are appended after them), causal among
+ * themselves [G "Speed and speculative decoding"]:
+ *   out(b, i, h) = sum_{t <= L_b + i} softmax_t(sm_scale * <q(b, i, h), k_t>) v_t,
+ * the tokens read back as in orc_decode with the quantized region of a
+ * sequence of L_b tokens (tokens from L_b on are fp16).
+ * q: [batch][M][Hq][D]; rows: n (b, i, h) triples; out: [n][D]. */
+int orc_decode_mq(const int32_t *cfg, const uint8_t *krec, const uint8_t *vrec,
+                  const uint16_t *k16, const uint16_t *v16,
+                  const int32_t *block_table, const int32_t *seq_lens, int max_pages,
+                  const void *q, int q_is_bf16, int M, int Hq, double sm_scale,
+                  const int32_t *rows, int n_rows, double *out, int n_threads)
+{
+    int T = cfg[C_T], D = cfg[C_D], H = cfg[C_H];
+    int G = Hq / H;
+#ifdef _OPENMP
+    if (n_threads > 0)
+        omp_set_num_threads(n_threads);
+#pragma omp parallel for schedule(dynamic, 1)
+#endif
+    for (int ri = 0; ri < n_rows; ri++) {
+        int b = rows[3 * ri], i = rows[3 * ri + 1], h = rows[3 * ri + 2];
+        int Lr = seq_lens[b];
+        int La = Lr + i + 1;
+        if (La > max_pages * T)
+            La = max_pages * T;
+        int npages = (La + T - 1) / T;
+        double *qv = (double *)malloc(sizeof(double) * D);
+        double *Kh = (double *)malloc(sizeof(double) * (size_t)npages * T * D + 8);
+        double *Vh = (double *)malloc(sizeof(double) * (size_t)npages * T * D + 8);
+        load_query(q, q_is_bf16, Hq, D, b * M + i, h, qv);
+        read_back(cfg, krec, vrec, k16, v16, block_table, max_pages, b, h / G, Lr, La, Kh, Vh);
+        attend(qv, Kh, Vh, La, D, sm_scale, out + (int64_t)ri * D);
         free(qv); free(Kh); free(Vh);
     }
     return 0;

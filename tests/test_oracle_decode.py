@@ -221,3 +221,83 @@ def test_commit_plan_promotes_exactly_the_pages_entering_the_quantized_region(T,
     # refusals leave the sequence unchanged
     bad = oracle.commit_plan(lay, bt[:2], [10, 10], [T + 1, -1], newq[:2], B * max_pages, 2000)
     assert list(bad[2]) == [-2, -2] and list(bad[1]) == [10, 10]
+
+
+def _mq_case(lens, M, **over):
+    """Sequences of lens[b] committed tokens plus M appended query tokens:
+    the pools hold L + M tokens, the records only the pages of the committed
+    length's quantized region (pages that L + M alone would move out of the
+    tail stay fp16, as before their commit)."""
+    w = small(**over)
+    c = make_case(w, seq_lens=[L + M for L in lens], batch=len(lens))
+    krec, vrec = quantized_pools(c)
+    lay = c["layout"]
+    T, sp = lay["T"], lay["sink"] // lay["T"]
+    bt = c["block_table"].numpy().copy()
+    src = c["src"].numpy()
+    base = 0
+    for b, L in enumerate(lens):
+        n_all, n_com = oracle.quantized_pages(lay, L + M), oracle.quantized_pages(lay, L)
+        for i in range(n_com, n_all):
+            bt[b, sp + i] = src[base + i]   # back to the fp16 page
+        base += n_all
+    c["block_table"] = torch.from_numpy(bt)
+    c["seq_lens"] = torch.tensor(lens, dtype=torch.int32)
+    return c, krec, vrec
+
+
+def _readback_mq(c, krec, vrec, b, g, Lr, La):
+    lay = c["layout"]
+    T, D = lay["T"], lay["D"]
+    k16, v16, bt, _, _ = np_case(c)
+    nq = oracle.quantized_pages(lay, Lr)
+    sp = lay["sink"] // T
+    K, V = [], []
+    for p in range(math.ceil(La / T)):
+        if sp <= p < sp + nq:
+            K.append(oracle.dequantize_record(krec[bt[b, p], g], T, D, lay["k_bits"]))
+            V.append(oracle.dequantize_record(vrec[bt[b, p], g], T, D, lay["v_bits"], True))
+        else:
+            K.append(k16[bt[b, p], g].view(np.float16).astype(np.float64))
+            V.append(v16[bt[b, p], g].view(np.float16).astype(np.float64))
+    return np.concatenate(K)[:La], np.concatenate(V)[:La]
+
+
+@pytest.mark.parametrize("M", [1, 2, 4])
+def test_verify_decode_is_causal_attention_over_the_committed_regions(M):
+    """gmlx "Speed and speculative decoding": up to four tokens a row are
+    verified at once.  Token i attends the first L + i + 1 tokens; the
+    records cover only the committed length's quantized region (lengths
+    chosen so that L + M crosses a page boundary of the region rule for some
+    sequences)."""
+    lens = [1024 - 1, 1151, 777, 1279, 1152 - M + 1]
+    c, krec, vrec = _mq_case(lens, M, sink=128, tail=256, permute=True)
+    lay = c["layout"]
+    k16, v16, bt, sl, _ = np_case(c)
+    Hq = c["Hq"]
+    q = np.random.default_rng(M).standard_normal((len(lens), M, Hq, lay["D"])).astype(np.float32)
+    out = oracle.decode_mq(lay, krec, vrec, k16, v16, bt, sl, q, Hq, c["sm_scale"])
+    crossing = 0
+    for b, L in enumerate(lens):
+        crossing += oracle.quantized_pages(lay, L + M) > oracle.quantized_pages(lay, L)
+        for i in range(M):
+            for h in (0, 13, Hq - 1):
+                K, V = _readback_mq(c, krec, vrec, b, h // 4, L, L + i + 1)
+                ref = sdpa_reference(K, V, q[b, i, h], c["sm_scale"])
+                assert np.allclose(out[b, i, h], ref, rtol=1e-11, atol=1e-12), (b, i, h)
+    if M > 1:
+        assert crossing >= 1
+
+
+def test_verify_decode_of_one_token_is_decode_of_one_more_token():
+    # where L + 1 moves no page into the quantized region, one verified token
+    # is a plain decode step over L + 1 tokens
+    lens = [1000, 1200, 1300]
+    c, krec, vrec = _mq_case(lens, 1, sink=128, tail=256, permute=True)
+    lay = c["layout"]
+    assert all(oracle.quantized_pages(lay, L + 1) == oracle.quantized_pages(lay, L) for L in lens)
+    k16, v16, bt, sl, _ = np_case(c)
+    q = np.random.default_rng(0).standard_normal((3, 1, c["Hq"], lay["D"])).astype(np.float32)
+    a = oracle.decode_mq(lay, krec, vrec, k16, v16, bt, sl, q, c["Hq"], c["sm_scale"])
+    b = oracle.decode(lay, krec, vrec, k16, v16, bt, sl + 1, q[:, 0], c["Hq"], c["sm_scale"])
+    assert np.array_equal(a[:, 0], b)
