@@ -29,6 +29,8 @@ Reported (one JSON line):
              records written) and decode, each as GB/s and fraction of HBM
              peak, median with p10 / p90 of the per-call times; the MLA decode
              also as a fraction of the fp16 MFMA peak (its roofline).
+             The headline workload also times a verify step (decode of 4
+             uncommitted query tokens per sequence, causal among themselves).
   cpu_baseline the oracle (plain C, fp64, OpenMP) on a bounded sample of the
              headline workload, same byte formulas; per_core: the oracle on
              one thread over the one-layer 1024-token case.
@@ -210,8 +212,72 @@ class Runner:
             comp["note"] = "cache-resident (fits L2 and the last-level cache): parity case, not a bandwidth figure"
         return comp
 
+    def verify_setup(self, M):
+        """A verify step over the same pools: the last M tokens of every
+        sequence become uncommitted query tokens (committed length L - M; pages
+        that only L would have quantized point back to their fp16 pages)."""
+        torch, kv, c = self.torch, self.kv, self.case
+        lay = c["layout"]
+        T, sp = lay["T"], lay["sink"] // lay["T"]
+        nq = lambda L: max(0, (L - lay["sink"] - lay["tail"]) // T)
+        bt = c["block_table"].cpu().numpy().copy()
+        src = c["src"].cpu().numpy()
+        lens = c["seq_lens"].cpu().tolist()
+        base = 0
+        for b, L in enumerate(lens):
+            for i in range(nq(L - M), nq(L)):
+                bt[b, sp + i] = src[base + i]
+            base += nq(L)
+        dev = c["q"].device
+        self.v_M = M
+        self.v_bt = torch.tensor(bt, device=dev)
+        self.v_lens = torch.tensor([L - M for L in lens], dtype=torch.int32, device=dev)
+        from synth import normal
+
+        B, Hq, D = c["B"], c["Hq"], lay["D"]
+        self.v_q = normal(self.w["seed"], 60, B * M * Hq * D, device=dev).view(B, M, Hq, D).to(c["q"].dtype)
+        self.v_out = torch.empty((B, M, Hq, D), dtype=torch.float32, device=dev)
+        n = kv.decode_workspace_bytes_mq(self.L, B, M, Hq, c["max_pages"])
+        self.v_ws = torch.empty(max(n, 256), dtype=torch.uint8, device=dev)
+        rec = lambda bits: T * D * bits // 8 + 4 * T + 2 * D
+        kinds = [lay["k_bits"]] if lay["mla"] else [lay["k_bits"], lay["v_bits"]]
+        byts = 0
+        for L in lens:
+            n_q = nq(L - M)
+            byts += n_q * lay["H"] * sum(rec(bb) for bb in kinds) + (L - n_q * T) * lay["H"] * D * 2 * len(kinds)
+        byts += self.v_q.numel() * self.v_q.element_size() + self.v_out.numel() * 4
+        self.v_bytes = byts
+
+    def verify(self):
+        c = self.case
+        self.kv.decode_attn_mq(self.L, self.krec, self.vrec, c["k16"], c["v16"], self.v_bt, self.v_lens, self.v_q,
+                               c["sm_scale"], out=self.v_out, workspace=self.v_ws)
+
+    def time_verify(self, steps, warmup, flush):
+        torch = self.torch
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ts = []
+        for i in range(warmup + steps):
+            flush()
+            e0.record()
+            self.verify()
+            e1.record()
+            torch.cuda.synchronize()
+            if i >= warmup:
+                ts.append(e0.elapsed_time(e1) * 1e-3)
+        st = stats(ts)
+        return {"query_tokens": self.v_M, "us": round(st["median"], 2), "us_p10": round(st["p10"], 2),
+                "us_p90": round(st["p90"], 2), "bytes": self.v_bytes,
+                "GBs": round(self.v_bytes / st["median"] / 1e3, 1),
+                "frac": round(self.v_bytes / st["median"] / 1e3 / HBM_PEAK_GBS, 4),
+                "note": "verify step: M uncommitted query tokens per sequence, causal among themselves, one read of "
+                        "the cache; bytes = cache + q + out"}
+
     def free(self):
         del self.case, self.krec, self.vrec, self.out, self.ws
+        for k in ("v_bt", "v_lens", "v_q", "v_out", "v_ws"):
+            if hasattr(self, k):
+                delattr(self, k)
         self.torch.cuda.empty_cache()
 
 
@@ -224,6 +290,8 @@ def main():
     ap.add_argument("--component-steps", type=int, default=20,
                     help="timed calls per other workload of the suite (0: headline only)")
     ap.add_argument("--component-warmup", type=int, default=3)
+    ap.add_argument("--verify-tokens", type=int, default=4,
+                    help="query tokens per sequence of the headline workload's verify-step component (0: none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-records", type=int, default=0,
                     help="records in the oracle's quantize sample (0: every record of the workload)")
@@ -295,6 +363,10 @@ def main():
                      "traffic": recorded_traffic(args.workload)},
         "components": {args.workload: head},
     }
+    if args.verify_tokens > 0:
+        run.verify_setup(args.verify_tokens)
+        res["components"][args.workload]["verify"] = run.time_verify(args.component_steps or 10, 3, flush)
+        print(f"[bench] verify step with {args.verify_tokens} query tokens timed", file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(run.case, run.krec, run.vrec, args.cpu_records, args.cpu_rows)
         print(f"[bench] oracle timed on the host", file=sys.stderr, flush=True)
