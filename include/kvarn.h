@@ -41,7 +41,9 @@
  * 16 for every supported shape):
  *   [0, T*D*b/8)         codes, element e in bits [e*b, e*b+b), LSB first;
  *                        K and the MLA latent token-major (e = t*D + j),
- *                        V channel-major (e = j*T + t)
+ *                        V channel-major in blocks of TB = min(T, 64) tokens
+ *                        (e = (t/TB)*TB*D + j*TB + t%TB: block by block, each
+ *                        channel's TB codes in a row)
  *   next 4*T bytes       per token t: fp16 scale S_t, then fp16 zero-point Zp_t
  *   next 2*D bytes       per channel j: fp16 column scale C_j
  * A stored value reads back, in the rotated basis, as

@@ -399,6 +399,10 @@ __global__ void __launch_bounds__(64 * split_waves<D>(), 3) decode_split_kernel(
     // the wave's value words of a step prefetched one step ahead (24 words at most)
     constexpr bool PREV = NS * VHW <= 24;
     static_assert(VRW == TS * VHW, "a channel row is TS halves");
+    // value codes of channel c over the 64 tokens of step half hh: records
+    // keep values in 64-token blocks, each channel's 64 codes in a row, so a
+    // step reads one contiguous run of the record
+    auto vseg = [](int hh, int c) -> int64_t { return (int64_t)hh * (64 * D * VB / 8) + (int64_t)c * (8 * VB); };
     const int npg = nq > split ? (nq - split + a.nsplit - 1) / a.nsplit : 0;  // quantized pages of this split
     const int nst = npg * TS;
     const uint8_t* const krec = static_cast<const uint8_t*>(a.k_records);
@@ -455,7 +459,7 @@ __global__ void __launch_bounds__(64 * split_waves<D>(), 3) decode_split_kernel(
         const uint8_t* rv = vrec + ((int64_t)r.id * a.H + h) * VREC;
 #pragma unroll
         for (int sv = 0; sv < NS; sv++) {
-            if constexpr (PREV) load_seg<VHW>(vw[sv], rv + (int64_t)(64 * (NS * wave + sv) + lane) * VROW + r.h * (4 * VHW));
+            if constexpr (PREV) load_seg<VHW>(vw[sv], rv + vseg(r.h, 64 * (NS * wave + sv) + lane));
             if (r.h == 0) {
                 const uint32_t c16 = reinterpret_cast<const uint16_t*>(rv + VCB + 4 * T)[64 * (NS * wave + sv) + lane];
                 cvr[sv >> 1] = (sv & 1) ? (cvr[sv >> 1] | (c16 << 16)) : c16;
@@ -599,7 +603,7 @@ __global__ void __launch_bounds__(64 * split_waves<D>(), 3) decode_split_kernel(
 #pragma unroll
                     for (int kk = 0; kk < VHW; kk++) w[kk] = vw[sv][PREV ? kk : 0];
                 } else {
-                    load_seg<VHW>(w, rv + (int64_t)(64 * (NS * wave + sv) + lane) * VROW + cur.h * (4 * VHW));
+                    load_seg<VHW>(w, rv + vseg(cur.h, 64 * (NS * wave + sv) + lane));
                 }
                 f4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
                 static_for<16>([&](auto ic) {
@@ -808,7 +812,6 @@ __global__ void __launch_bounds__(64) decode_split128_kernel(DecodeArgs a) {
     constexpr int VREC = VCB + 4 * T + 2 * D;
     constexpr int KROW = D * KB / 8;      // code bytes of a token
     constexpr int KW = KROW / 8;          // words of half a token row (64 channels)
-    constexpr int VROW = T * VB / 8;      // code bytes of a channel (whole page)
     constexpr int VW = VB;                // words of 32 tokens of a channel
     constexpr int WS = D + 4;           // partial: m, l, pad, pad, value sums
     constexpr int QROW = D, WROW = 64;    // bytes per row of the query / weight digit tables
@@ -974,8 +977,10 @@ __global__ void __launch_bounds__(64) decode_split128_kernel(DecodeArgs a) {
         }
 #pragma unroll
         for (int i = 0; i < VST / 1024; i++) {
-            const int u = 64 * i + lane;   // piece u: channel u / (VB / 2), part u % (VB / 2)
-            lds_dma16(sb + VSO + 1024 * i, rsv, (u / (VB / 2)) * VROW + 16 * (u % (VB / 2)), sv + 8 * VB * r.h);
+            // piece u = channel u / (VB / 2), part u % (VB / 2): values are kept
+            // in 64-token blocks, so a step's pieces are one contiguous run
+            const int u = 64 * i + lane;
+            lds_dma16(sb + VSO + 1024 * i, rsv, 16 * u, sv + (64 * D * VB / 8) * r.h);
         }
     };
     // the lane's operands of a step out of the stage (after its loads have

@@ -448,7 +448,13 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ tile,
     // byte per code (record order), which for 8 bits is the record itself
     constexpr bool BYTE_IMAGE = BITS == 3 || BITS == 5 || BITS == 8;
     static_assert(BITS == 2 || BITS == 3 || BITS == 4 || BITS == 5 || BITS == 6 || BITS == 8, "code width");
-    static_assert(BYTE_IMAGE || CODE_BYTES + 4 * (D / 16) <= S::SMEM_CODES, "the code image and its channel-row pad fit");
+    // channel-major codes go in blocks of TB tokens (record format: block by
+    // block, each channel's TB codes in a row), so a 64-token step of the
+    // decode reads one contiguous run
+    constexpr int TB = T < 64 ? T : 64;
+    static_assert(T % TB == 0 && TB % 4 == 0, "whole token blocks; a lane's 4 tokens in one block");
+    static_assert(BYTE_IMAGE || CODE_BYTES + (T / TB) * 4 * (D / 16) <= S::SMEM_CODES,
+                  "the code image and its channel-row pads fit");
     static_assert(T * D <= S::SMEM_CODES, "one byte per code fits");
 
     float* colpart = reinterpret_cast<float*>(smem + S::PART_OFF);
@@ -702,10 +708,11 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ tile,
                                pk4(x[12], x[13], x[14], x[15]));
             }
         } else {
-            // channel row c: codes of tokens row0 .. row0 + 3 at bytes c T + row0 ..
+            // channel row c of token block row0 / TB: codes of tokens row0 .. row0 + 3
 #pragma unroll
             for (int c = 0; c < QC; c++)
-                *reinterpret_cast<uint32_t*>(img + (ch0 + c) * T + row0) = pk4(u[0][c], u[1][c], u[2][c], u[3][c]);
+                *reinterpret_cast<uint32_t*>(img + (row0 / TB) * (D * TB) + (ch0 + c) * TB + row0 % TB) =
+                    pk4(u[0][c], u[1][c], u[2][c], u[3][c]);
         }
     } else if constexpr (!CHMAJOR) {
         // token-major: this lane's 16 codes of a row are contiguous
@@ -742,10 +749,14 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ tile,
         }
     } else {
         // channel-major: this lane's 4 tokens of a channel are contiguous.
-        // Channel c's row of the image starts at cm_off(c): 4 bytes of pad
+        // In the image, token block k (TB tokens) starts at k CM_BLK and
+        // channel c's row of it at c TB BITS / 8 + 4 (c >> 4): 4 bytes of pad
         // after every 16 channels put the rows of the D/16 lanes that store
         // the same code position of their channels on different banks.
-        auto cm_off = [](int c) { return c * (T * BITS / 8) + 4 * (c >> 4); };
+        constexpr int CM_BLK = D * TB * BITS / 8 + 4 * (D / 16);
+        auto cm_at = [](int c, int t) {
+            return (t / TB) * CM_BLK + c * (TB * BITS / 8) + 4 * (c >> 4) + (t % TB) * BITS / 8;
+        };
         if constexpr (BITS == 2) {
             // byte of channel c = its 4 codes, token-ascending, 2 bits each
 #pragma unroll
@@ -755,7 +766,7 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ tile,
                 for (int r = 0; r < QR; r++) p[r] = pk4(u[r][4 * c4], u[r][4 * c4 + 1], u[r][4 * c4 + 2], u[r][4 * c4 + 3]);
                 const uint32_t v = p[0] | (p[1] << 2) | (p[2] << 4) | (p[3] << 6);  // byte k: channel 4 c4 + k
 #pragma unroll
-                for (int k = 0; k < 4; k++) img[cm_off(ch0 + 4 * c4 + k) + row0 / 4] = (uint8_t)(v >> (8 * k));
+                for (int k = 0; k < 4; k++) img[cm_at(ch0 + 4 * c4 + k, row0)] = (uint8_t)(v >> (8 * k));
             }
         } else if constexpr (BITS == 4) {
             // 16 bits of channel c: (c_t0 | c_t1 << 4) then (c_t2 | c_t3 << 4)
@@ -768,16 +779,16 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ tile,
                 const uint32_t w01 = __builtin_amdgcn_perm(hi, lo, 0x05010400u);  // channels 0, 1
                 const uint32_t w23 = __builtin_amdgcn_perm(hi, lo, 0x07030602u);  // channels 2, 3
                 const int c0 = ch0 + 4 * c4;
-                *reinterpret_cast<uint16_t*>(img + cm_off(c0) + row0 / 2) = (uint16_t)w01;
-                *reinterpret_cast<uint16_t*>(img + cm_off(c0 + 1) + row0 / 2) = (uint16_t)(w01 >> 16);
-                *reinterpret_cast<uint16_t*>(img + cm_off(c0 + 2) + row0 / 2) = (uint16_t)w23;
-                *reinterpret_cast<uint16_t*>(img + cm_off(c0 + 3) + row0 / 2) = (uint16_t)(w23 >> 16);
+                *reinterpret_cast<uint16_t*>(img + cm_at(c0, row0)) = (uint16_t)w01;
+                *reinterpret_cast<uint16_t*>(img + cm_at(c0 + 1, row0)) = (uint16_t)(w01 >> 16);
+                *reinterpret_cast<uint16_t*>(img + cm_at(c0 + 2, row0)) = (uint16_t)w23;
+                *reinterpret_cast<uint16_t*>(img + cm_at(c0 + 3, row0)) = (uint16_t)(w23 >> 16);
             }
         } else {
 #pragma unroll
             for (int c = 0; c < QC; c++) {
                 const uint32_t v = pack6x4(fq(0, c), fq(1, c), fq(2, c), fq(3, c));
-                uint8_t* d8 = img + cm_off(ch0 + c) + row0 * 6 / 8;
+                uint8_t* d8 = img + cm_at(ch0 + c, row0);
                 d8[0] = (uint8_t)v;
                 d8[1] = (uint8_t)(v >> 8);
                 d8[2] = (uint8_t)(v >> 16);
@@ -849,10 +860,13 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ tile,
         for (int k = 0; k < UNITS; k++) {
             const int u = tid + k * NT;
             if constexpr (CHMAJOR) {
-                // unit u lies in channel row 16 u / (T BITS / 8) (rows are 16-byte
-                // multiples), shifted by that row's pad: 4-byte aligned
-                static_assert((T * BITS / 8) % 16 == 0, "channel rows of whole 16-byte units");
-                const uint32_t* p = reinterpret_cast<const uint32_t*>(img + 16 * u + 4 * ((16 * u / (T * BITS / 8)) >> 4));
+                // unit u lies in token block 16 u / RBLK, channel row o / (TB BITS / 8)
+                // of it (rows are 16-byte multiples), shifted by the block's and
+                // the row's pads: 4-byte aligned
+                constexpr int RROW = TB * BITS / 8, RBLK = D * RROW, CM_BLK = RBLK + 4 * (D / 16);
+                static_assert(RROW % 16 == 0, "channel rows of whole 16-byte units");
+                const int blk = 16 * u / RBLK, o = 16 * u - blk * RBLK;
+                const uint32_t* p = reinterpret_cast<const uint32_t*>(img + blk * CM_BLK + o + 4 * ((o / RROW) >> 4));
                 dst4[u] = make_uint4(p[0], p[1], p[2], p[3]);
             } else {
                 int pu = u;

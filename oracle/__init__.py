@@ -172,7 +172,12 @@ def split_record(rec, T, D, bits, channel_major=False):
     rec = _c(rec, np.uint8)
     nb = T * D * bits // 8
     flat = unpack(rec[:nb], T * D, bits)
-    codes = flat.reshape(D, T).T.copy() if channel_major else flat.reshape(T, D)
+    if channel_major:
+        # blocks of min(T, 64) tokens, each channel's codes of a block in a row
+        TB = min(T, 64)
+        codes = flat.reshape(T // TB, D, TB).transpose(0, 2, 1).reshape(T, D).copy()
+    else:
+        codes = flat.reshape(T, D)
     sz = rec[nb:nb + 4 * T].view(np.uint16).reshape(T, 2)
     C = rec[nb + 4 * T:nb + 4 * T + 2 * D].view(np.uint16)
     f = lambda a: a.view(np.float16).astype(np.float64)

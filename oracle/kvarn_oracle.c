@@ -315,6 +315,20 @@ static uint16_t get_u16(const uint8_t *p)
     return (uint16_t)(p[0] | (p[1] << 8));
 }
 
+/* Position of the code of token t, channel j in a record's code stream.
+ * Token-major: e = t D + j.  Channel-major: tokens in blocks of TB =
+ * min(T, 64); block by block, each channel's TB codes in a row:
+ * e = (t / TB) TB D + j TB + t % TB (for T <= 64 simply j T + t).  The pages
+ * leave the order open; this one makes the codes of one 64-token block a
+ * contiguous run. */
+static int64_t code_pos(int T, int D, int t, int j, int channel_major)
+{
+    if (!channel_major)
+        return (int64_t)t * D + j;
+    int TB = T < 64 ? T : 64;
+    return (int64_t)(t / TB) * TB * D + (int64_t)j * TB + t % TB;
+}
+
 /* ------------------------------------------------------------------------ */
 /* One record: fp16 tile -> stages 2..4 -> packed bytes.                    */
 /* Outputs (optional, may be NULL): u (T*D), lc (D), lr (T) for the checks. */
@@ -342,8 +356,7 @@ int orc_quantize_record(const uint16_t *x16, int T, int D, int bits, int n_iters
 
     for (int t = 0; t < T; t++)
         for (int j = 0; j < D; j++) {
-            int64_t e = channel_major ? (int64_t)j * T + t : (int64_t)t * D + j;
-            qo[e] = q[(int64_t)t * D + j];
+            qo[code_pos(T, D, t, j, channel_major)] = q[(int64_t)t * D + j];
         }
     int64_t cbytes = (int64_t)T * D * bits / 8;
     orc_pack(qo, (int64_t)nel, bits, record);
@@ -378,8 +391,7 @@ void orc_dequantize_record(const uint8_t *record, int T, int D, int bits,
         double Z = orc_half_to_double(get_u16(record + cbytes + 4 * t + 2));
         for (int j = 0; j < D; j++) {
             double C = orc_half_to_double(get_u16(record + cbytes + 4 * T + 2 * j));
-            int64_t e = channel_major ? (int64_t)j * T + t : (int64_t)t * D + j;
-            Yh[(int64_t)t * D + j] = C * (S * qo[e] + Z);
+            Yh[(int64_t)t * D + j] = C * (S * qo[code_pos(T, D, t, j, channel_major)] + Z);
         }
     }
     orc_rotate(T, D, Yh, Xhat);

@@ -90,3 +90,22 @@ def test_record_fields_roundtrip():
         exp = np.clip(np.rint(u), 0, 15).astype(np.uint8)
         assert np.array_equal(codes, exp)
         assert np.allclose(C, np.exp(lc), rtol=1e-3)
+
+
+@pytest.mark.parametrize("T,bits", [(128, 2), (128, 6), (64, 4), (128, 5)])
+def test_value_codes_channel_major_in_64_token_blocks(T, bits):
+    """Value records keep their codes channel-major in blocks of 64 tokens:
+    the code of token t, channel j is element (t // 64) * 64 * D + j * 64 +
+    t % 64 of the LSB-first stream (a layout choice the pages leave open; it
+    makes the codes of a 64-token block one contiguous run).  Read straight
+    from the packed bits and compared with the same tile's key-order record."""
+    D = 128
+    rng = np.random.default_rng(T + bits)
+    x = rng.standard_normal((T, D)).astype(np.float16).view(np.uint16)
+    vrec, _, _, _ = oracle.quantize_record(x, bits, 6, channel_major=True)
+    krec, _, _, _ = oracle.quantize_record(x, bits, 6, channel_major=False)
+    flat = oracle.unpack(vrec[:T * D * bits // 8], T * D, bits)
+    tok = oracle.unpack(krec[:T * D * bits // 8], T * D, bits).reshape(T, D)
+    t, j = np.meshgrid(np.arange(T), np.arange(D), indexing="ij")
+    assert np.array_equal(flat[(t // 64) * 64 * D + j * 64 + t % 64], tok)
+    assert np.array_equal(vrec[T * D * bits // 8:], krec[T * D * bits // 8:])
