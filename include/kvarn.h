@@ -165,7 +165,8 @@ size_t kvarn_decode_workspace_bytes(const kvarn_layout *layout, int32_t batch,
  * L = 0 gives zeros.  workspace: device, at least
  * kvarn_decode_workspace_bytes(...) bytes, 256-byte aligned; its contents
  * need no initialisation and are clobbered.  num_q_heads must be a multiple
- * of H (GQA group 4 here; MLA: 16, 32, 64 or 128).  With head_dim 128
+ * of H (GQA: a group of any multiple of 4 query heads per KV head, at
+ * most 65535 groups of 4 in all; MLA: 16, 32, 64 or 128).  With head_dim 128
  * (GQA) and with MLA each record pool, n_qpages * H * record bytes, must be
  * below 4 GiB, and with MLA the fp16 pool too; GQA takes at most 32767
  * sequences per call (KVARN_EUNSUPPORTED otherwise).  Negative pool sizes are

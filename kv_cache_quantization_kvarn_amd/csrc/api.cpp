@@ -106,8 +106,10 @@ kvarn_status decode_common(const kvarn_layout* layout, const kvarn_cache* cache,
     if (layout->mla) {
         if (num_q_heads != 16 && num_q_heads != 32 && num_q_heads != 64 && num_q_heads != 128)
             return fail(KVARN_EUNSUPPORTED, "mla: %d query heads; 16, 32, 64 or 128 are implemented", num_q_heads);
-    } else if (G != 4) {
-        return fail(KVARN_EUNSUPPORTED, "GQA group %d: this build implements groups of 4 query heads", G);
+    } else if (G % 4 != 0) {
+        return fail(KVARN_EUNSUPPORTED, "GQA group %d: groups of a multiple of 4 query heads are implemented", G);
+    } else if ((int64_t)H * (G / 4) > 65535) {
+        return fail(KVARN_EUNSUPPORTED, "GQA: %d groups of 4 query heads; at most 65535", num_q_heads / 4);
     }
     if (!cache->k_fp16 || (!layout->mla && !cache->v_fp16)) return fail(KVARN_EINVAL, "fp16 pools are NULL");
     if (cache->n_qpages < 0 || cache->n_fpages < 0) return fail(KVARN_EINVAL, "negative pool size");
@@ -159,6 +161,7 @@ kvarn_status decode_common(const kvarn_layout* layout, const kvarn_cache* cache,
     a.H = H;
     a.mla = layout->mla;
     a.G = G;
+    a.GS = layout->mla ? 1 : G / 4;
     a.B = (int)rows;
     a.M = M;
     a.causal = causal;

@@ -40,12 +40,12 @@ hipError_t gqa_bits(const DecodeArgs& a, hipStream_t st) {
 
 void decode_plan(int D, int H, int G, int mla, int B, int max_pages, int T, int kb, int vb, int* nsplit,
                  int* pps) {
-    (void)G; (void)T; (void)kb; (void)vb;
+    (void)T; (void)kb; (void)vb;
     // GQA: as many waves as fit at once: three per SIMD (head_dim 128: 128
     // VGPRs, but the fp16 slots take the fourth; 256 and 512: up to 170 VGPRs,
     // splits of two and four waves).  MLA: one 8-wave workgroup per CU holds 64 heads,
     // so up to 128 heads take two workgroups per split.
-    const int units = mla ? B * ((G + 63) / 64) : B * H;
+    const int units = mla ? B * ((G + 63) / 64) : B * H * (G / 4);  // GQA: one per group of 4 query heads
     // (head_dim 128: 3584 one-wave workgroups, a seventh more than the 3072
     // resident at once, measured best: the splits' lengths vary with the
     // sequence lengths and the fp16 slots fill in behind them)
@@ -82,7 +82,7 @@ size_t decode_workspace_floats(int D, int Hq, int B, int nsplit, int nfsplit) {
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
     if (a.mla) return launch_mla(a, st);
-    if (a.G != 4) return hipErrorInvalidValue;
+    if (a.G < 4 || a.G % 4 != 0 || a.GS != a.G / 4) return hipErrorInvalidValue;
     if (a.D == 128 && a.T == 128) return gqa_bits<128, 128>(a, st);
     if (a.D == 128 && a.T == 64) return gqa_bits<128, 64>(a, st);
     if (a.D == 256 && a.T == 128) return gqa_bits<256, 128>(a, st);

@@ -174,7 +174,8 @@ __device__ __forceinline__ float sum_blocks_half(float v) {
 
 // fp16 sink and tail pages (gmlx "KV cache quantization", "The two
 // schemes"): workgroups of the split kernels' grid past the splits, one wave
-// per (fp16 slot f, KV head, sequence).  Slot f is the 64-token part f % (T /
+// per (fp16 slot f, group h of 4 query heads, query row); the group's KV head
+// is h / GS.  Slot f is the 64-token part f % (T /
 // 64) of the (f / (T / 64))-th fp16 page of the sequence (sink pages, then
 // tail pages); its partial goes to split nsplit + f with a zero rotated-basis
 // sum.  Scores on the MFMA with the plain query (fp16 high and low parts),
@@ -235,7 +236,7 @@ __device__ __forceinline__ void fp16_block(const DecodeArgs& a, const int f, con
             }
         float s[G];
         {
-            const uint16_t* kr = static_cast<const uint16_t*>(a.k_fp16) + (((int64_t)id * a.H + h) * T + 64 * sb + lane) * D;
+            const uint16_t* kr = static_cast<const uint16_t*>(a.k_fp16) + (((int64_t)id * a.H + h / a.GS) * T + 64 * sb + lane) * D;
             f4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int c = 0; c < NC; c++) {
@@ -267,7 +268,7 @@ __device__ __forceinline__ void fp16_block(const DecodeArgs& a, const int f, con
         wave_sync();
         // value sums: D/8 lanes per token row (16-byte loads of 8 channels), TG
         // tokens per load instruction, the token groups summed at the end
-        const uint16_t* vp = static_cast<const uint16_t*>(a.v_fp16) + (((int64_t)id * a.H + h) * T + 64 * sb) * D;
+        const uint16_t* vp = static_cast<const uint16_t*>(a.v_fp16) + (((int64_t)id * a.H + h / a.GS) * T + 64 * sb) * D;
         const int tg = lane / LPT, cc = lane % LPT;
         // branch-free: a token past the end has weight 0 (its score is
         // -inf) and reads the last valid token's values instead of its own
@@ -352,7 +353,8 @@ __global__ void __launch_bounds__(64 * split_waves<D>(), 3) decode_split_kernel(
         return;
     }
     if ((int)blockIdx.x >= a.nsplit) return;
-    const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    // h: group of 4 query heads 4 h .. 4 h + 3, of KV head kvh (G / 4 groups per KV head)
+    const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z, kvh = h / a.GS;
     const int blk = lane >> 2, m = lane & 3;  // MFMA block; row (query head) of the broadcast operand
     const int Hq = a.Hq;
     const float sm2 = a.sm_scale * kLog2e;
@@ -437,7 +439,7 @@ __global__ void __launch_bounds__(64 * split_waves<D>(), 3) decode_split_kernel(
     }
     auto issue_k = [&](const StepRef& r) {
         if (!r.ok) return;
-        const uint8_t* rk = krec + ((int64_t)r.id * a.H + h) * KREC;
+        const uint8_t* rk = krec + ((int64_t)r.id * a.H + kvh) * KREC;
         const int tok = 64 * r.h + lane;
         if constexpr (PREK) {
 #pragma unroll
@@ -456,7 +458,7 @@ __global__ void __launch_bounds__(64 * split_waves<D>(), 3) decode_split_kernel(
     };
     auto issue_v = [&](const StepRef& r) {
         if (!r.ok) return;
-        const uint8_t* rv = vrec + ((int64_t)r.id * a.H + h) * VREC;
+        const uint8_t* rv = vrec + ((int64_t)r.id * a.H + kvh) * VREC;
 #pragma unroll
         for (int sv = 0; sv < NS; sv++) {
             if constexpr (PREV) load_seg<VHW>(vw[sv], rv + vseg(r.h, 64 * (NS * wave + sv) + lane));
@@ -493,20 +495,23 @@ __global__ void __launch_bounds__(64 * split_waves<D>(), 3) decode_split_kernel(
         }
         const int id = cur.id;
         const int tok = 64 * cur.h + lane;
-        const uint8_t* rk = krec + ((int64_t)id * a.H + h) * KREC;
-        const uint8_t* rv = vrec + ((int64_t)id * a.H + h) * VREC;
+        const uint8_t* rk = krec + ((int64_t)id * a.H + kvh) * KREC;
+        const uint8_t* rv = vrec + ((int64_t)id * a.H + kvh) * VREC;
 
         // ---- scores, lane = token ----
         float s[G];
         {
             if (cur.h == 0) {
-                // score operands of the new page (fp16 high and low parts) and their per-head sums
+                // score operands of the new page (fp16 high and low parts) and
+                // their per-head sums, both from one fp32 product per channel
+                // (the MFMA and the sum must see the same high part)
                 float part = 0.f;
 #pragma unroll
                 for (int r = 0; r < NS; r++) {
 #pragma unroll
                     for (int kk = 0; kk < 4; kk++) {
-                        const float x = qv[r][kk] * half_bits_to_float((ckr[r][kk >> 1] >> (16 * (kk & 1))) & 0xffffu);
+                        const float x =
+                            fp32_value(qv[r][kk] * half_bits_to_float((ckr[r][kk >> 1] >> (16 * (kk & 1))) & 0xffffu));
                         const _Float16 hi = (_Float16)x;
                         const _Float16 lo = (_Float16)(x - (float)hi);
                         qa[r][kk] = hi;
@@ -577,13 +582,14 @@ __global__ void __launch_bounds__(64 * split_waves<D>(), 3) decode_split_kernel(
         {
             // weights times S_V (fp16 high and low parts) into LDS by operand
             // position; the constant 1 of the code operands returns through
-            // sum (p Zp - 2^B p S)
+            // sum (p Zp - 2^B p S).  Both parts come from one fp32 product, so
+            // that e below subtracts exactly what the MFMA adds.
             const float S = half_bits_to_float(vsz & 0xffffu), Z = half_bits_to_float(vsz >> 16);
             const int pos = pos_of<VB>(lane);
             float e[G];
 #pragma unroll
             for (int g = 0; g < G; g++) {
-                const float x = p[g] * S;
+                const float x = fp32_value(p[g] * S);
                 const _Float16 hi = (_Float16)x;
                 const _Float16 lo = (_Float16)(x - (float)hi);
                 pt[wave][0][g][pos] = hi;
@@ -966,21 +972,24 @@ __global__ void __launch_bounds__(64) decode_split128_kernel(DecodeArgs a) {
     // all of a step's loads into the stage
     auto issue = [&](const StepRef& r) {
         if (!r.ok) return;
-        const uint32_t rec = (uint32_t)r.id * (uint32_t)a.H + (uint32_t)h;
-        const int sk = __builtin_amdgcn_readfirstlane((int)(rec * (uint32_t)KREC));
-        const int sv = __builtin_amdgcn_readfirstlane((int)(rec * (uint32_t)VREC));
+        const uint32_t rec = (uint32_t)r.id * (uint32_t)a.H + (uint32_t)(h / a.GS);
+        // byte offsets in the pools (each below 4 GiB) as unsigned 32-bit
+        // values: the buffer load adds its scalar offset modulo 2^32
+        const uint32_t sk = (uint32_t)__builtin_amdgcn_readfirstlane((int)(rec * (uint32_t)KREC));
+        const uint32_t sv = (uint32_t)__builtin_amdgcn_readfirstlane((int)(rec * (uint32_t)VREC));
 #pragma unroll
-        for (int i = 0; i < KST / 1024; i++) lds_dma16(sb + 1024 * i, rsk, 16 * kswz(64 * i + lane), sk + KST * r.h);
+        for (int i = 0; i < KST / 1024; i++)
+            lds_dma16(sb + 1024 * i, rsk, 16 * kswz(64 * i + lane), (int)(sk + (uint32_t)(KST * r.h)));
         if (r.h == 0 && lane < SB / 16) {  // the page's scale blocks
-            lds_dma16(sb + KSC, rsk, 16 * lane, sk + KCB);
-            lds_dma16(sb + VSC, rsv, 16 * lane, sv + VCB);
+            lds_dma16(sb + KSC, rsk, 16 * lane, (int)(sk + (uint32_t)KCB));
+            lds_dma16(sb + VSC, rsv, 16 * lane, (int)(sv + (uint32_t)VCB));
         }
 #pragma unroll
         for (int i = 0; i < VST / 1024; i++) {
             // piece u = channel u / (VB / 2), part u % (VB / 2): values are kept
             // in 64-token blocks, so a step's pieces are one contiguous run
             const int u = 64 * i + lane;
-            lds_dma16(sb + VSO + 1024 * i, rsv, 16 * u, sv + (64 * D * VB / 8) * r.h);
+            lds_dma16(sb + VSO + 1024 * i, rsv, 16 * u, (int)(sv + (uint32_t)((64 * D * VB / 8) * r.h)));
         }
     };
     // the lane's operands of a step out of the stage (after its loads have
@@ -1267,8 +1276,10 @@ __global__ void __launch_bounds__(D * combine_groups<D>()) decode_combine_kernel
 // workgroups return at once) so that x * y is a multiple of 8, which puts
 // the rows' workgroups -- dispatched to the 8 XCDs in turn by linear id -- on
 // one XCD, where they read the sequence's records through one L2.
-inline unsigned split_grid_x(unsigned gx, unsigned gy, int M) {
-    if (M > 1)
+inline unsigned split_grid_x(unsigned gx, unsigned gy, int M, int GS) {
+    if (GS > 1)  // the query-head groups of one KV head are adjacent in y
+        while (gx % 8u) gx++;
+    else if (M > 1)
         while ((gx * gy) % 8u) gx++;
     return gx;
 }
@@ -1284,7 +1295,8 @@ hipError_t launch_gqa(const DecodeArgs& a, hipStream_t st) {
     // one launch: the quantized-page splits (z < B), then the fp16 page slots
     constexpr int NWV = D == 128 ? 1 : split_waves<D>();
     const int nfx = (a.nfsplit + NWV - 1) / NWV;  // fp16 slots: one per wave
-    const dim3 grid(split_grid_x(a.nsplit > nfx ? a.nsplit : nfx, a.H, a.M), a.H, a.nfsplit > 0 ? 2 * a.B : a.B);
+    const int gy = a.H * a.GS;
+    const dim3 grid(split_grid_x(a.nsplit > nfx ? a.nsplit : nfx, gy, a.M, a.GS), gy, a.nfsplit > 0 ? 2 * a.B : a.B);
     if constexpr (D == 128)
         hipLaunchKernelGGL((decode_split128_kernel<T, KB, VB>), grid, dim3(64), 0, st, a);
     else

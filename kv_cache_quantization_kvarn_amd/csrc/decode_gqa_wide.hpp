@@ -16,7 +16,8 @@ hipError_t launch_gqa_wide(const DecodeArgs& a, hipStream_t st) {
     if (e != hipSuccess) return e;
     constexpr int NWV = split_waves<D>();
     const int nfx = (a.nfsplit + NWV - 1) / NWV;  // fp16 slots: one per wave
-    const dim3 grid(split_grid_x(a.nsplit > nfx ? a.nsplit : nfx, a.H, a.M), a.H, a.nfsplit > 0 ? 2 * a.B : a.B);
+    const int gy = a.H * a.GS;
+    const dim3 grid(split_grid_x(a.nsplit > nfx ? a.nsplit : nfx, gy, a.M, a.GS), gy, a.nfsplit > 0 ? 2 * a.B : a.B);
     hipLaunchKernelGGL((decode_split_kernel<D, T, KB, VB>), grid, dim3(64 * NWV), 0, st, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;

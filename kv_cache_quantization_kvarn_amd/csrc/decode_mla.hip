@@ -378,16 +378,19 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
         if (cj < nqc) qchunk(cj, page, c0, id);
         const bool q = id >= 0;
         const uint32_t sl = ring_lds + (uint32_t)((cj % NR) * SLOT);
-        const int rec = q ? id * KREC : 0;
+        // byte offsets in the pool (below 4 GiB) as unsigned 32-bit values:
+        // the buffer load adds its scalar offset modulo 2^32
+        const uint32_t rec = q ? (uint32_t)id * (uint32_t)KREC : 0u;
         if (q) {  // slot piece 64 w + l holds piece k ^ (t & 7) of token t's row (t = piece >> 4, k = piece & 15)
             const int pc = 64 * wave + lane, t = pc >> 4;
-            lds_dma16(sl + 1024 * wave, rs, t * (MD / 2) + 16 * ((pc & 15) ^ (t & 7)), rec + c0 * (MD / 2));
+            lds_dma16(sl + 1024 * wave, rs, t * (MD / 2) + 16 * ((pc & 15) ^ (t & 7)),
+                      (int)(rec + (uint32_t)(c0 * (MD / 2))));
         }
         else if (lane == 0) lds_dma16(dummy_lds, rs, 0, 0);
         if (q && wave == 0) {
-            if (lane < CH / 4) lds_dma16(sl + SSC, rs, 16 * lane, rec + KCB + 4 * c0);
+            if (lane < CH / 4) lds_dma16(sl + SSC, rs, 16 * lane, (int)(rec + (uint32_t)(KCB + 4 * c0)));
         } else if (q && wave == 1 && c0 == 0) {
-            lds_dma16(sl + SCC, rs, 16 * lane, rec + KCB + 4 * T);
+            lds_dma16(sl + SCC, rs, 16 * lane, (int)(rec + (uint32_t)(KCB + 4 * T)));
         } else if (lane == 0) {
             lds_dma16(dummy_lds, rs, 0, 0);
         }
@@ -557,13 +560,13 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
     auto issue_f = [&](FChunk f, int buf) {
         if (f.j >= nfp) return;
         const int id = page_id(nqp + f.j);
-        const int base = (id * T + f.cc * CH) * (MD * 2);
+        const uint32_t base = ((uint32_t)id * (uint32_t)T + (uint32_t)(f.cc * CH)) * (uint32_t)(MD * 2);
         const int nvalid = min(CH, L - (fpage(f.j) * T + f.cc * CH));  // >= 1
         uint8_t* yb = ybuf[1 + buf];
 #pragma unroll
         for (int i = 0; i < 4; i++) {
             const int t = 4 * wave + i;  // token of the chunk
-            if (t < nvalid) lds_dma16(lds_address(yb) + (uint32_t)yoff(t, 0), rf, 16 * lane, base + 1024 * t);
+            if (t < nvalid) lds_dma16(lds_address(yb) + (uint32_t)yoff(t, 0), rf, 16 * lane, (int)(base + 1024u * t));
             else *reinterpret_cast<uint4*>(yb + yoff(t, lane)) = make_uint4(0u, 0u, 0u, 0u);
         }
     };

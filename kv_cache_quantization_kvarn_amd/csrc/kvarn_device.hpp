@@ -81,6 +81,17 @@ __device__ __forceinline__ uint32_t float_to_half_bits(float f) {
     return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
 }
 
+// x, rounded to fp32, as a value the compiler cannot see through: an fp16
+// conversion of it is not fused with the product that made it.  (A fused
+// v_fma_mix rounds the exact product to fp16 once, a conversion of the fp32
+// product rounds twice; the two differ by one fp16 ulp where the fp32
+// product lands on an fp16 tie, so a value split into fp16 high and low
+// parts must take both parts, at every use, from the same fp32 number.)
+__device__ __forceinline__ float fp32_value(float x) {
+    asm("" : "+v"(x));
+    return x;
+}
+
 
 // Query elements of the three query dtypes of the C ABI (0 float32, 1
 // float16, 2 bfloat16), widened exactly to float.

@@ -35,6 +35,7 @@ hipError_t launch_quantize_one(const QuantizeArgs& a, hipStream_t st);
 struct DecodeArgs {
     int D, T, k_bits, v_bits, sink, tail, H, mla;
     int G;            // query heads per KV head (MLA: all query heads)
+    int GS;           // GQA: groups of 4 query heads per KV head (G / 4); one grid row each
     int B, Hq, max_pages;  // B: query rows = sequences x query tokens (row b = sequence b / M, token b % M)
     int M;            // query tokens per sequence (1 for a plain decode step)
     int causal;       // 0: every row attends the seq_lens tokens; 1: token i of a sequence sits at

@@ -122,7 +122,12 @@ def test_decode_rejects_before_any_device_work():
     need = kv.decode_workspace_bytes(L, 2, 32, 4)
     assert need > 0
     assert lib.kvarn_decode_attn(*args(30, ctypes.c_void_p(256), need)) == kv.KVARN_EINVAL
-    assert lib.kvarn_decode_attn(*args(64, ctypes.c_void_p(256), need)) == kv.KVARN_EUNSUPPORTED
+    # GQA groups: any multiple of 4 query heads per KV head
+    assert lib.kvarn_decode_attn(*args(48, ctypes.c_void_p(256), need)) == kv.KVARN_EUNSUPPORTED
+    assert lib.kvarn_decode_attn(*args(24, ctypes.c_void_p(256), need)) == kv.KVARN_EUNSUPPORTED
+    need8 = kv.decode_workspace_bytes(L, 2, 64, 4)
+    assert need8 > need
+    assert lib.kvarn_decode_attn(*args(64, ctypes.c_void_p(256), need8 - 1)) == kv.KVARN_EWORKSPACE
     assert lib.kvarn_decode_attn(*args(32, ctypes.c_void_p(256), need - 1)) == kv.KVARN_EWORKSPACE
     assert lib.kvarn_decode_attn(*args(32, None, need)) == kv.KVARN_EWORKSPACE
     assert lib.kvarn_decode_attn(*args(32, ctypes.c_void_p(256), need, qd=7)) == kv.KVARN_EINVAL

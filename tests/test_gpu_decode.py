@@ -185,6 +185,46 @@ def test_decode_width_pairs(D, kb, vb):
     check(case, out, krec, vrec)
 
 
+# GQA groups beyond 4 query heads per KV head (each group of 4 is a grid row
+# reading its KV head's records): 64 query over 8 KV heads and wider groups,
+# even and odd widths, every head dim
+GROUPS = [
+    # D, T, kb, vb, Hq, H
+    (128, 64, 4, 2, 64, 8),
+    (128, 128, 3, 5, 16, 1),
+    (256, 128, 6, 6, 16, 2),
+    (512, 64, 4, 2, 24, 1),
+    (512, 128, 8, 4, 8, 1),
+]
+
+
+@pytest.mark.parametrize("D,T,kb,vb,Hq,H", GROUPS)
+def test_decode_query_groups(D, T, kb, vb, Hq, H):
+    w = workload("wide_d256_b8_64k_k6v6", D=D, T=T, k_bits=kb, v_bits=vb, Hq=Hq, H=H, L=1400, sink=T, tail=200,
+                 dist="normal", outliers=("per_head", 4), seed=0x4300 + D + T + Hq)
+    case = gpu_case(w, seq_lens=[1400, 813, 1, 0], batch=4)
+    say("decode groups", D, T, kb, vb, Hq, H)
+    L, krec, vrec = run_quantize(case)
+    out = run_decode(case, L, krec, vrec)
+    assert np.all(out.cpu().numpy()[3] == 0)
+    groups = np.array([(b, g) for b in range(3) for g in range(H)], np.int32)
+    check_groups(case, out, krec, vrec, groups, f"D{D} k{kb}v{vb} {Hq}/{H} heads")
+
+
+def test_decode_query_groups_full_size():
+    """A 64-query / 8-KV-head layer (group 8) at 16 sequences x 32K tokens:
+    every query head of four sequences."""
+    w = workload("dense8b_b16_32k_k4v2_g128", Hq=64, seed=0x4310)
+    case = gpu_case(w)
+    say("decode full, group 8")
+    L, krec, vrec = run_quantize(case)
+    out = run_decode(case, L, krec, vrec)
+    assert np.all(np.isfinite(out.cpu().numpy()))
+    B, H = case["B"], case["layout"]["H"]
+    groups = np.array([(b, g) for b in (0, 5, 11, B - 1) for g in range(H)], np.int32)
+    check_groups(case, out, krec, vrec, groups, "16 x 32K, 64/8 heads")
+
+
 @pytest.mark.parametrize("qd", ["bf16", "f16"])
 @pytest.mark.parametrize("D,kb,vb", [(128, 4, 2), (256, 4, 2), (512, 4, 2), (128, 3, 5)])
 def test_decode_16bit_queries(D, kb, vb, qd):

@@ -66,6 +66,8 @@ CASES = [
     (256, 128, 6, 6, 8, 2, 128, 256, 4, "f32"),
     (512, 128, 6, 6, 8, 2, 128, 256, 2, "f16"),
     (512, 64, 4, 2, 4, 1, 0, 64, 1, "f32"),
+    (128, 64, 4, 2, 32, 4, 64, 128, 4, "bf16"),  # groups of 8 query heads
+    (256, 128, 3, 5, 16, 1, 128, 256, 3, "f32"),  # a group of 16
 ]
 
 
