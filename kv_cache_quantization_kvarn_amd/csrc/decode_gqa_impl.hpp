@@ -314,6 +314,46 @@ __device__ __forceinline__ void fp16_block(const DecodeArgs& a, const int f, con
     }
 }
 
+// exponent e of x = f 2^e with 0.5 <= |f| < 1 (0 for x = 0)
+__device__ __forceinline__ int frexp_exp(float x) { return __builtin_amdgcn_frexp_expf(x); }
+
+// Reductions of four values per lane (one per query head) over the 64 lanes,
+// returned wave-uniform.  Inside each 16-lane row: fused DPP (xor 1, xor 2,
+// rotate 4, rotate 8); across rows the heads are paired, so one
+// v_permlane16_swap serves heads 0/1 (and 2/3) and one v_permlane32_swap
+// serves all four: afterwards row r holds head r's result, read from lane 16 r.
+#define KVARN_DPP4(OP, CTRL)                                                                  \
+    asm volatile("s_nop 1\n\t"                                                                 \
+                 OP "_dpp %0, %0, %0 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                 \
+                 OP "_dpp %1, %1, %1 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                 \
+                 OP "_dpp %2, %2, %2 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                 \
+                 OP "_dpp %3, %3, %3 " CTRL " row_mask:0xf bank_mask:0xf"                     \
+                 : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]))
+
+template <bool MAX>
+__device__ __forceinline__ void wave_reduce4(float (&v)[4], float (&out)[4]) {
+    if constexpr (MAX) {
+        KVARN_DPP4("v_max_f32", "quad_perm:[1,0,3,2]");
+        KVARN_DPP4("v_max_f32", "quad_perm:[2,3,0,1]");
+        KVARN_DPP4("v_max_f32", "row_ror:4");
+        KVARN_DPP4("v_max_f32", "row_ror:8");
+    } else {
+        KVARN_DPP4("v_add_f32", "quad_perm:[1,0,3,2]");
+        KVARN_DPP4("v_add_f32", "quad_perm:[2,3,0,1]");
+        KVARN_DPP4("v_add_f32", "row_ror:4");
+        KVARN_DPP4("v_add_f32", "row_ror:8");
+    }
+    auto op = [](float x, float y) { return MAX ? fmaxf(x, y) : x + y; };
+    const auto p01 = __builtin_amdgcn_permlane16_swap((unsigned)f2i(v[0]), (unsigned)f2i(v[1]), false, false);
+    const auto p23 = __builtin_amdgcn_permlane16_swap((unsigned)f2i(v[2]), (unsigned)f2i(v[3]), false, false);
+    const float m01 = op(i2f((int)p01[0]), i2f((int)p01[1]));  // rows 0, 2: head 0; rows 1, 3: head 1
+    const float m23 = op(i2f((int)p23[0]), i2f((int)p23[1]));  // rows 0, 2: head 2; rows 1, 3: head 3
+    const auto q = __builtin_amdgcn_permlane32_swap((unsigned)f2i(m01), (unsigned)f2i(m23), false, false);
+    const float r = op(i2f((int)q[0]), i2f((int)q[1]));        // row g: head g
+#pragma unroll
+    for (int g = 0; g < 4; g++) out[g] = i2f(__builtin_amdgcn_readlane(f2i(r), 16 * g));
+}
+
 // Waves per (split, KV head, sequence) of decode_split_kernel: one per 128
 // channels, the partial scores summed through LDS once per step, so that a
 // whole step's codes are prefetched in the registers of three waves per SIMD.
@@ -582,19 +622,30 @@ __global__ void __launch_bounds__(64 * split_waves<D>(), 3) decode_split_kernel(
         {
             // weights times S_V (fp16 high and low parts) into LDS by operand
             // position; the constant 1 of the code operands returns through
-            // sum (p Zp - 2^B p S).  Both parts come from one fp32 product, so
-            // that e below subtracts exactly what the MFMA adds.
+            // sum (p Zp - 2^B p S).  Both parts come from one fp32 value, so
+            // that e below subtracts exactly what the MFMA adds.  Each head's
+            // weights are scaled by 2^(14 - e), e the exponent of its largest
+            // weight of the step: the step's weights then stay in fp16's
+            // normal range down to 2^-28 of that weight, where otherwise most
+            // weights of a long sequence (far below the running maximum) would
+            // be fp16 subnormals, whose treatment by the MFMA is not that of
+            // the fp32 sum e.
             const float S = half_bits_to_float(vsz & 0xffffu), Z = half_bits_to_float(vsz >> 16);
             const int pos = pos_of<VB>(lane);
-            float e[G];
+            float pmax[G], mxw[G], fvs[G], e[G];
+#pragma unroll
+            for (int g = 0; g < G; g++) pmax[g] = p[g] * S;
+            wave_reduce4<true>(pmax, mxw);
 #pragma unroll
             for (int g = 0; g < G; g++) {
-                const float x = fp32_value(p[g] * S);
+                const int ex = frexp_exp(mxw[g]);
+                const float x = fp32_value(__builtin_amdgcn_ldexpf(p[g] * S, 14 - ex));
+                fvs[g] = __builtin_amdgcn_ldexpf(FV, ex - 14);
                 const _Float16 hi = (_Float16)x;
                 const _Float16 lo = (_Float16)(x - (float)hi);
                 pt[wave][0][g][pos] = hi;
                 pt[wave][1][g][pos] = lo;
-                e[g] = fmaf(p[g], Z, -FV * ((float)hi + (float)lo));
+                e[g] = fmaf(p[g], Z, -fvs[g] * ((float)hi + (float)lo));
             }
             float E[G];
 #pragma unroll
@@ -620,7 +671,7 @@ __global__ void __launch_bounds__(64 * split_waves<D>(), 3) decode_split_kernel(
                 });
                 const f4 R = acc0 + acc1;
 #pragma unroll
-                for (int g = 0; g < G; g++) accr[sv][g] = fmaf(cvv[sv], fmaf(FV, R[g], E[g]), accr[sv][g]);
+                for (int g = 0; g < G; g++) accr[sv][g] = fmaf(cvv[sv], fmaf(fvs[g], R[g], E[g]), accr[sv][g]);
             }
             wave_sync();  // pt is rewritten by the next step
         }
@@ -698,46 +749,6 @@ __device__ __forceinline__ float sum_class4(float v) {
     v = i2f((int)a16[0]) + i2f((int)a16[1]);
     const auto a32 = __builtin_amdgcn_permlane32_swap((unsigned)f2i(v), (unsigned)f2i(v), false, false);
     return i2f((int)a32[0]) + i2f((int)a32[1]);
-}
-
-// exponent e of x = f 2^e with 0.5 <= |f| < 1 (0 for x = 0)
-__device__ __forceinline__ int frexp_exp(float x) { return __builtin_amdgcn_frexp_expf(x); }
-
-// Reductions of four values per lane (one per query head) over the 64 lanes,
-// returned wave-uniform.  Inside each 16-lane row: fused DPP (xor 1, xor 2,
-// rotate 4, rotate 8); across rows the heads are paired, so one
-// v_permlane16_swap serves heads 0/1 (and 2/3) and one v_permlane32_swap
-// serves all four: afterwards row r holds head r's result, read from lane 16 r.
-#define KVARN_DPP4(OP, CTRL)                                                                  \
-    asm volatile("s_nop 1\n\t"                                                                 \
-                 OP "_dpp %0, %0, %0 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                 \
-                 OP "_dpp %1, %1, %1 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                 \
-                 OP "_dpp %2, %2, %2 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                 \
-                 OP "_dpp %3, %3, %3 " CTRL " row_mask:0xf bank_mask:0xf"                     \
-                 : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]))
-
-template <bool MAX>
-__device__ __forceinline__ void wave_reduce4(float (&v)[4], float (&out)[4]) {
-    if constexpr (MAX) {
-        KVARN_DPP4("v_max_f32", "quad_perm:[1,0,3,2]");
-        KVARN_DPP4("v_max_f32", "quad_perm:[2,3,0,1]");
-        KVARN_DPP4("v_max_f32", "row_ror:4");
-        KVARN_DPP4("v_max_f32", "row_ror:8");
-    } else {
-        KVARN_DPP4("v_add_f32", "quad_perm:[1,0,3,2]");
-        KVARN_DPP4("v_add_f32", "quad_perm:[2,3,0,1]");
-        KVARN_DPP4("v_add_f32", "row_ror:4");
-        KVARN_DPP4("v_add_f32", "row_ror:8");
-    }
-    auto op = [](float x, float y) { return MAX ? fmaxf(x, y) : x + y; };
-    const auto p01 = __builtin_amdgcn_permlane16_swap((unsigned)f2i(v[0]), (unsigned)f2i(v[1]), false, false);
-    const auto p23 = __builtin_amdgcn_permlane16_swap((unsigned)f2i(v[2]), (unsigned)f2i(v[3]), false, false);
-    const float m01 = op(i2f((int)p01[0]), i2f((int)p01[1]));  // rows 0, 2: head 0; rows 1, 3: head 1
-    const float m23 = op(i2f((int)p23[0]), i2f((int)p23[1]));  // rows 0, 2: head 2; rows 1, 3: head 3
-    const auto q = __builtin_amdgcn_permlane32_swap((unsigned)f2i(m01), (unsigned)f2i(m23), false, false);
-    const float r = op(i2f((int)q[0]), i2f((int)q[1]));        // row g: head g
-#pragma unroll
-    for (int g = 0; g < 4; g++) out[g] = i2f(__builtin_amdgcn_readlane(f2i(r), 16 * g));
 }
 
 // ---- D = 128: scores and value sums on the 32x32x32 int8 MFMA --------------
