@@ -49,16 +49,31 @@ __device__ __forceinline__ h4 tr16(const void* p) {
     return __builtin_bit_cast(h4, v);
 }
 
-// LDS layout of a read-back chunk: token rows of YROW bytes (512 halves + 32
-// bytes of pad), row t starting 16 bytes late when bit 2 of t is set; the
-// 16-byte unit u of token t sits at 16 u of its row.  Every access is a
-// per-lane base plus a constant, and in 128 bytes of banks the 16-byte units
-// of 8 consecutive tokens in one column fall on 8 different bank groups
-// (score operand reads, read-back stores) while 4 rows x 32 bytes of the
-// transposed value reads cover all 32 banks once.
-constexpr int YROW = 2 * 512 + 32;
-__device__ __forceinline__ int yoff(int t, int u) { return t * YROW + 16 * ((t >> 2) & 1) + 16 * u; }
-static_assert(31 * YROW + 16 + 16 * 64 <= 32 * YROW, "the last row fits");
+// LDS layout of a read-back chunk: token rows of YROW = 1 KB (512 halves),
+// the 16-byte unit u of token t at position u ^ (t & 15) of its row.  The
+// gfx950 LDS serves a 128-bit access 16 lanes at a time from 64 banks; the
+// swizzle puts the units of 16 consecutive tokens in one column on 16
+// different 4-bank groups, so the score operand reads (16 tokens, one unit)
+// and the read-back stores (8 tokens, two units 8 apart) are free of bank
+// conflicts.  (Padded rows of 1040, 1056 or 1088 bytes measured 1.8x slower
+// for the score reads.)
+constexpr int YROW = 2 * 512;
+__device__ __forceinline__ int yoff(int t, int u) { return t * YROW + 16 * (u ^ (t & 15)); }
+// position of piece k (16 bytes) of a token's 256-byte code row in a ring
+// slot: the 8 tokens (t & 7) read by 8 lanes for one piece, and the two
+// pieces 2 apart of lanes 8 further on, land on 16 different bank groups
+__device__ __forceinline__ int cswz(int t) { return (t & 1) | ((t & 6) << 1); }
+// 0, as a value the compiler cannot see through.  Taken once per chunk
+// (right after a barrier, where the wait the compiler puts before inline asm
+// costs nothing) and XOR-ed into the lane keys of the swizzled addresses, it
+// makes them chunk-local: each stage forms its few addresses per chunk
+// instead of all of them being hoisted out of the chunk loop, one register
+// each.
+__device__ __forceinline__ int opaque_zero() {
+    int z = 0;
+    asm volatile("" : "+v"(z));
+    return z;
+}
 // Within a 16-byte unit the eight channels are held in the order
 // 0,4,1,5,2,6,3,7 (the order in which packed nibbles unpack to fp16 pairs);
 // position p holds channel upos(p).
@@ -147,7 +162,7 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
     static_assert(HQ * 2 <= 160, "weight rows hold at most 64 heads");
     __shared__ __attribute__((aligned(16))) uint8_t ybuf[3][CH * YROW];  // chunks, rotated basis (fp16)
     __shared__ __attribute__((aligned(16))) uint8_t pbuf[2][PBYTES];      // weights [token][head] (fp16)
-    __shared__ __attribute__((aligned(16))) uint4 cbuf[2][MD / 8];       // column scales by unit, by page parity
+    __shared__ __attribute__((aligned(16))) uint4 cbuf[2][MD / 8];       // column scales by unit (u at u ^ ((u >> 3) & 7)), by page parity
     __shared__ float alpha[2][HQ];
     __shared__ int rescale_flag[3];
     // ring of chunk slots: codes, token scales (SSC), column scales (SCC)
@@ -181,6 +196,12 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
     const float sm2 = a.sm_scale * kLog2e;
     const bool qk_wave = wave < HB;     // score wave with a head block
     const bool rb_wave = wave >= 4;     // read-back wave
+    // lane keys of yoff's swizzle: score operands (unit 4 j + g4 of token l16
+    // at sk ^ 4 j) and value operands (unit 8 (wave & 1) + (q4 >> 1) of token
+    // 8 g4 + (l16 >> 2) at ak)
+    const int sk = g4 ^ l16;
+    int zk = 0;  // opaque_zero(), renewed per chunk
+    const int ak = (8 * (wave & 1) + ((l16 & 3) >> 1)) ^ ((8 * g4 + (l16 >> 2)) & 15);
 
     // rotated queries of this wave's head block, as QK A operands
     const _Float16* qr = reinterpret_cast<const _Float16*>(a.ws);  // q' at the start of the workspace
@@ -251,8 +272,12 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
         // 32 k-steps (token half th = k >> 4, channels 32 (k & 15) ..), the B
         // operand loaded PF steps ahead; two accumulation chains per half
         constexpr int PF = 8;
+        // unit 4 (k & 15) + g4 of token 16 (k >> 4) + l16: with yoff's swizzle,
+        // 256 ((k & 15) >> 2) + 16 (sk ^ 4 (k & 3)) into the row
+        const uint8_t* yrow = yb + l16 * YROW;
         auto ld = [&](int k) {
-            return *reinterpret_cast<const h8*>(yb + yoff(16 * (k >> 4) + l16, 4 * (k & 15) + g4));
+            const int pos = (sk ^ zk) ^ (4 * (k & 3));
+            return *reinterpret_cast<const h8*>(yrow + 16 * pos + (16 * (k >> 4)) * YROW + 256 * ((k & 15) >> 2));
         };
         h8 by[PF];
 #pragma unroll
@@ -340,12 +365,16 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
         if (tid == 0) rescale_flag[(seq + 2) % 3] = 0;
         // tr16: lane 4k + q of a 16-lane group reads row k, columns 4q .. 4q+3;
         // lane j receives column j of the 4 rows.  Rows are tokens.
+        // unit uu = 8 wave + 2 c + (q4 >> 1) of tokens row and row + 4 (row & 4 = 0):
+        // with yoff's swizzle, 16 (wave >> 1) + (ak ^ 2 c ^ 4 h) into row + 4 h
         const int row = 8 * g4 + (l16 >> 2), q4 = l16 & 3;
+        static_assert(CPW == 64, "a wave's channels are units 8 wave .. 8 wave + 7");
+        const uint8_t* yrow = yb + row * YROW + 8 * (q4 & 1) + 256 * (wave >> 1);
         h8 bv[CBW];  // Y[32 tokens][16 channels]: lane channel l16, tokens 8*g4 .. +7
 #pragma unroll
         for (int c = 0; c < CBW; c++) {
-            const int uu = (CPW * wave + 16 * c) / 8 + (q4 >> 1), hb8 = 8 * (q4 & 1);
-            bv[c] = cat(tr16(yb + yoff(row, uu) + hb8), tr16(yb + yoff(row + 4, uu) + hb8));
+            const int p0 = (ak ^ zk) ^ (2 * c), p1 = (ak ^ zk) ^ (2 * c) ^ 4;
+            bv[c] = cat(tr16(yrow + 16 * p0), tr16(yrow + 4 * YROW + 16 * p1));
         }
 #pragma unroll
         for (int hb = 0; hb < HB; hb++) {
@@ -381,16 +410,17 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
         // byte offsets in the pool (below 4 GiB) as unsigned 32-bit values:
         // the buffer load adds its scalar offset modulo 2^32
         const uint32_t rec = q ? (uint32_t)id * (uint32_t)KREC : 0u;
-        if (q) {  // slot piece 64 w + l holds piece k ^ (t & 7) of token t's row (t = piece >> 4, k = piece & 15)
+        if (q) {  // slot piece 64 w + l holds piece k ^ cswz(t) of token t's row (t = piece >> 4, k = piece & 15)
             const int pc = 64 * wave + lane, t = pc >> 4;
-            lds_dma16(sl + 1024 * wave, rs, t * (MD / 2) + 16 * ((pc & 15) ^ (t & 7)),
+            lds_dma16(sl + 1024 * wave, rs, t * (MD / 2) + 16 * ((pc & 15) ^ cswz(t)),
                       (int)(rec + (uint32_t)(c0 * (MD / 2))));
         }
         else if (lane == 0) lds_dma16(dummy_lds, rs, 0, 0);
         if (q && wave == 0) {
             if (lane < CH / 4) lds_dma16(sl + SSC, rs, 16 * lane, (int)(rec + (uint32_t)(KCB + 4 * c0)));
         } else if (q && wave == 1 && c0 == 0) {
-            lds_dma16(sl + SCC, rs, 16 * lane, (int)(rec + (uint32_t)(KCB + 4 * T)));
+            // unit u at position u ^ ((u >> 3) & 7): the 8 units 8 apart read at once by read_back lie on 8 bank groups
+            lds_dma16(sl + SCC, rs, 16 * (lane ^ ((lane >> 3) & 7)), (int)(rec + (uint32_t)(KCB + 4 * T)));
         } else if (lane == 0) {
             lds_dma16(dummy_lds, rs, 0, 0);
         }
@@ -402,6 +432,7 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
     // come from the slot of its first chunk, where they are also staged in
     // cbuf[page & 1] for its later chunks.
     const int tt = 8 * ((wave - 4) & 3) + (lane & 7), part = (lane >> 3) & 7;
+    const int rk = (8 * (part & 1)) ^ (tt & 15);  // read-back store key: unit 8 part + q8 at 16 (part >> 1) + (rk ^ q8)
     auto read_back = [&](int ci) {
         int page, c0, id;
         qchunk(ci, page, c0, id);
@@ -413,7 +444,7 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
         uint32_t cw[8];
 #pragma unroll
         for (int k = 0; k < 2; k++) {  // pieces 2 part + k of the token's row (see issue_chunk)
-            const uint4 v = *reinterpret_cast<const uint4*>(slot + tt * (MD / 2) + 16 * ((2 * part + k) ^ (tt & 7)));
+            const uint4 v = *reinterpret_cast<const uint4*>(slot + tt * (MD / 2) + 16 * ((2 * part + k) ^ cswz(tt)));
             cw[4 * k] = v.x; cw[4 * k + 1] = v.y; cw[4 * k + 2] = v.z; cw[4 * k + 3] = v.w;
         }
         const uint32_t szw = reinterpret_cast<const uint32_t*>(slot + SSC)[tt];
@@ -432,22 +463,23 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
                 const h2 y = __builtin_elementwise_fma(c, S2, Z2) * __builtin_bit_cast(h2, cs[k]);
                 o[k] = __builtin_bit_cast(uint32_t, y);
             }
-            *reinterpret_cast<uint4*>(yb + yoff(tt, 8 * part + q8)) = make_uint4(o[0], o[1], o[2], o[3]);
+            // yoff(tt, 8 part + q8) = 16 (part >> 1) + (rk ^ q8) into the row
+            *reinterpret_cast<uint4*>(yb + tt * YROW + 256 * (part >> 1) + 16 * ((rk ^ zk) ^ q8)) = make_uint4(o[0], o[1], o[2], o[3]);
         };
         if (c0 == 0) {  // uniform: the page's first chunk brings its column scales
             uint4 keep = make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
             for (int q8 = 0; q8 < 8; q8++) {
-                const uint4 c = cpg[8 * part + q8];  // pairs (0,4) (1,5) (2,6) (3,7) of unit 8 part + q8
+                const uint4 c = cpg[8 * part + ((part ^ zk) ^ q8)];  // pairs (0,4) (1,5) (2,6) (3,7) of unit 8 part + q8
                 const uint4 cv = make_uint4(__builtin_amdgcn_perm(c.z, c.x, 0x05040100u), __builtin_amdgcn_perm(c.z, c.x, 0x07060302u),
                                             __builtin_amdgcn_perm(c.w, c.y, 0x05040100u), __builtin_amdgcn_perm(c.w, c.y, 0x07060302u));
                 if (q8 == (tt & 7)) keep = cv;
                 unit(q8, cv);
             }
-            if (tt < 8) cb[8 * part + tt] = keep;  // staged once per unit for the page's later chunks
+            if (tt < 8) cb[(8 * part + tt) ^ part] = keep;  // staged once per unit for the page's later chunks (same swizzle)
         } else {
 #pragma unroll
-            for (int q8 = 0; q8 < 8; q8++) unit(q8, cb[8 * part + q8]);
+            for (int q8 = 0; q8 < 8; q8++) unit(q8, cb[8 * part + ((part ^ zk) ^ q8)]);
         }
     };
     auto chunk_ok = [&](int ci) {
@@ -461,6 +493,7 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
     if (nqc > 0) {
         asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * (NR - 2)) : "memory");  // chunk 0 has landed
         __syncthreads();
+        zk = opaque_zero();
         if (rb_wave) read_back(0);
         __syncthreads();
     }
@@ -471,6 +504,7 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
         issue_chunk(ci + NR - 1);
         asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * (NR - 2)) : "memory");  // chunk ci + 1 has landed
         __syncthreads();
+        zk = opaque_zero();
         if (ci < nqc) {
             if (qk_wave) {
                 int page, c0, id;
@@ -517,7 +551,8 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
     // against the stored rows, value sums into a fresh accumulator.  The 32 KB
     // of a chunk come by LDS-DMA loads one chunk ahead straight into the
     // read-back row layout of ybuf[1] or ybuf[2] (idle now; one 1 KB token
-    // row per load, channels in natural order); rows past the sequence end
+    // row per load, units swizzled as in yoff, channels in natural order
+    // within a unit); rows past the sequence end
     // are zeroed instead (their weight is 0 and must not meet NaN). ----
 #pragma unroll
     for (int i = 0; i < 4; i++) {
@@ -566,7 +601,8 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
 #pragma unroll
         for (int i = 0; i < 4; i++) {
             const int t = 4 * wave + i;  // token of the chunk
-            if (t < nvalid) lds_dma16(lds_address(yb) + (uint32_t)yoff(t, 0), rf, 16 * lane, (int)(base + 1024u * t));
+            // LDS position l of row t holds unit l ^ (t & 15)
+            if (t < nvalid) lds_dma16(lds_address(yb) + (uint32_t)(t * YROW), rf, 16 * (lane ^ (t & 15)), (int)(base + 1024u * t));
             else *reinterpret_cast<uint4*>(yb + yoff(t, lane)) = make_uint4(0u, 0u, 0u, 0u);
         }
     };
@@ -577,6 +613,7 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
     while (fc.j < nfp) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this chunk has landed
         __syncthreads();
+        zk = opaque_zero();
         const FChunk fn = fnext(fc);
         issue_f(fn, fb ^ 1);  // the other buffer's last reader finished before the barrier above
         const uint8_t* yb = ybuf[1 + fb];
