@@ -58,6 +58,7 @@ def _load():
     lib.orc_decode.argtypes = [P, P, P, P, P, P, P, i32, P, i32, i32, dbl, P, i32, P, i32]
     lib.orc_decode_groups.argtypes = [P, P, P, P, P, P, P, i32, P, i32, i32, dbl, P, i32, P, i32]
     lib.orc_decode_mq.argtypes = [P, P, P, P, P, P, P, i32, P, i32, i32, i32, dbl, P, i32, P, i32]
+    lib.orc_decode_rope.argtypes = [P, P, P, P, P, i32, P, P, i32, P, i32, i32, i32, i32, dbl, P, i32, P, i32]
     _lib = lib
     return lib
 
@@ -315,4 +316,41 @@ def decode_mq(layout, krec, vrec, k16, v16, block_table, seq_lens, q, Hq, sm_sca
     _load().orc_decode_mq(_p(cfg), _p(krec), _p(vrec), _p(k16), _p(v16), _p(block_table), _p(seq_lens),
                           int(max_pages), _p(q), int(is_bf16), M, int(Hq), float(sm_scale), _p(rows), len(rows),
                           _p(out), int(n_threads))
+    return out.reshape(B, M, Hq, D) if full else out
+
+
+def decode_rope(layout, krec, k16, rope_q, rope_f, block_table, seq_lens, q, Hq, sm_scale, causal=False,
+                rows=None, n_threads=0):
+    """MLA decode with a rope sidecar by its plain definition: key t is the
+    latent read-back x_t together with the fp16 rope key r_t, the value is
+    x_t, and score_t = sm_scale (<q_lat, x_t> + <q_rope, r_t>).  r_t comes
+    from rope_q [n_qpages, T, R] (uint16 fp16 bits, indexed like the record
+    pool) when t's page is in the quantized region of the seq_lens[b]
+    committed tokens, else from rope_f [n_fpages, T, R] (indexed like the
+    fp16 pool).  q: [B, M, Hq, D + R] float32 or uint16 bfloat16 bits (M = 1
+    when causal is False).  causal: token i of sequence b sits at
+    seq_lens[b] + i and attends up to itself (a verify step).
+    Returns float64 [B, M, Hq, D] (rows None) or [n_rows, D] for (b, i, h) rows."""
+    cfg = _cfg(layout)
+    assert int(layout["mla"]) == 1
+    block_table = _c(block_table, np.int32)
+    seq_lens = _c(seq_lens, np.int32)
+    B, max_pages = block_table.shape
+    is_bf16 = q.dtype == np.uint16
+    q = np.ascontiguousarray(q)
+    M = int(q.shape[1])
+    D = int(layout["D"])
+    R = int(q.shape[3]) - D
+    assert causal or M == 1
+    rope_q = np.ascontiguousarray(rope_q, dtype=np.uint16)
+    rope_f = np.ascontiguousarray(rope_f, dtype=np.uint16)
+    assert rope_q.shape[-1] == R and rope_f.shape[-1] == R
+    full = rows is None
+    if full:
+        rows = np.array([(b, i, h) for b in range(B) for i in range(M) for h in range(Hq)], np.int32)
+    rows = _c(rows, np.int32).reshape(-1, 3)
+    out = np.zeros((len(rows), D), np.float64)
+    _load().orc_decode_rope(_p(cfg), _p(krec), _p(k16), _p(rope_q), _p(rope_f), R, _p(block_table), _p(seq_lens),
+                            int(max_pages), _p(q), int(is_bf16), M, int(bool(causal)), int(Hq), float(sm_scale),
+                            _p(rows), len(rows), _p(out), int(n_threads))
     return out.reshape(B, M, Hq, D) if full else out

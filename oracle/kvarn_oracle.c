@@ -640,3 +640,79 @@ int orc_decode_mq(const int32_t *cfg, const uint8_t *krec, const uint8_t *vrec,
     }
     return 0;
 }
+
+/* MLA with a rope sidecar.  An MLA model's key has two parts: the
+ * compressed latent, which this method quantizes to int4 [R ¶4] and which
+ * is also the value, and a small rotary-position key beside it (64 wide in
+ * DeepSeek-style MLA), which stays fp16 (the survey's reading of the 2.77x
+ * capacity figure of [R ¶4]: the rope key kept 16-bit is consistent with
+ * it).  Plain definition, per requested row (b, i, h):
+ *   key t = (x_t, r_t), value t = x_t, query = (q_lat[D], q_rope[R]),
+ *   score_t = sm_scale * (<q_lat, x_t> + <q_rope, r_t>),
+ *   out = sum_t softmax_t(score_t) x_t,
+ * with x_t read back as in orc_decode (quantized region of the seq_lens[b]
+ * committed tokens) and r_t, fp16, from the rope pool paired with the
+ * region of t's page: rope_q [n_qpages][T][R] (indexed like the record
+ * pool) for quantized pages, rope_f [n_fpages][T][R] for fp16 pages.
+ * causal = 0: M = 1 and every row attends the seq_lens tokens (a decode
+ * step); causal = 1: token i at position seq_lens[b] + i attends the tokens
+ * up to and including itself (a verify step, as orc_decode_mq).
+ * q: [batch][M][Hq][D + R]; rows: n (b, i, h) triples; out: [n][D]. */
+int orc_decode_rope(const int32_t *cfg, const uint8_t *krec, const uint16_t *k16,
+                    const uint16_t *rope_q, const uint16_t *rope_f, int R,
+                    const int32_t *block_table, const int32_t *seq_lens, int max_pages,
+                    const void *q, int q_is_bf16, int M, int causal, int Hq, double sm_scale,
+                    const int32_t *rows, int n_rows, double *out, int n_threads)
+{
+    int T = cfg[C_T], D = cfg[C_D];
+    int W = D + R;
+    int sink_pages = cfg[C_SINK] / T;
+#ifdef _OPENMP
+    if (n_threads > 0)
+        omp_set_num_threads(n_threads);
+#pragma omp parallel for schedule(dynamic, 1)
+#endif
+    for (int ri = 0; ri < n_rows; ri++) {
+        int b = rows[3 * ri], i = rows[3 * ri + 1], h = rows[3 * ri + 2];
+        int Lr = seq_lens[b];
+        int La = causal ? Lr + i + 1 : Lr;
+        if (La > max_pages * T)
+            La = max_pages * T;
+        int npages = (La + T - 1) / T;
+        int nq = orc_quantized_pages(cfg, Lr);
+        double *qv = (double *)malloc(sizeof(double) * W);
+        double *Kh = (double *)malloc(sizeof(double) * (size_t)npages * T * D + 8);
+        double *Vh = (double *)malloc(sizeof(double) * (size_t)npages * T * D + 8);
+        double *sc = (double *)malloc(sizeof(double) * (size_t)(La > 0 ? La : 1));
+        load_query(q, q_is_bf16, Hq, W, b * M + i, h, qv);
+        read_back(cfg, krec, NULL, k16, NULL, block_table, max_pages, b, 0, Lr, La, Kh, Vh);
+        double m = -INFINITY;
+        for (int t = 0; t < La; t++) {
+            int p = t / T;
+            int id = block_table[(int64_t)b * max_pages + p];
+            int quant = (p >= sink_pages) && (p < sink_pages + nq);
+            const uint16_t *rt = (quant ? rope_q : rope_f) + ((int64_t)id * T + t % T) * R;
+            double acc = 0.0;
+            for (int j = 0; j < D; j++)
+                acc += qv[j] * Kh[(int64_t)t * D + j];
+            for (int r = 0; r < R; r++)
+                acc += qv[D + r] * orc_half_to_double(rt[r]);
+            sc[t] = sm_scale * acc;
+            if (sc[t] > m)
+                m = sc[t];
+        }
+        double l = 0.0;
+        for (int t = 0; t < La; t++) {
+            sc[t] = exp(sc[t] - m);
+            l += sc[t];
+        }
+        for (int j = 0; j < D; j++) {
+            double acc = 0.0;
+            for (int t = 0; t < La; t++)
+                acc += sc[t] * Vh[(int64_t)t * D + j];
+            out[(int64_t)ri * D + j] = La > 0 ? acc / l : 0.0;
+        }
+        free(qv); free(Kh); free(Vh); free(sc);
+    }
+    return 0;
+}

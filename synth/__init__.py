@@ -23,6 +23,7 @@ _M2 = 0x94D049BB133111EB
 # stream ids
 K_STREAM, V_STREAM, Q_STREAM, K_OUT_STREAM, V_OUT_STREAM, PAGE_STREAM = 1, 2, 3, 4, 5, 6
 QPAGE_STREAM = 7
+ROPE_STREAM, QROPE_STREAM = 8, 9
 
 _CHUNK = 1 << 24
 

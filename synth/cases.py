@@ -14,7 +14,12 @@ A case holds, on one device:
   seq_lens      int32 [B]
   src, dst      int32 [n]: fp16 page id -> record page id, for every page
                 that is quantized
-  q             [B][Hq][D], float32 or bfloat16
+  q             [B][Hq][D], float32 or bfloat16 ([B][Hq][D + R] with a rope
+                sidecar: the latent query, then the rope query)
+  rope16, rope_q  (MLA with a rope sidecar of R = w["rope"] channels) fp16
+                rope keys [n_fpages][T][R] placed like k16, and [n_qpages][T][R]
+                holding, for every quantized page, the rope keys of its fp16
+                page at its record page id (what quantizing the page leaves)
 
 Values are keyed by logical coordinate (b, page, head, token, channel), so
 they do not depend on where a page is placed.
@@ -23,8 +28,8 @@ import math
 
 import torch
 
-from . import (K_OUT_STREAM, K_STREAM, PAGE_STREAM, Q_STREAM, QPAGE_STREAM, V_OUT_STREAM,
-               V_STREAM, choose, normal, permutation, student_t3, to_f16)
+from . import (K_OUT_STREAM, K_STREAM, PAGE_STREAM, Q_STREAM, QPAGE_STREAM, QROPE_STREAM, ROPE_STREAM,
+               V_OUT_STREAM, V_STREAM, choose, normal, permutation, student_t3, to_f16)
 
 # fp16 sink (first tokens) and tail (newest tokens) kept unquantized by
 # default: 128 and 1024 tokens.
@@ -66,7 +71,9 @@ LAYOUT_KEYS = ("T", "D", "k_bits", "v_bits", "n_iters", "sink", "tail", "H", "ml
 
 
 def layout_of(w):
-    return {k: int(w[k]) for k in LAYOUT_KEYS}
+    d = {k: int(w[k]) for k in LAYOUT_KEYS}
+    d["rope"] = int(w.get("rope", 0))
+    return d
 
 
 def quantized_page_count(L, T, sink, tail):
@@ -145,6 +152,17 @@ def make_case(w, device="cpu", seq_lens=None, batch=None, with_v=True):
 
     nq_elems = B * Hq * D
     qv = normal(w["seed"], Q_STREAM, nq_elems, device=device).view(B, Hq, D)
+    R = int(w.get("rope", 0)) if mla else 0
+    rope16 = rope_q = None
+    if R > 0:
+        logical = to_f16(normal(w["seed"], ROPE_STREAM, n_f * T * R, device=device)).view(n_f, T, R)
+        rope16 = torch.empty_like(logical)
+        rope16[fperm.long()] = logical
+        rope_q = torch.zeros((max(n_q, 1), T, R), dtype=torch.float16, device=device)
+        if n_q:
+            rope_q[torch.tensor(dst, device=device).long()] = rope16[torch.tensor(src, device=device).long()]
+        qr = normal(w["seed"], QROPE_STREAM, B * Hq * R, device=device).view(B, Hq, R)
+        qv = torch.cat([qv, qr], dim=2)
     q = qv.to({"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[w["q_dtype"]])
 
     return dict(
@@ -152,5 +170,5 @@ def make_case(w, device="cpu", seq_lens=None, batch=None, with_v=True):
                                                                   device=device),
         max_pages=max_pages, n_fpages=n_f, n_qpages=n_q, k16=k16, v16=v16, block_table=bt,
         src=torch.tensor(src, dtype=torch.int32, device=device),
-        dst=torch.tensor(dst, dtype=torch.int32, device=device), q=q,
-        sm_scale=1.0 / math.sqrt(D))
+        dst=torch.tensor(dst, dtype=torch.int32, device=device), q=q, R=R, rope16=rope16, rope_q=rope_q,
+        sm_scale=1.0 / math.sqrt(D + R))

@@ -301,3 +301,126 @@ def test_verify_decode_of_one_token_is_decode_of_one_more_token():
     a = oracle.decode_mq(lay, krec, vrec, k16, v16, bt, sl, q, c["Hq"], c["sm_scale"])
     b = oracle.decode(lay, krec, vrec, k16, v16, bt, sl + 1, q[:, 0], c["Hq"], c["sm_scale"])
     assert np.array_equal(a[:, 0], b)
+
+
+# ---- MLA with a rope sidecar: the latent (int4 records, the value too) plus
+# an fp16 rotary key beside it (evermx.com KVarN review, MLA paragraph: the
+# compressed latent is quantized to int4; the rope key stays 16-bit) ----
+
+def _rope_case(lens, Hq=8, M=0, seed=0x2207):
+    w = dict(WORKLOADS["mla_d512_b32_32k_int4"])
+    w.update(sink=128, tail=256, Hq=Hq, rope=64, seed=seed)
+    c = make_case(w, seq_lens=[L + M for L in lens], batch=len(lens))
+    lay = c["layout"]
+    k16, _, bt, _, q = np_case(c)
+    kb = oracle.record_bytes(lay["T"], 512, 4)
+    krec = np.zeros((max(c["n_qpages"], 1), 1, kb), np.uint8)
+    oracle.quantize_pages(lay, k16, None, c["src"].numpy(), c["dst"].numpy(), krec, None)
+    rf = c["rope16"].numpy().view(np.uint16)
+    rq = c["rope_q"].numpy().view(np.uint16)
+    return c, krec, k16, bt, q, rf, rq
+
+
+def _latent_and_rope(c, krec, k16, rf, rq, bt, b, Lr, La):
+    """Per-token keys (latent read-back, rope key) of sequence b, by page
+    region, through the record fields and the pools (not the oracle decode)."""
+    lay = c["layout"]
+    T = lay["T"]
+    nq = oracle.quantized_pages(lay, Lr)
+    sp = lay["sink"] // T
+    X, Rk = [], []
+    for p in range(math.ceil(La / T)):
+        if sp <= p < sp + nq:
+            X.append(oracle.dequantize_record(krec[bt[b, p], 0], T, 512, 4))
+            Rk.append(rq[bt[b, p]].view(np.float16).astype(np.float64))
+        else:
+            X.append(k16[bt[b, p], 0].view(np.float16).astype(np.float64))
+            Rk.append(rf[bt[b, p]].view(np.float16).astype(np.float64))
+    return np.concatenate(X)[:La], np.concatenate(Rk)[:La]
+
+
+def _bf16(q):
+    return torch.tensor(q.view(np.uint16).astype(np.int32) << 16).view(torch.float32).double().numpy()
+
+
+def test_rope_sidecar_is_attention_over_concatenated_keys():
+    lens = [1000, 1279, 384]
+    c, krec, k16, bt, q, rf, rq = _rope_case(lens)
+    assert c["n_qpages"] > 0
+    sl = c["seq_lens"].numpy()
+    out = oracle.decode_rope(c["layout"], krec, k16, rq, rf, bt, sl, q[:, None], c["Hq"], c["sm_scale"])
+    qd = _bf16(q)
+    for b, L in enumerate(lens):
+        X, Rk = _latent_and_rope(c, krec, k16, rf, rq, bt, b, L, L)
+        for h in (0, 5, 7):
+            ref = sdpa_reference(np.concatenate([X, Rk], axis=1), X, qd[b, h], c["sm_scale"])
+            assert np.allclose(out[b, 0, h], ref, rtol=1e-11, atol=1e-12), (b, h)
+
+
+def test_rope_sidecar_with_zero_rope_query_is_the_latent_decode():
+    lens = [1000, 777]
+    c, krec, k16, bt, q, rf, rq = _rope_case(lens)
+    sl = c["seq_lens"].numpy()
+    q0 = q.copy()
+    q0[..., 512:] = 0
+    a = oracle.decode_rope(c["layout"], krec, k16, rq, rf, bt, sl, q0[:, None], c["Hq"], c["sm_scale"])
+    b = oracle.decode(c["layout"], krec, None, k16, None, bt, sl, np.ascontiguousarray(q0[..., :512]), c["Hq"],
+                      c["sm_scale"])
+    assert np.array_equal(a[:, 0], b)
+
+
+def test_rope_sidecar_reads_each_page_rope_key_from_its_region_pool():
+    # rope keys a page's region does not use are poisoned: the fp16 pages
+    # behind quantized pages (their rope keys were copied out at quantization)
+    # and the unused record ids; the result must stay finite and unchanged
+    lens = [1000, 1279]
+    c, krec, k16, bt, q, rf, rq = _rope_case(lens)
+    sl = c["seq_lens"].numpy()
+    out = oracle.decode_rope(c["layout"], krec, k16, rq, rf, bt, sl, q[:, None], c["Hq"], c["sm_scale"])
+    rf2, rq2 = rf.copy(), np.full((rq.shape[0] + 3,) + rq.shape[1:], 0x7E00, np.uint16)  # NaN
+    rq2[:rq.shape[0]] = rq
+    rf2[c["src"].numpy()] = 0x7E00
+    out2 = oracle.decode_rope(c["layout"], krec, k16, rq2, rf2, bt, sl, q[:, None], c["Hq"], c["sm_scale"])
+    assert np.isfinite(out2).all() and np.array_equal(out, out2)
+
+
+def test_rope_sidecar_dominant_rope_score_selects_its_token():
+    lens = [1000]
+    c, krec, k16, bt, q, rf, rq = _rope_case(lens, Hq=4)
+    sl = c["seq_lens"].numpy()
+    L = lens[0]
+    X, Rk = _latent_and_rope(c, krec, k16, rf, rq, bt, 0, L, L)
+    q2 = np.zeros((1, 1, 4, 576), np.float32)
+    toks = (3, 300, 600, 999)   # fp16 sink, quantized (pages 1..4), quantized, fp16 tail
+    for h, t in enumerate(toks):
+        q2[0, 0, h, 512:] = 4000.0 * Rk[t] / np.linalg.norm(Rk[t])
+    out = oracle.decode_rope(c["layout"], krec, k16, rq, rf, bt, sl, q2, 4, c["sm_scale"])
+    for h, t in enumerate(toks):
+        assert np.allclose(out[0, 0, h], X[t], rtol=1e-9, atol=1e-9), (h, t)
+
+
+@pytest.mark.parametrize("M", [1, 3])
+def test_rope_sidecar_verify_rows_are_causal(M):
+    lens = [1023, 1151, 700]
+    c, krec, k16, bt, q, rf, rq = _rope_case(lens, M=M)
+    lay = c["layout"]
+    # committed lengths: pages that only L + M would quantize stay fp16
+    sp = lay["sink"] // lay["T"]
+    src = c["src"].numpy()
+    base = 0
+    bt = bt.copy()
+    for b, L in enumerate(lens):
+        n_all, n_com = oracle.quantized_pages(lay, L + M), oracle.quantized_pages(lay, L)
+        for i in range(n_com, n_all):
+            bt[b, sp + i] = src[base + i]
+        base += n_all
+    sl = np.array(lens, np.int32)
+    qm = np.random.default_rng(M).standard_normal((len(lens), M, c["Hq"], 576)).astype(np.float32)
+    out = oracle.decode_rope(lay, krec, k16, rq, rf, bt, sl, qm, c["Hq"], c["sm_scale"], causal=True)
+    for b, L in enumerate(lens):
+        for i in range(M):
+            X, Rk = _latent_and_rope(c, krec, k16, rf, rq, bt, b, L, L + i + 1)
+            for h in (0, 7):
+                ref = sdpa_reference(np.concatenate([X, Rk], axis=1), X, qm[b, i, h].astype(np.float64),
+                                     c["sm_scale"])
+                assert np.allclose(out[b, i, h], ref, rtol=1e-11, atol=1e-12), (b, i, h)
