@@ -53,6 +53,14 @@
  * Pools:
  *   record pools  [n_qpages][H][record bytes]   (K and V separately)
  *   fp16 pools    [n_fpages][H][T][D] fp16       (K and V separately)
+ *   MLA with a rope sidecar of R = rope_dim channels (the rotary-position key
+ *   that DeepSeek-style MLA keeps beside the compressed latent; the latent is
+ *   quantized to int4 -- evermx.com review, MLA paragraph -- and the rope key
+ *   stays fp16):
+ *   rope pools    [n_qpages][T][R] fp16 beside the records (rope_records) and
+ *                 [n_fpages][T][R] fp16 beside the fp16 pages (rope_fp16);
+ *                 a token's rope key sits in the pool of its page's region,
+ *                 at the page id the block table gives for that page.
  *
  * Regions of a sequence of L tokens (page p covers tokens [p*T, p*T+T)):
  *   nq(L) = max(0, floor((L - sink - tail) / T)) quantized pages;
@@ -93,6 +101,8 @@ typedef struct kvarn_layout {
     int32_t tail_tokens;   /* newest tokens kept fp16, >= 0 (default 1024) */
     int32_t num_kv_heads;  /* H >= 1; 1 when mla = 1 */
     int32_t mla;           /* 1: one latent record per token serves as key and value */
+    int32_t rope_dim;      /* MLA only: width R of the fp16 rope key kept beside each latent,
+                              0 (none) or 64; 0 when mla = 0 */
 } kvarn_layout;
 
 /* Device pools of one layer.  Caller-owned; all pointers 16-byte aligned. */
@@ -103,6 +113,8 @@ typedef struct kvarn_cache {
     void *v_fp16;          /* device, fp16 [n_fpages][H][T][D]; NULL if mla */
     int64_t n_qpages;      /* pages in each record pool */
     int64_t n_fpages;      /* pages in each fp16 pool */
+    void *rope_records;    /* device, fp16 [n_qpages][T][rope_dim]; NULL if rope_dim = 0 */
+    void *rope_fp16;       /* device, fp16 [n_fpages][T][rope_dim]; NULL if rope_dim = 0 */
 } kvarn_cache;
 
 /* Page table of a decode batch.  Caller-owned device arrays. */
@@ -142,7 +154,9 @@ int32_t kvarn_quantized_pages(const kvarn_layout *layout, int32_t seq_len);
  * src_fpages, dst_qpages: device int32 [n].  The caller passes only pages
  * that are full and whose every token has been accepted (the commit rule of
  * the evermx.com review, MLA and hybrid paragraph) and distinct dst ids.  n = 0 is a
- * no-op.  Reads cache->k_fp16/v_fp16, writes cache->k_records/v_records. */
+ * no-op.  Reads cache->k_fp16/v_fp16, writes cache->k_records/v_records; with
+ * a rope sidecar also copies rope page src_fpages[i] of rope_fp16 to rope
+ * page dst_qpages[i] of rope_records unchanged. */
 kvarn_status kvarn_quantize(const kvarn_layout *layout, const kvarn_cache *cache,
                             const int32_t *src_fpages, const int32_t *dst_qpages,
                             int32_t n, void *stream);
@@ -160,7 +174,11 @@ size_t kvarn_decode_workspace_bytes(const kvarn_layout *layout, int32_t batch,
  * applied once to q and once (inverse) to the output, and the scales are
  * folded into the score and value sums: no dequantized cache is written.
  * q: device [batch][num_q_heads][D] of q_dtype (KVARN_F32, KVARN_F16 or
- * KVARN_BF16; any other value is KVARN_EINVAL), 16-byte aligned.
+ * KVARN_BF16; any other value is KVARN_EINVAL), 16-byte aligned.  MLA with a
+ * rope sidecar: q is [batch][num_q_heads][D + R] (the latent query, then the
+ * rope query), k_t is the pair (latent read-back, rope key) and
+ *   <q, k_t> = <q_latent, latent_t> + <q_rope, rope_t>,
+ * the value still the latent alone.
  * out: device fp32 [batch][num_q_heads][D], original basis; a sequence with
  * L = 0 gives zeros.  workspace: device, at least
  * kvarn_decode_workspace_bytes(...) bytes, 256-byte aligned; its contents
@@ -168,7 +186,7 @@ size_t kvarn_decode_workspace_bytes(const kvarn_layout *layout, int32_t batch,
  * of H (GQA: a group of any multiple of 4 query heads per KV head, at
  * most 65535 groups of 4 in all; MLA: 16, 32, 64 or 128).  With head_dim 128
  * (GQA) and with MLA each record pool, n_qpages * H * record bytes, must be
- * below 4 GiB, and with MLA the fp16 pool too; GQA takes at most 32767
+ * below 4 GiB, and with MLA the fp16 pool and the rope pools too; GQA takes at most 32767
  * sequences per call (KVARN_EUNSUPPORTED otherwise).  Negative pool sizes are
  * KVARN_EINVAL. */
 kvarn_status kvarn_decode_attn(const kvarn_layout *layout, const kvarn_cache *cache,
@@ -213,6 +231,8 @@ kvarn_status kvarn_decode_attn_mq(const kvarn_layout *layout, const kvarn_cache 
  * k_new, v_new: device [batch][n_new][H][D] of dtype (KVARN_F32, KVARN_F16
  * or KVARN_BF16; converted to fp16 by round to nearest even, values beyond
  * the fp16 range become infinities), 16-byte aligned; v_new is NULL for MLA.
+ * MLA with a rope sidecar: k_new rows are [D + R], the latent (to k_fp16)
+ * then the rope key (to rope_fp16, same page and slot).
  * The caller assigns the block-table entries of pages that receive tokens
  * (ids of fp16 pages).  A position past max_pages * T or a page id outside
  * the fp16 pool is skipped.  n_new = 0 is a no-op. */
@@ -227,8 +247,8 @@ kvarn_status kvarn_append(const kvarn_layout *layout, const kvarn_cache *cache,
  *     whole pages after the sink, leaving at least tail_tokens in fp16), the
  *     page -- every token of which is now committed, the commit rule of the
  *     evermx.com review, MLA and hybrid paragraph -- is quantized (as by
- *     kvarn_quantize) from its fp16 page into record page new_qpages[b], and
- *     block_table[b][page] is set to new_qpages[b].
+ *     kvarn_quantize, rope keys included) from its fp16 page into record page
+ *     new_qpages[b], and block_table[b][page] is set to new_qpages[b].
  * promoted_fpages[b] reports, per sequence: the fp16 page id that was
  * quantized (>= 0; the caller may reuse that fp16 page), -1 nothing
  * promoted, -2 n_accept[b] outside [0, T] or seq_lens[b] + n_accept[b] past

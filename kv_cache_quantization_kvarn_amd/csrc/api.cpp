@@ -31,6 +31,8 @@ kvarn_status ok() {
 // code widths of the gmlx documentation, "The two schemes": 2, 3, 4, 5, 6 and 8
 bool width_ok(int b) { return b == 2 || b == 3 || b == 4 || b == 5 || b == 6 || b == 8; }
 
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
 kvarn_status check_layout(const kvarn_layout* L) {
     if (!L) return fail(KVARN_EINVAL, "layout is NULL");
     if (L->head_dim != 128 && L->head_dim != 256 && L->head_dim != 512)
@@ -55,14 +57,28 @@ kvarn_status check_layout(const kvarn_layout* L) {
         return fail(KVARN_EUNSUPPORTED, "sink_tokens %d must be a non-negative multiple of tile_tokens %d",
                     L->sink_tokens, L->tile_tokens);
     if (L->tail_tokens < 0) return fail(KVARN_EINVAL, "tail_tokens %d must be >= 0", L->tail_tokens);
+    if (L->rope_dim != 0) {
+        if (!L->mla) return fail(KVARN_EINVAL, "rope_dim %d: a rope sidecar belongs to MLA layouts only", L->rope_dim);
+        if (L->rope_dim != 64)
+            return fail(KVARN_EUNSUPPORTED, "rope_dim %d: a 64-wide rope key (or none) is implemented", L->rope_dim);
+    }
+    return KVARN_OK;
+}
+
+// rope pools of a layout with a rope sidecar: present and 16-byte aligned
+// (the record-side pool only where record pages exist)
+kvarn_status check_rope_pools(const kvarn_layout* L, const kvarn_cache* c, bool need_records) {
+    if (L->rope_dim == 0) return KVARN_OK;
+    if (!c->rope_fp16 || (need_records && !c->rope_records))
+        return fail(KVARN_EINVAL, "rope_dim %d: the rope pools are NULL", L->rope_dim);
+    if (!aligned16(c->rope_fp16) || (c->rope_records && !aligned16(c->rope_records)))
+        return fail(KVARN_EINVAL, "rope pools must be 16-byte aligned");
     return KVARN_OK;
 }
 
 size_t rec_bytes(const kvarn_layout* L, int bits) {
     return (size_t)L->tile_tokens * L->head_dim * bits / 8 + 4 * (size_t)L->tile_tokens + 2 * (size_t)L->head_dim;
 }
-
-bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 
 // Workspace of a decode call with M query tokens per sequence (rows =
@@ -124,6 +140,14 @@ kvarn_status decode_common(const kvarn_layout* layout, const kvarn_cache* cache,
     if (cache->n_qpages > 0 && (!cache->k_records || (!layout->mla && !cache->v_records)))
         return fail(KVARN_EINVAL, "record pools are NULL");
     if (!(sm_scale > 0.f) || sm_scale > 1e30f) return fail(KVARN_EINVAL, "sm_scale must be positive and finite");
+    st = check_rope_pools(layout, cache, cache->n_qpages > 0);
+    if (st != KVARN_OK) return st;
+    if (layout->rope_dim) {
+        // the MLA kernel streams the rope pools through 32-bit offsets too
+        const uint64_t page = (uint64_t)layout->tile_tokens * (uint64_t)layout->rope_dim * 2u;
+        if ((uint64_t)cache->n_qpages * page >= (1ull << 32) || (uint64_t)cache->n_fpages * page >= (1ull << 32))
+            return fail(KVARN_EUNSUPPORTED, "mla: rope pools below 4 GiB each are implemented");
+    }
     if (layout->mla || layout->head_dim == 128) {
         // the MLA and head_dim 128 kernels address each record pool with 32-bit byte offsets
         const uint64_t kb = (uint64_t)cache->n_qpages * (uint64_t)H * kvarn_record_bytes(layout, 0);
@@ -180,6 +204,9 @@ kvarn_status decode_common(const kvarn_layout* layout, const kvarn_cache* cache,
     a.seq_lens = pages->seq_lens;
     a.q = q;
     a.q_dtype = q_dtype;
+    a.R = layout->rope_dim;
+    a.rope_records = cache->rope_records;
+    a.rope_fp16 = cache->rope_fp16;
     a.sm_scale = sm_scale;
     a.out = out;
     a.ws = static_cast<float*>(workspace);
@@ -265,6 +292,8 @@ kvarn_status kvarn_quantize(const kvarn_layout* layout, const kvarn_cache* cache
     if (cache->n_fpages < 1 || cache->n_qpages < 1) return fail(KVARN_EINVAL, "empty pools");
     if ((int64_t)n * layout->num_kv_heads * (layout->mla ? 1 : 2) > 0x7fffffffLL)
         return fail(KVARN_EINVAL, "too many pages in one call: pages x heads x (K, V) must fit one grid");
+    st = check_rope_pools(layout, cache, true);
+    if (st != KVARN_OK) return st;
     kvarn::QuantizeArgs a{};
     a.D = layout->head_dim;
     a.T = layout->tile_tokens;
@@ -282,6 +311,9 @@ kvarn_status kvarn_quantize(const kvarn_layout* layout, const kvarn_cache* cache
     a.n = n;
     a.n_fpages = cache->n_fpages;
     a.n_qpages = cache->n_qpages;
+    a.R = layout->rope_dim;
+    a.rope_fp16 = cache->rope_fp16;
+    a.rope_records = cache->rope_records;
     hipError_t e = kvarn::launch_quantize(a, (hipStream_t)stream);
     if (e != hipSuccess) return fail(KVARN_EHIP, "quantize launch failed: %s", hipGetErrorString(e));
     return ok();
@@ -336,7 +368,10 @@ kvarn_status kvarn_append(const kvarn_layout* layout, const kvarn_cache* cache, 
         (!layout->mla && !aligned16(cache->v_fp16)))
         return fail(KVARN_EINVAL, "new tokens and fp16 pools must be 16-byte aligned");
     if (cache->n_fpages < 1) return fail(KVARN_EINVAL, "empty fp16 pool");
-    const int64_t threads = (int64_t)pages->batch * n_new * layout->num_kv_heads * (layout->head_dim / 8);
+    st = check_rope_pools(layout, cache, false);
+    if (st != KVARN_OK) return st;
+    const int64_t threads =
+        (int64_t)pages->batch * n_new * layout->num_kv_heads * ((layout->head_dim + layout->rope_dim) / 8);
     if (threads > ((int64_t)1 << 40)) return fail(KVARN_EINVAL, "too many new values in one call");
     kvarn::AppendArgs a{};
     a.D = layout->head_dim;
@@ -346,6 +381,8 @@ kvarn_status kvarn_append(const kvarn_layout* layout, const kvarn_cache* cache, 
     a.n_new = n_new;
     a.max_pages = pages->max_pages;
     a.dtype = dtype;
+    a.R = layout->rope_dim;
+    a.rope_fp16 = cache->rope_fp16;
     a.k_new = k_new;
     a.v_new = layout->mla ? nullptr : v_new;
     a.k_fp16 = cache->k_fp16;
@@ -374,6 +411,8 @@ kvarn_status kvarn_commit(const kvarn_layout* layout, const kvarn_cache* cache, 
     if (cache->n_fpages < 1 || cache->n_qpages < 1) return fail(KVARN_EINVAL, "empty pools");
     if ((int64_t)batch * layout->num_kv_heads * (layout->mla ? 1 : 2) > 0x7fffffffLL)
         return fail(KVARN_EINVAL, "batch x heads x (K, V) must fit one grid");
+    st = check_rope_pools(layout, cache, true);
+    if (st != KVARN_OK) return st;
     kvarn::CommitArgs c{};
     c.T = layout->tile_tokens;
     c.sink = layout->sink_tokens;
@@ -404,6 +443,9 @@ kvarn_status kvarn_commit(const kvarn_layout* layout, const kvarn_cache* cache, 
     q.n = batch;
     q.n_fpages = cache->n_fpages;
     q.n_qpages = cache->n_qpages;
+    q.R = layout->rope_dim;
+    q.rope_fp16 = cache->rope_fp16;
+    q.rope_records = cache->rope_records;
     hipError_t e = kvarn::launch_commit(c, q, (hipStream_t)stream);
     if (e != hipSuccess) return fail(KVARN_EHIP, "commit launch failed: %s", hipGetErrorString(e));
     return ok();

@@ -57,14 +57,16 @@ __device__ __forceinline__ uint4 load8_as_f16(const void* src, int64_t e) {
     }
 }
 
-// thread = 8 channels of one (sequence b, new token i, head h)
+// thread = 8 channels of one (sequence b, new token i, head h); with an MLA
+// rope sidecar (R > 0, H = 1) a new row holds the D latent channels, then
+// the R rope channels, which go to the rope pool
 template <int DT>
 __global__ void append_kernel(const void* __restrict__ knew, const void* __restrict__ vnew,
-                              uint16_t* __restrict__ kpool, uint16_t* __restrict__ vpool,
+                              uint16_t* __restrict__ kpool, uint16_t* __restrict__ vpool, uint16_t* __restrict__ rpool,
                               const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens, int B,
-                              int n_new, int H, int D, int T, int max_pages, int64_t n_fpages) {
+                              int n_new, int H, int D, int R, int T, int max_pages, int64_t n_fpages) {
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int per_row = D / 8;
+    const int per_row = (D + R) / 8;
     const int64_t total = (int64_t)B * n_new * H * per_row;
     if (idx >= total) return;
     const int c8 = (int)(idx % per_row);
@@ -80,7 +82,12 @@ __global__ void append_kernel(const void* __restrict__ knew, const void* __restr
     if (p >= max_pages) return;
     const int id = block_table[(int64_t)b * max_pages + p];
     if (id < 0 || (int64_t)id >= n_fpages) return;
-    const int64_t src = (((int64_t)b * n_new + i) * H + h) * D + 8 * c8;
+    const int64_t src = (((int64_t)b * n_new + i) * H + h) * (D + R) + 8 * c8;
+    if (8 * c8 >= D) {  // rope channels (R > 0: MLA, H = 1)
+        const int64_t rdst = ((int64_t)id * T + (pos % T)) * R + (8 * c8 - D);
+        *reinterpret_cast<uint4*>(rpool + rdst) = load8_as_f16<DT>(knew, src);
+        return;
+    }
     const int64_t dst = (((int64_t)id * H + h) * T + (pos % T)) * D + 8 * c8;
     *reinterpret_cast<uint4*>(kpool + dst) = load8_as_f16<DT>(knew, src);
     if (vpool) *reinterpret_cast<uint4*>(vpool + dst) = load8_as_f16<DT>(vnew, src);
@@ -132,16 +139,18 @@ __global__ void commit_apply_kernel(int32_t* __restrict__ block_table, int32_t* 
 }  // namespace
 
 hipError_t launch_append(const AppendArgs& a, hipStream_t st) {
-    const int64_t total = (int64_t)a.B * a.n_new * a.H * (a.D / 8);
+    const int64_t total = (int64_t)a.B * a.n_new * a.H * ((a.D + a.R) / 8);
     if (total == 0) return hipSuccess;
+    if (a.R > 0 && (a.H != 1 || a.v_fp16 || !a.rope_fp16)) return hipErrorInvalidValue;
     const int threads = 256;
     const int64_t blocks = (total + threads - 1) / threads;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
     auto* kp = static_cast<uint16_t*>(a.k_fp16);
     auto* vp = static_cast<uint16_t*>(a.v_fp16);
+    auto* rp = static_cast<uint16_t*>(a.rope_fp16);
 #define KVARN_APPEND(DT)                                                                                     \
     hipLaunchKernelGGL(append_kernel<DT>, dim3((unsigned)blocks), dim3(threads), 0, st, a.k_new, a.v_new, kp, vp, \
-                       a.block_table, a.seq_lens, a.B, a.n_new, a.H, a.D, a.T, a.max_pages, a.n_fpages)
+                       rp, a.block_table, a.seq_lens, a.B, a.n_new, a.H, a.D, a.R, a.T, a.max_pages, a.n_fpages)
     switch (a.dtype) {
         case 0: KVARN_APPEND(0); break;
         case 1: KVARN_APPEND(1); break;

@@ -109,11 +109,13 @@ __device__ __forceinline__ float rsum16(float v) {
     return v;
 }
 
-// q' = H q / sqrt(D) as fp16, one workgroup per (sequence, head).
-__global__ void __launch_bounds__(256) qrot_kernel(const void* __restrict__ q, int q_dtype, _Float16* __restrict__ qr) {
+// q' = H q / sqrt(D) as fp16, one workgroup per (sequence, head); query rows
+// of W elements (the latent query first: W = D, or D + R with a rope sidecar).
+__global__ void __launch_bounds__(256) qrot_kernel(const void* __restrict__ q, int q_dtype, int W,
+                                                   _Float16* __restrict__ qr) {
     __shared__ float x[MD];
     const int bh = blockIdx.x;
-    for (int j = threadIdx.x; j < MD; j += 256) x[j] = q_at(q, q_dtype, (int64_t)bh * MD + j);
+    for (int j = threadIdx.x; j < MD; j += 256) x[j] = q_at(q, q_dtype, (int64_t)bh * W + j);
     __syncthreads();
     for (int hs = 1; hs < MD; hs <<= 1) {
         const int k = threadIdx.x;  // 256 butterflies per stage
@@ -151,7 +153,15 @@ struct MlaShape {
 // and chunk c scored, and the value sums of chunk c - 1 are formed), then its
 // fp16 chunks.  Chunk s (the quantized ones, then the fp16 ones) uses read-back
 // buffer s mod 3 (quantized) or 0 (fp16), weight and rescale buffers s mod 2 and rescale flag s mod 3.
-template <int T, int HB>
+//
+// ROPE: a 64-wide fp16 rope key beside each latent (DeepSeek-style MLA; the
+// latent alone is quantized, evermx.com KVarN review, MLA paragraph) adds
+// <q_rope, r_t> to every score.  A chunk's rope keys (4 KB) come by LDS-DMA
+// into rbuf[s mod 3] one iteration ahead of its score, as each wave's first
+// load of the iteration (so the fixed wait count rises by one); they take two
+// more k-steps per token half of the score MFMAs, with the rope query (fp16,
+// natural channel order) as their A operand.
+template <int T, int HB, bool ROPE>
 __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs a) {
     using SH = MlaShape<HB>;
     constexpr int NWV = SH::NWV, CPW = SH::CPW, CBW = SH::CBW, HQ = SH::HQ;
@@ -171,6 +181,10 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
     static_assert(SSC == NWV * 1024, "one 1 KB code load per wave and chunk");
     __shared__ __attribute__((aligned(16))) uint8_t ring[NR * SLOT];
     __shared__ __attribute__((aligned(16))) uint8_t scratch[16 * NWV];  // targets of the stand-in loads
+    // rope keys of a chunk: token rows of RROW bytes, unit u of token t at
+    // position u ^ ((t >> 1) & 7) (16 tokens read together lie on 16 bank groups)
+    constexpr int RD = ROPE ? 64 : 0, RROW = 2 * RD;
+    __shared__ __attribute__((aligned(16))) uint8_t rbuf[ROPE ? 3 : 1][ROPE ? CH * RROW : 16];
 
     // Workgroup id -> (head group hg, query token m, split, sequence bs).
     // Workgroups are dealt to the 8 XCDs round-robin; the head groups and the
@@ -214,6 +228,21 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
             qa[ks] = h8{v[0], v[4], v[1], v[5], v[2], v[6], v[3], v[7]};  // unit order
         } else {
             qa[ks] = h8{0, 0, 0, 0, 0, 0, 0, 0};
+        }
+    }
+    // rope query of this wave's head block (natural channel order), as the A
+    // operand of two more k-steps: lane head l16, channels 32 kk + 8 g4 ..
+    h8 qro[2] = {h8{0, 0, 0, 0, 0, 0, 0, 0}, h8{0, 0, 0, 0, 0, 0, 0, 0}};
+    if constexpr (ROPE) {
+        if (qk_wave) {
+            const int64_t qi = ((int64_t)b * a.Hq + h0 + wave * 16 + l16) * (MD + RD) + MD + 8 * g4;
+#pragma unroll
+            for (int kk = 0; kk < 2; kk++) {
+                float x[8];
+                q_load<8>(a.q, a.q_dtype, qi + 32 * kk, x);
+                qro[kk] = h8{(_Float16)x[0], (_Float16)x[1], (_Float16)x[2], (_Float16)x[3],
+                             (_Float16)x[4], (_Float16)x[5], (_Float16)x[6], (_Float16)x[7]};
+            }
         }
     }
     if (tid < 3) rescale_flag[tid] = 0;
@@ -262,13 +291,14 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
     };
 #pragma unroll
     for (int ks = 0; ks < 16; ks++) asm volatile("" ::"v"(qa[ks]));
+    asm volatile("" ::"v"(qro[0]), "v"(qro[1]));
     __syncthreads();
 
     // ---- score waves: scores, softmax and weights of chunk seq, held in yb
     // (32 tokens from sequence position tok0; positions past the sequence end
     // get weight 0).  Sets bit `wave` of rescale_flag[seq % 3] when a
     // running maximum of its head block moves. ----
-    auto score = [&](const uint8_t* yb, int tok0, int seq) {
+    auto score = [&](const uint8_t* yb, const uint8_t* rb, int tok0, int seq) {
         // 32 k-steps (token half th = k >> 4, channels 32 (k & 15) ..), the B
         // operand loaded PF steps ahead; two accumulation chains per half
         constexpr int PF = 8;
@@ -288,6 +318,20 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
             const h8 cur = by[k % PF];
             if (k + PF < 32) by[k % PF] = ld(k + PF);
             acc[k >> 4][k & 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[k & 15], cur, acc[k >> 4][k & 1], 0, 0, 0);
+        }
+        if constexpr (ROPE) {  // unit 4 kk + g4 of token 16 th + l16's rope key, with rbuf's swizzle
+            h8 br[2][2];
+#pragma unroll
+            for (int th = 0; th < 2; th++)
+#pragma unroll
+                for (int kk = 0; kk < 2; kk++)
+                    br[th][kk] = *reinterpret_cast<const h8*>(rb + (16 * th + l16) * RROW +
+                                                               16 * ((4 * kk + g4) ^ ((l16 >> 1) & 7)));
+#pragma unroll
+            for (int th = 0; th < 2; th++)
+#pragma unroll
+                for (int kk = 0; kk < 2; kk++)
+                    acc[th][kk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qro[kk], br[th][kk], acc[th][kk], 0, 0, 0);
         }
         const f4 sacc[2] = {acc[0][0] + acc[0][1], acc[1][0] + acc[1][1]};
         // lane: heads 16*wave + 4*g4 + i, tokens 16*th + l16 of the chunk
@@ -425,6 +469,26 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
             lds_dma16(dummy_lds, rs, 0, 0);
         }
     };
+    // rope keys of quantized chunk cj -> rbuf[cj % 3]: wave w loads tokens
+    // 4 w .. 4 w + 3 (lanes 0..31, position l & 7 of token 4 w + (l >> 3));
+    // a one-lane stand-in load where there is nothing to load
+    const i32x4 rrs = raw_buffer(a.rope_records, ROPE ? (uint32_t)(a.n_qpages * T * RROW) : 0u);
+    auto issue_rope = [&](int cj) {
+        if constexpr (ROPE) {
+            int page = 0, c0 = 0, id = -1;
+            if (cj < nqc) qchunk(cj, page, c0, id);
+            if (id >= 0) {
+                if (lane < 32) {
+                    const int t = 4 * wave + (lane >> 3);
+                    lds_dma16(lds_address(rbuf[cj % 3]) + 512u * wave, rrs,
+                              t * RROW + 16 * ((lane & 7) ^ ((t >> 1) & 7)),
+                              (int)(((uint32_t)id * (uint32_t)T + (uint32_t)c0) * (uint32_t)RROW));
+                }
+            } else if (lane == 0) {
+                lds_dma16(dummy_lds, rs, 0, 0);
+            }
+        }
+    };
     // read-back waves: chunk ci (landed) -> ybuf[ci % 3], rotated basis, fp16.
     // Lane l of read-back wave 4 + v takes token tt = 8 v + (l & 7), units
     // 8 part .. +8 (channels 64 part ..) with part = l >> 3: the 8 lanes of an
@@ -488,10 +552,15 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
         return id >= 0;
     };
 
+    // loads in flight after the ones a wait needs: the codes and scales of the
+    // next two chunks, and with ROPE the rope keys of the next chunk
+    constexpr int VMW = 2 * (NR - 2) + (ROPE ? 1 : 0);
+    issue_chunk(0);
+    issue_rope(0);
 #pragma unroll
-    for (int cj = 0; cj < NR - 1; cj++) issue_chunk(cj);
+    for (int cj = 1; cj < NR - 1; cj++) issue_chunk(cj);
     if (nqc > 0) {
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * (NR - 2)) : "memory");  // chunk 0 has landed
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(VMW) : "memory");  // chunk 0 has landed
         __syncthreads();
         zk = opaque_zero();
         if (rb_wave) read_back(0);
@@ -501,15 +570,16 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
     // score chunk ci while chunk ci + 1 is read back, then the value sums of
     // chunk ci - 1 (iteration nqc only forms those of the last chunk)
     for (int ci = 0; ci <= nqc; ci++) {
+        issue_rope(ci + 1);
         issue_chunk(ci + NR - 1);
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * (NR - 2)) : "memory");  // chunk ci + 1 has landed
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(VMW) : "memory");  // chunk ci + 1 (and rope ci) have landed
         __syncthreads();
         zk = opaque_zero();
         if (ci < nqc) {
             if (qk_wave) {
                 int page, c0, id;
                 qchunk(ci, page, c0, id);
-                if (id >= 0) score(ybuf[ci % 3], page * T + c0, ci);
+                if (id >= 0) score(ybuf[ci % 3], rbuf[ROPE ? ci % 3 : 0], page * T + c0, ci);
             } else if (rb_wave && ci + 1 < nqc) {
                 read_back(ci + 1);
             }
@@ -564,7 +634,7 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
 #pragma unroll
         for (int c = 0; c < CBW; c++) O[hb][c] = f4{0.f, 0.f, 0.f, 0.f};
     if (qk_wave && nfp > 0) {  // the plain query of this wave's head block, natural channel order
-        const int64_t qi = ((int64_t)b * a.Hq + h0 + wave * 16 + l16) * MD + 8 * g4;
+        const int64_t qi = ((int64_t)b * a.Hq + h0 + wave * 16 + l16) * (MD + RD) + 8 * g4;
 #pragma unroll
         for (int ks = 0; ks < 16; ks++) {
             float x[8];
@@ -575,6 +645,7 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
     }
     static_assert(CH * MD * 2 <= CH * YROW, "an fp16 chunk fits a read-back buffer");
     const i32x4 rf = raw_buffer(a.k_fp16, (uint32_t)(a.n_fpages * T * MD * 2));
+    const i32x4 rfr = raw_buffer(a.rope_fp16, ROPE ? (uint32_t)(a.n_fpages * T * RROW) : 0u);
     auto fchunks = [&](int j) {  // chunks holding tokens of the split's j-th fp16 page (0: none or a bad id)
         const int page = fpage(j);
         const int id = page_id(nqp + j);
@@ -605,6 +676,13 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
             if (t < nvalid) lds_dma16(lds_address(yb) + (uint32_t)(t * YROW), rf, 16 * (lane ^ (t & 15)), (int)(base + 1024u * t));
             else *reinterpret_cast<uint4*>(yb + yoff(t, lane)) = make_uint4(0u, 0u, 0u, 0u);
         }
+        if constexpr (ROPE) {  // the chunk's 32 rope keys (rows past the end only meet scores set to -inf)
+            if (lane < 32) {
+                const int t = 4 * wave + (lane >> 3);
+                lds_dma16(lds_address(rbuf[buf]) + 512u * wave, rfr, t * RROW + 16 * ((lane & 7) ^ ((t >> 1) & 7)),
+                          (int)(((uint32_t)id * (uint32_t)T + (uint32_t)(f.cc * CH)) * (uint32_t)RROW));
+            }
+        }
     };
     int fseq = nqc;  // chunk numbering continues from the quantized chunks
     FChunk fc = fnext(FChunk{0, -1});
@@ -617,7 +695,7 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
         const FChunk fn = fnext(fc);
         issue_f(fn, fb ^ 1);  // the other buffer's last reader finished before the barrier above
         const uint8_t* yb = ybuf[1 + fb];
-        if (qk_wave) score(yb, fpage(fc.j) * T + fc.cc * CH, fseq);
+        if (qk_wave) score(yb, rbuf[ROPE ? fb : 0], fpage(fc.j) * T + fc.cc * CH, fseq);
         __syncthreads();
         accumulate(yb, fseq);
         fseq++;
@@ -674,14 +752,16 @@ __global__ void __launch_bounds__(256) mla_combine_kernel(const float* __restric
 
 template <int T, int HB>
 hipError_t launch_mla_t(const DecodeArgs& a, hipStream_t st) {
-    hipLaunchKernelGGL(qrot_kernel, dim3(a.B * a.Hq), dim3(256), 0, st, a.q, a.q_dtype,
+    if (a.R != 0 && a.R != 64) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(qrot_kernel, dim3(a.B * a.Hq), dim3(256), 0, st, a.q, a.q_dtype, MD + a.R,
                        reinterpret_cast<_Float16*>(a.ws));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int nhg = a.Hq / (16 * HB);
     const int units = (a.B / a.M) * a.nsplit;
     const int blocks = ((units + 7) / 8) * 8 * nhg * a.M;
-    hipLaunchKernelGGL((mla_split_kernel<T, HB>), dim3(blocks), dim3(MlaShape<HB>::NT), 0, st, a);
+    if (a.R) hipLaunchKernelGGL((mla_split_kernel<T, HB, true>), dim3(blocks), dim3(MlaShape<HB>::NT), 0, st, a);
+    else hipLaunchKernelGGL((mla_split_kernel<T, HB, false>), dim3(blocks), dim3(MlaShape<HB>::NT), 0, st, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const float* wsp = a.ws + (int64_t)a.B * a.Hq * MD / 2;

@@ -20,8 +20,13 @@ struct QuantizeArgs {
     const int32_t* dst;
     int32_t n;
     int64_t n_fpages, n_qpages;
+    int R;                    // MLA rope sidecar width (0: none)
+    const void* rope_fp16;    // fp16 [n_fpages][T][R]: rope keys of the fp16 pages
+    void* rope_records;       // fp16 [n_qpages][T][R]: rope keys of the record pages
 };
 
+// Quantize the pages, and with a rope sidecar copy each page's rope keys to
+// its record page.
 hipError_t launch_quantize(const QuantizeArgs& a, hipStream_t st);
 
 // One kernel launch for keys and values (HASV) or the MLA latent alone;
@@ -50,8 +55,11 @@ struct DecodeArgs {
     int64_t n_qpages, n_fpages;
     const int32_t* block_table;
     const int32_t* seq_lens;
-    const void* q;
+    const void* q;    // [B][Hq][D + R]
     int q_dtype;      // 0 float32, 1 float16, 2 bfloat16
+    int R;            // MLA rope sidecar width (0: none, 64)
+    const void* rope_records;  // fp16 [n_qpages][T][R]
+    const void* rope_fp16;     // fp16 [n_fpages][T][R]
     float sm_scale;
     float* out;
     float* ws;        // split partials
@@ -80,10 +88,12 @@ hipError_t launch_gqa_wide(const DecodeArgs& a, hipStream_t st);
 
 struct AppendArgs {
     int D, T, H, B, n_new, max_pages, dtype;  // dtype: 0 f32, 1 f16, 2 bf16
+    int R;              // MLA rope sidecar width: k_new rows hold D + R values
     const void* k_new;
     const void* v_new;  // NULL for MLA
     void* k_fp16;
     void* v_fp16;       // NULL for MLA
+    void* rope_fp16;    // fp16 [n_fpages][T][R] (R > 0)
     const int32_t* block_table;
     const int32_t* seq_lens;
     int64_t n_fpages;

@@ -29,6 +29,32 @@ hipError_t one_kind(int bits, const QuantizeArgs& a, hipStream_t st) {
 
 bool even_width(int b) { return b == 2 || b == 4 || b == 6; }
 
+// Rope sidecar: page i's T x R fp16 rope keys, fp16 page src[i] -> record
+// page dst[i], 16 bytes a thread; a pair with an id outside its pool is
+// skipped (as the quantize kernel skips it).
+__global__ void __launch_bounds__(256) rope_copy_kernel(const uint4* __restrict__ from, uint4* __restrict__ to,
+                                                        const int32_t* __restrict__ src,
+                                                        const int32_t* __restrict__ dst, int n, int units,
+                                                        int64_t n_fpages, int64_t n_qpages) {
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (int64_t)n * units) return;
+    const int i = (int)(idx / units), u = (int)(idx % units);
+    const int s = src[i], d = dst[i];
+    if (s < 0 || (int64_t)s >= n_fpages || d < 0 || (int64_t)d >= n_qpages) return;
+    to[(int64_t)d * units + u] = from[(int64_t)s * units + u];
+}
+
+hipError_t launch_rope_copy(const QuantizeArgs& a, hipStream_t st) {
+    const int units = a.T * a.R * 2 / 16;  // 16-byte units of a page's rope keys
+    const int64_t total = (int64_t)a.n * units;
+    const int64_t blocks = (total + 255) / 256;
+    if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(rope_copy_kernel, dim3((unsigned)blocks), dim3(256), 0, st,
+                       static_cast<const uint4*>(a.rope_fp16), static_cast<uint4*>(a.rope_records), a.src, a.dst,
+                       a.n, units, a.n_fpages, a.n_qpages);
+    return hipGetLastError();
+}
+
 template <int D, int T>
 hipError_t by_bits(const QuantizeArgs& a, hipStream_t st) {
     if (!a.mla && !(even_width(a.k_bits) && even_width(a.v_bits))) {
@@ -54,13 +80,15 @@ hipError_t by_bits(const QuantizeArgs& a, hipStream_t st) {
 
 hipError_t launch_quantize(const QuantizeArgs& a, hipStream_t st) {
     if (a.n == 0) return hipSuccess;
-    if (a.D == 128 && a.T == 128) return by_bits<128, 128>(a, st);
-    if (a.D == 128 && a.T == 64) return by_bits<128, 64>(a, st);
-    if (a.D == 256 && a.T == 128) return by_bits<256, 128>(a, st);
-    if (a.D == 256 && a.T == 64) return by_bits<256, 64>(a, st);
-    if (a.D == 512 && a.T == 128) return by_bits<512, 128>(a, st);
-    if (a.D == 512 && a.T == 64) return by_bits<512, 64>(a, st);
-    return hipErrorInvalidValue;
+    hipError_t e = hipErrorInvalidValue;
+    if (a.D == 128 && a.T == 128) e = by_bits<128, 128>(a, st);
+    else if (a.D == 128 && a.T == 64) e = by_bits<128, 64>(a, st);
+    else if (a.D == 256 && a.T == 128) e = by_bits<256, 128>(a, st);
+    else if (a.D == 256 && a.T == 64) e = by_bits<256, 64>(a, st);
+    else if (a.D == 512 && a.T == 128) e = by_bits<512, 128>(a, st);
+    else if (a.D == 512 && a.T == 64) e = by_bits<512, 64>(a, st);
+    if (e != hipSuccess || a.R == 0) return e;
+    return launch_rope_copy(a, st);
 }
 
 }  // namespace kvarn

@@ -142,3 +142,34 @@ def test_decode_rejects_before_any_device_work():
                                  kv.KVARN_F32, 32, ctypes.c_float(0.1), ctypes.c_void_p(16), ctypes.c_void_p(256),
                                  1 << 40, None) == kv.KVARN_EUNSUPPORTED
     assert "32767" in lib.kvarn_last_error().decode()
+
+
+def test_rope_sidecar_gates():
+    # a 64-wide rope key beside an MLA latent, or none
+    M = kv.make_layout(512, 128, 4, 4, num_kv_heads=1, mla=1, rope_dim=64)
+    assert kv.layout_check(M) == kv.KVARN_OK
+    assert kv.record_bytes(M, 0) == 128 * 512 // 2 + 4 * 128 + 2 * 512   # the record itself is unchanged
+    assert kv.layout_check(kv.make_layout(512, 128, 4, 4, num_kv_heads=1, mla=1, rope_dim=32)) == kv.KVARN_EUNSUPPORTED
+    assert kv.layout_check(kv.make_layout(128, 128, 4, 2, num_kv_heads=8, rope_dim=64)) == kv.KVARN_EINVAL
+    lib = kv.lib()
+    pt = kv.PageTable(ctypes.c_void_p(16), ctypes.c_void_p(16), 2, 4)
+    need = kv.decode_workspace_bytes(M, 2, 16, 4)
+    assert need > 0
+
+    def decode(cache):
+        return lib.kvarn_decode_attn(ctypes.byref(M), ctypes.byref(cache), ctypes.byref(pt), ctypes.c_void_p(16),
+                                     kv.KVARN_BF16, 16, ctypes.c_float(0.1), ctypes.c_void_p(16),
+                                     ctypes.c_void_p(256), need, None)
+
+    p = ctypes.c_void_p(16)
+    assert decode(kv.Cache(p, None, p, None, 1, 1, None, p)) == kv.KVARN_EINVAL        # record-side pool missing
+    assert decode(kv.Cache(p, None, p, None, 1, 1, p, None)) == kv.KVARN_EINVAL        # fp16-side pool missing
+    assert decode(kv.Cache(p, None, p, None, 1, 1, p, ctypes.c_void_p(24))) == kv.KVARN_EINVAL  # misaligned
+    huge = kv.Cache(p, None, p, None, 1, (1 << 32) // (128 * 128) + 1, p, p)           # rope pool of 4 GiB
+    assert decode(huge) == kv.KVARN_EUNSUPPORTED
+    st = lib.kvarn_quantize(ctypes.byref(M), ctypes.byref(kv.Cache(p, None, p, None, 1, 1, None, p)), p, p, 1, None)
+    assert st == kv.KVARN_EINVAL
+    st = lib.kvarn_append(ctypes.byref(M), ctypes.byref(kv.Cache(p, None, p, None, 1, 1, p, None)), ctypes.byref(pt),
+                          p, None, kv.KVARN_F16, 1, None)
+    assert st == kv.KVARN_EINVAL
+    assert "rope" in lib.kvarn_last_error().decode()
