@@ -32,6 +32,7 @@
 
 #include <utility>
 
+#include "decode_combine.hpp"
 #include "kvarn_device.hpp"
 #include "kvarn_internal.hpp"
 
@@ -1218,68 +1219,9 @@ __global__ void __launch_bounds__(D / 2) qrot_kernel(const void* __restrict__ q,
     for (int j = k; j < D; j += D / 2) qr[(int64_t)bh * D + j] = x[j] * rs;
 }
 
-// One workgroup per (sequence, query head): merge the partials (the first
-// nq of them are quantized-page splits with rotated-basis value sums, the
-// rest fp16 slots with original-basis ones), rotate the record part back
-// once, add the fp16 part, normalize.  CG groups of D threads take every
-// CG-th partial, so each thread has few loads in a row, and meet in LDS.
 template <int D>
-constexpr int combine_groups() { return D <= 256 ? 4 : 2; }
-template <int D>
-__global__ void __launch_bounds__(D * combine_groups<D>()) decode_combine_kernel(const float* __restrict__ ws,
-                                                                                  float* __restrict__ out, int nq,
-                                                                                  int nsplit) {
-    constexpr int WS = D + 4;           // partial: m, l, pad, pad, value sums
-    constexpr int CG = combine_groups<D>();
-    __shared__ float x[D];
-    __shared__ float part[CG][2 * D + 2];
-    const int bh = blockIdx.x;
-    const int j = threadIdx.x % D, grp = threadIdx.x / D;
-    const float* base = ws + (int64_t)bh * nsplit * WS;
-    float M = -INFINITY;
-#pragma unroll 4
-    for (int s = grp; s < nsplit; s += CG) M = fmaxf(M, base[s * WS]);
-    if (j == 0) part[grp][2 * D] = M;
-    __syncthreads();
-#pragma unroll
-    for (int g = 0; g < CG; g++) M = fmaxf(M, part[g][2 * D]);
-    float Ls = 0.f, r = 0.f, pl = 0.f;
-    if (M != -INFINITY) {
-#pragma unroll 4
-        for (int s = grp; s < nsplit; s += CG) {
-            const float ms = base[s * WS];
-            const float e = ms == -INFINITY ? 0.f : exp2f(ms - M);  // empty splits hold zeros
-            Ls = fmaf(base[s * WS + 1], e, Ls);
-            const float v = base[s * WS + 4 + j] * e;
-            if (s < nq) r += v;
-            else pl += v;
-        }
-    }
-    __syncthreads();  // every group has read the maxima
-    part[grp][j] = r;
-    part[grp][D + j] = pl;
-    if (j == 0) part[grp][2 * D + 1] = Ls;
-    __syncthreads();
-    r = pl = Ls = 0.f;
-#pragma unroll
-    for (int g = 0; g < CG; g++) {
-        r += part[g][j];
-        pl += part[g][D + j];
-        Ls += part[g][2 * D + 1];
-    }
-    if (grp == 0) x[j] = r;
-    __syncthreads();
-    for (int hs = 1; hs < D; hs <<= 1) {
-        const float v = x[j];
-        const float pv = x[j ^ hs];
-        __syncthreads();
-        if (grp == 0) x[j] = (j & hs) ? (pv - v) : (v + pv);
-        __syncthreads();
-    }
-    if (grp == 0) {
-        const float o = Ls > 0.f ? (x[j] * (1.0f / sqrtf((float)D)) + pl) / Ls : 0.f;
-        out[(int64_t)bh * D + j] = o;
-    }
+hipError_t launch_combine(const DecodeArgs& a, hipStream_t st) {
+    return launch_split_merge<D>(a.ws + (int64_t)a.B * a.Hq * D, a.out, a.B * a.Hq, a.nsplit, a.nsplit + a.nfsplit, st);
 }
 
 // Grid x of a split launch.  With several query rows per sequence (M > 1)
@@ -1314,9 +1256,7 @@ hipError_t launch_gqa(const DecodeArgs& a, hipStream_t st) {
         hipLaunchKernelGGL((decode_split_kernel<D, T, KB, VB>), grid, dim3(64 * NWV), 0, st, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(a.B * a.Hq), dim3(combine_groups<D>() * D), 0, st,
-                       a.ws + (int64_t)a.B * a.Hq * D, a.out, a.nsplit, a.nsplit + a.nfsplit);
-    return hipGetLastError();
+    return launch_combine<D>(a, st);
 }
 
 }  // namespace

@@ -21,9 +21,7 @@ hipError_t launch_gqa_wide(const DecodeArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((decode_split_kernel<D, T, KB, VB>), grid, dim3(64 * NWV), 0, st, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(a.B * a.Hq), dim3(combine_groups<D>() * D), 0, st,
-                       a.ws + (int64_t)a.B * a.Hq * D, a.out, a.nsplit, a.nsplit + a.nfsplit);
-    return hipGetLastError();
+    return launch_combine<D>(a, st);
 }
 
 // every (K, V) width pair with a width of 3, 5 or 8, for tiles of T tokens

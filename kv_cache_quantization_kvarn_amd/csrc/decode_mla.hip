@@ -24,6 +24,7 @@
 // columns of halves transposed per 16 lanes).
 #include <math.h>
 
+#include "decode_combine.hpp"
 #include "kvarn_device.hpp"
 #include "kvarn_internal.hpp"
 
@@ -706,50 +707,6 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
     write_partial(a.nsplit + split, true);
 }
 
-// merge the splits of one (sequence, head), rotate back once, normalize
-__global__ void __launch_bounds__(256) mla_combine_kernel(const float* __restrict__ wsp, float* __restrict__ out, int nsplit) {
-    constexpr int WS = MD + 4;
-    __shared__ float x[MD];
-    const int bh = blockIdx.x;
-    const int np = 2 * nsplit;  // partials s < nsplit: rotated basis; s >= nsplit: original basis
-    const float* base = wsp + (int64_t)bh * np * WS;
-    float M = -INFINITY;
-    for (int s = 0; s < np; s++) M = fmaxf(M, base[s * WS]);
-    float Ls = 0.f, r0 = 0.f, r1 = 0.f, p0 = 0.f, p1 = 0.f;
-    const int j0 = threadIdx.x, j1 = threadIdx.x + 256;
-    if (M != -INFINITY) {
-        for (int s = 0; s < np; s++) {
-            const float ms = base[s * WS];
-            if (ms == -INFINITY) continue;
-            const float e = exp2f(ms - M);
-            Ls = fmaf(base[s * WS + 1], e, Ls);
-            if (s < nsplit) {
-                r0 = fmaf(base[s * WS + 4 + j0], e, r0);
-                r1 = fmaf(base[s * WS + 4 + j1], e, r1);
-            } else {
-                p0 = fmaf(base[s * WS + 4 + j0], e, p0);
-                p1 = fmaf(base[s * WS + 4 + j1], e, p1);
-            }
-        }
-    }
-    x[j0] = r0;
-    x[j1] = r1;
-    __syncthreads();
-    for (int hs = 1; hs < MD; hs <<= 1) {
-        const int k = threadIdx.x;
-        const int i0 = (k / hs) * 2 * hs + (k % hs), i1 = i0 + hs;
-        const float u = x[i0], v = x[i1];
-        __syncthreads();
-        x[i0] = u + v;
-        x[i1] = u - v;
-        __syncthreads();
-    }
-    const float il = Ls > 0.f ? 1.0f / Ls : 0.f;
-    const float sc = il / sqrtf((float)MD);
-    out[(int64_t)bh * MD + j0] = fmaf(x[j0], sc, p0 * il);
-    out[(int64_t)bh * MD + j1] = fmaf(x[j1], sc, p1 * il);
-}
-
 template <int T, int HB>
 hipError_t launch_mla_t(const DecodeArgs& a, hipStream_t st) {
     if (a.R != 0 && a.R != 64) return hipErrorInvalidValue;
@@ -764,9 +721,9 @@ hipError_t launch_mla_t(const DecodeArgs& a, hipStream_t st) {
     else hipLaunchKernelGGL((mla_split_kernel<T, HB, false>), dim3(blocks), dim3(MlaShape<HB>::NT), 0, st, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
+    // partials s < nsplit: quantized chunks, rotated basis; s >= nsplit: fp16 chunks, original basis
     const float* wsp = a.ws + (int64_t)a.B * a.Hq * MD / 2;
-    hipLaunchKernelGGL(mla_combine_kernel, dim3(a.B * a.Hq), dim3(256), 0, st, wsp, a.out, a.nsplit);
-    return hipGetLastError();
+    return launch_split_merge<MD>(wsp, a.out, a.B * a.Hq, a.nsplit, 2 * a.nsplit, st);
 }
 
 template <int T>
