@@ -28,7 +28,10 @@ Reported (one JSON line):
              quantize under both byte readings (fp16 consumed; fp16 read +
              records written) and decode, each as GB/s and fraction of HBM
              peak, median with p10 / p90 of the per-call times; the MLA decode
-             also as a fraction of the fp16 MFMA peak (its roofline).
+             also as a fraction of the fp16 MFMA peak (its roofline), and
+             once more with a 64-wide fp16 rope key beside every latent
+             (decode_rope64: the same cache plus its rope pools and 576-wide
+             queries; bytes and flops include the rope part).
              The headline workload also times a verify step (decode of 4
              uncommitted query tokens per sequence, causal among themselves).
   cpu_baseline the oracle (plain C, fp64, OpenMP) on a bounded sample of the
@@ -273,6 +276,46 @@ class Runner:
                 "note": "verify step: M uncommitted query tokens per sequence, causal among themselves, one read of "
                         "the cache; bytes = cache + q + out"}
 
+    def time_rope(self, steps, warmup, flush, R=64):
+        """MLA decode of the same cache with an R-wide fp16 rope key beside
+        every latent: seeded rope pools (the quantize call copies each
+        quantized page's rope keys to its record page) and queries of
+        D + R channels."""
+        torch, kv, c = self.torch, self.kv, self.case
+        from synth import QROPE_STREAM, ROPE_STREAM, normal, to_f16
+
+        lay = c["layout"]
+        T, D, B, Hq = lay["T"], lay["D"], c["B"], c["Hq"]
+        dev = c["q"].device
+        Lr = kv.layout_from_dict(dict(lay, rope=R))
+        rope16 = to_f16(normal(self.w["seed"], ROPE_STREAM, c["n_fpages"] * T * R, device=dev)).view(-1, T, R)
+        rrec = torch.empty((max(c["n_qpages"], 1), T, R), dtype=torch.float16, device=dev)
+        kv.quantize(Lr, c["k16"], None, self.krec, None, c["src"], c["dst"], rope_fp16=rope16, rope_records=rrec)
+        qr = normal(self.w["seed"], QROPE_STREAM, B * Hq * R, device=dev).view(B, Hq, R).to(c["q"].dtype)
+        q = torch.cat([c["q"], qr], dim=2).contiguous()
+        sm = 1.0 / math.sqrt(D + R)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ts = []
+        for i in range(warmup + steps):
+            flush()
+            e0.record()
+            kv.decode_attn(Lr, self.krec, None, c["k16"], None, c["block_table"], c["seq_lens"], q, sm, out=self.out,
+                           workspace=self.ws, rope_records=rrec, rope_fp16=rope16)
+            e1.record()
+            torch.cuda.synchronize()
+            if i >= warmup:
+                ts.append(e0.elapsed_time(e1) * 1e-3)
+        st = stats(ts)
+        _, _, dec, flops = self.bytes
+        ntok = sum(c["seq_lens"].cpu().tolist())
+        byts = dec + ntok * R * 2 + B * Hq * R * q.element_size()
+        fl = flops + 2 * Hq * R * ntok   # one multiply-add per query head, rope channel and token (scores)
+        tf = fl / st["median"] / 1e6
+        return {"rope_dim": R, "us": round(st["median"], 2), "us_p10": round(st["p10"], 2),
+                "us_p90": round(st["p90"], 2), "bytes": byts, "flops": fl, "bound": "mfma",
+                "TFLOPs": round(tf, 1), "mfma_frac": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
+                "GBs": round(byts / st["median"] / 1e3, 1), "frac": round(byts / st["median"] / 1e3 / HBM_PEAK_GBS, 4)}
+
     def free(self):
         del self.case, self.krec, self.vrec, self.out, self.ws
         for k in ("v_bt", "v_lens", "v_q", "v_out", "v_ws"):
@@ -379,6 +422,9 @@ def main():
             r = Runner(name, dev)
             tq, td = r.time_steps(args.component_steps, args.component_warmup, flush)
             res["components"][name] = r.component(tq, td)
+            if r.case["layout"]["mla"]:
+                res["components"][name]["decode_rope64"] = r.time_rope(args.component_steps, args.component_warmup,
+                                                                       flush)
             r.free()
             print(f"[bench] component {name} done", file=sys.stderr, flush=True)
     print(json.dumps(res), flush=True)

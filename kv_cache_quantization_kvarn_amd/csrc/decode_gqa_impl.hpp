@@ -976,10 +976,11 @@ __global__ void __launch_bounds__(64) decode_split128_kernel(DecodeArgs a) {
     const i4v rsk = raw_buffer(krec, (uint32_t)(a.n_qpages * a.H * KREC));
     const i4v rsv = raw_buffer(vrec, (uint32_t)(a.n_qpages * a.H * VREC));
     // key piece u (16 bytes; u = KB t + p for token t of the step) sits at
-    // stage piece kswz(u): for KB = 4 the 4 pieces of a row rotate with bits
-    // 1-2 of the token, so that 8 lanes reading one piece of 8 consecutive
-    // tokens hit 8 different bank groups (kswz is an involution)
-    auto kswz = [](int u) { return KB == 4 ? (u ^ ((u >> 3) & 3)) : u; };
+    // stage piece kswz(u): for KB = 2 and 4 the KB pieces of a row rotate
+    // with bits 2-3 (KB = 4) or bit 3 (KB = 2) of the token, so that the 16
+    // lanes of a 128-bit read pass (one piece of 16 consecutive tokens) hit 16
+    // different 4-bank groups of the 64-bank LDS (kswz is an involution)
+    auto kswz = [](int u) { return (KB == 4 || KB == 2) ? (u ^ ((u >> 4) & (KB - 1))) : u; };
     const uint32_t sb = lds_address(stage);
     // all of a step's loads into the stage
     auto issue = [&](const StepRef& r) {

@@ -18,7 +18,7 @@
  *      fourth paragraph: MLA latent quantized to int4.
  *  [G] gmlx documentation "KV cache quantization", section "The two schemes":
  *      each head rotated with a Hadamard transform; records of 128 tokens
- *      scaled so no token or channel dominates; first 128 tokens and the
+ *      whose token and channel spreads are evened out; first 128 tokens and the
  *      newest --kv-tail-tokens tokens (default 1024) stay fp16; widths
  *      2,3,4,5,6,8.  Section "Which layers quantize": head dims 128/256/512.
  *
