@@ -518,34 +518,56 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
         const h2 S2 = __builtin_bit_cast(h2, (szw & 0xffffu) * 0x10001u);
         const h2 Z2 = __builtin_bit_cast(h2, (szw >> 16) * 0x10001u);
         const h2 k1024 = h2{(_Float16)1024.0f, (_Float16)1024.0f};
-        auto unit = [&](int q8, const uint4 cv) {  // cv: column scales of the unit, pair order
-            const uint32_t cs[4] = {cv.x, cv.y, cv.z, cv.w};
-            const uint32_t w = cw[q8];
-            uint32_t o[4];
+        // the nibble mask and the exponent of 1024 in registers (an SGPR and a
+        // VGPR), so that the and and the or fuse into one v_and_or_b32
+        const uint32_t nmask = (uint32_t)__builtin_amdgcn_readfirstlane(0x000F000F + zk);
+        uint32_t e1024 = 0x64006400u;
+        asm volatile("" : "+v"(e1024));
+        // the 32 pairs of a unit row stage by stage, so that their chains
+        // interleave: codes as (1024 + c) pairs, then S c + Zp, then times C
+        auto units = [&](const uint4 (&cvs)[8]) {
+            h2 y[8][4];
 #pragma unroll
-            for (int k = 0; k < 4; k++) {
-                const h2 c = __builtin_bit_cast(h2, ((w >> (4 * k)) & 0x000F000Fu) | 0x64006400u) - k1024;
-                const h2 y = __builtin_elementwise_fma(c, S2, Z2) * __builtin_bit_cast(h2, cs[k]);
-                o[k] = __builtin_bit_cast(uint32_t, y);
+            for (int q8 = 0; q8 < 8; q8++)
+#pragma unroll
+                for (int k = 0; k < 4; k++)
+                    y[q8][k] = __builtin_bit_cast(h2, ((cw[q8] >> (4 * k)) & nmask) | e1024) - k1024;
+#pragma unroll
+            for (int q8 = 0; q8 < 8; q8++)
+#pragma unroll
+                for (int k = 0; k < 4; k++) y[q8][k] = __builtin_elementwise_fma(y[q8][k], S2, Z2);
+#pragma unroll
+            for (int q8 = 0; q8 < 8; q8++) {
+                const uint32_t cs[4] = {cvs[q8].x, cvs[q8].y, cvs[q8].z, cvs[q8].w};
+                uint32_t o[4];
+#pragma unroll
+                for (int k = 0; k < 4; k++) o[k] = __builtin_bit_cast(uint32_t, y[q8][k] * __builtin_bit_cast(h2, cs[k]));
+                // yoff(tt, 8 part + q8) = 16 (part >> 1) + (rk ^ q8) into the row
+                *reinterpret_cast<uint4*>(yb + tt * YROW + 256 * (part >> 1) + 16 * ((rk ^ zk) ^ q8)) =
+                    make_uint4(o[0], o[1], o[2], o[3]);
             }
-            // yoff(tt, 8 part + q8) = 16 (part >> 1) + (rk ^ q8) into the row
-            *reinterpret_cast<uint4*>(yb + tt * YROW + 256 * (part >> 1) + 16 * ((rk ^ zk) ^ q8)) = make_uint4(o[0], o[1], o[2], o[3]);
         };
+        // every unit's column scales are read before the first store: the
+        // compiler cannot tell the stores to yb from these reads apart, and
+        // would otherwise wait for each unit's store before the next read
+        uint4 cvs[8];
         if (c0 == 0) {  // uniform: the page's first chunk brings its column scales
-            uint4 keep = make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
             for (int q8 = 0; q8 < 8; q8++) {
                 const uint4 c = cpg[8 * part + ((part ^ zk) ^ q8)];  // pairs (0,4) (1,5) (2,6) (3,7) of unit 8 part + q8
-                const uint4 cv = make_uint4(__builtin_amdgcn_perm(c.z, c.x, 0x05040100u), __builtin_amdgcn_perm(c.z, c.x, 0x07060302u),
-                                            __builtin_amdgcn_perm(c.w, c.y, 0x05040100u), __builtin_amdgcn_perm(c.w, c.y, 0x07060302u));
-                if (q8 == (tt & 7)) keep = cv;
-                unit(q8, cv);
+                cvs[q8] = make_uint4(__builtin_amdgcn_perm(c.z, c.x, 0x05040100u), __builtin_amdgcn_perm(c.z, c.x, 0x07060302u),
+                                     __builtin_amdgcn_perm(c.w, c.y, 0x05040100u), __builtin_amdgcn_perm(c.w, c.y, 0x07060302u));
             }
+            uint4 keep = cvs[0];
+#pragma unroll
+            for (int q8 = 1; q8 < 8; q8++)
+                if (q8 == (tt & 7)) keep = cvs[q8];
             if (tt < 8) cb[(8 * part + tt) ^ part] = keep;  // staged once per unit for the page's later chunks (same swizzle)
         } else {
 #pragma unroll
-            for (int q8 = 0; q8 < 8; q8++) unit(q8, cb[8 * part + ((part ^ zk) ^ q8)]);
+            for (int q8 = 0; q8 < 8; q8++) cvs[q8] = cb[8 * part + ((part ^ zk) ^ q8)];
         }
+        units(cvs);
     };
     auto chunk_ok = [&](int ci) {
         int page, c0, id;
@@ -570,22 +592,33 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
     // iteration ci: issue chunk ci + NR - 1 into the slot chunk ci - 1 used;
     // score chunk ci while chunk ci + 1 is read back, then the value sums of
     // chunk ci - 1 (iteration nqc only forms those of the last chunk)
-    for (int ci = 0; ci <= nqc; ci++) {
+    // The loop runs in two copies with the same loads and barriers, one for
+    // the score waves and one for the others: the score waves' query operands
+    // (qa, qro) are dead in the second, which leaves the read-back the
+    // registers to keep its loads and unit chains in flight together.
+    auto head = [&](int ci) {
         issue_rope(ci + 1);
         issue_chunk(ci + NR - 1);
         asm volatile("s_waitcnt vmcnt(%0)" ::"n"(VMW) : "memory");  // chunk ci + 1 (and rope ci) have landed
         __syncthreads();
         zk = opaque_zero();
-        if (ci < nqc) {
-            if (qk_wave) {
+    };
+    if (qk_wave) {
+        for (int ci = 0; ci <= nqc; ci++) {
+            head(ci);
+            if (ci < nqc) {
                 int page, c0, id;
                 qchunk(ci, page, c0, id);
                 if (id >= 0) score(ybuf[ci % 3], rbuf[ROPE ? ci % 3 : 0], page * T + c0, ci);
-            } else if (rb_wave && ci + 1 < nqc) {
-                read_back(ci + 1);
             }
+            if (ci > 0 && chunk_ok(ci - 1)) accumulate(ybuf[(ci - 1) % 3], ci - 1);
         }
-        if (ci > 0 && chunk_ok(ci - 1)) accumulate(ybuf[(ci - 1) % 3], ci - 1);
+    } else {
+        for (int ci = 0; ci <= nqc; ci++) {
+            head(ci);
+            if (rb_wave && ci + 1 < nqc) read_back(ci + 1);
+            if (ci > 0 && chunk_ok(ci - 1)) accumulate(ybuf[(ci - 1) % 3], ci - 1);
+        }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no load may land in LDS after this point
     __syncthreads();
@@ -634,7 +667,11 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
     for (int hb = 0; hb < HB; hb++)
 #pragma unroll
         for (int c = 0; c < CBW; c++) O[hb][c] = f4{0.f, 0.f, 0.f, 0.f};
-    if (qk_wave && nfp > 0) {  // the plain query of this wave's head block, natural channel order
+    // the plain query of this wave's head block, natural channel order (set in
+    // every wave, so that no earlier value of qa lives through the loop above)
+#pragma unroll
+    for (int ks = 0; ks < 16; ks++) qa[ks] = h8{0, 0, 0, 0, 0, 0, 0, 0};
+    if (qk_wave && nfp > 0) {
         const int64_t qi = ((int64_t)b * a.Hq + h0 + wave * 16 + l16) * (MD + RD) + 8 * g4;
 #pragma unroll
         for (int ks = 0; ks < 16; ks++) {
