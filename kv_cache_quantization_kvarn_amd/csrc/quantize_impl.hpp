@@ -52,43 +52,38 @@ __device__ __forceinline__ float xsum(float v) {
     else return v + xor_lane<BIT>(v);
 }
 
-template <int CGB>
-__device__ __forceinline__ float row_sum(float v) {
-    v = xsum<0>(v);
-    v = xsum<1>(v);
-    v = xsum<3>(v);
-    if constexpr (CGB >= 4) v = xsum<2>(v);
-    if constexpr (CGB >= 5) v = xsum<4>(v);
-    return v;
+// Row k = 2 b0 + b1 of this lane's quad (b0, b1: lane bits 0 and 1) from
+// the per-lane values v[0..3] of the lane's 4 rows: the value of row k sits
+// in quad lane b0 + 2 b1, so rows 0..3 come from quad lanes 0, 2, 1, 3.
+__device__ __forceinline__ void quad_bcast_rows(float v, float (&out)[4]) {
+    out[0] = i2f(__builtin_amdgcn_mov_dpp(f2i(v), 0x00, 0xF, 0xF, false));
+    out[1] = i2f(__builtin_amdgcn_mov_dpp(f2i(v), 0xAA, 0xF, 0xF, false));
+    out[2] = i2f(__builtin_amdgcn_mov_dpp(f2i(v), 0x55, 0xF, 0xF, false));
+    out[3] = i2f(__builtin_amdgcn_mov_dpp(f2i(v), 0xFF, 0xF, 0xF, false));
 }
 
-// min and max of each of the lane's 4 rows over the D/16 lanes of a token
-// row.  Lane bits 0, 1 and 3 take one fused v_min/v_max_f32_dpp each (the
-// register is its own DPP source; s_nop 1 covers the VALU-write-then-DPP-read
-// wait states); bits 2 and 4 go through ds_swizzle.
-#define KVARN_MINMAX_DPP8(CTRL)                                                                 \
-    asm volatile("s_nop 1\n\t"                                                                   \
-                 "v_min_f32_dpp %0, %0, %0 " CTRL " row_mask:0xf bank_mask:0xf\n\t"             \
-                 "v_max_f32_dpp %4, %4, %4 " CTRL " row_mask:0xf bank_mask:0xf\n\t"             \
-                 "v_min_f32_dpp %1, %1, %1 " CTRL " row_mask:0xf bank_mask:0xf\n\t"             \
-                 "v_max_f32_dpp %5, %5, %5 " CTRL " row_mask:0xf bank_mask:0xf\n\t"             \
-                 "v_min_f32_dpp %2, %2, %2 " CTRL " row_mask:0xf bank_mask:0xf\n\t"             \
-                 "v_max_f32_dpp %6, %6, %6 " CTRL " row_mask:0xf bank_mask:0xf\n\t"             \
-                 "v_min_f32_dpp %3, %3, %3 " CTRL " row_mask:0xf bank_mask:0xf\n\t"             \
-                 "v_max_f32_dpp %7, %7, %7 " CTRL " row_mask:0xf bank_mask:0xf"                 \
-                 : "+v"(mn[0]), "+v"(mn[1]), "+v"(mn[2]), "+v"(mn[3]), "+v"(mx[0]), "+v"(mx[1]),   \
-                   "+v"(mx[2]), "+v"(mx[3]))
-
+// Minimum and maximum over the D/16 lanes of a token row, reduce-scattered:
+// over lane bits 0 and 1 each lane keeps one of its quad's rows (row
+// 2 b0 + b1) and passes the other on, then the remaining channel-group bits
+// combine that row (bit 3 by DPP, bits 2 and 4 by ds_swizzle).
 template <int CGB>
-__device__ __forceinline__ void row_minmax4(float (&mn)[4], float (&mx)[4]) {
-    KVARN_MINMAX_DPP8("quad_perm:[1,0,3,2]");
-    KVARN_MINMAX_DPP8("quad_perm:[2,3,0,1]");
-    KVARN_MINMAX_DPP8("row_ror:8");
-#pragma unroll
-    for (int r = 0; r < 4; r++) {
-        if constexpr (CGB >= 4) { mn[r] = fminf(mn[r], xor_lane<2>(mn[r])); mx[r] = fmaxf(mx[r], xor_lane<2>(mx[r])); }
-        if constexpr (CGB >= 5) { mn[r] = fminf(mn[r], xor_lane<4>(mn[r])); mx[r] = fmaxf(mx[r], xor_lane<4>(mx[r])); }
-    }
+__device__ __forceinline__ void row_minmax_scatter(const float (&mn)[4], const float (&mx)[4], bool b0, bool b1,
+                                                   float& mnk, float& mxk) {
+    auto x1 = [](float v) { return i2f(__builtin_amdgcn_update_dpp(0, f2i(v), 0xB1, 0xF, 0xF, true)); };
+    auto x2 = [](float v) { return i2f(__builtin_amdgcn_update_dpp(0, f2i(v), 0x4E, 0xF, 0xF, true)); };
+    auto x8 = [](float v) { return i2f(__builtin_amdgcn_update_dpp(0, f2i(v), 0x128, 0xF, 0xF, true)); };
+    const float n02 = fminf(b0 ? mn[2] : mn[0], x1(b0 ? mn[0] : mn[2]));
+    const float n13 = fminf(b0 ? mn[3] : mn[1], x1(b0 ? mn[1] : mn[3]));
+    const float m02 = fmaxf(b0 ? mx[2] : mx[0], x1(b0 ? mx[0] : mx[2]));
+    const float m13 = fmaxf(b0 ? mx[3] : mx[1], x1(b0 ? mx[1] : mx[3]));
+    float n = fminf(b1 ? n13 : n02, x2(b1 ? n02 : n13));
+    float m = fmaxf(b1 ? m13 : m02, x2(b1 ? m02 : m13));
+    n = fminf(n, x8(n));
+    m = fmaxf(m, x8(m));
+    if constexpr (CGB >= 4) { n = fminf(n, xor_lane<2>(n)); m = fmaxf(m, xor_lane<2>(m)); }
+    if constexpr (CGB >= 5) { n = fminf(n, xor_lane<4>(n)); m = fmaxf(m, xor_lane<4>(m)); }
+    mnk = n;
+    mxk = m;
 }
 
 // Cross-lane butterfly on lane bit BIT for 16 values: v <- v + s * partner,
@@ -530,6 +525,8 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ tile,
     // step is a bare reciprocal; the column step's T / D restores b.
     constexpr float kInvD = 1.0f / (float)D;
     float aw[QR] = {kInvD, kInvD, kInvD, kInvD};
+    float my_a = kInvD;  // a / D of this lane's row in the row step's reduce-scatter
+    const bool rb0 = lane & 1, rb1 = (lane >> 1) & 1;
     float bw[QC];
     for (int it = 0; it < n_iters; it++) {
         const bool last = it == n_iters - 1;
@@ -607,6 +604,7 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ tile,
             bw[4 * c4 + 3] = v.w;
         }
         // row step
+        float rs[QR];
 #pragma unroll
         for (int r = 0; r < QR; r++) {
             float s;
@@ -619,10 +617,24 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ tile,
 #pragma unroll
                 for (int c = 1; c < QC; c++) s = fma_abs(A[r][c], bw[c], s);
             }
-            s = row_sum<CGB>(s);
-            const float rc = __builtin_amdgcn_rcpf(s);
-            aw[r] = usable(s) ? rc : aw[r];
+            rs[r] = s;
         }
+        // Reduce-scatter over lane bits 0 and 1: lane (b0, b1) of a quad ends
+        // with row 2 b0 + b1 summed over its quad, then over the remaining
+        // channel-group bits; one reciprocal a lane, the four rows broadcast
+        // back from their quad lanes.  Every add pairs the same two operands
+        // as an all-reduce of each row would, so the sums are the same.
+        const float r02 = rb0 ? rs[2] : rs[0], x02 = rb0 ? rs[0] : rs[2];
+        const float r13 = rb0 ? rs[3] : rs[1], x13 = rb0 ? rs[1] : rs[3];
+        const float t02 = r02 + i2f(__builtin_amdgcn_update_dpp(0, f2i(x02), 0xB1, 0xF, 0xF, true));
+        const float t13 = r13 + i2f(__builtin_amdgcn_update_dpp(0, f2i(x13), 0xB1, 0xF, 0xF, true));
+        const float tk = rb1 ? t13 : t02, tx = rb1 ? t02 : t13;
+        float u = tk + i2f(__builtin_amdgcn_update_dpp(0, f2i(tx), 0x4E, 0xF, 0xF, true));
+        u = xsum<3>(u);
+        if constexpr (CGB >= 4) u = xsum<2>(u);
+        if constexpr (CGB >= 5) u = xsum<4>(u);
+        my_a = usable(u) ? __builtin_amdgcn_rcpf(u) : my_a;
+        quad_bcast_rows(my_a, aw);
     }
 
     // ---- stage 4: per-token asymmetric round-to-nearest, packed in LDS ------
@@ -640,7 +652,7 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ tile,
     // [0, 255] and drops the byte into place; 6-bit codes: magic-number
     // rounding (x + 1.5 * 2^23 keeps rint(x) in the low mantissa bits).
     constexpr bool PKU8 = BITS != 6;
-    uint32_t sz[QR];
+    uint32_t szk;  // fp16 scale and zero-point of row 2 b0 + b1 (quad lane b0 + 2 b1)
     // W = y / c, then u = (W - mn) / s, then (6-bit) the magic-rounded code
     // bits, all in place in the array that held y (or y^2 for D = 512)
     float (&u)[QR][QC] = *[&]() -> float(*)[QR][QC] {
@@ -671,18 +683,23 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ tile,
                 mx[r] = fmaxf(mx[r], u[r][c]);
             }
         }
-        row_minmax4<CGB>(mn, mx);
+        // lane (b0, b1) of a quad ends with row 2 b0 + b1's minimum and maximum
+        float mnk, mxk;
+        row_minmax_scatter<CGB>(mn, mx, rb0, rb1, mnk, mxk);
+        const float m0 = mnk + 0.0f;  // a zero row stores +0, not the -0 of a sign-flipped channel
+        const float range = mxk - m0;
+        const float sc = range * (1.0f / (float)QMAX);
+        const float inv = range > 0.f ? (float)QMAX * __builtin_amdgcn_rcpf(range) : 0.f;
+        const float nb = -m0 * inv;
+        szk = float_to_half_bits(sc) | (float_to_half_bits(m0) << 16);
+        float invr[QR], nbr[QR];
+        quad_bcast_rows(inv, invr);
+        quad_bcast_rows(nb, nbr);
 #pragma unroll
         for (int r = 0; r < QR; r++) {
-            const float m0 = mn[r] + 0.0f;  // a zero row stores +0, not the -0 of a sign-flipped channel
-            const float range = mx[r] - m0;
-            const float sc = range * (1.0f / (float)QMAX);
-            const float inv = range > 0.f ? (float)QMAX * __builtin_amdgcn_rcpf(range) : 0.f;
-            const float nb = -m0 * inv;
-            sz[r] = float_to_half_bits(sc) | (float_to_half_bits(m0) << 16);
 #pragma unroll
             for (int c = 0; c < QC; c++) {
-                u[r][c] = fmaf(u[r][c], inv, nb);
+                u[r][c] = fmaf(u[r][c], invr[r], nbr[r]);
                 if constexpr (!PKU8) u[r][c] += kMagic;  // rint(u) in the low mantissa bits
             }
         }
@@ -795,9 +812,10 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ tile,
             }
         }
     }
-    // per-token scale and zero-point: 4 consecutive tokens = 16 bytes
-    if (cg == 0) {
-        *reinterpret_cast<uint4*>(rec + CODE_BYTES + 4 * row0) = make_uint4(sz[0], sz[1], sz[2], sz[3]);
+    // per-token scale and zero-point: the quad of channel groups 0..3 holds
+    // the row group's 4 tokens, one each
+    if (cg < 4) {
+        *reinterpret_cast<uint32_t*>(rec + CODE_BYTES + 4 * (row0 + 2 * (int)rb0 + (int)rb1)) = szk;
     }
     // column scales, normalized basis
     if (tid < D / 8) {
