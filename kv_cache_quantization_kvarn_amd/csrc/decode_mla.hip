@@ -276,14 +276,21 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
         return f < sp ? f : sp + nq + (f - sp);
     };
     // the split's page ids (128 at most), entry k in lane k & 63 of pid[k >> 6]:
-    // quantized pages first, then its fp16 pages
+    // quantized pages first, then its fp16 pages; an id outside its pool
+    // becomes -1 here, once, so the chunk loops test only the sign
     int pid[2];
 #pragma unroll
     for (int r = 0; r < 2; r++) {
         const int k = 64 * r + lane;
-        pid[r] = -1;
-        if (k < nqp) pid[r] = a.block_table[(int64_t)bs * a.max_pages + qbeg + k];
-        else if (k < nqp + nfp) pid[r] = a.block_table[(int64_t)bs * a.max_pages + fpage(k - nqp)];
+        int id = -1;
+        if (k < nqp) {
+            id = a.block_table[(int64_t)bs * a.max_pages + qbeg + k];
+            if ((int64_t)id >= a.n_qpages) id = -1;
+        } else if (k < nqp + nfp) {
+            id = a.block_table[(int64_t)bs * a.max_pages + fpage(k - nqp)];
+            if ((int64_t)id >= a.n_fpages) id = -1;
+        }
+        pid[r] = id < 0 ? -1 : id;
         asm volatile("" ::"v"(pid[r]));  // loaded before any LDS-DMA load is in flight
     }
     auto page_id = [&](int k) {  // k wave-uniform, < 128
@@ -433,17 +440,20 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
 
     // ---- quantized chunks: chunk ci is page qbeg + ci / CPP, tokens
     // (ci % CPP) * CH .. +CH.  A ring of NR chunk slots in LDS is filled by
-    // LDS-DMA loads: the codes (1 KB per wave), the token scales and, on a
-    // page's first chunk, the column scales.  Every wave issues exactly two
-    // such loads per chunk (a one-lane load into a scratch line stands in for
-    // a load it has no use for), so a fixed s_waitcnt vmcnt count marks a
-    // chunk as landed. ----
+    // LDS-DMA loads: the codes, the token scales and, on a page's first
+    // chunk, the column scales.  Waves 0..3 issue every load (2 KB of codes
+    // each, then wave 0 the token scales and wave 1 the column scales), the
+    // read-back waves none: their issue time would sit on the critical path,
+    // while waves 0..3 otherwise wait at the chunk barrier.  Each of waves
+    // 0..3 issues exactly three loads per chunk (a one-lane load into a
+    // scratch line stands in for a load it has no use for), so a fixed
+    // s_waitcnt vmcnt count before the barrier marks a chunk as landed for
+    // the whole workgroup. ----
     const int nqc = nqp * CPP;
     auto qchunk = [&](int ci, int& page, int& c0, int& id) {
         page = qbeg + ci / CPP;
         c0 = (ci % CPP) * CH;
         id = page_id(ci / CPP);
-        if (id < 0 || (int64_t)id >= a.n_qpages) id = -1;
     };
     const i32x4 rs = raw_buffer(a.k_records, (uint32_t)(a.n_qpages * KREC));
     const uint32_t ring_lds = lds_address(ring), dummy_lds = lds_address(scratch) + 16 * wave;
@@ -455,12 +465,14 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
         // byte offsets in the pool (below 4 GiB) as unsigned 32-bit values:
         // the buffer load adds its scalar offset modulo 2^32
         const uint32_t rec = q ? (uint32_t)id * (uint32_t)KREC : 0u;
-        if (q) {  // slot piece 64 w + l holds piece k ^ cswz(t) of token t's row (t = piece >> 4, k = piece & 15)
-            const int pc = 64 * wave + lane, t = pc >> 4;
-            lds_dma16(sl + 1024 * wave, rs, t * (MD / 2) + 16 * ((pc & 15) ^ cswz(t)),
-                      (int)(rec + (uint32_t)(c0 * (MD / 2))));
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+            // slot piece 64 p + l (p = 2 wave + h) holds piece k ^ cswz(t) of
+            // token t's row (t = piece >> 4, k = piece & 15)
+            const int p = 2 * wave + h, pc = 64 * p + lane, t = pc >> 4;
+            if (q) lds_dma16(sl + 1024 * p, rs, t * (MD / 2) + 16 * ((pc & 15) ^ cswz(t)), (int)(rec + (uint32_t)(c0 * (MD / 2))));
+            else if (lane == 0) lds_dma16(dummy_lds, rs, 0, 0);
         }
-        else if (lane == 0) lds_dma16(dummy_lds, rs, 0, 0);
         if (q && wave == 0) {
             if (lane < CH / 4) lds_dma16(sl + SSC, rs, 16 * lane, (int)(rec + (uint32_t)(KCB + 4 * c0)));
         } else if (q && wave == 1 && c0 == 0) {
@@ -470,21 +482,18 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
             lds_dma16(dummy_lds, rs, 0, 0);
         }
     };
-    // rope keys of quantized chunk cj -> rbuf[cj % 3]: wave w loads tokens
-    // 4 w .. 4 w + 3 (lanes 0..31, position l & 7 of token 4 w + (l >> 3));
-    // a one-lane stand-in load where there is nothing to load
+    // rope keys of quantized chunk cj -> rbuf[cj % 3]: wave w (0..3) loads
+    // tokens 8 w .. 8 w + 7 (position l & 7 of token 8 w + (l >> 3)); a
+    // one-lane stand-in load where there is nothing to load
     const i32x4 rrs = raw_buffer(a.rope_records, ROPE ? (uint32_t)(a.n_qpages * T * RROW) : 0u);
     auto issue_rope = [&](int cj) {
         if constexpr (ROPE) {
             int page = 0, c0 = 0, id = -1;
             if (cj < nqc) qchunk(cj, page, c0, id);
             if (id >= 0) {
-                if (lane < 32) {
-                    const int t = 4 * wave + (lane >> 3);
-                    lds_dma16(lds_address(rbuf[cj % 3]) + 512u * wave, rrs,
-                              t * RROW + 16 * ((lane & 7) ^ ((t >> 1) & 7)),
-                              (int)(((uint32_t)id * (uint32_t)T + (uint32_t)c0) * (uint32_t)RROW));
-                }
+                const int t = 8 * wave + (lane >> 3);
+                lds_dma16(lds_address(rbuf[cj % 3]) + 1024u * wave, rrs, t * RROW + 16 * ((lane & 7) ^ ((t >> 1) & 7)),
+                          (int)(((uint32_t)id * (uint32_t)T + (uint32_t)c0) * (uint32_t)RROW));
             } else if (lane == 0) {
                 lds_dma16(dummy_lds, rs, 0, 0);
             }
@@ -575,13 +584,16 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
         return id >= 0;
     };
 
-    // loads in flight after the ones a wait needs: the codes and scales of the
-    // next two chunks, and with ROPE the rope keys of the next chunk
-    constexpr int VMW = 2 * (NR - 2) + (ROPE ? 1 : 0);
-    issue_chunk(0);
-    issue_rope(0);
+    // loads of waves 0..3 in flight after the ones a wait needs: the codes
+    // and scales of the next two chunks (three loads each), and with ROPE the
+    // rope keys of the next chunk; the read-back waves have none in flight
+    constexpr int VMW = 3 * (NR - 2) + (ROPE ? 1 : 0);
+    if (!rb_wave) {
+        issue_chunk(0);
+        issue_rope(0);
 #pragma unroll
-    for (int cj = 1; cj < NR - 1; cj++) issue_chunk(cj);
+        for (int cj = 1; cj < NR - 1; cj++) issue_chunk(cj);
+    }
     if (nqc > 0) {
         asm volatile("s_waitcnt vmcnt(%0)" ::"n"(VMW) : "memory");  // chunk 0 has landed
         __syncthreads();
@@ -597,8 +609,10 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
     // (qa, qro) are dead in the second, which leaves the read-back the
     // registers to keep its loads and unit chains in flight together.
     auto head = [&](int ci) {
-        issue_rope(ci + 1);
-        issue_chunk(ci + NR - 1);
+        if (!rb_wave) {
+            issue_rope(ci + 1);
+            issue_chunk(ci + NR - 1);
+        }
         asm volatile("s_waitcnt vmcnt(%0)" ::"n"(VMW) : "memory");  // chunk ci + 1 (and rope ci) have landed
         __syncthreads();
         zk = opaque_zero();
@@ -686,8 +700,7 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
     const i32x4 rfr = raw_buffer(a.rope_fp16, ROPE ? (uint32_t)(a.n_fpages * T * RROW) : 0u);
     auto fchunks = [&](int j) {  // chunks holding tokens of the split's j-th fp16 page (0: none or a bad id)
         const int page = fpage(j);
-        const int id = page_id(nqp + j);
-        if (id < 0 || (int64_t)id >= a.n_fpages) return 0;
+        if (page_id(nqp + j) < 0) return 0;
         return (min(L - page * T, T) + CH - 1) / CH;
     };
     struct FChunk {
