@@ -173,7 +173,6 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
     static_assert(HQ * 2 <= 160, "weight rows hold at most 64 heads");
     __shared__ __attribute__((aligned(16))) uint8_t ybuf[3][CH * YROW];  // chunks, rotated basis (fp16)
     __shared__ __attribute__((aligned(16))) uint8_t pbuf[2][PBYTES];      // weights [token][head] (fp16)
-    __shared__ __attribute__((aligned(16))) uint4 cbuf[2][MD / 8];       // column scales by unit (u at u ^ ((u >> 3) & 7)), by page parity
     __shared__ float alpha[2][HQ];
     __shared__ int rescale_flag[3];
     // ring of chunk slots: codes, token scales (SSC), column scales (SCC)
@@ -503,9 +502,12 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
     // Lane l of read-back wave 4 + v takes token tt = 8 v + (l & 7), units
     // 8 part .. +8 (channels 64 part ..) with part = l >> 3: the 8 lanes of an
     // 8-lane group hold 8 tokens of one column.  The column scales of a page
-    // come from the slot of its first chunk, where they are also staged in
-    // cbuf[page & 1] for its later chunks.
+    // come from the slot of its first chunk and stay in registers (cvk) for
+    // its later chunks: a split's chunks are read back in order.
     const int tt = 8 * ((wave - 4) & 3) + (lane & 7), part = (lane >> 3) & 7;
+    uint4 cvk[8];  // column scales of the lane's 8 units, as fp16 pairs in unpacking order
+#pragma unroll
+    for (int q8 = 0; q8 < 8; q8++) cvk[q8] = make_uint4(0u, 0u, 0u, 0u);
     const int rk = (8 * (part & 1)) ^ (tt & 15);  // read-back store key: unit 8 part + q8 at 16 (part >> 1) + (rk ^ q8)
     auto read_back = [&](int ci) {
         int page, c0, id;
@@ -513,7 +515,6 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
         if (id < 0) return;
         const uint8_t* slot = ring + (ci % NR) * SLOT;
         uint8_t* yb = ybuf[ci % 3];
-        uint4* cb = cbuf[page & 1];
         const uint4* cpg = reinterpret_cast<const uint4*>(slot + SCC);
         uint32_t cw[8];
 #pragma unroll
@@ -556,27 +557,18 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
                     make_uint4(o[0], o[1], o[2], o[3]);
             }
         };
-        // every unit's column scales are read before the first store: the
-        // compiler cannot tell the stores to yb from these reads apart, and
-        // would otherwise wait for each unit's store before the next read
-        uint4 cvs[8];
-        if (c0 == 0) {  // uniform: the page's first chunk brings its column scales
+        // a page's first chunk brings its column scales (uniform branch); they
+        // are all read before the first store, which the compiler cannot tell
+        // apart from these reads
+        if (c0 == 0) {
 #pragma unroll
             for (int q8 = 0; q8 < 8; q8++) {
                 const uint4 c = cpg[8 * part + ((part ^ zk) ^ q8)];  // pairs (0,4) (1,5) (2,6) (3,7) of unit 8 part + q8
-                cvs[q8] = make_uint4(__builtin_amdgcn_perm(c.z, c.x, 0x05040100u), __builtin_amdgcn_perm(c.z, c.x, 0x07060302u),
+                cvk[q8] = make_uint4(__builtin_amdgcn_perm(c.z, c.x, 0x05040100u), __builtin_amdgcn_perm(c.z, c.x, 0x07060302u),
                                      __builtin_amdgcn_perm(c.w, c.y, 0x05040100u), __builtin_amdgcn_perm(c.w, c.y, 0x07060302u));
             }
-            uint4 keep = cvs[0];
-#pragma unroll
-            for (int q8 = 1; q8 < 8; q8++)
-                if (q8 == (tt & 7)) keep = cvs[q8];
-            if (tt < 8) cb[(8 * part + tt) ^ part] = keep;  // staged once per unit for the page's later chunks (same swizzle)
-        } else {
-#pragma unroll
-            for (int q8 = 0; q8 < 8; q8++) cvs[q8] = cb[8 * part + ((part ^ zk) ^ q8)];
         }
-        units(cvs);
+        units(cvk);
     };
     auto chunk_ok = [&](int ci) {
         int page, c0, id;
