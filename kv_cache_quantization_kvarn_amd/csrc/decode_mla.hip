@@ -464,13 +464,20 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
         // byte offsets in the pool (below 4 GiB) as unsigned 32-bit values:
         // the buffer load adds its scalar offset modulo 2^32
         const uint32_t rec = q ? (uint32_t)id * (uint32_t)KREC : 0u;
+        // slot piece 64 p + l (p = 2 wave + h, h = 0, 1) holds piece k ^
+        // cswz(t) of token t's row (t = piece >> 4, k = piece & 15); both
+        // loads under one M0, the second 1 KB further on
+        if (q) {
+            uint32_t vo[2];
 #pragma unroll
-        for (int h = 0; h < 2; h++) {
-            // slot piece 64 p + l (p = 2 wave + h) holds piece k ^ cswz(t) of
-            // token t's row (t = piece >> 4, k = piece & 15)
-            const int p = 2 * wave + h, pc = 64 * p + lane, t = pc >> 4;
-            if (q) lds_dma16(sl + 1024 * p, rs, t * (MD / 2) + 16 * ((pc & 15) ^ cswz(t)), (int)(rec + (uint32_t)(c0 * (MD / 2))));
-            else if (lane == 0) lds_dma16(dummy_lds, rs, 0, 0);
+            for (int h = 0; h < 2; h++) {
+                const int p = 2 * wave + h, pc = 64 * p + lane, t = pc >> 4;
+                vo[h] = t * (MD / 2) + 16 * ((pc & 15) ^ cswz(t));
+            }
+            lds_dma16x2(sl + 2048 * wave, rs, vo[0], vo[1] - 1024u, (int)(rec + (uint32_t)(c0 * (MD / 2))));
+        } else if (lane == 0) {
+            lds_dma16(dummy_lds, rs, 0, 0);
+            lds_dma16(dummy_lds, rs, 0, 0);
         }
         if (q && wave == 0) {
             if (lane < CH / 4) lds_dma16(sl + SSC, rs, 16 * lane, (int)(rec + (uint32_t)(KCB + 4 * c0)));

@@ -152,6 +152,16 @@ __device__ __forceinline__ void lds_dma16(uint32_t lds, i32x4 rsrc, uint32_t vof
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                  ::"s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
 }
+// Two such loads with one M0: the second one's 16 bytes land 1024 bytes
+// further on in LDS, and its instruction offset of 1024 is added to both of
+// its addresses, so voff1 is its byte offset less 1024 (voff1 + 1024 >= 1024).
+__device__ __forceinline__ void lds_dma16x2(uint32_t lds, i32x4 rsrc, uint32_t voff0, uint32_t voff1, int soff) {
+    lds = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds);
+    soff = __builtin_amdgcn_readfirstlane(soff);
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %3, %4 offen lds\n\t"
+                 "buffer_load_dwordx4 %2, %3, %4 offen offset:1024 lds"
+                 ::"s"(lds), "v"(voff0), "v"(voff1), "s"(rsrc), "s"(soff) : "memory", "m0");
+}
 #pragma clang diagnostic pop
 // LDS byte address of a pointer into __shared__ memory
 __device__ __forceinline__ uint32_t lds_address(const void* p) {
