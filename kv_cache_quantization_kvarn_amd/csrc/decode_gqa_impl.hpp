@@ -990,20 +990,18 @@ __global__ void __launch_bounds__(64) decode_split128_kernel(DecodeArgs a) {
         // values: the buffer load adds its scalar offset modulo 2^32
         const uint32_t sk = (uint32_t)__builtin_amdgcn_readfirstlane((int)(rec * (uint32_t)KREC));
         const uint32_t sv = (uint32_t)__builtin_amdgcn_readfirstlane((int)(rec * (uint32_t)VREC));
-#pragma unroll
-        for (int i = 0; i < KST / 1024; i++)
-            lds_dma16(sb + 1024 * i, rsk, 16 * kswz(64 * i + lane), (int)(sk + (uint32_t)(KST * r.h)));
+        // kswz(64 i + lane) = 64 i + kswz(lane): the KST / 1024 key loads
+        // are runs under one M0 each
+        static_assert(KST % 1024 == 0, "key runs");
+        lds_dma16_runs<KST / 1024>(sb, rsk, 16 * kswz(lane), (int)(sk + (uint32_t)(KST * r.h)));
         if (r.h == 0 && lane < SB / 16) {  // the page's scale blocks
             lds_dma16(sb + KSC, rsk, 16 * lane, (int)(sk + (uint32_t)KCB));
             lds_dma16(sb + VSC, rsv, 16 * lane, (int)(sv + (uint32_t)VCB));
         }
-#pragma unroll
-        for (int i = 0; i < VST / 1024; i++) {
-            // piece u = channel u / (VB / 2), part u % (VB / 2): values are kept
-            // in 64-token blocks, so a step's pieces are one contiguous run
-            const int u = 64 * i + lane;
-            lds_dma16(sb + VSO + 1024 * i, rsv, 16 * u, (int)(sv + (uint32_t)((64 * D * VB / 8) * r.h)));
-        }
+        // piece u = channel u / (VB / 2), part u % (VB / 2): values are kept
+        // in 64-token blocks, so a step's pieces are one contiguous run
+        static_assert(VST % 1024 == 0, "value runs");
+        lds_dma16_runs<VST / 1024>(sb + VSO, rsv, 16 * lane, (int)(sv + (uint32_t)((64 * D * VB / 8) * r.h)));
     };
     // the lane's operands of a step out of the stage (after its loads have
     // landed); once these reads are done the stage may be refilled

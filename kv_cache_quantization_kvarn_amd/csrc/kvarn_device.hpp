@@ -162,6 +162,39 @@ __device__ __forceinline__ void lds_dma16x2(uint32_t lds, i32x4 rsrc, uint32_t v
                  "buffer_load_dwordx4 %2, %3, %4 offen offset:1024 lds"
                  ::"s"(lds), "v"(voff0), "v"(voff1), "s"(rsrc), "s"(soff) : "memory", "m0");
 }
+// N (1, 2 or 4) such loads with one M0 and one lane offset: load i reads the
+// memory 1024 i bytes after load 0's and lands 1024 i bytes after it in LDS.
+template <int N>
+__device__ __forceinline__ void lds_dma16_run(uint32_t lds, i32x4 rsrc, uint32_t voff, int soff) {
+    static_assert(N == 1 || N == 2 || N == 4, "runs of 1, 2 or 4 KB");
+    lds = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds);
+    soff = __builtin_amdgcn_readfirstlane(soff);
+    if constexpr (N == 1) {
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                     ::"s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
+    } else if constexpr (N == 2) {
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds\n\t"
+                     "buffer_load_dwordx4 %1, %2, %3 offen offset:1024 lds"
+                     ::"s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
+    } else {
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds\n\t"
+                     "buffer_load_dwordx4 %1, %2, %3 offen offset:1024 lds\n\t"
+                     "buffer_load_dwordx4 %1, %2, %3 offen offset:2048 lds\n\t"
+                     "buffer_load_dwordx4 %1, %2, %3 offen offset:3072 lds"
+                     ::"s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
+    }
+}
+// N KB (N = 1 .. 8 but 3, 5, 7) as runs of at most 4 (the instruction offset
+// stops at 4095)
+template <int N>
+__device__ __forceinline__ void lds_dma16_runs(uint32_t lds, i32x4 rsrc, uint32_t voff, int soff) {
+    if constexpr (N <= 4) {
+        lds_dma16_run<N>(lds, rsrc, voff, soff);
+    } else {
+        lds_dma16_run<4>(lds, rsrc, voff, soff);
+        lds_dma16_run<N - 4>(lds + 4096u, rsrc, voff + 4096u, soff);
+    }
+}
 #pragma clang diagnostic pop
 // LDS byte address of a pointer into __shared__ memory
 __device__ __forceinline__ uint32_t lds_address(const void* p) {
