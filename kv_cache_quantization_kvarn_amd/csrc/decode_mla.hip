@@ -153,13 +153,14 @@ struct MlaShape {
 // stream through an LDS ring; between two barriers chunk c + 1 is read back
 // and chunk c scored, and the value sums of chunk c - 1 are formed), then its
 // fp16 chunks.  Chunk s (the quantized ones, then the fp16 ones) uses read-back
-// buffer s mod 3 (quantized) or 0 (fp16), weight and rescale buffers s mod 2 and rescale flag s mod 3.
+// buffer s mod 3 (quantized) or 1 and 2 in turn (fp16), weight and rescale
+// buffers s mod 2 and rescale flag s mod 3.
 //
 // ROPE: a 64-wide fp16 rope key beside each latent (DeepSeek-style MLA; the
 // latent alone is quantized, evermx.com KVarN review, MLA paragraph) adds
 // <q_rope, r_t> to every score.  A chunk's rope keys (4 KB) come by LDS-DMA
-// into rbuf[s mod 3] one iteration ahead of its score, as each wave's first
-// load of the iteration (so the fixed wait count rises by one); they take two
+// into rbuf[s mod 3] one iteration ahead of its score, one load for each of
+// waves 0..3 per chunk (so their fixed wait count rises by one); they take two
 // more k-steps per token half of the score MFMAs, with the rope query (fp16,
 // natural channel order) as their A operand.
 template <int T, int HB, bool ROPE>
@@ -178,7 +179,7 @@ __global__ void __launch_bounds__(MlaShape<HB>::NT) mla_split_kernel(DecodeArgs 
     // ring of chunk slots: codes, token scales (SSC), column scales (SCC)
     constexpr int NR = 4;
     constexpr int SSC = CH * MD / 2, SCC = SSC + 4 * CH, SLOT = SCC + 2 * MD;
-    static_assert(SSC == NWV * 1024, "one 1 KB code load per wave and chunk");
+    static_assert(SSC == NWV * 1024, "8 KB of codes a chunk: two 1 KB loads for each of waves 0..3");
     __shared__ __attribute__((aligned(16))) uint8_t ring[NR * SLOT];
     __shared__ __attribute__((aligned(16))) uint8_t scratch[16 * NWV];  // targets of the stand-in loads
     // rope keys of a chunk: token rows of RROW bytes, unit u of token t at
