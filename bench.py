@@ -33,7 +33,10 @@ Reported (one JSON line):
              (decode_rope64: the same cache plus its rope pools and 576-wide
              queries; bytes and flops include the rope part).
              The headline workload also times a verify step (decode of 4
-             uncommitted query tokens per sequence, causal among themselves).
+             uncommitted query tokens per sequence, causal among themselves);
+             the 16 x 32K workload also runs with the key/value code widths
+             3/5, 5/3 and 8/8 (widths: quantize and decode times and
+             fractions, records of those widths).
   cpu_baseline the oracle (plain C, fp64, OpenMP) on a bounded sample of the
              headline workload, same byte formulas; per_core: the oracle on
              one thread over the one-layer 1024-token case.
@@ -51,6 +54,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 MFMA_F16_PEAK_TFLOPS = 2500.0   # dense fp16 / bf16 matrix peak of the MI355X
 HEADLINE = "dense8b_b64_16k_k4v2_g64"
+# the 16 x 32K layer also runs with these key/value code widths
+WIDTHS_WORKLOAD, WIDTH_PAIRS = "dense8b_b16_32k_k4v2_g128", [(3, 5), (5, 3), (8, 8)]
 SUITE = ["tiny_d128_k4v2", "dense8b_b16_32k_k4v2_g128", "dense8b_b64_16k_k4v2_g64", "wide_d256_b8_64k_k6v6",
          "wide_d512_b8_64k_k6v6", "mla_d512_b32_32k_int4"]
 # sources whose compiled code the recorded counter passes measured
@@ -276,6 +281,34 @@ class Runner:
                 "note": "verify step: M uncommitted query tokens per sequence, causal among themselves, one read of "
                         "the cache; bytes = cache + q + out"}
 
+    def time_widths(self, pairs, steps, warmup, flush):
+        """Quantize and decode of the same fp16 pages with other key/value code
+        widths (3, 5 and 8 bits straddle or fill bytes; their quantize runs
+        keys and values as two launches): per pair the same figures as the
+        workload's own component."""
+        torch, kv, c = self.torch, self.kv, self.case
+        lay0, L0, k0, v0, b0 = c["layout"], self.L, self.krec, self.vrec, self.bytes
+        H, nq = lay0["H"], max(c["n_qpages"], 1)
+        dev = c["q"].device
+        out = {}
+        try:
+            for kb, vb in pairs:
+                lay = dict(lay0, k_bits=kb, v_bits=vb)
+                c["layout"] = lay
+                self.L = kv.layout_from_dict(lay)
+                self.krec = torch.empty((nq, H, kv.record_bytes(self.L, 0)), dtype=torch.uint8, device=dev)
+                self.vrec = torch.empty((nq, H, kv.record_bytes(self.L, 1)), dtype=torch.uint8, device=dev)
+                self.bytes = byte_counts(c)
+                tq, td = self.time_steps(steps, warmup, flush)
+                comp = self.component(tq, td)
+                out[f"k{kb}v{vb}"] = {"quantize": {k: comp["quantize"][k] for k in ("us", "us_p10", "us_p90",
+                                                                                      "traffic_frac", "fp16_frac")},
+                                      "decode": {k: comp["decode"][k] for k in ("us", "us_p10", "us_p90", "frac")}}
+                del self.krec, self.vrec
+        finally:
+            c["layout"], self.L, self.krec, self.vrec, self.bytes = lay0, L0, k0, v0, b0
+        return out
+
     def time_rope(self, steps, warmup, flush, R=64):
         """MLA decode of the same cache with an R-wide fp16 rope key beside
         every latent: seeded rope pools (the quantize call copies each
@@ -425,6 +458,9 @@ def main():
             if r.case["layout"]["mla"]:
                 res["components"][name]["decode_rope64"] = r.time_rope(args.component_steps, args.component_warmup,
                                                                        flush)
+            if name == WIDTHS_WORKLOAD:
+                res["components"][name]["widths"] = r.time_widths(WIDTH_PAIRS, args.component_steps,
+                                                                  args.component_warmup, flush)
             r.free()
             print(f"[bench] component {name} done", file=sys.stderr, flush=True)
     print(json.dumps(res), flush=True)
