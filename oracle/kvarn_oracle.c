@@ -644,9 +644,8 @@ int orc_decode_mq(const int32_t *cfg, const uint8_t *krec, const uint8_t *vrec,
 /* MLA with a rope sidecar.  An MLA model's key has two parts: the
  * compressed latent, which this method quantizes to int4 [R ¶4] and which
  * is also the value, and a small rotary-position key beside it (64 wide in
- * DeepSeek-style MLA), which stays fp16 (the survey's reading of the 2.77x
- * capacity figure of [R ¶4]: the rope key kept 16-bit is consistent with
- * it).  Plain definition, per requested row (b, i, h):
+ * DeepSeek-style MLA), which stays fp16 (a reading of the 2.77x capacity
+ * figure of [R ¶4]: the rope key kept 16-bit is consistent with it).  Plain definition, per requested row (b, i, h):
  *   key t = (x_t, r_t), value t = x_t, query = (q_lat[D], q_rope[R]),
  *   score_t = sm_scale * (<q_lat, x_t> + <q_rope, r_t>),
  *   out = sum_t softmax_t(score_t) x_t,
