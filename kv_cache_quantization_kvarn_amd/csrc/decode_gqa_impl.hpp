@@ -49,6 +49,13 @@ template <int ABID>
 __device__ __forceinline__ f4 mfma_bcast(h4 a, h4 b, f4 c) {
     return __builtin_amdgcn_mfma_f32_4x4x4f16(a, b, c, 4, ABID, 0);
 }
+// the same with broadcast groups of 8 blocks: blocks 0-7 (lanes 0-31) take
+// operand A from block ABID, blocks 8-15 (lanes 32-63) from block 8 + ABID
+template <int ABID>
+__device__ __forceinline__ f4 mfma_bcast8(h4 a, h4 b, f4 c) {
+    static_assert(ABID < 8, "source block inside the group");
+    return __builtin_amdgcn_mfma_f32_4x4x4f16(a, b, c, 3, ABID, 0);
+}
 
 template <typename F, int... I>
 __device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
@@ -181,6 +188,21 @@ __device__ __forceinline__ float sum_blocks_half(float v) {
 // tail pages); its partial goes to split nsplit + f with a zero rotated-basis
 // sum.  Scores on the MFMA with the plain query (fp16 high and low parts),
 // lane = token; value sums on the VALU, D/8 lanes per token row.
+//
+// Key rows are read so that both 64-byte halves of every 128-byte line are
+// requested by one load instruction: a line whose halves are requested by
+// different instructions, the second while the fill of the first is still
+// pending, is fetched from HBM twice (about 2x the key bytes, measured
+// with the L2's read-request counters).  Tokens t and 32 + t pair up: one
+// load gives lane t (< 32) piece p of token t and lane 32 + t piece p + 4 of
+// token t, the next gives lane t piece p + 4 of token 32 + t and lane 32 + t
+// piece p of token 32 + t.  Each lane accumulates what it holds: the lower
+// and the upper lane halves hold different channel groups in one register,
+// so the MFMA broadcasts its query operand within groups of 8 blocks, with
+// the query slots held a second time, half-swapped, for the second load.
+// The first load's sums of lanes t and 32 + t make token t's score, the
+// second load's those of token 32 + t: one v_permlane32_swap per head adds
+// them up at the end.
 template <int D, int T>
 __device__ __forceinline__ void fp16_block(const DecodeArgs& a, const int f, const int h, const int b,
                                            float4* pf /* LDS, 64 entries: weights of the part */) {
@@ -235,24 +257,67 @@ __device__ __forceinline__ void fp16_block(const DecodeArgs& a, const int f, con
                 qp[r][kk] = (_Float16)qx[r][kk];
                 qpl[r][kk] = (_Float16)(qx[r][kk] - (float)qp[r][kk]);
             }
+        // the same slots half-swapped: lane l holds what lane l ^ 32 holds
+        // above, i.e. block blk the channel group of block blk ^ 8
+        const bool upper = lane >= 32;
+        auto half_swap = [&](h4 v) {
+            uint2 w = __builtin_bit_cast(uint2, v);
+            const auto x = __builtin_amdgcn_permlane32_swap(w.x, w.x, false, false);
+            const auto y = __builtin_amdgcn_permlane32_swap(w.y, w.y, false, false);
+            // x[0]: lower half of w.x in both halves; x[1]: upper half of w.x in both
+            return __builtin_bit_cast(h4, make_uint2(upper ? x[0] : x[1], upper ? y[0] : y[1]));
+        };
+        h4 qps[NS], qpls[NS];
+#pragma unroll
+        for (int r = 0; r < NS; r++) {
+            qps[r] = half_swap(qp[r]);
+            qpls[r] = half_swap(qpl[r]);
+        }
         float s[G];
         {
-            const uint16_t* kr = static_cast<const uint16_t*>(a.k_fp16) + (((int64_t)id * a.H + h / a.GS) * T + 64 * sb + lane) * D;
-            f4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+            // token 0 of the part; a 16-byte piece p holds channels 8 p .. 8 p + 7
+            const uint16_t* kt = static_cast<const uint16_t*>(a.k_fp16) + (((int64_t)id * a.H + h / a.GS) * T + 64 * sb) * D;
+            const int t5 = lane & 31;
+            const int hx = upper ? 4 : 0;  // piece offset of the first load in this lane half
+            const f4 zero = {0.f, 0.f, 0.f, 0.f};
+            f4 ax0 = zero, ax1 = zero, ay0 = zero, ay1 = zero;
 #pragma unroll
             for (int c = 0; c < NC; c++) {
-                static_for<16>([&](auto ic) {
-                    constexpr int il = 2 * decltype(ic)::value;
-                    const uint4 v = *reinterpret_cast<const uint4*>(kr + 128 * c + 4 * il);
-                    const h4 b0 = __builtin_bit_cast(h4, make_uint2(v.x, v.y));
-                    const h4 b1 = __builtin_bit_cast(h4, make_uint2(v.z, v.w));
-                    acc0 = mfma_bcast<il & 15>(qp[2 * c + (il >> 4)], b0, acc0);
-                    acc1 = mfma_bcast<il & 15>(qpl[2 * c + (il >> 4)], b0, acc1);
-                    acc0 = mfma_bcast<(il + 1) & 15>(qp[2 * c + ((il + 1) >> 4)], b1, acc0);
-                    acc1 = mfma_bcast<(il + 1) & 15>(qpl[2 * c + ((il + 1) >> 4)], b1, acc1);
+                // pieces pa and pa + 4 (the two halves of a 128-byte line) of a
+                // 256-byte chunk of 128 channels
+                static_for<8>([&](auto jc) {
+                    constexpr int j = decltype(jc)::value;
+                    constexpr int pa = (j & 3) + 8 * (j >> 2);
+                    // x: tokens 0-31, piece pa (lower lanes) or pa + 4 (upper);
+                    // y: tokens 32-63, piece pa + 4 (lower lanes) or pa (upper)
+                    const uint4 x = *reinterpret_cast<const uint4*>(kt + (int64_t)t5 * D + 128 * c + 8 * (pa + hx));
+                    const uint4 y = *reinterpret_cast<const uint4*>(kt + (int64_t)(32 + t5) * D + 128 * c + 8 * (pa + 4 - hx));
+                    const h4 x0 = __builtin_bit_cast(h4, make_uint2(x.x, x.y));
+                    const h4 x1 = __builtin_bit_cast(h4, make_uint2(x.z, x.w));
+                    const h4 y0 = __builtin_bit_cast(h4, make_uint2(y.x, y.y));
+                    const h4 y1 = __builtin_bit_cast(h4, make_uint2(y.z, y.w));
+                    // channel group 2 pa + e of the chunk (lower lanes of x): slot
+                    // r, block ab + e; the upper lanes' group is 8 higher, block 8 + ab + e
+                    constexpr int ab = (2 * pa) & 15;
+                    const int r = 2 * c + (pa >> 3);
+                    ax0 = mfma_bcast8<ab>(qp[r], x0, ax0);
+                    ax1 = mfma_bcast8<ab>(qpl[r], x0, ax1);
+                    ax0 = mfma_bcast8<ab + 1>(qp[r], x1, ax0);
+                    ax1 = mfma_bcast8<ab + 1>(qpl[r], x1, ax1);
+                    ay0 = mfma_bcast8<ab>(qps[r], y0, ay0);
+                    ay1 = mfma_bcast8<ab>(qpls[r], y0, ay1);
+                    ay0 = mfma_bcast8<ab + 1>(qps[r], y1, ay0);
+                    ay1 = mfma_bcast8<ab + 1>(qpls[r], y1, ay1);
                 });
             }
-            const f4 R = acc0 + acc1;
+            // lane t < 32: x sums of lanes t and t + 32 (token t); lane t + 32: y sums (token t + 32)
+            const f4 X = ax0 + ax1, Y = ay0 + ay1;
+            f4 R;
+#pragma unroll
+            for (int g = 0; g < G; g++) {
+                const auto w = __builtin_amdgcn_permlane32_swap((unsigned)f2i(X[g]), (unsigned)f2i(Y[g]), false, false);
+                R[g] = i2f((int)w[0]) + i2f((int)w[1]);
+            }
             const bool valid = lane < nvalid;
 #pragma unroll
             for (int g = 0; g < G; g++) s[g] = valid ? sm2 * R[g] : -INFINITY;
