@@ -16,7 +16,8 @@ namespace {
 // part added, the sum normalized.  Lane l holds channels CPL l .. CPL l +
 // CPL - 1 (CPL = D / 64).  The partials' maxima and weight sums meet through
 // wave reductions; the value sums stream through, each split's weight read
-// from the lane that owns the split (v_readlane); the inverse rotation is an
+// from the lane that owns the split (v_readlane), U of them a step (their
+// loads in flight together); the inverse rotation is an
 // in-register fast Walsh-Hadamard transform: in-lane stages over the low
 // channel bits, then one cross-lane stage per lane bit.  With many rows each
 // of a workgroup's 4 waves takes a row of its own (no LDS, no barrier); with
@@ -27,7 +28,7 @@ __global__ void __launch_bounds__(256) split_merge_kernel(const float* __restric
                                                           int nrows, int nq, int np, int wpr) {
     constexpr int WS = D + 4;           // partial: m, l, pad, pad, value sums
     constexpr int CPL = D / 64;
-    constexpr int U = 8;                // splits per step, their loads issued together
+    constexpr int U = CPL == 8 ? 8 : 16;  // splits per step, their loads issued together
     static_assert(CPL == 2 || CPL == 4 || CPL == 8, "head dims 128, 256, 512");
     __shared__ float red[3][2 * D + 1];  // waves 1..3 of a shared row: r, pl, Ls
     const int wave = (int)(threadIdx.x >> 6);
@@ -36,8 +37,14 @@ __global__ void __launch_bounds__(256) split_merge_kernel(const float* __restric
     if (row >= nrows) return;  // whole waves (wpr = 4: the whole workgroup)
     const int lane = threadIdx.x & 63;
     const float* base = ws + (int64_t)row * np * WS;
-    float M = -INFINITY;
-    for (int s = lane; s < np; s += 64) M = fmaxf(M, base[(int64_t)s * WS]);
+    // maxima and weight sums of the first 64 partials, kept for the weights
+    float m0 = -INFINITY, l0 = 0.f;
+    if (lane < np) {
+        m0 = base[(int64_t)lane * WS];
+        l0 = base[(int64_t)lane * WS + 1];
+    }
+    float M = m0;
+    for (int s = 64 + lane; s < np; s += 64) M = fmaxf(M, base[(int64_t)s * WS]);
     M = wave_max_all(M);
     float r[CPL], pl[CPL];
 #pragma unroll
@@ -47,9 +54,9 @@ __global__ void __launch_bounds__(256) split_merge_kernel(const float* __restric
         for (int s0 = 0; s0 < np; s0 += 64) {
             float e = 0.f;
             if (s0 + lane < np) {
-                const float ms = base[(int64_t)(s0 + lane) * WS];
+                const float ms = s0 == 0 ? m0 : base[(int64_t)(s0 + lane) * WS];
                 e = ms == -INFINITY ? 0.f : exp2f(ms - M);
-                if (part == 0) Ls = fmaf(base[(int64_t)(s0 + lane) * WS + 1], e, Ls);
+                if (part == 0) Ls = fmaf(s0 == 0 ? l0 : base[(int64_t)(s0 + lane) * WS + 1], e, Ls);
             }
             const int n = min(64, np - s0);
             // a loop holding v_readlane is not unrolled by the compiler: U
