@@ -8,6 +8,7 @@ import numpy as np
 import pytest
 import torch
 
+import kv_cache_quantization_kvarn_amd as kv
 from gpu_util import gpu_case, oracle_decode, run_decode, run_quantize, say, workload
 from parity_util import DECODE_RTOL, decode_rel_err
 
@@ -297,3 +298,25 @@ def test_decode_mla_other_query_dtypes(qd):
     L, krec, vrec = run_quantize(case)
     out = run_decode(case, L, krec, vrec)
     check(case, out, krec, None)
+
+
+@pytest.mark.parametrize("name,length", [("dense8b_b64_16k_k4v2_g64", 16384), ("wide_d512_b8_64k_k6v6", 16384),
+                                         ("mla_d512_b32_32k_int4", 32768)])
+def test_decode_one_long_sequence(name, length):
+    """A batch of one long sequence: the split count grows until the pages
+    are spread thin, and each row has far more than 64 partials, which the
+    merge takes 64 at a time (maxima, weight sums, then the value sums)."""
+    w = workload(name, L=length, seed=0x4500)
+    case = gpu_case(w, seq_lens=[length], batch=1)
+    lay = case["layout"]
+    say("one long sequence", name, length)
+    L, krec, vrec = run_quantize(case)
+    D, hq = lay["D"], case["Hq"]
+    ws = kv.decode_workspace_bytes(L, 1, hq, case["max_pages"]) // 4
+    lead = hq * D // 2 if lay["mla"] else hq * D  # rotated queries ahead of the partials
+    partials = (ws - lead) // (hq * (D + 4))
+    say("partials per row", partials)
+    assert partials > 64
+    out = run_decode(case, L, krec, vrec)
+    pairs = np.array([(0, h) for h in sorted({0, 1, hq // 2, hq - 1})], np.int32)
+    check(case, out, krec, None if lay["mla"] else vrec, pairs)
